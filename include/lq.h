@@ -1,0 +1,237 @@
+/*
+ * lq.h -- LoRA / QLoRA adapted linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the library liblq.so.  Every entry point takes plain pointers and
+ * sizes; device pointers are HIP device memory owned by the caller, contiguous
+ * and row-major unless stated.  No call allocates device memory or keeps a
+ * pointer after it returns, and none synchronises: work is enqueued on the
+ * caller's stream and the call returns.
+ *
+ * Notation (batched row form): X is M x K, the frozen base W0 is N x K
+ * (d_out x d_in), A is r x K, B is N x r, s = alpha / r ("scale"), Y is M x N,
+ * T = X A^T (M x r), U = dY B (M x r).
+ *
+ * Errors: argument problems (null pointer where one is required, a size that
+ * is zero where it must not be, an unsupported dtype / shape / rank, a short
+ * workspace) are detected before anything is launched and return a negative
+ * lq_status; lq_last_error() then gives a message for the calling thread.
+ * A failed launch returns LQ_ERR_HIP with HIP's message.  Faults inside a
+ * kernel surface at the caller's next synchronisation of the stream.
+ *
+ * Sources, cited by page title and section:
+ *   [MF]  "Low-Rank Adaptation (LoRA) and QLoRA: Mathematical Foundations,
+ *          Intrinsic Rank Dynamics, NF4 Quantization, and Parameter-Efficient
+ *          Fine-Tuning" (llms.blog)
+ *   [FT]  "Large Language Model Fine-tuning and LoRA" (aicomputerinstitute.com)
+ *   [UH]  "LoRA and QLoRA fine-tuning under the hood" (codingpancake.com)
+ *   [L26] "Lesson 26: LoRA / QLoRA theory" (teology.holyping.network)
+ */
+#ifndef LQ_H
+#define LQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lq_status {
+  LQ_OK = 0,
+  LQ_ERR_INVALID_ARG = -1,   /* null pointer, bad size, inconsistent metadata   */
+  LQ_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement      */
+  LQ_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required       */
+  LQ_ERR_HIP = -4            /* a HIP call failed; message in lq_last_error()    */
+} lq_status;
+
+typedef enum lq_dtype {
+  LQ_F32 = 0,                /* IEEE binary32                                    */
+  LQ_BF16 = 1                /* bfloat16 (upper half of binary32), RNE stores    */
+} lq_dtype;
+
+typedef enum lq_weight_kind {
+  LQ_WEIGHT_DENSE = 0,       /* W0 stored densely in ``dtype``                   */
+  LQ_WEIGHT_NF4 = 1          /* W0 stored as NF4 codes + block constants         */
+} lq_weight_kind;
+
+/* NF4 block sizes fixed by [FT] "Quantizing the frozen weights: NF4 and double
+ * quantization" (64 weights per absmax) and [MF] "2. Double Quantization (DQ)"
+ * (256 first-level constants per second-level block). */
+#define LQ_NF4_BLOCK 64
+#define LQ_NF4_DQ_BLOCK 256
+
+/*
+ * The frozen base weight W0, N x K, as seen by every LoRA entry point.
+ *
+ * kind == LQ_WEIGHT_DENSE: ``dense`` points at N*K elements of ``dtype``.
+ * kind == LQ_WEIGHT_NF4: the flattened row-major tensor in NF4 with
+ *   codes     ceil(N*K/2) bytes, element 2j in the low nibble of byte j and
+ *             element 2j+1 in the high nibble (an odd count leaves the last
+ *             high nibble 0);
+ *   q8        ceil(N*K/64) bytes (double_quant = 1): 8-bit first-level
+ *             constants, 0..127;
+ *   c2        ceil(ceil(N*K/64)/256) floats (double_quant = 1): second-level
+ *             constants;
+ *   absmax    ceil(N*K/64) floats (double_quant = 0): float32 first-level
+ *             constants;
+ *   the dequantised element is fl32(cb[code] * a') with a' =
+ *   fl32(q8 * fl32(c2/127)) (or a' = absmax), fed to bf16 arithmetic as its
+ *   round-to-nearest-even bf16 value ([MF] "1. 4-bit NormalFloat (NF4)
+ *   Quantization": dequantised to BF16 right before the multiply).
+ * ``dtype`` for NF4 is the compute dtype the caller intends (checked against
+ * the call's dtype).  All pointers are device pointers owned by the caller.
+ */
+typedef struct lq_weight {
+  int32_t kind;              /* lq_weight_kind                                  */
+  int32_t dtype;             /* lq_dtype of ``dense`` (dense) / compute (NF4)   */
+  int64_t N;                 /* rows, d_out                                     */
+  int64_t K;                 /* columns, d_in                                   */
+  const void* dense;
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* c2;
+  const float* absmax;
+  int32_t double_quant;      /* 1: q8 + c2, 0: absmax                            */
+  int32_t reserved;          /* must be 0                                       */
+} lq_weight;
+
+/* --------------------------------------------------------------- NF4 codec */
+
+/*
+ * Host copy of the 16 NF4 levels ([MF] "1. 4-bit NormalFloat (NF4)
+ * Quantization": normal quantiles normalised to [-1, 1]).  Built on the host
+ * in double precision as the asymmetric quantile set with an exact zero
+ * (8 positive levels, 7 negative, 0; outer probability 1 - (1/32 + 1/30)/2),
+ * then rounded to float32.  ``out`` is host memory for 16 floats.
+ * Returns LQ_OK or LQ_ERR_INVALID_ARG (null out).
+ */
+int lq_nf4_codebook(float* out);
+
+/*
+ * Quantise n elements of W (flattened, row-major) to NF4
+ * ([MF] "1. 4-bit NormalFloat (NF4) Quantization" steps 1-3, and
+ * "2. Double Quantization (DQ)"; [FT] "Quantizing the frozen weights").
+ *   W        device, n elements of wdt (LQ_F32 or LQ_BF16; bf16 widened
+ *            exactly to float32)
+ *   blocks of 64 consecutive elements (last may be partial): c1 = max|w|,
+ *   x = fl32(w / c1), code = number of the 15 float32 midpoints between
+ *   neighbouring levels that are strictly below x (c1 = 0: code 7).
+ *   double_quant = 1: groups of 256 blocks, c2 = max c1 (float32, written to
+ *   c2[ceil(nb/256)]), q8 = rint(fl32(fl32(c1/c2) * 127)) (ties to even,
+ *   c2 = 0 gives 0) written to q8[nb]; ``absmax`` may be NULL.
+ *   double_quant = 0: c1 written to absmax[nb]; q8 and c2 may be NULL.
+ *   codes    device, ceil(n/2) bytes (packing as in lq_weight).
+ * Results are bit-exact functions of the input.  n >= 1.
+ */
+int lq_nf4_quantize(const void* W, lq_dtype wdt, int64_t n, int32_t double_quant,
+                    uint8_t* codes, uint8_t* q8, float* c2, float* absmax,
+                    hipStream_t stream);
+
+/*
+ * Dequantise n NF4 elements (layout as in lq_weight) to ``out``: n elements
+ * of odt, fl32(cb[code] * a') for LQ_F32, its RNE bf16 for LQ_BF16.
+ * Bit-exact.  The inverse of lq_nf4_quantize up to the quantisation error.
+ */
+int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
+                      const float* absmax, int32_t double_quant, int64_t n,
+                      void* out, lq_dtype odt, hipStream_t stream);
+
+/* ------------------------------------------------------- adapted linear */
+
+/*
+ * Forward: Y = X W0^T + s (X A^T) B^T   ([MF] forward-pass equation
+ * h = W0 x + (alpha/r) B A x, and the diagram placing alpha/r after B;
+ * [UH] 1.2; [L26] "The Decomposition").
+ *   X  device M x K of dt;  A device r x K of dt;  B device N x r of dt;
+ *   Y  device M x N of dt (written, not accumulated);
+ *   T_out  optional device M x r float32: receives T = X A^T for lq_lora_bwd.
+ *   ws / ws_bytes: device workspace of lq_workspace_size(LQ_OP_FWD, M, N, K,
+ *   r, 0) bytes (M * r floats), needed only when T_out is NULL and the call
+ *   takes the float32 or the decode path, which keep T in memory between two
+ *   kernels; otherwise ws may be NULL.
+ *   dt = LQ_BF16: bf16 inputs, float32 accumulation, bf16 RNE output; W0 dense
+ *   bf16 or NF4 (dequantised in registers / LDS, never written to memory).
+ *   Requires K % 64 == 0, N % 32 == 0, 1 <= r <= 64.  M <= 16 takes the
+ *   memory-bound decode path.
+ *   dt = LQ_F32: float32 throughout (W0 dense f32 or NF4), 1 <= r <= 64.
+ * M = 0 is a no-op returning LQ_OK.
+ */
+int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A,
+                const void* B, int64_t r, float scale, lq_dtype dt, void* Y,
+                float* T_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward ([MF] "Gradient Dynamics and Backpropagation Mechanics", summed
+ * over the batch rows; W0 receives no gradient):
+ *   dX = dY W0 + s (dY B) A      (optional: dX may be NULL)
+ *   dA = s (dY B)^T X            (r x K float32)
+ *   dB = s dY^T (X A^T)          (N x r float32)
+ *   dY device M x N of dt, X device M x K of dt, A and B as in lq_lora_fwd.
+ *   T_saved: optional device M x r float32 from lq_lora_fwd's T_out; when
+ *   NULL, T is recomputed.
+ *   accumulate = 1 adds into dA and dB (gradient accumulation over
+ *   micro-batches); 0 overwrites them.
+ *   ws / ws_bytes: device workspace of at least
+ *   lq_workspace_size(LQ_OP_BWD, M, N, K, r, 0) bytes (caller-owned).
+ * Same shape rules as lq_lora_fwd.
+ */
+int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0,
+                const void* A, const void* B, int64_t r, float scale, lq_dtype dt,
+                const float* T_saved, void* dX, float* dA, float* dB,
+                int32_t accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Merge for deployment: W_out = deq(W0) + s B A, N x K of dt
+ * ([MF] "1. Static Weight Merging"; [FT] "Merging adapters vs keeping them
+ * separate"; [L26] "4. Merging Adapters").  The merged matrix has W0's shape
+ * and the compute dtype; float32 accumulation, one rounding to dt.
+ */
+int lq_lora_merge(const lq_weight* W0, const void* A, const void* B, int64_t r,
+                  float scale, lq_dtype dt, void* W_out, hipStream_t stream);
+
+/*
+ * Segmented multi-adapter forward on one shared base ([FT] "Serving many
+ * adapters at once: the multi-tenant problem"; [MF] "2. Multi-Tenant Dynamic
+ * Multiplexing", segmented GEMM):
+ *   for each segment i: rows seg_offsets[i] .. seg_offsets[i+1]-1 of X get
+ *   Y_i = X_i W0^T + s (X_i A_{id}^T) B_{id}^T with id = seg_adapter[i].
+ *   X        device T_tokens x K of dt (bf16)
+ *   A_stack  device n_adapters x r x K;  B_stack device n_adapters x N x r
+ *   seg_offsets device int32[n_seg+1], seg_adapter device int32[n_seg]
+ *   (preconditions: offsets non-decreasing from 0 to T_tokens, ids in
+ *   [0, n_adapters); lq_check_segments verifies host copies).
+ *   ws: at least lq_workspace_size(LQ_OP_FWD_MULTI, T_tokens, N, K, r,
+ *   n_adapters) bytes.
+ *   Requires dt = LQ_BF16, K % 64 == 0, N % 32 == 0, r * n_adapters <= 64.
+ */
+int lq_lora_fwd_multi(const void* X, int64_t T_tokens, const lq_weight* W0,
+                      const void* A_stack, const void* B_stack, int32_t n_adapters,
+                      int64_t r, float scale, const int32_t* seg_offsets,
+                      const int32_t* seg_adapter, int32_t n_seg, lq_dtype dt,
+                      void* Y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Host-side check of segment metadata (host pointers).  LQ_OK when offsets
+ * start at 0, never decrease, end at T_tokens and every id is in range;
+ * LQ_ERR_INVALID_ARG otherwise. */
+int lq_check_segments(const int32_t* h_offsets, const int32_t* h_adapter,
+                      int32_t n_seg, int64_t T_tokens, int32_t n_adapters);
+
+/* Workspace sizes (bytes) for the ops that need one. */
+#define LQ_OP_FWD 0
+#define LQ_OP_BWD 1
+#define LQ_OP_FWD_MULTI 2
+size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
+                         int32_t n_adapters);
+
+/* Trainable parameters LoRA adds to one N x K matrix: r (N + K)
+ * ([FT] "Choosing what to adapt: targets and rank"). */
+int64_t lq_lora_num_params(int64_t N, int64_t K, int64_t r);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* lq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LQ_H */

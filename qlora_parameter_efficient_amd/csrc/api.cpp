@@ -1,0 +1,244 @@
+// C ABI of liblq: argument validation, workspace carving and dispatch to the
+// HIP kernels.  Nothing here computes; every step of the layer runs in the
+// kernels of the .hip translation units.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+#include "dispatch.h"
+
+namespace lq {
+
+static thread_local char g_err[512];
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  if (e == hipSuccess) return LQ_OK;
+  set_error("%s: %s", where, hipGetErrorString(e));
+  return LQ_ERR_HIP;
+}
+
+}  // namespace lq
+
+using namespace lq;
+
+#define REQUIRE(cond, code, ...)   \
+  do {                             \
+    if (!(cond)) {                 \
+      set_error(__VA_ARGS__);      \
+      return (code);               \
+    }                              \
+  } while (0)
+
+namespace {
+
+constexpr int64_t kMaxRank = 64;
+constexpr int64_t kDecodeMaxM = 16;
+
+int check_weight(const lq_weight* w, lq_dtype dt) {
+  REQUIRE(w != nullptr, LQ_ERR_INVALID_ARG, "W0 descriptor is NULL");
+  REQUIRE(w->N > 0 && w->K > 0, LQ_ERR_INVALID_ARG, "W0 has N=%lld K=%lld", (long long)w->N,
+          (long long)w->K);
+  REQUIRE(w->reserved == 0, LQ_ERR_INVALID_ARG, "W0.reserved must be 0");
+  REQUIRE(w->dtype == dt, LQ_ERR_INVALID_ARG, "W0 dtype %d does not match call dtype %d",
+          (int)w->dtype, (int)dt);
+  if (w->kind == LQ_WEIGHT_DENSE) {
+    REQUIRE(w->dense != nullptr, LQ_ERR_INVALID_ARG, "dense W0 pointer is NULL");
+  } else if (w->kind == LQ_WEIGHT_NF4) {
+    REQUIRE(w->codes != nullptr, LQ_ERR_INVALID_ARG, "NF4 codes pointer is NULL");
+    if (w->double_quant) {
+      REQUIRE(w->q8 && w->c2, LQ_ERR_INVALID_ARG, "NF4 double-quant constants are NULL");
+    } else {
+      REQUIRE(w->absmax != nullptr, LQ_ERR_INVALID_ARG, "NF4 absmax pointer is NULL");
+    }
+  } else {
+    REQUIRE(false, LQ_ERR_INVALID_ARG, "unknown W0 kind %d", (int)w->kind);
+  }
+  return LQ_OK;
+}
+
+int check_bf16_shape(const lq_weight* w) {
+  REQUIRE(w->K % 64 == 0, LQ_ERR_UNSUPPORTED, "bf16 path needs K %% 64 == 0 (K=%lld)",
+          (long long)w->K);
+  REQUIRE(w->N % 32 == 0, LQ_ERR_UNSUPPORTED, "bf16 path needs N %% 32 == 0 (N=%lld)",
+          (long long)w->N);
+  return LQ_OK;
+}
+
+size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+  // U (M x r f32), T (M x r f32), dA / dB split partials
+  return (size_t)(2 * M * r) * 4 + dispatch::grad_partial_bytes(M, N, K, r);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lq_last_error(void) { return g_err; }
+
+int lq_nf4_codebook(float* out) {
+  REQUIRE(out != nullptr, LQ_ERR_INVALID_ARG, "out is NULL");
+  std::memcpy(out, nf4_table().cb, sizeof(float) * 16);
+  return LQ_OK;
+}
+
+int64_t lq_lora_num_params(int64_t N, int64_t K, int64_t r) { return r * (N + K); }
+
+int lq_check_segments(const int32_t* h_offsets, const int32_t* h_adapter, int32_t n_seg,
+                      int64_t T_tokens, int32_t n_adapters) {
+  REQUIRE(n_seg >= 0 && T_tokens >= 0 && n_adapters >= 1, LQ_ERR_INVALID_ARG,
+          "bad segment counts");
+  REQUIRE(h_offsets != nullptr, LQ_ERR_INVALID_ARG, "offsets NULL");
+  REQUIRE(n_seg == 0 || h_adapter != nullptr, LQ_ERR_INVALID_ARG, "adapter ids NULL");
+  REQUIRE(h_offsets[0] == 0, LQ_ERR_INVALID_ARG, "offsets[0] = %d, must be 0", h_offsets[0]);
+  for (int32_t i = 0; i < n_seg; ++i) {
+    REQUIRE(h_offsets[i + 1] >= h_offsets[i], LQ_ERR_INVALID_ARG,
+            "offsets decrease at segment %d", i);
+    REQUIRE(h_adapter[i] >= 0 && h_adapter[i] < n_adapters, LQ_ERR_INVALID_ARG,
+            "segment %d adapter id %d out of range", i, h_adapter[i]);
+  }
+  REQUIRE(h_offsets[n_seg] == T_tokens, LQ_ERR_INVALID_ARG, "offsets end at %d, not %lld",
+          h_offsets[n_seg], (long long)T_tokens);
+  return LQ_OK;
+}
+
+size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
+                         int32_t n_adapters) {
+  if (M < 0 || N < 0 || K < 0 || r < 0) return 0;
+  switch (op) {
+    case LQ_OP_FWD:
+      return (size_t)(M * r) * 4;
+    case LQ_OP_BWD:
+      return bwd_ws_bytes(M, N, K, r);
+    case LQ_OP_FWD_MULTI:
+      return dispatch::multi_ws_bytes(M, r, n_adapters);
+    default:
+      return 0;
+  }
+}
+
+int lq_nf4_quantize(const void* W, lq_dtype wdt, int64_t n, int32_t double_quant, uint8_t* codes,
+                    uint8_t* q8, float* c2, float* absmax, hipStream_t stream) {
+  REQUIRE(W != nullptr && codes != nullptr, LQ_ERR_INVALID_ARG, "W or codes is NULL");
+  REQUIRE(n >= 1, LQ_ERR_INVALID_ARG, "n = %lld", (long long)n);
+  REQUIRE(wdt == LQ_F32 || wdt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad dtype %d", (int)wdt);
+  if (double_quant) {
+    REQUIRE(q8 && c2, LQ_ERR_INVALID_ARG, "q8 or c2 is NULL");
+  } else {
+    REQUIRE(absmax != nullptr, LQ_ERR_INVALID_ARG, "absmax is NULL");
+  }
+  return launch_nf4_quantize(W, wdt, n, double_quant, codes, q8, c2, absmax, stream);
+}
+
+int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
+                      const float* absmax, int32_t double_quant, int64_t n, void* out,
+                      lq_dtype odt, hipStream_t stream) {
+  REQUIRE(codes != nullptr && out != nullptr, LQ_ERR_INVALID_ARG, "codes or out is NULL");
+  REQUIRE(n >= 1, LQ_ERR_INVALID_ARG, "n = %lld", (long long)n);
+  REQUIRE(odt == LQ_F32 || odt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad dtype %d", (int)odt);
+  if (double_quant) {
+    REQUIRE(q8 && c2, LQ_ERR_INVALID_ARG, "q8 or c2 is NULL");
+  } else {
+    REQUIRE(absmax != nullptr, LQ_ERR_INVALID_ARG, "absmax is NULL");
+  }
+  return launch_nf4_dequantize(codes, q8, c2, absmax, double_quant, n, out, odt, stream);
+}
+
+int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, const void* B,
+                int64_t r, float scale, lq_dtype dt, void* Y, float* T_out, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+  REQUIRE(dt == LQ_F32 || dt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
+  int rc = check_weight(W0, dt);
+  if (rc) return rc;
+  REQUIRE(M >= 0, LQ_ERR_INVALID_ARG, "M = %lld", (long long)M);
+  REQUIRE(r >= 1 && r <= kMaxRank, LQ_ERR_UNSUPPORTED, "rank %lld outside [1, %lld]",
+          (long long)r, (long long)kMaxRank);
+  if (dt == LQ_BF16 && (rc = check_bf16_shape(W0))) return rc;
+  if (M == 0) return LQ_OK;
+  REQUIRE(X && A && B && Y, LQ_ERR_INVALID_ARG, "X, A, B or Y is NULL");
+  float* T = T_out;
+  const bool path_keeps_t = dt == LQ_F32 || M <= kDecodeMaxM;  // T crosses two kernels
+  if (!T && path_keeps_t) {
+    const size_t need = (size_t)(M * r) * 4;
+    REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE,
+            "workspace %zu bytes, need %zu", ws_bytes, need);
+    T = (float*)ws;
+  }
+  if (dt == LQ_F32)
+    return f32_lora_fwd((const float*)X, M, *W0, (const float*)A, (const float*)B, r, scale,
+                        (float*)Y, T, stream);
+  if (M <= kDecodeMaxM)
+    return dispatch::decode_fwd(X, M, *W0, A, B, r, scale, Y, T, stream);
+  return dispatch::bf16_fwd(X, M, *W0, A, B, r, scale, Y, T_out, stream);
+}
+
+int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0, const void* A,
+                const void* B, int64_t r, float scale, lq_dtype dt, const float* T_saved,
+                void* dX, float* dA, float* dB, int32_t accumulate, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  REQUIRE(dt == LQ_F32 || dt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
+  int rc = check_weight(W0, dt);
+  if (rc) return rc;
+  REQUIRE(M >= 0, LQ_ERR_INVALID_ARG, "M = %lld", (long long)M);
+  REQUIRE(r >= 1 && r <= kMaxRank, LQ_ERR_UNSUPPORTED, "rank %lld outside [1, %lld]",
+          (long long)r, (long long)kMaxRank);
+  REQUIRE(A && B && dA && dB, LQ_ERR_INVALID_ARG, "A, B, dA or dB is NULL");
+  REQUIRE(M == 0 || (dY && X), LQ_ERR_INVALID_ARG, "dY or X is NULL");
+  if (dt == LQ_BF16 && (rc = check_bf16_shape(W0))) return rc;
+  const int64_t N = W0->N, K = W0->K;
+  const size_t need = bwd_ws_bytes(M, N, K, r);
+  REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu",
+          ws_bytes, need);
+  if (dt == LQ_F32)
+    return f32_lora_bwd((const float*)dY, (const float*)X, M, *W0, (const float*)A,
+                        (const float*)B, r, scale, T_saved, (float*)dX, dA, dB, accumulate,
+                        (float*)ws, stream);
+  return dispatch::bf16_bwd(dY, X, M, *W0, A, B, r, scale, T_saved, dX, dA, dB, accumulate, ws,
+                            stream);
+}
+
+int lq_lora_merge(const lq_weight* W0, const void* A, const void* B, int64_t r, float scale,
+                  lq_dtype dt, void* W_out, hipStream_t stream) {
+  REQUIRE(dt == LQ_F32 || dt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
+  int rc = check_weight(W0, dt);
+  if (rc) return rc;
+  REQUIRE(r >= 1 && r <= kMaxRank, LQ_ERR_UNSUPPORTED, "rank %lld outside [1, %lld]",
+          (long long)r, (long long)kMaxRank);
+  REQUIRE(A && B && W_out, LQ_ERR_INVALID_ARG, "A, B or W_out is NULL");
+  if (dt == LQ_F32)
+    return f32_lora_merge(*W0, (const float*)A, (const float*)B, r, scale, (float*)W_out, stream);
+  if ((rc = check_bf16_shape(W0))) return rc;
+  return dispatch::bf16_merge(*W0, A, B, r, scale, W_out, stream);
+}
+
+int lq_lora_fwd_multi(const void* X, int64_t T_tokens, const lq_weight* W0, const void* A_stack,
+                      const void* B_stack, int32_t n_adapters, int64_t r, float scale,
+                      const int32_t* seg_offsets, const int32_t* seg_adapter, int32_t n_seg,
+                      lq_dtype dt, void* Y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  REQUIRE(dt == LQ_BF16, LQ_ERR_UNSUPPORTED, "multi-adapter forward supports bf16 only");
+  int rc = check_weight(W0, dt);
+  if (rc) return rc;
+  if ((rc = check_bf16_shape(W0))) return rc;
+  REQUIRE(T_tokens >= 0 && n_seg >= 0, LQ_ERR_INVALID_ARG, "negative size");
+  REQUIRE(n_adapters >= 1, LQ_ERR_INVALID_ARG, "n_adapters = %d", n_adapters);
+  REQUIRE(r >= 1 && r * n_adapters <= kMaxRank, LQ_ERR_UNSUPPORTED,
+          "r * n_adapters = %lld exceeds %lld", (long long)(r * n_adapters), (long long)kMaxRank);
+  if (T_tokens == 0) return LQ_OK;
+  REQUIRE(n_seg >= 1, LQ_ERR_INVALID_ARG, "no segments for %lld tokens", (long long)T_tokens);
+  REQUIRE(X && A_stack && B_stack && Y && seg_offsets && seg_adapter, LQ_ERR_INVALID_ARG,
+          "a required pointer is NULL");
+  const size_t need = dispatch::multi_ws_bytes(T_tokens, r, n_adapters);
+  REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu",
+          ws_bytes, need);
+  return dispatch::bf16_fwd_multi(X, T_tokens, *W0, A_stack, B_stack, n_adapters, r, scale,
+                                  seg_offsets, seg_adapter, n_seg, Y, ws, stream);
+}
+
+}  // extern "C"

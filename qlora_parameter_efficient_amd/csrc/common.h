@@ -1,0 +1,58 @@
+// Internal definitions shared by the HIP translation units of liblq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lq.h"
+
+namespace lq {
+
+// NF4 levels and the 15 decision points between them, passed by value to the
+// kernels that need them (built once on the host, see codebook.cpp).
+struct NF4Table {
+  float cb[16];
+  float thr[15];
+  float pad;
+};
+
+const NF4Table& nf4_table();  // host: built on first use, immutable afterwards
+
+// Per-thread error reporting used by the ABI layer.
+void set_error(const char* fmt, ...);
+int hip_fail(hipError_t e, const char* where);
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Round-to-nearest-even float32 -> bfloat16 (finite inputs).  gfx950 has a
+// native packed conversion with the default rounding mode (nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Second-level step fl32(c2 / 127) with IEEE division (correctly rounded).
+__device__ __forceinline__ float dq_step(float c2) { return c2 / 127.0f; }
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace lq

@@ -1,0 +1,120 @@
+// Device helpers shared by the bf16 kernels: MFMA wrappers, NF4 dequantisation
+// through a byte-indexed LDS table, and small register transposes.
+//
+// MFMA operand layout used throughout (gfx950 v_mfma_f32_32x32x16_bf16):
+// lane l supplies row (l % 32) of the A operand and column (l % 32) of the B
+// operand, each as 8 consecutive reduction elements starting at 8 * (l / 32);
+// the 16 accumulator values of lane l are C[8*(v/4) + 4*(l/32) + v%4][l % 32].
+// Because both operands carry the reduction index the same way, any fixed
+// relabelling of the 16 reduction elements that is applied to both operands
+// leaves the product unchanged; the kernels use that to read each operand
+// in the order that is cheapest for it.
+#pragma once
+
+#include "common.h"
+
+namespace lq {
+
+constexpr int kPitch = 72;  // LDS row pitch in bf16 elements: 64 + 8 padding
+
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// NF4 weight descriptor as the kernels see it.
+struct WeightArgs {
+  const uint16_t* dense;
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* c2;
+  const float* absmax;
+  int64_t N, K;
+  int32_t dq;
+  int32_t pad;
+};
+
+inline WeightArgs weight_args(const lq_weight& w) {
+  WeightArgs a;
+  a.dense = (const uint16_t*)w.dense;
+  a.codes = w.codes;
+  a.q8 = w.q8;
+  a.c2 = w.c2;
+  a.absmax = w.absmax;
+  a.N = w.N;
+  a.K = w.K;
+  a.dq = w.double_quant;
+  a.pad = 0;
+  return a;
+}
+
+// Block scale a' = fl32(q8 * fl32(c2 / 127)) (or the float32 absmax), with the
+// second-level step cached while consecutive blocks stay in one group.
+struct ScaleCache {
+  int64_t g;
+  float step;
+  __device__ __forceinline__ void init() {
+    g = -1;
+    step = 0.0f;
+  }
+  __device__ __forceinline__ float scale(const WeightArgs& w, int64_t blk) {
+    if (!w.dq) return w.absmax[blk];
+    const int64_t gg = blk >> 8;
+    if (gg != g) {
+      g = gg;
+      step = dq_step(w.c2[gg]);
+    }
+    return (float)w.q8[blk] * step;
+  }
+};
+
+// lut[b] = (cb[b & 15], cb[b >> 4]): both levels of one code byte.  Built by a
+// 256-thread workgroup; the caller synchronises before use.
+__device__ __forceinline__ void build_lut(float2* lut, const NF4Table& tab) {
+  const int t = threadIdx.x;
+  if (t < 256) {
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((t & 15) == i) lo = tab.cb[i];
+      if ((t >> 4) == i) hi = tab.cb[i];
+    }
+    lut[t] = make_float2(lo, hi);
+  }
+}
+
+// Eight codes (one 32-bit word, element e in bits 4e..4e+3) -> eight bf16
+// values RNE(fl32(cb[code] * a)) packed in natural element order.
+__device__ __forceinline__ u32x4 deq8(uint32_t w, float a, const float2* lut) {
+  u32x4 o;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float2 v = lut[(w >> (8 * p)) & 0xFFu];
+    o[p] = pack_bf16x2(v.x * a, v.y * a);
+  }
+  return o;
+}
+
+// (lo half of x, lo half of y) and (hi half of x, hi half of y).
+__device__ __forceinline__ uint32_t pair_lo(uint32_t x, uint32_t y) {
+  return (x & 0xFFFFu) | (y << 16);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t x, uint32_t y) {
+  return (x >> 16) | (y & 0xFFFF0000u);
+}
+
+// Tile -> workgroup mapping.  Workgroups are dispatched round-robin over the
+// eight XCDs (block b runs on XCD b % 8); each XCD is given one contiguous
+// range of tile indices so that the tiles sharing its L2 are neighbours.
+__device__ __forceinline__ int xcd_tile(int bid, int total) {
+  const int xcd = bid & 7, local = bid >> 3;
+  const int per = total >> 3, rem = total & 7;
+  return (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+}  // namespace lq

@@ -1,0 +1,243 @@
+// NF4 quantisation with blockwise absmax and 8-bit double quantisation, and
+// the standalone dequantiser.
+//
+// "Low-Rank Adaptation (LoRA) and QLoRA: Mathematical Foundations ..."
+// (llms.blog), sections "1. 4-bit NormalFloat (NF4) Quantization" (absmax per
+// block, normalise, nearest level) and "2. Double Quantization (DQ)"
+// (c1_8bit = round(c1 / c2 * 127) over 256 first-level constants);
+// "Large Language Model Fine-tuning and LoRA" (aicomputerinstitute.com),
+// section "Quantizing the frozen weights" (block size 64, DQ block 256).
+//
+// Both kernels are HBM-bound streaming passes.  Bit-exactness rests on: exact
+// float32 max, correctly rounded float32 division (HIP's default), no fused
+// multiply-add anywhere in the arithmetic (only lone products and quotients),
+// rintf (ties to even) for the 8-bit constant, and RNE for bf16 stores.
+#include "common.h"
+
+namespace lq {
+namespace {
+
+constexpr int kGroupElems = LQ_NF4_BLOCK * LQ_NF4_DQ_BLOCK;  // 16384
+constexpr int kQuantThreads = 256;
+constexpr int kChunk = 8;            // elements per thread per step
+constexpr int kSteps = kGroupElems / (kQuantThreads * kChunk);  // 8
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* W, int64_t e0, int64_t n, float (&v)[8]);
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* W, int64_t e0, int64_t n,
+                                                float (&v)[8]) {
+  if (e0 + 8 <= n) {
+    u32x4 q = *reinterpret_cast<const u32x4*>(W + e0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = lo_bf16(q[i]);
+      v[2 * i + 1] = hi_bf16(q[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (e0 + i < n) ? bf16_to_f32(W[e0 + i]) : 0.0f;
+  }
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* W, int64_t e0, int64_t n, float (&v)[8]) {
+  if (e0 + 8 <= n) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(W + e0);
+    f32x4 b = *reinterpret_cast<const f32x4*>(W + e0 + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (e0 + i < n) ? W[e0 + i] : 0.0f;
+  }
+}
+
+// code = number of thresholds strictly below x
+__device__ __forceinline__ uint32_t nf4_code(float x, const NF4Table& t) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 15; ++i) c += (x > t.thr[i]) ? 1u : 0u;
+  return c;
+}
+
+// One workgroup per group of 256 blocks (16384 elements).  Step s, thread t
+// handles elements [g0 + (s*256 + t)*8, +8): eight consecutive threads cover
+// one 64-element block, whose absmax is reduced across those lanes.
+template <typename T>
+__global__ __launch_bounds__(kQuantThreads) void nf4_quantize_kernel(
+    const T* __restrict__ W, int64_t n, int32_t double_quant, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ q8, float* __restrict__ c2out, float* __restrict__ absmax,
+    NF4Table tab) {
+  __shared__ float c1s[LQ_NF4_DQ_BLOCK];
+  __shared__ float wmax[kQuantThreads / 64];
+  const int t = threadIdx.x;
+  const int64_t g0 = (int64_t)blockIdx.x * kGroupElems;
+  const int64_t nb_total = (n + LQ_NF4_BLOCK - 1) / LQ_NF4_BLOCK;
+
+#pragma unroll 1
+  for (int s = 0; s < kSteps; ++s) {
+    const int chunk = s * kQuantThreads + t;
+    const int64_t e0 = g0 + (int64_t)chunk * kChunk;
+    float v[8];
+    if (e0 < n) {
+      load8<T>(W, e0, n, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    // max over the 8 lanes of this block (lanes 8k .. 8k+7)
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    const float c1 = m;
+    if ((t & 7) == 0) c1s[chunk >> 3] = c1;
+    if (e0 < n) {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t code = 7u;
+        if (e0 + i >= n) code = 0u;  // padding nibble past the end stays 0
+        else if (c1 != 0.0f) code = nf4_code(v[i] / c1, tab);
+        packed |= code << (4 * i);
+      }
+      const int64_t byte0 = e0 >> 1;
+      if (e0 + 8 <= n) {
+        *reinterpret_cast<uint32_t*>(codes + byte0) = packed;
+      } else {
+        const int64_t nbytes = (n - e0 + 1) >> 1;
+        for (int64_t b = 0; b < nbytes; ++b) codes[byte0 + b] = (uint8_t)(packed >> (8 * b));
+      }
+    }
+  }
+  __syncthreads();
+
+  const int64_t blk = (int64_t)blockIdx.x * LQ_NF4_DQ_BLOCK + t;
+  const float c1 = c1s[t];
+  if (!double_quant) {
+    if (blk < nb_total) absmax[blk] = c1;
+    return;
+  }
+  // c2 = max c1 over the group (blocks past the end hold 0)
+  float m = c1;
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((t & 63) == 0) wmax[t >> 6] = m;
+  __syncthreads();
+  const float c2 = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  if (t == 0) c2out[blockIdx.x] = c2;
+  if (blk < nb_total) {
+    uint32_t q = 0;
+    if (c2 != 0.0f) {
+      const float ratio = c1 / c2;
+      const float scaled = ratio * 127.0f;
+      q = (uint32_t)__builtin_rintf(scaled);
+    }
+    q8[blk] = (uint8_t)q;
+  }
+}
+
+// Standalone dequantiser: each thread handles 32 elements (16 code bytes,
+// half of one block), so one scale a' per thread.
+constexpr int kDeqThreads = 256;
+
+template <bool BF16OUT>
+__global__ __launch_bounds__(kDeqThreads) void nf4_dequantize_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
+    const float* __restrict__ c2, const float* __restrict__ absmax, int32_t double_quant,
+    int64_t n, void* __restrict__ out, NF4Table tab) {
+  __shared__ float cbs[16];
+  if (threadIdx.x < 16) cbs[threadIdx.x] = tab.cb[threadIdx.x];
+  __syncthreads();
+  const int64_t e0 = ((int64_t)blockIdx.x * kDeqThreads + threadIdx.x) * 32;
+  if (e0 >= n) return;
+  const int64_t blk = e0 / LQ_NF4_BLOCK;
+  float a;
+  if (double_quant) {
+    const float step = dq_step(c2[blk / LQ_NF4_DQ_BLOCK]);
+    a = (float)q8[blk] * step;
+  } else {
+    a = absmax[blk];
+  }
+  if (e0 + 32 <= n) {
+    const u32x4 cw = *reinterpret_cast<const u32x4*>(codes + (e0 >> 1));
+    if (BF16OUT) {
+      u32x4 o[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t w = cw[d];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float lo = cbs[(w >> (8 * p)) & 15] * a;
+          const float hi = cbs[(w >> (8 * p + 4)) & 15] * a;
+          o[d][p] = pack_bf16x2(lo, hi);
+        }
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + e0);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) dst[d] = o[d];
+    } else {
+      f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + e0);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t w = cw[d];
+        f32x4 lo4, hi4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo4[i] = cbs[(w >> (4 * i)) & 15] * a;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hi4[i] = cbs[(w >> (16 + 4 * i)) & 15] * a;
+        dst[2 * d] = lo4;
+        dst[2 * d + 1] = hi4;
+      }
+    }
+  } else {
+    for (int64_t e = e0; e < n; ++e) {
+      const uint32_t byte = codes[e >> 1];
+      const uint32_t code = (e & 1) ? (byte >> 4) : (byte & 15);
+      const float w = cbs[code] * a;
+      if (BF16OUT) reinterpret_cast<uint16_t*>(out)[e] = f32_to_bf16(w);
+      else reinterpret_cast<float*>(out)[e] = w;
+    }
+  }
+}
+
+}  // namespace
+
+int launch_nf4_quantize(const void* W, lq_dtype wdt, int64_t n, int32_t double_quant,
+                        uint8_t* codes, uint8_t* q8, float* c2, float* absmax,
+                        hipStream_t stream) {
+  const int64_t groups = cdiv(n, kGroupElems);
+  const NF4Table& tab = nf4_table();
+  if (wdt == LQ_BF16) {
+    hipLaunchKernelGGL(nf4_quantize_kernel<uint16_t>, dim3((unsigned)groups), dim3(kQuantThreads),
+                       0, stream, (const uint16_t*)W, n, double_quant, codes, q8, c2, absmax, tab);
+  } else {
+    hipLaunchKernelGGL(nf4_quantize_kernel<float>, dim3((unsigned)groups), dim3(kQuantThreads), 0,
+                       stream, (const float*)W, n, double_quant, codes, q8, c2, absmax, tab);
+  }
+  return hip_fail(hipGetLastError(), "nf4_quantize launch");
+}
+
+int launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
+                          const float* absmax, int32_t double_quant, int64_t n, void* out,
+                          lq_dtype odt, hipStream_t stream) {
+  const int64_t threads = cdiv(n, 32);
+  const int64_t blocks = cdiv(threads, kDeqThreads);
+  const NF4Table& tab = nf4_table();
+  if (odt == LQ_BF16) {
+    hipLaunchKernelGGL(nf4_dequantize_kernel<true>, dim3((unsigned)blocks), dim3(kDeqThreads), 0,
+                       stream, codes, q8, c2, absmax, double_quant, n, out, tab);
+  } else {
+    hipLaunchKernelGGL(nf4_dequantize_kernel<false>, dim3((unsigned)blocks), dim3(kDeqThreads), 0,
+                       stream, codes, q8, c2, absmax, double_quant, n, out, tab);
+  }
+  return hip_fail(hipGetLastError(), "nf4_dequantize launch");
+}
+
+}  // namespace lq

@@ -1,0 +1,276 @@
+"""ctypes binding of liblq.so (include/lq.h): argument marshalling only.
+
+Each function here has the name of the C entry point it calls and does
+nothing but check tensor placement / dtype, allocate outputs with torch (device
+memory plumbing), pass raw pointers and the current HIP stream, and turn a
+negative status into an exception.  All arithmetic runs in the library's
+kernels; if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblq.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "lq.h")
+
+LQ_F32, LQ_BF16 = 0, 1
+LQ_WEIGHT_DENSE, LQ_WEIGHT_NF4 = 0, 1
+LQ_OP_FWD, LQ_OP_BWD, LQ_OP_FWD_MULTI = 0, 1, 2
+STATUS = {0: "LQ_OK", -1: "LQ_ERR_INVALID_ARG", -2: "LQ_ERR_UNSUPPORTED",
+          -3: "LQ_ERR_WORKSPACE", -4: "LQ_ERR_HIP"}
+
+
+class LqError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class LqWeightStruct(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("dense", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+        ("q8", ctypes.c_void_p), ("c2", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
+        ("double_quant", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_WP = ctypes.POINTER(LqWeightStruct)
+
+_SIGS = {
+    "lq_nf4_codebook": (ctypes.c_int, [_vp]),
+    "lq_nf4_quantize": (ctypes.c_int, [_vp, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "lq_nf4_dequantize": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i64, _vp, _i32, _vp]),
+    "lq_lora_fwd": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i64, _f32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "lq_lora_bwd": (ctypes.c_int, [_vp, _vp, _i64, _WP, _vp, _vp, _i64, _f32, _i32, _vp, _vp, _vp,
+                                   _vp, _i32, _vp, _sz, _vp]),
+    "lq_lora_merge": (ctypes.c_int, [_WP, _vp, _vp, _i64, _f32, _i32, _vp, _vp]),
+    "lq_lora_fwd_multi": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i32, _i64, _f32, _vp, _vp, _i32,
+                                         _i32, _vp, _vp, _sz, _vp]),
+    "lq_check_segments": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i32]),
+    "lq_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i64, _i32]),
+    "lq_lora_num_params": (_i64, [_i64, _i64, _i64]),
+    "lq_last_error": (ctypes.c_char_p, []),
+}
+
+
+def declared_symbols(header: str = HEADER):
+    """Function names declared in include/lq.h."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lq_[a-z0-9_]+)\s*\(", text)))
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run qlora_parameter_efficient_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise LqError(rc, lib().lq_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return LQ_F32
+    if t.dtype == torch.bfloat16:
+        return LQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _torch_dt(dt):
+    return torch.float32 if dt == LQ_F32 else torch.bfloat16
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+@dataclass
+class NF4Weight:
+    """Device buffers of an NF4 weight (N x K, flattened row-major)."""
+    codes: torch.Tensor
+    N: int
+    K: int
+    q8: torch.Tensor | None = None
+    c2: torch.Tensor | None = None
+    absmax: torch.Tensor | None = None
+    double_quant: bool = True
+
+
+def weight_struct(W0, dtype):
+    s = LqWeightStruct()
+    s.dtype = dtype
+    if isinstance(W0, NF4Weight):
+        _dev(W0.codes, W0.q8, W0.c2, W0.absmax)
+        s.kind = LQ_WEIGHT_NF4
+        s.N, s.K = W0.N, W0.K
+        s.codes = W0.codes.data_ptr()
+        s.q8 = W0.q8.data_ptr() if W0.q8 is not None else None
+        s.c2 = W0.c2.data_ptr() if W0.c2 is not None else None
+        s.absmax = W0.absmax.data_ptr() if W0.absmax is not None else None
+        s.double_quant = 1 if W0.double_quant else 0
+    else:
+        _dev(W0)
+        s.kind = LQ_WEIGHT_DENSE
+        s.N, s.K = W0.shape
+        s.dense = W0.data_ptr()
+        s.double_quant = 0
+    return s
+
+
+# ------------------------------------------------------------------ calls
+
+def lq_nf4_codebook():
+    buf = (ctypes.c_float * 16)()
+    _check(lib().lq_nf4_codebook(ctypes.cast(buf, ctypes.c_void_p)))
+    return list(buf)
+
+
+def lq_nf4_quantize(W: torch.Tensor, double_quant: bool = True) -> NF4Weight:
+    _dev(W)
+    n = W.numel()
+    nb = -(-n // 64)
+    dev = W.device
+    codes = torch.empty(-(-n // 2), dtype=torch.uint8, device=dev)
+    q8 = c2 = absmax = None
+    if double_quant:
+        q8 = torch.empty(nb, dtype=torch.uint8, device=dev)
+        c2 = torch.empty(-(-nb // 256), dtype=torch.float32, device=dev)
+    else:
+        absmax = torch.empty(nb, dtype=torch.float32, device=dev)
+    _check(lib().lq_nf4_quantize(_ptr(W), _dt(W), n, int(double_quant), _ptr(codes), _ptr(q8),
+                                 _ptr(c2), _ptr(absmax), _stream()))
+    N, K = (W.shape if W.dim() == 2 else (1, n))
+    return NF4Weight(codes, N, K, q8, c2, absmax, double_quant)
+
+
+def lq_nf4_dequantize(q: NF4Weight, dtype=torch.bfloat16, n: int | None = None) -> torch.Tensor:
+    n = q.N * q.K if n is None else n
+    out = torch.empty(n, dtype=dtype, device=q.codes.device)
+    _check(lib().lq_nf4_dequantize(_ptr(q.codes), _ptr(q.q8), _ptr(q.c2), _ptr(q.absmax),
+                                   int(q.double_quant), n, _ptr(out),
+                                   LQ_F32 if dtype == torch.float32 else LQ_BF16, _stream()))
+    return out
+
+
+def lq_workspace_size(op, M, N, K, r, n_adapters=0):
+    return int(lib().lq_workspace_size(op, M, N, K, r, n_adapters))
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def lq_lora_fwd(X, W0, A, B, scale, T_out=None, ws=None, Y=None):
+    _dev(X, A, B, T_out)
+    dt = _dt(X)
+    M = X.shape[0]
+    ws_struct = weight_struct(W0, dt)
+    if Y is None:
+        Y = torch.empty((M, ws_struct.N), dtype=X.dtype, device=X.device)
+    r = A.shape[0]
+    need = 0 if T_out is not None else lq_workspace_size(LQ_OP_FWD, M, ws_struct.N, ws_struct.K, r)
+    if ws is None and need:
+        ws = _ws(need, X.device)
+    _check(lib().lq_lora_fwd(_ptr(X), M, ctypes.byref(ws_struct), _ptr(A), _ptr(B), r, scale, dt,
+                             _ptr(Y), _ptr(T_out), _ptr(ws), 0 if ws is None else ws.numel(),
+                             _stream()))
+    return Y
+
+
+def lq_lora_bwd(dY, X, W0, A, B, scale, T_saved=None, need_dx=True, dA=None, dB=None,
+                accumulate=False, ws=None):
+    _dev(dY, X, A, B, T_saved, dA, dB)
+    dt = _dt(X)
+    M = X.shape[0]
+    w = weight_struct(W0, dt)
+    r = A.shape[0]
+    dev = X.device
+    dX = torch.empty((M, w.K), dtype=X.dtype, device=dev) if need_dx else None
+    if dA is None:
+        dA = torch.empty((r, w.K), dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty((w.N, r), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _ws(lq_workspace_size(LQ_OP_BWD, M, w.N, w.K, r), dev)
+    _check(lib().lq_lora_bwd(_ptr(dY), _ptr(X), M, ctypes.byref(w), _ptr(A), _ptr(B), r, scale, dt,
+                             _ptr(T_saved), _ptr(dX), _ptr(dA), _ptr(dB), int(accumulate),
+                             _ptr(ws), ws.numel(), _stream()))
+    return dX, dA, dB
+
+
+def lq_lora_merge(W0, A, B, scale, dtype=None):
+    _dev(A, B)
+    dt = _dt(A) if dtype is None else (LQ_F32 if dtype == torch.float32 else LQ_BF16)
+    w = weight_struct(W0, dt)
+    out = torch.empty((w.N, w.K), dtype=_torch_dt(dt), device=A.device)
+    _check(lib().lq_lora_merge(ctypes.byref(w), _ptr(A), _ptr(B), A.shape[0], scale, dt,
+                               _ptr(out), _stream()))
+    return out
+
+
+def lq_lora_fwd_multi(X, W0, A_stack, B_stack, scale, seg_offsets, seg_adapter, ws=None, Y=None):
+    _dev(X, A_stack, B_stack, seg_offsets, seg_adapter)
+    dt = _dt(X)
+    T = X.shape[0]
+    w = weight_struct(W0, dt)
+    n_ad, r = A_stack.shape[0], A_stack.shape[1]
+    n_seg = seg_adapter.numel()
+    if Y is None:
+        Y = torch.empty((T, w.N), dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = _ws(lq_workspace_size(LQ_OP_FWD_MULTI, T, w.N, w.K, r, n_ad), X.device)
+    _check(lib().lq_lora_fwd_multi(_ptr(X), T, ctypes.byref(w), _ptr(A_stack), _ptr(B_stack), n_ad,
+                                   r, scale, _ptr(seg_offsets), _ptr(seg_adapter), n_seg, dt,
+                                   _ptr(Y), _ptr(ws), ws.numel(), _stream()))
+    return Y
+
+
+def lq_check_segments(offsets, adapter, T_tokens, n_adapters):
+    import numpy as np
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    ad = np.ascontiguousarray(adapter, dtype=np.int32)
+    return int(lib().lq_check_segments(off.ctypes.data_as(ctypes.c_void_p),
+                                       ad.ctypes.data_as(ctypes.c_void_p), ad.size, T_tokens,
+                                       n_adapters))
+
+
+def lq_lora_num_params(N, K, r):
+    return int(lib().lq_lora_num_params(N, K, r))
+
+
+def lq_last_error():
+    return lib().lq_last_error().decode()

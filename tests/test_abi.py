@@ -1,0 +1,110 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/lq.h declares, its host-side entry points agree with the pages and the
+oracle, and argument errors are reported before anything would launch."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+from oracle import lora as olora
+from oracle import nf4 as onf4
+from qlora_parameter_efficient_amd import lq
+
+pytestmark = pytest.mark.skipif(not os.path.exists(lq.LIB_PATH),
+                                reason="liblq.so not built (run __graft_entry__.build())")
+
+
+def test_exports_every_declared_symbol():
+    declared = lq.declared_symbols()
+    assert len(declared) == 11
+    L = lq.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(declared) == set(lq._SIGS)
+
+
+def test_library_codebook_equals_oracle_bitwise():
+    ours = np.array(lq.lq_nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(ours.view(np.uint32), onf4.nf4_codebook().view(np.uint32))
+
+
+def test_num_params_matches_oracle():
+    for N, K, r in ((4096, 4096, 16), (4096, 4096, 8), (11008, 4096, 64), (4096, 11008, 16)):
+        assert lq.lq_lora_num_params(N, K, r) == olora.lora_num_params(N, K, r)
+    assert lq.lq_lora_num_params(4096, 4096, 16) == 131072
+
+
+def test_check_segments():
+    off = np.array([0, 3, 3, 10], np.int32)
+    ad = np.array([1, 0, 3], np.int32)
+    assert lq.lq_check_segments(off, ad, 10, 4) == 0
+    assert lq.lq_check_segments(off, ad, 11, 4) == -1               # wrong end
+    assert lq.lq_check_segments(off, np.array([1, 0, 4], np.int32), 10, 4) == -1   # id range
+    assert lq.lq_check_segments(np.array([0, 5, 3, 10], np.int32), ad, 10, 4) == -1  # decrease
+    assert lq.lq_check_segments(np.array([1, 3, 3, 10], np.int32), ad, 10, 4) == -1  # start
+    assert "adapter id" in lq.lq_last_error() or "offsets" in lq.lq_last_error()
+
+
+def test_workspace_sizes():
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 64, 256, 256, 8) == 64 * 8 * 4
+    assert lq.lq_workspace_size(lq.LQ_OP_BWD, 2048, 4096, 4096, 16) >= 2 * 2048 * 16 * 4
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD_MULTI, 1000, 4096, 4096, 16, 4) >= 1000 * 4
+
+
+def _weight(kind=0, N=256, K=256, dtype=lq.LQ_BF16, ptr=0x1000):
+    w = lq.LqWeightStruct()
+    w.kind, w.dtype, w.N, w.K = kind, dtype, N, K
+    if kind == 0:
+        w.dense = ptr
+    else:
+        w.codes, w.q8, w.c2 = ptr, ptr, ptr
+        w.double_quant = 1
+    return w
+
+
+def _fwd(w, X=0x1000, M=64, A=0x1000, B=0x1000, r=8, dt=lq.LQ_BF16, Y=0x1000, ws=None, wsb=0):
+    return lq.lib().lq_lora_fwd(X, M, ctypes.byref(w), A, B, r, 2.0, dt, Y, None, ws, wsb, None)
+
+
+def test_argument_errors_launch_nothing():
+    L = lq.lib()
+    # null weight pointers / descriptors
+    assert _fwd(_weight(ptr=0)) == -1
+    assert L.lq_lora_fwd(0x1000, 64, None, 0x1000, 0x1000, 8, 2.0, 1, 0x1000, None, None, 0, None) == -1
+    # rank outside [1, 64]
+    assert _fwd(_weight(), r=0) == -2 and _fwd(_weight(), r=65) == -2
+    # bf16 shape rules: K % 64, N % 32
+    assert _fwd(_weight(K=200)) == -2
+    assert _fwd(_weight(N=100)) == -2
+    # dtype mismatch between descriptor and call
+    assert _fwd(_weight(dtype=lq.LQ_F32)) == -1
+    # missing workspace when T_out is NULL (M > 0)
+    assert _fwd(_weight(), M=8) == -3               # decode path keeps T in ws
+    assert "workspace" in lq.lq_last_error()
+    # M = 0 is a no-op
+    assert _fwd(_weight(), M=0) == 0
+    # bad quantise arguments
+    assert L.lq_nf4_quantize(None, 1, 10, 1, 0x1000, 0x1000, 0x1000, None, None) == -1
+    assert L.lq_nf4_quantize(0x1000, 1, 0, 1, 0x1000, 0x1000, 0x1000, None, None) == -1
+    assert L.lq_nf4_quantize(0x1000, 1, 10, 1, 0x1000, None, 0x1000, None, None) == -1
+    assert L.lq_nf4_quantize(0x1000, 7, 10, 1, 0x1000, 0x1000, 0x1000, None, None) == -1
+    assert L.lq_nf4_dequantize(0x1000, None, None, None, 0, 10, 0x1000, 1, None) == -1
+    # backward workspace
+    w = _weight()
+    assert L.lq_lora_bwd(0x1000, 0x1000, 64, ctypes.byref(w), 0x1000, 0x1000, 8, 2.0, 1, None,
+                         0x1000, 0x1000, 0x1000, 0, None, 0, None) == -3
+    # multi-adapter: rank * adapters over 64, float32, no segments
+    assert L.lq_lora_fwd_multi(0x1000, 10, ctypes.byref(w), 0x1000, 0x1000, 5, 16, 2.0, 0x1000,
+                               0x1000, 1, 1, 0x1000, 0x1000, 1 << 20, None) == -2
+    wf = _weight(dtype=lq.LQ_F32)
+    assert L.lq_lora_fwd_multi(0x1000, 10, ctypes.byref(wf), 0x1000, 0x1000, 4, 16, 2.0, 0x1000,
+                               0x1000, 1, 0, 0x1000, 0x1000, 1 << 20, None) == -2
+    assert L.lq_lora_fwd_multi(0x1000, 10, ctypes.byref(w), 0x1000, 0x1000, 4, 16, 2.0, 0x1000,
+                               0x1000, 0, 1, 0x1000, 0x1000, 1 << 20, None) == -1
+    # merge
+    assert L.lq_lora_merge(ctypes.byref(w), None, 0x1000, 8, 2.0, 1, 0x1000, None) == -1
+    # reserved field must be zero
+    w2 = _weight()
+    w2.reserved = 1
+    assert _fwd(w2) == -1

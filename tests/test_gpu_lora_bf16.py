@@ -1,0 +1,142 @@
+"""bf16 path (MFMA kernels) against the float64 oracle, 2e-2 relative max error.
+
+Small cases span several tiles with ragged edges (M not a multiple of the
+128/256-row tiles, N with a partial 128-column tile and a partial 64-row
+reduction step, odd ranks); full workload sizes are checked on sampled rows
+for Y and dX (each row computed by the oracle on its own) and in full for dA,
+dB and the merged weight."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import lora as olora
+from oracle import nf4 as onf4
+from qlora_parameter_efficient_amd import lq
+from qlora_parameter_efficient_amd import workloads as wl
+
+from .gpu_helpers import BF16_TOL, announce, f64, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def base_for(c, kind):
+    """(device W0 argument, oracle float64 W0 the GEMM multiplies by)."""
+    W0v = c["W0"].value
+    if kind == "nf4":
+        Wd = lq.lq_nf4_quantize(to_dev(c["W0"]))
+        q = onf4.nf4_quantize(W0v)
+        Wo = onf4.bf16_bits_to_f64(onf4.nf4_dequantize_bf16(q)).reshape(W0v.shape)
+        return Wd, Wo
+    return to_dev(c["W0"]), W0v.astype(np.float64)
+
+
+def check_layer(c, kind, rows=None, bwd=True, merge=True, label=""):
+    s = c["alpha"] / c["r"]
+    X, A, B = to_dev(c["X"]), to_dev(c["A"]), to_dev(c["B"])
+    Wd, Wo = base_for(c, kind)
+    M, r = X.shape[0], A.shape[0]
+    Xo, Ao, Bo = c["X"].f64(), c["A"].f64(), c["B"].f64()
+    sel = np.arange(M) if rows is None else rows
+    announce(f"bf16 fwd {label} {kind} M={M} N={Wo.shape[0]} K={Wo.shape[1]} r={r}")
+    T = torch.empty((M, r), dtype=torch.float32, device=X.device)
+    Y = lq.lq_lora_fwd(X, Wd, A, B, s, T_out=T)
+    torch.cuda.synchronize()
+    Yo, _, To = olora.lora_forward(Xo[sel], Wo, Ao, Bo, s)
+    e = rel_err(f64(Y)[sel], Yo)
+    assert e <= BF16_TOL, f"Y rel err {e:.3e}"
+    e = rel_err(f64(T)[sel], To)
+    assert e <= BF16_TOL, f"T rel err {e:.3e}"
+    if bwd:
+        announce(f"bf16 bwd {label} {kind} M={M}")
+        dY = to_dev(c["dY"])
+        dX, dA, dB = lq.lq_lora_bwd(dY, X, Wd, A, B, s, T_saved=T if M > 16 else None)
+        torch.cuda.synchronize()
+        dYo = c["dY"].f64()
+        dXo = dYo[sel] @ Wo + s * ((dYo[sel] @ Bo) @ Ao)
+        e = rel_err(f64(dX)[sel], dXo)
+        assert e <= BF16_TOL, f"dX rel err {e:.3e}"
+        U = dYo @ Bo
+        dAo = s * (U.T @ Xo)
+        dBo = s * (dYo.T @ (Xo @ Ao.T))
+        for name, got, want in (("dA", dA, dAo), ("dB", dB, dBo)):
+            e = rel_err(f64(got), want)
+            assert e <= BF16_TOL, f"{name} rel err {e:.3e}"
+    if merge:
+        announce(f"bf16 merge {label} {kind}")
+        Wm = lq.lq_lora_merge(Wd, A, B, s, dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        e = rel_err(f64(Wm), olora.lora_merge(Wo, Ao, Bo, s))
+        assert e <= BF16_TOL, f"merge rel err {e:.3e}"
+
+
+SMALL = [
+    (300, 384, 512, 16),     # ragged M, three 128-column tiles
+    (2100, 256, 256, 16),    # 256-row tiles, ragged
+    (700, 256, 320, 64),     # rank 64 (two 32-row shrink blocks)
+    (130, 160, 192, 5),      # odd rank, partial column tile, partial reduction step
+    (17, 96, 128, 8),        # smallest non-decode M
+]
+
+
+@pytest.mark.parametrize("kind", ["dense", "nf4"])
+@pytest.mark.parametrize("shape", SMALL, ids=[f"{m}x{n}x{k}r{r}" for m, n, k, r in SMALL])
+def test_small(shape, kind):
+    M, N, K, r = shape
+    c = wl.small_case(M, N, K, r, seed=M + N + K + r)
+    check_layer(c, kind, label="small")
+
+
+@pytest.mark.parametrize("kind", ["dense", "nf4"])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_small(M, kind):
+    c = wl.small_case(M, 256, 512, 16, seed=100 + M)
+    check_layer(c, kind, label="decode", bwd=True, merge=False)
+    c = wl.small_case(M, 96, 192, 5, seed=200 + M)
+    check_layer(c, kind, label="decode-odd", bwd=False, merge=False)
+
+
+@pytest.mark.parametrize("kind", ["dense", "nf4"])
+@pytest.mark.parametrize("M", [3, 300])
+def test_zero_b_is_base_output(M, kind):
+    """B = 0: the adapter branch adds exact zeros -- same bits as with A = 0."""
+    announce(f"bf16 B=0 {kind} M={M}")
+    c = wl.small_case(M, 256, 256, 16, seed=5, zero_b=True)
+    X, A, B = to_dev(c["X"]), to_dev(c["A"]), to_dev(c["B"])
+    Wd, Wo = base_for(c, kind)
+    Y = lq.lq_lora_fwd(X, Wd, A, B, 2.0)
+    Y0 = lq.lq_lora_fwd(X, Wd, torch.zeros_like(A), B, 2.0)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Y0.view(torch.int16))
+    assert rel_err(f64(Y), c["X"].f64() @ Wo.T) <= BF16_TOL
+    dY = to_dev(c["dY"])
+    _, dA, dB = lq.lq_lora_bwd(dY, X, Wd, A, B, 2.0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dA).item() == 0
+
+
+def sample_rows(M, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = rng.choice(M, size=min(n, M), replace=False)
+    return np.unique(np.concatenate([rows, [0, M - 1]]))
+
+
+def test_config3_qlora_full():
+    """QLoRA linear 4096^2, NF4 + DQ base, r = 16, alpha = 32, M = 2048."""
+    c = wl.config3()
+    check_layer(c, "nf4", rows=sample_rows(2048), label="config3")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_config3_decode(M):
+    c = wl.config3(M=32)
+    c["X"] = wl.decode_inputs(M)
+    check_layer(c, "nf4", bwd=False, merge=False, label=f"config3-decode")
+
+
+@pytest.mark.parametrize("proj", ["q", "v"])
+def test_config2_lora_bf16(proj):
+    """LoRA on q_proj / v_proj shapes, dense bf16 base, r = 8, M = 4096."""
+    c2 = wl.config2(projections=(proj,))
+    p = c2["proj"][proj]
+    c = dict(W0=p["W0"], A=p["A"], B=p["B"], dY=p["dY"], X=c2["X"], r=8, alpha=16.0)
+    check_layer(c, "dense", rows=sample_rows(4096, seed=1), label=f"config2-{proj}", merge=False)
