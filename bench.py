@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA adapted linear layer on one MI355X.
+
+Default run (python bench.py [--steps K] [--warmup W]):
+
+* step = one forward + backward of the QLoRA linear at 4096 x 4096, NF4 base
+  with double quantisation, r = 16, alpha = 32, M = 2048 tokens, bf16 compute
+  (the fused forward kernel, then the fused dX kernel and the dA / dB
+  reductions).  value = algorithmic fwd+bwd FLOPs / wall time per step.
+* roofline: the fused forward kernel, timed alone with HIP events on the
+  stream it runs on, algorithmic FLOPs per launch / average duration, against
+  the bf16 dense MFMA peak; traffic from rocprofv3 counters when they were
+  taken on the current kernel source.
+* cpu_baseline: the CPU oracle (float64 NumPy) on the same step.
+* secondary lines in the same JSON object: NF4 decode (M = 1, 4, 16) GB/s on
+  the weight stream with cold weights, merge, quantise, multi-adapter.
+
+Profiling helpers (for rocprofv3): --mode fwd | step | decode | copy | quant
+run only that part, a few iterations, and print one line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QLoRA linear fwd+bwd TFLOP/s (4096²,r=16,M=2048); NF4 decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+M, N, K, R = 2048, 4096, 4096, 16
+FWD_FLOP = 2 * M * N * K + 2 * M * R * K + 2 * M * N * R          # fused forward kernel
+STEP_FLOP = 2 * (2 * M * N * K) + 6 * M * R * (N + K)             # fwd + bwd, algorithmic
+NF4_STREAM_BYTES = N * K // 2 + N * K // 64 + 4 * (N * K // 64 // 256)   # 8,654,848
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "qlora_parameter_efficient_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(KERNEL_SRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+FWD_SOURCES = ["lora_bf16.hip", "device_util.h", "common.h"]
+
+
+def traffic_for(kernel, sources):
+    """HBM bytes per launch from stored counter runs, if taken on this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("source_sha") != src_hash(sources):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cuda_time(fn, iters, torch):
+    """Average GPU time (ms) of fn() over iters back-to-back calls (HIP events)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def setup(torch):
+    import numpy as np
+
+    from qlora_parameter_efficient_amd import lq
+    from qlora_parameter_efficient_amd import workloads as wl
+
+    dev = "cuda:0"
+    c = wl.config3()
+
+    def to_dev(t):
+        return torch.from_numpy(t.bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+
+    S = dict(c=c, lq=lq, dev=dev, s=c["alpha"] / c["r"])
+    S["W0d"] = to_dev(c["W0"])
+    S["W"] = lq.lq_nf4_quantize(S["W0d"])
+    for k in ("X", "A", "B", "dY"):
+        S[k] = to_dev(c[k])
+    S["Y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    S["T"] = torch.empty((M, R), dtype=torch.float32, device=dev)
+    S["dX"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    S["dA"] = torch.empty((R, K), dtype=torch.float32, device=dev)
+    S["dB"] = torch.empty((N, R), dtype=torch.float32, device=dev)
+    S["ws"] = torch.empty(lq.lq_workspace_size(lq.LQ_OP_BWD, M, N, K, R), dtype=torch.uint8,
+                          device=dev)
+    torch.cuda.synchronize()
+    return S
+
+
+def fwd(S):
+    lq = S["lq"]
+    lq.lq_lora_fwd(S["X"], S["W"], S["A"], S["B"], S["s"], T_out=S["T"], Y=S["Y"])
+
+
+def bwd(S):
+    lq = S["lq"]
+    lq.lq_lora_bwd(S["dY"], S["X"], S["W"], S["A"], S["B"], S["s"], T_saved=S["T"], dA=S["dA"],
+                   dB=S["dB"], ws=S["ws"], dX=S["dX"])
+
+
+def step(S):
+    fwd(S)
+    bwd(S)
+
+
+def cpu_baseline(S):
+    """The oracle on the same fwd+bwd step, on the host cores."""
+    import numpy as np
+
+    from oracle import lora as olora
+    from oracle import nf4 as onf4
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    c = S["c"]
+    q = onf4.nf4_quantize(c["W0"].value)
+    Wo = onf4.bf16_bits_to_f64(onf4.nf4_dequantize_bf16(q)).reshape(N, K)
+    X, A, B, dY = c["X"].f64(), c["A"].f64(), c["B"].f64(), c["dY"].f64()
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        olora.lora_forward(X, Wo, A, B, S["s"])
+        olora.lora_backward(dY, X, Wo, A, B, S["s"])
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": round(STEP_FLOP / t / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "full step: float64 NumPy forward + backward of the 4096^2, r=16, M=2048 "
+                      f"layer on the NF4-dequantised weight, median of 3 ({t:.2f} s each)"}
+
+
+def decode_bench(S, torch, iters=200, copies=40):
+    """NF4 decode GEMV, cold weights: cycle over `copies` distinct NF4 copies
+    (copies x 8.65 MB > the 256 MB Infinity Cache)."""
+    import numpy as np
+
+    from qlora_parameter_efficient_amd import workloads as wl
+    lq = S["lq"]
+    W = S["W"]
+    Ws = [lq.NF4Weight(W.codes.clone(), N, K, W.q8.clone(), W.c2.clone()) for _ in range(copies)]
+    out = {}
+    for m in (1, 4, 16):
+        Xm = torch.from_numpy(wl.decode_inputs(m).bits.view(np.int16).copy()).view(
+            torch.bfloat16).to(S["dev"])
+        Ym = torch.empty((m, N), dtype=torch.bfloat16, device=S["dev"])
+        Tm = torch.empty((m, R), dtype=torch.float32, device=S["dev"])
+        it = iter(range(10 ** 9))
+
+        def call_cold():
+            w = Ws[next(it) % copies]
+            lq.lq_lora_fwd(Xm, w, S["A"], S["B"], S["s"], T_out=Tm, Y=Ym)
+
+        def call_warm():
+            lq.lq_lora_fwd(Xm, W, S["A"], S["B"], S["s"], T_out=Tm, Y=Ym)
+
+        for _ in range(20):
+            call_cold()
+        t_cold = cuda_time(call_cold, iters, torch)
+        t_warm = cuda_time(call_warm, iters, torch)
+        out[f"M{m}"] = {"us_per_call_cold": round(t_cold * 1e3, 2),
+                        "weight_stream_GBs_cold": round(NF4_STREAM_BYTES / (t_cold * 1e-3) / 1e9, 1),
+                        "us_per_call_warm": round(t_warm * 1e3, 2)}
+    del Ws
+    return out
+
+
+def secondary(S, torch):
+    import numpy as np
+    lq = S["lq"]
+    res = {}
+    res["decode_nf4"] = decode_bench(S, torch)
+    t = cuda_time(lambda: lq.lq_lora_merge(S["W"], S["A"], S["B"], S["s"],
+                                           dtype=torch.bfloat16), 20, torch)
+    mbytes = NF4_STREAM_BYTES + 2 * N * K + 2 * R * (N + K)
+    res["merge_nf4_to_bf16"] = {"us": round(t * 1e3, 2), "GBs": round(mbytes / (t * 1e-3) / 1e9, 1)}
+    t = cuda_time(lambda: lq.lq_nf4_quantize(S["W0d"]), 20, torch)
+    qbytes = 2 * N * K + NF4_STREAM_BYTES
+    res["nf4_quantize_bf16"] = {"us": round(t * 1e3, 2), "GBs": round(qbytes / (t * 1e-3) / 1e9, 1)}
+    t = cuda_time(lambda: lq.lq_nf4_dequantize(S["W"], dtype=torch.bfloat16), 20, torch)
+    res["nf4_dequantize_bf16"] = {"us": round(t * 1e3, 2),
+                                  "GBs": round(qbytes / (t * 1e-3) / 1e9, 1)}
+    # multi-adapter serving workload: 4 adapters r=16 over 256 requests, 4096^2 bf16 base
+    from qlora_parameter_efficient_amd import workloads as wl
+    c5 = wl.config5()
+    T5 = int(c5["offsets"][-1])
+
+    def td(t_):
+        return torch.from_numpy(t_.bits.view(np.int16).copy()).view(torch.bfloat16).to(S["dev"])
+
+    X5, W5, A5, B5 = td(c5["X"]), td(c5["W0"]), td(c5["A"]), td(c5["B"])
+    off = torch.from_numpy(c5["offsets"]).to(S["dev"])
+    ad = torch.from_numpy(c5["adapter"]).to(S["dev"])
+    Y5 = torch.empty((T5, N), dtype=torch.bfloat16, device=S["dev"])
+    ws5 = torch.empty(lq.lq_workspace_size(lq.LQ_OP_FWD_MULTI, T5, N, K, 16, 4), dtype=torch.uint8,
+                      device=S["dev"])
+    f = lambda: lq.lq_lora_fwd_multi(X5, W5, A5, B5, 2.0, off, ad, ws=ws5, Y=Y5)  # noqa: E731
+    f()
+    t = cuda_time(f, 5, torch)
+    flop = 2 * T5 * N * K + 2 * T5 * 16 * (N + K)
+    res["multi_adapter_config5"] = {"tokens": T5, "ms": round(t, 3),
+                                    "TFLOPs": round(flop / (t * 1e-3) / 1e12, 1)}
+    del X5, Y5, ws5
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--mode", default="full",
+                    choices=["full", "step", "fwd", "decode", "copy", "quant"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-secondary", action="store_true")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the layer shards by tokens with one all-reduce of dA/dB; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    if a.mode == "copy":
+        # plain copy of known size, for scaling the HBM byte counters
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(a.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                          "launches": a.steps}))
+        return 0
+
+    S = setup(torch)
+    if a.mode == "fwd":
+        for _ in range(a.steps):
+            fwd(S)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "fwd", "launches": a.steps}))
+        return 0
+    if a.mode == "step":
+        for _ in range(a.steps):
+            step(S)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "step", "steps": a.steps}))
+        return 0
+    if a.mode == "quant":
+        for _ in range(a.steps):
+            S["lq"].lq_nf4_quantize(S["W0d"])
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "quant", "launches": a.steps}))
+        return 0
+    if a.mode == "decode":
+        print(json.dumps({"mode": "decode", "decode_nf4": decode_bench(S, torch, iters=a.steps)}))
+        return 0
+
+    for _ in range(a.warmup):
+        step(S)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step(S)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / a.steps
+    value = STEP_FLOP / (wall / a.steps) / 1e12
+
+    # dominant kernel: the fused forward GEMM, alone, HIP events on its stream
+    t_fwd = cuda_time(lambda: fwd(S), 50, torch)
+    t_step_ev = cuda_time(lambda: step(S), 20, torch)
+    achieved = FWD_FLOP / (t_fwd * 1e-3) / 1e12
+    roof = {"kernel": "fwd_kernel (fused NF4 dequant + GEMM + shrink/expand)",
+            "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_for("fwd_kernel", FWD_SOURCES),
+            "flop_per_launch": FWD_FLOP, "us_per_launch": round(t_fwd * 1e3, 2)}
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": "QLoRA linear fwd+bwd: W0 4096x4096 NF4 (block 64, 8-bit double "
+                                  "quant block 256), r=16, alpha=32, X 2048x4096 bf16, dY 2048x4096",
+                      "M": M, "N": N, "K": K, "r": R, "step_flop": STEP_FLOP},
+           "gpu_event_ms_per_step": round(t_step_ev, 4),
+           "roofline": roof}
+    if not a.no_cpu:
+        log("timing the CPU oracle ...")
+        out["cpu_baseline"] = cpu_baseline(S)
+    if not a.no_secondary:
+        log("secondary measurements ...")
+        out["secondary"] = secondary(S, torch)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -152,7 +152,7 @@ int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
  *   kernels; otherwise ws may be NULL.
  *   dt = LQ_BF16: bf16 inputs, float32 accumulation, bf16 RNE output; W0 dense
  *   bf16 or NF4 (dequantised in registers / LDS, never written to memory).
- *   Requires K % 64 == 0, N % 32 == 0, 1 <= r <= 64.  M <= 16 takes the
+ *   Requires K % 64 == 0, N % 32 == 0, N, K <= 65536, 1 <= r <= 64.  M <= 16 takes the
  *   memory-bound decode path.
  *   dt = LQ_F32: float32 throughout (W0 dense f32 or NF4), 1 <= r <= 64.
  * M = 0 is a no-op returning LQ_OK.

@@ -69,6 +69,8 @@ int check_bf16_shape(const lq_weight* w) {
           (long long)w->K);
   REQUIRE(w->N % 32 == 0, LQ_ERR_UNSUPPORTED, "bf16 path needs N %% 32 == 0 (N=%lld)",
           (long long)w->N);
+  REQUIRE(w->K <= 65536 && w->N <= 65536, LQ_ERR_UNSUPPORTED,
+          "bf16 path supports N, K <= 65536 (N=%lld K=%lld)", (long long)w->N, (long long)w->K);
   return LQ_OK;
 }
 

@@ -116,8 +116,14 @@ struct GemvParams {
   NF4Table tab;
 };
 
+// Granule = 32 consecutive weights of one row (16 code bytes, half an NF4
+// block).  Lane (q, l16) of wave w takes granules 4 t + q for t = w, w + 4, ...
+// CH of them at a time: all their loads (codes, block constants, activations)
+// are issued before any is used, so each lane keeps CH 16-byte weight loads in
+// flight.
 template <int WK>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
+  constexpr int CH = WK == 0 ? 4 : 8;
   __shared__ float2 lut[256];
   __shared__ f32x4 part[4][64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -128,43 +134,55 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
     build_lut(lut, p.tab);
     __syncthreads();
   }
-  const int64_t n = n0 + l16;  // A-operand row of this lane (N % 32 == 0)
+  const int64_t n = n0 + l16;  // A-operand row of this lane (N % 16 == 0)
   const bool mrow = l16 < M;   // B-operand column (activation row) of this lane
   const int64_t xm = mrow ? l16 : 0;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   ScaleCache sc;
   sc.init();
-  // K is split into 32-element granules (half an NF4 block); a step covers four
-  // consecutive granules, one per quarter-wave q, and steps go round-robin to
-  // the four waves.  Lanes past the end feed zeros to the MFMA.
   const int64_t G = K / 32;
   const int64_t steps = (G + 3) / 4;
-  for (int64_t t = wave; t < steps; t += 4) {
-    const int64_t g = 4 * t + q;
-    const bool ok = g < G;
-    const int64_t k = ok ? 32 * g : 0;
-    u32x4 wf[4];
-    if (WK == 0) {
+  for (int64_t base = wave; base < steps; base += 4 * CH) {
+    u32x4 wraw[CH][WK == 0 ? 4 : 1];
+    ScaleRaw sr[CH];
+    u32x4 xf[CH][4];
+    bool ok[CH];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        wf[i] = ok ? *reinterpret_cast<const u32x4*>(p.W.dense + n * K + k + 8 * i)
-                   : u32x4{0, 0, 0, 0};
-    } else {
-      const int64_t e = n * K + k;
-      u32x4 cw = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-      float a = 0.0f;
-      if (ok) {
-        cw = *reinterpret_cast<const u32x4*>(p.W.codes + (e >> 1));
-        a = sc.scale(p.W, e >> 6);
+    for (int i = 0; i < CH; ++i) {
+      const int64_t t = base + 4 * i;
+      const int64_t g = 4 * t + q;
+      ok[i] = t < steps && g < G;
+      const int64_t k = ok[i] ? 32 * g : 0;
+      if (WK == 0) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          wraw[i][d] = ok[i] ? *reinterpret_cast<const u32x4*>(p.W.dense + n * K + k + 8 * d)
+                             : u32x4{0, 0, 0, 0};
+      } else {
+        const int64_t e = n * K + k;
+        if (ok[i]) {
+          wraw[i][0] = *reinterpret_cast<const u32x4*>(p.W.codes + (e >> 1));
+          sr[i] = load_scale(p.W, e >> 6);
+        } else {
+          wraw[i][0] = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
+          sr[i] = ScaleRaw{0u, 0.0f, -2};
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wf[i] = deq8(cw[i], a, lut);
+      for (int d = 0; d < 4; ++d)
+        xf[i][d] = (mrow && ok[i]) ? *reinterpret_cast<const u32x4*>(p.X + xm * K + k + 8 * d)
+                                   : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 xf = (mrow && ok) ? *reinterpret_cast<const u32x4*>(p.X + xm * K + k + 8 * i)
-                                    : u32x4{0, 0, 0, 0};
-      acc = mfma16(wf[i], xf, acc);
+    for (int i = 0; i < CH; ++i) {
+      if (WK == 0) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) acc = mfma16(wraw[i][d], xf[i][d], acc);
+      } else {
+        const float a = sr[i].g == -2 ? 0.0f : sc.finish(p.W, sr[i]);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) acc = mfma16(deq8(wraw[i][0][d], a, lut), xf[i][d], acc);
+      }
     }
   }
   // acc lane l: rows n0 + 4 q + i, column m = l16 (16x16 accumulator layout)
@@ -193,6 +211,68 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
       u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
 }
 
+// T = X A^T for M <= 16 rows in one workgroup of 16 waves.  Granules of 32
+// reduction elements go round-robin to the waves; each wave runs
+// v_mfma_f32_16x16x32_bf16 with A rows as the A operand (16 per tile, JT
+// tiles) and the activation rows as the B operand, all loads of a wave issued
+// up front; the 16 partial tiles are added through LDS.
+template <int JT>
+__global__ __launch_bounds__(1024) void tsmall_kernel(const uint16_t* __restrict__ X, int64_t M,
+                                                      int64_t K, const uint16_t* __restrict__ A,
+                                                      int r, float* __restrict__ T) {
+  constexpr int CH = 8;
+  __shared__ f32x4 part[16][JT][64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, q = lane >> 4;
+  const bool mrow = l16 < M;
+  const int64_t xm = mrow ? l16 : 0;
+  const int64_t G = K / 32;
+  f32x4 acc[JT];
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t base = wave; base < G; base += 16 * CH) {
+    u32x4 af[CH][JT], xf[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int64_t g = base + 16 * i;
+      const bool ok = g < G;
+      const int64_t k = ok ? 32 * g + 8 * q : 0;
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) {
+        const int j = 16 * jt + l16;
+        af[i][jt] = (ok && j < r) ? *reinterpret_cast<const u32x4*>(A + (int64_t)j * K + k)
+                                  : u32x4{0, 0, 0, 0};
+      }
+      xf[i] = (ok && mrow) ? *reinterpret_cast<const u32x4*>(X + xm * K + k) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) acc[jt] = mfma16(af[i][jt], xf[i], acc[jt]);
+  }
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt) part[wave][jt][lane] = acc[jt];
+  __syncthreads();
+  // thread -> (jt, lane) of the sum; lane holds rows j = 16 jt + 4 q + i, column m = l16
+  if (tid < JT * 64) {
+    const int jt = tid >> 6, ln = tid & 63;
+    f32x4 s4 = part[0][jt][ln];
+    for (int w = 1; w < 16; ++w) {
+      const f32x4 o = part[w][jt][ln];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s4[i] += o[i];
+    }
+    const int m = ln & 15, qq = ln >> 4;
+    if (m < M) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * jt + 4 * qq + i;
+        if (j < r) T[m * r + j] = s4[i];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 namespace dispatch {
@@ -209,7 +289,24 @@ int u_only(const void* dY, int64_t M, int64_t N, const void* B, int64_t r, float
 
 int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
                int64_t r, float s, void* Y, float* T, hipStream_t st) {
-  int e = t_only(X, M, W.K, A, r, T, st);
+  const int jt = (int)((r + 15) / 16);
+  const uint16_t* Xh = (const uint16_t*)X;
+  const uint16_t* Ah = (const uint16_t*)A;
+  switch (jt) {
+    case 1:
+      hipLaunchKernelGGL(tsmall_kernel<1>, dim3(1), dim3(1024), 0, st, Xh, M, W.K, Ah, (int)r, T);
+      break;
+    case 2:
+      hipLaunchKernelGGL(tsmall_kernel<2>, dim3(1), dim3(1024), 0, st, Xh, M, W.K, Ah, (int)r, T);
+      break;
+    case 3:
+      hipLaunchKernelGGL(tsmall_kernel<3>, dim3(1), dim3(1024), 0, st, Xh, M, W.K, Ah, (int)r, T);
+      break;
+    default:
+      hipLaunchKernelGGL(tsmall_kernel<4>, dim3(1), dim3(1024), 0, st, Xh, M, W.K, Ah, (int)r, T);
+      break;
+  }
+  int e = hip_fail(hipGetLastError(), "tsmall launch");
   if (e) return e;
   GemvParams p;
   p.X = (const uint16_t*)X;

@@ -53,6 +53,29 @@ inline WeightArgs weight_args(const lq_weight& w) {
   return a;
 }
 
+// Raw block constants as loaded: the 8-bit constant and its group's c2 (or
+// the float32 absmax bits).  Kept raw so that no arithmetic waits on the load
+// until the value is needed.
+struct ScaleRaw {
+  uint32_t q;
+  float c2;
+  int64_t g;
+};
+
+__device__ __forceinline__ ScaleRaw load_scale(const WeightArgs& w, int64_t blk) {
+  ScaleRaw s;
+  if (w.dq) {
+    s.q = w.q8[blk];
+    s.g = blk >> 8;
+    s.c2 = w.c2[s.g];
+  } else {
+    s.q = __float_as_uint(w.absmax[blk]);
+    s.g = -1;
+    s.c2 = 0.0f;
+  }
+  return s;
+}
+
 // Block scale a' = fl32(q8 * fl32(c2 / 127)) (or the float32 absmax), with the
 // second-level step cached while consecutive blocks stay in one group.
 struct ScaleCache {
@@ -62,16 +85,50 @@ struct ScaleCache {
     g = -1;
     step = 0.0f;
   }
-  __device__ __forceinline__ float scale(const WeightArgs& w, int64_t blk) {
-    if (!w.dq) return w.absmax[blk];
-    const int64_t gg = blk >> 8;
-    if (gg != g) {
-      g = gg;
-      step = dq_step(w.c2[gg]);
+  __device__ __forceinline__ float finish(const WeightArgs& w, const ScaleRaw& s) {
+    if (!w.dq) return __uint_as_float(s.q);
+    if (s.g != g) {
+      g = s.g;
+      step = dq_step(s.c2);
     }
-    return (float)w.q8[blk] * step;
+    return (float)s.q * step;
+  }
+  __device__ __forceinline__ float scale(const WeightArgs& w, int64_t blk) {
+    return finish(w, load_scale(w, blk));
   }
 };
+
+// Second-level steps fl32(c2[g] / 127) for groups g_lo .. g_lo + count - 1,
+// computed cooperatively into LDS so that a block scale is one LDS read and
+// one multiply: a' = fl32(q8 * tab[g - g_lo]).
+__device__ __forceinline__ void build_steps(float* tab, const WeightArgs& w, int64_t g_lo,
+                                            int count) {
+  for (int i = threadIdx.x; i < count; i += blockDim.x) tab[i] = dq_step(w.c2[g_lo + i]);
+}
+
+// The raw 8-bit constant of a block and its group relative to a table base
+// (or the float32 absmax bits when there is no second level).
+struct ScaleRef {
+  uint32_t q;
+  int32_t gi;
+};
+
+__device__ __forceinline__ ScaleRef load_scale_ref(const WeightArgs& w, int64_t blk, int64_t g_lo) {
+  ScaleRef s;
+  if (w.dq) {
+    s.q = w.q8[blk];
+    s.gi = (int32_t)((blk >> 8) - g_lo);
+  } else {
+    s.q = __float_as_uint(w.absmax[blk]);
+    s.gi = 0;
+  }
+  return s;
+}
+
+__device__ __forceinline__ float scale_from(const WeightArgs& w, const ScaleRef& s,
+                                            const float* tab) {
+  return w.dq ? (float)s.q * tab[s.gi] : __uint_as_float(s.q);
+}
 
 // lut[b] = (cb[b & 15], cb[b >> 4]): both levels of one code byte.  Built by a
 // 256-thread workgroup; the caller synchronises before use.

@@ -77,27 +77,40 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(GradParams p) {
       *reinterpret_cast<u32x2*>(dst + (8 * cc + 2 * d + 1) * kPitch + 4 * mg) = od;
     }
   };
-  auto stage_v = [&](int64_t m0r, uint16_t* dst) {
-    for (int e = tid; e < 64 * RP; e += kThreads) {
-      const int m = e / RP, j = e - m * RP;
-      float v = 0.0f;
-      if (j < r && m0r + m < mend) v = p.V[(m0r + m) * r + j];
-      dst[j * kPitch + m] = f32_to_bf16(v);
+  // V^T tile: thread owns row m = tid % 64, columns j = tid / 64 + 4 i; the
+  // values are loaded with the Z prefetch and stored after the MFMAs.
+  const int vm = tid & 63, vj0 = tid >> 6;
+  auto load_v = [&](int64_t m0r, float (&vv)[RP / 4]) {
+    const bool ok = m0r + vm < mend;
+    const float* row = p.V + (m0r + vm) * r;
+#pragma unroll
+    for (int i = 0; i < RP / 4; ++i) {
+      const int j = vj0 + 4 * i;
+      vv[i] = (ok && j < r) ? row[j] : 0.0f;
     }
+  };
+  auto store_v = [&](const float (&vv)[RP / 4], uint16_t* dst) {
+#pragma unroll
+    for (int i = 0; i < RP / 4; ++i) dst[(vj0 + 4 * i) * kPitch + vm] = f32_to_bf16(vv[i]);
   };
 
   uint32_t raw[16];
+  float vv[RP / 4];
   if (steps > 0) {
     load(mbeg, raw);
+    load_v(mbeg, vv);
     store(raw, zt[0]);
-    stage_v(mbeg, vt[0]);
+    store_v(vv, vt[0]);
   }
   __syncthreads();
   for (int st = 0; st < steps; ++st) {
     const int buf = st & 1;
     const bool more = st + 1 < steps;
     const int64_t m1 = mbeg + (int64_t)(st + 1) * 64;
-    if (more) load(m1, raw);
+    if (more) {
+      load(m1, raw);
+      load_v(m1, vv);
+    }
     const uint16_t* z = zt[buf];
     const uint16_t* v = vt[buf];
 #pragma unroll
@@ -113,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(GradParams p) {
     }
     if (more) {
       store(raw, zt[buf ^ 1]);
-      stage_v(m1, vt[buf ^ 1]);
+      store_v(vv, vt[buf ^ 1]);
     }
     __syncthreads();
   }

@@ -212,14 +212,15 @@ def lq_lora_fwd(X, W0, A, B, scale, T_out=None, ws=None, Y=None):
 
 
 def lq_lora_bwd(dY, X, W0, A, B, scale, T_saved=None, need_dx=True, dA=None, dB=None,
-                accumulate=False, ws=None):
-    _dev(dY, X, A, B, T_saved, dA, dB)
+                accumulate=False, ws=None, dX=None):
+    _dev(dY, X, A, B, T_saved, dA, dB, dX)
     dt = _dt(X)
     M = X.shape[0]
     w = weight_struct(W0, dt)
     r = A.shape[0]
     dev = X.device
-    dX = torch.empty((M, w.K), dtype=X.dtype, device=dev) if need_dx else None
+    if dX is None and need_dx:
+        dX = torch.empty((M, w.K), dtype=X.dtype, device=dev)
     if dA is None:
         dA = torch.empty((r, w.K), dtype=torch.float32, device=dev)
     if dB is None:
