@@ -152,7 +152,8 @@ int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
  *   kernels; otherwise ws may be NULL.
  *   dt = LQ_BF16: bf16 inputs, float32 accumulation, bf16 RNE output; W0 dense
  *   bf16 or NF4 (dequantised in registers / LDS, never written to memory).
- *   Requires K % 64 == 0, N % 32 == 0, N, K <= 65536, 1 <= r <= 64.  M <= 16 takes the
+ *   Requires K % 64 == 0, N % 64 == 0, N, K <= 65536, M*K and M*N < 2^31,
+ *   1 <= r <= 64.  M <= 16 takes the
  *   memory-bound decode path.
  *   dt = LQ_F32: float32 throughout (W0 dense f32 or NF4), 1 <= r <= 64.
  * M = 0 is a no-op returning LQ_OK.
@@ -203,7 +204,7 @@ int lq_lora_merge(const lq_weight* W0, const void* A, const void* B, int64_t r,
  *   [0, n_adapters); lq_check_segments verifies host copies).
  *   ws: at least lq_workspace_size(LQ_OP_FWD_MULTI, T_tokens, N, K, r,
  *   n_adapters) bytes.
- *   Requires dt = LQ_BF16, K % 64 == 0, N % 32 == 0, r * n_adapters <= 64.
+ *   Requires dt = LQ_BF16, K % 64 == 0, N % 64 == 0, r * n_adapters <= 64.
  */
 int lq_lora_fwd_multi(const void* X, int64_t T_tokens, const lq_weight* W0,
                       const void* A_stack, const void* B_stack, int32_t n_adapters,

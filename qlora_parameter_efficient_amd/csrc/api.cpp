@@ -67,10 +67,18 @@ int check_weight(const lq_weight* w, lq_dtype dt) {
 int check_bf16_shape(const lq_weight* w) {
   REQUIRE(w->K % 64 == 0, LQ_ERR_UNSUPPORTED, "bf16 path needs K %% 64 == 0 (K=%lld)",
           (long long)w->K);
-  REQUIRE(w->N % 32 == 0, LQ_ERR_UNSUPPORTED, "bf16 path needs N %% 32 == 0 (N=%lld)",
+  REQUIRE(w->N % 64 == 0, LQ_ERR_UNSUPPORTED, "bf16 path needs N %% 64 == 0 (N=%lld)",
           (long long)w->N);
   REQUIRE(w->K <= 65536 && w->N <= 65536, LQ_ERR_UNSUPPORTED,
           "bf16 path supports N, K <= 65536 (N=%lld K=%lld)", (long long)w->N, (long long)w->K);
+  return LQ_OK;
+}
+
+// The bf16 kernels address activations with 32-bit byte offsets.
+int check_bf16_rows(int64_t M, const lq_weight* w) {
+  const int64_t lim = (int64_t)1 << 31;
+  REQUIRE(M * w->K < lim && M * w->N < lim, LQ_ERR_UNSUPPORTED,
+          "bf16 path needs M*K and M*N below 2^31 elements (M=%lld)", (long long)M);
   return LQ_OK;
 }
 
@@ -163,6 +171,7 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
   REQUIRE(r >= 1 && r <= kMaxRank, LQ_ERR_UNSUPPORTED, "rank %lld outside [1, %lld]",
           (long long)r, (long long)kMaxRank);
   if (dt == LQ_BF16 && (rc = check_bf16_shape(W0))) return rc;
+  if (dt == LQ_BF16 && (rc = check_bf16_rows(M, W0))) return rc;
   if (M == 0) return LQ_OK;
   REQUIRE(X && A && B && Y, LQ_ERR_INVALID_ARG, "X, A, B or Y is NULL");
   float* T = T_out;
@@ -194,6 +203,7 @@ int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0, c
   REQUIRE(A && B && dA && dB, LQ_ERR_INVALID_ARG, "A, B, dA or dB is NULL");
   REQUIRE(M == 0 || (dY && X), LQ_ERR_INVALID_ARG, "dY or X is NULL");
   if (dt == LQ_BF16 && (rc = check_bf16_shape(W0))) return rc;
+  if (dt == LQ_BF16 && (rc = check_bf16_rows(M, W0))) return rc;
   const int64_t N = W0->N, K = W0->K;
   const size_t need = bwd_ws_bytes(M, N, K, r);
   REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu",
@@ -232,6 +242,7 @@ int lq_lora_fwd_multi(const void* X, int64_t T_tokens, const lq_weight* W0, cons
   REQUIRE(n_adapters >= 1, LQ_ERR_INVALID_ARG, "n_adapters = %d", n_adapters);
   REQUIRE(r >= 1 && r * n_adapters <= kMaxRank, LQ_ERR_UNSUPPORTED,
           "r * n_adapters = %lld exceeds %lld", (long long)(r * n_adapters), (long long)kMaxRank);
+  if ((rc = check_bf16_rows(T_tokens, W0))) return rc;
   if (T_tokens == 0) return LQ_OK;
   REQUIRE(n_seg >= 1, LQ_ERR_INVALID_ARG, "no segments for %lld tokens", (long long)T_tokens);
   REQUIRE(X && A_stack && B_stack && Y && seg_offsets && seg_adapter, LQ_ERR_INVALID_ARG,

@@ -45,8 +45,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTileI = 128;   // weight-side outputs per workgroup
-constexpr int kBK = 128;      // reduction elements per step
-constexpr int kLP = kBK + 8;  // LDS row pitch (bf16): 272 bytes, conflict-free 16-byte reads
+constexpr int kBK = 64;       // reduction elements per step
+constexpr int kLP = kBK + 8;  // LDS row pitch (bf16): 144 bytes, conflict-free 16-byte reads
 
 __device__ __forceinline__ u32x4 sel4(bool ok, const u32x4& v) {
   return ok ? v : u32x4{0u, 0u, 0u, 0u};
@@ -71,75 +71,107 @@ __device__ __forceinline__ u32x4 t_operand(const f32x16& t, int cc, float s) {
   return o;
 }
 
-// 8 x 8 bf16 patch, rows[i][d] = elements (2d, 2d+1) of row i, stored
-// transposed: output row c holds element c of rows 0..7 (16 bytes).
-__device__ __forceinline__ void store_transposed8(const uint32_t (&rows)[8][4], uint16_t* dst,
-                                                  int pitch) {
+// R x 8 bf16 patch, rows[i][d] = elements (2d, 2d+1) of row i (R = 4 or 8),
+// stored transposed: output row c (c = 0..7) holds element c of rows 0..R-1.
+template <int R>
+__device__ __forceinline__ void store_transposed(const uint32_t (&rows)[R][4], uint16_t* dst,
+                                                 int pitch) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const u32x4 ev{pair_lo(rows[0][d], rows[1][d]), pair_lo(rows[2][d], rows[3][d]),
-                   pair_lo(rows[4][d], rows[5][d]), pair_lo(rows[6][d], rows[7][d])};
-    const u32x4 od{pair_hi(rows[0][d], rows[1][d]), pair_hi(rows[2][d], rows[3][d]),
-                   pair_hi(rows[4][d], rows[5][d]), pair_hi(rows[6][d], rows[7][d])};
-    *reinterpret_cast<u32x4*>(dst + (2 * d) * pitch) = ev;
-    *reinterpret_cast<u32x4*>(dst + (2 * d + 1) * pitch) = od;
-  }
-}
-
-// Activation fragments of one step for a wave: for each m-subtile, lane
-// (h, l32) holds row l32, reduction elements kb + 64 h + 8 sg .. +7 for
-// substeps sg = 0..7 (one contiguous 128-byte run per lane).
-template <int MS>
-struct ActRegs {
-  u32x4 f[MS][8];
-};
-
-template <int MS>
-__device__ __forceinline__ void load_act(ActRegs<MS>& a, const uint16_t* const (&rowp)[MS],
-                                         int64_t kb, int64_t kmax, int h) {
-  const int64_t k = kb + 64 * h;
+    uint32_t ev[R / 2], od[R / 2];
 #pragma unroll
-  for (int ms = 0; ms < MS; ++ms) {
-#pragma unroll
-    for (int sg = 0; sg < 8; ++sg) {
-      const bool ok = k + 8 * sg < kmax;
-      const int64_t kk = ok ? k + 8 * sg : 0;
-      a.f[ms][sg] = sel4(ok, *reinterpret_cast<const u32x4*>(rowp[ms] + kk));
+    for (int e = 0; e < R / 2; ++e) {
+      ev[e] = pair_lo(rows[2 * e][d], rows[2 * e + 1][d]);
+      od[e] = pair_hi(rows[2 * e][d], rows[2 * e + 1][d]);
+    }
+    if (R == 8) {
+      *reinterpret_cast<u32x4*>(dst + (2 * d) * pitch) = u32x4{ev[0], ev[1], ev[2], ev[3]};
+      *reinterpret_cast<u32x4*>(dst + (2 * d + 1) * pitch) = u32x4{od[0], od[1], od[2], od[3]};
+    } else {
+      *reinterpret_cast<u32x2*>(dst + (2 * d) * pitch) = u32x2{ev[0], ev[1]};
+      *reinterpret_cast<u32x2*>(dst + (2 * d + 1) * pitch) = u32x2{od[0], od[1]};
     }
   }
 }
 
-// One MFMA step over the tile in LDS: 4 weight-side subtiles (rows 32 ns + l32)
-// plus JT shrink subtiles (tile rows 128 + 32 jt + l32), against the MS
-// activation subtiles.  LDS fragment reads run one substep ahead; after the
-// MFMAs of substep sg, part(sg) stores one eighth of the next tile.
+// Activation tile of one step, 128 MS rows x 64: thread t loads chunks
+// c = t + 256 i (row c / 8, 16-byte chunk c % 8), so eight consecutive lanes
+// read one row's 128 contiguous bytes.  Offsets are per-thread constants
+// (rows past the end clamped: their outputs are never stored); the step only
+// moves the uniform base pointer.
+template <int MS>
+struct ActStage {
+  u32x4 v[4 * MS];
+};
+
+template <int MS>
+__device__ __forceinline__ void act_offsets(uint32_t (&off)[4 * MS], int64_t ld, int64_t m0,
+                                            int64_t rows) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4 * MS; ++i) {
+    int64_t m = m0 + (tid >> 3) + 32 * i;
+    m = m < rows ? m : rows - 1;
+    off[i] = (uint32_t)((m * ld + 8 * (tid & 7)) * 2);
+  }
+}
+
+template <int MS>
+__device__ __forceinline__ void act_load(ActStage<MS>& st, const char* base,
+                                         const uint32_t (&off)[4 * MS]) {
+#pragma unroll
+  for (int i = 0; i < 4 * MS; ++i) st.v[i] = *reinterpret_cast<const u32x4*>(base + off[i]);
+}
+
+// part (0..3) of storing an activation stage: chunks i = MS part .. +MS
+template <int MS>
+__device__ __forceinline__ void act_part(const ActStage<MS>& st, uint16_t* tile, int part) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < MS; ++j) {
+    const int i = MS * part + j;
+    *reinterpret_cast<u32x4*>(tile + ((tid >> 3) + 32 * i) * kLP + 8 * (tid & 7)) = st.v[i];
+  }
+}
+
+// One MFMA step over the tiles in LDS: weight tile rows 32 ns + l32 (4 output
+// subtiles, then JT shrink subtiles at rows 128 + 32 jt + l32) against the
+// activation tile rows of this wave (32 MS wave + 32 ms + l32).  Reduction
+// elements of substep s for lane half h: 32 h + 8 s .. +7.  LDS fragment reads
+// run one substep ahead; after the MFMAs of substep s, part(s) stores one
+// quarter of the next step's tiles.
 template <int MS, int JT, typename Part>
-__device__ __forceinline__ void mfma_step(const uint16_t* tile, int l32, int h,
-                                          const ActRegs<MS>& cur, f32x16 (&acc)[4][MS],
+__device__ __forceinline__ void mfma_step(const uint16_t* wtile, const uint16_t* atile, int wave,
+                                          int l32, int h, f32x16 (&acc)[4][MS],
                                           f32x16 (&tacc)[JT > 0 ? JT : 1][MS], Part&& part) {
   constexpr int NR = 4 + JT;
-  const uint16_t* wbase = tile + l32 * kLP + 64 * h;
-  u32x4 wf[2][NR];
+  const uint16_t* wbase = wtile + l32 * kLP + 32 * h;
+  const uint16_t* abase = atile + (32 * MS * wave + l32) * kLP + 32 * h;
+  u32x4 wf[2][NR], af[2][MS];
 #pragma unroll
   for (int ns = 0; ns < NR; ++ns) wf[0][ns] = *reinterpret_cast<const u32x4*>(wbase + 32 * ns * kLP);
 #pragma unroll
-  for (int sg = 0; sg < 8; ++sg) {
-    const int c = sg & 1;
-    if (sg < 7) {
+  for (int ms = 0; ms < MS; ++ms) af[0][ms] = *reinterpret_cast<const u32x4*>(abase + 32 * ms * kLP);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c = s & 1;
+    if (s < 3) {
 #pragma unroll
       for (int ns = 0; ns < NR; ++ns)
-        wf[c ^ 1][ns] = *reinterpret_cast<const u32x4*>(wbase + 32 * ns * kLP + 8 * (sg + 1));
+        wf[c ^ 1][ns] = *reinterpret_cast<const u32x4*>(wbase + 32 * ns * kLP + 8 * (s + 1));
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms)
+        af[c ^ 1][ms] = *reinterpret_cast<const u32x4*>(abase + 32 * ms * kLP + 8 * (s + 1));
     }
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
-      for (int ms = 0; ms < MS; ++ms) acc[ns][ms] = mfma32(wf[c][ns], cur.f[ms][sg], acc[ns][ms]);
+      for (int ms = 0; ms < MS; ++ms) acc[ns][ms] = mfma32(wf[c][ns], af[c][ms], acc[ns][ms]);
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-      for (int ms = 0; ms < MS; ++ms)
-        tacc[jt][ms] = mfma32(wf[c][4 + jt], cur.f[ms][sg], tacc[jt][ms]);
-    part(sg);
+      for (int ms = 0; ms < MS; ++ms) tacc[jt][ms] = mfma32(wf[c][4 + jt], af[c][ms], tacc[jt][ms]);
+    part(s);
   }
 }
 
@@ -176,144 +208,187 @@ struct FwdParams {
 
 constexpr int kFwdTab = 1024;  // second-level steps of one tile's 128 rows (K <= 65536)
 
-// Staging for one forward step: weight rows n0 .. n0+127, columns kb .. kb+127.
-// NF4: thread t takes row t/2, one whole 64-element block (32 code bytes).
-// Dense: thread t takes eight 16-byte chunks.  The JT = RP/32 shrink operand
-// tiles (A rows, RP x 128) ride along as tile rows 128 ...  Stages are loaded
-// two steps ahead and written to LDS one eighth per MFMA substep.
+// Weight formats, fixed at compile time: dense bf16, NF4 with 8-bit double
+// quantised constants, NF4 with float32 absmax.
+constexpr int kDense = 0, kNF4DQ = 1, kNF4 = 2;
+
+// Block constant as loaded (8-bit value, or float32 absmax bits) and its
+// second-level group relative to the step table; turned into the scale a'
+// only when the tile is written, a step after the load was issued.
+struct RawScale {
+  uint32_t q;
+  int32_t gi;
+};
+
+template <int WK>
+__device__ __forceinline__ RawScale load_raw_scale(const uint8_t* q8, const float* absmax,
+                                                   uint32_t qoff, int32_t gi) {
+  RawScale r;
+  r.gi = gi;
+  r.q = WK == kNF4DQ ? (uint32_t)q8[qoff] : __float_as_uint(absmax[qoff]);
+  return r;
+}
+
+template <int WK>
+__device__ __forceinline__ float raw_scale_value(const RawScale& r, const float* tab) {
+  if (WK == kNF4DQ) return (float)r.q * tab[r.gi];
+  return __uint_as_float(r.q);
+}
+
+// Weight staging for one forward step: rows n0 .. n0+127, columns kb .. kb+63.
+// NF4: thread t takes row t/2, half a block (16 code bytes).  Dense: thread t
+// takes four 16-byte chunks (row t/8 + 32 i).  The JT = RP/32 shrink operand
+// tiles (A rows, RP x 64; thread t takes row t/8 + 32 i) ride along as tile
+// rows 128 ...  Stages are loaded two steps ahead and written to LDS a
+// quarter per MFMA substep.  Per-thread offsets are fixed; rows past the end
+// are clamped (they only feed outputs that are never stored).
 template <int WK, int JT>
 struct FwdStage {
-  u32x4 w[WK == 0 ? 8 : 2];
-  ScaleRef sr;
-  bool wok;
-  u32x4 a[JT > 0 ? 2 * JT : 1];
+  u32x4 w[WK == kDense ? 4 : 1];
+  RawScale sc;
+  u32x4 at[JT > 0 ? JT : 1];
+};
+
+struct FwdOffsets {
+  uint32_t w[4];       // dense: byte offsets of the 4 chunks; NF4: w[0] code byte offset
+  uint32_t q;          // NF4: block index at k = 0
+  uint32_t e;          // NF4: element index at k = 0 (for the group of each step)
+  uint32_t a[2];       // A rows
 };
 
 template <int WK, int JT>
 __device__ __forceinline__ void fwd_stage_load(FwdStage<WK, JT>& st, const FwdParams& p,
-                                               int64_t n0, int64_t kb, int64_t g_lo) {
-  const int tid = threadIdx.x;
-  const int64_t N = p.W.N, K = p.W.K;
-  if (WK == 0) {
+                                               const FwdOffsets& o, int64_t kb, int64_t g_lo) {
+  if (WK == kDense) {
+    const char* base = reinterpret_cast<const char*>(p.W.dense + kb);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + kThreads * i;
-      const int64_t n = n0 + (c >> 4), k = kb + 8 * (c & 15);
-      const bool ok = n < N && k < K;
-      const int64_t nn = n < N ? n : N - 1, kk = k < K ? k : 0;
-      st.w[i] = sel4(ok, *reinterpret_cast<const u32x4*>(p.W.dense + nn * K + kk));
-    }
+    for (int i = 0; i < 4; ++i) st.w[i] = *reinterpret_cast<const u32x4*>(base + o.w[i]);
   } else {
-    const int64_t n = n0 + (tid >> 1), k = kb + 64 * (tid & 1);
-    st.wok = n < N && k < K;
-    const int64_t e = (n < N ? n : N - 1) * K + (k < K ? k : 0);
-    const u32x4* src = reinterpret_cast<const u32x4*>(p.W.codes + (e >> 1));
-    st.w[0] = src[0];
-    st.w[1] = src[1];
-    st.sr = load_scale_ref(p.W, e >> 6, g_lo);
+    st.w[0] = *reinterpret_cast<const u32x4*>(p.W.codes + (kb >> 1) + o.w[0]);
+    const uint32_t qoff = o.q + (uint32_t)(kb >> 6);
+    const int32_t gi = (int32_t)((((int64_t)o.e + kb) >> 14) - g_lo);
+    st.sc = load_raw_scale<WK>(p.W.q8, p.W.absmax, qoff, gi);
   }
+  const char* abase = reinterpret_cast<const char*>(p.A + kb);
 #pragma unroll
-  for (int i = 0; i < 2 * JT; ++i) {
-    const int c = tid + kThreads * i;
-    const int j = c >> 4;
-    const int64_t k = kb + 8 * (c & 15);
-    const bool ok = j < p.r && k < K;
-    const int jj = j < p.r ? j : 0;
-    const int64_t kk = k < K ? k : 0;
-    st.a[i] = sel4(ok, *reinterpret_cast<const u32x4*>(p.A + (int64_t)jj * K + kk));
-  }
+  for (int i = 0; i < JT; ++i) st.at[i] = *reinterpret_cast<const u32x4*>(abase + o.a[i]);
 }
 
-// part sg (0..7) of writing a staged forward tile; a = the thread's block scale
+// part (0..3) of writing a staged forward weight tile; a = its block scale
 template <int WK, int JT>
 __device__ __forceinline__ void fwd_stage_part(const FwdStage<WK, JT>& st, uint16_t* tile,
-                                               const float2* lut, float a, int sg) {
+                                               const float2* lut, float a, int part) {
   const int tid = threadIdx.x;
-  if (WK == 0) {
-    const int c = tid + kThreads * sg;
-    *reinterpret_cast<u32x4*>(tile + (c >> 4) * kLP + 8 * (c & 15)) = st.w[sg];
+  if (WK == kDense) {
+    *reinterpret_cast<u32x4*>(tile + ((tid >> 3) + 32 * part) * kLP + 8 * (tid & 7)) = st.w[part];
   } else {
-    const u32x4 v = deq8(st.w[sg >> 2][sg & 3], a, lut);
-    *reinterpret_cast<u32x4*>(tile + (tid >> 1) * kLP + 64 * (tid & 1) + 8 * sg) = sel4(st.wok, v);
+    *reinterpret_cast<u32x4*>(tile + (tid >> 1) * kLP + 32 * (tid & 1) + 8 * part) =
+        deq8(st.w[0][part], a, lut);
   }
-  if (sg < 2 * JT) {
-    const int c = tid + kThreads * sg;
-    *reinterpret_cast<u32x4*>(tile + (kTileI + (c >> 4)) * kLP + 8 * (c & 15)) = st.a[sg];
-  }
+  if (part < JT)
+    *reinterpret_cast<u32x4*>(tile + (kTileI + (tid >> 3) + 32 * part) * kLP + 8 * (tid & 7)) =
+        st.at[part];
 }
 
 template <int WK, int MS, int RP, bool MULTI>
 __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
   constexpr int JT = MULTI ? 0 : RP / 32;
-  constexpr int ROWS = kTileI + 32 * JT;
-  __shared__ __attribute__((aligned(16))) uint16_t tl[2][ROWS * kLP];
+  constexpr int WROWS = kTileI + 32 * JT;
+  constexpr int AROWS = 128 * MS;
+  __shared__ __attribute__((aligned(16))) uint16_t wt[2][WROWS * kLP];
+  __shared__ __attribute__((aligned(16))) uint16_t xt[2][AROWS * kLP];
   __shared__ float2 lut[256];
-  __shared__ float stab[WK != 0 ? kFwdTab : 1];
+  __shared__ float stab[WK == kNF4DQ ? kFwdTab : 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
   const int tile = xcd_tile(blockIdx.x, p.m_tiles * p.n_tiles);
   const int tile_n = tile % p.n_tiles, tile_m = tile / p.n_tiles;
   const int64_t N = p.W.N, K = p.W.K, M = p.M;
-  const int64_t n0 = (int64_t)tile_n * kTileI, m0 = (int64_t)tile_m * (128 * MS);
+  const int64_t n0 = (int64_t)tile_n * kTileI, m0 = (int64_t)tile_m * AROWS;
   const int64_t mw = m0 + wave * 32 * MS;  // this wave's first row
-  const int KT = (int)((K + kBK - 1) / kBK);
+  const int KT = (int)(K / kBK);
 
   // groups of this tile's rows, for the second-level step table
   const int64_t nlast = (n0 + kTileI < N ? n0 + kTileI : N) - 1;
   const int64_t g_lo = (n0 * K) >> 14;
-  if (WK != 0) {
-    build_lut(lut, p.tab);
-    if (p.W.dq) build_steps(stab, p.W, g_lo, (int)(((nlast * K + K - 1) >> 14) - g_lo + 1));
+  if (WK != kDense) build_lut(lut, p.tab);
+  if (WK == kNF4DQ) build_steps(stab, p.W, g_lo, (int)(((nlast * K + K - 1) >> 14) - g_lo + 1));
+
+  FwdOffsets o;
+  if (WK == kDense) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int64_t n = n0 + (tid >> 3) + 32 * i;
+      n = n < N ? n : N - 1;
+      o.w[i] = (uint32_t)((n * K + 8 * (tid & 7)) * 2);
+    }
+  } else {
+    int64_t n = n0 + (tid >> 1);
+    n = n < N ? n : N - 1;
+    const int64_t e = n * K + 32 * (tid & 1);
+    o.w[0] = (uint32_t)(e >> 1);
+    o.q = (uint32_t)(e >> 6);
+    o.e = (uint32_t)e;
   }
+#pragma unroll
+  for (int i = 0; i < JT; ++i) {
+    int j = (tid >> 3) + 32 * i;
+    j = j < p.r ? j : p.r - 1;
+    o.a[i] = (uint32_t)((j * K + 8 * (tid & 7)) * 2);
+  }
+  uint32_t xo[4 * MS];
+  act_offsets<MS>(xo, K, m0, M);
+  const char* xbase = reinterpret_cast<const char*>(p.X);
 
   f32x16 acc[4][MS];
   f32x16 tacc[JT > 0 ? JT : 1][MS];
   zero_acc(acc);
   zero_acc(tacc);
 
-  const uint16_t* xrow[MS];
-#pragma unroll
-  for (int ms = 0; ms < MS; ++ms) {
-    const int64_t m = mw + 32 * ms + l32;
-    xrow[ms] = p.X + (m < M ? m : M - 1) * K;
-  }
-
   FwdStage<WK, JT> s0, s1;
-  ActRegs<MS> xa, xb;
+  ActStage<MS> x0, x1;
 
-  fwd_stage_load<WK, JT>(s0, p, n0, 0, g_lo);
-  load_act<MS>(xa, xrow, 0, K, h);
+  fwd_stage_load<WK, JT>(s0, p, o, 0, g_lo);
+  act_load<MS>(x0, xbase, xo);
   __syncthreads();  // level and step tables ready
   {
-    const float a = WK != 0 ? scale_from(p.W, s0.sr, stab) : 0.0f;
+    const float a = WK != kDense ? raw_scale_value<WK>(s0.sc, stab) : 0.0f;
 #pragma unroll
-    for (int sg = 0; sg < 8; ++sg) fwd_stage_part<WK, JT>(s0, tl[0], lut, a, sg);
+    for (int q = 0; q < 4; ++q) {
+      fwd_stage_part<WK, JT>(s0, wt[0], lut, a, q);
+      act_part<MS>(x0, xt[0], q);
+    }
   }
-  fwd_stage_load<WK, JT>(s1, p, n0, (KT > 1 ? 1 : 0) * (int64_t)kBK, g_lo);
+  const int64_t kb1 = (int64_t)(KT > 1 ? 1 : 0) * kBK;
+  fwd_stage_load<WK, JT>(s1, p, o, kb1, g_lo);
+  act_load<MS>(x1, xbase + 2 * kb1, xo);
   __syncthreads();
 
-  // step kt: loads stage kt+2 into snxt and activations kt+1 into nxt, runs
-  // the MFMAs of step kt, writes stage kt+1 (scur) into the other buffer
-  auto step = [&](int kt, const ActRegs<MS>& cur, ActRegs<MS>& nxt, const FwdStage<WK, JT>& scur,
-                  FwdStage<WK, JT>& snxt) {
-    const int64_t k1 = (int64_t)(kt + 1 < KT ? kt + 1 : KT - 1) * kBK;
+  // step kt: loads stage kt+2 into (snxt, xnxt), runs the MFMAs of step kt on
+  // LDS buffer kt & 1, writes stage kt+1 (scur, xcur) into the other buffer
+  auto step = [&](int kt, const FwdStage<WK, JT>& scur, const ActStage<MS>& xcur,
+                  FwdStage<WK, JT>& snxt, ActStage<MS>& xnxt) {
     const int64_t k2 = (int64_t)(kt + 2 < KT ? kt + 2 : KT - 1) * kBK;
-    fwd_stage_load<WK, JT>(snxt, p, n0, k2, g_lo);
-    load_act<MS>(nxt, xrow, k1, K, h);
-    const float a = WK != 0 ? scale_from(p.W, scur.sr, stab) : 0.0f;
-    uint16_t* nt = tl[(kt & 1) ^ 1];
-    mfma_step<MS, JT>(tl[kt & 1], l32, h, cur, acc, tacc,
-                      [&](int sg) { fwd_stage_part<WK, JT>(scur, nt, lut, a, sg); });
+    fwd_stage_load<WK, JT>(snxt, p, o, k2, g_lo);
+    act_load<MS>(xnxt, xbase + 2 * k2, xo);
+    const float a = WK != kDense ? raw_scale_value<WK>(scur.sc, stab) : 0.0f;
+    const int b = kt & 1;
+    uint16_t* wn = wt[b ^ 1];
+    uint16_t* xn = xt[b ^ 1];
+    mfma_step<MS, JT>(wt[b], xt[b], wave, l32, h, acc, tacc, [&](int q) {
+      fwd_stage_part<WK, JT>(scur, wn, lut, a, q);
+      act_part<MS>(xcur, xn, q);
+    });
     __syncthreads();
   };
 
   int kt = 0;
   for (; kt + 1 < KT; kt += 2) {
-    step(kt, xa, xb, s1, s0);
-    step(kt + 1, xb, xa, s0, s1);
+    step(kt, s1, x1, s0, x0);
+    step(kt + 1, s0, x0, s1, x1);
   }
-  if (kt < KT) step(kt, xa, xb, s1, s0);
+  if (kt < KT) step(kt, s1, x1, s0, x0);
 
   // ---------------------------------------------------------------- epilogue
   const int r = p.r;
@@ -440,79 +515,94 @@ struct BwdParams {
   NF4Table tab;
 };
 
-constexpr int kDxTab = 1024;  // second-level steps of one step's 128 x 128 tile (K <= 65536)
+constexpr int kDxTab = 512;  // second-level steps of one step's 64 x 128 tile (K <= 65536)
 
-// Staging for one dX step: W rows n0r .. n0r+127 (reduction) and columns
-// k0 .. k0+127 (outputs), stored transposed: tile[k][n].  Thread t covers
-// columns k0 + 8 (t & 15) .. +7 of rows n0r + 8 (t >> 4) .. +7 and transposes
-// that 8 x 8 patch in registers.  B^T (RP x 128) rides along as tile rows
-// 128 ..: thread t < 2 RP takes B rows n0r + 8 (t & 15) .. +7, columns
-// 8 (t >> 4) .. +7 (zero past r), transposed the same way.  The step's
+// Weight staging for one dX step: W rows n0r .. n0r+63 (reduction) and
+// columns k0 .. k0+127 (outputs), stored transposed: tile[k][n].  Thread t
+// covers columns k0 + 8 (t & 15) .. +7 of rows n0r + 4 (t >> 4) .. +3 and
+// transposes that 4 x 8 patch in registers.  B^T (RP x 64) rides along as
+// tile rows 128 ..: its RP 8 x 8 patches (B rows n0r + 8 (t & 7) .., columns
+// 8 (t / 8) ..) go to the first RP / 4 lanes of every wave.  The step's
 // second-level constants (at most kDxTab groups) are loaded with the stage and
-// turned into the step table of its LDS slot while the previous step runs.
+// turned into that stage's step table while the previous step runs.  Offsets
+// are per-thread constants; columns past K are clamped (their outputs are
+// never stored) and N % 64 == 0 keeps every reduction step full.
 template <int WK, int RP>
 struct BwdStage {
-  uint32_t w[8][WK == 0 ? 4 : 1];
-  ScaleRef sr[WK == 0 ? 1 : 8];
-  bool ok[8];
+  uint32_t w[4][WK == kDense ? 4 : 1];
+  RawScale sc[WK == kDense ? 1 : 4];
   uint32_t b[8][4];
-  float c2[WK == 0 ? 1 : kDxTab / kThreads];
+  float c2[kDxTab / kThreads];
 };
 
-__device__ __forceinline__ int64_t dx_group_base(int64_t n0r, int64_t k0, int64_t K) {
-  return (n0r * K + k0) >> 14;
+struct BwdOffsets {
+  uint32_t w[4];   // per patch row: dense byte offset, NF4 code byte offset
+  uint32_t q[4];   // NF4: block index of the patch row (relative to the step's first row)
+  uint32_t e[4];   // NF4: element index (relative to the step's first row)
+  uint32_t b[8];   // B^T patch rows: byte offsets (relative to the step's first row)
+  int bt;          // B^T patch index of this lane, or -1
+};
+
+template <int RP>
+__device__ __forceinline__ int bt_task(int tid) {
+  // RP patches: RP / 4 lanes in each of the 4 waves
+  const int lane = tid & 63, wave = tid >> 6;
+  return lane < RP / 4 ? wave * (RP / 4) + lane : -1;
 }
 
 template <int WK, int RP>
 __device__ __forceinline__ void bwd_stage_load(BwdStage<WK, RP>& st, const BwdParams& p,
-                                               int64_t n0r, int64_t k0) {
+                                               const BwdOffsets& o, int64_t n0r, int64_t k0) {
   const int tid = threadIdx.x;
-  const int64_t N = p.W.N, K = p.W.K;
-  const int64_t k = k0 + 8 * (tid & 15);
-  const int64_t kk = k < K ? k : K - 8;  // stays at or after k0, so groups stay >= g_lo
-  const int64_t g_lo = dx_group_base(n0r, k0, K);
+  const int64_t K = p.W.K;
+  const int64_t eb = n0r * K;  // first element of the step's rows
+  if (WK == kDense) {
+    const char* base = reinterpret_cast<const char*>(p.W.dense + eb);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t n = n0r + 8 * (tid >> 4) + i;
-    st.ok[i] = n < N && k < K;
-    const int64_t nn = n < N ? n : N - 1;
-    if (WK == 0) {
-      const u32x4 v = sel4(st.ok[i], *reinterpret_cast<const u32x4*>(p.W.dense + nn * K + kk));
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(base + o.w[i]);
 #pragma unroll
       for (int d = 0; d < 4; ++d) st.w[i][d] = v[d];
-    } else {
-      const int64_t e = nn * K + kk;
-      st.w[i][0] = *reinterpret_cast<const uint32_t*>(p.W.codes + (e >> 1));
-      st.sr[i] = load_scale_ref(p.W, e >> 6, g_lo);
     }
-  }
-  if (WK != 0 && p.W.dq) {
-    const int64_t ng = (N * K + 16383) >> 14;  // number of groups
+  } else {
+    const uint8_t* cb = p.W.codes + (eb >> 1);
+    const int64_t g_lo = (eb + k0) >> 14;
+    const int64_t elo = eb & 16383;
 #pragma unroll
-    for (int i = 0; i < kDxTab / kThreads; ++i) {
-      const int64_t g = g_lo + tid + kThreads * i;
-      st.c2[i] = p.W.c2[g < ng ? g : ng - 1];
+    for (int i = 0; i < 4; ++i) {
+      st.w[i][0] = *reinterpret_cast<const uint32_t*>(cb + o.w[i]);
+      const int32_t gi = (int32_t)(((elo + o.e[i]) >> 14) - ((elo + k0) >> 14));
+      st.sc[i] = load_raw_scale<WK>(p.W.q8 + (eb >> 6), p.W.absmax + (eb >> 6), o.q[i], gi);
+    }
+    if (WK == kNF4DQ) {
+      const int64_t ng = (p.W.N * K + 16383) >> 14;  // number of groups
+#pragma unroll
+      for (int i = 0; i < kDxTab / kThreads; ++i) {
+        const int64_t g = g_lo + tid + kThreads * i;
+        st.c2[i] = p.W.c2[g < ng ? g : ng - 1];
+      }
     }
   }
-  const int jb = 8 * (tid >> 4);
-  if (jb < RP) {
+  if (o.bt >= 0) {
+    const char* base = reinterpret_cast<const char*>(p.B + n0r * p.r);
+    const int jb = 8 * (o.bt >> 3);
     const int r = p.r;
-    const bool vec = (r & 7) == 0 && jb + 8 <= r;
+    if ((r & 7) == 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t n = n0r + 8 * (tid & 15) + i;
-      const bool nok = n < N;
-      const uint16_t* row = p.B + (nok ? n : N - 1) * r;
-      if (vec) {
-        const u32x4 q = sel4(nok, *reinterpret_cast<const u32x4*>(row + jb));
+      for (int i = 0; i < 8; ++i) {
+        const u32x4 v = sel4(jb < r, *reinterpret_cast<const u32x4*>(base + o.b[i]));
 #pragma unroll
-        for (int d = 0; d < 4; ++d) st.b[i][d] = q[d];
-      } else {
+        for (int d = 0; d < 4; ++d) st.b[i][d] = v[d];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint16_t* row = reinterpret_cast<const uint16_t*>(base + o.b[i]);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const int j = jb + 2 * d;
-          const uint32_t lo = (nok && j < r) ? row[j] : 0u;
-          const uint32_t hi = (nok && j + 1 < r) ? row[j + 1] : 0u;
+          const uint32_t lo = j < r ? row[j - jb] : 0u;
+          const uint32_t hi = j + 1 < r ? row[j + 1 - jb] : 0u;
           st.b[i][d] = lo | (hi << 16);
         }
       }
@@ -520,108 +610,131 @@ __device__ __forceinline__ void bwd_stage_load(BwdStage<WK, RP>& st, const BwdPa
   }
 }
 
-// second-level step table of a loaded stage (written by every thread)
+// part (0..3): dequantise row `part` of the weight patch; the last part
+// transposes and stores the weight patch and the B^T patch.
 template <int WK, int RP>
-__device__ __forceinline__ void bwd_stage_steps(const BwdStage<WK, RP>& st, float* tab) {
-  if (WK != 0) {
+__device__ __forceinline__ void bwd_stage_part(const BwdStage<WK, RP>& st, uint32_t (&rows)[4][4],
+                                               uint16_t* tile, const float2* lut, const float* tab,
+                                               int bt, int part) {
+  const int tid = threadIdx.x;
+  if (WK == kDense) {
 #pragma unroll
-    for (int i = 0; i < kDxTab / kThreads; ++i) tab[threadIdx.x + kThreads * i] = dq_step(st.c2[i]);
+    for (int d = 0; d < 4; ++d) rows[part][d] = st.w[part][d];
+  } else {
+    const u32x4 v = deq8(st.w[part][0], raw_scale_value<WK>(st.sc[part], tab), lut);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) rows[part][d] = v[d];
+  }
+  if (part == 3) {
+    store_transposed<4>(rows, tile + (8 * (tid & 15)) * kLP + 4 * (tid >> 4), kLP);
+    if (bt >= 0) store_transposed<8>(st.b, tile + (kTileI + 8 * (bt >> 3)) * kLP + 8 * (bt & 7), kLP);
   }
 }
 
-// part sg (0..7): dequantise row sg of the patch; the last part transposes and
-// stores the weight patch and the B^T patch.
 template <int WK, int RP>
-__device__ __forceinline__ void bwd_stage_part(const BwdStage<WK, RP>& st, uint32_t (&rows)[8][4],
-                                               uint16_t* tile, const float2* lut,
-                                               const WeightArgs& w, const float* tab, int sg) {
-  const int tid = threadIdx.x;
-  if (WK == 0) {
+__device__ __forceinline__ void bwd_stage_steps(const BwdStage<WK, RP>& st, float* tab) {
+  if (WK == kNF4DQ) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) rows[sg][d] = st.w[sg][d];
-  } else {
-    const float a = scale_from(w, st.sr[sg], tab);
-    const u32x4 v = sel4(st.ok[sg], deq8(st.w[sg][0], a, lut));
-#pragma unroll
-    for (int d = 0; d < 4; ++d) rows[sg][d] = v[d];
-  }
-  if (sg == 7) {
-    store_transposed8(rows, tile + (8 * (tid & 15)) * kLP + 8 * (tid >> 4), kLP);
-    const int jb = 8 * (tid >> 4);
-    if (jb < RP) store_transposed8(st.b, tile + (kTileI + jb) * kLP + 8 * (tid & 15), kLP);
+    for (int i = 0; i < kDxTab / kThreads; ++i) tab[threadIdx.x + kThreads * i] = dq_step(st.c2[i]);
   }
 }
 
 template <int WK, int MS, int RP>
 __global__ __launch_bounds__(kThreads) void dx_kernel(BwdParams p) {
   constexpr int JT = RP / 32;
-  constexpr int ROWS = kTileI + RP;
-  __shared__ __attribute__((aligned(16))) uint16_t tl[2][ROWS * kLP];
+  constexpr int WROWS = kTileI + RP;
+  constexpr int AROWS = 128 * MS;
+  __shared__ __attribute__((aligned(16))) uint16_t wt[2][WROWS * kLP];
+  __shared__ __attribute__((aligned(16))) uint16_t gt[2][AROWS * kLP];
   __shared__ float2 lut[256];
-  __shared__ float stab[2][WK != 0 ? kDxTab : 1];
+  __shared__ float stab[2][WK == kNF4DQ ? kDxTab : 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
   const int tile = xcd_tile(blockIdx.x, p.m_tiles * p.k_tiles);
   const int tile_k = tile % p.k_tiles, tile_m = tile / p.k_tiles;
   const int64_t N = p.W.N, K = p.W.K, M = p.M;
-  const int64_t k0 = (int64_t)tile_k * kTileI, m0 = (int64_t)tile_m * (128 * MS);
+  const int64_t k0 = (int64_t)tile_k * kTileI, m0 = (int64_t)tile_m * AROWS;
   const int64_t mw = m0 + wave * 32 * MS;
-  const int RT = (int)((N + kBK - 1) / kBK);
+  const int RT = (int)(N / kBK);
 
-  if (WK != 0) build_lut(lut, p.tab);
+  if (WK != kDense) build_lut(lut, p.tab);
+
+  BwdOffsets o;
+  {
+    int64_t k = k0 + 8 * (tid & 15);
+    k = k < K ? k : K - 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t e = (int64_t)(4 * (tid >> 4) + i) * K + k;  // relative to the step's rows
+      o.w[i] = WK == kDense ? (uint32_t)(e * 2) : (uint32_t)(e >> 1);
+      o.q[i] = (uint32_t)(e >> 6);
+      o.e[i] = (uint32_t)e;
+    }
+    o.bt = bt_task<RP>(tid);
+    const int bt = o.bt < 0 ? 0 : o.bt;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int jb = 8 * (bt >> 3);
+      const int jc = jb < p.r ? jb : 0;
+      o.b[i] = (uint32_t)(((8 * (bt & 7) + i) * p.r + jc) * 2);
+    }
+  }
+  uint32_t go[4 * MS];
+  act_offsets<MS>(go, N, m0, M);
+  const char* gbase = reinterpret_cast<const char*>(p.dY);
 
   f32x16 acc[4][MS];
   f32x16 uacc[JT][MS];
   zero_acc(acc);
   zero_acc(uacc);
 
-  const uint16_t* grow[MS];
-#pragma unroll
-  for (int ms = 0; ms < MS; ++ms) {
-    const int64_t m = mw + 32 * ms + l32;
-    grow[ms] = p.dY + (m < M ? m : M - 1) * N;
-  }
-
   BwdStage<WK, RP> s0, s1;
-  ActRegs<MS> ga, gb;
-  uint32_t rows[8][4];
+  ActStage<MS> g0, g1;
+  uint32_t rows[4][4];
 
   // stage s uses step-table slot s & 1
-  bwd_stage_load<WK, RP>(s0, p, 0, k0);
-  load_act<MS>(ga, grow, 0, N, h);
+  bwd_stage_load<WK, RP>(s0, p, o, 0, k0);
+  act_load<MS>(g0, gbase, go);
   bwd_stage_steps<WK, RP>(s0, stab[0]);
   __syncthreads();  // level table and stage-0 step table ready
 #pragma unroll
-  for (int sg = 0; sg < 8; ++sg) bwd_stage_part<WK, RP>(s0, rows, tl[0], lut, p.W, stab[0], sg);
-  bwd_stage_load<WK, RP>(s1, p, (RT > 1 ? 1 : 0) * (int64_t)kBK, k0);
+  for (int q = 0; q < 4; ++q) {
+    bwd_stage_part<WK, RP>(s0, rows, wt[0], lut, stab[0], o.bt, q);
+    act_part<MS>(g0, gt[0], q);
+  }
+  const int64_t n1 = (int64_t)(RT > 1 ? 1 : 0) * kBK;
+  bwd_stage_load<WK, RP>(s1, p, o, n1, k0);
+  act_load<MS>(g1, gbase + 2 * n1, go);
   bwd_stage_steps<WK, RP>(s1, stab[1]);
   __syncthreads();
 
-  // step rt: loads stage rt+2 into snxt and activations rt+1 into nxt, runs
-  // the MFMAs of step rt, writes stage rt+1 (scur) into the other buffer and
-  // the step table of stage rt+2 into slot (rt+2) & 1 = rt & 1
-  auto step = [&](int rt, const ActRegs<MS>& cur, ActRegs<MS>& nxt, const BwdStage<WK, RP>& scur,
-                  BwdStage<WK, RP>& snxt) {
-    const int64_t n1 = (int64_t)(rt + 1 < RT ? rt + 1 : RT - 1) * kBK;
+  // step rt: loads stage rt+2 into (snxt, gnxt), runs the MFMAs of step rt on
+  // buffer rt & 1, writes stage rt+1 (scur, gcur) into the other buffer and
+  // the step table of stage rt+2 into slot rt & 1
+  auto step = [&](int rt, const BwdStage<WK, RP>& scur, const ActStage<MS>& gcur,
+                  BwdStage<WK, RP>& snxt, ActStage<MS>& gnxt) {
     const int64_t n2 = (int64_t)(rt + 2 < RT ? rt + 2 : RT - 1) * kBK;
-    bwd_stage_load<WK, RP>(snxt, p, n2, k0);
-    load_act<MS>(nxt, grow, n1, N, h);
-    uint16_t* nt = tl[(rt & 1) ^ 1];
-    const float* tcur = stab[(rt & 1) ^ 1];
-    mfma_step<MS, JT>(tl[rt & 1], l32, h, cur, acc, uacc, [&](int sg) {
-      bwd_stage_part<WK, RP>(scur, rows, nt, lut, p.W, tcur, sg);
-      if (sg == 7) bwd_stage_steps<WK, RP>(snxt, stab[rt & 1]);
+    bwd_stage_load<WK, RP>(snxt, p, o, n2, k0);
+    act_load<MS>(gnxt, gbase + 2 * n2, go);
+    const int b = rt & 1;
+    uint16_t* wn = wt[b ^ 1];
+    uint16_t* gn = gt[b ^ 1];
+    const float* tcur = stab[b ^ 1];
+    mfma_step<MS, JT>(wt[b], gt[b], wave, l32, h, acc, uacc, [&](int q) {
+      bwd_stage_part<WK, RP>(scur, rows, wn, lut, tcur, o.bt, q);
+      act_part<MS>(gcur, gn, q);
+      if (q == 3) bwd_stage_steps<WK, RP>(snxt, stab[b]);
     });
     __syncthreads();
   };
 
   int rt = 0;
   for (; rt + 1 < RT; rt += 2) {
-    step(rt, ga, gb, s1, s0);
-    step(rt + 1, gb, ga, s0, s1);
+    step(rt, s1, g1, s0, g0);
+    step(rt + 1, s0, g0, s1, g1);
   }
-  if (rt < RT) step(rt, ga, gb, s1, s0);
+  if (rt < RT) step(rt, s1, g1, s0, g0);
 
   const int r = p.r;
   if (p.U_out && tile_k == 0) {
@@ -709,7 +822,8 @@ __global__ void rowmap_kernel(const int32_t* __restrict__ off, const int32_t* __
 
 // Tm[m][c] = s * sum_k X[m][k] Acat[c][k] if adapter(m) == c / r else 0, for
 // c < n_ad * r (Acat = A_stack viewed as (n_ad r) x K), zero up to RP; bf16.
-// Each wave takes 32 rows; A_stack rows are read straight from L2.
+// Each wave takes 32 rows; lane (h, l32) reads row l32, 32 contiguous columns
+// per 64-step (the same relabelling of the reduction index on both operands).
 template <int RP>
 __global__ __launch_bounds__(kThreads) void multi_shrink_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t K, const uint16_t* __restrict__ Acat,
@@ -719,30 +833,33 @@ __global__ __launch_bounds__(kThreads) void multi_shrink_kernel(
   const int h = lane >> 5, l32 = lane & 31;
   const int64_t mw = ((int64_t)blockIdx.x * 4 + wave) * 32;
   const int64_t m = mw + l32;
-  const uint16_t* xrow[1] = {X + (m < M ? m : M - 1) * K};
+  const uint16_t* xrow = X + (m < M ? m : M - 1) * K + 32 * h;
   const uint16_t* arow[JT];
+  bool aok[JT];
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) {
     const int j = 32 * jt + l32;
-    arow[jt] = Acat + (int64_t)(j < rc ? j : 0) * K;
+    aok[jt] = j < rc;
+    arow[jt] = Acat + (int64_t)(j < rc ? j : 0) * K + 32 * h;
   }
   f32x16 t[JT];
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) t[jt][v] = 0.0f;
-  for (int64_t kb = 0; kb < K; kb += kBK) {
-    ActRegs<1> xf;
-    load_act<1>(xf, xrow, kb, K, h);
-    ActRegs<JT> af;
-    load_act<JT>(af, arow, kb, K, h);
+  for (int64_t kb = 0; kb < K; kb += 64) {
+    u32x4 xf[4], af[JT][4];
 #pragma unroll
-    for (int sg = 0; sg < 8; ++sg)
+    for (int q = 0; q < 4; ++q) {
+      xf[q] = *reinterpret_cast<const u32x4*>(xrow + kb + 8 * q);
 #pragma unroll
-      for (int jt = 0; jt < JT; ++jt) {
-        const bool jok = 32 * jt + l32 < rc;
-        t[jt] = mfma32(sel4(jok, af.f[jt][sg]), xf.f[0][sg], t[jt]);
-      }
+      for (int jt = 0; jt < JT; ++jt)
+        af[jt][q] = sel4(aok[jt], *reinterpret_cast<const u32x4*>(arow[jt] + kb + 8 * q));
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) t[jt] = mfma32(af[jt][q], xf[q], t[jt]);
   }
   if (m >= M) return;
   const int a = row_ad[m];
@@ -788,8 +905,9 @@ int fwd_pick(const FwdParams& p, int rp, hipStream_t st) {
 
 template <bool MULTI>
 int fwd_dispatch(const FwdParams& p, const lq_weight& W, int rp, hipStream_t st) {
-  if (W.kind == LQ_WEIGHT_DENSE) return fwd_pick<0, MULTI>(p, rp, st);
-  return fwd_pick<1, MULTI>(p, rp, st);
+  if (W.kind == LQ_WEIGHT_DENSE) return fwd_pick<kDense, MULTI>(p, rp, st);
+  if (W.double_quant) return fwd_pick<kNF4DQ, MULTI>(p, rp, st);
+  return fwd_pick<kNF4, MULTI>(p, rp, st);
 }
 
 template <int WK, int MS, int RP>
@@ -844,8 +962,9 @@ int bf16_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const 
   p.dX = (uint16_t*)dX;
   p.U_out = U_out;
   p.tab = nf4_table();
-  if (W.kind == LQ_WEIGHT_DENSE) return dx_pick<0>(p, st);
-  return dx_pick<1>(p, st);
+  if (W.kind == LQ_WEIGHT_DENSE) return dx_pick<kDense>(p, st);
+  if (W.double_quant) return dx_pick<kNF4DQ>(p, st);
+  return dx_pick<kNF4>(p, st);
 }
 
 size_t multi_ws_bytes(int64_t T_tokens, int64_t r, int32_t n_adapters) {

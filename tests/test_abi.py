@@ -77,6 +77,7 @@ def test_argument_errors_launch_nothing():
     # bf16 shape rules: K % 64, N % 32
     assert _fwd(_weight(K=200)) == -2
     assert _fwd(_weight(N=100)) == -2
+    assert _fwd(_weight(N=96)) == -2                # N % 64
     # dtype mismatch between descriptor and call
     assert _fwd(_weight(dtype=lq.LQ_F32)) == -1
     # missing workspace when T_out is NULL (M > 0)

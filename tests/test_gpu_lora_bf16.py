@@ -73,8 +73,8 @@ SMALL = [
     (300, 384, 512, 16),     # ragged M, three 128-column tiles
     (2100, 256, 256, 16),    # 256-row tiles, ragged
     (700, 256, 320, 64),     # rank 64 (two 32-row shrink blocks)
-    (130, 160, 192, 5),      # odd rank, partial column tile, partial reduction step
-    (17, 96, 128, 8),        # smallest non-decode M
+    (130, 192, 192, 5),      # odd rank, partial column tile, partial k tile
+    (17, 128, 128, 8),       # smallest non-decode M
 ]
 
 
@@ -91,7 +91,7 @@ def test_small(shape, kind):
 def test_decode_small(M, kind):
     c = wl.small_case(M, 256, 512, 16, seed=100 + M)
     check_layer(c, kind, label="decode", bwd=True, merge=False)
-    c = wl.small_case(M, 96, 192, 5, seed=200 + M)
+    c = wl.small_case(M, 192, 192, 5, seed=200 + M)
     check_layer(c, kind, label="decode-odd", bwd=False, merge=False)
 
 
