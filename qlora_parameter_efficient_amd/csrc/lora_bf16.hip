@@ -71,29 +71,6 @@ __device__ __forceinline__ u32x4 t_operand(const f32x16& t, int cc, float s) {
   return o;
 }
 
-// R x 8 bf16 patch, rows[i][d] = elements (2d, 2d+1) of row i (R = 4 or 8),
-// stored transposed: output row c (c = 0..7) holds element c of rows 0..R-1.
-template <int R>
-__device__ __forceinline__ void store_transposed(const uint32_t (&rows)[R][4], uint16_t* dst,
-                                                 int pitch) {
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    uint32_t ev[R / 2], od[R / 2];
-#pragma unroll
-    for (int e = 0; e < R / 2; ++e) {
-      ev[e] = pair_lo(rows[2 * e][d], rows[2 * e + 1][d]);
-      od[e] = pair_hi(rows[2 * e][d], rows[2 * e + 1][d]);
-    }
-    if (R == 8) {
-      *reinterpret_cast<u32x4*>(dst + (2 * d) * pitch) = u32x4{ev[0], ev[1], ev[2], ev[3]};
-      *reinterpret_cast<u32x4*>(dst + (2 * d + 1) * pitch) = u32x4{od[0], od[1], od[2], od[3]};
-    } else {
-      *reinterpret_cast<u32x2*>(dst + (2 * d) * pitch) = u32x2{ev[0], ev[1]};
-      *reinterpret_cast<u32x2*>(dst + (2 * d + 1) * pitch) = u32x2{od[0], od[1]};
-    }
-  }
-}
-
 // Activation tile of one step, 128 MS rows x 64: thread t loads chunks
 // c = t + 256 i (row c / 8, 16-byte chunk c % 8), so eight consecutive lanes
 // read one row's 128 contiguous bytes.  Offsets are per-thread constants
@@ -229,10 +206,28 @@ __device__ __forceinline__ RawScale load_raw_scale(const uint8_t* q8, const floa
   return r;
 }
 
+// Marks v as produced here.  The compiler otherwise converts a freshly loaded
+// constant right after its load, which waits for that load (a full memory
+// latency) in the middle of the step that issued it.
+__device__ __forceinline__ uint32_t pin(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ float pin(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ u32x4 pin(u32x4 v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 template <int WK>
 __device__ __forceinline__ float raw_scale_value(const RawScale& r, const float* tab) {
-  if (WK == kNF4DQ) return (float)r.q * tab[r.gi];
-  return __uint_as_float(r.q);
+  if (WK == kNF4DQ) return (float)pin(r.q) * tab[r.gi];
+  return __uint_as_float(pin(r.q));
 }
 
 // Weight staging for one forward step: rows n0 .. n0+127, columns kb .. kb+63.
@@ -515,139 +510,168 @@ struct BwdParams {
   NF4Table tab;
 };
 
-constexpr int kDxTab = 512;  // second-level steps of one step's 64 x 128 tile (K <= 65536)
-
-// Weight staging for one dX step: W rows n0r .. n0r+63 (reduction) and
-// columns k0 .. k0+127 (outputs), stored transposed: tile[k][n].  Thread t
-// covers columns k0 + 8 (t & 15) .. +7 of rows n0r + 4 (t >> 4) .. +3 and
-// transposes that 4 x 8 patch in registers.  B^T (RP x 64) rides along as
-// tile rows 128 ..: its RP 8 x 8 patches (B rows n0r + 8 (t & 7) .., columns
-// 8 (t / 8) ..) go to the first RP / 4 lanes of every wave.  The step's
-// second-level constants (at most kDxTab groups) are loaded with the stage and
-// turned into that stage's step table while the previous step runs.  Offsets
-// are per-thread constants; columns past K are clamped (their outputs are
-// never stored) and N % 64 == 0 keeps every reduction step full.
-template <int WK, int RP>
-struct BwdStage {
-  uint32_t w[4][WK == kDense ? 4 : 1];
-  RawScale sc[WK == kDense ? 1 : 4];
-  uint32_t b[8][4];
-  float c2[kDxTab / kThreads];
-};
-
-struct BwdOffsets {
-  uint32_t w[4];   // per patch row: dense byte offset, NF4 code byte offset
-  uint32_t q[4];   // NF4: block index of the patch row (relative to the step's first row)
-  uint32_t e[4];   // NF4: element index (relative to the step's first row)
-  uint32_t b[8];   // B^T patch rows: byte offsets (relative to the step's first row)
-  int bt;          // B^T patch index of this lane, or -1
-};
-
+// dX weight tile of one step: W rows n0r .. n0r+63 (the reduction) by
+// columns k0 .. k0+127 (the outputs), kept in LDS in storage order (row n, k
+// contiguous), and B rows n0r .. n0r+63 as columns 128 .. 128+RP of the same
+// tile rows.  The MFMA operands (one column, eight consecutive rows) are read
+// with the gfx950 transposing LDS read ds_read_b64_tr_b16: inside each group
+// of 16 lanes, lane c addresses row c / 4, columns 4 (c % 4) .. +3 of a 4 x 16
+// block, and lane i receives column i of rows 0..3.  16-byte chunk q of row n
+// is stored at chunk q ^ (n & 3); with a row pitch of 20 (RP = 32) or 28
+// (RP = 64) chunks, both the 16-byte stores and the transposing reads of 16
+// lanes land on 16 distinct 16-byte bank groups.
 template <int RP>
-__device__ __forceinline__ int bt_task(int tid) {
-  // RP patches: RP / 4 lanes in each of the 4 waves
-  const int lane = tid & 63, wave = tid >> 6;
-  return lane < RP / 4 ? wave * (RP / 4) + lane : -1;
+struct DxPitch {
+  static constexpr int P = RP == 32 ? 160 : 224;  // elements
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4* lds_ptr;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
+// mfma_step with the weight operands read transposed from a storage-order
+// tile of pitch P: subtile ns covers columns 32 ns .. +31, substep s rows
+// 32 h + 8 s .. +7 (lane half h), the same reduction labels as the
+// activation operand.
+template <int MS, int JT, int P, typename Part>
+__device__ __forceinline__ void mfma_step_tr(const uint16_t* wtile, const uint16_t* atile, int wave,
+                                             int lane, f32x16 (&acc)[4][MS],
+                                             f32x16 (&tacc)[JT][MS], Part&& part) {
+  constexpr int NR = 4 + JT;
+  const int c = lane & 15, g = lane >> 4, h = lane >> 5, l32 = lane & 31;
+  const uint16_t* wbase = wtile + (32 * h + (c >> 2)) * P +
+                          8 * ((2 * (g & 1) + ((c >> 1) & 1)) ^ (c >> 2)) + 4 * (c & 1);
+  const uint16_t* abase = atile + (32 * MS * wave + l32) * kLP + 32 * h;
+  auto wread = [&](int ns, int s) {
+    const uint16_t* q = wbase + 8 * s * P + 32 * ns;
+    const u32x2 lo = lds_read_tr(q), hi = lds_read_tr(q + 4 * P);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  u32x4 wf[2][NR], af[2][MS];
+#pragma unroll
+  for (int ns = 0; ns < NR; ++ns) wf[0][ns] = wread(ns, 0);
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) af[0][ms] = *reinterpret_cast<const u32x4*>(abase + 32 * ms * kLP);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int cb = s & 1;
+    if (s < 3) {
+#pragma unroll
+      for (int ns = 0; ns < NR; ++ns) wf[cb ^ 1][ns] = wread(ns, s + 1);
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms)
+        af[cb ^ 1][ms] = *reinterpret_cast<const u32x4*>(abase + 32 * ms * kLP + 8 * (s + 1));
+    }
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) acc[ns][ms] = mfma32(wf[cb][ns], af[cb][ms], acc[ns][ms]);
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) tacc[jt][ms] = mfma32(wf[cb][4 + jt], af[cb][ms], tacc[jt][ms]);
+    part(s);
+  }
+}
+
+// Staging of one dX step, loaded two steps ahead.  NF4: thread t takes row
+// t / 4 and the 32 columns k0 + 32 (t % 4) .. (16 code bytes, half a block:
+// one block constant, and for double quantisation its group's c2).  Dense:
+// thread t takes the 16-byte chunk t % 16 of rows t / 16 + 16 i.  B: thread t
+// takes row t / 4, columns 8 (t % 4 + 4 i) .. +7 (whole 16-byte chunks when
+// r % 8 == 0 (BV), element loads otherwise).  Columns past K are clamped
+// (their outputs are never stored) and N % 64 == 0 keeps every step full.
 template <int WK, int RP>
-__device__ __forceinline__ void bwd_stage_load(BwdStage<WK, RP>& st, const BwdParams& p,
-                                               const BwdOffsets& o, int64_t n0r, int64_t k0) {
-  const int tid = threadIdx.x;
+struct DxStage {
+  u32x4 w[WK == kDense ? 4 : 1];
+  uint32_t q;
+  float c2;
+  u32x4 b[RP / 32];
+};
+
+struct DxOffsets {
+  uint32_t w[4];  // dense: byte offsets of the 4 chunks; NF4: w[0] code byte offset
+  uint32_t e;     // NF4: element index of the thread's first code
+  uint32_t b[2];  // B: element offset of each chunk (row * r + 8 chunk)
+  uint32_t st[4]; // LDS element offsets of the 4 weight parts
+  uint32_t sb;    // LDS element offset of the B chunks
+};
+
+template <int WK, int RP, bool BV>
+__device__ __forceinline__ void dx_stage_load(DxStage<WK, RP>& st, const BwdParams& p,
+                                              const DxOffsets& o, int64_t n0r) {
   const int64_t K = p.W.K;
   const int64_t eb = n0r * K;  // first element of the step's rows
   if (WK == kDense) {
     const char* base = reinterpret_cast<const char*>(p.W.dense + eb);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(base + o.w[i]);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) st.w[i][d] = v[d];
-    }
+    for (int i = 0; i < 4; ++i) st.w[i] = *reinterpret_cast<const u32x4*>(base + o.w[i]);
   } else {
-    const uint8_t* cb = p.W.codes + (eb >> 1);
-    const int64_t g_lo = (eb + k0) >> 14;
-    const int64_t elo = eb & 16383;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st.w[i][0] = *reinterpret_cast<const uint32_t*>(cb + o.w[i]);
-      const int32_t gi = (int32_t)(((elo + o.e[i]) >> 14) - ((elo + k0) >> 14));
-      st.sc[i] = load_raw_scale<WK>(p.W.q8 + (eb >> 6), p.W.absmax + (eb >> 6), o.q[i], gi);
-    }
+    st.w[0] = *reinterpret_cast<const u32x4*>(p.W.codes + (eb >> 1) + o.w[0]);
+    const uint32_t blk = o.e >> 6;
     if (WK == kNF4DQ) {
-      const int64_t ng = (p.W.N * K + 16383) >> 14;  // number of groups
-#pragma unroll
-      for (int i = 0; i < kDxTab / kThreads; ++i) {
-        const int64_t g = g_lo + tid + kThreads * i;
-        st.c2[i] = p.W.c2[g < ng ? g : ng - 1];
-      }
-    }
-  }
-  if (o.bt >= 0) {
-    const char* base = reinterpret_cast<const char*>(p.B + n0r * p.r);
-    const int jb = 8 * (o.bt >> 3);
-    const int r = p.r;
-    if ((r & 7) == 0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const u32x4 v = sel4(jb < r, *reinterpret_cast<const u32x4*>(base + o.b[i]));
-#pragma unroll
-        for (int d = 0; d < 4; ++d) st.b[i][d] = v[d];
-      }
+      st.q = p.W.q8[(eb >> 6) + blk];
+      const int64_t g = (eb >> 14) + (((eb & 16383) + o.e) >> 14);
+      st.c2 = p.W.c2[g];
     } else {
+      st.q = __float_as_uint(p.W.absmax[(eb >> 6) + blk]);
+    }
+  }
+  const int r = p.r;
+  const uint16_t* bb = p.B + n0r * r;
+  const int cb = threadIdx.x & 3;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint16_t* row = reinterpret_cast<const uint16_t*>(base + o.b[i]);
+  for (int i = 0; i < RP / 32; ++i) {
+    const int j0 = 8 * (cb + 4 * i);
+    if (BV) {
+      st.b[i] = *reinterpret_cast<const u32x4*>(bb + o.b[i]);  // chunks past r masked when stored
+    } else {
+      uint32_t v[4];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int j = jb + 2 * d;
-          const uint32_t lo = j < r ? row[j - jb] : 0u;
-          const uint32_t hi = j + 1 < r ? row[j + 1 - jb] : 0u;
-          st.b[i][d] = lo | (hi << 16);
-        }
+      for (int d = 0; d < 4; ++d) {
+        const int j = j0 + 2 * d;
+        const uint32_t lo = bb[o.b[i] + (j < r ? 2 * d : 0)];
+        const uint32_t hi = bb[o.b[i] + (j + 1 < r ? 2 * d + 1 : 0)];
+        v[d] = (j < r ? lo : 0u) | ((j + 1 < r ? hi : 0u) << 16);
       }
+      st.b[i] = u32x4{v[0], v[1], v[2], v[3]};
     }
   }
 }
 
-// part (0..3): dequantise row `part` of the weight patch; the last part
-// transposes and stores the weight patch and the B^T patch.
 template <int WK, int RP>
-__device__ __forceinline__ void bwd_stage_part(const BwdStage<WK, RP>& st, uint32_t (&rows)[4][4],
-                                               uint16_t* tile, const float2* lut, const float* tab,
-                                               int bt, int part) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ float dx_scale(const DxStage<WK, RP>& st) {
+  if (WK == kNF4DQ) return (float)pin(st.q) * dq_step(pin(st.c2));
+  return __uint_as_float(pin(st.q));
+}
+
+// part (0..3) of writing a staged dX tile (a = its block scale)
+template <int WK, int RP>
+__device__ __forceinline__ void dx_stage_part(const DxStage<WK, RP>& st, const DxOffsets& o,
+                                              uint16_t* tile, const float2* lut, float a, int r,
+                                              int part) {
   if (WK == kDense) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) rows[part][d] = st.w[part][d];
+    *reinterpret_cast<u32x4*>(tile + o.st[part]) = st.w[part];
   } else {
-    const u32x4 v = deq8(st.w[part][0], raw_scale_value<WK>(st.sc[part], tab), lut);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) rows[part][d] = v[d];
+    *reinterpret_cast<u32x4*>(tile + o.st[part]) = deq8(st.w[0][part], a, lut);
   }
-  if (part == 3) {
-    store_transposed<4>(rows, tile + (8 * (tid & 15)) * kLP + 4 * (tid >> 4), kLP);
-    if (bt >= 0) store_transposed<8>(st.b, tile + (kTileI + 8 * (bt >> 3)) * kLP + 8 * (bt & 7), kLP);
-  }
+  if (part < RP / 32)
+    *reinterpret_cast<u32x4*>(tile + o.sb + 32 * part) =
+        sel4(8 * ((threadIdx.x & 3) + 4 * part) < r, pin(st.b[part]));
 }
 
-template <int WK, int RP>
-__device__ __forceinline__ void bwd_stage_steps(const BwdStage<WK, RP>& st, float* tab) {
-  if (WK == kNF4DQ) {
-#pragma unroll
-    for (int i = 0; i < kDxTab / kThreads; ++i) tab[threadIdx.x + kThreads * i] = dq_step(st.c2[i]);
-  }
-}
-
-template <int WK, int MS, int RP>
+template <int WK, int MS, int RP, bool BV>
 __global__ __launch_bounds__(kThreads) void dx_kernel(BwdParams p) {
   constexpr int JT = RP / 32;
-  constexpr int WROWS = kTileI + RP;
+  constexpr int P = DxPitch<RP>::P;
   constexpr int AROWS = 128 * MS;
-  __shared__ __attribute__((aligned(16))) uint16_t wt[2][WROWS * kLP];
+  __shared__ __attribute__((aligned(16))) uint16_t wt[2][kBK * P];
   __shared__ __attribute__((aligned(16))) uint16_t gt[2][AROWS * kLP];
   __shared__ float2 lut[256];
-  __shared__ float stab[2][WK == kNF4DQ ? kDxTab : 1];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
@@ -660,25 +684,35 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(BwdParams p) {
 
   if (WK != kDense) build_lut(lut, p.tab);
 
-  BwdOffsets o;
+  DxOffsets o;
   {
-    int64_t k = k0 + 8 * (tid & 15);
-    k = k < K ? k : K - 8;
+    const int r = p.r;
+    const int nt = tid >> 2, ct = tid & 3;
+    if (WK == kDense) {
+      const int c = tid & 15, nr = tid >> 4;
+      int64_t k = k0 + 8 * c;
+      k = k < K ? k : K - 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t e = (int64_t)(4 * (tid >> 4) + i) * K + k;  // relative to the step's rows
-      o.w[i] = WK == kDense ? (uint32_t)(e * 2) : (uint32_t)(e >> 1);
-      o.q[i] = (uint32_t)(e >> 6);
-      o.e[i] = (uint32_t)e;
-    }
-    o.bt = bt_task<RP>(tid);
-    const int bt = o.bt < 0 ? 0 : o.bt;
+      for (int i = 0; i < 4; ++i) {
+        o.w[i] = (uint32_t)(((int64_t)(nr + 16 * i) * K + k) * 2);
+        o.st[i] = (uint32_t)((nr + 16 * i) * P + 8 * (c ^ (nr & 3)));
+      }
+    } else {
+      int64_t k = k0 + 32 * ct;
+      k = k < K ? k : K - 32;
+      const int64_t e = (int64_t)nt * K + k;
+      o.w[0] = (uint32_t)(e >> 1);
+      o.e = (uint32_t)e;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int jb = 8 * (bt >> 3);
-      const int jc = jb < p.r ? jb : 0;
-      o.b[i] = (uint32_t)(((8 * (bt & 7) + i) * p.r + jc) * 2);
+      for (int q = 0; q < 4; ++q) o.st[q] = (uint32_t)(nt * P + 8 * ((4 * ct + q) ^ (nt & 3)));
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int j0 = 8 * (ct + 4 * i);
+      j0 = j0 < r ? j0 : 0;
+      o.b[i] = (uint32_t)(nt * r + j0);
+    }
+    o.sb = (uint32_t)(nt * P + 128 + 8 * (ct ^ (nt & 3)));
   }
   uint32_t go[4 * MS];
   act_offsets<MS>(go, N, m0, M);
@@ -689,42 +723,39 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(BwdParams p) {
   zero_acc(acc);
   zero_acc(uacc);
 
-  BwdStage<WK, RP> s0, s1;
+  DxStage<WK, RP> s0, s1;
   ActStage<MS> g0, g1;
-  uint32_t rows[4][4];
 
-  // stage s uses step-table slot s & 1
-  bwd_stage_load<WK, RP>(s0, p, o, 0, k0);
+  dx_stage_load<WK, RP, BV>(s0, p, o, 0);
   act_load<MS>(g0, gbase, go);
-  bwd_stage_steps<WK, RP>(s0, stab[0]);
-  __syncthreads();  // level table and stage-0 step table ready
+  __syncthreads();  // level table ready
+  {
+    const float a = WK != kDense ? dx_scale<WK, RP>(s0) : 0.0f;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    bwd_stage_part<WK, RP>(s0, rows, wt[0], lut, stab[0], o.bt, q);
-    act_part<MS>(g0, gt[0], q);
+    for (int q = 0; q < 4; ++q) {
+      dx_stage_part<WK, RP>(s0, o, wt[0], lut, a, p.r, q);
+      act_part<MS>(g0, gt[0], q);
+    }
   }
   const int64_t n1 = (int64_t)(RT > 1 ? 1 : 0) * kBK;
-  bwd_stage_load<WK, RP>(s1, p, o, n1, k0);
+  dx_stage_load<WK, RP, BV>(s1, p, o, n1);
   act_load<MS>(g1, gbase + 2 * n1, go);
-  bwd_stage_steps<WK, RP>(s1, stab[1]);
   __syncthreads();
 
   // step rt: loads stage rt+2 into (snxt, gnxt), runs the MFMAs of step rt on
-  // buffer rt & 1, writes stage rt+1 (scur, gcur) into the other buffer and
-  // the step table of stage rt+2 into slot rt & 1
-  auto step = [&](int rt, const BwdStage<WK, RP>& scur, const ActStage<MS>& gcur,
-                  BwdStage<WK, RP>& snxt, ActStage<MS>& gnxt) {
+  // buffer rt & 1 and writes stage rt+1 (scur, gcur) into the other buffer
+  auto step = [&](int rt, const DxStage<WK, RP>& scur, const ActStage<MS>& gcur,
+                  DxStage<WK, RP>& snxt, ActStage<MS>& gnxt) {
     const int64_t n2 = (int64_t)(rt + 2 < RT ? rt + 2 : RT - 1) * kBK;
-    bwd_stage_load<WK, RP>(snxt, p, o, n2, k0);
+    dx_stage_load<WK, RP, BV>(snxt, p, o, n2);
     act_load<MS>(gnxt, gbase + 2 * n2, go);
+    const float a = WK != kDense ? dx_scale<WK, RP>(scur) : 0.0f;
     const int b = rt & 1;
     uint16_t* wn = wt[b ^ 1];
     uint16_t* gn = gt[b ^ 1];
-    const float* tcur = stab[b ^ 1];
-    mfma_step<MS, JT>(wt[b], gt[b], wave, l32, h, acc, uacc, [&](int q) {
-      bwd_stage_part<WK, RP>(scur, rows, wn, lut, tcur, o.bt, q);
+    mfma_step_tr<MS, JT, P>(wt[b], gt[b], wave, lane, acc, uacc, [&](int q) {
+      dx_stage_part<WK, RP>(scur, o, wn, lut, a, p.r, q);
       act_part<MS>(gcur, gn, q);
-      if (q == 3) bwd_stage_steps<WK, RP>(snxt, stab[b]);
     });
     __syncthreads();
   };
@@ -910,21 +941,26 @@ int fwd_dispatch(const FwdParams& p, const lq_weight& W, int rp, hipStream_t st)
   return fwd_pick<kNF4, MULTI>(p, rp, st);
 }
 
-template <int WK, int MS, int RP>
+template <int WK, int MS, int RP, bool BV>
 int launch_dx(const BwdParams& p0, hipStream_t st) {
   BwdParams p = p0;
   p.k_tiles = (int)cdiv(p.W.K, kTileI);
   p.m_tiles = (int)cdiv(p.M, 128 * MS);
   const int blocks = p.k_tiles * p.m_tiles;
-  hipLaunchKernelGGL((dx_kernel<WK, MS, RP>), dim3(blocks), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((dx_kernel<WK, MS, RP, BV>), dim3(blocks), dim3(kThreads), 0, st, p);
   return hip_fail(hipGetLastError(), "dx_kernel launch");
+}
+
+template <int WK, int RP>
+int dx_pick_ms(const BwdParams& p, hipStream_t st) {
+  const bool big = big_tiles(p.M), bv = p.r % 8 == 0;
+  if (big) return bv ? launch_dx<WK, 2, RP, true>(p, st) : launch_dx<WK, 2, RP, false>(p, st);
+  return bv ? launch_dx<WK, 1, RP, true>(p, st) : launch_dx<WK, 1, RP, false>(p, st);
 }
 
 template <int WK>
 int dx_pick(const BwdParams& p, hipStream_t st) {
-  const bool big = big_tiles(p.M);
-  if (p.r <= 32) return big ? launch_dx<WK, 2, 32>(p, st) : launch_dx<WK, 1, 32>(p, st);
-  return big ? launch_dx<WK, 2, 64>(p, st) : launch_dx<WK, 1, 64>(p, st);
+  return p.r <= 32 ? dx_pick_ms<WK, 32>(p, st) : dx_pick_ms<WK, 64>(p, st);
 }
 
 }  // namespace
