@@ -156,9 +156,12 @@ def cpu_baseline(S):
                       f"layer on the NF4-dequantised weight, median of 3 ({t:.2f} s each)"}
 
 
-def decode_bench(S, torch, iters=200, copies=40):
-    """NF4 decode GEMV, cold weights: cycle over `copies` distinct NF4 copies
-    (copies x 8.65 MB > the 256 MB Infinity Cache)."""
+def decode_bench(S, torch, iters=200, copies=40, replays=20):
+    """NF4 decode (M = 1, 4, 16) with cold weights: a sequence of calls over
+    `copies` distinct NF4 copies (copies x 8.65 MB > the 256 MB Infinity
+    Cache).  Graph: the sequence captured once in a HIP graph and replayed
+    (launch and host overhead amortised); eager: back-to-back calls from
+    Python.  GB/s counts the 4-bit weight stream only."""
     import numpy as np
 
     from qlora_parameter_efficient_amd import workloads as wl
@@ -171,22 +174,36 @@ def decode_bench(S, torch, iters=200, copies=40):
             torch.bfloat16).to(S["dev"])
         Ym = torch.empty((m, N), dtype=torch.bfloat16, device=S["dev"])
         Tm = torch.empty((m, R), dtype=torch.float32, device=S["dev"])
+        wsm = torch.empty(lq.lq_workspace_size(lq.LQ_OP_FWD, m, N, K, R), dtype=torch.uint8,
+                          device=S["dev"])
         it = iter(range(10 ** 9))
 
-        def call_cold():
-            w = Ws[next(it) % copies]
-            lq.lq_lora_fwd(Xm, w, S["A"], S["B"], S["s"], T_out=Tm, Y=Ym)
+        def call(w):
+            lq.lq_lora_fwd(Xm, w, S["A"], S["B"], S["s"], T_out=Tm, ws=wsm, Y=Ym)
 
-        def call_warm():
-            lq.lq_lora_fwd(Xm, W, S["A"], S["B"], S["s"], T_out=Tm, Y=Ym)
+        def call_cold():
+            call(Ws[next(it) % copies])
 
         for _ in range(20):
             call_cold()
-        t_cold = cuda_time(call_cold, iters, torch)
-        t_warm = cuda_time(call_warm, iters, torch)
-        out[f"M{m}"] = {"us_per_call_cold": round(t_cold * 1e3, 2),
-                        "weight_stream_GBs_cold": round(NF4_STREAM_BYTES / (t_cold * 1e-3) / 1e9, 1),
-                        "us_per_call_warm": round(t_warm * 1e3, 2)}
+        t_eager = cuda_time(call_cold, iters, torch)
+        t_warm = cuda_time(lambda: call(W), iters, torch)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call(Ws[0])
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(g):
+            for w in Ws:
+                call(w)
+        g.replay()
+        t_graph = cuda_time(g.replay, replays, torch) / copies
+        out[f"M{m}"] = {"us_per_call_graph_cold": round(t_graph * 1e3, 2),
+                        "weight_stream_GBs_graph_cold": round(NF4_STREAM_BYTES / (t_graph * 1e-3) / 1e9, 1),
+                        "us_per_call_eager_cold": round(t_eager * 1e3, 2),
+                        "us_per_call_eager_warm": round(t_warm * 1e3, 2)}
+        del g
     del Ws
     return out
 

@@ -147,9 +147,9 @@ int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
  *   Y  device M x N of dt (written, not accumulated);
  *   T_out  optional device M x r float32: receives T = X A^T for lq_lora_bwd.
  *   ws / ws_bytes: device workspace of lq_workspace_size(LQ_OP_FWD, M, N, K,
- *   r, 0) bytes (M * r floats), needed only when T_out is NULL and the call
- *   takes the float32 or the decode path, which keep T in memory between two
- *   kernels; otherwise ws may be NULL.
+ *   r, 0) bytes, needed by the decode path (dt = LQ_BF16, M <= 16: 8 M r
+ *   floats of partial sums of T) and by the float32 path when T_out is NULL
+ *   (M r floats of T); otherwise ws may be NULL.
  *   dt = LQ_BF16: bf16 inputs, float32 accumulation, bf16 RNE output; W0 dense
  *   bf16 or NF4 (dequantised in registers / LDS, never written to memory).
  *   Requires K % 64 == 0, N % 64 == 0, N, K <= 65536, M*K and M*N < 2^31,

@@ -123,8 +123,8 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
                          int32_t n_adapters) {
   if (M < 0 || N < 0 || K < 0 || r < 0) return 0;
   switch (op) {
-    case LQ_OP_FWD:
-      return (size_t)(M * r) * 4;
+    case LQ_OP_FWD:  // float32 T, or the decode path's partial sums of T
+      return (size_t)((M <= kDecodeMaxM ? kTParts : 1) * M * r) * 4;
     case LQ_OP_BWD:
       return bwd_ws_bytes(M, N, K, r);
     case LQ_OP_FWD_MULTI:
@@ -174,19 +174,23 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
   if (dt == LQ_BF16 && (rc = check_bf16_rows(M, W0))) return rc;
   if (M == 0) return LQ_OK;
   REQUIRE(X && A && B && Y, LQ_ERR_INVALID_ARG, "X, A, B or Y is NULL");
-  float* T = T_out;
-  const bool path_keeps_t = dt == LQ_F32 || M <= kDecodeMaxM;  // T crosses two kernels
-  if (!T && path_keeps_t) {
-    const size_t need = (size_t)(M * r) * 4;
-    REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE,
-            "workspace %zu bytes, need %zu", ws_bytes, need);
-    T = (float*)ws;
-  }
-  if (dt == LQ_F32)
+  if (dt == LQ_F32) {  // T crosses two kernels
+    float* T = T_out;
+    if (!T) {
+      const size_t need = (size_t)(M * r) * 4;
+      REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE,
+              "workspace %zu bytes, need %zu", ws_bytes, need);
+      T = (float*)ws;
+    }
     return f32_lora_fwd((const float*)X, M, *W0, (const float*)A, (const float*)B, r, scale,
                         (float*)Y, T, stream);
-  if (M <= kDecodeMaxM)
-    return dispatch::decode_fwd(X, M, *W0, A, B, r, scale, Y, T, stream);
+  }
+  if (M <= kDecodeMaxM) {  // partial sums of T cross two kernels
+    const size_t need = (size_t)(kTParts * M * r) * 4;
+    REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE,
+            "workspace %zu bytes, need %zu", ws_bytes, need);
+    return dispatch::decode_fwd(X, M, *W0, A, B, r, scale, Y, T_out, (float*)ws, stream);
+  }
   return dispatch::bf16_fwd(X, M, *W0, A, B, r, scale, Y, T_out, stream);
 }
 

@@ -108,8 +108,9 @@ struct GemvParams {
   const uint16_t* X;  // M x K
   int64_t M;
   WeightArgs W;
-  const float* T;     // M x r
+  const float* Tp;    // kTParts x M x r partial sums of X A^T
   const uint16_t* B;  // N x r
+  float* T_out;       // M x r or NULL (written by workgroup 0)
   int32_t r;
   float s;
   uint16_t* Y;        // M x N
@@ -117,138 +118,189 @@ struct GemvParams {
 };
 
 // Granule = 32 consecutive weights of one row (16 code bytes, half an NF4
-// block).  Lane (q, l16) of wave w takes granules 4 t + q for t = w, w + 4, ...
-// CH of them at a time: all their loads (codes, block constants, activations)
-// are issued before any is used, so each lane keeps CH 16-byte weight loads in
-// flight.
+// block).  A workgroup of 16 waves owns 16 output rows; lane (q, l16) of wave
+// w takes row n0 + l16 and granules 4 t + q for t = w, w + 16, ..., CH of them
+// per round, all loads issued from clamped addresses before any is used.
+// Each granule feeds four v_mfma_f32_16x16x32_bf16 (X padded to 16 rows, the
+// 32 reduction elements of a lane relabelled so that they are contiguous) on
+// its own accumulator chain.  The inputs of the rank-r expand (the T partial
+// sums and this workgroup's 16 rows of B) are loaded into registers before
+// the weight stream and only summed and staged in LDS after it; the 16 wave
+// partials are added through LDS.
+constexpr int kGemvWaves = 16;
+
 template <int WK>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
-  constexpr int CH = WK == 0 ? 4 : 8;
+__global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
+  constexpr int CH = 2;
+  constexpr int NT = 64 * kGemvWaves;
   __shared__ float2 lut[256];
-  __shared__ f32x4 part[4][64];
+  __shared__ f32x4 part[kGemvWaves][64];
+  __shared__ float tT[16 * 64];
+  __shared__ float tB[16 * 64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, q = lane >> 4;
   const int64_t N = p.W.N, K = p.W.K, M = p.M;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  if (WK != 0) {
-    build_lut(lut, p.tab);
-    __syncthreads();
+  const int r = p.r;
+
+  // expand inputs: element tid of T (M x r <= 1024) and of B rows n0.. (16 x r)
+  const int ET = (int)M * r, EB = 16 * r;
+  float tp[kTParts];
+  uint32_t braw = 0u;
+#pragma unroll
+  for (int b = 0; b < kTParts; ++b) tp[b] = 0.0f;
+  if (tid < ET) {  // threads without an element issue no load
+#pragma unroll
+    for (int b = 0; b < kTParts; ++b) tp[b] = p.Tp[b * ET + tid];
   }
+  if (tid < EB) braw = p.B[n0 * r + tid];
+
+  if (WK != kDense) build_lut(lut, p.tab);
   const int64_t n = n0 + l16;  // A-operand row of this lane (N % 16 == 0)
   const bool mrow = l16 < M;   // B-operand column (activation row) of this lane
   const int64_t xm = mrow ? l16 : 0;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  ScaleCache sc;
-  sc.init();
+  f32x4 acc[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const int64_t G = K / 32;
   const int64_t steps = (G + 3) / 4;
-  for (int64_t base = wave; base < steps; base += 4 * CH) {
-    u32x4 wraw[CH][WK == 0 ? 4 : 1];
-    ScaleRaw sr[CH];
+  if (WK != kDense) __syncthreads();  // level table
+  for (int64_t base = wave; base < steps; base += kGemvWaves * CH) {
+    u32x4 wraw[CH][WK == kDense ? 4 : 1];
+    uint32_t sq[CH];
+    float sc2[CH];
     u32x4 xf[CH][4];
     bool ok[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int64_t t = base + 4 * i;
+      const int64_t t = base + kGemvWaves * i;
       const int64_t g = 4 * t + q;
       ok[i] = t < steps && g < G;
       const int64_t k = ok[i] ? 32 * g : 0;
-      if (WK == 0) {
+      const int64_t e = n * K + k;
+      if (WK == kDense) {
 #pragma unroll
         for (int d = 0; d < 4; ++d)
-          wraw[i][d] = ok[i] ? *reinterpret_cast<const u32x4*>(p.W.dense + n * K + k + 8 * d)
-                             : u32x4{0, 0, 0, 0};
+          wraw[i][d] = *reinterpret_cast<const u32x4*>(p.W.dense + e + 8 * d);
       } else {
-        const int64_t e = n * K + k;
-        if (ok[i]) {
-          wraw[i][0] = *reinterpret_cast<const u32x4*>(p.W.codes + (e >> 1));
-          sr[i] = load_scale(p.W, e >> 6);
+        wraw[i][0] = *reinterpret_cast<const u32x4*>(p.W.codes + (e >> 1));
+        if (WK == kNF4DQ) {
+          sq[i] = p.W.q8[e >> 6];
+          sc2[i] = p.W.c2[e >> 14];
         } else {
-          wraw[i][0] = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-          sr[i] = ScaleRaw{0u, 0.0f, -2};
+          sq[i] = __float_as_uint(p.W.absmax[e >> 6]);
         }
       }
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
-        xf[i][d] = (mrow && ok[i]) ? *reinterpret_cast<const u32x4*>(p.X + xm * K + k + 8 * d)
-                                   : u32x4{0, 0, 0, 0};
+      for (int d = 0; d < 4; ++d) xf[i][d] = u32x4{0u, 0u, 0u, 0u};
+      if (mrow) {  // lanes without an activation row issue no load
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          xf[i][d] = *reinterpret_cast<const u32x4*>(p.X + xm * K + k + 8 * d);
+      }
     }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      if (WK == 0) {
+      if (WK == kDense) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) acc = mfma16(wraw[i][d], xf[i][d], acc);
+        for (int d = 0; d < 4; ++d) acc[i] = mfma16(wraw[i][d], sel4(ok[i], xf[i][d]), acc[i]);
       } else {
-        const float a = sr[i].g == -2 ? 0.0f : sc.finish(p.W, sr[i]);
+        const float a = WK == kNF4DQ ? (float)sq[i] * dq_step(sc2[i]) : __uint_as_float(sq[i]);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) acc = mfma16(deq8(wraw[i][0][d], a, lut), xf[i][d], acc);
+        for (int d = 0; d < 4; ++d)
+          acc[i] = mfma16(deq8(wraw[i][0][d], a, lut), sel4(ok[i], xf[i][d]), acc[i]);
       }
     }
   }
+  // stage the expand inputs (their loads finished long ago)
+  if (tid < ET) {
+    float t = 0.0f;
+#pragma unroll
+    for (int b = 0; b < kTParts; ++b) t += tp[b];
+    const int m = tid / r, j = tid - m * r;
+    tT[m * 64 + j] = t;
+    if (blockIdx.x == 0 && p.T_out) p.T_out[tid] = t;
+  }
+  if (tid < EB) {
+    const int nn = tid / r, j = tid - nn * r;
+    tB[nn * 64 + j] = bf16_to_f32((uint16_t)braw);
+  }
   // acc lane l: rows n0 + 4 q + i, column m = l16 (16x16 accumulator layout)
-  part[wave][lane] = acc;
+  f32x4 a0 = acc[0];
+#pragma unroll
+  for (int i = 1; i < CH; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) a0[v] += acc[i][v];
+  part[wave][lane] = a0;
   __syncthreads();
   if (wave != 0) return;
   f32x4 sum = part[0][lane];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) {
+  for (int w = 1; w < kGemvWaves; ++w) {
     const f32x4 o = part[w][lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sum[i] += o[i];
   }
   if (!mrow) return;
-  const int64_t m = l16;
-  const int r = p.r;
+  const int m = l16;
+  float d[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < r; ++j) {
+    const float t = tT[m * 64 + j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = fmaf(t, tB[(4 * q + i) * 64 + j], d[i]);
+  }
   float y[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t nn = n0 + 4 * q + i;
-    float d = 0.0f;
-    for (int j = 0; j < r; ++j) d = fmaf(p.T[m * r + j], bf16_to_f32(p.B[nn * r + j]), d);
-    y[i] = sum[i] + p.s * d;
-  }
+  for (int i = 0; i < 4; ++i) y[i] = sum[i] + p.s * d[i];
   *reinterpret_cast<u32x2*>(p.Y + m * N + n0 + 4 * q) =
       u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
 }
 
-// T = X A^T for M <= 16 rows in one workgroup of 16 waves.  Granules of 32
-// reduction elements go round-robin to the waves; each wave runs
+// Partial sums of T = X A^T for M <= 16 rows: workgroup b reduces granules
+// [b G / kTParts, (b + 1) G / kTParts) of the G = K / 32 granules of 32
+// reduction elements; its four waves take every fourth granule and run
 // v_mfma_f32_16x16x32_bf16 with A rows as the A operand (16 per tile, JT
-// tiles) and the activation rows as the B operand, all loads of a wave issued
-// up front; the 16 partial tiles are added through LDS.
+// tiles) and the activation rows as the B operand; the wave partials are added
+// through LDS and Tp[b] (M x r) is written.  The decode GEMV adds the
+// kTParts partials in a fixed order.
 template <int JT>
-__global__ __launch_bounds__(1024) void tsmall_kernel(const uint16_t* __restrict__ X, int64_t M,
-                                                      int64_t K, const uint16_t* __restrict__ A,
-                                                      int r, float* __restrict__ T) {
-  constexpr int CH = 8;
-  __shared__ f32x4 part[16][JT][64];
+__global__ __launch_bounds__(kThreads) void tpart_kernel(const uint16_t* __restrict__ X, int64_t M,
+                                                         int64_t K, const uint16_t* __restrict__ A,
+                                                         int r, float* __restrict__ Tp) {
+  constexpr int CH = 4;
+  __shared__ f32x4 part[4][JT][64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, q = lane >> 4;
   const bool mrow = l16 < M;
   const int64_t xm = mrow ? l16 : 0;
   const int64_t G = K / 32;
+  const int64_t g0 = (int64_t)blockIdx.x * G / kTParts, g1 = (int64_t)(blockIdx.x + 1) * G / kTParts;
   f32x4 acc[JT];
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t base = wave; base < G; base += 16 * CH) {
+  for (int64_t gb = g0 + wave; gb < g1; gb += 4 * CH) {
     u32x4 af[CH][JT], xf[CH];
+    bool ok[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int64_t g = base + 16 * i;
-      const bool ok = g < G;
-      const int64_t k = ok ? 32 * g + 8 * q : 0;
+      const int64_t g = gb + 4 * i;
+      ok[i] = g < g1;
+      const int64_t k = 32 * (ok[i] ? g : g0) + 8 * q;
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) {
         const int j = 16 * jt + l16;
-        af[i][jt] = (ok && j < r) ? *reinterpret_cast<const u32x4*>(A + (int64_t)j * K + k)
-                                  : u32x4{0, 0, 0, 0};
+        af[i][jt] = *reinterpret_cast<const u32x4*>(A + (int64_t)(j < r ? j : 0) * K + k);
       }
-      xf[i] = (ok && mrow) ? *reinterpret_cast<const u32x4*>(X + xm * K + k) : u32x4{0, 0, 0, 0};
+      xf[i] = u32x4{0u, 0u, 0u, 0u};
+      if (mrow) xf[i] = *reinterpret_cast<const u32x4*>(X + xm * K + k);
     }
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
+    for (int i = 0; i < CH; ++i) {
+      const u32x4 x = sel4(ok[i], xf[i]);
 #pragma unroll
-      for (int jt = 0; jt < JT; ++jt) acc[jt] = mfma16(af[i][jt], xf[i], acc[jt]);
+      for (int jt = 0; jt < JT; ++jt)
+        acc[jt] = mfma16(sel4(16 * jt + l16 < r, af[i][jt]), x, acc[jt]);
+    }
   }
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) part[wave][jt][lane] = acc[jt];
@@ -257,17 +309,19 @@ __global__ __launch_bounds__(1024) void tsmall_kernel(const uint16_t* __restrict
   if (tid < JT * 64) {
     const int jt = tid >> 6, ln = tid & 63;
     f32x4 s4 = part[0][jt][ln];
-    for (int w = 1; w < 16; ++w) {
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
       const f32x4 o = part[w][jt][ln];
 #pragma unroll
       for (int i = 0; i < 4; ++i) s4[i] += o[i];
     }
     const int m = ln & 15, qq = ln >> 4;
     if (m < M) {
+      float* out = Tp + (int64_t)blockIdx.x * M * r + m * r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 16 * jt + 4 * qq + i;
-        if (j < r) T[m * r + j] = s4[i];
+        if (j < r) out[j] = s4[i];
       }
     }
   }
@@ -288,41 +342,50 @@ int u_only(const void* dY, int64_t M, int64_t N, const void* B, int64_t r, float
 }
 
 int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
-               int64_t r, float s, void* Y, float* T, hipStream_t st) {
+               int64_t r, float s, void* Y, float* T_out, float* Tp, hipStream_t st) {
   const int jt = (int)((r + 15) / 16);
   const uint16_t* Xh = (const uint16_t*)X;
   const uint16_t* Ah = (const uint16_t*)A;
+  const dim3 tg(kTParts), tb(kThreads);
   switch (jt) {
     case 1:
-      hipLaunchKernelGGL(tsmall_kernel<1>, dim3(1), dim3(1024), 0, st, Xh, M, W.K, Ah, (int)r, T);
+      hipLaunchKernelGGL(tpart_kernel<1>, tg, tb, 0, st, Xh, M, W.K, Ah, (int)r, Tp);
       break;
     case 2:
-      hipLaunchKernelGGL(tsmall_kernel<2>, dim3(1), dim3(1024), 0, st, Xh, M, W.K, Ah, (int)r, T);
+      hipLaunchKernelGGL(tpart_kernel<2>, tg, tb, 0, st, Xh, M, W.K, Ah, (int)r, Tp);
       break;
     case 3:
-      hipLaunchKernelGGL(tsmall_kernel<3>, dim3(1), dim3(1024), 0, st, Xh, M, W.K, Ah, (int)r, T);
+      hipLaunchKernelGGL(tpart_kernel<3>, tg, tb, 0, st, Xh, M, W.K, Ah, (int)r, Tp);
       break;
     default:
-      hipLaunchKernelGGL(tsmall_kernel<4>, dim3(1), dim3(1024), 0, st, Xh, M, W.K, Ah, (int)r, T);
+      hipLaunchKernelGGL(tpart_kernel<4>, tg, tb, 0, st, Xh, M, W.K, Ah, (int)r, Tp);
       break;
   }
-  int e = hip_fail(hipGetLastError(), "tsmall launch");
+  int e = hip_fail(hipGetLastError(), "tpart launch");
   if (e) return e;
   GemvParams p;
-  p.X = (const uint16_t*)X;
+  p.X = Xh;
   p.M = M;
   p.W = weight_args(W);
-  p.T = T;
+  p.Tp = Tp;
   p.B = (const uint16_t*)B;
+  p.T_out = T_out;
   p.r = (int32_t)r;
   p.s = s;
   p.Y = (uint16_t*)Y;
   p.tab = nf4_table();
-  const unsigned blocks = (unsigned)(W.N / 16);
-  if (W.kind == LQ_WEIGHT_DENSE)
-    hipLaunchKernelGGL(gemv_kernel<0>, dim3(blocks), dim3(kThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL(gemv_kernel<1>, dim3(blocks), dim3(kThreads), 0, st, p);
+  const dim3 grid((unsigned)(W.N / 16)), block(64 * kGemvWaves);
+  switch (weight_format(W)) {
+    case kDense:
+      hipLaunchKernelGGL(gemv_kernel<kDense>, grid, block, 0, st, p);
+      break;
+    case kNF4DQ:
+      hipLaunchKernelGGL(gemv_kernel<kNF4DQ>, grid, block, 0, st, p);
+      break;
+    default:
+      hipLaunchKernelGGL(gemv_kernel<kNF4>, grid, block, 0, st, p);
+      break;
+  }
   return hip_fail(hipGetLastError(), "gemv launch");
 }
 

@@ -27,6 +27,19 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f3
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Weight formats, fixed at compile time: dense bf16, NF4 with 8-bit double
+// quantised constants, NF4 with float32 absmax.
+constexpr int kDense = 0, kNF4DQ = 1, kNF4 = 2;
+
+inline int weight_format(const lq_weight& w) {
+  if (w.kind == LQ_WEIGHT_DENSE) return kDense;
+  return w.double_quant ? kNF4DQ : kNF4;
+}
+
+__device__ __forceinline__ u32x4 sel4(bool ok, const u32x4& v) {
+  return ok ? v : u32x4{0u, 0u, 0u, 0u};
+}
+
 // NF4 weight descriptor as the kernels see it.
 struct WeightArgs {
   const uint16_t* dense;

@@ -22,6 +22,9 @@ int f32_lora_bwd(const float* dY, const float* X, int64_t M, const lq_weight& W,
 int f32_lora_merge(const lq_weight& W, const float* A, const float* B, int64_t r, float s,
                    float* Wout, hipStream_t st);
 
+// Partial sums of T = X A^T kept by the decode path.
+constexpr int kTParts = 8;
+
 namespace dispatch {
 
 size_t grad_partial_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
@@ -29,8 +32,10 @@ size_t multi_ws_bytes(int64_t T_tokens, int64_t r, int32_t n_adapters);
 
 int bf16_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
              int64_t r, float s, void* Y, float* T_out, hipStream_t st);
+// Decode path (M <= 16): T partial sums (kTParts x M x r floats) go to Tp;
+// T_out (optional) receives T.
 int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
-               int64_t r, float s, void* Y, float* T, hipStream_t st);
+               int64_t r, float s, void* Y, float* T_out, float* Tp, hipStream_t st);
 int bf16_bwd(const void* dY, const void* X, int64_t M, const lq_weight& W, const void* A,
              const void* B, int64_t r, float s, const float* T_saved, void* dX, float* dA,
              float* dB, int accumulate, void* ws, hipStream_t st);

@@ -48,10 +48,6 @@ constexpr int kTileI = 128;   // weight-side outputs per workgroup
 constexpr int kBK = 64;       // reduction elements per step
 constexpr int kLP = kBK + 8;  // LDS row pitch (bf16): 144 bytes, conflict-free 16-byte reads
 
-__device__ __forceinline__ u32x4 sel4(bool ok, const u32x4& v) {
-  return ok ? v : u32x4{0u, 0u, 0u, 0u};
-}
-
 // Four consecutive bf16 of a row (8 bytes) or zeros, with element masking.
 __device__ __forceinline__ u32x2 load4_masked(const uint16_t* row, int j0, int jmax) {
   if (j0 + 4 <= jmax && ((reinterpret_cast<uintptr_t>(row + j0) & 7) == 0))
@@ -184,10 +180,6 @@ struct FwdParams {
 };
 
 constexpr int kFwdTab = 1024;  // second-level steps of one tile's 128 rows (K <= 65536)
-
-// Weight formats, fixed at compile time: dense bf16, NF4 with 8-bit double
-// quantised constants, NF4 with float32 absmax.
-constexpr int kDense = 0, kNF4DQ = 1, kNF4 = 2;
 
 // Block constant as loaded (8-bit value, or float32 absmax bits) and its
 // second-level group relative to the step table; turned into the scale a'

@@ -202,7 +202,9 @@ def lq_lora_fwd(X, W0, A, B, scale, T_out=None, ws=None, Y=None):
     if Y is None:
         Y = torch.empty((M, ws_struct.N), dtype=X.dtype, device=X.device)
     r = A.shape[0]
-    need = 0 if T_out is not None else lq_workspace_size(LQ_OP_FWD, M, ws_struct.N, ws_struct.K, r)
+    decode = dt == LQ_BF16 and M <= 16
+    need = (lq_workspace_size(LQ_OP_FWD, M, ws_struct.N, ws_struct.K, r)
+            if (T_out is None or decode) else 0)
     if ws is None and need:
         ws = _ws(need, X.device)
     _check(lib().lq_lora_fwd(_ptr(X), M, ctypes.byref(ws_struct), _ptr(A), _ptr(B), r, scale, dt,

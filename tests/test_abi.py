@@ -48,6 +48,7 @@ def test_check_segments():
 
 def test_workspace_sizes():
     assert lq.lq_workspace_size(lq.LQ_OP_FWD, 64, 256, 256, 8) == 64 * 8 * 4
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 16, 256, 256, 8) == 8 * 16 * 8 * 4  # decode partials
     assert lq.lq_workspace_size(lq.LQ_OP_BWD, 2048, 4096, 4096, 16) >= 2 * 2048 * 16 * 4
     assert lq.lq_workspace_size(lq.LQ_OP_FWD_MULTI, 1000, 4096, 4096, 16, 4) >= 1000 * 4
 
@@ -81,7 +82,7 @@ def test_argument_errors_launch_nothing():
     # dtype mismatch between descriptor and call
     assert _fwd(_weight(dtype=lq.LQ_F32)) == -1
     # missing workspace when T_out is NULL (M > 0)
-    assert _fwd(_weight(), M=8) == -3               # decode path keeps T in ws
+    assert _fwd(_weight(), M=8) == -3               # decode path keeps partial sums of T in ws
     assert "workspace" in lq.lq_last_error()
     # M = 0 is a no-op
     assert _fwd(_weight(), M=0) == 0
