@@ -6,13 +6,16 @@
 //
 // Both have the form out[j][c] = s * sum_m V[m][j] Z[m][c] with V = U or T
 // (M x r float32, from the dX / forward kernels) and Z = X or dY (M x C bf16).
-// They are skinny (r <= 64 outputs per column) and HBM-bound on Z.  Each
-// workgroup streams a 64-row slab of Z at a time with coalesced 16-byte
-// loads, transposes it in registers into LDS so the row index m becomes the
-// MFMA reduction index, and accumulates a 128-column x r block; the rows are
-// split over several workgroups, whose partial sums land in a workspace and
-// are added in a fixed order by a second small kernel (deterministic, no
-// atomics), which also applies s and the accumulate flag.
+// They are skinny (r <= 64 outputs per column) and HBM-bound on Z.  Both run
+// in one launch (the grid holds the dA tiles, then the dB tiles).  Each
+// workgroup issues the coalesced 16-byte loads of up to four 64-row slabs of
+// Z (and the matching rows of V) at once, stores each slab in LDS in storage
+// order, reads it back as MFMA operands with the row index m as the reduction
+// index, and accumulates a 128-column x r block;
+// the rows are split over several workgroups, whose partial sums land in a
+// workspace and are added in a fixed order by one small finishing kernel for
+// both outputs (deterministic, no atomics), which also applies s and the
+// accumulate flag.
 #include "device_util.h"
 #include "dispatch.h"
 
@@ -21,31 +24,63 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTileC = 128;
+constexpr int kChunk = 4;  // 64-row steps whose loads are in flight together
 
-struct GradParams {
+// One reduction job: out[j][c] = s * sum_m V[m][j] Z[m][c] over a range of
+// rows, for one 128-column tile of Z.
+struct GradJob {
   const uint16_t* Z;   // M x C bf16
   const float* V;      // M x r float32
-  int64_t M, C;
-  int32_t r;
+  int64_t C;
+  int32_t c_tiles;
   int32_t splits;
   int64_t rows_per_split;  // multiple of 64
   float* P;            // splits x r x C partial sums
 };
 
+struct GradParams {
+  GradJob job[2];
+  int64_t M;
+  int32_t r;
+  int32_t blocks0;     // workgroups of job 0; the rest belong to job 1
+};
+
+// LDS tile of one 64-row step in storage order: row m holds Z[m][c0 .. c0+127]
+// then V[m][0 .. RP-1] (bf16), 16-byte chunk q at q ^ (m & 3), pitch 20 or 28
+// chunks.  MFMA operands (one column, eight consecutive rows m) come from the
+// transposing LDS read ds_read_b64_tr_b16 (in each 16-lane group lane c
+// addresses row c / 4, columns 4 (c % 4) ..; lane i receives column i of the
+// four rows), so neither operand is transposed in registers.
 template <int RP>
+struct GradPitch {
+  static constexpr int P = RP == 32 ? 160 : 224;
+};
+
+typedef short s16x4g __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 lds_tr(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4g* lds_ptr;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p)));
+}
+
+template <int RP, bool V4>
 __global__ __launch_bounds__(kThreads) void grad_kernel(GradParams p) {
   constexpr int JT = RP / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t zt[2][kTileC * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][RP * kPitch];
+  constexpr int PT = GradPitch<RP>::P;
+  constexpr int NV = RP / 16;  // float4 chunks of V per thread per step (64 rows x RP / 4)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][64 * PT];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
-  const int c_tiles = (int)cdiv(p.C, kTileC);
-  const int tile = xcd_tile(blockIdx.x, c_tiles * p.splits);
-  const int tc = tile % c_tiles, split = tile / c_tiles;
+  const bool second = (int)blockIdx.x >= p.blocks0;
+  const GradJob& jb = second ? p.job[1] : p.job[0];
+  const int bid = second ? (int)blockIdx.x - p.blocks0 : (int)blockIdx.x;
+  const int tl = xcd_tile(bid, jb.c_tiles * jb.splits);
+  const int tc = tl % jb.c_tiles, split = tl / jb.c_tiles;
+  const int64_t C = jb.C, M = p.M;
   const int64_t c0 = (int64_t)tc * kTileC;
-  const int64_t mbeg = (int64_t)split * p.rows_per_split;
-  int64_t mend = mbeg + p.rows_per_split;
-  mend = mend < p.M ? mend : p.M;
+  const int64_t mbeg = (int64_t)split * jb.rows_per_split;
+  int64_t mend = mbeg + jb.rows_per_split;
+  mend = mend < M ? mend : M;
   const int steps = mend > mbeg ? (int)cdiv(mend - mbeg, 64) : 0;
   const int r = p.r;
 
@@ -55,83 +90,101 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(GradParams p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[jt][v] = 0.0f;
 
-  // staging: thread covers columns c0 + 8 (tid & 15) .. +7 of rows 4 (tid >> 4) .. +3
-  const int cc = tid & 15, mg = tid >> 4;
-  const int64_t ccol = c0 + 8 * cc;
-  auto load = [&](int64_t m0r, uint32_t (&raw)[16]) {
+  // Z staging: chunk zc = tid & 15 of rows zr + 16 i (columns past C clamped,
+  // zeroed when stored); V staging: row vr = tid / 4, float4 chunks
+  // vc = tid % 4 + 4 i (j = 4 vc ..); rows past mend are zeroed when stored.
+  const int zc = tid & 15, zr = tid >> 4;
+  int64_t zcol = c0 + 8 * zc;
+  const bool zok = zcol < C;
+  zcol = zok ? zcol : C - 8;
+  const int vr = tid >> 2;
+  uint32_t zst[4], vst[NV];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = zr + 16 * i;
+    zst[i] = (uint32_t)(m * PT + 8 * (zc ^ (m & 3)));
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vc = (tid & 3) + 4 * i;  // float4 chunk: half of 16-byte chunk 16 + vc / 2
+    vst[i] = (uint32_t)(vr * PT + 8 * ((16 + (vc >> 1)) ^ (vr & 3)) + 4 * (vc & 1));
+  }
+  struct Stage {
+    u32x4 z[4];
+    f32x4 v[NV];
+  };
+  auto load = [&](int64_t m0r, Stage& st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0r + 4 * mg + i;
-      u32x4 v = u32x4{0, 0, 0, 0};
-      if (m < mend && ccol < p.C) v = *reinterpret_cast<const u32x4*>(p.Z + m * p.C + ccol);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) raw[4 * i + d] = v[d];
+      int64_t m = m0r + zr + 16 * i;
+      m = m < mend ? m : mend - 1;
+      st.z[i] = *reinterpret_cast<const u32x4*>(jb.Z + m * C + zcol);
     }
-  };
-  auto store = [&](const uint32_t (&raw)[16], uint16_t* dst) {
+    int64_t m = m0r + vr;
+    m = m < mend ? m : mend - 1;
+    const float* row = jb.V + m * r;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const u32x2 ev{pair_lo(raw[d], raw[4 + d]), pair_lo(raw[8 + d], raw[12 + d])};
-      const u32x2 od{pair_hi(raw[d], raw[4 + d]), pair_hi(raw[8 + d], raw[12 + d])};
-      *reinterpret_cast<u32x2*>(dst + (8 * cc + 2 * d) * kPitch + 4 * mg) = ev;
-      *reinterpret_cast<u32x2*>(dst + (8 * cc + 2 * d + 1) * kPitch + 4 * mg) = od;
-    }
-  };
-  // V^T tile: thread owns row m = tid % 64, columns j = tid / 64 + 4 i; the
-  // values are loaded with the Z prefetch and stored after the MFMAs.
-  const int vm = tid & 63, vj0 = tid >> 6;
-  auto load_v = [&](int64_t m0r, float (&vv)[RP / 4]) {
-    const bool ok = m0r + vm < mend;
-    const float* row = p.V + (m0r + vm) * r;
+    for (int i = 0; i < NV; ++i) {
+      const int j0 = 4 * ((tid & 3) + 4 * i);
+      if (V4) {
+        st.v[i] = *reinterpret_cast<const f32x4*>(row + (j0 < r ? j0 : 0));
+      } else {
 #pragma unroll
-    for (int i = 0; i < RP / 4; ++i) {
-      const int j = vj0 + 4 * i;
-      vv[i] = (ok && j < r) ? row[j] : 0.0f;
-    }
-  };
-  auto store_v = [&](const float (&vv)[RP / 4], uint16_t* dst) {
-#pragma unroll
-    for (int i = 0; i < RP / 4; ++i) dst[(vj0 + 4 * i) * kPitch + vm] = f32_to_bf16(vv[i]);
-  };
-
-  uint32_t raw[16];
-  float vv[RP / 4];
-  if (steps > 0) {
-    load(mbeg, raw);
-    load_v(mbeg, vv);
-    store(raw, zt[0]);
-    store_v(vv, vt[0]);
-  }
-  __syncthreads();
-  for (int st = 0; st < steps; ++st) {
-    const int buf = st & 1;
-    const bool more = st + 1 < steps;
-    const int64_t m1 = mbeg + (int64_t)(st + 1) * 64;
-    if (more) {
-      load(m1, raw);
-      load_v(m1, vv);
-    }
-    const uint16_t* z = zt[buf];
-    const uint16_t* v = vt[buf];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const u32x4 zf =
-          *reinterpret_cast<const u32x4*>(z + (32 * wave + l32) * kPitch + 32 * h + 8 * s);
-#pragma unroll
-      for (int jt = 0; jt < JT; ++jt) {
-        const u32x4 vf =
-            *reinterpret_cast<const u32x4*>(v + (32 * jt + l32) * kPitch + 32 * h + 8 * s);
-        acc[jt] = mfma32(zf, vf, acc[jt]);
+        for (int e = 0; e < 4; ++e) st.v[i][e] = row[j0 + e < r ? j0 + e : 0];
       }
     }
-    if (more) {
-      store(raw, zt[buf ^ 1]);
-      store_v(vv, vt[buf ^ 1]);
+  };
+  auto store = [&](int64_t m0r, const Stage& st, uint16_t* t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = zok && m0r + zr + 16 * i < mend;
+      *reinterpret_cast<u32x4*>(t + zst[i]) = sel4(ok, st.z[i]);
+    }
+    const bool vok = m0r + vr < mend;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j0 = 4 * ((tid & 3) + 4 * i);
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (vok && j0 + e < r) ? st.v[i][e] : 0.0f;
+      *reinterpret_cast<u32x2*>(t + vst[i]) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+  };
+  // operand reads: lane (g = lane / 16, c = lane % 16)
+  const int c = lane & 15, g = lane >> 4;
+  const int rbase = (32 * h + (c >> 2)) * PT + 8 * ((2 * (g & 1) + ((c >> 1) & 1)) ^ (c >> 2)) + 4 * (c & 1);
+  auto frag = [&](const uint16_t* t, int col32, int s) {
+    const uint16_t* q = t + rbase + 8 * s * PT + 32 * col32;
+    const u32x2 lo = lds_tr(q), hi = lds_tr(q + 4 * PT);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+
+  // chunks of kChunk steps: all their loads are issued together
+  for (int s0 = 0; s0 < steps; s0 += kChunk) {
+    Stage st[kChunk];
+#pragma unroll
+    for (int q = 0; q < kChunk; ++q) {
+      const int sq = s0 + q < steps ? s0 + q : steps - 1;
+      load(mbeg + (int64_t)sq * 64, st[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < kChunk; ++q) {
+      if (s0 + q < steps) {  // uniform
+        uint16_t* t = tile[q & 1];
+        store(mbeg + (int64_t)(s0 + q) * 64, st[q], t);
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 zf = frag(t, wave, s);
+#pragma unroll
+          for (int jt = 0; jt < JT; ++jt) acc[jt] = mfma32(zf, frag(t, 4 + jt, s), acc[jt]);
+        }
+      }
     }
     __syncthreads();
   }
   // acc[jt] lane l: rows c = c0 + 32 wave + 8q + 4h + i, column j = 32 jt + l32
-  float* P = p.P + (int64_t)split * r * p.C;
+  float* P = jb.P + (int64_t)split * r * C;
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) {
     const int j = 32 * jt + l32;
@@ -139,38 +192,52 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(GradParams p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t c = c0 + 32 * wave + 8 * q + 4 * h;
-      if (c + 4 <= p.C) {
-        *reinterpret_cast<f32x4*>(P + (int64_t)j * p.C + c) =
+      if (c + 4 <= C) {
+        *reinterpret_cast<f32x4*>(P + (int64_t)j * C + c) =
             f32x4{acc[jt][4 * q], acc[jt][4 * q + 1], acc[jt][4 * q + 2], acc[jt][4 * q + 3]};
       } else {
         for (int i = 0; i < 4; ++i)
-          if (c + i < p.C) P[(int64_t)j * p.C + c + i] = acc[jt][4 * q + i];
+          if (c + i < C) P[(int64_t)j * C + c + i] = acc[jt][4 * q + i];
       }
     }
   }
 }
 
-// out = s * sum_split P[split] (+ out if accumulate); layout jc: out[j][c]
-// (dA, r x K) or cj: out[c][j] (dB, N x r).
-__global__ void grad_reduce_kernel(const float* __restrict__ P, int splits, int r, int64_t C,
-                                   float s, int accumulate, int transpose,
-                                   float* __restrict__ out) {
+// Both reductions' finishing pass: out = s * sum_split P[split] (+ out if
+// accumulate), the split partials added in a fixed order.  Index space: dA
+// (r x K, out[j][c]) then dB (N x r, out[c][j]).
+struct ReduceParams {
+  const float* P[2];
+  float* out[2];
+  int64_t C[2];
+  int32_t splits[2];
+  int32_t r;
+  float s;
+  int32_t accumulate;
+};
+
+__global__ void grad_reduce_kernel(ReduceParams p) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)r * C;
-  if (idx >= total) return;
+  const int64_t t0 = (int64_t)p.r * p.C[0];
+  const int jb = idx < t0 ? 0 : 1;
+  const int64_t total = (int64_t)p.r * p.C[jb];
+  const int64_t i = jb ? idx - t0 : idx;
+  if (i >= total) return;
+  const int64_t C = p.C[jb];
   int64_t j, c;
-  if (transpose) {  // idx runs over out[c][j]
-    c = idx / r;
-    j = idx - c * r;
-  } else {
-    j = idx / C;
-    c = idx - j * C;
+  if (jb) {  // out[c][j]
+    c = i / p.r;
+    j = i - c * p.r;
+  } else {   // out[j][c]
+    j = i / C;
+    c = i - j * C;
   }
+  const float* P = p.P[jb];
   float sum = 0.0f;
-  for (int t = 0; t < splits; ++t) sum += P[(int64_t)t * total + j * C + c];
-  float v = s * sum;
-  if (accumulate) v += out[idx];
-  out[idx] = v;
+  for (int t = 0; t < p.splits[jb]; ++t) sum += P[(int64_t)t * total + j * C + c];
+  float v = p.s * sum;
+  if (p.accumulate) v += p.out[jb][i];
+  p.out[jb][i] = v;
 }
 
 int pick_splits(int64_t M, int64_t C) {
@@ -182,28 +249,58 @@ int pick_splits(int64_t M, int64_t C) {
   return (int)want;
 }
 
-int run_grad(const uint16_t* Z, const float* V, int64_t M, int64_t C, int r, float s,
-             int accumulate, int transpose, float* out, float* P, hipStream_t st) {
-  const int splits = pick_splits(M, C);
+GradJob make_job(const uint16_t* Z, const float* V, int64_t M, int64_t C, float* P) {
+  GradJob j;
+  j.Z = Z;
+  j.V = V;
+  j.C = C;
+  j.c_tiles = (int)cdiv(C, kTileC);
+  j.splits = pick_splits(M, C);
+  j.rows_per_split = cdiv(cdiv(M, j.splits), 64) * 64;
+  j.P = P;
+  return j;
+}
+
+// dA = s U^T X (r x K) and dB = s dY^T T (N x r) in one launch plus one
+// finishing launch.
+int run_grads(const uint16_t* X, const float* U, const uint16_t* dY, const float* T, int64_t M,
+              int64_t N, int64_t K, int r, float s, int accumulate, float* dA, float* dB,
+              float* PA, float* PB, hipStream_t st) {
   GradParams p;
-  p.Z = Z;
-  p.V = V;
+  p.job[0] = make_job(X, U, M, K, PA);
+  p.job[1] = make_job(dY, T, M, N, PB);
   p.M = M;
-  p.C = C;
   p.r = r;
-  p.splits = splits;
-  p.rows_per_split = cdiv(cdiv(M, splits), 64) * 64;
-  p.P = P;
-  const int blocks = (int)cdiv(C, kTileC) * splits;
-  if (r <= 32)
-    hipLaunchKernelGGL(grad_kernel<32>, dim3(blocks), dim3(kThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL(grad_kernel<64>, dim3(blocks), dim3(kThreads), 0, st, p);
+  p.blocks0 = p.job[0].c_tiles * p.job[0].splits;
+  const int blocks = p.blocks0 + p.job[1].c_tiles * p.job[1].splits;
+  const bool v4 = r % 4 == 0;
+  if (r <= 32) {
+    if (v4)
+      hipLaunchKernelGGL((grad_kernel<32, true>), dim3(blocks), dim3(kThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((grad_kernel<32, false>), dim3(blocks), dim3(kThreads), 0, st, p);
+  } else {
+    if (v4)
+      hipLaunchKernelGGL((grad_kernel<64, true>), dim3(blocks), dim3(kThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((grad_kernel<64, false>), dim3(blocks), dim3(kThreads), 0, st, p);
+  }
   int e = hip_fail(hipGetLastError(), "grad_kernel launch");
   if (e) return e;
-  const int64_t total = (int64_t)r * C;
-  hipLaunchKernelGGL(grad_reduce_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, st, P,
-                     splits, r, C, s, accumulate, transpose, out);
+  ReduceParams q;
+  q.P[0] = PA;
+  q.P[1] = PB;
+  q.out[0] = dA;
+  q.out[1] = dB;
+  q.C[0] = K;
+  q.C[1] = N;
+  q.splits[0] = p.job[0].splits;
+  q.splits[1] = p.job[1].splits;
+  q.r = r;
+  q.s = s;
+  q.accumulate = accumulate;
+  const int64_t total = (int64_t)r * (K + N);
+  hipLaunchKernelGGL(grad_reduce_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, st, q);
   return hip_fail(hipGetLastError(), "grad_reduce launch");
 }
 
@@ -250,8 +347,8 @@ int bf16_bwd(const void* dY, const void* X, int64_t M, const lq_weight& W, const
   } else {
     if ((e = u_only(dY, M, N, B, r, U, st))) return e;
   }
-  if ((e = run_grad((const uint16_t*)X, U, M, K, (int)r, s, accumulate, 0, dA, PA, st))) return e;
-  return run_grad((const uint16_t*)dY, T, M, N, (int)r, s, accumulate, 1, dB, PB, st);
+  return run_grads((const uint16_t*)X, U, (const uint16_t*)dY, T, M, N, K, (int)r, s, accumulate,
+                   dA, dB, PA, PB, st);
 }
 
 }  // namespace dispatch
