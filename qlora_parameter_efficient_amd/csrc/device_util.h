@@ -159,15 +159,30 @@ __device__ __forceinline__ void build_lut(float2* lut, const NF4Table& tab) {
 }
 
 // Eight codes (one 32-bit word, element e in bits 4e..4e+3) -> eight bf16
-// values RNE(fl32(cb[code] * a)) packed in natural element order.
-__device__ __forceinline__ u32x4 deq8(uint32_t w, float a, const float2* lut) {
+// values RNE(fl32(cb[code] * a)) packed in natural element order, in two
+// halves so that the table reads can be issued well before the products:
+// lut_fetch reads the levels of the four code bytes, lut_finish scales and
+// rounds them.
+struct LutFetch {
+  float2 v[4];
+};
+
+__device__ __forceinline__ LutFetch lut_fetch(uint32_t w, const float2* lut) {
+  LutFetch f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) f.v[p] = lut[(w >> (8 * p)) & 0xFFu];
+  return f;
+}
+
+__device__ __forceinline__ u32x4 lut_finish(const LutFetch& f, float a) {
   u32x4 o;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const float2 v = lut[(w >> (8 * p)) & 0xFFu];
-    o[p] = pack_bf16x2(v.x * a, v.y * a);
-  }
+  for (int p = 0; p < 4; ++p) o[p] = pack_bf16x2(f.v[p].x * a, f.v[p].y * a);
   return o;
+}
+
+__device__ __forceinline__ u32x4 deq8(uint32_t w, float a, const float2* lut) {
+  return lut_finish(lut_fetch(w, lut), a);
 }
 
 // (lo half of x, lo half of y) and (hi half of x, hi half of y).

@@ -148,6 +148,76 @@ __device__ __forceinline__ void mfma_step(const uint16_t* wtile, const uint16_t*
   }
 }
 
+// Activation fragments of one step loaded straight into MFMA operand
+// registers: lane (h, l32) of wave w takes row mw + 32 ms + l32 (clamped; its
+// outputs are never stored) and the reduction elements kb + 32 h .. +31, one
+// 16-byte fragment per substep (the same labels as the weight tile reads).
+template <int MS>
+struct FragStage {
+  u32x4 v[MS][4];
+};
+
+template <int MS>
+__device__ __forceinline__ void frag_offsets(uint32_t (&off)[MS], int64_t ld, int64_t mw,
+                                             int64_t rows, int l32, int h) {
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) {
+    int64_t m = mw + 32 * ms + l32;
+    m = m < rows ? m : rows - 1;
+    off[ms] = (uint32_t)((m * ld + 32 * h) * 2);
+  }
+}
+
+template <int MS>
+__device__ __forceinline__ void frag_load(FragStage<MS>& st, const char* base,
+                                          const uint32_t (&off)[MS]) {
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      st.v[ms][s] = *reinterpret_cast<const u32x4*>(base + off[ms] + 16 * s);
+}
+
+// mfma_step with the activation operands taken from registers.  Substep s
+// issues its LDS reads first -- the weight fragments of substep s + 1 and
+// pre(s + 1), the table reads of the next part of the staged tile -- then,
+// behind a scheduling fence, its MFMAs and post(s), which finishes the part
+// whose reads were issued a substep earlier.  Every LDS read therefore has a
+// full substep of MFMAs to land, and the in-order LDS return queue never
+// makes a product wait for reads issued after its own.
+template <int MS, int JT, typename Pre, typename Post>
+__device__ __forceinline__ void mfma_step_rx(const uint16_t* wtile, const FragStage<MS>& xf,
+                                             int l32, int h, f32x16 (&acc)[4][MS],
+                                             f32x16 (&tacc)[JT > 0 ? JT : 1][MS], Pre&& pre,
+                                             Post&& post) {
+  constexpr int NR = 4 + JT;
+  const uint16_t* wbase = wtile + l32 * kLP + 32 * h;
+  u32x4 wf[2][NR];
+#pragma unroll
+  for (int ns = 0; ns < NR; ++ns) wf[0][ns] = *reinterpret_cast<const u32x4*>(wbase + 32 * ns * kLP);
+  pre(0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c = s & 1;
+    if (s < 3) {
+#pragma unroll
+      for (int ns = 0; ns < NR; ++ns)
+        wf[c ^ 1][ns] = *reinterpret_cast<const u32x4*>(wbase + 32 * ns * kLP + 8 * (s + 1));
+      pre(s + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf.v[ms][s], acc[ns][ms]);
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) tacc[jt][ms] = mfma32(wf[c][4 + jt], xf.v[ms][s], tacc[jt][ms]);
+    post(s);
+  }
+}
+
 template <int N1, int N2>
 __device__ __forceinline__ void zero_acc(f32x16 (&a)[N1][N2]) {
 #pragma unroll
@@ -261,16 +331,25 @@ __device__ __forceinline__ void fwd_stage_load(FwdStage<WK, JT>& st, const FwdPa
   for (int i = 0; i < JT; ++i) st.at[i] = *reinterpret_cast<const u32x4*>(abase + o.a[i]);
 }
 
-// part (0..3) of writing a staged forward weight tile; a = its block scale
+// part (0..3) of writing a staged forward weight tile: fwd_stage_fetch issues
+// the level-table reads of the part, fwd_stage_finish scales (a = the block
+// scale), rounds and stores it (and the part's shrink-operand rows).
 template <int WK, int JT>
-__device__ __forceinline__ void fwd_stage_part(const FwdStage<WK, JT>& st, uint16_t* tile,
-                                               const float2* lut, float a, int part) {
+__device__ __forceinline__ LutFetch fwd_stage_fetch(const FwdStage<WK, JT>& st, const float2* lut,
+                                                    int part) {
+  if (WK == kDense) return LutFetch{};
+  return lut_fetch(st.w[0][part], lut);
+}
+
+template <int WK, int JT>
+__device__ __forceinline__ void fwd_stage_finish(const FwdStage<WK, JT>& st, const LutFetch& f,
+                                                 uint16_t* tile, float a, int part) {
   const int tid = threadIdx.x;
   if (WK == kDense) {
     *reinterpret_cast<u32x4*>(tile + ((tid >> 3) + 32 * part) * kLP + 8 * (tid & 7)) = st.w[part];
   } else {
     *reinterpret_cast<u32x4*>(tile + (tid >> 1) * kLP + 32 * (tid & 1) + 8 * part) =
-        deq8(st.w[0][part], a, lut);
+        lut_finish(f, a);
   }
   if (part < JT)
     *reinterpret_cast<u32x4*>(tile + (kTileI + (tid >> 3) + 32 * part) * kLP + 8 * (tid & 7)) =
@@ -283,7 +362,6 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
   constexpr int WROWS = kTileI + 32 * JT;
   constexpr int AROWS = 128 * MS;
   __shared__ __attribute__((aligned(16))) uint16_t wt[2][WROWS * kLP];
-  __shared__ __attribute__((aligned(16))) uint16_t xt[2][AROWS * kLP];
   __shared__ float2 lut[256];
   __shared__ float stab[WK == kNF4DQ ? kFwdTab : 1];
 
@@ -324,8 +402,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
     j = j < p.r ? j : p.r - 1;
     o.a[i] = (uint32_t)((j * K + 8 * (tid & 7)) * 2);
   }
-  uint32_t xo[4 * MS];
-  act_offsets<MS>(xo, K, m0, M);
+  uint32_t xo[MS];
+  frag_offsets<MS>(xo, K, mw, M, l32, h);
   const char* xbase = reinterpret_cast<const char*>(p.X);
 
   f32x16 acc[4][MS];
@@ -334,48 +412,51 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
   zero_acc(tacc);
 
   FwdStage<WK, JT> s0, s1;
-  ActStage<MS> x0, x1;
+  FragStage<MS> x0, x1, x2;
 
   fwd_stage_load<WK, JT>(s0, p, o, 0, g_lo);
-  act_load<MS>(x0, xbase, xo);
+  frag_load<MS>(x0, xbase, xo);
+  frag_load<MS>(x1, xbase + 2 * ((int64_t)(KT > 1 ? 1 : 0) * kBK), xo);
   __syncthreads();  // level and step tables ready
   {
     const float a = WK != kDense ? raw_scale_value<WK>(s0.sc, stab) : 0.0f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      fwd_stage_part<WK, JT>(s0, wt[0], lut, a, q);
-      act_part<MS>(x0, xt[0], q);
-    }
+    for (int q = 0; q < 4; ++q)
+      fwd_stage_finish<WK, JT>(s0, fwd_stage_fetch<WK, JT>(s0, lut, q), wt[0], a, q);
   }
   const int64_t kb1 = (int64_t)(KT > 1 ? 1 : 0) * kBK;
   fwd_stage_load<WK, JT>(s1, p, o, kb1, g_lo);
-  act_load<MS>(x1, xbase + 2 * kb1, xo);
   __syncthreads();
 
-  // step kt: loads stage kt+2 into (snxt, xnxt), runs the MFMAs of step kt on
-  // LDS buffer kt & 1, writes stage kt+1 (scur, xcur) into the other buffer
-  auto step = [&](int kt, const FwdStage<WK, JT>& scur, const ActStage<MS>& xcur,
-                  FwdStage<WK, JT>& snxt, ActStage<MS>& xnxt) {
+  // step kt: loads weight stage kt+2 into snxt and the activation fragments
+  // of step kt+2 into xnxt, runs the MFMAs of step kt (LDS buffer kt & 1,
+  // fragments xcur), writes weight stage kt+1 (scur) into the other buffer.
+  // Weight stages rotate over two register sets, activation fragments over
+  // three, so the main loop is unrolled by six.
+  auto step = [&](int kt, const FwdStage<WK, JT>& scur, const FragStage<MS>& xcur,
+                  FwdStage<WK, JT>& snxt, FragStage<MS>& xnxt) {
     const int64_t k2 = (int64_t)(kt + 2 < KT ? kt + 2 : KT - 1) * kBK;
     fwd_stage_load<WK, JT>(snxt, p, o, k2, g_lo);
-    act_load<MS>(xnxt, xbase + 2 * k2, xo);
+    frag_load<MS>(xnxt, xbase + 2 * k2, xo);
     const float a = WK != kDense ? raw_scale_value<WK>(scur.sc, stab) : 0.0f;
     const int b = kt & 1;
     uint16_t* wn = wt[b ^ 1];
-    uint16_t* xn = xt[b ^ 1];
-    mfma_step<MS, JT>(wt[b], xt[b], wave, l32, h, acc, tacc, [&](int q) {
-      fwd_stage_part<WK, JT>(scur, wn, lut, a, q);
-      act_part<MS>(xcur, xn, q);
-    });
+    LutFetch lf[2];
+    mfma_step_rx<MS, JT>(
+        wt[b], xcur, l32, h, acc, tacc,
+        [&](int q) { lf[q & 1] = fwd_stage_fetch<WK, JT>(scur, lut, q); },
+        [&](int q) { fwd_stage_finish<WK, JT>(scur, lf[q & 1], wn, a, q); });
     __syncthreads();
   };
 
-  int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
-    step(kt, s1, x1, s0, x0);
-    step(kt + 1, s0, x0, s1, x1);
+  for (int kt = 0; kt < KT; kt += 6) {
+    step(kt, s1, x0, s0, x2);
+    if (kt + 1 < KT) step(kt + 1, s0, x1, s1, x0);
+    if (kt + 2 < KT) step(kt + 2, s1, x2, s0, x1);
+    if (kt + 3 < KT) step(kt + 3, s0, x0, s1, x2);
+    if (kt + 4 < KT) step(kt + 4, s1, x1, s0, x0);
+    if (kt + 5 < KT) step(kt + 5, s0, x2, s1, x1);
   }
-  if (kt < KT) step(kt, s1, x1, s0, x0);
 
   // ---------------------------------------------------------------- epilogue
   const int r = p.r;
