@@ -7,15 +7,17 @@ Default run (python bench.py [--steps K] [--warmup W]):
   with double quantisation, r = 16, alpha = 32, M = 2048 tokens, bf16 compute
   (the fused forward kernel, then the fused dX kernel and the dA / dB
   reductions).  value = algorithmic fwd+bwd FLOPs / wall time per step.
-* roofline: the fused forward kernel, timed alone with HIP events on the
-  stream it runs on, algorithmic FLOPs per launch / average duration, against
-  the bf16 dense MFMA peak; traffic from rocprofv3 counters when they were
-  taken on the current kernel source.
+* roofline: the dominant kernel -- the fused forward or the fused dX kernel,
+  whichever is slower (both do 2 M N K + 2 M r (N + K) FLOPs) -- timed alone
+  with HIP events on the stream it runs on, algorithmic FLOPs per launch /
+  average duration, against the bf16 dense MFMA peak; traffic (HBM bytes per
+  launch) from rocprofv3 FETCH_SIZE / WRITE_SIZE counters scaled by the same
+  counters on a plain copy, when they were taken on the current kernel source.
 * cpu_baseline: the CPU oracle (float64 NumPy) on the same step.
 * secondary lines in the same JSON object: NF4 decode (M = 1, 4, 16) GB/s on
   the weight stream with cold weights, merge, quantise, multi-adapter.
 
-Profiling helpers (for rocprofv3): --mode fwd | step | decode | copy | quant
+Profiling helpers (for rocprofv3): --mode fwd | dx | step | decode | copy | quant
 run only that part, a few iterations, and print one line.
 """
 from __future__ import annotations
@@ -120,6 +122,12 @@ def bwd(S):
     lq = S["lq"]
     lq.lq_lora_bwd(S["dY"], S["X"], S["W"], S["A"], S["B"], S["s"], T_saved=S["T"], dA=S["dA"],
                    dB=S["dB"], ws=S["ws"], dX=S["dX"])
+
+
+def dx_only(S):
+    lq = S["lq"]
+    lq.lq_lora_bwd(S["dY"], S["X"], S["W"], S["A"], S["B"], S["s"], ws=S["ws"], dX=S["dX"],
+                   need_grads=False)
 
 
 def step(S):
@@ -253,7 +261,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--mode", default="full",
-                    choices=["full", "step", "fwd", "decode", "copy", "quant"])
+                    choices=["full", "step", "fwd", "dx", "decode", "copy", "quant"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-secondary", action="store_true")
     a = ap.parse_args(argv)
@@ -269,15 +277,16 @@ def main(argv=None):
         return 2
 
     if a.mode == "copy":
-        # plain copy of known size, for scaling the HBM byte counters
+        # a plain elementwise kernel of known traffic (reads 1 GiB, writes
+        # 1 GiB), for scaling the HBM byte counters
         nbytes = 1 << 30
-        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(a.steps):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        print(json.dumps({"mode": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
-                          "launches": a.steps}))
+        print(json.dumps({"mode": "copy", "kernel": "neg (elementwise float32)",
+                          "bytes_read": nbytes, "bytes_written": nbytes, "launches": a.steps}))
         return 0
 
     S = setup(torch)
@@ -286,6 +295,12 @@ def main(argv=None):
             fwd(S)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "fwd", "launches": a.steps}))
+        return 0
+    if a.mode == "dx":
+        for _ in range(a.steps):
+            dx_only(S)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "dx", "launches": a.steps}))
         return 0
     if a.mode == "step":
         for _ in range(a.steps):
@@ -314,15 +329,23 @@ def main(argv=None):
     ms_per_step = wall * 1e3 / a.steps
     value = STEP_FLOP / (wall / a.steps) / 1e12
 
-    # dominant kernel: the fused forward GEMM, alone, HIP events on its stream
+    # dominant kernel: the fused forward GEMM or the fused dX GEMM (the same
+    # algorithmic FLOPs), each alone, HIP events on the stream it runs on
     t_fwd = cuda_time(lambda: fwd(S), 50, torch)
+    t_dx = cuda_time(lambda: dx_only(S), 50, torch)
     t_step_ev = cuda_time(lambda: step(S), 20, torch)
-    achieved = FWD_FLOP / (t_fwd * 1e-3) / 1e12
-    roof = {"kernel": "fwd_kernel (fused NF4 dequant + GEMM + shrink/expand)",
-            "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_for("fwd_kernel", FWD_SOURCES),
-            "flop_per_launch": FWD_FLOP, "us_per_launch": round(t_fwd * 1e3, 2)}
+    if t_dx > t_fwd:
+        name, t_dom = "dx_kernel (fused NF4 dequant + transposed GEMM + shrink/expand)", t_dx
+        traffic = traffic_for("dx_kernel", FWD_SOURCES)
+    else:
+        name, t_dom = "fwd_kernel (fused NF4 dequant + GEMM + shrink/expand)", t_fwd
+        traffic = traffic_for("fwd_kernel", FWD_SOURCES)
+    achieved = FWD_FLOP / (t_dom * 1e-3) / 1e12
+    roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 1),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "flop_per_launch": FWD_FLOP, "us_per_launch": round(t_dom * 1e3, 2),
+            "us_fwd_kernel": round(t_fwd * 1e3, 2), "us_dx_kernel": round(t_dx * 1e3, 2)}
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",

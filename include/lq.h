@@ -168,6 +168,9 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A,
  *   dX = dY W0 + s (dY B) A      (optional: dX may be NULL)
  *   dA = s (dY B)^T X            (r x K float32)
  *   dB = s dY^T (X A^T)          (N x r float32)
+ *   dA and dB are given together or both NULL; with both NULL only dX is
+ *   computed (X and T_saved are then not read).  dX, dA and dB all NULL is
+ *   LQ_ERR_INVALID_ARG.
  *   dY device M x N of dt, X device M x K of dt, A and B as in lq_lora_fwd.
  *   T_saved: optional device M x r float32 from lq_lora_fwd's T_out; when
  *   NULL, T is recomputed.

@@ -204,8 +204,11 @@ int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0, c
   REQUIRE(M >= 0, LQ_ERR_INVALID_ARG, "M = %lld", (long long)M);
   REQUIRE(r >= 1 && r <= kMaxRank, LQ_ERR_UNSUPPORTED, "rank %lld outside [1, %lld]",
           (long long)r, (long long)kMaxRank);
-  REQUIRE(A && B && dA && dB, LQ_ERR_INVALID_ARG, "A, B, dA or dB is NULL");
-  REQUIRE(M == 0 || (dY && X), LQ_ERR_INVALID_ARG, "dY or X is NULL");
+  REQUIRE(A && B, LQ_ERR_INVALID_ARG, "A or B is NULL");
+  REQUIRE((dA == nullptr) == (dB == nullptr), LQ_ERR_INVALID_ARG,
+          "dA and dB must both be given or both be NULL");
+  REQUIRE(dA || dX, LQ_ERR_INVALID_ARG, "nothing to compute: dX, dA and dB are NULL");
+  REQUIRE(M == 0 || (dY && (X || !dA)), LQ_ERR_INVALID_ARG, "dY or X is NULL");
   if (dt == LQ_BF16 && (rc = check_bf16_shape(W0))) return rc;
   if (dt == LQ_BF16 && (rc = check_bf16_rows(M, W0))) return rc;
   const int64_t N = W0->N, K = W0->K;

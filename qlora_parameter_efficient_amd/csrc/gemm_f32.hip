@@ -132,7 +132,8 @@ int f32_lora_bwd(const float* dY, const float* X, int64_t M, const lq_weight& W,
   int rc;
   float* U = ws;
   const float* T = T_saved;
-  if (!T) {
+  const bool grads = dA != nullptr;  // dX only when both gradients are NULL
+  if (!T && grads) {
     float* Tw = ws + M * r;
     if ((rc = gemm(dense(X, K, 1), dense(A, 1, K), Tw, r, M, r, K, 1.0f, 0, st))) return rc;
     T = Tw;
@@ -142,6 +143,7 @@ int f32_lora_bwd(const float* dY, const float* X, int64_t M, const lq_weight& W,
     if ((rc = gemm(dense(dY, N, 1), weight_acc(W, K, 1), dX, K, M, K, N, 1.0f, 0, st))) return rc;
     if ((rc = gemm(dense(U, r, 1), dense(A, K, 1), dX, K, M, K, r, s, 1, st))) return rc;
   }
+  if (!grads) return LQ_OK;
   if (M == 0) {
     if (!accumulate) {
       if ((rc = launch_zero_f32(dA, r * K, st))) return rc;

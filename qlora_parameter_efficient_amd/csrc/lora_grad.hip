@@ -332,11 +332,13 @@ int bf16_bwd(const void* dY, const void* X, int64_t M, const lq_weight& W, const
   float* PA = (float*)pa;
   float* PB = PA + (int64_t)pick_splits(M, K) * r * K;
   int e;
+  const bool grads = dA != nullptr;  // dX only when both gradients are NULL
   if (M == 0) {
-    if (accumulate) return LQ_OK;
+    if (accumulate || !grads) return LQ_OK;
     if ((e = launch_zero_f32(dA, r * K, st))) return e;
     return launch_zero_f32(dB, N * r, st);
   }
+  if (!grads) return bf16_dx(dY, M, W, A, B, r, s, dX, nullptr, st);
   const float* T = T_saved;
   if (!T) {
     if ((e = t_only(X, M, K, A, r, Tw, st))) return e;

@@ -214,18 +214,18 @@ def lq_lora_fwd(X, W0, A, B, scale, T_out=None, ws=None, Y=None):
 
 
 def lq_lora_bwd(dY, X, W0, A, B, scale, T_saved=None, need_dx=True, dA=None, dB=None,
-                accumulate=False, ws=None, dX=None):
+                accumulate=False, ws=None, dX=None, need_grads=True):
     _dev(dY, X, A, B, T_saved, dA, dB, dX)
-    dt = _dt(X)
-    M = X.shape[0]
+    dt = _dt(dY)
+    M = dY.shape[0]
     w = weight_struct(W0, dt)
     r = A.shape[0]
-    dev = X.device
+    dev = dY.device
     if dX is None and need_dx:
-        dX = torch.empty((M, w.K), dtype=X.dtype, device=dev)
-    if dA is None:
+        dX = torch.empty((M, w.K), dtype=dY.dtype, device=dev)
+    if need_grads and dA is None:
         dA = torch.empty((r, w.K), dtype=torch.float32, device=dev)
-    if dB is None:
+    if need_grads and dB is None:
         dB = torch.empty((w.N, r), dtype=torch.float32, device=dev)
     if ws is None:
         ws = _ws(lq_workspace_size(LQ_OP_BWD, M, w.N, w.K, r), dev)

@@ -96,6 +96,11 @@ def test_argument_errors_launch_nothing():
     w = _weight()
     assert L.lq_lora_bwd(0x1000, 0x1000, 64, ctypes.byref(w), 0x1000, 0x1000, 8, 2.0, 1, None,
                          0x1000, 0x1000, 0x1000, 0, None, 0, None) == -3
+    # dA and dB go together; nothing requested is an error
+    assert L.lq_lora_bwd(0x1000, 0x1000, 64, ctypes.byref(w), 0x1000, 0x1000, 8, 2.0, 1, None,
+                         0x1000, 0x1000, None, 0, 0x1000, 1 << 30, None) == -1
+    assert L.lq_lora_bwd(0x1000, 0x1000, 64, ctypes.byref(w), 0x1000, 0x1000, 8, 2.0, 1, None,
+                         None, None, None, 0, 0x1000, 1 << 30, None) == -1
     # multi-adapter: rank * adapters over 64, float32, no segments
     assert L.lq_lora_fwd_multi(0x1000, 10, ctypes.byref(w), 0x1000, 0x1000, 5, 16, 2.0, 0x1000,
                                0x1000, 1, 1, 0x1000, 0x1000, 1 << 20, None) == -2

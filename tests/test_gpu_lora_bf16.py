@@ -61,6 +61,11 @@ def check_layer(c, kind, rows=None, bwd=True, merge=True, label=""):
         for name, got, want in (("dA", dA, dAo), ("dB", dB, dBo)):
             e = rel_err(f64(got), want)
             assert e <= BF16_TOL, f"{name} rel err {e:.3e}"
+        # dX alone (dA = dB = NULL) runs the same kernel: bit-identical dX
+        dX2, dA2, dB2 = lq.lq_lora_bwd(dY, X, Wd, A, B, s, need_grads=False)
+        torch.cuda.synchronize()
+        assert dA2 is None and dB2 is None
+        assert torch.equal(dX2, dX), "dX-only call differs from the full backward"
     if merge:
         announce(f"bf16 merge {label} {kind}")
         Wm = lq.lq_lora_merge(Wd, A, B, s, dtype=torch.bfloat16)

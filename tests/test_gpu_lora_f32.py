@@ -30,6 +30,7 @@ def run_case(c, nf4=False):
     Y2 = lq.lq_lora_fwd(X, W0, A, B, s)          # T through the workspace
     dX, dA, dB = lq.lq_lora_bwd(dY, X, W0, A, B, s, T_saved=T)
     dX2, dA2, dB2 = lq.lq_lora_bwd(dY, X, W0, A, B, s)   # T recomputed
+    dX3, _, _ = lq.lq_lora_bwd(dY, X, W0, A, B, s, need_grads=False)   # dX alone
     Wm = lq.lq_lora_merge(W0, A, B, s, dtype=torch.float32)
     torch.cuda.synchronize()
     Yo, Ybo, To = olora.lora_forward(c["X"].f64(), Wo, c["A"].f64(), c["B"].f64(), s)
@@ -38,7 +39,8 @@ def run_case(c, nf4=False):
     Wmo = olora.lora_merge(Wo, c["A"].f64(), c["B"].f64(), s)
     for name, got, want in (("Y", Y, Yo), ("Y(ws)", Y2, Yo), ("T", T, To), ("dX", dX, dXo),
                             ("dA", dA, dAo), ("dB", dB, dBo), ("dX2", dX2, dXo),
-                            ("dA2", dA2, dAo), ("dB2", dB2, dBo), ("merge", Wm, Wmo)):
+                            ("dA2", dA2, dAo), ("dB2", dB2, dBo), ("dX3", dX3, dXo),
+                            ("merge", Wm, Wmo)):
         e = rel_err(f64(got), want)
         assert e <= F32_TOL, f"{name}: rel err {e:.3e}"
     return Y, dA, dB
