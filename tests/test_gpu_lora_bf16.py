@@ -145,3 +145,15 @@ def test_config2_lora_bf16(proj):
     p = c2["proj"][proj]
     c = dict(W0=p["W0"], A=p["A"], B=p["B"], dY=p["dY"], X=c2["X"], r=8, alpha=16.0)
     check_layer(c, "dense", rows=sample_rows(4096, seed=1), label=f"config2-{proj}", merge=False)
+
+
+@pytest.mark.parametrize("proj", ["q", "gate", "down"])
+def test_config4_block(proj):
+    """One Llama-2-7B-shaped block, NF4 + DQ base, r = 64, alpha = 128, M = 8192:
+    the three distinct shapes (4096 x 4096, 11008 x 4096, 4096 x 11008)."""
+    c4 = wl.config4(only=(proj,))
+    p = c4["proj"][proj]
+    X = c4["X_down"] if proj == "down" else c4["X"]
+    c = dict(W0=p["W0"], A=p["A"], B=p["B"], dY=p["dY"], X=X, r=64, alpha=128.0)
+    check_layer(c, "nf4", rows=sample_rows(8192, n=32, seed=4), label=f"config4-{proj}",
+                merge=False)
