@@ -221,8 +221,10 @@ def secondary(S, torch):
     lq = S["lq"]
     res = {}
     res["decode_nf4"] = decode_bench(S, torch)
+    Wm = torch.empty((N, K), dtype=torch.bfloat16, device=S["dev"])
     t = cuda_time(lambda: lq.lq_lora_merge(S["W"], S["A"], S["B"], S["s"],
-                                           dtype=torch.bfloat16), 20, torch)
+                                           dtype=torch.bfloat16, out=Wm), 20, torch)
+    del Wm
     mbytes = NF4_STREAM_BYTES + 2 * N * K + 2 * R * (N + K)
     res["merge_nf4_to_bf16"] = {"us": round(t * 1e3, 2), "GBs": round(mbytes / (t * 1e-3) / 1e9, 1)}
     t = cuda_time(lambda: lq.lq_nf4_quantize(S["W0d"]), 20, torch)

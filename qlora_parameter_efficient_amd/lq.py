@@ -235,11 +235,12 @@ def lq_lora_bwd(dY, X, W0, A, B, scale, T_saved=None, need_dx=True, dA=None, dB=
     return dX, dA, dB
 
 
-def lq_lora_merge(W0, A, B, scale, dtype=None):
-    _dev(A, B)
+def lq_lora_merge(W0, A, B, scale, dtype=None, out=None):
+    _dev(A, B, out)
     dt = _dt(A) if dtype is None else (LQ_F32 if dtype == torch.float32 else LQ_BF16)
     w = weight_struct(W0, dt)
-    out = torch.empty((w.N, w.K), dtype=_torch_dt(dt), device=A.device)
+    if out is None:
+        out = torch.empty((w.N, w.K), dtype=_torch_dt(dt), device=A.device)
     _check(lib().lq_lora_merge(ctypes.byref(w), _ptr(A), _ptr(B), A.shape[0], scale, dt,
                                _ptr(out), _stream()))
     return out
