@@ -216,21 +216,40 @@ def decode_bench(S, torch, iters=200, copies=40, replays=20):
     return out
 
 
+def graph_time(fn, torch, calls=20, replays=10):
+    """GPU time (ms) per fn() call: `calls` calls captured in one HIP graph,
+    replayed `replays` times (host and launch overhead amortised)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    t = cuda_time(g.replay, replays, torch) / calls
+    del g
+    return t
+
+
 def secondary(S, torch):
     import numpy as np
     lq = S["lq"]
     res = {}
     res["decode_nf4"] = decode_bench(S, torch)
+    # one-time ops, HBM-bound: GPU time per call from graph-captured sequences
     Wm = torch.empty((N, K), dtype=torch.bfloat16, device=S["dev"])
-    t = cuda_time(lambda: lq.lq_lora_merge(S["W"], S["A"], S["B"], S["s"],
-                                           dtype=torch.bfloat16, out=Wm), 20, torch)
+    t = graph_time(lambda: lq.lq_lora_merge(S["W"], S["A"], S["B"], S["s"],
+                                            dtype=torch.bfloat16, out=Wm), torch)
     del Wm
     mbytes = NF4_STREAM_BYTES + 2 * N * K + 2 * R * (N + K)
     res["merge_nf4_to_bf16"] = {"us": round(t * 1e3, 2), "GBs": round(mbytes / (t * 1e-3) / 1e9, 1)}
-    t = cuda_time(lambda: lq.lq_nf4_quantize(S["W0d"]), 20, torch)
+    t = graph_time(lambda: lq.lq_nf4_quantize(S["W0d"]), torch)
     qbytes = 2 * N * K + NF4_STREAM_BYTES
     res["nf4_quantize_bf16"] = {"us": round(t * 1e3, 2), "GBs": round(qbytes / (t * 1e-3) / 1e9, 1)}
-    t = cuda_time(lambda: lq.lq_nf4_dequantize(S["W"], dtype=torch.bfloat16), 20, torch)
+    t = graph_time(lambda: lq.lq_nf4_dequantize(S["W"], dtype=torch.bfloat16), torch)
     res["nf4_dequantize_bf16"] = {"us": round(t * 1e3, 2),
                                   "GBs": round(qbytes / (t * 1e-3) / 1e9, 1)}
     # multi-adapter serving workload: 4 adapters r=16 over 256 requests, 4096^2 bf16 base

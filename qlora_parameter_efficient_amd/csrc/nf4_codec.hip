@@ -79,17 +79,23 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quantize_kernel(
   const int64_t g0 = (int64_t)blockIdx.x * kGroupElems;
   const int64_t nb_total = (n + LQ_NF4_BLOCK - 1) / LQ_NF4_BLOCK;
 
-#pragma unroll 1
+  // all steps' loads are issued before any arithmetic
+  float vall[kSteps][8];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int64_t e0 = g0 + (int64_t)(s * kQuantThreads + t) * kChunk;
+    if (e0 < n) {
+      load8<T>(W, e0, n, vall[s]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vall[s][i] = 0.0f;
+    }
+  }
+#pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     const int chunk = s * kQuantThreads + t;
     const int64_t e0 = g0 + (int64_t)chunk * kChunk;
-    float v[8];
-    if (e0 < n) {
-      load8<T>(W, e0, n, v);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-    }
+    const float (&v)[8] = vall[s];
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
@@ -143,9 +149,16 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quantize_kernel(
   }
 }
 
-// Standalone dequantiser: each thread handles 32 elements (16 code bytes,
-// half of one block), so one scale a' per thread.
+// Standalone dequantiser.  A workgroup covers 32768 elements (two groups of
+// 256 blocks); thread t owns the 16 chunks of 8 elements t + 256 i, so
+// consecutive lanes read consecutive code words and write consecutive 16-byte
+// (bf16) or 32-byte (float32) pieces.  All code words and block constants are
+// loaded before any arithmetic; the second-level steps fl32(c2 / 127) of the
+// workgroup's groups come from a small LDS table.  A partial last chunk (n
+// not a multiple of 8) is finished element by element.
 constexpr int kDeqThreads = 256;
+constexpr int kDeqChunks = 16;                                   // chunks of 8 per thread
+constexpr int64_t kDeqSpan = (int64_t)kDeqThreads * kDeqChunks * 8;  // 32768 elements
 
 template <bool BF16OUT>
 __global__ __launch_bounds__(kDeqThreads) void nf4_dequantize_kernel(
@@ -153,56 +166,50 @@ __global__ __launch_bounds__(kDeqThreads) void nf4_dequantize_kernel(
     const float* __restrict__ c2, const float* __restrict__ absmax, int32_t double_quant,
     int64_t n, void* __restrict__ out, NF4Table tab) {
   __shared__ float cbs[16];
-  if (threadIdx.x < 16) cbs[threadIdx.x] = tab.cb[threadIdx.x];
-  __syncthreads();
-  const int64_t e0 = ((int64_t)blockIdx.x * kDeqThreads + threadIdx.x) * 32;
-  if (e0 >= n) return;
-  const int64_t blk = e0 / LQ_NF4_BLOCK;
-  float a;
-  if (double_quant) {
-    const float step = dq_step(c2[blk / LQ_NF4_DQ_BLOCK]);
-    a = (float)q8[blk] * step;
-  } else {
-    a = absmax[blk];
+  __shared__ float steps[4];
+  const int t = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * kDeqSpan;
+  const int64_t g_lo = base / kGroupElems;
+  const int64_t ngroups = (n + kGroupElems - 1) / kGroupElems;
+  if (t < 16) cbs[t] = tab.cb[t];
+  if (double_quant && t < 3 && g_lo + t < ngroups) steps[t] = dq_step(c2[g_lo + t]);
+  uint32_t cw[kDeqChunks], qv[kDeqChunks];
+#pragma unroll
+  for (int i = 0; i < kDeqChunks; ++i) {
+    int64_t e = base + 8 * (int64_t)(t + kDeqThreads * i);
+    e = e < n ? e : 0;  // chunks past the end are not stored
+    const int64_t blk = e / LQ_NF4_BLOCK;
+    cw[i] = e + 8 <= n ? *reinterpret_cast<const uint32_t*>(codes + (e >> 1)) : 0u;
+    qv[i] = double_quant ? (uint32_t)q8[blk] : __float_as_uint(absmax[blk]);
   }
-  if (e0 + 32 <= n) {
-    const u32x4 cw = *reinterpret_cast<const u32x4*>(codes + (e0 >> 1));
-    if (BF16OUT) {
-      u32x4 o[4];
+  __syncthreads();
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t w = cw[d];
+  for (int i = 0; i < kDeqChunks; ++i) {
+    const int64_t e = base + 8 * (int64_t)(t + kDeqThreads * i);
+    if (e >= n) continue;
+    const float a = double_quant ? (float)qv[i] * steps[e / kGroupElems - g_lo]
+                                 : __uint_as_float(qv[i]);
+    if (e + 8 <= n) {
+      float w[8];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const float lo = cbs[(w >> (8 * p)) & 15] * a;
-          const float hi = cbs[(w >> (8 * p + 4)) & 15] * a;
-          o[d][p] = pack_bf16x2(lo, hi);
-        }
+      for (int j = 0; j < 8; ++j) w[j] = cbs[(cw[i] >> (4 * j)) & 15u] * a;
+      if (BF16OUT) {
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + e) =
+            u32x4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
+                  pack_bf16x2(w[6], w[7])};
+      } else {
+        f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + e);
+        dst[0] = f32x4{w[0], w[1], w[2], w[3]};
+        dst[1] = f32x4{w[4], w[5], w[6], w[7]};
       }
-      u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + e0);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) dst[d] = o[d];
     } else {
-      f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + e0);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t w = cw[d];
-        f32x4 lo4, hi4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lo4[i] = cbs[(w >> (4 * i)) & 15] * a;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hi4[i] = cbs[(w >> (16 + 4 * i)) & 15] * a;
-        dst[2 * d] = lo4;
-        dst[2 * d + 1] = hi4;
+      for (int64_t k = e; k < n; ++k) {
+        const uint32_t byte = codes[k >> 1];
+        const uint32_t code = (k & 1) ? (byte >> 4) : (byte & 15u);
+        const float w = cbs[code] * a;
+        if (BF16OUT) reinterpret_cast<uint16_t*>(out)[k] = f32_to_bf16(w);
+        else reinterpret_cast<float*>(out)[k] = w;
       }
-    }
-  } else {
-    for (int64_t e = e0; e < n; ++e) {
-      const uint32_t byte = codes[e >> 1];
-      const uint32_t code = (e & 1) ? (byte >> 4) : (byte & 15);
-      const float w = cbs[code] * a;
-      if (BF16OUT) reinterpret_cast<uint16_t*>(out)[e] = f32_to_bf16(w);
-      else reinterpret_cast<float*>(out)[e] = w;
     }
   }
 }
@@ -227,8 +234,7 @@ int launch_nf4_quantize(const void* W, lq_dtype wdt, int64_t n, int32_t double_q
 int launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
                           const float* absmax, int32_t double_quant, int64_t n, void* out,
                           lq_dtype odt, hipStream_t stream) {
-  const int64_t threads = cdiv(n, 32);
-  const int64_t blocks = cdiv(threads, kDeqThreads);
+  const int64_t blocks = cdiv(n, kDeqSpan);
   const NF4Table& tab = nf4_table();
   if (odt == LQ_BF16) {
     hipLaunchKernelGGL(nf4_dequantize_kernel<true>, dim3((unsigned)blocks), dim3(kDeqThreads), 0,
