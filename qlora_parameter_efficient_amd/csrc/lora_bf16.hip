@@ -14,7 +14,7 @@
 // Structure shared by both kernels.  A workgroup of 256 threads (4 waves)
 // owns a 128-wide slice of the weight-side output dimension (n for the
 // forward, k for dX) and 128 * MS activation rows; wave w owns rows
-// 32 MS w .. +32 MS.  The reduction runs in steps of 128.  Each step the whole
+// 32 MS w .. +32 MS.  The reduction runs in steps of 64.  Each step the whole
 // workgroup stages one LDS tile holding the 128 weight rows -- NF4 codes
 // dequantised through a byte-indexed level table, and for dX transposed in
 // registers so the reduction index n is contiguous -- plus the RP rows of the
@@ -25,7 +25,7 @@
 //
 // Software pipeline per step: issue the next step's global loads (activation
 // fragments into the idle half of a ping-pong register pair, weight codes
-// into staging registers), run the 8 MFMA substeps on the current LDS tile
+// into staging registers), run the 4 MFMA substeps on the current LDS tile
 // with each substep's LDS fragment reads issued one substep ahead, then
 // dequantise / transpose the staged next tile into the other LDS buffer, one
 // barrier.  All loads are issued from clamped addresses; lanes out of range
