@@ -225,6 +225,8 @@ int lq_check_segments(const int32_t* h_offsets, const int32_t* h_adapter,
 #define LQ_OP_FWD 0
 #define LQ_OP_BWD 1
 #define LQ_OP_FWD_MULTI 2
+#define LQ_OP_FWD_FUSED 3
+#define LQ_OP_BWD_FUSED 4
 size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
                          int32_t n_adapters);
 

@@ -87,6 +87,19 @@ size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
   return (size_t)(2 * M * r) * 4 + dispatch::grad_partial_bytes(M, N, K, r);
 }
 
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// The large-tile path of the bf16 forward / dX runs when the call's workspace
+// holds its extra part (the bf16 weight copy and the split-K slots); with a
+// smaller workspace the fused kernels run instead.
+size_t fwd_big_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+  return dispatch::big_fwd_eligible(M, N, K) ? dispatch::big_fwd_ws_bytes(M, N, K, r) : 0;
+}
+
+size_t bwd_big_bytes(int64_t M, int64_t N, int64_t K) {
+  return dispatch::big_dx_eligible(M, N, K) ? dispatch::big_dx_ws_bytes(M, N, K) : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -123,12 +136,21 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
                          int32_t n_adapters) {
   if (M < 0 || N < 0 || K < 0 || r < 0) return 0;
   switch (op) {
-    case LQ_OP_FWD:  // float32 T, or the decode path's partial sums of T
-      return (size_t)((M <= kDecodeMaxM ? kTParts : 1) * M * r) * 4;
-    case LQ_OP_BWD:
-      return bwd_ws_bytes(M, N, K, r);
+    case LQ_OP_FWD: {  // float32 T, or the decode path's partial sums of T
+      const size_t base = (size_t)((M <= kDecodeMaxM ? kTParts : 1) * M * r) * 4;
+      const size_t big = fwd_big_bytes(M, N, K, r);
+      return big > base ? big : base;
+    }
+    case LQ_OP_BWD: {
+      const size_t big = bwd_big_bytes(M, N, K);
+      return big ? align256(bwd_ws_bytes(M, N, K, r)) + big : bwd_ws_bytes(M, N, K, r);
+    }
     case LQ_OP_FWD_MULTI:
       return dispatch::multi_ws_bytes(M, r, n_adapters);
+    case LQ_OP_FWD_FUSED:
+      return (size_t)((M <= kDecodeMaxM ? kTParts : 1) * M * r) * 4;
+    case LQ_OP_BWD_FUSED:
+      return bwd_ws_bytes(M, N, K, r);
     default:
       return 0;
   }
@@ -191,6 +213,9 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
             "workspace %zu bytes, need %zu", ws_bytes, need);
     return dispatch::decode_fwd(X, M, *W0, A, B, r, scale, Y, T_out, (float*)ws, stream);
   }
+  const size_t big = fwd_big_bytes(M, W0->N, W0->K, r);
+  if (big && ws && ws_bytes >= big)
+    return dispatch::big_fwd(X, M, *W0, A, B, r, scale, Y, T_out, ws, stream);
   return dispatch::bf16_fwd(X, M, *W0, A, B, r, scale, Y, T_out, stream);
 }
 
@@ -219,8 +244,11 @@ int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0, c
     return f32_lora_bwd((const float*)dY, (const float*)X, M, *W0, (const float*)A,
                         (const float*)B, r, scale, T_saved, (float*)dX, dA, dB, accumulate,
                         (float*)ws, stream);
+  const size_t big = dX ? bwd_big_bytes(M, N, K) : 0;
+  void* big_ws = nullptr;
+  if (big && ws_bytes >= align256(need) + big) big_ws = (char*)ws + align256(need);
   return dispatch::bf16_bwd(dY, X, M, *W0, A, B, r, scale, T_saved, dX, dA, dB, accumulate, ws,
-                            stream);
+                            big_ws, stream);
 }
 
 int lq_lora_merge(const lq_weight* W0, const void* A, const void* B, int64_t r, float scale,

@@ -27,10 +27,15 @@ template <int RP, bool GT>
 __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __restrict__ Z,
                                                           int64_t M, int64_t K,
                                                           const uint16_t* __restrict__ G, int r,
-                                                          float* __restrict__ out) {
+                                                          float* __restrict__ out,
+                                                          int32_t* __restrict__ zero, int nzero) {
   constexpr int JT = RP / 32;
   __shared__ __attribute__((aligned(16))) uint16_t gl[RP * kPitch];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // side job: clear the next kernel's flag words (a kernel store, so it also
+  // replays correctly inside a captured graph)
+  if (blockIdx.x == 0)
+    for (int i = tid; i < nzero; i += kThreads) zero[i] = 0;
   const int h = lane >> 5, l32 = lane & 31;
   const int64_t mrow = ((int64_t)blockIdx.x * 4 + wave) * 32 + l32;
   const int64_t mr = mrow < M ? mrow : M - 1;
@@ -82,22 +87,22 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
 }
 
 int launch_skinny(const uint16_t* Z, int64_t M, int64_t K, const uint16_t* G, bool gt, int64_t r,
-                  float* out, hipStream_t st) {
-  const unsigned blocks = (unsigned)cdiv(M, 128);
+                  float* out, int32_t* zero, int nzero, hipStream_t st) {
+  const dim3 grid((unsigned)cdiv(M, 128)), block(kThreads);
   if (r <= 32) {
     if (gt)
-      hipLaunchKernelGGL((skinny_kernel<32, true>), dim3(blocks), dim3(kThreads), 0, st, Z, M, K, G,
-                         (int)r, out);
+      hipLaunchKernelGGL((skinny_kernel<32, true>), grid, block, 0, st, Z, M, K, G, (int)r, out,
+                         zero, nzero);
     else
-      hipLaunchKernelGGL((skinny_kernel<32, false>), dim3(blocks), dim3(kThreads), 0, st, Z, M, K,
-                         G, (int)r, out);
+      hipLaunchKernelGGL((skinny_kernel<32, false>), grid, block, 0, st, Z, M, K, G, (int)r, out,
+                         zero, nzero);
   } else {
     if (gt)
-      hipLaunchKernelGGL((skinny_kernel<64, true>), dim3(blocks), dim3(kThreads), 0, st, Z, M, K, G,
-                         (int)r, out);
+      hipLaunchKernelGGL((skinny_kernel<64, true>), grid, block, 0, st, Z, M, K, G, (int)r, out,
+                         zero, nzero);
     else
-      hipLaunchKernelGGL((skinny_kernel<64, false>), dim3(blocks), dim3(kThreads), 0, st, Z, M, K,
-                         G, (int)r, out);
+      hipLaunchKernelGGL((skinny_kernel<64, false>), grid, block, 0, st, Z, M, K, G, (int)r, out,
+                         zero, nzero);
   }
   return hip_fail(hipGetLastError(), "skinny launch");
 }
@@ -332,13 +337,17 @@ __global__ __launch_bounds__(kThreads) void tpart_kernel(const uint16_t* __restr
 namespace dispatch {
 
 int t_only(const void* X, int64_t M, int64_t K, const void* A, int64_t r, float* T,
-           hipStream_t st) {
-  return launch_skinny((const uint16_t*)X, M, K, (const uint16_t*)A, false, r, T, st);
+           hipStream_t st, int32_t* zero, int nzero) {
+  if (shrink_eligible(false, r)) return launch_shrink(X, M, K, A, false, r, T, zero, nzero, st);
+  return launch_skinny((const uint16_t*)X, M, K, (const uint16_t*)A, false, r, T, zero, nzero,
+                       st);
 }
 
 int u_only(const void* dY, int64_t M, int64_t N, const void* B, int64_t r, float* U,
-           hipStream_t st) {
-  return launch_skinny((const uint16_t*)dY, M, N, (const uint16_t*)B, true, r, U, st);
+           hipStream_t st, int32_t* zero, int nzero) {
+  if (shrink_eligible(true, r)) return launch_shrink(dY, M, N, B, true, r, U, zero, nzero, st);
+  return launch_skinny((const uint16_t*)dY, M, N, (const uint16_t*)B, true, r, U, zero, nzero,
+                       st);
 }
 
 int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,

@@ -36,9 +36,39 @@ int bf16_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const 
 // T_out (optional) receives T.
 int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
                int64_t r, float s, void* Y, float* T_out, float* Tp, hipStream_t st);
+// big_ws: workspace of the large-tile dX path (big_dx_ws_bytes), or NULL for
+// the fused kernel
 int bf16_bwd(const void* dY, const void* X, int64_t M, const lq_weight& W, const void* A,
              const void* B, int64_t r, float s, const float* T_saved, void* dX, float* dA,
-             float* dB, int accumulate, void* ws, hipStream_t st);
+             float* dB, int accumulate, void* ws, void* big_ws, hipStream_t st);
+int bf16_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B,
+            int64_t r, float s, void* dX, float* U_out, hipStream_t st);
+
+// Skinny products T = X A^T and U = dY B (float32, M x r).  zero / nzero: int
+// words cleared by the first workgroup as a side job (the split-K flags of the
+// large-tile kernel that follows), or NULL / 0.
+int t_only(const void* X, int64_t M, int64_t K, const void* A, int64_t r, float* T,
+           hipStream_t st, int32_t* zero, int nzero);
+int u_only(const void* dY, int64_t M, int64_t N, const void* B, int64_t r, float* U,
+           hipStream_t st, int32_t* zero, int nzero);
+// The 8-wave shrink kernel behind t_only / u_only (gt: G is B, K x r; needs
+// r % 4 == 0), with the older one-pass kernel as the fallback.
+bool shrink_eligible(bool gt, int64_t r);
+int launch_shrink(const void* Z, int64_t M, int64_t K, const void* G, bool gt, int64_t r,
+                  float* out, int32_t* zero, int nzero, hipStream_t st);
+
+// Large-M path: the NF4 weight dequantised to a bf16 workspace copy, then the
+// 256 x 256-tile product with the rank-r expand fused.  Eligible when the
+// product's output width is a multiple of 256 and there are enough rows.
+bool big_fwd_eligible(int64_t M, int64_t N, int64_t K);
+bool big_dx_eligible(int64_t M, int64_t N, int64_t K);
+size_t big_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+size_t big_dx_ws_bytes(int64_t M, int64_t N, int64_t K);
+int big_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,
+            float s, void* Y, float* T_out, void* ws, hipStream_t st);
+// U (M x r float32) is written as well: the expand needs it.
+int big_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,
+           float s, void* dX, float* U, void* ws, hipStream_t st);
 int bf16_merge(const lq_weight& W, const void* A, const void* B, int64_t r, float s, void* Wout,
                hipStream_t st);
 int bf16_fwd_multi(const void* X, int64_t T_tokens, const lq_weight& W, const void* A_stack,

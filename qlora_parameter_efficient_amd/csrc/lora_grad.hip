@@ -308,15 +308,6 @@ int run_grads(const uint16_t* X, const float* U, const uint16_t* dY, const float
 
 namespace dispatch {
 
-int bf16_fwd(const void*, int64_t, const lq_weight&, const void*, const void*, int64_t, float,
-             void*, float*, hipStream_t);
-int bf16_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B,
-            int64_t r, float s, void* dX, float* U_out, hipStream_t st);
-int t_only(const void* X, int64_t M, int64_t K, const void* A, int64_t r, float* T,
-           hipStream_t st);
-int u_only(const void* dY, int64_t M, int64_t N, const void* B, int64_t r, float* U,
-           hipStream_t st);
-
 size_t grad_partial_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
   const int64_t sa = pick_splits(M, K), sb = pick_splits(M, N);
   return (size_t)(sa * r * K + sb * r * N) * 4 + 512;
@@ -324,7 +315,7 @@ size_t grad_partial_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
 
 int bf16_bwd(const void* dY, const void* X, int64_t M, const lq_weight& W, const void* A,
              const void* B, int64_t r, float s, const float* T_saved, void* dX, float* dA,
-             float* dB, int accumulate, void* ws, hipStream_t st) {
+             float* dB, int accumulate, void* ws, void* big_ws, hipStream_t st) {
   const int64_t N = W.N, K = W.K;
   float* U = (float*)ws;
   float* Tw = U + M * r;
@@ -338,16 +329,22 @@ int bf16_bwd(const void* dY, const void* X, int64_t M, const lq_weight& W, const
     if ((e = launch_zero_f32(dA, r * K, st))) return e;
     return launch_zero_f32(dB, N * r, st);
   }
-  if (!grads) return bf16_dx(dY, M, W, A, B, r, s, dX, nullptr, st);
+  // dX (and U = dY B on the way) by the large-tile path when it has its
+  // workspace, else by the fused kernel
+  auto run_dx = [&](float* Uo) {
+    return big_ws ? big_dx(dY, M, W, A, B, r, s, dX, U, big_ws, st)
+                  : bf16_dx(dY, M, W, A, B, r, s, dX, Uo, st);
+  };
+  if (!grads) return run_dx(nullptr);
   const float* T = T_saved;
   if (!T) {
-    if ((e = t_only(X, M, K, A, r, Tw, st))) return e;
+    if ((e = t_only(X, M, K, A, r, Tw, st, nullptr, 0))) return e;
     T = Tw;
   }
   if (dX) {
-    if ((e = bf16_dx(dY, M, W, A, B, r, s, dX, U, st))) return e;
+    if ((e = run_dx(U))) return e;
   } else {
-    if ((e = u_only(dY, M, N, B, r, U, st))) return e;
+    if ((e = u_only(dY, M, N, B, r, U, st, nullptr, 0))) return e;
   }
   return run_grads((const uint16_t*)X, U, (const uint16_t*)dY, T, M, N, K, (int)r, s, accumulate,
                    dA, dB, PA, PB, st);

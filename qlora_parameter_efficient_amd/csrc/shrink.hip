@@ -1,0 +1,203 @@
+// Skinny rank-r products of the adapted linear layer, float32 results:
+//   T = X A^T   (forward, M x r; kept for the backward)
+//   U = dY B    (backward, M x r; feeds dX and dA)
+// ("Low-Rank Adaptation (LoRA) and QLoRA: Mathematical Foundations ...": the
+// forward-pass equation applies A to x first; section "Gradient Dynamics and
+// Backpropagation Mechanics": dY B appears in both dL/dA and dL/dx.)
+//
+// Both read their M x K activation operand once and are bound by that stream.
+// A workgroup of 8 waves owns 16 rows; the waves split the reduction into
+// eight contiguous ranges of 32-wide units and add their partial sums through
+// LDS in a fixed order at the end.  Each unit is one v_mfma_f32_16x16x32_bf16
+// per 16 rank columns, the activation rows as the A operand (lane (g, l16):
+// row l16, 16 bytes at reduction 8 g, loaded straight from global memory) and
+// the rank-side matrix as the B operand:
+//   * G = A (r x K, reduction contiguous): lane (g, l16) loads row l16 of A
+//     (clamped to r - 1; those result columns are never stored);
+//   * G = B^T (B is K x r, rank contiguous): the 32 R rows of B that a round
+//     of R units needs are one contiguous block of memory, loaded with
+//     16-byte loads, stored to a per-wave LDS tile in storage order and read
+//     back with the transposing ds_read_b64_tr_b16 (inside each 16-lane group
+//     lane c addresses row c / 4, columns 4 (c % 4) .. +3; lane i receives
+//     column i of the four rows).  8-byte aligned reads need r % 4 == 0.
+// The loads of the next round are issued before the products of the current
+// one; reduction units past the wave's range (clamped loads) are masked to
+// zero.
+#include "device_util.h"
+#include "dispatch.h"
+
+namespace lq {
+namespace {
+
+constexpr int kSW = 8;  // waves per workgroup
+constexpr int kSThreads = 64 * kSW;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 tr_read(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4* lds_ptr;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <int JT, bool GT>
+__global__ __launch_bounds__(kSThreads) void shrink_kernel(const uint16_t* __restrict__ Z,
+                                                           int64_t M, int64_t K,
+                                                           const uint16_t* __restrict__ G,
+                                                           int r, float* __restrict__ out,
+                                                           int32_t* __restrict__ zero, int nzero) {
+  constexpr int RC = 16 * JT;    // rank columns, padded
+  constexpr int R = 8 / JT;      // units per round
+  constexpr int NB = R * JT;     // GT: 1 KB pieces of B per round (32 R rows of up to RC)
+  __shared__ __attribute__((aligned(16))) uint16_t gtile[GT ? kSW : 1][GT ? NB * 512 : 8];
+  __shared__ f32x4 red[kSW][JT][64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  // side job: clear the next kernel's flag words (a kernel store, so it also
+  // replays correctly inside a captured graph)
+  if (blockIdx.x == 0)
+    for (int i = tid; i < nzero; i += kSThreads) zero[i] = 0;
+
+  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  int64_t mr = m0 + l16;
+  mr = mr < M ? mr : M - 1;
+  const int64_t UT = K >> 5;
+  const int64_t u0 = UT * wave / kSW, u1 = UT * (wave + 1) / kSW;
+  const uint16_t* zrow = Z + mr * K + 8 * g;
+  const uint16_t* arow[JT];
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt) {
+    int j = 16 * jt + l16;
+    j = j < r ? j : r - 1;
+    arow[jt] = G + (int64_t)j * K + 8 * g;
+  }
+  const int64_t gbytes = K * r * 2;  // GT: bytes of B
+  const char* gb = reinterpret_cast<const char*>(G);
+
+  struct Round {
+    u32x4 z[R];
+    u32x4 a[GT ? 1 : R][JT];
+    u32x4 b[GT ? NB : 1];
+  };
+  auto load = [&](Round& d, int64_t u) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      int64_t uq = u + q;
+      uq = uq < u1 ? uq : u1 - 1;
+      d.z[q] = *reinterpret_cast<const u32x4*>(zrow + 32 * uq);
+      if (!GT)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+          d.a[q][jt] = *reinterpret_cast<const u32x4*>(arow[jt] + 32 * uq);
+    }
+    if (GT) {
+      const int64_t base = u * 32 * r * 2;
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        int64_t off = base + 1024 * t + 16 * lane;
+        off = off <= gbytes - 16 ? off : gbytes - 16;
+        d.b[t] = *reinterpret_cast<const u32x4*>(gb + off);
+      }
+    }
+  };
+
+  f32x4 acc[JT];
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](const Round& d, int64_t u) {
+    uint16_t* tl = gtile[GT ? wave : 0];
+    if (GT) {
+      // the wave's own tile; its LDS operations run in order, so these stores
+      // land before the reads below and after the previous round's reads
+#pragma unroll
+      for (int t = 0; t < NB; ++t) *reinterpret_cast<u32x4*>(tl + 512 * t + 8 * lane) = d.b[t];
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const u32x4 zq = sel4(u + q < u1, d.z[q]);
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) {
+        u32x4 gf;
+        if (GT) {
+          const uint16_t* p = tl + (32 * q + 8 * g + (l16 >> 2)) * r + 16 * jt + 4 * (l16 & 3);
+          const u32x2 lo = tr_read(p), hi = tr_read(p + 4 * r);
+          gf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          gf = d.a[q][jt];
+        }
+        acc[jt] = mfma16(zq, gf, acc[jt]);
+      }
+    }
+  };
+
+  if (u0 < u1) {
+    Round d0, d1;
+    load(d0, u0);
+    for (int64_t u = u0; u < u1; u += 2 * R) {
+      if (u + R < u1) load(d1, u + R);
+      compute(d0, u);
+      if (u + R < u1) {
+        if (u + 2 * R < u1) load(d0, u + 2 * R);
+        compute(d1, u + R);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt) red[wave][jt][lane] = acc[jt];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      f32x4 s = red[0][jt][lane];
+#pragma unroll
+      for (int w = 1; w < kSW; ++w) s += red[w][jt][lane];
+      const int j = 16 * jt + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + 4 * g + i;
+        if (m < M && j < r) out[m * r + j] = s[i];
+      }
+    }
+  }
+}
+
+template <bool GT>
+int launch(const uint16_t* Z, int64_t M, int64_t K, const uint16_t* G, int64_t r, float* out,
+           int32_t* zero, int nzero, hipStream_t st) {
+  const dim3 grid((unsigned)cdiv(M, 16)), block(kSThreads);
+  switch ((r + 15) / 16) {
+    case 1:
+      hipLaunchKernelGGL((shrink_kernel<1, GT>), grid, block, 0, st, Z, M, K, G, (int)r, out,
+                         zero, nzero);
+      break;
+    case 2:
+      hipLaunchKernelGGL((shrink_kernel<2, GT>), grid, block, 0, st, Z, M, K, G, (int)r, out,
+                         zero, nzero);
+      break;
+    default:
+      hipLaunchKernelGGL((shrink_kernel<4, GT>), grid, block, 0, st, Z, M, K, G, (int)r, out,
+                         zero, nzero);
+      break;
+  }
+  return hip_fail(hipGetLastError(), "shrink launch");
+}
+
+}  // namespace
+
+namespace dispatch {
+
+bool shrink_eligible(bool gt, int64_t r) { return !gt || r % 4 == 0; }
+
+int launch_shrink(const void* Z, int64_t M, int64_t K, const void* G, bool gt, int64_t r,
+                  float* out, int32_t* zero, int nzero, hipStream_t st) {
+  if (gt)
+    return launch<true>((const uint16_t*)Z, M, K, (const uint16_t*)G, r, out, zero, nzero, st);
+  return launch<false>((const uint16_t*)Z, M, K, (const uint16_t*)G, r, out, zero, nzero, st);
+}
+
+}  // namespace dispatch
+}  // namespace lq

@@ -21,7 +21,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "lq.h")
 
 LQ_F32, LQ_BF16 = 0, 1
 LQ_WEIGHT_DENSE, LQ_WEIGHT_NF4 = 0, 1
-LQ_OP_FWD, LQ_OP_BWD, LQ_OP_FWD_MULTI = 0, 1, 2
+LQ_OP_FWD, LQ_OP_BWD, LQ_OP_FWD_MULTI, LQ_OP_FWD_FUSED, LQ_OP_BWD_FUSED = 0, 1, 2, 3, 4
 STATUS = {0: "LQ_OK", -1: "LQ_ERR_INVALID_ARG", -2: "LQ_ERR_UNSUPPORTED",
           -3: "LQ_ERR_WORKSPACE", -4: "LQ_ERR_HIP"}
 
@@ -200,7 +200,7 @@ def _ws(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def lq_lora_fwd(X, W0, A, B, scale, T_out=None, ws=None, Y=None):
+def lq_lora_fwd(X, W0, A, B, scale, T_out=None, ws=None, Y=None, fused=False):
     _dev(X, A, B, T_out)
     dt = _dt(X)
     M = X.shape[0]
@@ -208,11 +208,11 @@ def lq_lora_fwd(X, W0, A, B, scale, T_out=None, ws=None, Y=None):
     if Y is None:
         Y = torch.empty((M, ws_struct.N), dtype=X.dtype, device=X.device)
     r = A.shape[0]
-    decode = dt == LQ_BF16 and M <= 16
-    need = (lq_workspace_size(LQ_OP_FWD, M, ws_struct.N, ws_struct.K, r)
-            if (T_out is None or decode) else 0)
-    if ws is None and need:
-        ws = _ws(need, X.device)
+    if ws is None:
+        need = lq_workspace_size(LQ_OP_FWD_FUSED if fused else LQ_OP_FWD, M, ws_struct.N,
+                                 ws_struct.K, r)
+        if need:
+            ws = _ws(need, X.device)
     _check(lib().lq_lora_fwd(_ptr(X), M, ctypes.byref(ws_struct), _ptr(A), _ptr(B), r, scale, dt,
                              _ptr(Y), _ptr(T_out), _ptr(ws), 0 if ws is None else ws.numel(),
                              _stream()))
@@ -220,7 +220,7 @@ def lq_lora_fwd(X, W0, A, B, scale, T_out=None, ws=None, Y=None):
 
 
 def lq_lora_bwd(dY, X, W0, A, B, scale, T_saved=None, need_dx=True, dA=None, dB=None,
-                accumulate=False, ws=None, dX=None, need_grads=True):
+                accumulate=False, ws=None, dX=None, need_grads=True, fused=False):
     _dev(dY, X, A, B, T_saved, dA, dB, dX)
     dt = _dt(dY)
     M = dY.shape[0]
@@ -234,7 +234,7 @@ def lq_lora_bwd(dY, X, W0, A, B, scale, T_saved=None, need_dx=True, dA=None, dB=
     if need_grads and dB is None:
         dB = torch.empty((w.N, r), dtype=torch.float32, device=dev)
     if ws is None:
-        ws = _ws(lq_workspace_size(LQ_OP_BWD, M, w.N, w.K, r), dev)
+        ws = _ws(lq_workspace_size(LQ_OP_BWD_FUSED if fused else LQ_OP_BWD, M, w.N, w.K, r), dev)
     _check(lib().lq_lora_bwd(_ptr(dY), _ptr(X), M, ctypes.byref(w), _ptr(A), _ptr(B), r, scale, dt,
                              _ptr(T_saved), _ptr(dX), _ptr(dA), _ptr(dB), int(accumulate),
                              _ptr(ws), ws.numel(), _stream()))

@@ -30,7 +30,7 @@ def base_for(c, kind):
     return to_dev(c["W0"]), W0v.astype(np.float64)
 
 
-def check_layer(c, kind, rows=None, bwd=True, merge=True, label=""):
+def check_layer(c, kind, rows=None, bwd=True, merge=True, label="", fused=False):
     s = c["alpha"] / c["r"]
     X, A, B = to_dev(c["X"]), to_dev(c["A"]), to_dev(c["B"])
     Wd, Wo = base_for(c, kind)
@@ -39,7 +39,7 @@ def check_layer(c, kind, rows=None, bwd=True, merge=True, label=""):
     sel = np.arange(M) if rows is None else rows
     announce(f"bf16 fwd {label} {kind} M={M} N={Wo.shape[0]} K={Wo.shape[1]} r={r}")
     T = torch.empty((M, r), dtype=torch.float32, device=X.device)
-    Y = lq.lq_lora_fwd(X, Wd, A, B, s, T_out=T)
+    Y = lq.lq_lora_fwd(X, Wd, A, B, s, T_out=T, fused=fused)
     torch.cuda.synchronize()
     Yo, _, To = olora.lora_forward(Xo[sel], Wo, Ao, Bo, s)
     e = rel_err(f64(Y)[sel], Yo)
@@ -49,7 +49,8 @@ def check_layer(c, kind, rows=None, bwd=True, merge=True, label=""):
     if bwd:
         announce(f"bf16 bwd {label} {kind} M={M}")
         dY = to_dev(c["dY"])
-        dX, dA, dB = lq.lq_lora_bwd(dY, X, Wd, A, B, s, T_saved=T if M > 16 else None)
+        dX, dA, dB = lq.lq_lora_bwd(dY, X, Wd, A, B, s, T_saved=T if M > 16 else None,
+                                    fused=fused)
         torch.cuda.synchronize()
         dYo = c["dY"].f64()
         dXo = dYo[sel] @ Wo + s * ((dYo[sel] @ Bo) @ Ao)
@@ -62,7 +63,7 @@ def check_layer(c, kind, rows=None, bwd=True, merge=True, label=""):
             e = rel_err(f64(got), want)
             assert e <= BF16_TOL, f"{name} rel err {e:.3e}"
         # dX alone (dA = dB = NULL) runs the same kernel: bit-identical dX
-        dX2, dA2, dB2 = lq.lq_lora_bwd(dY, X, Wd, A, B, s, need_grads=False)
+        dX2, dA2, dB2 = lq.lq_lora_bwd(dY, X, Wd, A, B, s, need_grads=False, fused=fused)
         torch.cuda.synchronize()
         assert dA2 is None and dB2 is None
         assert torch.equal(dX2, dX), "dX-only call differs from the full backward"
@@ -89,6 +90,30 @@ def test_small(shape, kind):
     M, N, K, r = shape
     c = wl.small_case(M, N, K, r, seed=M + N + K + r)
     check_layer(c, kind, label="small")
+
+
+# Shapes that take the large-tile path (256 x 256 tiles, bf16 weight copy in
+# the workspace) with the default workspace, and the fused kernels with the
+# smaller LQ_OP_*_FUSED workspace.
+LARGE = [
+    (2100, 256, 256, 16),    # split K (9 tiles), ragged last row tile
+    (2304, 512, 768, 5),     # split K, odd rank, three 256-wide dX tiles
+    (2048, 5376, 256, 64),   # 256 x 128 forward tiles, no split; rank 64
+    (4096, 3072, 256, 16),   # 256 x 256 forward tiles
+]
+
+
+@pytest.mark.parametrize("kind", ["dense", "nf4"])
+@pytest.mark.parametrize("shape", LARGE, ids=[f"{m}x{n}x{k}r{r}" for m, n, k, r in LARGE])
+def test_large_tile_path(shape, kind):
+    M, N, K, r = shape
+    assert (lq.lq_workspace_size(lq.LQ_OP_FWD, M, N, K, r)
+            > lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, M, N, K, r))
+    assert (lq.lq_workspace_size(lq.LQ_OP_BWD, M, N, K, r)
+            > lq.lq_workspace_size(lq.LQ_OP_BWD_FUSED, M, N, K, r))
+    c = wl.small_case(M, N, K, r, seed=M + N + K + r + 7)
+    check_layer(c, kind, merge=False, label="large")
+    check_layer(c, kind, merge=False, bwd=kind == "nf4", label="large-fused", fused=True)
 
 
 @pytest.mark.parametrize("kind", ["dense", "nf4"])
