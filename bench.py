@@ -4,15 +4,18 @@
 Default run (python bench.py [--steps K] [--warmup W]):
 
 * step = one forward + backward of the QLoRA linear at 4096 x 4096, NF4 base
-  with double quantisation, r = 16, alpha = 32, M = 2048 tokens, bf16 compute
-  (the fused forward kernel, then the fused dX kernel and the dA / dB
-  reductions).  value = algorithmic fwd+bwd FLOPs / wall time per step.
-* roofline: the dominant kernel -- the fused forward or the fused dX kernel,
-  whichever is slower (both do 2 M N K + 2 M r (N + K) FLOPs) -- timed alone
-  with HIP events on the stream it runs on, algorithmic FLOPs per launch /
-  average duration, against the bf16 dense MFMA peak; traffic (HBM bytes per
-  launch) from rocprofv3 FETCH_SIZE / WRITE_SIZE counters scaled by the same
-  counters on a plain copy, when they were taken on the current kernel source.
+  with double quantisation, r = 16, alpha = 32, M = 2048 tokens, bf16 compute.
+  Forward: NF4 -> bf16 weight copy, T = X A^T, then the large-tile product
+  with the expand.  Backward: the same for dX (U = dY B), then the dA / dB
+  reductions.  value = algorithmic fwd+bwd FLOPs / wall time per step.
+* roofline: the dominant kernel -- the large-tile product of the forward or
+  of dX, whichever is slower (each does 2 M N K + 2 M N r FLOPs: the product
+  and the rank-r expand) -- timed with HIP events that the library records
+  around its launches on the launch stream (lq_timing_enable), algorithmic
+  FLOPs per launch / average duration, against the bf16 dense MFMA peak;
+  traffic (HBM bytes per launch) from rocprofv3 FETCH_SIZE / WRITE_SIZE
+  counters scaled by the same counters on a plain copy, when they were taken
+  on the current kernel source.
 * cpu_baseline: the CPU oracle (float64 NumPy) on the same step.
 * secondary lines in the same JSON object: NF4 decode (M = 1, 4, 16) GB/s on
   the weight stream with cold weights, merge, quantise, multi-adapter.
@@ -37,7 +40,7 @@ METRIC = "QLoRA linear fwd+bwd TFLOP/s (4096²,r=16,M=2048); NF4 decode HBM GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 M, N, K, R = 2048, 4096, 4096, 16
-FWD_FLOP = 2 * M * N * K + 2 * M * R * K + 2 * M * N * R          # fused forward kernel
+G256_FLOP = 2 * M * N * K + 2 * M * N * R                         # product + expand kernel
 STEP_FLOP = 2 * (2 * M * N * K) + 6 * M * R * (N + K)             # fwd + bwd, algorithmic
 NF4_STREAM_BYTES = N * K // 2 + N * K // 64 + 4 * (N * K // 64 // 256)   # 8,654,848
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -56,7 +59,7 @@ def src_hash(files):
     return h.hexdigest()[:16]
 
 
-FWD_SOURCES = ["lora_bf16.hip", "device_util.h", "common.h"]
+G256_SOURCES = ["gemm256.hip", "device_util.h", "common.h"]
 
 
 def traffic_for(kernel, sources):
@@ -109,13 +112,15 @@ def setup(torch):
     S["dB"] = torch.empty((N, R), dtype=torch.float32, device=dev)
     S["ws"] = torch.empty(lq.lq_workspace_size(lq.LQ_OP_BWD, M, N, K, R), dtype=torch.uint8,
                           device=dev)
+    S["wsf"] = torch.empty(lq.lq_workspace_size(lq.LQ_OP_FWD, M, N, K, R), dtype=torch.uint8,
+                           device=dev)
     torch.cuda.synchronize()
     return S
 
 
 def fwd(S):
     lq = S["lq"]
-    lq.lq_lora_fwd(S["X"], S["W"], S["A"], S["B"], S["s"], T_out=S["T"], Y=S["Y"])
+    lq.lq_lora_fwd(S["X"], S["W"], S["A"], S["B"], S["s"], T_out=S["T"], Y=S["Y"], ws=S["wsf"])
 
 
 def bwd(S):
@@ -288,7 +293,7 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
-              "(the layer shards by tokens with one all-reduce of dA/dB; see DESIGN.md)",
+              "(the layer would shard by tokens, with one all-reduce of dA and dB)",
               file=sys.stderr)
         return 2
 
@@ -350,23 +355,38 @@ def main(argv=None):
     ms_per_step = wall * 1e3 / a.steps
     value = STEP_FLOP / (wall / a.steps) / 1e12
 
-    # dominant kernel: the fused forward GEMM or the fused dX GEMM (the same
-    # algorithmic FLOPs), each alone, HIP events on the stream it runs on
-    t_fwd = cuda_time(lambda: fwd(S), 50, torch)
-    t_dx = cuda_time(lambda: dx_only(S), 50, torch)
+    # dominant kernel: the large-tile product of the forward or of dX (the
+    # same algorithmic FLOPs); event pairs recorded by the library around each
+    # launch, on the stream it is launched on
+    lq = S["lq"]
+    t_fwd_call = cuda_time(lambda: fwd(S), 50, torch)
+    t_dx_call = cuda_time(lambda: dx_only(S), 50, torch)
     t_step_ev = cuda_time(lambda: step(S), 20, torch)
+    lq.lq_timing_enable(True)
+    lq.lq_timing_read("g256_fwd")
+    lq.lq_timing_read("g256_dx")
+    for _ in range(50):
+        fwd(S)
+        dx_only(S)
+    torch.cuda.synchronize()
+    ms_f, n_f = lq.lq_timing_read("g256_fwd")
+    ms_d, n_d = lq.lq_timing_read("g256_dx")
+    lq.lq_timing_enable(False)
+    t_fwd, t_dx = ms_f / max(n_f, 1), ms_d / max(n_d, 1)
     if t_dx > t_fwd:
-        name, t_dom = "dx_kernel (fused NF4 dequant + transposed GEMM + shrink/expand)", t_dx
-        traffic = traffic_for("dx_kernel", FWD_SOURCES)
+        name, t_dom = "g256_kernel<dX> (bf16 product dY Wd + expand, 256x128 tiles)", t_dx
+        traffic = traffic_for("g256_dx", G256_SOURCES)
     else:
-        name, t_dom = "fwd_kernel (fused NF4 dequant + GEMM + shrink/expand)", t_fwd
-        traffic = traffic_for("fwd_kernel", FWD_SOURCES)
-    achieved = FWD_FLOP / (t_dom * 1e-3) / 1e12
+        name, t_dom = "g256_kernel<fwd> (bf16 product X Wd^T + expand, 256x128 tiles)", t_fwd
+        traffic = traffic_for("g256_fwd", G256_SOURCES)
+    achieved = G256_FLOP / (t_dom * 1e-3) / 1e12
     roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 1),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-            "flop_per_launch": FWD_FLOP, "us_per_launch": round(t_dom * 1e3, 2),
-            "us_fwd_kernel": round(t_fwd * 1e3, 2), "us_dx_kernel": round(t_dx * 1e3, 2)}
+            "flop_per_launch": G256_FLOP, "us_per_launch": round(t_dom * 1e3, 2),
+            "launches_timed": min(n_f, n_d),
+            "us_fwd_kernel": round(t_fwd * 1e3, 2), "us_dx_kernel": round(t_dx * 1e3, 2),
+            "us_fwd_call": round(t_fwd_call * 1e3, 2), "us_dx_call": round(t_dx_call * 1e3, 2)}
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",

@@ -237,6 +237,20 @@ int64_t lq_lora_num_params(int64_t N, int64_t K, int64_t r);
 /* Message for the last failed call on this thread ("" if none). */
 const char* lq_last_error(void);
 
+/*
+ * Kernel timing, a measurement aid for benchmarks (not from the pages).  While
+ * enabled (on != 0), each launch of the product kernels is bracketed by a
+ * pair of HIP events recorded on the launch stream; names: "g256_fwd" and
+ * "g256_dx" (large-tile forward and dX products), "fwd_kernel" and
+ * "dx_kernel" (fused forward and dX).  Off by default; do not enable it while
+ * a stream is being captured into a graph.
+ * lq_timing_read waits for the recorded launches of kernel ``name`` and
+ * returns the sum of their event-measured durations (milliseconds) and their
+ * number, then forgets them.  Host pointers; LQ_ERR_INVALID_ARG on NULL.
+ */
+int lq_timing_enable(int32_t on);
+int lq_timing_read(const char* name, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

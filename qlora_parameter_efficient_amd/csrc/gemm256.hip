@@ -528,6 +528,7 @@ int launch_g256(bool tr, const void* P, const void* Q, const float* V, const voi
   p.part = (float*)(w + g256_flag_bytes(M, NI));
   p.tpx = (int32_t)cdiv(pl.tiles, 8);
   const unsigned blocks = (unsigned)(p.splits == 2 ? 16 * (int64_t)p.tpx : pl.tiles);
+  timing_begin(tr ? "g256_dx" : "g256_fwd", st);
   if (tr) {
     if (pl.jm == 4) launch_shape<true, 4>(p, blocks, st);
     else launch_shape<true, 2>(p, blocks, st);
@@ -535,6 +536,7 @@ int launch_g256(bool tr, const void* P, const void* Q, const float* V, const voi
     if (pl.jm == 4) launch_shape<false, 4>(p, blocks, st);
     else launch_shape<false, 2>(p, blocks, st);
   }
+  timing_end(st);
   return hip_fail(hipGetLastError(), "g256 launch");
 }
 

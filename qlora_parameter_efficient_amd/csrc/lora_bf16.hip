@@ -991,7 +991,9 @@ int launch_fwd(const FwdParams& p0, hipStream_t st) {
   p.n_tiles = (int)cdiv(p.W.N, kTileI);
   p.m_tiles = (int)cdiv(p.M, 128 * MS);
   const int blocks = p.n_tiles * p.m_tiles;
+  timing_begin("fwd_kernel", st);
   hipLaunchKernelGGL((fwd_kernel<WK, MS, RP, MULTI>), dim3(blocks), dim3(kThreads), 0, st, p);
+  timing_end(st);
   return hip_fail(hipGetLastError(), "fwd_kernel launch");
 }
 
@@ -1020,7 +1022,9 @@ int launch_dx(const BwdParams& p0, hipStream_t st) {
   p.k_tiles = (int)cdiv(p.W.K, kTileI);
   p.m_tiles = (int)cdiv(p.M, 128 * MS);
   const int blocks = p.k_tiles * p.m_tiles;
+  timing_begin("dx_kernel", st);
   hipLaunchKernelGGL((dx_kernel<WK, MS, RP, BV>), dim3(blocks), dim3(kThreads), 0, st, p);
+  timing_end(st);
   return hip_fail(hipGetLastError(), "dx_kernel launch");
 }
 

@@ -60,6 +60,9 @@ _SIGS = {
     "lq_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i64, _i32]),
     "lq_lora_num_params": (_i64, [_i64, _i64, _i64]),
     "lq_last_error": (ctypes.c_char_p, []),
+    "lq_timing_enable": (ctypes.c_int, [_i32]),
+    "lq_timing_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_int64)]),
 }
 
 
@@ -284,3 +287,14 @@ def lq_lora_num_params(N, K, r):
 
 def lq_last_error():
     return lib().lq_last_error().decode()
+
+
+def lq_timing_enable(on=True):
+    _check(lib().lq_timing_enable(int(bool(on))))
+
+
+def lq_timing_read(name):
+    """(total milliseconds, launches) of kernel ``name`` since the last read."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(lib().lq_timing_read(name.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

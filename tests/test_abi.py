@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(lq.LIB_PATH),
 
 def test_exports_every_declared_symbol():
     declared = lq.declared_symbols()
-    assert len(declared) == 11
+    assert len(declared) == 13
     L = lq.lib()
     for name in declared:
         assert hasattr(L, name), name
@@ -115,3 +115,10 @@ def test_argument_errors_launch_nothing():
     w2 = _weight()
     w2.reserved = 1
     assert _fwd(w2) == -1
+
+
+def test_timing_read_without_launches():
+    lq.lq_timing_enable(True)
+    assert lq.lq_timing_read("g256_fwd") == (0.0, 0)
+    lq.lq_timing_enable(False)
+    assert lq.lib().lq_timing_read(None, None, None) == -1
