@@ -7,7 +7,9 @@ Default run (python bench.py [--steps K] [--warmup W]):
   with double quantisation, r = 16, alpha = 32, M = 2048 tokens, bf16 compute.
   Forward: NF4 -> bf16 weight copy, T = X A^T, then the large-tile product
   with the expand.  Backward: the same for dX (U = dY B), then the dA / dB
-  reductions.  value = algorithmic fwd+bwd FLOPs / wall time per step.
+  reductions.  value = algorithmic fwd+bwd FLOPs / wall time per step, the
+  step launched eagerly (the same step replayed from a HIP graph is reported
+  beside it: on this stack the replay is not faster).
 * roofline: the dominant kernel -- the large-tile product of the forward or
   of dX, whichever is slower (each does 2 M N K + 2 M N r FLOPs: the product
   and the rank-r expand) -- timed with HIP events that the library records
@@ -138,6 +140,20 @@ def dx_only(S):
 def step(S):
     fwd(S)
     bwd(S)
+
+
+def step_graph(S, torch):
+    """One step captured in a HIP graph (all buffers preallocated in S)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(S)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(S)
+    torch.cuda.synchronize()
+    return g
 
 
 def cpu_baseline(S):
@@ -354,6 +370,17 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / a.steps
     value = STEP_FLOP / (wall / a.steps) / 1e12
+    # the same step captured in a HIP graph and replayed, for reference
+    g = step_graph(S, torch)
+    for _ in range(a.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms_graph = (time.perf_counter() - t0) * 1e3 / a.steps
+    del g
 
     # dominant kernel: the large-tile product of the forward or of dX (the
     # same algorithmic FLOPs); event pairs recorded by the library around each
@@ -395,6 +422,7 @@ def main(argv=None):
                                   "quant block 256), r=16, alpha=32, X 2048x4096 bf16, dY 2048x4096",
                       "M": M, "N": N, "K": K, "r": R, "step_flop": STEP_FLOP},
            "gpu_event_ms_per_step": round(t_step_ev, 4),
+           "graph_ms_per_step": round(ms_graph, 4),
            "roofline": roof}
     if not a.no_cpu:
         log("timing the CPU oracle ...")

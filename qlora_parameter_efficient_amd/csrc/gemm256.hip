@@ -71,6 +71,8 @@ struct Shape {
   static constexpr int PBytes = TJ * kGK * 2;             // activation tile of one step
   static constexpr int Stage = kTileBytes + PBytes;       // LDS stage
   static constexpr int Slot = kGT * TJ;                   // split-K partial (floats)
+  static constexpr int NST = 2;                           // LDS stages (3 measured no faster)
+  static constexpr int DMA = 8 + 2 * JM;                  // loads per wave per step
 };
 constexpr int kSpinLimit = 1 << 22;          // split-K wait bound (s_sleep 2 each)
 
@@ -113,6 +115,12 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t l
 }
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// wait until at most N of this wave's loads are outstanding
+template <int N>
+__device__ __forceinline__ void wait_dma_but() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -180,7 +188,7 @@ __device__ __forceinline__ u32x4 e_operand_col(const uint16_t* A, int64_t ld, in
 template <bool TR, int JM>
 __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
   using S = Shape<JM>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * S::Stage];
+  __shared__ __attribute__((aligned(1024))) char smem[S::NST * S::Stage];
   __shared__ int s_first, s_ready;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -310,11 +318,15 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
   // one step on LDS stage B (compile-time, so that every operand address is a
-  // per-lane base plus an immediate): loads of step kt + 1 into the other
-  // stage first, then four substeps whose LDS reads run one substep ahead
+  // per-lane base plus an immediate): the loads of step kt + NST - 1 go into
+  // the stage read one step earlier, then four substeps whose LDS reads run
+  // one substep ahead; before the barrier, wait until the loads of step
+  // kt + 1 have landed (those of later steps stay in flight)
+  constexpr int NST = S::NST;
   auto step = [&](int kt, auto stage) {
     constexpr int B = decltype(stage)::value;
-    if (kt + 1 < kt1) issue(kt + 1, B ^ 1);
+    const bool more = kt + NST - 1 < kt1;
+    if (more) issue(kt + NST - 1, (B + NST - 1) % NST);
     const uint32_t st = sbase + B * S::Stage;
     u32x4 wf[2][4], xf[2][JM];
     load_frags(st, 0, wf[0], xf[0]);
@@ -328,19 +340,40 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
 #pragma unroll
         for (int ms = 0; ms < JM; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf[c][ms], acc[ns][ms]);
     }
-    wait_dma();
+    if (NST > 2 && more)
+      wait_dma_but<S::DMA>();
+    else
+      wait_dma();
     __syncthreads();
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   if (kt0 < kt1) {
     issue(kt0, 0);
-    wait_dma();
+    if (NST > 2 && kt0 + 1 < kt1) {
+      issue(kt0 + 1, 1);
+      wait_dma_but<S::DMA>();
+    } else {
+      wait_dma();
+    }
     __syncthreads();
     int kt = kt0;
-    for (; kt + 1 < kt1; kt += 2) {
-      step(kt, std::integral_constant<int, 0>{});
-      step(kt + 1, std::integral_constant<int, 1>{});
+    if (NST == 2) {
+      for (; kt + 1 < kt1; kt += 2) {
+        step(kt, I0{});
+        step(kt + 1, I1{});
+      }
+      if (kt < kt1) step(kt, I0{});
+    } else {
+      for (; kt + 2 < kt1; kt += 3) {
+        step(kt, I0{});
+        step(kt + 1, I1{});
+        step(kt + 2, I2{});
+      }
+      if (kt < kt1) step(kt, I0{});
+      if (kt + 1 < kt1) step(kt + 1, I1{});
     }
-    if (kt < kt1) step(kt, std::integral_constant<int, 0>{});
   }
 
   // ---- split-K: the second workgroup of a tile to finish completes it.
