@@ -54,6 +54,10 @@ int u_only(const void* dY, int64_t M, int64_t N, const void* B, int64_t r, float
 // The 8-wave shrink kernel behind t_only / u_only (gt: G is B, K x r; needs
 // r % 4 == 0), with the older one-pass kernel as the fallback.
 bool shrink_eligible(bool gt, int64_t r);
+// One launch: the NF4 weight W dequantised to bf16 at wout, and the shrink of
+// launch_shrink (same arguments), the flag words cleared as well.
+int launch_prep(const lq_weight& W, void* wout, const void* Z, int64_t M, int64_t K, const void* G,
+                bool gt, int64_t r, float* out, int32_t* zero, int nzero, hipStream_t st);
 int launch_shrink(const void* Z, int64_t M, int64_t K, const void* G, bool gt, int64_t r,
                   float* out, int32_t* zero, int nzero, hipStream_t st);
 

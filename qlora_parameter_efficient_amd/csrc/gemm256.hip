@@ -573,13 +573,11 @@ int launch_g256(bool tr, const void* P, const void* Q, const float* V, const voi
   return hip_fail(hipGetLastError(), "g256 launch");
 }
 
-// bf16 weight for the product: the dense W0 itself, or W0 dequantised into
-// the workspace at q
-const void* bf16_weight(const lq_weight& W, void* q, hipStream_t st, int* err) {
-  if (W.kind == LQ_WEIGHT_DENSE) return W.dense;
-  *err = launch_nf4_dequantize(W.codes, W.q8, W.c2, W.absmax, W.double_quant, W.N * W.K, q,
+// the NF4 weight dequantised to bf16 into the workspace at q (when the prep
+// kernel cannot take the shrink as well)
+int bf16_weight(const lq_weight& W, void* q, hipStream_t st) {
+  return launch_nf4_dequantize(W.codes, W.q8, W.c2, W.absmax, W.double_quant, W.N * W.K, q,
                                LQ_BF16, st);
-  return q;
 }
 
 }  // namespace
@@ -606,10 +604,13 @@ int big_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const v
   float* T = T_out ? T_out : (float*)w;
   w += align256((size_t)(M * r) * 4);
   int e = 0;
-  const void* Q = bf16_weight(W, w, st, &e);
+  const int nz = (int)(g256_flag_bytes(M, N) / 4);
+  const void* Q = W.kind == LQ_WEIGHT_DENSE ? W.dense : (const void*)w;
+  if (W.kind != LQ_WEIGHT_DENSE && shrink_eligible(false, r))
+    e = launch_prep(W, w, X, M, K, A, false, r, T, (int32_t*)gws, nz, st);
+  else if (!(e = W.kind == LQ_WEIGHT_DENSE ? 0 : bf16_weight(W, w, st)))
+    e = t_only(X, M, K, A, r, T, st, (int32_t*)gws, nz);
   if (e) return e;
-  if ((e = t_only(X, M, K, A, r, T, st, (int32_t*)gws, (int)(g256_flag_bytes(M, N) / 4))))
-    return e;
   return launch_g256(false, X, Q, T, B, M, N, K, r, s, Y, gws, st);
 }
 
@@ -620,10 +621,13 @@ int big_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const v
   void* gws = w;
   w += align256(g256_ws_bytes(M, K));
   int e = 0;
-  const void* Q = bf16_weight(W, w, st, &e);
+  const int nz = (int)(g256_flag_bytes(M, K) / 4);
+  const void* Q = W.kind == LQ_WEIGHT_DENSE ? W.dense : (const void*)w;
+  if (W.kind != LQ_WEIGHT_DENSE && shrink_eligible(true, r))
+    e = launch_prep(W, w, dY, M, N, B, true, r, U, (int32_t*)gws, nz, st);
+  else if (!(e = W.kind == LQ_WEIGHT_DENSE ? 0 : bf16_weight(W, w, st)))
+    e = u_only(dY, M, N, B, r, U, st, (int32_t*)gws, nz);
   if (e) return e;
-  if ((e = u_only(dY, M, N, B, r, U, st, (int32_t*)gws, (int)(g256_flag_bytes(M, K) / 4))))
-    return e;
   return launch_g256(true, dY, Q, U, A, M, K, N, r, s, dX, gws, st);
 }
 

@@ -13,6 +13,7 @@
 // multiply-add anywhere in the arithmetic (only lone products and quotients),
 // rintf (ties to even) for the 8-bit constant, and RNE for bf16 stores.
 #include "common.h"
+#include "nf4_deq.h"
 
 namespace lq {
 namespace {
@@ -149,69 +150,12 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quantize_kernel(
   }
 }
 
-// Standalone dequantiser.  A workgroup covers 32768 elements (two groups of
-// 256 blocks); thread t owns the 16 chunks of 8 elements t + 256 i, so
-// consecutive lanes read consecutive code words and write consecutive 16-byte
-// (bf16) or 32-byte (float32) pieces.  All code words and block constants are
-// loaded before any arithmetic; the second-level steps fl32(c2 / 127) of the
-// workgroup's groups come from a small LDS table.  A partial last chunk (n
-// not a multiple of 8) is finished element by element.
-constexpr int kDeqThreads = 256;
-constexpr int kDeqChunks = 16;                                   // chunks of 8 per thread
-constexpr int64_t kDeqSpan = (int64_t)kDeqThreads * kDeqChunks * 8;  // 32768 elements
-
 template <bool BF16OUT>
 __global__ __launch_bounds__(kDeqThreads) void nf4_dequantize_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
     const float* __restrict__ c2, const float* __restrict__ absmax, int32_t double_quant,
     int64_t n, void* __restrict__ out, NF4Table tab) {
-  __shared__ float cbs[16];
-  __shared__ float steps[4];
-  const int t = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * kDeqSpan;
-  const int64_t g_lo = base / kGroupElems;
-  const int64_t ngroups = (n + kGroupElems - 1) / kGroupElems;
-  if (t < 16) cbs[t] = tab.cb[t];
-  if (double_quant && t < 3 && g_lo + t < ngroups) steps[t] = dq_step(c2[g_lo + t]);
-  uint32_t cw[kDeqChunks], qv[kDeqChunks];
-#pragma unroll
-  for (int i = 0; i < kDeqChunks; ++i) {
-    int64_t e = base + 8 * (int64_t)(t + kDeqThreads * i);
-    e = e < n ? e : 0;  // chunks past the end are not stored
-    const int64_t blk = e / LQ_NF4_BLOCK;
-    cw[i] = e + 8 <= n ? *reinterpret_cast<const uint32_t*>(codes + (e >> 1)) : 0u;
-    qv[i] = double_quant ? (uint32_t)q8[blk] : __float_as_uint(absmax[blk]);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kDeqChunks; ++i) {
-    const int64_t e = base + 8 * (int64_t)(t + kDeqThreads * i);
-    if (e >= n) continue;
-    const float a = double_quant ? (float)qv[i] * steps[e / kGroupElems - g_lo]
-                                 : __uint_as_float(qv[i]);
-    if (e + 8 <= n) {
-      float w[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) w[j] = cbs[(cw[i] >> (4 * j)) & 15u] * a;
-      if (BF16OUT) {
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + e) =
-            u32x4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
-                  pack_bf16x2(w[6], w[7])};
-      } else {
-        f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + e);
-        dst[0] = f32x4{w[0], w[1], w[2], w[3]};
-        dst[1] = f32x4{w[4], w[5], w[6], w[7]};
-      }
-    } else {
-      for (int64_t k = e; k < n; ++k) {
-        const uint32_t byte = codes[k >> 1];
-        const uint32_t code = (k & 1) ? (byte >> 4) : (byte & 15u);
-        const float w = cbs[code] * a;
-        if (BF16OUT) reinterpret_cast<uint16_t*>(out)[k] = f32_to_bf16(w);
-        else reinterpret_cast<float*>(out)[k] = w;
-      }
-    }
-  }
+  nf4_deq_span<BF16OUT>(threadIdx.x, blockIdx.x, codes, q8, c2, absmax, double_quant, n, out, tab);
 }
 
 }  // namespace

@@ -6,9 +6,10 @@
 // Backpropagation Mechanics": dY B appears in both dL/dA and dL/dx.)
 //
 // Both read their M x K activation operand once and are bound by that stream.
-// A workgroup of 8 waves owns 16 rows; the waves split the reduction into
-// eight contiguous ranges of 32-wide units and add their partial sums through
-// LDS in a fixed order at the end.  Each unit is one v_mfma_f32_16x16x32_bf16
+// A workgroup owns 16 rows; its waves (8 in the standalone kernel, 4 in the
+// prep kernel that also writes the bf16 weight copy) split the reduction into
+// contiguous ranges of 32-wide units and add their partial sums through LDS in
+// a fixed order at the end.  Each unit is one v_mfma_f32_16x16x32_bf16
 // per 16 rank columns, the activation rows as the A operand (lane (g, l16):
 // row l16, 16 bytes at reduction 8 g, loaded straight from global memory) and
 // the rank-side matrix as the B operand:
@@ -25,11 +26,12 @@
 // zero.
 #include "device_util.h"
 #include "dispatch.h"
+#include "nf4_deq.h"
 
 namespace lq {
 namespace {
 
-constexpr int kSW = 8;  // waves per workgroup
+constexpr int kSW = 8;  // waves per workgroup of the standalone kernel
 constexpr int kSThreads = 64 * kSW;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -40,31 +42,27 @@ __device__ __forceinline__ u32x2 tr_read(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <int JT, bool GT>
-__global__ __launch_bounds__(kSThreads) void shrink_kernel(const uint16_t* __restrict__ Z,
-                                                           int64_t M, int64_t K,
-                                                           const uint16_t* __restrict__ G,
-                                                           int r, float* __restrict__ out,
-                                                           int32_t* __restrict__ zero, int nzero) {
+// 16 rows (rb * 16 ..) of out with NW waves; every thread of the workgroup
+// (64 NW of them) calls it.
+template <int JT, bool GT, int NW>
+__device__ __forceinline__ void shrink_rows(int64_t rb, const uint16_t* __restrict__ Z, int64_t M,
+                                            int64_t K, const uint16_t* __restrict__ G, int r,
+                                            float* __restrict__ out) {
   constexpr int RC = 16 * JT;    // rank columns, padded
   constexpr int R = 8 / JT;      // units per round
   constexpr int NB = R * JT;     // GT: 1 KB pieces of B per round (32 R rows of up to RC)
-  __shared__ __attribute__((aligned(16))) uint16_t gtile[GT ? kSW : 1][GT ? NB * 512 : 8];
-  __shared__ f32x4 red[kSW][JT][64];
+  __shared__ __attribute__((aligned(16))) uint16_t gtile[GT ? NW : 1][GT ? NB * 512 : 8];
+  __shared__ f32x4 red[NW][JT][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  // side job: clear the next kernel's flag words (a kernel store, so it also
-  // replays correctly inside a captured graph)
-  if (blockIdx.x == 0)
-    for (int i = tid; i < nzero; i += kSThreads) zero[i] = 0;
 
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  const int64_t m0 = rb * 16;
   int64_t mr = m0 + l16;
   mr = mr < M ? mr : M - 1;
   const int64_t UT = K >> 5;
-  const int64_t u0 = UT * wave / kSW, u1 = UT * (wave + 1) / kSW;
+  const int64_t u0 = UT * wave / NW, u1 = UT * (wave + 1) / NW;
   const uint16_t* zrow = Z + mr * K + 8 * g;
   const uint16_t* arow[JT];
 #pragma unroll
@@ -154,7 +152,7 @@ __global__ __launch_bounds__(kSThreads) void shrink_kernel(const uint16_t* __res
     for (int jt = 0; jt < JT; ++jt) {
       f32x4 s = red[0][jt][lane];
 #pragma unroll
-      for (int w = 1; w < kSW; ++w) s += red[w][jt][lane];
+      for (int w = 1; w < NW; ++w) s += red[w][jt][lane];
       const int j = 16 * jt + l16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -163,6 +161,49 @@ __global__ __launch_bounds__(kSThreads) void shrink_kernel(const uint16_t* __res
       }
     }
   }
+}
+
+template <int JT, bool GT>
+__global__ __launch_bounds__(kSThreads) void shrink_kernel(const uint16_t* __restrict__ Z,
+                                                           int64_t M, int64_t K,
+                                                           const uint16_t* __restrict__ G,
+                                                           int r, float* __restrict__ out,
+                                                           int32_t* __restrict__ zero, int nzero) {
+  // side job: clear the next kernel's flag words (a kernel store, so it also
+  // replays correctly inside a captured graph)
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += kSThreads) zero[i] = 0;
+  shrink_rows<JT, GT, kSW>(blockIdx.x, Z, M, K, G, r, out);
+}
+
+// Prep of the large-M path in one launch: workgroups below nd write the bf16
+// copy of the NF4 weight (32768 elements each), the others compute 16 rows of
+// T or U with four waves; the two HBM streams overlap.
+struct PrepArgs {
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* c2;
+  const float* absmax;
+  int32_t dq;
+  int32_t nd;  // dequantising workgroups
+  int64_t n;   // weight elements
+  uint16_t* wout;
+  NF4Table tab;
+};
+
+template <int JT, bool GT>
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs pa, const uint16_t* __restrict__ Z,
+                                                   int64_t M, int64_t K,
+                                                   const uint16_t* __restrict__ G, int r,
+                                                   float* __restrict__ out,
+                                                   int32_t* __restrict__ zero, int nzero) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += 256) zero[i] = 0;
+  if ((int)blockIdx.x < pa.nd)
+    nf4_deq_span<true>(threadIdx.x, blockIdx.x, pa.codes, pa.q8, pa.c2, pa.absmax, pa.dq, pa.n,
+                       pa.wout, pa.tab);
+  else
+    shrink_rows<JT, GT, 4>((int64_t)blockIdx.x - pa.nd, Z, M, K, G, r, out);
 }
 
 template <bool GT>
@@ -197,6 +238,50 @@ int launch_shrink(const void* Z, int64_t M, int64_t K, const void* G, bool gt, i
   if (gt)
     return launch<true>((const uint16_t*)Z, M, K, (const uint16_t*)G, r, out, zero, nzero, st);
   return launch<false>((const uint16_t*)Z, M, K, (const uint16_t*)G, r, out, zero, nzero, st);
+}
+
+int launch_prep(const lq_weight& W, void* wout, const void* Z, int64_t M, int64_t K, const void* G,
+                bool gt, int64_t r, float* out, int32_t* zero, int nzero, hipStream_t st) {
+  PrepArgs pa;
+  pa.codes = W.codes;
+  pa.q8 = W.q8;
+  pa.c2 = W.c2;
+  pa.absmax = W.absmax;
+  pa.dq = W.double_quant;
+  pa.n = W.N * W.K;
+  pa.nd = (int32_t)cdiv(pa.n, kDeqSpan);
+  pa.wout = (uint16_t*)wout;
+  pa.tab = nf4_table();
+  const dim3 grid((unsigned)(pa.nd + cdiv(M, 16))), block(256);
+  const uint16_t* Zh = (const uint16_t*)Z;
+  const uint16_t* Gh = (const uint16_t*)G;
+  switch ((r + 15) / 16) {
+    case 1:
+      if (gt)
+        hipLaunchKernelGGL((prep_kernel<1, true>), grid, block, 0, st, pa, Zh, M, K, Gh, (int)r,
+                           out, zero, nzero);
+      else
+        hipLaunchKernelGGL((prep_kernel<1, false>), grid, block, 0, st, pa, Zh, M, K, Gh, (int)r,
+                           out, zero, nzero);
+      break;
+    case 2:
+      if (gt)
+        hipLaunchKernelGGL((prep_kernel<2, true>), grid, block, 0, st, pa, Zh, M, K, Gh, (int)r,
+                           out, zero, nzero);
+      else
+        hipLaunchKernelGGL((prep_kernel<2, false>), grid, block, 0, st, pa, Zh, M, K, Gh, (int)r,
+                           out, zero, nzero);
+      break;
+    default:
+      if (gt)
+        hipLaunchKernelGGL((prep_kernel<4, true>), grid, block, 0, st, pa, Zh, M, K, Gh, (int)r,
+                           out, zero, nzero);
+      else
+        hipLaunchKernelGGL((prep_kernel<4, false>), grid, block, 0, st, pa, Zh, M, K, Gh, (int)r,
+                           out, zero, nzero);
+      break;
+  }
+  return hip_fail(hipGetLastError(), "prep launch");
 }
 
 }  // namespace dispatch
