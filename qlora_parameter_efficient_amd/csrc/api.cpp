@@ -100,6 +100,10 @@ size_t bwd_big_bytes(int64_t M, int64_t N, int64_t K) {
   return dispatch::big_dx_eligible(M, N, K) ? dispatch::big_dx_ws_bytes(M, N, K) : 0;
 }
 
+size_t multi_big_bytes(int64_t T, int64_t N, int64_t K, int64_t rc) {
+  return dispatch::big_fwd_eligible(T, N, K) ? dispatch::big_multi_ws_bytes(T, N, K, rc) : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,8 +149,11 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
       const size_t big = bwd_big_bytes(M, N, K);
       return big ? align256(bwd_ws_bytes(M, N, K, r)) + big : bwd_ws_bytes(M, N, K, r);
     }
-    case LQ_OP_FWD_MULTI:
-      return dispatch::multi_ws_bytes(M, r, n_adapters);
+    case LQ_OP_FWD_MULTI: {
+      const size_t base = dispatch::multi_ws_bytes(M, r, n_adapters);
+      const size_t big = multi_big_bytes(M, N, K, r * (n_adapters > 0 ? n_adapters : 1));
+      return big > base ? big : base;
+    }
     case LQ_OP_FWD_FUSED:
       return (size_t)((M <= kDecodeMaxM ? kTParts : 1) * M * r) * 4;
     case LQ_OP_BWD_FUSED:
@@ -285,6 +292,10 @@ int lq_lora_fwd_multi(const void* X, int64_t T_tokens, const lq_weight* W0, cons
   const size_t need = dispatch::multi_ws_bytes(T_tokens, r, n_adapters);
   REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu",
           ws_bytes, need);
+  const size_t big = multi_big_bytes(T_tokens, W0->N, W0->K, r * n_adapters);
+  if (big && ws_bytes >= big)
+    return dispatch::big_fwd_multi(X, T_tokens, *W0, A_stack, B_stack, n_adapters, r, scale,
+                                   seg_offsets, seg_adapter, n_seg, Y, ws, stream);
   return dispatch::bf16_fwd_multi(X, T_tokens, *W0, A_stack, B_stack, n_adapters, r, scale,
                                   seg_offsets, seg_adapter, n_seg, Y, ws, stream);
 }

@@ -90,6 +90,7 @@ struct G256Params {
   float s;
   int32_t ti, tj, splits, ksteps;
   int32_t tpx;  // split K: tiles per XCD
+  int32_t ead_r; // multi-adapter forward: rank of one adapter (E = stacked B), else 0
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -171,6 +172,24 @@ __device__ __forceinline__ u32x4 e_operand_row(const uint16_t* row, int j0, int 
   uint16_t v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = (j0 + i < r) ? row[j0 + i] : (uint16_t)0;
+  return u32x4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
+               (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
+}
+
+// Multi-adapter forward: concatenated rank c of row n is B_{c / rs}[n][c % rs]
+// (E = the stacked B, n_ad x NI x rs); ranks j0 .. j0 + 7, zeros past rc.
+__device__ __forceinline__ u32x4 e_operand_multi(const uint16_t* Bs, int64_t NI, int rs, int64_t n,
+                                                 int j0, int rc) {
+  if (rs % 8 == 0 && j0 + 8 <= rc) {
+    const int a = j0 / rs;
+    return *reinterpret_cast<const u32x4*>(Bs + ((int64_t)a * NI + n) * rs + (j0 - a * rs));
+  }
+  uint16_t v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = j0 + i, a = c / rs;
+    v[i] = c < rc ? Bs[((int64_t)a * NI + n) * rs + (c - a * rs)] : (uint16_t)0;
+  }
   return u32x4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
                (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
 }
@@ -445,7 +464,9 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
       const int64_t i = i0 + 128 * wi + 32 * ns + l32;
-      ef[ns] = TR ? e_operand_col(p.E, NI, i, jr, r) : e_operand_row(p.E + i * r, jr, r);
+      ef[ns] = TR           ? e_operand_col(p.E, NI, i, jr, r)
+               : p.ead_r ? e_operand_multi(p.E, NI, p.ead_r, i, jr, r)
+                         : e_operand_row(p.E + i * r, jr, r);
     }
 #pragma unroll
     for (int ms = 0; ms < JM; ++ms) {
@@ -538,7 +559,8 @@ void launch_shape(const G256Params& p, unsigned blocks, hipStream_t st) {
 }
 
 int launch_g256(bool tr, const void* P, const void* Q, const float* V, const void* E, int64_t M,
-                int64_t NI, int64_t KR, int64_t r, float s, void* Y, void* ws, hipStream_t st) {
+                int64_t NI, int64_t KR, int64_t r, float s, void* Y, void* ws, hipStream_t st,
+                int ead_r = 0) {
   const G256Plan pl = g256_plan(M, NI);
   G256Params p{};
   p.P = (const uint16_t*)P;
@@ -551,6 +573,7 @@ int launch_g256(bool tr, const void* P, const void* Q, const float* V, const voi
   p.KR = KR;
   p.r = (int32_t)r;
   p.s = s;
+  p.ead_r = ead_r;
   p.ti = (int32_t)pl.ti;
   p.tj = (int32_t)pl.tj;
   p.splits = pl.splits;
@@ -629,6 +652,38 @@ int big_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const v
     e = u_only(dY, M, N, B, r, U, st, (int32_t*)gws, nz);
   if (e) return e;
   return launch_g256(true, dY, Q, U, A, M, K, N, r, s, dX, gws, st);
+}
+
+// [row -> adapter, int32 T] [masked T, float32 T x (n_ad r)] [g256 workspace] [bf16 W0]
+size_t big_multi_ws_bytes(int64_t T, int64_t N, int64_t K, int64_t rc) {
+  return align256((size_t)T * 4) + align256((size_t)(T * rc) * 4) +
+         align256(g256_ws_bytes(T, N)) + (size_t)(N * K) * 2;
+}
+
+// Multi-adapter forward at large T: T_m = X A_cat^T masked to each row's
+// adapter block (A_cat = the stacked A viewed as (n_ad r) x K), then the
+// large-tile product whose expand multiplies by the stacked B.
+int big_fwd_multi(const void* X, int64_t T, const lq_weight& W, const void* A_stack,
+                  const void* B_stack, int32_t n_ad, int64_t r, float s, const int32_t* seg_off,
+                  const int32_t* seg_ad, int32_t n_seg, void* Y, void* ws, hipStream_t st) {
+  const int64_t N = W.N, K = W.K, rc = r * n_ad;
+  char* w = (char*)ws;
+  int32_t* row_ad = (int32_t*)w;
+  w += align256((size_t)T * 4);
+  float* Tm = (float*)w;
+  w += align256((size_t)(T * rc) * 4);
+  void* gws = w;
+  w += align256(g256_ws_bytes(T, N));
+  int e = launch_rowmap(seg_off, seg_ad, n_seg, T, row_ad, st);
+  if (e) return e;
+  const int nz = (int)(g256_flag_bytes(T, N) / 4);
+  const void* Q = W.kind == LQ_WEIGHT_DENSE ? W.dense : (const void*)w;
+  if (W.kind != LQ_WEIGHT_DENSE)
+    e = launch_prep(W, w, X, T, K, A_stack, false, rc, Tm, (int32_t*)gws, nz, st, row_ad, (int)r);
+  else
+    e = launch_shrink(X, T, K, A_stack, false, rc, Tm, (int32_t*)gws, nz, st, row_ad, (int)r);
+  if (e) return e;
+  return launch_g256(false, X, Q, Tm, B_stack, T, N, K, rc, s, Y, gws, st, (int)r);
 }
 
 }  // namespace dispatch

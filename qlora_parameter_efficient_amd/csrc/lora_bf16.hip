@@ -1080,6 +1080,12 @@ int bf16_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const 
   return dx_pick<kNF4>(p, st);
 }
 
+int launch_rowmap(const int32_t* seg_off, const int32_t* seg_ad, int32_t n_seg, int64_t T,
+                  int32_t* row_ad, hipStream_t st) {
+  hipLaunchKernelGGL(rowmap_kernel, dim3(n_seg), dim3(256), 0, st, seg_off, seg_ad, T, row_ad);
+  return hip_fail(hipGetLastError(), "rowmap launch");
+}
+
 size_t multi_ws_bytes(int64_t T_tokens, int64_t r, int32_t n_adapters) {
   const int64_t rp = (r * n_adapters <= 32) ? 32 : 64;
   return (size_t)T_tokens * 4 + (size_t)T_tokens * rp * 2 + 256;

@@ -97,3 +97,17 @@ def test_config5_full():
                                      c["offsets"][1:-1][:16], c["offsets"][1:-1][:16] - 1]))
     run_multi(c["X"], c["W0"], c["A"], c["B"], c["offsets"], c["adapter"], c["alpha"] / c["r"],
               rows=rows, label="config5")
+
+
+@pytest.mark.parametrize("n_ad,r", [(3, 8), (4, 5), (2, 32)])
+def test_large_segments(n_ad, r):
+    """T >= 2048 with N = 256: the large-tile path (masked T from the shrink
+    kernel, expand over the stacked B), including an odd rank."""
+    counts = [0, 700, 1, 513, 0, 900, 129, 64]
+    T = sum(counts)
+    assert (lq.lq_workspace_size(lq.LQ_OP_FWD_MULTI, T, 256, 256, r, n_ad)
+            > lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, T, 256, 256, r))
+    rng = np.random.default_rng(n_ad * 10 + r)
+    ids = rng.integers(0, n_ad, len(counts))
+    X, W0, A, B, off, ids = small_multi(counts, ids, n_ad, r, seed=r)
+    run_multi(X, W0, A, B, off, ids, 2.0, label="large")
