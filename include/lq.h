@@ -146,15 +146,20 @@ int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
  *   X  device M x K of dt;  A device r x K of dt;  B device N x r of dt;
  *   Y  device M x N of dt (written, not accumulated);
  *   T_out  optional device M x r float32: receives T = X A^T for lq_lora_bwd.
- *   ws / ws_bytes: device workspace of lq_workspace_size(LQ_OP_FWD, M, N, K,
- *   r, 0) bytes, needed by the decode path (dt = LQ_BF16, M <= 16: 8 M r
- *   floats of partial sums of T) and by the float32 path when T_out is NULL
- *   (M r floats of T); otherwise ws may be NULL.
+ *   ws / ws_bytes: device workspace (caller-owned, contents not preserved).
+ *   lq_workspace_size(LQ_OP_FWD, M, N, K, r, 0) bytes select the fastest
+ *   path; lq_workspace_size(LQ_OP_FWD_FUSED, ...) is the smallest workspace
+ *   that works.  The decode path (dt = LQ_BF16, M <= 16) needs 8 M r floats
+ *   of partial sums of T, the float32 path M r floats of T when T_out is
+ *   NULL; otherwise ws may be NULL.
  *   dt = LQ_BF16: bf16 inputs, float32 accumulation, bf16 RNE output; W0 dense
- *   bf16 or NF4 (dequantised in registers / LDS, never written to memory).
+ *   bf16 or NF4.  With the LQ_OP_FWD size at M >= 2048 and N % 256 == 0 the
+ *   large-tile path runs: NF4 W0 is first dequantised (bit-exactly, as
+ *   lq_nf4_dequantize) to a bf16 copy inside ws, then multiplied; otherwise
+ *   the fused kernels dequantise NF4 in registers / LDS and never write a
+ *   dense W0.  Both give "dequantise, then multiply in bf16".
  *   Requires K % 64 == 0, N % 64 == 0, N, K <= 65536, M*K and M*N < 2^31,
- *   1 <= r <= 64.  M <= 16 takes the
- *   memory-bound decode path.
+ *   1 <= r <= 64.  M <= 16 takes the memory-bound decode path.
  *   dt = LQ_F32: float32 throughout (W0 dense f32 or NF4), 1 <= r <= 64.
  * M = 0 is a no-op returning LQ_OK.
  */
@@ -177,7 +182,9 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A,
  *   accumulate = 1 adds into dA and dB (gradient accumulation over
  *   micro-batches); 0 overwrites them.
  *   ws / ws_bytes: device workspace of at least
- *   lq_workspace_size(LQ_OP_BWD, M, N, K, r, 0) bytes (caller-owned).
+ *   lq_workspace_size(LQ_OP_BWD_FUSED, M, N, K, r, 0) bytes (caller-owned);
+ *   with lq_workspace_size(LQ_OP_BWD, ...) bytes at M >= 2048 and
+ *   K % 256 == 0, dX takes the large-tile path (bf16 copy of W0 in ws).
  * Same shape rules as lq_lora_fwd.
  */
 int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0,
@@ -205,8 +212,10 @@ int lq_lora_merge(const lq_weight* W0, const void* A, const void* B, int64_t r,
  *   seg_offsets device int32[n_seg+1], seg_adapter device int32[n_seg]
  *   (preconditions: offsets non-decreasing from 0 to T_tokens, ids in
  *   [0, n_adapters); lq_check_segments verifies host copies).
- *   ws: at least lq_workspace_size(LQ_OP_FWD_MULTI, T_tokens, N, K, r,
- *   n_adapters) bytes.
+ *   ws: at least lq_workspace_size(LQ_OP_FWD_MULTI_FUSED, T_tokens, N, K, r,
+ *   n_adapters) bytes; with lq_workspace_size(LQ_OP_FWD_MULTI, ...) bytes at
+ *   T_tokens >= 2048 and N % 256 == 0 the large-tile path runs (adapter-masked
+ *   T, then the large product whose expand reads the stacked B).
  *   Requires dt = LQ_BF16, K % 64 == 0, N % 64 == 0, r * n_adapters <= 64.
  */
 int lq_lora_fwd_multi(const void* X, int64_t T_tokens, const lq_weight* W0,
@@ -221,12 +230,18 @@ int lq_lora_fwd_multi(const void* X, int64_t T_tokens, const lq_weight* W0,
 int lq_check_segments(const int32_t* h_offsets, const int32_t* h_adapter,
                       int32_t n_seg, int64_t T_tokens, int32_t n_adapters);
 
-/* Workspace sizes (bytes) for the ops that need one. */
+/* Workspace sizes (bytes) for the ops that need one.  LQ_OP_FWD, LQ_OP_BWD
+ * and LQ_OP_FWD_MULTI: the size that lets the call take its fastest path
+ * (at large M the large-tile path, whose part holds the bf16 copy of W0 and
+ * the split-K slots); LQ_OP_FWD_FUSED, LQ_OP_BWD_FUSED and
+ * LQ_OP_FWD_MULTI_FUSED: the smallest size each call accepts, with which the
+ * fused kernels run. */
 #define LQ_OP_FWD 0
 #define LQ_OP_BWD 1
 #define LQ_OP_FWD_MULTI 2
 #define LQ_OP_FWD_FUSED 3
 #define LQ_OP_BWD_FUSED 4
+#define LQ_OP_FWD_MULTI_FUSED 5
 size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
                          int32_t n_adapters);
 

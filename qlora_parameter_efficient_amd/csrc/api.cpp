@@ -158,6 +158,8 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
       return (size_t)((M <= kDecodeMaxM ? kTParts : 1) * M * r) * 4;
     case LQ_OP_BWD_FUSED:
       return bwd_ws_bytes(M, N, K, r);
+    case LQ_OP_FWD_MULTI_FUSED:
+      return dispatch::multi_ws_bytes(M, r, n_adapters);
     default:
       return 0;
   }

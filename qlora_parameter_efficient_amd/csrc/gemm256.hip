@@ -277,16 +277,21 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
   const char* pbase0 = reinterpret_cast<const char*>(p.P);
   const char* qbase0 = reinterpret_cast<const char*>(p.Q);
 
-  auto issue = [&](int kt, int b) {
+  // loads of one step, in four parts (u = 2 part, 2 part + 1)
+  auto issue_part = [&](int kt, int b, int part) {
     const uint32_t st = sbase + b * S::Stage;
     const char* qb = TR ? qbase0 + (int64_t)kt * kGK * NI * 2 : qbase0 + (int64_t)kt * kGK * 2;
     const char* pb = pbase0 + (int64_t)kt * kGK * 2;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 2 * part; u < 2 * part + 2; ++u) {
       const uint32_t qd = TR ? st + (16 * wave + 2 * u) * 512 : st + (64 * wave + 8 * u) * 128;
       dma16(qb, qoff[u], qd);
       if (u < 2 * JM) dma16(pb, poff[u], st + kTileBytes + (16 * JM * wave + 8 * u) * 128);
     }
+  };
+  auto issue = [&](int kt, int b) {
+#pragma unroll
+    for (int part = 0; part < 4; ++part) issue_part(kt, b, part);
   };
 
   // ---- per-lane LDS read offsets
@@ -338,20 +343,23 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
 
   // one step on LDS stage B (compile-time, so that every operand address is a
   // per-lane base plus an immediate): the loads of step kt + NST - 1 go into
-  // the stage read one step earlier, then four substeps whose LDS reads run
-  // one substep ahead; before the barrier, wait until the loads of step
-  // kt + 1 have landed (those of later steps stay in flight)
+  // the stage read one step earlier (all at once for 256 x 128 tiles, a
+  // quarter per substep for 256 x 256, which measured slightly faster there),
+  // then four substeps whose LDS reads run one substep ahead; before the
+  // barrier, wait until the loads of step kt + 1 have landed (those of later
+  // steps stay in flight)
   constexpr int NST = S::NST;
   auto step = [&](int kt, auto stage) {
     constexpr int B = decltype(stage)::value;
     const bool more = kt + NST - 1 < kt1;
-    if (more) issue(kt + NST - 1, (B + NST - 1) % NST);
+    if (more && JM == 2) issue(kt + NST - 1, (B + NST - 1) % NST);
     const uint32_t st = sbase + B * S::Stage;
     u32x4 wf[2][4], xf[2][JM];
     load_frags(st, 0, wf[0], xf[0]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c = s & 1;
+      if (more && JM == 4) issue_part(kt + NST - 1, (B + NST - 1) % NST, s);
       if (s < 3) load_frags(st, s + 1, wf[c ^ 1], xf[c ^ 1]);
       __builtin_amdgcn_sched_barrier(0);  // next substep's reads before these products
 #pragma unroll

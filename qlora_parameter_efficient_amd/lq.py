@@ -22,6 +22,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "lq.h")
 LQ_F32, LQ_BF16 = 0, 1
 LQ_WEIGHT_DENSE, LQ_WEIGHT_NF4 = 0, 1
 LQ_OP_FWD, LQ_OP_BWD, LQ_OP_FWD_MULTI, LQ_OP_FWD_FUSED, LQ_OP_BWD_FUSED = 0, 1, 2, 3, 4
+LQ_OP_FWD_MULTI_FUSED = 5
 STATUS = {0: "LQ_OK", -1: "LQ_ERR_INVALID_ARG", -2: "LQ_ERR_UNSUPPORTED",
           -3: "LQ_ERR_WORKSPACE", -4: "LQ_ERR_HIP"}
 
@@ -255,7 +256,8 @@ def lq_lora_merge(W0, A, B, scale, dtype=None, out=None):
     return out
 
 
-def lq_lora_fwd_multi(X, W0, A_stack, B_stack, scale, seg_offsets, seg_adapter, ws=None, Y=None):
+def lq_lora_fwd_multi(X, W0, A_stack, B_stack, scale, seg_offsets, seg_adapter, ws=None, Y=None,
+                      fused=False):
     _dev(X, A_stack, B_stack, seg_offsets, seg_adapter)
     dt = _dt(X)
     T = X.shape[0]
@@ -265,7 +267,8 @@ def lq_lora_fwd_multi(X, W0, A_stack, B_stack, scale, seg_offsets, seg_adapter, 
     if Y is None:
         Y = torch.empty((T, w.N), dtype=X.dtype, device=X.device)
     if ws is None:
-        ws = _ws(lq_workspace_size(LQ_OP_FWD_MULTI, T, w.N, w.K, r, n_ad), X.device)
+        ws = _ws(lq_workspace_size(LQ_OP_FWD_MULTI_FUSED if fused else LQ_OP_FWD_MULTI, T, w.N,
+                                   w.K, r, n_ad), X.device)
     _check(lib().lq_lora_fwd_multi(_ptr(X), T, ctypes.byref(w), _ptr(A_stack), _ptr(B_stack), n_ad,
                                    r, scale, _ptr(seg_offsets), _ptr(seg_adapter), n_seg, dt,
                                    _ptr(Y), _ptr(ws), ws.numel(), _stream()))

@@ -14,15 +14,15 @@ from .gpu_helpers import BF16_TOL, DEV, announce, f64, rel_err, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def run_multi(X_t, W0_t, A_t, B_t, offsets, ids, s, rows=None, label=""):
+def run_multi(X_t, W0_t, A_t, B_t, offsets, ids, s, rows=None, label="", fused=False):
     announce(f"multi {label} T={X_t.shape[0]} n_seg={len(ids)} n_ad={A_t.shape[0]} r={A_t.shape[1]}")
     T = X_t.shape[0]
     assert lq.lq_check_segments(offsets, ids, T, A_t.shape[0]) == 0
     X, W0, A, B = to_dev(X_t), to_dev(W0_t), to_dev(A_t), to_dev(B_t)
     off = torch.from_numpy(offsets.astype(np.int32)).to(DEV)
     ad = torch.from_numpy(ids.astype(np.int32)).to(DEV)
-    Y = lq.lq_lora_fwd_multi(X, W0, A, B, s, off, ad)
-    Yb = lq.lq_lora_fwd_multi(X, W0, A, torch.zeros_like(B), s, off, ad)
+    Y = lq.lq_lora_fwd_multi(X, W0, A, B, s, off, ad, fused=fused)
+    Yb = lq.lq_lora_fwd_multi(X, W0, A, torch.zeros_like(B), s, off, ad, fused=fused)
     torch.cuda.synchronize()
     Xo, Wo, Ao, Bo = X_t.f64(), W0_t.f64(), A_t.f64(), B_t.f64()
     if rows is None:
@@ -106,8 +106,9 @@ def test_large_segments(n_ad, r):
     counts = [0, 700, 1, 513, 0, 900, 129, 64]
     T = sum(counts)
     assert (lq.lq_workspace_size(lq.LQ_OP_FWD_MULTI, T, 256, 256, r, n_ad)
-            > lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, T, 256, 256, r))
+            > lq.lq_workspace_size(lq.LQ_OP_FWD_MULTI_FUSED, T, 256, 256, r, n_ad))
     rng = np.random.default_rng(n_ad * 10 + r)
     ids = rng.integers(0, n_ad, len(counts))
     X, W0, A, B, off, ids = small_multi(counts, ids, n_ad, r, seed=r)
     run_multi(X, W0, A, B, off, ids, 2.0, label="large")
+    run_multi(X, W0, A, B, off, ids, 2.0, label="large-fused", fused=True)
