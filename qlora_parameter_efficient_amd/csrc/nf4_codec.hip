@@ -58,12 +58,40 @@ __device__ __forceinline__ void load8<float>(const float* W, int64_t e0, int64_t
   }
 }
 
-// code = number of thresholds strictly below x
-__device__ __forceinline__ uint32_t nf4_code(float x, const NF4Table& t) {
-  uint32_t c = 0;
-#pragma unroll
-  for (int i = 0; i < 15; ++i) c += (x > t.thr[i]) ? 1u : 0u;
-  return c;
+// code = number of thresholds strictly below x.  The 15 thresholds ascend, so
+// the count is found by a four-level binary search (x > th[c + 2^k - 1]
+// decides bit k of c), the same count as comparing against all 15; every
+// level is a compare and selects, no branches.  NaN gives 0.
+struct Thr {  // named scalars, so that every select below is a register select
+  float t0, t1, t2, t3, t4, t5, t6, t7, t8, t9, t10, t11, t12, t13, t14;
+};
+
+// each threshold held in a register the compiler cannot see through, so that
+// it keeps the selects as register selects instead of indexing memory
+__device__ __forceinline__ float in_reg(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ Thr make_thr(const NF4Table& tab) {
+  return Thr{in_reg(tab.thr[0]),  in_reg(tab.thr[1]),  in_reg(tab.thr[2]),  in_reg(tab.thr[3]),
+             in_reg(tab.thr[4]),  in_reg(tab.thr[5]),  in_reg(tab.thr[6]),  in_reg(tab.thr[7]),
+             in_reg(tab.thr[8]),  in_reg(tab.thr[9]),  in_reg(tab.thr[10]), in_reg(tab.thr[11]),
+             in_reg(tab.thr[12]), in_reg(tab.thr[13]), in_reg(tab.thr[14])};
+}
+
+// value select (operands by value: a ternary on two lvalues would select
+// addresses and load)
+__device__ __forceinline__ float fsel(bool c, float a, float b) { return c ? a : b; }
+
+__device__ __forceinline__ uint32_t nf4_code(float x, const Thr t) {
+  const bool b3 = x > t.t7;
+  const bool b2 = x > fsel(b3, t.t11, t.t3);
+  const bool b1 = x > fsel(b3, fsel(b2, t.t13, t.t9), fsel(b2, t.t5, t.t1));
+  const float l0h = fsel(b2, fsel(b1, t.t14, t.t12), fsel(b1, t.t10, t.t8));
+  const float l0l = fsel(b2, fsel(b1, t.t6, t.t4), fsel(b1, t.t2, t.t0));
+  const bool b0 = x > fsel(b3, l0h, l0l);
+  return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
 }
 
 // One workgroup per group of 256 blocks (16384 elements).  Step s, thread t
@@ -77,6 +105,7 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quantize_kernel(
   __shared__ float c1s[LQ_NF4_DQ_BLOCK];
   __shared__ float wmax[kQuantThreads / 64];
   const int t = threadIdx.x;
+  const Thr th = make_thr(tab);
   const int64_t g0 = (int64_t)blockIdx.x * kGroupElems;
   const int64_t nb_total = (n + LQ_NF4_BLOCK - 1) / LQ_NF4_BLOCK;
 
@@ -106,22 +135,27 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quantize_kernel(
     m = fmaxf(m, __shfl_xor(m, 4));
     const float c1 = m;
     if ((t & 7) == 0) c1s[chunk >> 3] = c1;
-    if (e0 < n) {
+    const int64_t byte0 = e0 >> 1;
+    if (e0 + 8 <= n) {
+      // whole chunk, no per-element branches: the eight divisions interleave.
+      // c1 == 0 (an all-zero block) encodes every element as level 7 (zero).
       uint32_t packed = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        const uint32_t code = nf4_code(v[i] / c1, th);
+        packed |= (c1 != 0.0f ? code : 7u) << (4 * i);
+      }
+      *reinterpret_cast<uint32_t*>(codes + byte0) = packed;
+    } else if (e0 < n) {
+      uint32_t packed = 0;
+      for (int i = 0; i < 8; ++i) {
         uint32_t code = 7u;
         if (e0 + i >= n) code = 0u;  // padding nibble past the end stays 0
-        else if (c1 != 0.0f) code = nf4_code(v[i] / c1, tab);
+        else if (c1 != 0.0f) code = nf4_code(v[i] / c1, th);
         packed |= code << (4 * i);
       }
-      const int64_t byte0 = e0 >> 1;
-      if (e0 + 8 <= n) {
-        *reinterpret_cast<uint32_t*>(codes + byte0) = packed;
-      } else {
-        const int64_t nbytes = (n - e0 + 1) >> 1;
-        for (int64_t b = 0; b < nbytes; ++b) codes[byte0 + b] = (uint8_t)(packed >> (8 * b));
-      }
+      const int64_t nbytes = (n - e0 + 1) >> 1;
+      for (int64_t b = 0; b < nbytes; ++b) codes[byte0 + b] = (uint8_t)(packed >> (8 * b));
     }
   }
   __syncthreads();
