@@ -230,3 +230,24 @@ def test_graph_replay_matches_eager(shape):
         run()  # eager work between replays
         torch.cuda.synchronize()
     assert int(wsf[:4].view(torch.int32).item()) == 0  # no split-K wait gave up
+
+
+def test_timing_aid_counts_large_tile_launches():
+    """lq_timing_enable brackets the product launches with events on their
+    stream: two forward calls on the large-tile path give two g256_fwd
+    records with positive durations, and reading forgets them."""
+    M, N, K, r = 2100, 256, 256, 16
+    c = wl.small_case(M, N, K, r, seed=5)
+    X, A, B = to_dev(c["X"]), to_dev(c["A"]), to_dev(c["B"])
+    Wd, _ = base_for(c, "nf4")
+    lq.lq_timing_enable(True)
+    try:
+        lq.lq_timing_read("g256_fwd")
+        for _ in range(2):
+            lq.lq_lora_fwd(X, Wd, A, B, 2.0)
+        torch.cuda.synchronize()
+        ms, n = lq.lq_timing_read("g256_fwd")
+        assert n == 2 and ms > 0.0
+        assert lq.lq_timing_read("g256_fwd") == (0.0, 0)
+    finally:
+        lq.lq_timing_enable(False)
