@@ -62,7 +62,13 @@ def lora_merge(W0, A, B, s):
 
 
 def lora_forward_multi(X, W0, A_stack, B_stack, s, offsets, adapter):
-    """Segment i = rows offsets[i]:offsets[i+1] of X uses adapter adapter[i]."""
+    """Segment i = rows offsets[i]:offsets[i+1] of X uses adapter adapter[i].
+
+    A_stack[a] (r_a x K) and B_stack[a] (N x r_a) may differ in rank from one
+    adapter to the next (the serving page's batches hold "adapters of
+    different ranks"); ``s`` is one scale for all adapters or a sequence with
+    adapter a's own alpha_a / r_a.
+    """
     X, W0 = _f64(X), _f64(W0)
     Y = np.zeros((X.shape[0], W0.shape[0]), dtype=np.float64)
     for i in range(len(adapter)):
@@ -70,7 +76,8 @@ def lora_forward_multi(X, W0, A_stack, B_stack, s, offsets, adapter):
         if hi == lo:
             continue
         a = int(adapter[i])
-        Y[lo:hi] = lora_forward(X[lo:hi], W0, A_stack[a], B_stack[a], s)[0]
+        sa = s[a] if np.ndim(s) else s
+        Y[lo:hi] = lora_forward(X[lo:hi], W0, A_stack[a], B_stack[a], sa)[0]
     return Y
 
 

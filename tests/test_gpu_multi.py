@@ -6,6 +6,7 @@ import pytest
 import torch
 
 from oracle import lora as olora
+from oracle import nf4 as onf4
 from qlora_parameter_efficient_amd import lq
 from qlora_parameter_efficient_amd import workloads as wl
 
@@ -14,11 +15,16 @@ from .gpu_helpers import BF16_TOL, DEV, announce, f64, rel_err, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def run_multi(X_t, W0_t, A_t, B_t, offsets, ids, s, rows=None, label="", fused=False):
+def run_multi(X_t, W0_t, A_t, B_t, offsets, ids, s, rows=None, label="", fused=False, nf4=False):
     announce(f"multi {label} T={X_t.shape[0]} n_seg={len(ids)} n_ad={A_t.shape[0]} r={A_t.shape[1]}")
     T = X_t.shape[0]
     assert lq.lq_check_segments(offsets, ids, T, A_t.shape[0]) == 0
     X, W0, A, B = to_dev(X_t), to_dev(W0_t), to_dev(A_t), to_dev(B_t)
+    if nf4:  # shared NF4 base: the oracle multiplies by its own bf16 dequantisation
+        W0 = lq.lq_nf4_quantize(W0)
+        q = onf4.nf4_quantize(W0_t.value)
+        W0_t = wl.Tensor(onf4.bf16_bits_to_f64(onf4.nf4_dequantize_bf16(q))
+                         .reshape(W0_t.value.shape).astype(np.float32), "f32")
     off = torch.from_numpy(offsets.astype(np.int32)).to(DEV)
     ad = torch.from_numpy(ids.astype(np.int32)).to(DEV)
     Y = lq.lq_lora_fwd_multi(X, W0, A, B, s, off, ad, fused=fused)
@@ -112,3 +118,14 @@ def test_large_segments(n_ad, r):
     X, W0, A, B, off, ids = small_multi(counts, ids, n_ad, r, seed=r)
     run_multi(X, W0, A, B, off, ids, 2.0, label="large")
     run_multi(X, W0, A, B, off, ids, 2.0, label="large-fused", fused=True)
+
+
+@pytest.mark.parametrize("counts", [[0, 37, 129, 300, 2], [0, 700, 1, 513, 0, 900, 129, 64]],
+                         ids=["fused", "large"])
+def test_nf4_shared_base(counts):
+    """Segmented forward over one NF4 + DQ base (the fused kernel at small T;
+    the prep kernel's bf16 copy and masked T at T >= 2048)."""
+    rng = np.random.default_rng(len(counts))
+    ids = rng.integers(0, 3, len(counts))
+    X, W0, A, B, off, ids = small_multi(counts, ids, 3, 16, seed=7)
+    run_multi(X, W0, A, B, off, ids, 2.0, label="nf4 base", nf4=True)

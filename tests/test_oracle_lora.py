@@ -126,6 +126,36 @@ def test_multi_is_loop_of_single():
     np.testing.assert_allclose(Y1, lora.lora_forward(X, W0, As[1], Bs[1], 2.0)[0], rtol=1e-12)
 
 
+def test_multi_mixed_ranks_equals_zero_padded_uniform():
+    """Adapters of different ranks, each with its own scale: padding every
+    adapter to the largest rank with zero rows of A (and zero columns of B)
+    and folding its scale into B gives the same output through the uniform
+    path with scale 1 (zero rank directions add nothing)."""
+    rng = np.random.default_rng(21)
+    K, N = 10, 7
+    ranks, scales = [1, 4, 2], [3.0, 0.5, 1.25]
+    W0 = rng.standard_normal((N, K))
+    As = [rng.standard_normal((r, K)) for r in ranks]
+    Bs = [rng.standard_normal((N, r)) for r in ranks]
+    counts = np.array([2, 3, 0, 4, 1])
+    ids = np.array([1, 0, 2, 2, 1])
+    off = np.concatenate([[0], np.cumsum(counts)])
+    X = rng.standard_normal((off[-1], K))
+    Y = lora.lora_forward_multi(X, W0, As, Bs, scales, off, ids)
+    R = max(ranks)
+    Ap = np.zeros((3, R, K))
+    Bp = np.zeros((3, N, R))
+    for a, r in enumerate(ranks):
+        Ap[a, :r] = As[a]
+        Bp[a, :, :r] = scales[a] * Bs[a]
+    np.testing.assert_allclose(Y, lora.lora_forward_multi(X, W0, Ap, Bp, 1.0, off, ids),
+                               rtol=1e-12, atol=1e-12)
+    # equal ranks and one scale given per adapter reduce to the scalar form
+    Yu = lora.lora_forward_multi(X, W0, Ap, Bp, [2.0] * 3, off, ids)
+    np.testing.assert_allclose(Yu, lora.lora_forward_multi(X, W0, Ap, Bp, 2.0, off, ids),
+                               rtol=0, atol=0)
+
+
 def test_parameter_counts_match_pages():
     g = golden()
     d, ffn = 4096, 11008
