@@ -224,6 +224,30 @@ int lq_lora_fwd_multi(const void* X, int64_t T_tokens, const lq_weight* W0,
                       const int32_t* seg_adapter, int32_t n_seg, lq_dtype dt,
                       void* Y, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Segmented multi-adapter forward over adapters of different ranks ([FT]
+ * "Serving many adapters at once": batched kernels for adapters of different
+ * ranks in the same batch, on one possibly quantised base): segment i gets
+ *   Y_i = X_i W0^T + scales[a] (X_i A_a^T) B_a^T,  a = seg_adapter[i].
+ *   A_cat   device R x K of dt: the adapters' A (r_a x K each) stacked by
+ *           rows; adapter a owns rows rank_offsets[a] .. rank_offsets[a+1]-1.
+ *   B_cat   device, dt: the adapters' B (N x r_a each, row-major) one after
+ *           another; adapter a's starts at element N * rank_offsets[a].
+ *   rank_offsets  host int32[n_adapters + 1]: starts at 0, strictly
+ *           increasing (every r_a >= 1), R = rank_offsets[n_adapters] <= 64.
+ *   scales  host float[n_adapters]: each adapter's alpha_a / r_a.
+ *   Segments, W0, dtypes, shape rules and errors as lq_lora_fwd_multi (which
+ *   is the case r_a = r, scales[a] = s); ws as
+ *   lq_workspace_size(LQ_OP_FWD_MULTI or LQ_OP_FWD_MULTI_FUSED, T_tokens, N,
+ *   K, R, 1).  1 <= n_adapters <= 64.
+ */
+int lq_lora_fwd_multi_ranks(const void* X, int64_t T_tokens, const lq_weight* W0,
+                            const void* A_cat, const void* B_cat, int32_t n_adapters,
+                            const int32_t* rank_offsets, const float* scales,
+                            const int32_t* seg_offsets, const int32_t* seg_adapter,
+                            int32_t n_seg, lq_dtype dt, void* Y, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
 /* Host-side check of segment metadata (host pointers).  LQ_OK when offsets
  * start at 0, never decrease, end at T_tokens and every id is in range;
  * LQ_ERR_INVALID_ARG otherwise. */

@@ -104,6 +104,50 @@ size_t multi_big_bytes(int64_t T, int64_t N, int64_t K, int64_t rc) {
   return dispatch::big_fwd_eligible(T, N, K) ? dispatch::big_multi_ws_bytes(T, N, K, rc) : 0;
 }
 
+// Column table of the multi-adapter forward from host rank offsets (n + 1
+// entries, checked by the caller) and per-adapter scales.
+MultiTab make_multi_tab(int32_t n, const int32_t* roff, const float* scales, int64_t N) {
+  MultiTab t{};
+  t.n_ad = n;
+  t.rc = roff[n];
+  for (int32_t a = 0; a <= n; ++a) t.roff[a] = roff[a];
+  for (int32_t a = 0; a < n; ++a) {
+    t.scale[a] = scales[a];
+    for (int32_t c = roff[a]; c < roff[a + 1]; ++c) {
+      t.col_base[c] = (int32_t)(N * roff[a] + (c - roff[a]));
+      t.col_stride[c] = roff[a + 1] - roff[a];
+    }
+  }
+  return t;
+}
+
+int multi_common(const void* X, int64_t T_tokens, const lq_weight* W0, const void* A_cat,
+                 const void* B_cat, int32_t n_adapters, const int32_t* roff, const float* scales,
+                 const int32_t* seg_offsets, const int32_t* seg_adapter, int32_t n_seg,
+                 lq_dtype dt, void* Y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  REQUIRE(dt == LQ_BF16, LQ_ERR_UNSUPPORTED, "multi-adapter forward supports bf16 only");
+  int rc = check_weight(W0, dt);
+  if (rc) return rc;
+  if ((rc = check_bf16_shape(W0))) return rc;
+  REQUIRE(T_tokens >= 0 && n_seg >= 0, LQ_ERR_INVALID_ARG, "negative size");
+  if ((rc = check_bf16_rows(T_tokens, W0))) return rc;
+  if (T_tokens == 0) return LQ_OK;
+  REQUIRE(n_seg >= 1, LQ_ERR_INVALID_ARG, "no segments for %lld tokens", (long long)T_tokens);
+  REQUIRE(X && A_cat && B_cat && Y && seg_offsets && seg_adapter, LQ_ERR_INVALID_ARG,
+          "a required pointer is NULL");
+  const int64_t R = roff[n_adapters];
+  const size_t need = dispatch::multi_ws_bytes(T_tokens, R, 1);
+  REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu",
+          ws_bytes, need);
+  const MultiTab mt = make_multi_tab(n_adapters, roff, scales, W0->N);
+  const size_t big = multi_big_bytes(T_tokens, W0->N, W0->K, R);
+  if (big && ws_bytes >= big)
+    return dispatch::big_fwd_multi(X, T_tokens, *W0, A_cat, B_cat, mt, seg_offsets, seg_adapter,
+                                   n_seg, Y, ws, stream);
+  return dispatch::bf16_fwd_multi(X, T_tokens, *W0, A_cat, B_cat, mt, seg_offsets, seg_adapter,
+                                  n_seg, Y, ws, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -278,28 +322,36 @@ int lq_lora_fwd_multi(const void* X, int64_t T_tokens, const lq_weight* W0, cons
                       const void* B_stack, int32_t n_adapters, int64_t r, float scale,
                       const int32_t* seg_offsets, const int32_t* seg_adapter, int32_t n_seg,
                       lq_dtype dt, void* Y, void* ws, size_t ws_bytes, hipStream_t stream) {
-  REQUIRE(dt == LQ_BF16, LQ_ERR_UNSUPPORTED, "multi-adapter forward supports bf16 only");
-  int rc = check_weight(W0, dt);
-  if (rc) return rc;
-  if ((rc = check_bf16_shape(W0))) return rc;
-  REQUIRE(T_tokens >= 0 && n_seg >= 0, LQ_ERR_INVALID_ARG, "negative size");
   REQUIRE(n_adapters >= 1, LQ_ERR_INVALID_ARG, "n_adapters = %d", n_adapters);
   REQUIRE(r >= 1 && r * n_adapters <= kMaxRank, LQ_ERR_UNSUPPORTED,
           "r * n_adapters = %lld exceeds %lld", (long long)(r * n_adapters), (long long)kMaxRank);
-  if ((rc = check_bf16_rows(T_tokens, W0))) return rc;
-  if (T_tokens == 0) return LQ_OK;
-  REQUIRE(n_seg >= 1, LQ_ERR_INVALID_ARG, "no segments for %lld tokens", (long long)T_tokens);
-  REQUIRE(X && A_stack && B_stack && Y && seg_offsets && seg_adapter, LQ_ERR_INVALID_ARG,
-          "a required pointer is NULL");
-  const size_t need = dispatch::multi_ws_bytes(T_tokens, r, n_adapters);
-  REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu",
-          ws_bytes, need);
-  const size_t big = multi_big_bytes(T_tokens, W0->N, W0->K, r * n_adapters);
-  if (big && ws_bytes >= big)
-    return dispatch::big_fwd_multi(X, T_tokens, *W0, A_stack, B_stack, n_adapters, r, scale,
-                                   seg_offsets, seg_adapter, n_seg, Y, ws, stream);
-  return dispatch::bf16_fwd_multi(X, T_tokens, *W0, A_stack, B_stack, n_adapters, r, scale,
-                                  seg_offsets, seg_adapter, n_seg, Y, ws, stream);
+  int32_t roff[kMaxRankCols + 1];
+  float scales[kMaxRankCols];
+  for (int32_t a = 0; a <= n_adapters; ++a) roff[a] = (int32_t)(a * r);
+  for (int32_t a = 0; a < n_adapters; ++a) scales[a] = scale;
+  return multi_common(X, T_tokens, W0, A_stack, B_stack, n_adapters, roff, scales, seg_offsets,
+                      seg_adapter, n_seg, dt, Y, ws, ws_bytes, stream);
+}
+
+int lq_lora_fwd_multi_ranks(const void* X, int64_t T_tokens, const lq_weight* W0,
+                            const void* A_cat, const void* B_cat, int32_t n_adapters,
+                            const int32_t* rank_offsets, const float* scales,
+                            const int32_t* seg_offsets, const int32_t* seg_adapter,
+                            int32_t n_seg, lq_dtype dt, void* Y, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  REQUIRE(n_adapters >= 1 && n_adapters <= kMaxRankCols, LQ_ERR_INVALID_ARG, "n_adapters = %d",
+          n_adapters);
+  REQUIRE(rank_offsets && scales, LQ_ERR_INVALID_ARG, "rank_offsets or scales is NULL");
+  REQUIRE(rank_offsets[0] == 0, LQ_ERR_INVALID_ARG, "rank_offsets[0] = %d, must be 0",
+          rank_offsets[0]);
+  for (int32_t a = 0; a < n_adapters; ++a)
+    REQUIRE(rank_offsets[a + 1] > rank_offsets[a], LQ_ERR_INVALID_ARG,
+            "adapter %d has rank %d (ranks must be >= 1)", a,
+            rank_offsets[a + 1] - rank_offsets[a]);
+  REQUIRE(rank_offsets[n_adapters] <= kMaxRank, LQ_ERR_UNSUPPORTED,
+          "total rank %d exceeds %lld", rank_offsets[n_adapters], (long long)kMaxRank);
+  return multi_common(X, T_tokens, W0, A_cat, B_cat, n_adapters, rank_offsets, scales,
+                      seg_offsets, seg_adapter, n_seg, dt, Y, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -18,6 +18,21 @@ struct NF4Table {
 
 const NF4Table& nf4_table();  // host: built on first use, immutable afterwards
 
+// Multi-adapter rank layout, passed to the kernels by value.  Adapter a owns
+// the concatenated rank columns roff[a] .. roff[a+1]-1 and the scale scale[a]
+// (its alpha_a / r_a); its B (N x r_a, row-major) starts at element N roff[a]
+// of the concatenated B, so rank column c of output row n is element
+// col_base[c] + n col_stride[c].  Uniform ranks are the case roff[a] = a r.
+constexpr int kMaxRankCols = 64;
+struct MultiTab {
+  int32_t n_ad;
+  int32_t rc;  // total rank columns
+  int32_t roff[kMaxRankCols + 1];
+  float scale[kMaxRankCols];
+  int32_t col_base[kMaxRankCols];
+  int32_t col_stride[kMaxRankCols];
+};
+
 // Per-thread error reporting used by the ABI layer.
 void set_error(const char* fmt, ...);
 int hip_fail(hipError_t e, const char* where);

@@ -53,17 +53,17 @@ int u_only(const void* dY, int64_t M, int64_t N, const void* B, int64_t r, float
            hipStream_t st, int32_t* zero, int nzero);
 // The 8-wave shrink kernel behind t_only / u_only (gt: G is B, K x r; needs
 // r % 4 == 0), with the older one-pass kernel as the fallback.
-// row_ad / rmask (optional): column j of row m kept only when
-// j / rmask == row_ad[m] (multi-adapter T), else 0.
+// row_ad / mt (optional, multi-adapter T): column j of row m kept, times the
+// adapter's scale, only inside the columns of adapter row_ad[m], else 0.
 bool shrink_eligible(bool gt, int64_t r);
 // One launch: the NF4 weight W dequantised to bf16 at wout, and the shrink of
 // launch_shrink (same arguments), the flag words cleared as well.
 int launch_prep(const lq_weight& W, void* wout, const void* Z, int64_t M, int64_t K, const void* G,
                 bool gt, int64_t r, float* out, int32_t* zero, int nzero, hipStream_t st,
-                const int32_t* row_ad = nullptr, int rmask = 1);
+                const int32_t* row_ad = nullptr, const MultiTab* mt = nullptr);
 int launch_shrink(const void* Z, int64_t M, int64_t K, const void* G, bool gt, int64_t r,
                   float* out, int32_t* zero, int nzero, hipStream_t st,
-                  const int32_t* row_ad = nullptr, int rmask = 1);
+                  const int32_t* row_ad = nullptr, const MultiTab* mt = nullptr);
 
 // Large-M path: the NF4 weight dequantised to a bf16 workspace copy, then the
 // 256 x 256-tile product with the rank-r expand fused.  Eligible when the
@@ -76,8 +76,8 @@ int big_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const v
             float s, void* Y, float* T_out, void* ws, hipStream_t st);
 // Multi-adapter forward at large T (same eligibility as the forward).
 size_t big_multi_ws_bytes(int64_t T, int64_t N, int64_t K, int64_t rc);
-int big_fwd_multi(const void* X, int64_t T, const lq_weight& W, const void* A_stack,
-                  const void* B_stack, int32_t n_ad, int64_t r, float s, const int32_t* seg_off,
+int big_fwd_multi(const void* X, int64_t T, const lq_weight& W, const void* A_cat,
+                  const void* B_cat, const MultiTab& mt, const int32_t* seg_off,
                   const int32_t* seg_ad, int32_t n_seg, void* Y, void* ws, hipStream_t st);
 // row_ad[m] = adapter of the segment holding row m
 int launch_rowmap(const int32_t* seg_off, const int32_t* seg_ad, int32_t n_seg, int64_t T,
@@ -87,10 +87,9 @@ int big_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const v
            float s, void* dX, float* U, void* ws, hipStream_t st);
 int bf16_merge(const lq_weight& W, const void* A, const void* B, int64_t r, float s, void* Wout,
                hipStream_t st);
-int bf16_fwd_multi(const void* X, int64_t T_tokens, const lq_weight& W, const void* A_stack,
-                   const void* B_stack, int32_t n_adapters, int64_t r, float s,
-                   const int32_t* seg_offsets, const int32_t* seg_adapter, int32_t n_seg, void* Y,
-                   void* ws, hipStream_t st);
+int bf16_fwd_multi(const void* X, int64_t T_tokens, const lq_weight& W, const void* A_cat,
+                   const void* B_cat, const MultiTab& mt, const int32_t* seg_offsets,
+                   const int32_t* seg_adapter, int32_t n_seg, void* Y, void* ws, hipStream_t st);
 
 }  // namespace dispatch
 }  // namespace lq

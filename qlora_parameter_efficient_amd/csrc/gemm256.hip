@@ -90,7 +90,9 @@ struct G256Params {
   float s;
   int32_t ti, tj, splits, ksteps;
   int32_t tpx;  // split K: tiles per XCD
-  int32_t ead_r; // multi-adapter forward: rank of one adapter (E = stacked B), else 0
+  int32_t multi;  // multi-adapter forward: E is the concatenated B, read through col_*
+  int32_t col_base[kMaxRankCols];
+  int32_t col_stride[kMaxRankCols];
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -176,19 +178,20 @@ __device__ __forceinline__ u32x4 e_operand_row(const uint16_t* row, int j0, int 
                (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
 }
 
-// Multi-adapter forward: concatenated rank c of row n is B_{c / rs}[n][c % rs]
-// (E = the stacked B, n_ad x NI x rs); ranks j0 .. j0 + 7, zeros past rc.
-__device__ __forceinline__ u32x4 e_operand_multi(const uint16_t* Bs, int64_t NI, int rs, int64_t n,
-                                                 int j0, int rc) {
-  if (rs % 8 == 0 && j0 + 8 <= rc) {
-    const int a = j0 / rs;
-    return *reinterpret_cast<const u32x4*>(Bs + ((int64_t)a * NI + n) * rs + (j0 - a * rs));
-  }
+// Multi-adapter forward: rank column c of output row n is element
+// col_base[c] + n col_stride[c] of the concatenated B; columns j0 .. j0 + 7,
+// zeros past rc.  One 16-byte load when the eight columns are contiguous in
+// one adapter and aligned.
+__device__ __forceinline__ u32x4 e_operand_multi(const uint16_t* Bc, const int32_t* cb,
+                                                 const int32_t* cs, int64_t n, int j0, int rc) {
+  if (j0 + 8 <= rc && cb[j0 + 7] == cb[j0] + 7 && cs[j0] == cs[j0 + 7] && cs[j0] % 8 == 0 &&
+      cb[j0] % 8 == 0)
+    return *reinterpret_cast<const u32x4*>(Bc + cb[j0] + n * cs[j0]);
   uint16_t v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int c = j0 + i, a = c / rs;
-    v[i] = c < rc ? Bs[((int64_t)a * NI + n) * rs + (c - a * rs)] : (uint16_t)0;
+    const int c = j0 + i;
+    v[i] = c < rc ? Bc[cb[c] + n * cs[c]] : (uint16_t)0;
   }
   return u32x4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
                (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
@@ -472,8 +475,8 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
       const int64_t i = i0 + 128 * wi + 32 * ns + l32;
-      ef[ns] = TR           ? e_operand_col(p.E, NI, i, jr, r)
-               : p.ead_r ? e_operand_multi(p.E, NI, p.ead_r, i, jr, r)
+      ef[ns] = TR       ? e_operand_col(p.E, NI, i, jr, r)
+               : p.multi ? e_operand_multi(p.E, p.col_base, p.col_stride, i, jr, r)
                          : e_operand_row(p.E + i * r, jr, r);
     }
 #pragma unroll
@@ -568,7 +571,7 @@ void launch_shape(const G256Params& p, unsigned blocks, hipStream_t st) {
 
 int launch_g256(bool tr, const void* P, const void* Q, const float* V, const void* E, int64_t M,
                 int64_t NI, int64_t KR, int64_t r, float s, void* Y, void* ws, hipStream_t st,
-                int ead_r = 0) {
+                const MultiTab* mt = nullptr) {
   const G256Plan pl = g256_plan(M, NI);
   G256Params p{};
   p.P = (const uint16_t*)P;
@@ -581,7 +584,13 @@ int launch_g256(bool tr, const void* P, const void* Q, const float* V, const voi
   p.KR = KR;
   p.r = (int32_t)r;
   p.s = s;
-  p.ead_r = ead_r;
+  if (mt) {
+    p.multi = 1;
+    for (int c = 0; c < kMaxRankCols; ++c) {
+      p.col_base[c] = mt->col_base[c];
+      p.col_stride[c] = mt->col_stride[c];
+    }
+  }
   p.ti = (int32_t)pl.ti;
   p.tj = (int32_t)pl.tj;
   p.splits = pl.splits;
@@ -668,13 +677,14 @@ size_t big_multi_ws_bytes(int64_t T, int64_t N, int64_t K, int64_t rc) {
          align256(g256_ws_bytes(T, N)) + (size_t)(N * K) * 2;
 }
 
-// Multi-adapter forward at large T: T_m = X A_cat^T masked to each row's
-// adapter block (A_cat = the stacked A viewed as (n_ad r) x K), then the
-// large-tile product whose expand multiplies by the stacked B.
-int big_fwd_multi(const void* X, int64_t T, const lq_weight& W, const void* A_stack,
-                  const void* B_stack, int32_t n_ad, int64_t r, float s, const int32_t* seg_off,
+// Multi-adapter forward at large T: T_m = X A_cat^T (A_cat = the adapters' A
+// stacked by rows, rc x K) masked to each row's adapter columns and scaled by
+// its scale, then the large-tile product whose expand reads the concatenated
+// B through the column table.
+int big_fwd_multi(const void* X, int64_t T, const lq_weight& W, const void* A_cat,
+                  const void* B_cat, const MultiTab& mt, const int32_t* seg_off,
                   const int32_t* seg_ad, int32_t n_seg, void* Y, void* ws, hipStream_t st) {
-  const int64_t N = W.N, K = W.K, rc = r * n_ad;
+  const int64_t N = W.N, K = W.K, rc = mt.rc;
   char* w = (char*)ws;
   int32_t* row_ad = (int32_t*)w;
   w += align256((size_t)T * 4);
@@ -687,11 +697,11 @@ int big_fwd_multi(const void* X, int64_t T, const lq_weight& W, const void* A_st
   const int nz = (int)(g256_flag_bytes(T, N) / 4);
   const void* Q = W.kind == LQ_WEIGHT_DENSE ? W.dense : (const void*)w;
   if (W.kind != LQ_WEIGHT_DENSE)
-    e = launch_prep(W, w, X, T, K, A_stack, false, rc, Tm, (int32_t*)gws, nz, st, row_ad, (int)r);
+    e = launch_prep(W, w, X, T, K, A_cat, false, rc, Tm, (int32_t*)gws, nz, st, row_ad, &mt);
   else
-    e = launch_shrink(X, T, K, A_stack, false, rc, Tm, (int32_t*)gws, nz, st, row_ad, (int)r);
+    e = launch_shrink(X, T, K, A_cat, false, rc, Tm, (int32_t*)gws, nz, st, row_ad, &mt);
   if (e) return e;
-  return launch_g256(false, X, Q, Tm, B_stack, T, N, K, rc, s, Y, gws, st, (int)r);
+  return launch_g256(false, X, Q, Tm, B_cat, T, N, K, rc, 1.0f, Y, gws, st, &mt);
 }
 
 }  // namespace dispatch

@@ -236,8 +236,8 @@ struct FwdParams {
   WeightArgs W;
   const uint16_t* A;        // r x K            (single adapter)
   const uint16_t* B;        // N x r            (single adapter)
-  const uint16_t* Tm;       // M x RP bf16, s-scaled and adapter-masked (multi)
-  const uint16_t* Bstack;   // n_ad x N x r     (multi)
+  const uint16_t* Tm;       // M x RP bf16, scaled and adapter-masked (multi)
+  const uint16_t* Bstack;   // concatenated B of the adapters (multi), read through col_*
   int32_t r;
   int32_t n_ad;
   float s;
@@ -247,6 +247,9 @@ struct FwdParams {
   uint16_t* Y;
   float* T_out;
   NF4Table tab;
+  int32_t rc;               // multi: total rank columns
+  int32_t col_base[kMaxRankCols];    // multi: rank column c of row n is Bstack[col_base[c]
+  int32_t col_stride[kMaxRankCols];  //        + n col_stride[c]]
 };
 
 constexpr int kFwdTab = 1024;  // second-level steps of one tile's 128 rows (K <= 65536)
@@ -502,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
       }
     }
   } else {
-    const int rc = r * p.n_ad;
+    const int rc = p.rc;
     const int chunks = (rc + 15) >> 4;
 #pragma unroll
     for (int c = 0; c < RP / 16; ++c) {
@@ -520,11 +523,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int j = j0 + i;
-              e[i] = 0;
-              if (j < rc) {
-                const int a = j / r, jj = j - a * r;
-                e[i] = p.Bstack[((int64_t)a * N + n) * r + jj];
-              }
+              e[i] = j < rc ? p.Bstack[p.col_base[j] + n * p.col_stride[j]] : (uint16_t)0;
             }
             v[2 * half] = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
             v[2 * half + 1] = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
@@ -924,14 +923,15 @@ __global__ void rowmap_kernel(const int32_t* __restrict__ off, const int32_t* __
   for (int64_t m = lo + threadIdx.x; m < hi; m += blockDim.x) row_ad[m] = a;
 }
 
-// Tm[m][c] = s * sum_k X[m][k] Acat[c][k] if adapter(m) == c / r else 0, for
-// c < n_ad * r (Acat = A_stack viewed as (n_ad r) x K), zero up to RP; bf16.
+// Tm[m][c] = scale[a] * sum_k X[m][k] Acat[c][k] if column c belongs to the
+// row's adapter a = row_ad[m] (mt), else 0, for c < rc (Acat = the adapters' A
+// stacked by rows, rc x K), zero up to RP; bf16.
 // Each wave takes 32 rows; lane (h, l32) reads row l32, 32 contiguous columns
 // per 64-step (the same relabelling of the reduction index on both operands).
 template <int RP>
 __global__ __launch_bounds__(kThreads) void multi_shrink_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t K, const uint16_t* __restrict__ Acat,
-    int rc, int r, const int32_t* __restrict__ row_ad, float s, uint16_t* __restrict__ Tm) {
+    int rc, const int32_t* __restrict__ row_ad, MultiTab mt, uint16_t* __restrict__ Tm) {
   constexpr int JT = RP / 32;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, l32 = lane & 31;
@@ -966,7 +966,8 @@ __global__ __launch_bounds__(kThreads) void multi_shrink_kernel(
       for (int jt = 0; jt < JT; ++jt) t[jt] = mfma32(af[jt][q], xf[q], t[jt]);
   }
   if (m >= M) return;
-  const int a = row_ad[m];
+  int a = row_ad[m];  // clamped: ids are in range by precondition
+  a = a < 0 ? 0 : (a >= mt.n_ad ? mt.n_ad - 1 : a);
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
@@ -976,7 +977,8 @@ __global__ __launch_bounds__(kThreads) void multi_shrink_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = c0 + i;
-        v[i] = (c < rc && c / r == a) ? s * t[jt][4 * q + i] : 0.0f;
+        v[i] = (c < rc && c >= mt.roff[a] && c < mt.roff[a + 1]) ? mt.scale[a] * t[jt][4 * q + i]
+                                                                 : 0.0f;
       }
       *reinterpret_cast<u32x2*>(Tm + m * RP + c0) = u32x2{pack_bf16x2(v[0], v[1]),
                                                           pack_bf16x2(v[2], v[3])};
@@ -1091,11 +1093,10 @@ size_t multi_ws_bytes(int64_t T_tokens, int64_t r, int32_t n_adapters) {
   return (size_t)T_tokens * 4 + (size_t)T_tokens * rp * 2 + 256;
 }
 
-int bf16_fwd_multi(const void* X, int64_t T_tokens, const lq_weight& W, const void* A_stack,
-                   const void* B_stack, int32_t n_adapters, int64_t r, float s,
-                   const int32_t* seg_offsets, const int32_t* seg_adapter, int32_t n_seg, void* Y,
-                   void* ws, hipStream_t st) {
-  const int rc = (int)(r * n_adapters);
+int bf16_fwd_multi(const void* X, int64_t T_tokens, const lq_weight& W, const void* A_cat,
+                   const void* B_cat, const MultiTab& mt, const int32_t* seg_offsets,
+                   const int32_t* seg_adapter, int32_t n_seg, void* Y, void* ws, hipStream_t st) {
+  const int rc = mt.rc;
   const int rp = rc <= 32 ? 32 : 64;
   int32_t* row_ad = (int32_t*)ws;
   uintptr_t tm_addr = ((uintptr_t)ws + (size_t)T_tokens * 4 + 255) & ~(uintptr_t)255;
@@ -1108,22 +1109,27 @@ int bf16_fwd_multi(const void* X, int64_t T_tokens, const lq_weight& W, const vo
   const unsigned sblocks = (unsigned)cdiv(T_tokens, 128);
   if (rp == 32)
     hipLaunchKernelGGL(multi_shrink_kernel<32>, dim3(sblocks), dim3(kThreads), 0, st,
-                       (const uint16_t*)X, T_tokens, K, (const uint16_t*)A_stack, rc, (int)r,
-                       row_ad, s, Tm);
+                       (const uint16_t*)X, T_tokens, K, (const uint16_t*)A_cat, rc, row_ad, mt,
+                       Tm);
   else
     hipLaunchKernelGGL(multi_shrink_kernel<64>, dim3(sblocks), dim3(kThreads), 0, st,
-                       (const uint16_t*)X, T_tokens, K, (const uint16_t*)A_stack, rc, (int)r,
-                       row_ad, s, Tm);
+                       (const uint16_t*)X, T_tokens, K, (const uint16_t*)A_cat, rc, row_ad, mt,
+                       Tm);
   if ((e = hip_fail(hipGetLastError(), "multi shrink launch"))) return e;
   FwdParams p{};
   p.X = (const uint16_t*)X;
   p.M = T_tokens;
   p.W = weight_args(W);
   p.Tm = Tm;
-  p.Bstack = (const uint16_t*)B_stack;
-  p.r = (int32_t)r;
-  p.n_ad = n_adapters;
-  p.s = s;
+  p.Bstack = (const uint16_t*)B_cat;
+  p.r = rc;
+  p.n_ad = mt.n_ad;
+  p.s = 1.0f;
+  p.rc = rc;
+  for (int c = 0; c < kMaxRankCols; ++c) {
+    p.col_base[c] = mt.col_base[c];
+    p.col_stride[c] = mt.col_stride[c];
+  }
   p.Y = (uint16_t*)Y;
   p.tab = nf4_table();
   return fwd_dispatch<true>(p, W, rp, st);

@@ -44,13 +44,15 @@ __device__ __forceinline__ u32x2 tr_read(const uint16_t* p) {
 
 // 16 rows (rb * 16 ..) of out with NW waves; every thread of the workgroup
 // (64 NW of them) calls it.
-// row_ad (optional): result column j of row m is kept only when
-// j / rmask == row_ad[m] (the row's adapter block), else written as 0.
+// row_ad (optional, multi-adapter): result column j of row m is kept, times
+// the adapter's scale, only inside the columns of the row's adapter row_ad[m]
+// (mt), else written as 0.
 template <int JT, bool GT, int NW>
 __device__ __forceinline__ void shrink_rows(int64_t rb, const uint16_t* __restrict__ Z, int64_t M,
                                             int64_t K, const uint16_t* __restrict__ G, int r,
                                             float* __restrict__ out,
-                                            const int32_t* __restrict__ row_ad, int rmask) {
+                                            const int32_t* __restrict__ row_ad,
+                                            const MultiTab& mt) {
   constexpr int RC = 16 * JT;    // rank columns, padded
   constexpr int R = 8 / JT;      // units per round
   constexpr int NB = R * JT;     // GT: 1 KB pieces of B per round (32 R rows of up to RC)
@@ -160,7 +162,15 @@ __device__ __forceinline__ void shrink_rows(int64_t rb, const uint16_t* __restri
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + 4 * g + i;
-        if (m < M && j < r) out[m * r + j] = (row_ad && j / rmask != row_ad[m]) ? 0.0f : s[i];
+        if (m < M && j < r) {
+          float v = s[i];
+          if (row_ad) {
+            int a = row_ad[m];  // clamped: ids are in range by precondition
+            a = a < 0 ? 0 : (a >= mt.n_ad ? mt.n_ad - 1 : a);
+            v = (j >= mt.roff[a] && j < mt.roff[a + 1]) ? v * mt.scale[a] : 0.0f;
+          }
+          out[m * r + j] = v;
+        }
       }
     }
   }
@@ -173,12 +183,12 @@ __global__ __launch_bounds__(kSThreads) void shrink_kernel(const uint16_t* __res
                                                            int r, float* __restrict__ out,
                                                            int32_t* __restrict__ zero, int nzero,
                                                            const int32_t* __restrict__ row_ad,
-                                                           int rmask) {
+                                                           MultiTab mt) {
   // side job: clear the next kernel's flag words (a kernel store, so it also
   // replays correctly inside a captured graph)
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < nzero; i += kSThreads) zero[i] = 0;
-  shrink_rows<JT, GT, kSW>(blockIdx.x, Z, M, K, G, r, out, row_ad, rmask);
+  shrink_rows<JT, GT, kSW>(blockIdx.x, Z, M, K, G, r, out, row_ad, mt);
 }
 
 // Prep of the large-M path in one launch: workgroups below nd write the bf16
@@ -202,32 +212,33 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs pa, const uint16_t* 
                                                    const uint16_t* __restrict__ G, int r,
                                                    float* __restrict__ out,
                                                    int32_t* __restrict__ zero, int nzero,
-                                                   const int32_t* __restrict__ row_ad, int rmask) {
+                                                   const int32_t* __restrict__ row_ad,
+                                                   MultiTab mt) {
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < nzero; i += 256) zero[i] = 0;
   if ((int)blockIdx.x < pa.nd)
     nf4_deq_span<true>(threadIdx.x, blockIdx.x, pa.codes, pa.q8, pa.c2, pa.absmax, pa.dq, pa.n,
                        pa.wout, pa.tab);
   else
-    shrink_rows<JT, GT, 4>((int64_t)blockIdx.x - pa.nd, Z, M, K, G, r, out, row_ad, rmask);
+    shrink_rows<JT, GT, 4>((int64_t)blockIdx.x - pa.nd, Z, M, K, G, r, out, row_ad, mt);
 }
 
 template <bool GT>
 int launch(const uint16_t* Z, int64_t M, int64_t K, const uint16_t* G, int64_t r, float* out,
-           int32_t* zero, int nzero, const int32_t* row_ad, int rmask, hipStream_t st) {
+           int32_t* zero, int nzero, const int32_t* row_ad, const MultiTab& mt, hipStream_t st) {
   const dim3 grid((unsigned)cdiv(M, 16)), block(kSThreads);
   switch ((r + 15) / 16) {
     case 1:
       hipLaunchKernelGGL((shrink_kernel<1, GT>), grid, block, 0, st, Z, M, K, G, (int)r, out,
-                         zero, nzero, row_ad, rmask);
+                         zero, nzero, row_ad, mt);
       break;
     case 2:
       hipLaunchKernelGGL((shrink_kernel<2, GT>), grid, block, 0, st, Z, M, K, G, (int)r, out,
-                         zero, nzero, row_ad, rmask);
+                         zero, nzero, row_ad, mt);
       break;
     default:
       hipLaunchKernelGGL((shrink_kernel<4, GT>), grid, block, 0, st, Z, M, K, G, (int)r, out,
-                         zero, nzero, row_ad, rmask);
+                         zero, nzero, row_ad, mt);
       break;
   }
   return hip_fail(hipGetLastError(), "shrink launch");
@@ -241,17 +252,21 @@ bool shrink_eligible(bool gt, int64_t r) { return !gt || r % 4 == 0; }
 
 int launch_shrink(const void* Z, int64_t M, int64_t K, const void* G, bool gt, int64_t r,
                   float* out, int32_t* zero, int nzero, hipStream_t st, const int32_t* row_ad,
-                  int rmask) {
+                  const MultiTab* mt) {
+  const MultiTab none{};
+  const MultiTab& t = mt ? *mt : none;
   if (gt)
     return launch<true>((const uint16_t*)Z, M, K, (const uint16_t*)G, r, out, zero, nzero, row_ad,
-                        rmask, st);
+                        t, st);
   return launch<false>((const uint16_t*)Z, M, K, (const uint16_t*)G, r, out, zero, nzero, row_ad,
-                       rmask, st);
+                       t, st);
 }
 
 int launch_prep(const lq_weight& W, void* wout, const void* Z, int64_t M, int64_t K, const void* G,
                 bool gt, int64_t r, float* out, int32_t* zero, int nzero, hipStream_t st,
-                const int32_t* row_ad, int rmask) {
+                const int32_t* row_ad, const MultiTab* mt) {
+  const MultiTab none{};
+  const MultiTab& mtab = mt ? *mt : none;
   PrepArgs pa;
   pa.codes = W.codes;
   pa.q8 = W.q8;
@@ -269,26 +284,26 @@ int launch_prep(const lq_weight& W, void* wout, const void* Z, int64_t M, int64_
     case 1:
       if (gt)
         hipLaunchKernelGGL((prep_kernel<1, true>), grid, block, 0, st, pa, Zh, M, K, Gh, (int)r,
-                           out, zero, nzero, row_ad, rmask);
+                           out, zero, nzero, row_ad, mtab);
       else
         hipLaunchKernelGGL((prep_kernel<1, false>), grid, block, 0, st, pa, Zh, M, K, Gh, (int)r,
-                           out, zero, nzero, row_ad, rmask);
+                           out, zero, nzero, row_ad, mtab);
       break;
     case 2:
       if (gt)
         hipLaunchKernelGGL((prep_kernel<2, true>), grid, block, 0, st, pa, Zh, M, K, Gh, (int)r,
-                           out, zero, nzero, row_ad, rmask);
+                           out, zero, nzero, row_ad, mtab);
       else
         hipLaunchKernelGGL((prep_kernel<2, false>), grid, block, 0, st, pa, Zh, M, K, Gh, (int)r,
-                           out, zero, nzero, row_ad, rmask);
+                           out, zero, nzero, row_ad, mtab);
       break;
     default:
       if (gt)
         hipLaunchKernelGGL((prep_kernel<4, true>), grid, block, 0, st, pa, Zh, M, K, Gh, (int)r,
-                           out, zero, nzero, row_ad, rmask);
+                           out, zero, nzero, row_ad, mtab);
       else
         hipLaunchKernelGGL((prep_kernel<4, false>), grid, block, 0, st, pa, Zh, M, K, Gh, (int)r,
-                           out, zero, nzero, row_ad, rmask);
+                           out, zero, nzero, row_ad, mtab);
       break;
   }
   return hip_fail(hipGetLastError(), "prep launch");

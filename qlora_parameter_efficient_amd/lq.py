@@ -57,6 +57,8 @@ _SIGS = {
     "lq_lora_merge": (ctypes.c_int, [_WP, _vp, _vp, _i64, _f32, _i32, _vp, _vp]),
     "lq_lora_fwd_multi": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i32, _i64, _f32, _vp, _vp, _i32,
                                          _i32, _vp, _vp, _sz, _vp]),
+    "lq_lora_fwd_multi_ranks": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
+                                               _i32, _i32, _vp, _vp, _sz, _vp]),
     "lq_check_segments": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i32]),
     "lq_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i64, _i32]),
     "lq_lora_num_params": (_i64, [_i64, _i64, _i64]),
@@ -272,6 +274,33 @@ def lq_lora_fwd_multi(X, W0, A_stack, B_stack, scale, seg_offsets, seg_adapter, 
     _check(lib().lq_lora_fwd_multi(_ptr(X), T, ctypes.byref(w), _ptr(A_stack), _ptr(B_stack), n_ad,
                                    r, scale, _ptr(seg_offsets), _ptr(seg_adapter), n_seg, dt,
                                    _ptr(Y), _ptr(ws), ws.numel(), _stream()))
+    return Y
+
+
+def lq_lora_fwd_multi_ranks(X, W0, A_cat, B_cat, rank_offsets, scales, seg_offsets, seg_adapter,
+                            ws=None, Y=None, fused=False):
+    """Adapters of different ranks: A_cat (R x K) and B_cat (the adapters' B
+    flattened one after another) on the device; rank_offsets (n+1) and
+    scales (n) are host sequences."""
+    import numpy as np
+    _dev(X, A_cat, B_cat, seg_offsets, seg_adapter)
+    dt = _dt(X)
+    T = X.shape[0]
+    w = weight_struct(W0, dt)
+    roff = np.ascontiguousarray(rank_offsets, dtype=np.int32)
+    sc = np.ascontiguousarray(scales, dtype=np.float32)
+    n_ad = sc.size
+    R = int(roff[-1])
+    if Y is None:
+        Y = torch.empty((T, w.N), dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = _ws(lq_workspace_size(LQ_OP_FWD_MULTI_FUSED if fused else LQ_OP_FWD_MULTI, T, w.N,
+                                   w.K, R, 1), X.device)
+    _check(lib().lq_lora_fwd_multi_ranks(_ptr(X), T, ctypes.byref(w), _ptr(A_cat), _ptr(B_cat),
+                                         n_ad, roff.ctypes.data_as(ctypes.c_void_p),
+                                         sc.ctypes.data_as(ctypes.c_void_p), _ptr(seg_offsets),
+                                         _ptr(seg_adapter), seg_adapter.numel(), dt, _ptr(Y),
+                                         _ptr(ws), ws.numel(), _stream()))
     return Y
 
 

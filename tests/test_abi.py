@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(lq.LIB_PATH),
 
 def test_exports_every_declared_symbol():
     declared = lq.declared_symbols()
-    assert len(declared) == 13
+    assert len(declared) == 14
     L = lq.lib()
     for name in declared:
         assert hasattr(L, name), name
@@ -109,6 +109,18 @@ def test_argument_errors_launch_nothing():
                                0x1000, 1, 0, 0x1000, 0x1000, 1 << 20, None) == -2
     assert L.lq_lora_fwd_multi(0x1000, 10, ctypes.byref(w), 0x1000, 0x1000, 4, 16, 2.0, 0x1000,
                                0x1000, 0, 1, 0x1000, 0x1000, 1 << 20, None) == -1
+    # multi-adapter with per-adapter ranks: offsets must start at 0, rise, total <= 64
+    sc = (ctypes.c_float * 3)(2.0, 2.0, 2.0)
+
+    def ranks(*offs):
+        ro = (ctypes.c_int32 * len(offs))(*offs)
+        return L.lq_lora_fwd_multi_ranks(0x1000, 10, ctypes.byref(w), 0x1000, 0x1000, 3, ro, sc,
+                                         0x1000, 0x1000, 1, 1, 0x1000, 0x1000, 1 << 20, None)
+    assert ranks(1, 2, 3, 4) == -1
+    assert ranks(0, 4, 4, 8) == -1
+    assert ranks(0, 30, 50, 70) == -2
+    assert L.lq_lora_fwd_multi_ranks(0x1000, 10, ctypes.byref(w), 0x1000, 0x1000, 3, None, sc,
+                                     0x1000, 0x1000, 1, 1, 0x1000, 0x1000, 1 << 20, None) == -1
     # merge
     assert L.lq_lora_merge(ctypes.byref(w), None, 0x1000, 8, 2.0, 1, 0x1000, None) == -1
     # reserved field must be zero

@@ -129,3 +129,70 @@ def test_nf4_shared_base(counts):
     ids = rng.integers(0, 3, len(counts))
     X, W0, A, B, off, ids = small_multi(counts, ids, 3, 16, seed=7)
     run_multi(X, W0, A, B, off, ids, 2.0, label="nf4 base", nf4=True)
+
+
+def run_multi_ranks(counts, ids, ranks, scales, N=256, K=256, seed=13, nf4=False, fused=False,
+                    label=""):
+    """Adapters of different ranks and scales against the oracle's per-segment
+    forward, plus the adapter term on its own (as in run_multi)."""
+    rng = np.random.default_rng(seed)
+    T = int(np.sum(counts))
+    X = wl.Tensor(rng.standard_normal((T, K), dtype=np.float32), "bf16")
+    W0 = wl.Tensor(rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02), "bf16")
+    As = [wl.Tensor(rng.standard_normal((r, K), dtype=np.float32) * np.float32(0.1), "bf16")
+          for r in ranks]
+    Bs = [wl.Tensor(rng.standard_normal((N, r), dtype=np.float32) * np.float32(0.1), "bf16")
+          for r in ranks]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    ids = np.asarray(ids, np.int32)
+    roff = np.concatenate([[0], np.cumsum(ranks)]).astype(np.int32)
+    announce(f"multi ranks {label} T={T} ranks={list(ranks)} nf4={nf4} fused={fused}")
+    A_cat = torch.cat([to_dev(a) for a in As], 0).contiguous()
+    B_cat = torch.cat([to_dev(b).reshape(-1) for b in Bs]).contiguous()
+    Xd = to_dev(X)
+    Wd = to_dev(W0)
+    Wo = W0.f64()
+    if nf4:
+        Wd = lq.lq_nf4_quantize(Wd)
+        q = onf4.nf4_quantize(W0.value)
+        Wo = onf4.bf16_bits_to_f64(onf4.nf4_dequantize_bf16(q)).reshape(N, K)
+    so = torch.from_numpy(off).to(DEV)
+    sa = torch.from_numpy(ids).to(DEV)
+    Y = lq.lq_lora_fwd_multi_ranks(Xd, Wd, A_cat, B_cat, roff, scales, so, sa, fused=fused)
+    Yb = lq.lq_lora_fwd_multi_ranks(Xd, Wd, A_cat, torch.zeros_like(B_cat), roff, scales, so, sa,
+                                     fused=fused)
+    torch.cuda.synchronize()
+    Yo = olora.lora_forward_multi(X.f64(), Wo, [a.f64() for a in As], [b.f64() for b in Bs],
+                                  list(scales), off, ids)
+    base = X.f64() @ Wo.T
+    Yg, Ybg = f64(Y), f64(Yb)
+    assert rel_err(Yg, Yo) <= BF16_TOL
+    assert rel_err(Yg - Ybg, Yo - base) <= 0.05
+
+
+@pytest.mark.parametrize("nf4", [False, True], ids=["bf16", "nf4"])
+@pytest.mark.parametrize("fused", [False, True], ids=["large", "fused"])
+def test_mixed_ranks(fused, nf4):
+    """Ranks 4, 16, 1, 8 (R = 29) with their own scales; T = 2307 takes the
+    large-tile path unless the fused-size workspace is given."""
+    counts = [0, 700, 1, 513, 0, 900, 129, 64]
+    ids = [2, 0, 3, 1, 1, 2, 0, 3]
+    run_multi_ranks(counts, ids, [4, 16, 1, 8], [8.0, 2.0, 32.0, 4.0], nf4=nf4, fused=fused,
+                    label="mixed")
+
+
+def test_mixed_ranks_equal_ranks_match_uniform_call():
+    """Equal ranks through lq_lora_fwd_multi_ranks give exactly the result of
+    lq_lora_fwd_multi (the same kernels and the same table)."""
+    counts = [0, 700, 1, 513, 0, 900, 129, 64]
+    rng = np.random.default_rng(3)
+    ids = rng.integers(0, 3, len(counts))
+    X, W0, A, B, off, ids = small_multi(counts, ids, 3, 8)
+    Xd, Wd, Ad, Bd = to_dev(X), to_dev(W0), to_dev(A), to_dev(B)
+    so = torch.from_numpy(off).to(DEV)
+    sa = torch.from_numpy(ids).to(DEV)
+    Y1 = lq.lq_lora_fwd_multi(Xd, Wd, Ad, Bd, 2.0, so, sa)
+    Y2 = lq.lq_lora_fwd_multi_ranks(Xd, Wd, Ad.reshape(24, 256).contiguous(),
+                                    Bd.reshape(-1).contiguous(), [0, 8, 16, 24], [2.0] * 3, so, sa)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
