@@ -30,6 +30,7 @@ Modules:
     nf4   -- codebook, quantize / dequantize with double quantization
     lora  -- forward, backward, merge, segmented multi-adapter forward,
              trainable-parameter counts
+    optim -- AdamW step on the adapter factors (float32 master, m, v)
 
 Parity unpinned: none of the functions here is without a pin; what pins
 each one is listed in the test files under ``tests/`` (``test_oracle_*``).
@@ -38,4 +39,4 @@ second-level constants are readings of the pages (see the ``nf4`` module
 docstring); they are pinned to the pages' properties, not to an external
 NF4 implementation, which none of the pages prints.
 """
-from . import lora, nf4  # noqa: F401
+from . import lora, nf4, optim  # noqa: F401
