@@ -294,6 +294,23 @@ def secondary(S, torch):
     res["multi_adapter_config5"] = {"tokens": T5, "ms": round(t, 3),
                                     "TFLOPs": round(flop / (t * 1e-3) / 1e12, 1)}
     del X5, Y5, ws5
+    # AdamW step on the adapters: float32 master, m, v and gradient, bf16 working
+    # copy (16 bytes read and 14 written per parameter)
+    for name, sizes in (("adamw_config4_block_r64", wl.config4_adapter_sizes()),
+                        ("adamw_config3_r16", [R * K, N * R])):
+        masters, grads = wl.adamw_case(sizes, 1, seed=19)
+        ps = []
+        for m0, g0 in zip(masters, grads[0]):
+            n = m0.size
+            ps.append((torch.from_numpy(m0).to(S["dev"]), torch.zeros(n, device=S["dev"]),
+                       torch.zeros(n, device=S["dev"]), torch.from_numpy(g0).to(S["dev"]),
+                       torch.empty(n, dtype=torch.bfloat16, device=S["dev"])))
+        f = lambda: lq.lq_adamw_step(ps, 1, lr=1e-4, weight_decay=0.01)  # noqa: E731
+        t = graph_time(f, torch)
+        nparam = sum(sizes)
+        res[name] = {"tensors": len(sizes), "params": nparam, "us": round(t * 1e3, 2),
+                     "GBs": round(30 * nparam / (t * 1e-3) / 1e9, 1)}
+        del ps
     return res
 
 

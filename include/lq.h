@@ -248,6 +248,55 @@ int lq_lora_fwd_multi_ranks(const void* X, int64_t T_tokens, const lq_weight* W0
                             int32_t n_seg, lq_dtype dt, void* Y, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------- optimizer step (A, B) */
+
+/*
+ * One trainable tensor for lq_adamw_step.  All pointers are device memory
+ * owned by the caller; master, m, v and weight are updated in place.
+ *   master  n float32 master weights
+ *   m, v    n float32 first and second moments (zero before step 1)
+ *   grad    n gradient elements of the call's gdt (e.g. dA or dB of
+ *           lq_lora_bwd, accumulated over micro-batches with accumulate = 1)
+ *   weight  optional (NULL: not written): n bf16 working weights, written as
+ *           the round-to-nearest-even bf16 of the new master (the A or B the
+ *           next lq_lora_fwd reads)
+ *   n       element count (0: the entry is skipped and its pointers unused)
+ * Vector loads are used when master, m and v are 16-byte aligned, grad is
+ * 16-byte (float32) or 8-byte (bf16) aligned and weight 8-byte aligned;
+ * other alignments work element by element.
+ */
+typedef struct lq_adamw_tensor {
+  float* master;
+  float* m;
+  float* v;
+  const void* grad;
+  void* weight;
+  int64_t n;
+} lq_adamw_tensor;
+
+/*
+ * AdamW step t on the LoRA factors, float32 master weights and moments and a
+ * bf16 working copy ([FT] "The real memory ledger": 16 bytes per trainable
+ * parameter -- bf16 weight, bf16 gradient, float32 master, m and v; [MF] "The
+ * Memory Bottleneck of Full Fine-Tuning").  The pages name AdamW without its
+ * formula; the update is decoupled-weight-decay Adam (Loshchilov and Hutter,
+ * 2019), element-wise in float32 with g = grad_scale * grad:
+ *   p <- p (1 - lr weight_decay)
+ *   m <- beta1 m + (1 - beta1) g,   v <- beta2 v + (1 - beta2) g^2
+ *   p <- p - (lr / (1 - beta1^t)) m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ * The scalar factors are formed in double on the host and rounded once.
+ *   tensors   host array of n_tensors descriptors (read during the call only)
+ *   gdt       LQ_F32 or LQ_BF16, the gradients' type
+ *   step      t >= 1
+ *   grad_scale  e.g. 1 / (number of accumulated micro-batches)
+ * Requires 0 <= beta1, beta2 < 1, eps >= 0, lr >= 0, weight_decay >= 0, all
+ * finite; each n in [0, 2^40]; tensors must not overlap.  n_tensors = 0 is a
+ * no-op.  Several tensors go into one launch (up to 24 per launch).
+ */
+int lq_adamw_step(const lq_adamw_tensor* tensors, int32_t n_tensors, lq_dtype gdt, float lr,
+                  float beta1, float beta2, float eps, float weight_decay, int64_t step,
+                  float grad_scale, hipStream_t stream);
+
 /* Host-side check of segment metadata (host pointers).  LQ_OK when offsets
  * start at 0, never decrease, end at T_tokens and every id is in range;
  * LQ_ERR_INVALID_ARG otherwise. */

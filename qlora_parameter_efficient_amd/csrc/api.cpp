@@ -3,6 +3,7 @@
 // kernels of the .hip translation units.
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 
 #include "common.h"
@@ -161,6 +162,35 @@ int lq_nf4_codebook(float* out) {
 }
 
 int64_t lq_lora_num_params(int64_t N, int64_t K, int64_t r) { return r * (N + K); }
+
+int lq_adamw_step(const lq_adamw_tensor* tensors, int32_t n_tensors, lq_dtype gdt, float lr,
+                  float beta1, float beta2, float eps, float weight_decay, int64_t step,
+                  float grad_scale, hipStream_t stream) {
+  REQUIRE(n_tensors >= 0, LQ_ERR_INVALID_ARG, "n_tensors = %d", n_tensors);
+  if (n_tensors == 0) return LQ_OK;
+  REQUIRE(tensors != nullptr, LQ_ERR_INVALID_ARG, "tensor table is NULL");
+  REQUIRE(gdt == LQ_F32 || gdt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad gradient dtype %d", (int)gdt);
+  REQUIRE(step >= 1, LQ_ERR_INVALID_ARG, "step %lld (steps count from 1)", (long long)step);
+  REQUIRE(std::isfinite(lr) && lr >= 0.0f, LQ_ERR_INVALID_ARG, "lr must be finite and >= 0");
+  REQUIRE(std::isfinite(beta1) && beta1 >= 0.0f && beta1 < 1.0f, LQ_ERR_INVALID_ARG,
+          "beta1 must be in [0, 1)");
+  REQUIRE(std::isfinite(beta2) && beta2 >= 0.0f && beta2 < 1.0f, LQ_ERR_INVALID_ARG,
+          "beta2 must be in [0, 1)");
+  REQUIRE(std::isfinite(eps) && eps >= 0.0f, LQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  REQUIRE(std::isfinite(weight_decay) && weight_decay >= 0.0f, LQ_ERR_INVALID_ARG,
+          "weight_decay must be finite and >= 0");
+  REQUIRE(std::isfinite(grad_scale), LQ_ERR_INVALID_ARG, "grad_scale must be finite");
+  for (int32_t i = 0; i < n_tensors; ++i) {
+    const lq_adamw_tensor& t = tensors[i];
+    REQUIRE(t.n >= 0 && t.n <= ((int64_t)1 << 40), LQ_ERR_INVALID_ARG, "tensor %d: n = %lld", i,
+            (long long)t.n);
+    if (t.n == 0) continue;
+    REQUIRE(t.master && t.m && t.v && t.grad, LQ_ERR_INVALID_ARG,
+            "tensor %d: master, m, v and grad are required", i);
+  }
+  dispatch::AdamHyper h{lr, beta1, beta2, eps, weight_decay, grad_scale, step};
+  return dispatch::adamw_step(tensors, n_tensors, gdt == LQ_BF16, h, stream);
+}
 
 int lq_check_segments(const int32_t* h_offsets, const int32_t* h_adapter, int32_t n_seg,
                       int64_t T_tokens, int32_t n_adapters) {

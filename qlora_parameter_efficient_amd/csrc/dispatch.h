@@ -91,5 +91,15 @@ int bf16_fwd_multi(const void* X, int64_t T_tokens, const lq_weight& W, const vo
                    const void* B_cat, const MultiTab& mt, const int32_t* seg_offsets,
                    const int32_t* seg_adapter, int32_t n_seg, void* Y, void* ws, hipStream_t st);
 
+// AdamW step over a list of tensors (adamw.hip); launches in groups of
+// kAdamTensors tensors.  Arguments already validated.
+constexpr int kAdamTensors = 24;
+struct AdamHyper {
+  float lr, beta1, beta2, eps, weight_decay, grad_scale;
+  int64_t step;
+};
+int adamw_step(const lq_adamw_tensor* ts, int32_t n_tensors, bool bf16_grad, const AdamHyper& h,
+               hipStream_t st);
+
 }  // namespace dispatch
 }  // namespace lq

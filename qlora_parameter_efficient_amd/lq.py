@@ -43,6 +43,11 @@ class LqWeightStruct(ctypes.Structure):
     ]
 
 
+class LqAdamwTensor(ctypes.Structure):
+    _fields_ = [("master", ctypes.c_void_p), ("m", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("grad", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("n", ctypes.c_int64)]
+
+
 _lib = None
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 _WP = ctypes.POINTER(LqWeightStruct)
@@ -59,6 +64,8 @@ _SIGS = {
                                          _i32, _vp, _vp, _sz, _vp]),
     "lq_lora_fwd_multi_ranks": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
                                                _i32, _i32, _vp, _vp, _sz, _vp]),
+    "lq_adamw_step": (ctypes.c_int, [ctypes.POINTER(LqAdamwTensor), _i32, _i32, _f32, _f32, _f32,
+                                     _f32, _f32, _i64, _f32, _vp]),
     "lq_check_segments": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i32]),
     "lq_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i64, _i32]),
     "lq_lora_num_params": (_i64, [_i64, _i64, _i64]),
@@ -302,6 +309,39 @@ def lq_lora_fwd_multi_ranks(X, W0, A_cat, B_cat, rank_offsets, scales, seg_offse
                                          _ptr(seg_adapter), seg_adapter.numel(), dt, _ptr(Y),
                                          _ptr(ws), ws.numel(), _stream()))
     return Y
+
+
+def lq_adamw_step(params, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                  grad_scale=1.0):
+    """AdamW step t = ``step`` in place on a list of trainable tensors.
+
+    params: sequence of (master, m, v, grad, weight) device tensors; master, m
+    and v float32, grad float32 or bf16 (one dtype for the whole list), weight
+    a bf16 working copy or None; all of one element count per entry.
+    """
+    params = list(params)
+    if not params:
+        return
+    arr = (LqAdamwTensor * len(params))()
+    gdt = None
+    for i, (master, m, v, grad, weight) in enumerate(params):
+        _dev(master, m, v, grad, weight)
+        for t in (master, m, v):
+            if t.dtype != torch.float32:
+                raise TypeError("master, m and v must be float32")
+        if weight is not None and weight.dtype != torch.bfloat16:
+            raise TypeError("the working copy must be bf16")
+        n = master.numel()
+        if any(t is not None and t.numel() != n for t in (m, v, grad, weight)):
+            raise ValueError(f"entry {i}: element counts differ")
+        d = _dt(grad)
+        if gdt is None:
+            gdt = d
+        elif d != gdt:
+            raise TypeError("all gradients must have one dtype")
+        arr[i] = LqAdamwTensor(_ptr(master), _ptr(m), _ptr(v), _ptr(grad), _ptr(weight), n)
+    _check(lib().lq_adamw_step(arr, len(params), gdt, lr, beta1, beta2, eps, weight_decay,
+                               int(step), grad_scale, _stream()))
 
 
 def lq_check_segments(offsets, adapter, T_tokens, n_adapters):

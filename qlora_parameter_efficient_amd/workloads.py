@@ -27,6 +27,8 @@ __all__ = [
     "config5",
     "decode_inputs",
     "small_case",
+    "adamw_case",
+    "config4_adapter_sizes",
 ]
 
 
@@ -208,3 +210,35 @@ def small_case(M, N, K, r, dtype="bf16", seed=7, sw=0.02, sa=None, sb=0.01, zero
     if zero_b:
         B = Tensor(np.zeros((N, r), np.float32), dtype)
     return dict(W0=W0, A=A, B=B, X=X, dY=dY, r=r, alpha=2.0 * r)
+
+
+def config4_adapter_sizes(r: int = 64):
+    """Element counts of the trainable A (r x K) and B (N x r) of config 4's
+    seven projections, in block order: 14 tensors, 4,997,120 parameters."""
+    out = []
+    for _, N, K in LLAMA_BLOCK:
+        out += [r * K, N * r]
+    return out
+
+
+def adamw_case(sizes, steps: int, seed: int = 11, zero_frac: float = 0.01):
+    """Seeded state and gradients for AdamW steps on tensors of the given sizes.
+
+    Per tensor i: a float32 master ~ N(0, 0.02^2) (the B and A scales of the
+    workloads), then for every step a float32 gradient ~ N(0, sigma_i^2) with
+    sigma_i cycling through 1e-3, 1e-2, 1e-1, 1 (so eps matters for some), of
+    which a fraction ``zero_frac`` of entries is set exactly to 0.  Moments
+    start at zero.  Returns (masters, grads) with grads[t][i] for step t + 1.
+    """
+    rng = np.random.default_rng(seed)
+    sig = (1e-3, 1e-2, 1e-1, 1.0)
+    masters = [rng.standard_normal(n, dtype=np.float32) * np.float32(0.02) for n in sizes]
+    grads = []
+    for _ in range(steps):
+        gs = []
+        for i, n in enumerate(sizes):
+            g = rng.standard_normal(n, dtype=np.float32) * np.float32(sig[i % 4])
+            g[rng.random(n) < zero_frac] = 0.0
+            gs.append(g)
+        grads.append(gs)
+    return masters, grads

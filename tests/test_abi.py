@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(lq.LIB_PATH),
 
 def test_exports_every_declared_symbol():
     declared = lq.declared_symbols()
-    assert len(declared) == 14
+    assert len(declared) == 15
     L = lq.lib()
     for name in declared:
         assert hasattr(L, name), name
@@ -127,6 +127,26 @@ def test_argument_errors_launch_nothing():
     w2 = _weight()
     w2.reserved = 1
     assert _fwd(w2) == -1
+
+
+def test_adamw_argument_errors_launch_nothing():
+    L = lq.lib()
+
+    def step(entries, gdt=lq.LQ_F32, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0, t=1, gs=1.0):
+        arr = (lq.LqAdamwTensor * max(1, len(entries)))(*entries)
+        return L.lq_adamw_step(arr, len(entries), gdt, lr, b1, b2, eps, wd, t, gs, None)
+
+    ok = lq.LqAdamwTensor(0x1000, 0x2000, 0x3000, 0x4000, None, 100)
+    assert step([]) == 0                                  # nothing to do
+    assert L.lq_adamw_step(None, 1, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 1.0, None) == -1
+    assert step([ok], t=0) == -1                          # steps count from 1
+    assert step([ok], gdt=7) == -1
+    assert step([ok], b1=1.0) == -1 and step([ok], b2=-0.1) == -1
+    assert step([ok], lr=float("nan")) == -1 and step([ok], eps=-1.0) == -1
+    assert step([ok], wd=-0.5) == -1 and step([ok], gs=float("inf")) == -1
+    assert step([ok, lq.LqAdamwTensor(0x1000, None, 0x3000, 0x4000, None, 5)]) == -1
+    assert "tensor 1" in lq.lq_last_error()
+    assert step([lq.LqAdamwTensor(0x1000, 0x2000, 0x3000, 0x4000, None, -1)]) == -1
 
 
 def test_timing_read_without_launches():
