@@ -44,6 +44,25 @@ Readings where the pages are silent or garbled
 6. Dequantization (the plain inverse): a' = fl32(fl32(q8) * fl32(c2 / 127)),
    w' = fl32(cb[code] * a'); the bf16 value is RNE(w').  Without double
    quantization a' = c1.
+
+Format variants the pages also describe
+---------------------------------------
+7. FP8 second-level constants ("... Mathematical Foundations ...", section
+   "2. Double Quantization (DQ)": the constants go to "8-bit integers or FP8";
+   "LoRA and QLoRA fine-tuning under the hood", section 3.2, and "Lesson 26"
+   call the 8-bit format FP8).  Reading: the same printed formula with "round"
+   taken as rounding to the FP8 grid, q = E4M3(fl32(fl32(c1/c2) * 127)), and
+   a' = fl32(e4m3(q) * fl32(c2 / 127)).  E4M3 is the OCP 8-bit format with 4
+   exponent bits (bias 7), 3 mantissa bits, subnormals m * 2^-9, largest
+   finite value 448 and no infinities; rounding is to the nearest value, ties
+   to the even code.  Values here lie in [0, 127], so no saturation occurs.
+8. Symmetric codebook without zero ("... Mathematical Foundations ...", the
+   q_i formula read literally): q_i = (Q(p_i) + Q(p_{i+1})) / 2 for
+   i = 0..15 with p_j = j / 16, the infinite end quantiles Q(0) and Q(1)
+   replaced by Q(delta) and Q(1 - delta) with the delta of reading 1, then
+   divided by the largest so the ends are -1 and +1.  The set is symmetric
+   (q_{15-i} = -q_i) and holds no zero.  Ties and zero blocks follow readings
+   2 and 3 (code 7, now the negative level nearest zero, times a' = 0).
 """
 from __future__ import annotations
 
@@ -56,10 +75,22 @@ DQ_BLOCK = 256
 F32 = np.float32
 
 
-def nf4_codebook() -> np.ndarray:
-    """The 16 NF4 levels as float32, ascending; index 7 is exactly 0."""
+DELTA = 0.5 * (1.0 / 32.0 + 1.0 / 30.0)
+CODEBOOKS = ("nf4", "nf4_symmetric")
+DQ_FORMATS = ("int8", "fp8")
+
+
+def nf4_codebook(variant: str = "nf4") -> np.ndarray:
+    """The 16 levels as float32, ascending.
+
+    "nf4": reading 1, index 7 is exactly 0.  "nf4_symmetric": reading 8.
+    """
+    if variant == "nf4_symmetric":
+        return nf4_codebook_symmetric()
+    if variant != "nf4":
+        raise ValueError(f"unknown codebook {variant!r}")
     q = statistics.NormalDist(0.0, 1.0).inv_cdf
-    delta = 0.5 * (1.0 / 32.0 + 1.0 / 30.0)
+    delta = DELTA
     top = 1.0 - delta
     # equally spaced probabilities above 1/2, excluding 1/2 itself
     pos = [q(0.5 + (top - 0.5) * j / 8.0) for j in range(1, 9)]
@@ -67,6 +98,45 @@ def nf4_codebook() -> np.ndarray:
     levels = sorted(neg + [0.0] + pos)
     scale = q(top)
     return np.array([v / scale for v in levels], dtype=np.float64).astype(F32)
+
+
+def nf4_codebook_symmetric() -> np.ndarray:
+    """Reading 8: averages of neighbouring normal quantiles at j/16, ends at
+    delta and 1 - delta, normalised to [-1, 1]; symmetric, no zero."""
+    q = statistics.NormalDist(0.0, 1.0).inv_cdf
+    p = [DELTA] + [j / 16.0 for j in range(1, 16)] + [1.0 - DELTA]
+    Q = [q(v) for v in p]
+    levels = [0.5 * (Q[i] + Q[i + 1]) for i in range(16)]
+    top = levels[15]
+    return np.array([v / top for v in levels], dtype=np.float64).astype(F32)
+
+
+def e4m3_value(code: int) -> float:
+    """Value of a non-negative E4M3 code 0..126 (0x7F is NaN and never used)."""
+    if not 0 <= code <= 126:
+        raise ValueError("code outside the non-negative finite E4M3 range")
+    e, m = code >> 3, code & 7
+    if e == 0:
+        return m * 2.0 ** -9
+    return (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """Nearest non-negative E4M3 code (ties to the even code), by search over
+    all 127 finite non-negative values.  Inputs in [0, 448]."""
+    vals = np.array([e4m3_value(c) for c in range(127)])
+    y = np.asarray(y, dtype=np.float64).ravel()
+    out = np.empty(y.size, dtype=np.uint8)
+    for i, v in enumerate(y):
+        d = np.abs(vals - v)
+        best = np.flatnonzero(d == d.min())
+        out[i] = best[0] if best.size == 1 else best[best % 2 == 0][0]
+    return out
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    vals = np.array([e4m3_value(c) for c in range(127)], dtype=np.float64)
+    return vals[np.asarray(codes, dtype=np.int64)].astype(F32)
 
 
 def nf4_thresholds(cb: np.ndarray | None = None) -> np.ndarray:
@@ -94,10 +164,11 @@ def block_absmax(w: np.ndarray, block: int = BLOCK) -> np.ndarray:
     return c1
 
 
-def quantize_codes(w: np.ndarray, c1: np.ndarray, block: int = BLOCK) -> np.ndarray:
+def quantize_codes(w: np.ndarray, c1: np.ndarray, block: int = BLOCK,
+                   codebook: str = "nf4") -> np.ndarray:
     """Per-element NF4 codes given each block's exact absmax."""
     w = np.asarray(w, dtype=F32).ravel()
-    thr = nf4_thresholds()
+    thr = nf4_thresholds(nf4_codebook(codebook))
     scale = np.repeat(c1, block)[: w.size]
     codes = np.full(w.size, 7, dtype=np.uint8)
     nz = scale != 0
@@ -122,8 +193,12 @@ def unpack_codes(packed: np.ndarray, n: int) -> np.ndarray:
     return out[:n]
 
 
-def double_quantize(c1: np.ndarray, group: int = DQ_BLOCK):
-    """Second level: c2 = max c1 per group, q8 = rint(fl32(fl32(c1/c2)*127))."""
+def double_quantize(c1: np.ndarray, group: int = DQ_BLOCK, fmt: str = "int8"):
+    """Second level: c2 = max c1 per group, y = fl32(fl32(c1/c2)*127), and
+    q8 = rint(y) ("int8", reading 5) or the E4M3 code nearest y ("fp8",
+    reading 7)."""
+    if fmt not in DQ_FORMATS:
+        raise ValueError(f"unknown second-level format {fmt!r}")
     c1 = np.asarray(c1, dtype=F32)
     ng = -(-c1.size // group)
     c2 = np.zeros(ng, dtype=F32)
@@ -133,20 +208,23 @@ def double_quantize(c1: np.ndarray, group: int = DQ_BLOCK):
     q8 = np.zeros(c1.size, dtype=np.uint8)
     nz = c2e != 0
     ratio = (c1[nz] / c2e[nz]).astype(F32)
-    q8[nz] = np.rint((ratio * F32(127.0)).astype(F32)).astype(np.uint8)
+    y = (ratio * F32(127.0)).astype(F32)
+    q8[nz] = np.rint(y).astype(np.uint8) if fmt == "int8" else e4m3_encode(y)
     return q8, c2
 
 
 class NF4Tensor:
     """Quantised tensor: packed codes, first-level constants, optional DQ."""
 
-    def __init__(self, n, packed, c1, q8=None, c2=None):
+    def __init__(self, n, packed, c1, q8=None, c2=None, dq_format="int8", codebook="nf4"):
         self.n = n
         self.packed = packed
         self.c1 = c1          # exact float32 absmax per block
         self.q8 = q8          # uint8 per block (double quantization)
         self.c2 = c2          # float32 per group of 256 blocks
         self.double_quant = q8 is not None
+        self.dq_format = dq_format if self.double_quant else None
+        self.codebook = codebook
 
     def nbytes(self) -> int:
         b = self.packed.size
@@ -155,16 +233,17 @@ class NF4Tensor:
         return b + 4 * self.c1.size
 
 
-def nf4_quantize(w: np.ndarray, double_quant: bool = True) -> NF4Tensor:
+def nf4_quantize(w: np.ndarray, double_quant: bool = True, dq_format: str = "int8",
+                 codebook: str = "nf4") -> NF4Tensor:
     """Quantise a float32 (or bf16-valued float32) tensor in flattened order."""
     w = np.asarray(w, dtype=F32).ravel()
     c1 = block_absmax(w)
-    codes = quantize_codes(w, c1)
+    codes = quantize_codes(w, c1, codebook=codebook)
     packed = pack_codes(codes)
     if double_quant:
-        q8, c2 = double_quantize(c1)
-        return NF4Tensor(w.size, packed, c1, q8, c2)
-    return NF4Tensor(w.size, packed, c1)
+        q8, c2 = double_quantize(c1, fmt=dq_format)
+        return NF4Tensor(w.size, packed, c1, q8, c2, dq_format, codebook)
+    return NF4Tensor(w.size, packed, c1, codebook=codebook)
 
 
 def block_scale(q: NF4Tensor) -> np.ndarray:
@@ -173,12 +252,13 @@ def block_scale(q: NF4Tensor) -> np.ndarray:
         return q.c1.astype(F32)
     step = (q.c2 / F32(127.0)).astype(F32)                    # fl32(c2/127)
     step_e = np.repeat(step, DQ_BLOCK)[: q.q8.size]
-    return (q.q8.astype(F32) * step_e).astype(F32)            # fl32(q8 * step)
+    qv = q.q8.astype(F32) if q.dq_format == "int8" else e4m3_decode(q.q8)
+    return (qv * step_e).astype(F32)                          # fl32(q * step)
 
 
 def nf4_dequantize_f32(q: NF4Tensor) -> np.ndarray:
     """w' = fl32(cb[code] * a') for every element (flattened)."""
-    cb = nf4_codebook()
+    cb = nf4_codebook(q.codebook)
     codes = unpack_codes(q.packed, q.n)
     a = np.repeat(block_scale(q), BLOCK)[: q.n]
     return (cb[codes] * a).astype(F32)

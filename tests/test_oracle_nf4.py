@@ -276,3 +276,106 @@ def test_storage_rates_match_pages():
     assert round(7e9 * dq / 8 / 1e9, 2) == g["qlora_7b_base_gb"]
     # 4096^2 weight: 8,388,608 code bytes + 262,144 q8 + 4,096 c2
     assert -(-n // 2) + n // 64 + 4 * (n // 64 // 256) == 8654848
+
+
+# ------------------------------------------------ format variants (E4M3, symmetric)
+
+def test_e4m3_values_fixed_by_the_format():
+    # OCP E4M3: bias 7, 3 mantissa bits, subnormals m * 2^-9, max finite 448
+    assert nf4.e4m3_value(0x00) == 0.0
+    assert nf4.e4m3_value(0x01) == 2.0 ** -9
+    assert nf4.e4m3_value(0x07) == 7 * 2.0 ** -9
+    assert nf4.e4m3_value(0x08) == 2.0 ** -6
+    assert nf4.e4m3_value(0x38) == 1.0
+    assert nf4.e4m3_value(0x7E) == 448.0
+    vals = [nf4.e4m3_value(c) for c in range(127)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))          # codes are ordered
+    with pytest.raises(ValueError):
+        nf4.e4m3_value(0x7F)
+
+
+def test_e4m3_matches_torch_float8():
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch has no float8_e4m3fn")
+    codes = torch.arange(127, dtype=torch.uint8)
+    tv = codes.view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    assert np.array_equal(nf4.e4m3_decode(np.arange(127)), tv)
+    rng = np.random.default_rng(4)
+    y = np.concatenate([rng.uniform(0, 127, 4000), rng.uniform(0, 0.05, 2000),
+                        (tv[:-1].astype(np.float64) + tv[1:]) / 2]).astype(F32)   # ties
+    y = y[y <= 127]
+    ours = nf4.e4m3_encode(y)
+    theirs = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, theirs)
+
+
+def test_fp8_double_quant_scale_bound():
+    rng = np.random.default_rng(6)
+    w = (rng.standard_normal(64 * 600) * 0.02).astype(F32)
+    q = nf4.nf4_quantize(w, double_quant=True, dq_format="fp8")
+    assert q.dq_format == "fp8" and q.q8.max() <= 126
+    a = nf4.block_scale(q).astype(np.float64)
+    c2 = np.repeat(q.c2, nf4.DQ_BLOCK)[: q.c1.size].astype(np.float64)
+    # the group maximum is 127 before rounding -> 128 = code 0x70
+    for g in range(q.c2.size):
+        grp = q.c1[g * 256:(g + 1) * 256]
+        assert q.q8[g * 256 + int(np.argmax(grp))] == 0x70
+    # E4M3 keeps 3 mantissa bits: relative error at most 2^-4 in the normal
+    # range (y >= 2^-6), absolute 2^-10 * c2/127 below it; plus float32 steps
+    y = q.c1.astype(np.float64) / c2 * 127
+    bound = np.where(y >= 2 ** -6, 2.0 ** -4 * q.c1, 2.0 ** -10 * c2 / 127) + 1e-6 * q.c1
+    assert np.all(np.abs(a - q.c1) <= bound)
+    # same bytes as the integer format
+    assert q.nbytes() == nf4.nf4_quantize(w).nbytes()
+
+
+def test_fp8_and_int8_agree_where_the_integer_is_representable():
+    # integers 0..16 are exact in E4M3, so small ratios give the same code value
+    c1 = np.array([127, 16, 9, 3, 0.5, 0], dtype=F32)
+    qi, c2i = nf4.double_quantize(c1, fmt="int8")
+    qf, c2f = nf4.double_quantize(c1, fmt="fp8")
+    assert np.array_equal(c2i, c2f)
+    dec = nf4.e4m3_decode(qf)
+    assert list(dec[1:]) == [16.0, 9.0, 3.0, 0.5, 0.0]
+    assert list(qi[1:]) == [16, 9, 3, 0, 0]     # 0.5 rounds half to even -> 0
+    assert dec[0] == 128.0 and qi[0] == 127
+
+
+def test_symmetric_codebook_properties():
+    cb = nf4.nf4_codebook("nf4_symmetric")
+    assert cb.dtype == F32 and cb.size == 16
+    assert cb[0] == -1.0 and cb[15] == 1.0
+    assert np.all(np.diff(cb) > 0) and not np.any(cb == 0)
+    assert np.array_equal(cb[::-1], -cb)                       # exact mirror
+    t = nf4.nf4_thresholds(cb)
+    assert t[7] == 0.0
+
+
+def test_symmetric_codebook_matches_independent_inverse_cdf():
+    sp = pytest.importorskip("scipy.special")
+    delta = 0.5 * (1 / 32 + 1 / 30)
+    p = [delta] + [j / 16 for j in range(1, 16)] + [1 - delta]
+    Q = [float(sp.ndtri(v)) for v in p]
+    lv = np.array([(Q[i] + Q[i + 1]) / 2 for i in range(16)])
+    want = (lv / lv[15]).astype(F32)
+    got = nf4.nf4_codebook("nf4_symmetric")
+    assert np.max(np.abs(got.view(np.int32) - want.view(np.int32))) <= 1   # float32 steps
+
+
+def test_symmetric_codes_brute_force_nearest():
+    rng = np.random.default_rng(8)
+    w = rng.standard_normal(64 * 50).astype(F32)
+    q = nf4.nf4_quantize(w, double_quant=False, codebook="nf4_symmetric")
+    codes = nf4.unpack_codes(q.packed, q.n)
+    cb = nf4.nf4_codebook("nf4_symmetric").astype(np.float64)
+    x = (w / np.repeat(q.c1, 64)).astype(F32).astype(np.float64)
+    d = np.abs(x[:, None] - cb[None, :])
+    srt = np.sort(d, axis=1)
+    clear = (srt[:, 1] - srt[:, 0]) > 1e-6
+    assert np.array_equal(codes[clear], d.argmin(axis=1)[clear])
+    # each block's absmax element lands on an end level
+    blk = np.abs(w).reshape(-1, 64).argmax(axis=1) + 64 * np.arange(50)
+    assert set(codes[blk].tolist()) <= {0, 15}
+    deq = nf4.nf4_dequantize_f32(q)
+    assert np.all(np.abs(deq - w) <= np.repeat(q.c1, 64) * 0.5 * np.diff(cb).max() + 1e-7)
