@@ -61,6 +61,33 @@ typedef enum lq_weight_kind {
 #define LQ_NF4_BLOCK 64
 #define LQ_NF4_DQ_BLOCK 256
 
+/* First-level constant storage (lq_weight.double_quant and the quantiser's
+ * double_quant argument):
+ *   LQ_DQ_NONE  float32 absmax per block (single-level NF4, 4.5 bits/param;
+ *               [FT] "Quantizing the frozen weights")
+ *   LQ_DQ_INT8  8-bit integer q = rint(fl32(fl32(c1/c2) * 127)) per block plus
+ *               a float32 c2 per 256 blocks ([MF] "2. Double Quantization")
+ *   LQ_DQ_FP8   the same bytes holding the E4M3 code nearest (ties to even)
+ *               to fl32(fl32(c1/c2) * 127) ([MF] "2. Double Quantization": 8-bit
+ *               integers or FP8; [UH] 3.2).  E4M3: 4 exponent bits, bias 7, 3
+ *               mantissa bits, subnormals m * 2^-9, max 448.
+ * Reconstruction: a' = c1 (NONE), fl32(q * fl32(c2/127)) (INT8),
+ * fl32(e4m3(q) * fl32(c2/127)) (FP8). */
+#define LQ_DQ_NONE 0
+#define LQ_DQ_INT8 1
+#define LQ_DQ_FP8 2
+
+/* Codebooks (lq_weight.codebook and the codec's codebook argument):
+ *   LQ_CB_NF4            the default: 7 negative levels, an exact 0 and 8
+ *                        positive ones (see lq_nf4_codebook)
+ *   LQ_CB_NF4_SYMMETRIC  the printed midpoint formula read literally: level
+ *                        i = (Q(i/16) + Q((i+1)/16)) / 2 with the infinite end
+ *                        quantiles taken at delta and 1 - delta, normalised to
+ *                        [-1, 1]; symmetric, no zero ([MF] "1. 4-bit
+ *                        NormalFloat (NF4) Quantization"). */
+#define LQ_CB_NF4 0
+#define LQ_CB_NF4_SYMMETRIC 1
+
 /*
  * The frozen base weight W0, N x K, as seen by every LoRA entry point.
  *
@@ -69,16 +96,16 @@ typedef enum lq_weight_kind {
  *   codes     ceil(N*K/2) bytes, element 2j in the low nibble of byte j and
  *             element 2j+1 in the high nibble (an odd count leaves the last
  *             high nibble 0);
- *   q8        ceil(N*K/64) bytes (double_quant = 1): 8-bit first-level
- *             constants, 0..127;
- *   c2        ceil(ceil(N*K/64)/256) floats (double_quant = 1): second-level
+ *   q8        ceil(N*K/64) bytes (LQ_DQ_INT8: integers 0..127; LQ_DQ_FP8:
+ *             E4M3 codes 0..126): 8-bit first-level constants;
+ *   c2        ceil(ceil(N*K/64)/256) floats (LQ_DQ_INT8 / LQ_DQ_FP8):
+ *             second-level constants;
+ *   absmax    ceil(N*K/64) floats (LQ_DQ_NONE): float32 first-level
  *             constants;
- *   absmax    ceil(N*K/64) floats (double_quant = 0): float32 first-level
- *             constants;
- *   the dequantised element is fl32(cb[code] * a') with a' =
- *   fl32(q8 * fl32(c2/127)) (or a' = absmax), fed to bf16 arithmetic as its
- *   round-to-nearest-even bf16 value ([MF] "1. 4-bit NormalFloat (NF4)
- *   Quantization": dequantised to BF16 right before the multiply).
+ *   the dequantised element is fl32(cb[code] * a') with a' as listed under
+ *   LQ_DQ_*, fed to bf16 arithmetic as its round-to-nearest-even bf16 value
+ *   ([MF] "1. 4-bit NormalFloat (NF4) Quantization": dequantised to BF16
+ *   right before the multiply); cb is the weight's codebook (LQ_CB_*).
  * ``dtype`` for NF4 is the compute dtype the caller intends (checked against
  * the call's dtype).  All pointers are device pointers owned by the caller.
  */
@@ -92,21 +119,22 @@ typedef struct lq_weight {
   const uint8_t* q8;
   const float* c2;
   const float* absmax;
-  int32_t double_quant;      /* 1: q8 + c2, 0: absmax                            */
-  int32_t reserved;          /* must be 0                                       */
+  int32_t double_quant;      /* LQ_DQ_NONE / LQ_DQ_INT8 / LQ_DQ_FP8             */
+  int32_t codebook;          /* LQ_CB_NF4 / LQ_CB_NF4_SYMMETRIC                 */
 } lq_weight;
 
 /* --------------------------------------------------------------- NF4 codec */
 
 /*
- * Host copy of the 16 NF4 levels ([MF] "1. 4-bit NormalFloat (NF4)
- * Quantization": normal quantiles normalised to [-1, 1]).  Built on the host
- * in double precision as the asymmetric quantile set with an exact zero
- * (8 positive levels, 7 negative, 0; outer probability 1 - (1/32 + 1/30)/2),
+ * Host copy of the 16 levels of ``codebook`` ([MF] "1. 4-bit NormalFloat
+ * (NF4) Quantization": normal quantiles normalised to [-1, 1]), ascending.
+ * LQ_CB_NF4 is built on the host in double precision as the asymmetric
+ * quantile set with an exact zero (8 positive levels, 7 negative, 0; outer
+ * probability 1 - (1/32 + 1/30)/2), LQ_CB_NF4_SYMMETRIC as described above,
  * then rounded to float32.  ``out`` is host memory for 16 floats.
- * Returns LQ_OK or LQ_ERR_INVALID_ARG (null out).
+ * Returns LQ_OK or LQ_ERR_INVALID_ARG (null out, unknown codebook).
  */
-int lq_nf4_codebook(float* out);
+int lq_nf4_codebook(int32_t codebook, float* out);
 
 /*
  * Quantise n elements of W (flattened, row-major) to NF4
@@ -116,25 +144,28 @@ int lq_nf4_codebook(float* out);
  *            exactly to float32)
  *   blocks of 64 consecutive elements (last may be partial): c1 = max|w|,
  *   x = fl32(w / c1), code = number of the 15 float32 midpoints between
- *   neighbouring levels that are strictly below x (c1 = 0: code 7).
- *   double_quant = 1: groups of 256 blocks, c2 = max c1 (float32, written to
- *   c2[ceil(nb/256)]), q8 = rint(fl32(fl32(c1/c2) * 127)) (ties to even,
- *   c2 = 0 gives 0) written to q8[nb]; ``absmax`` may be NULL.
- *   double_quant = 0: c1 written to absmax[nb]; q8 and c2 may be NULL.
+ *   neighbouring levels of ``codebook`` that are strictly below x (c1 = 0:
+ *   code 7).
+ *   double_quant = LQ_DQ_INT8 or LQ_DQ_FP8: groups of 256 blocks, c2 = max c1
+ *   (float32, written to c2[ceil(nb/256)]), y = fl32(fl32(c1/c2) * 127), and
+ *   q8 = rint(y) (ties to even) or the E4M3 code nearest y (ties to the even
+ *   code); c2 = 0 gives 0; written to q8[nb]; ``absmax`` may be NULL.
+ *   double_quant = LQ_DQ_NONE: c1 written to absmax[nb]; q8 and c2 may be NULL.
  *   codes    device, ceil(n/2) bytes (packing as in lq_weight).
  * Results are bit-exact functions of the input.  n >= 1.
  */
 int lq_nf4_quantize(const void* W, lq_dtype wdt, int64_t n, int32_t double_quant,
-                    uint8_t* codes, uint8_t* q8, float* c2, float* absmax,
+                    int32_t codebook, uint8_t* codes, uint8_t* q8, float* c2, float* absmax,
                     hipStream_t stream);
 
 /*
- * Dequantise n NF4 elements (layout as in lq_weight) to ``out``: n elements
- * of odt, fl32(cb[code] * a') for LQ_F32, its RNE bf16 for LQ_BF16.
- * Bit-exact.  The inverse of lq_nf4_quantize up to the quantisation error.
+ * Dequantise n NF4 elements (layout as in lq_weight, format double_quant and
+ * codebook as given to lq_nf4_quantize) to ``out``: n elements of odt,
+ * fl32(cb[code] * a') for LQ_F32, its RNE bf16 for LQ_BF16.  Bit-exact.  The
+ * inverse of lq_nf4_quantize up to the quantisation error.
  */
 int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
-                      const float* absmax, int32_t double_quant, int64_t n,
+                      const float* absmax, int32_t double_quant, int32_t codebook, int64_t n,
                       void* out, lq_dtype odt, hipStream_t stream);
 
 /* ------------------------------------------------------- adapted linear */

@@ -47,7 +47,10 @@ int check_weight(const lq_weight* w, lq_dtype dt) {
   REQUIRE(w != nullptr, LQ_ERR_INVALID_ARG, "W0 descriptor is NULL");
   REQUIRE(w->N > 0 && w->K > 0, LQ_ERR_INVALID_ARG, "W0 has N=%lld K=%lld", (long long)w->N,
           (long long)w->K);
-  REQUIRE(w->reserved == 0, LQ_ERR_INVALID_ARG, "W0.reserved must be 0");
+  REQUIRE(w->codebook == LQ_CB_NF4 || w->codebook == LQ_CB_NF4_SYMMETRIC, LQ_ERR_INVALID_ARG,
+          "unknown W0 codebook %d", (int)w->codebook);
+  REQUIRE(w->double_quant >= LQ_DQ_NONE && w->double_quant <= LQ_DQ_FP8, LQ_ERR_INVALID_ARG,
+          "unknown W0 constant format %d", (int)w->double_quant);
   REQUIRE(w->dtype == dt, LQ_ERR_INVALID_ARG, "W0 dtype %d does not match call dtype %d",
           (int)w->dtype, (int)dt);
   if (w->kind == LQ_WEIGHT_DENSE) {
@@ -155,9 +158,11 @@ extern "C" {
 
 const char* lq_last_error(void) { return g_err; }
 
-int lq_nf4_codebook(float* out) {
+int lq_nf4_codebook(int32_t codebook, float* out) {
   REQUIRE(out != nullptr, LQ_ERR_INVALID_ARG, "out is NULL");
-  std::memcpy(out, nf4_table().cb, sizeof(float) * 16);
+  REQUIRE(codebook == LQ_CB_NF4 || codebook == LQ_CB_NF4_SYMMETRIC, LQ_ERR_INVALID_ARG,
+          "unknown codebook %d", (int)codebook);
+  std::memcpy(out, nf4_table(codebook).cb, sizeof(float) * 16);
   return LQ_OK;
 }
 
@@ -239,31 +244,41 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
   }
 }
 
-int lq_nf4_quantize(const void* W, lq_dtype wdt, int64_t n, int32_t double_quant, uint8_t* codes,
-                    uint8_t* q8, float* c2, float* absmax, hipStream_t stream) {
+int lq_nf4_quantize(const void* W, lq_dtype wdt, int64_t n, int32_t double_quant,
+                    int32_t codebook, uint8_t* codes, uint8_t* q8, float* c2, float* absmax,
+                    hipStream_t stream) {
   REQUIRE(W != nullptr && codes != nullptr, LQ_ERR_INVALID_ARG, "W or codes is NULL");
   REQUIRE(n >= 1, LQ_ERR_INVALID_ARG, "n = %lld", (long long)n);
   REQUIRE(wdt == LQ_F32 || wdt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad dtype %d", (int)wdt);
+  REQUIRE(double_quant >= LQ_DQ_NONE && double_quant <= LQ_DQ_FP8, LQ_ERR_INVALID_ARG,
+          "unknown constant format %d", (int)double_quant);
+  REQUIRE(codebook == LQ_CB_NF4 || codebook == LQ_CB_NF4_SYMMETRIC, LQ_ERR_INVALID_ARG,
+          "unknown codebook %d", (int)codebook);
   if (double_quant) {
     REQUIRE(q8 && c2, LQ_ERR_INVALID_ARG, "q8 or c2 is NULL");
   } else {
     REQUIRE(absmax != nullptr, LQ_ERR_INVALID_ARG, "absmax is NULL");
   }
-  return launch_nf4_quantize(W, wdt, n, double_quant, codes, q8, c2, absmax, stream);
+  return launch_nf4_quantize(W, wdt, n, double_quant, codebook, codes, q8, c2, absmax, stream);
 }
 
 int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
-                      const float* absmax, int32_t double_quant, int64_t n, void* out,
-                      lq_dtype odt, hipStream_t stream) {
+                      const float* absmax, int32_t double_quant, int32_t codebook, int64_t n,
+                      void* out, lq_dtype odt, hipStream_t stream) {
   REQUIRE(codes != nullptr && out != nullptr, LQ_ERR_INVALID_ARG, "codes or out is NULL");
   REQUIRE(n >= 1, LQ_ERR_INVALID_ARG, "n = %lld", (long long)n);
   REQUIRE(odt == LQ_F32 || odt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad dtype %d", (int)odt);
+  REQUIRE(double_quant >= LQ_DQ_NONE && double_quant <= LQ_DQ_FP8, LQ_ERR_INVALID_ARG,
+          "unknown constant format %d", (int)double_quant);
+  REQUIRE(codebook == LQ_CB_NF4 || codebook == LQ_CB_NF4_SYMMETRIC, LQ_ERR_INVALID_ARG,
+          "unknown codebook %d", (int)codebook);
   if (double_quant) {
     REQUIRE(q8 && c2, LQ_ERR_INVALID_ARG, "q8 or c2 is NULL");
   } else {
     REQUIRE(absmax != nullptr, LQ_ERR_INVALID_ARG, "absmax is NULL");
   }
-  return launch_nf4_dequantize(codes, q8, c2, absmax, double_quant, n, out, odt, stream);
+  return launch_nf4_dequantize(codes, q8, c2, absmax, double_quant, codebook, n, out, odt,
+                               stream);
 }
 
 int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, const void* B,

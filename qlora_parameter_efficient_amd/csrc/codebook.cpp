@@ -10,6 +10,12 @@
 // by the quantile at p_top = 1 - (1/32 + 1/30) / 2 (half of a bin of the
 // 16- and 15-bin grids the two sides use).
 //
+// The symmetric variant reads the midpoint formula literally: level i is the
+// mean of the normal quantiles at i/16 and (i+1)/16 for i = 0..15, with the
+// infinite end quantiles taken at probabilities delta and 1 - delta (the same
+// half-bin delta), divided by the largest level; it is symmetric and holds no
+// zero.  Its negative half is the exact mirror of the positive half.
+//
 // The inverse normal CDF is computed from the C library's erfc: bracketing
 // bisection followed by Newton steps, which converges to double precision.
 #include <cmath>
@@ -36,10 +42,37 @@ double normal_quantile(double p) {
   return x;
 }
 
+constexpr double kDelta = 0.5 * (1.0 / 32.0 + 1.0 / 30.0);
+
+void fill_thresholds(NF4Table& t) {
+  for (int i = 0; i < 15; ++i) {
+    float s = t.cb[i] + t.cb[i + 1];  // float32 sum, then exact halving
+    t.thr[i] = s * 0.5f;
+  }
+}
+
+NF4Table build_symmetric_table() {
+  NF4Table t;
+  std::memset(&t, 0, sizeof(t));
+  // quantiles at 8/16 .. 15/16 and 1 - delta; Q(1/2) = 0 exactly
+  double q[9];
+  q[0] = 0.0;
+  for (int j = 9; j <= 15; ++j) q[j - 8] = normal_quantile(j / 16.0);
+  q[8] = normal_quantile(1.0 - kDelta);
+  double lv[8];  // levels 8..15
+  for (int i = 0; i < 8; ++i) lv[i] = 0.5 * (q[i] + q[i + 1]);
+  for (int i = 0; i < 8; ++i) {
+    t.cb[8 + i] = (float)(lv[i] / lv[7]);
+    t.cb[7 - i] = -t.cb[8 + i];
+  }
+  fill_thresholds(t);
+  return t;
+}
+
 NF4Table build_table() {
   NF4Table t;
   std::memset(&t, 0, sizeof(t));
-  const double p_top = 1.0 - 0.5 * (1.0 / 32.0 + 1.0 / 30.0);
+  const double p_top = 1.0 - kDelta;
   const double z_top = normal_quantile(p_top);
   double lv[16];
   // ascending: 7 negatives (most negative first), zero, 8 positives
@@ -48,20 +81,20 @@ NF4Table build_table() {
   for (int j = 1; j <= 8; ++j) lv[7 + j] = normal_quantile(0.5 + (p_top - 0.5) * j / 8.0);
   for (int i = 0; i < 16; ++i) t.cb[i] = (float)(lv[i] / z_top);
   t.cb[7] = 0.0f;
-  for (int i = 0; i < 15; ++i) {
-    float s = t.cb[i] + t.cb[i + 1];  // float32 sum, then exact halving
-    t.thr[i] = s * 0.5f;
-  }
+  fill_thresholds(t);
   return t;
 }
 
 }  // namespace
 
-const NF4Table& nf4_table() {
+const NF4Table& nf4_table(int32_t codebook) {
   static std::once_flag once;
-  static NF4Table table;
-  std::call_once(once, [] { table = build_table(); });
-  return table;
+  static NF4Table tables[2];
+  std::call_once(once, [] {
+    tables[LQ_CB_NF4] = build_table();
+    tables[LQ_CB_NF4_SYMMETRIC] = build_symmetric_table();
+  });
+  return tables[codebook == LQ_CB_NF4_SYMMETRIC ? LQ_CB_NF4_SYMMETRIC : LQ_CB_NF4];
 }
 
 }  // namespace lq

@@ -16,7 +16,9 @@ struct NF4Table {
   float pad;
 };
 
-const NF4Table& nf4_table();  // host: built on first use, immutable afterwards
+// host: built on first use, immutable afterwards; LQ_CB_NF4 or
+// LQ_CB_NF4_SYMMETRIC
+const NF4Table& nf4_table(int32_t codebook);
 
 // Multi-adapter rank layout, passed to the kernels by value.  Adapter a owns
 // the concatenated rank columns roff[a] .. roff[a+1]-1 and the scale scale[a]
@@ -71,6 +73,28 @@ __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w 
 
 // Second-level step fl32(c2 / 127) with IEEE division (correctly rounded).
 __device__ __forceinline__ float dq_step(float c2) { return c2 / 127.0f; }
+
+// Value of a non-negative E4M3 code q (0..126): 4 exponent bits with bias 7,
+// 3 mantissa bits, subnormals m * 2^-9.  Exact: a small integer times a power
+// of two.
+__device__ __forceinline__ float e4m3_value(uint32_t q) {
+  const uint32_t e = (q >> 3) & 15u, m = q & 7u;
+  const uint32_t mant = e ? (m | 8u) : m;              // (8 + m) or m
+  const uint32_t ex = (e ? e : 1u) + 127u - 10u;       // 2^(e - 10), subnormal 2^-9
+  return (float)mant * __uint_as_float(ex << 23);
+}
+
+// The value the 8-bit second-level constant stands for: the integer itself
+// (LQ_DQ_INT8) or the E4M3 value of the byte (LQ_DQ_FP8).
+template <bool FP8>
+__device__ __forceinline__ float dq_value(uint32_t q) {
+  return FP8 ? e4m3_value(q) : (float)q;
+}
+
+// The same with the format a uniform argument: LQ_DQ_INT8 or LQ_DQ_FP8.
+__device__ __forceinline__ float dq_q_rt(int32_t dq, uint32_t q) {
+  return dq == LQ_DQ_FP8 ? dq_value<true>(q) : dq_value<false>(q);
+}
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

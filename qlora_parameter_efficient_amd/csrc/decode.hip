@@ -210,7 +210,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) acc[i] = mfma16(wraw[i][d], sel4(ok[i], xf[i][d]), acc[i]);
       } else {
-        const float a = WK == kNF4DQ ? (float)sq[i] * dq_step(sc2[i]) : __uint_as_float(sq[i]);
+        const float a =
+            WK == kNF4DQ ? dq_q_rt(p.W.dq, sq[i]) * dq_step(sc2[i]) : __uint_as_float(sq[i]);
 #pragma unroll
         for (int d = 0; d < 4; ++d)
           acc[i] = mfma16(deq8(wraw[i][0][d], a, lut), sel4(ok[i], xf[i][d]), acc[i]);
@@ -382,7 +383,7 @@ int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, cons
   p.r = (int32_t)r;
   p.s = s;
   p.Y = (uint16_t*)Y;
-  p.tab = nf4_table();
+  p.tab = nf4_table(W.codebook);
   const dim3 grid((unsigned)(W.N / 16)), block(64 * kGemvWaves);
   switch (weight_format(W)) {
     case kDense:

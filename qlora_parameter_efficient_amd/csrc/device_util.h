@@ -29,12 +29,15 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f3
 
 // Weight formats, fixed at compile time: dense bf16, NF4 with 8-bit double
 // quantised constants, NF4 with float32 absmax.
+// kNF4DQ covers both 8-bit constant formats (integer or E4M3); which one is
+// a uniform kernel argument, read where a block scale is formed.
 constexpr int kDense = 0, kNF4DQ = 1, kNF4 = 2;
 
 inline int weight_format(const lq_weight& w) {
   if (w.kind == LQ_WEIGHT_DENSE) return kDense;
   return w.double_quant ? kNF4DQ : kNF4;
 }
+
 
 __device__ __forceinline__ u32x4 sel4(bool ok, const u32x4& v) {
   return ok ? v : u32x4{0u, 0u, 0u, 0u};
@@ -89,7 +92,8 @@ __device__ __forceinline__ ScaleRaw load_scale(const WeightArgs& w, int64_t blk)
   return s;
 }
 
-// Block scale a' = fl32(q8 * fl32(c2 / 127)) (or the float32 absmax), with the
+// Block scale a' = fl32(q * fl32(c2 / 127)) (or the float32 absmax), q the
+// integer or E4M3 value of the 8-bit constant, with the
 // second-level step cached while consecutive blocks stay in one group.
 struct ScaleCache {
   int64_t g;
@@ -104,7 +108,7 @@ struct ScaleCache {
       g = s.g;
       step = dq_step(s.c2);
     }
-    return (float)s.q * step;
+    return dq_q_rt(w.dq, s.q) * step;
   }
   __device__ __forceinline__ float scale(const WeightArgs& w, int64_t blk) {
     return finish(w, load_scale(w, blk));
@@ -140,7 +144,7 @@ __device__ __forceinline__ ScaleRef load_scale_ref(const WeightArgs& w, int64_t 
 
 __device__ __forceinline__ float scale_from(const WeightArgs& w, const ScaleRef& s,
                                             const float* tab) {
-  return w.dq ? (float)s.q * tab[s.gi] : __uint_as_float(s.q);
+  return w.dq ? dq_q_rt(w.dq, s.q) * tab[s.gi] : __uint_as_float(s.q);
 }
 
 // lut[b] = (cb[b & 15], cb[b >> 4]): both levels of one code byte.  Built by a

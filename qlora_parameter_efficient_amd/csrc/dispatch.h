@@ -7,11 +7,11 @@
 namespace lq {
 
 int launch_nf4_quantize(const void* W, lq_dtype wdt, int64_t n, int32_t double_quant,
-                        uint8_t* codes, uint8_t* q8, float* c2, float* absmax,
+                        int32_t codebook, uint8_t* codes, uint8_t* q8, float* c2, float* absmax,
                         hipStream_t stream);
 int launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
-                          const float* absmax, int32_t double_quant, int64_t n, void* out,
-                          lq_dtype odt, hipStream_t stream);
+                          const float* absmax, int32_t double_quant, int32_t codebook, int64_t n,
+                          void* out, lq_dtype odt, hipStream_t stream);
 int launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 
 int f32_lora_fwd(const float* X, int64_t M, const lq_weight& W, const float* A, const float* B,

@@ -616,8 +616,8 @@ int launch_g256(bool tr, const void* P, const void* Q, const float* V, const voi
 // the NF4 weight dequantised to bf16 into the workspace at q (when the prep
 // kernel cannot take the shrink as well)
 int bf16_weight(const lq_weight& W, void* q, hipStream_t st) {
-  return launch_nf4_dequantize(W.codes, W.q8, W.c2, W.absmax, W.double_quant, W.N * W.K, q,
-                               LQ_BF16, st);
+  return launch_nf4_dequantize(W.codes, W.q8, W.c2, W.absmax, W.double_quant, W.codebook,
+                               W.N * W.K, q, LQ_BF16, st);
 }
 
 }  // namespace

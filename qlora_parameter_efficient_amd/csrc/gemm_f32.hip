@@ -8,6 +8,7 @@
 // Dynamics and Backpropagation Mechanics" for dA, dB, dx; section
 // "1. Static Weight Merging" for W0 + (alpha/r) B A.
 #include "common.h"
+#include "dispatch.h"
 
 namespace lq {
 namespace {
@@ -22,6 +23,7 @@ struct Acc {
   int64_t rs, cs;
   int32_t kind;
   int32_t double_quant;
+  int32_t codebook;
 };
 
 __device__ __forceinline__ float acc_load(const Acc& m, int64_t a, int64_t b, const float* cbs) {
@@ -31,7 +33,8 @@ __device__ __forceinline__ float acc_load(const Acc& m, int64_t a, int64_t b, co
   const uint32_t code = (e & 1) ? (byte >> 4) : (byte & 15u);
   const int64_t blk = e / LQ_NF4_BLOCK;
   float s;
-  if (m.double_quant) s = (float)m.q8[blk] * dq_step(m.c2[blk / LQ_NF4_DQ_BLOCK]);
+  if (m.double_quant)
+    s = dq_q_rt(m.double_quant, m.q8[blk]) * dq_step(m.c2[blk / LQ_NF4_DQ_BLOCK]);
   else s = m.absmax[blk];
   return cbs[code] * s;
 }
@@ -86,6 +89,7 @@ Acc weight_acc(const lq_weight& w, int64_t rs, int64_t cs) {
   a.c2 = w.c2;
   a.absmax = w.absmax;
   a.double_quant = w.double_quant;
+  a.codebook = w.codebook;
   a.rs = rs;
   a.cs = cs;
   a.kind = 1;
@@ -97,7 +101,7 @@ int gemm(const Acc& P, const Acc& Q, float* C, int64_t ldc, int64_t I, int64_t J
   if (I == 0 || J == 0) return LQ_OK;
   dim3 grid((unsigned)cdiv(J, TS), (unsigned)cdiv(I, TS));
   hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(TS * TS), 0, stream, P, Q, C, ldc, I, J, Kd, alpha,
-                     accumulate, nf4_table());
+                     accumulate, nf4_table(P.kind ? P.codebook : Q.codebook));
   return hip_fail(hipGetLastError(), "gemm_f32 launch");
 }
 
@@ -155,9 +159,6 @@ int f32_lora_bwd(const float* dY, const float* X, int64_t M, const lq_weight& W,
   return gemm(dense(dY, 1, N), dense(T, r, 1), dB, r, N, r, M, s, accumulate, st);
 }
 
-int launch_nf4_dequantize(const uint8_t*, const uint8_t*, const float*, const float*, int32_t,
-                          int64_t, void*, lq_dtype, hipStream_t);
-
 int f32_lora_merge(const lq_weight& W, const float* A, const float* B, int64_t r, float s,
                    float* Wout, hipStream_t st) {
   const int64_t N = W.N, K = W.K;
@@ -166,8 +167,8 @@ int f32_lora_merge(const lq_weight& W, const float* A, const float* B, int64_t r
     hipError_t e = hipMemcpyAsync(Wout, W.dense, sizeof(float) * N * K, hipMemcpyDeviceToDevice, st);
     if ((rc = hip_fail(e, "merge copy"))) return rc;
   } else {
-    if ((rc = launch_nf4_dequantize(W.codes, W.q8, W.c2, W.absmax, W.double_quant, N * K, Wout,
-                                    LQ_F32, st)))
+    if ((rc = launch_nf4_dequantize(W.codes, W.q8, W.c2, W.absmax, W.double_quant, W.codebook,
+                                    N * K, Wout, LQ_F32, st)))
       return rc;
   }
   return gemm(dense(B, r, 1), dense(A, K, 1), Wout, K, N, K, r, s, 1, st);

@@ -290,8 +290,8 @@ __device__ __forceinline__ u32x4 pin(u32x4 v) {
 }
 
 template <int WK>
-__device__ __forceinline__ float raw_scale_value(const RawScale& r, const float* tab) {
-  if (WK == kNF4DQ) return (float)pin(r.q) * tab[r.gi];
+__device__ __forceinline__ float raw_scale_value(const RawScale& r, const float* tab, int32_t dq) {
+  if (WK == kNF4DQ) return dq_q_rt(dq, pin(r.q)) * tab[r.gi];
   return __uint_as_float(pin(r.q));
 }
 
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
   frag_load<MS>(x1, xbase + 2 * ((int64_t)(KT > 1 ? 1 : 0) * kBK), xo);
   __syncthreads();  // level and step tables ready
   {
-    const float a = WK != kDense ? raw_scale_value<WK>(s0.sc, stab) : 0.0f;
+    const float a = WK != kDense ? raw_scale_value<WK>(s0.sc, stab, p.W.dq) : 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       fwd_stage_finish<WK, JT>(s0, fwd_stage_fetch<WK, JT>(s0, lut, q), wt[0], a, q);
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdParams p) {
     const int64_t k2 = (int64_t)(kt + 2 < KT ? kt + 2 : KT - 1) * kBK;
     fwd_stage_load<WK, JT>(snxt, p, o, k2, g_lo);
     frag_load<MS>(xnxt, xbase + 2 * k2, xo);
-    const float a = WK != kDense ? raw_scale_value<WK>(scur.sc, stab) : 0.0f;
+    const float a = WK != kDense ? raw_scale_value<WK>(scur.sc, stab, p.W.dq) : 0.0f;
     const int b = kt & 1;
     uint16_t* wn = wt[b ^ 1];
     LutFetch lf[2];
@@ -716,8 +716,8 @@ __device__ __forceinline__ void dx_stage_load(DxStage<WK, RP>& st, const BwdPara
 }
 
 template <int WK, int RP>
-__device__ __forceinline__ float dx_scale(const DxStage<WK, RP>& st) {
-  if (WK == kNF4DQ) return (float)pin(st.q) * dq_step(pin(st.c2));
+__device__ __forceinline__ float dx_scale(const DxStage<WK, RP>& st, int32_t dq) {
+  if (WK == kNF4DQ) return dq_q_rt(dq, pin(st.q)) * dq_step(pin(st.c2));
   return __uint_as_float(pin(st.q));
 }
 
@@ -802,7 +802,7 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(BwdParams p) {
   act_load<MS>(g0, gbase, go);
   __syncthreads();  // level table ready
   {
-    const float a = WK != kDense ? dx_scale<WK, RP>(s0) : 0.0f;
+    const float a = WK != kDense ? dx_scale<WK, RP>(s0, p.W.dq) : 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       dx_stage_part<WK, RP>(s0, o, wt[0], lut, a, p.r, q);
@@ -821,7 +821,7 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(BwdParams p) {
     const int64_t n2 = (int64_t)(rt + 2 < RT ? rt + 2 : RT - 1) * kBK;
     dx_stage_load<WK, RP, BV>(snxt, p, o, n2);
     act_load<MS>(gnxt, gbase + 2 * n2, go);
-    const float a = WK != kDense ? dx_scale<WK, RP>(scur) : 0.0f;
+    const float a = WK != kDense ? dx_scale<WK, RP>(scur, p.W.dq) : 0.0f;
     const int b = rt & 1;
     uint16_t* wn = wt[b ^ 1];
     uint16_t* gn = gt[b ^ 1];
@@ -1059,7 +1059,7 @@ int bf16_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const 
   p.s = s;
   p.Y = (uint16_t*)Y;
   p.T_out = T_out;
-  p.tab = nf4_table();
+  p.tab = nf4_table(W.codebook);
   return fwd_dispatch<false>(p, W, (int)r, st);
 }
 
@@ -1076,7 +1076,7 @@ int bf16_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const 
   p.s = s;
   p.dX = (uint16_t*)dX;
   p.U_out = U_out;
-  p.tab = nf4_table();
+  p.tab = nf4_table(W.codebook);
   if (W.kind == LQ_WEIGHT_DENSE) return dx_pick<kDense>(p, st);
   if (W.double_quant) return dx_pick<kNF4DQ>(p, st);
   return dx_pick<kNF4>(p, st);
@@ -1131,7 +1131,7 @@ int bf16_fwd_multi(const void* X, int64_t T_tokens, const lq_weight& W, const vo
     p.col_stride[c] = mt.col_stride[c];
   }
   p.Y = (uint16_t*)Y;
-  p.tab = nf4_table();
+  p.tab = nf4_table(W.codebook);
   return fwd_dispatch<true>(p, W, rp, st);
 }
 

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
         float a;
         if (WK == kNF4DQ) {
           const int64_t e = n * K + (k < K ? k : K - 8);
-          a = (float)sc.q8[i] * stab[(e >> 14) - g_lo];
+          a = dq_q_rt(p.W.dq, sc.q8[i]) * stab[(e >> 14) - g_lo];
         } else {
           a = __uint_as_float(sc.q8[i]);
         }
@@ -249,7 +249,7 @@ int bf16_merge(const lq_weight& W, const void* A, const void* B, int64_t r, floa
   p.k_tiles = (int32_t)cdiv(W.K, kTK);
   p.n_blocks = (int32_t)cdiv(W.N, kSlices * kTN);
   p.out = (uint16_t*)Wout;
-  p.tab = nf4_table();
+  p.tab = nf4_table(W.codebook);
   const unsigned blocks = (unsigned)(p.k_tiles * p.n_blocks);
   switch (weight_format(W)) {
     case kDense:

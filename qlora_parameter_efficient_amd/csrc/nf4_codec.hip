@@ -11,7 +11,8 @@
 // Both kernels are HBM-bound streaming passes.  Bit-exactness rests on: exact
 // float32 max, correctly rounded float32 division (HIP's default), no fused
 // multiply-add anywhere in the arithmetic (only lone products and quotients),
-// rintf (ties to even) for the 8-bit constant, and RNE for bf16 stores.
+// rintf (ties to even) for the 8-bit integer constant or an exact bit-level
+// E4M3 rounding for the FP8 one, and RNE for bf16 stores.
 #include "common.h"
 #include "nf4_deq.h"
 
@@ -94,6 +95,21 @@ __device__ __forceinline__ uint32_t nf4_code(float x, const Thr t) {
   return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
 }
 
+// Nearest non-negative E4M3 code to y in [0, 448], ties to the even code.
+// Below 2^-6 the codes are the subnormals m * 2^-9, so the code is rint(y *
+// 512) (8 is the first normal, 2^-6); above, the float32 exponent and the top
+// three mantissa bits form the code, rounded half-even on the dropped bits
+// (a carry out of the mantissa steps the exponent, as the encoding does).
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  if (y < 0.015625f) return (uint32_t)__builtin_rintf(y * 512.0f);
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t e = (b >> 23) - 127u + 7u;
+  const uint32_t mant = (b >> 20) & 7u;
+  const uint32_t rest = b & 0xFFFFFu;
+  const uint32_t up = (rest > 0x80000u || (rest == 0x80000u && (mant & 1u))) ? 1u : 0u;
+  return ((e << 3) | mant) + up;
+}
+
 // One workgroup per group of 256 blocks (16384 elements).  Step s, thread t
 // handles elements [g0 + (s*256 + t)*8, +8): eight consecutive threads cover
 // one 64-element block, whose absmax is reduced across those lanes.
@@ -138,7 +154,8 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quantize_kernel(
     const int64_t byte0 = e0 >> 1;
     if (e0 + 8 <= n) {
       // whole chunk, no per-element branches: the eight divisions interleave.
-      // c1 == 0 (an all-zero block) encodes every element as level 7 (zero).
+      // c1 == 0 (an all-zero block) encodes every element as level 7 (the
+      // zero of the default codebook; the level nearest zero otherwise).
       uint32_t packed = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -178,7 +195,7 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quantize_kernel(
     if (c2 != 0.0f) {
       const float ratio = c1 / c2;
       const float scaled = ratio * 127.0f;
-      q = (uint32_t)__builtin_rintf(scaled);
+      q = double_quant == LQ_DQ_FP8 ? e4m3_code(scaled) : (uint32_t)__builtin_rintf(scaled);
     }
     q8[blk] = (uint8_t)q;
   }
@@ -195,10 +212,10 @@ __global__ __launch_bounds__(kDeqThreads) void nf4_dequantize_kernel(
 }  // namespace
 
 int launch_nf4_quantize(const void* W, lq_dtype wdt, int64_t n, int32_t double_quant,
-                        uint8_t* codes, uint8_t* q8, float* c2, float* absmax,
+                        int32_t codebook, uint8_t* codes, uint8_t* q8, float* c2, float* absmax,
                         hipStream_t stream) {
   const int64_t groups = cdiv(n, kGroupElems);
-  const NF4Table& tab = nf4_table();
+  const NF4Table& tab = nf4_table(codebook);
   if (wdt == LQ_BF16) {
     hipLaunchKernelGGL(nf4_quantize_kernel<uint16_t>, dim3((unsigned)groups), dim3(kQuantThreads),
                        0, stream, (const uint16_t*)W, n, double_quant, codes, q8, c2, absmax, tab);
@@ -210,10 +227,10 @@ int launch_nf4_quantize(const void* W, lq_dtype wdt, int64_t n, int32_t double_q
 }
 
 int launch_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
-                          const float* absmax, int32_t double_quant, int64_t n, void* out,
-                          lq_dtype odt, hipStream_t stream) {
+                          const float* absmax, int32_t double_quant, int32_t codebook, int64_t n,
+                          void* out, lq_dtype odt, hipStream_t stream) {
   const int64_t blocks = cdiv(n, kDeqSpan);
-  const NF4Table& tab = nf4_table();
+  const NF4Table& tab = nf4_table(codebook);
   if (odt == LQ_BF16) {
     hipLaunchKernelGGL(nf4_dequantize_kernel<true>, dim3((unsigned)blocks), dim3(kDeqThreads), 0,
                        stream, codes, q8, c2, absmax, double_quant, n, out, tab);

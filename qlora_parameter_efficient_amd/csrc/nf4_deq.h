@@ -3,7 +3,8 @@
 //
 // ("Low-Rank Adaptation (LoRA) and QLoRA: Mathematical Foundations ...",
 // sections "1. 4-bit NormalFloat (NF4) Quantization" and "2. Double
-// Quantization (DQ)": w = cb[code] * a', a' = q8 * (c2 / 127).)
+// Quantization (DQ)": w = cb[code] * a', a' = q * (c2 / 127) with q the
+// integer or the E4M3 value of the 8-bit constant.)
 //
 // 256 threads cover 32768 elements (two groups of 256 blocks); thread t owns
 // the 16 chunks of 8 elements t + 256 i, so consecutive lanes read
@@ -52,8 +53,8 @@ __device__ __forceinline__ void nf4_deq_span(int t, int64_t span, const uint8_t*
   for (int i = 0; i < kDeqChunks; ++i) {
     const int64_t e = base + 8 * (int64_t)(t + kDeqThreads * i);
     if (e >= n) continue;
-    const float a = double_quant ? (float)qv[i] * steps[e / kDeqGroup - g_lo]
-                                 : __uint_as_float(qv[i]);
+    const float qf = double_quant == LQ_DQ_FP8 ? dq_value<true>(qv[i]) : dq_value<false>(qv[i]);
+    const float a = double_quant ? qf * steps[e / kDeqGroup - g_lo] : __uint_as_float(qv[i]);
     if (e + 8 <= n) {
       float w[8];
 #pragma unroll

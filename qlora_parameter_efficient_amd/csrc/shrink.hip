@@ -276,7 +276,7 @@ int launch_prep(const lq_weight& W, void* wout, const void* Z, int64_t M, int64_
   pa.n = W.N * W.K;
   pa.nd = (int32_t)cdiv(pa.n, kDeqSpan);
   pa.wout = (uint16_t*)wout;
-  pa.tab = nf4_table();
+  pa.tab = nf4_table(W.codebook);
   const dim3 grid((unsigned)(pa.nd + cdiv(M, 16))), block(256);
   const uint16_t* Zh = (const uint16_t*)Z;
   const uint16_t* Gh = (const uint16_t*)G;

@@ -23,6 +23,10 @@ LQ_F32, LQ_BF16 = 0, 1
 LQ_WEIGHT_DENSE, LQ_WEIGHT_NF4 = 0, 1
 LQ_OP_FWD, LQ_OP_BWD, LQ_OP_FWD_MULTI, LQ_OP_FWD_FUSED, LQ_OP_BWD_FUSED = 0, 1, 2, 3, 4
 LQ_OP_FWD_MULTI_FUSED = 5
+LQ_DQ_NONE, LQ_DQ_INT8, LQ_DQ_FP8 = 0, 1, 2
+LQ_CB_NF4, LQ_CB_NF4_SYMMETRIC = 0, 1
+DQ_FORMATS = {"int8": LQ_DQ_INT8, "fp8": LQ_DQ_FP8}
+CODEBOOKS = {"nf4": LQ_CB_NF4, "nf4_symmetric": LQ_CB_NF4_SYMMETRIC}
 STATUS = {0: "LQ_OK", -1: "LQ_ERR_INVALID_ARG", -2: "LQ_ERR_UNSUPPORTED",
           -3: "LQ_ERR_WORKSPACE", -4: "LQ_ERR_HIP"}
 
@@ -39,7 +43,7 @@ class LqWeightStruct(ctypes.Structure):
         ("N", ctypes.c_int64), ("K", ctypes.c_int64),
         ("dense", ctypes.c_void_p), ("codes", ctypes.c_void_p),
         ("q8", ctypes.c_void_p), ("c2", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
-        ("double_quant", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("double_quant", ctypes.c_int32), ("codebook", ctypes.c_int32),
     ]
 
 
@@ -53,9 +57,9 @@ _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ct
 _WP = ctypes.POINTER(LqWeightStruct)
 
 _SIGS = {
-    "lq_nf4_codebook": (ctypes.c_int, [_vp]),
-    "lq_nf4_quantize": (ctypes.c_int, [_vp, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp]),
-    "lq_nf4_dequantize": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i64, _vp, _i32, _vp]),
+    "lq_nf4_codebook": (ctypes.c_int, [_i32, _vp]),
+    "lq_nf4_quantize": (ctypes.c_int, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "lq_nf4_dequantize": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _vp, _i32, _vp]),
     "lq_lora_fwd": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i64, _f32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "lq_lora_bwd": (ctypes.c_int, [_vp, _vp, _i64, _WP, _vp, _vp, _i64, _f32, _i32, _vp, _vp, _vp,
                                    _vp, _i32, _vp, _sz, _vp]),
@@ -147,6 +151,11 @@ class NF4Weight:
     c2: torch.Tensor | None = None
     absmax: torch.Tensor | None = None
     double_quant: bool = True
+    dq_format: str = "int8"        # "int8" or "fp8" (second-level constants)
+    codebook: str = "nf4"          # "nf4" or "nf4_symmetric"
+
+    def dq_code(self):
+        return DQ_FORMATS[self.dq_format] if self.double_quant else LQ_DQ_NONE
 
 
 def weight_struct(W0, dtype):
@@ -160,7 +169,8 @@ def weight_struct(W0, dtype):
         s.q8 = W0.q8.data_ptr() if W0.q8 is not None else None
         s.c2 = W0.c2.data_ptr() if W0.c2 is not None else None
         s.absmax = W0.absmax.data_ptr() if W0.absmax is not None else None
-        s.double_quant = 1 if W0.double_quant else 0
+        s.double_quant = W0.dq_code()
+        s.codebook = CODEBOOKS[W0.codebook]
     else:
         _dev(W0)
         s.kind = LQ_WEIGHT_DENSE
@@ -172,13 +182,14 @@ def weight_struct(W0, dtype):
 
 # ------------------------------------------------------------------ calls
 
-def lq_nf4_codebook():
+def lq_nf4_codebook(codebook="nf4"):
     buf = (ctypes.c_float * 16)()
-    _check(lib().lq_nf4_codebook(ctypes.cast(buf, ctypes.c_void_p)))
+    _check(lib().lq_nf4_codebook(CODEBOOKS[codebook], ctypes.cast(buf, ctypes.c_void_p)))
     return list(buf)
 
 
-def lq_nf4_quantize(W: torch.Tensor, double_quant: bool = True) -> NF4Weight:
+def lq_nf4_quantize(W: torch.Tensor, double_quant: bool = True, dq_format: str = "int8",
+                    codebook: str = "nf4") -> NF4Weight:
     _dev(W)
     n = W.numel()
     nb = -(-n // 64)
@@ -190,17 +201,18 @@ def lq_nf4_quantize(W: torch.Tensor, double_quant: bool = True) -> NF4Weight:
         c2 = torch.empty(-(-nb // 256), dtype=torch.float32, device=dev)
     else:
         absmax = torch.empty(nb, dtype=torch.float32, device=dev)
-    _check(lib().lq_nf4_quantize(_ptr(W), _dt(W), n, int(double_quant), _ptr(codes), _ptr(q8),
-                                 _ptr(c2), _ptr(absmax), _stream()))
-    N, K = (W.shape if W.dim() == 2 else (1, n))
-    return NF4Weight(codes, N, K, q8, c2, absmax, double_quant)
+    out = NF4Weight(codes, *(W.shape if W.dim() == 2 else (1, n)), q8, c2, absmax,
+                    double_quant, dq_format, codebook)
+    _check(lib().lq_nf4_quantize(_ptr(W), _dt(W), n, out.dq_code(), CODEBOOKS[codebook],
+                                 _ptr(codes), _ptr(q8), _ptr(c2), _ptr(absmax), _stream()))
+    return out
 
 
 def lq_nf4_dequantize(q: NF4Weight, dtype=torch.bfloat16, n: int | None = None) -> torch.Tensor:
     n = q.N * q.K if n is None else n
     out = torch.empty(n, dtype=dtype, device=q.codes.device)
     _check(lib().lq_nf4_dequantize(_ptr(q.codes), _ptr(q.q8), _ptr(q.c2), _ptr(q.absmax),
-                                   int(q.double_quant), n, _ptr(out),
+                                   q.dq_code(), CODEBOOKS[q.codebook], n, _ptr(out),
                                    LQ_F32 if dtype == torch.float32 else LQ_BF16, _stream()))
     return out
 

@@ -24,9 +24,11 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(lq._SIGS)
 
 
-def test_library_codebook_equals_oracle_bitwise():
-    ours = np.array(lq.lq_nf4_codebook(), dtype=np.float32)
-    assert np.array_equal(ours.view(np.uint32), onf4.nf4_codebook().view(np.uint32))
+@pytest.mark.parametrize("cb", ["nf4", "nf4_symmetric"])
+def test_library_codebook_equals_oracle_bitwise(cb):
+    ours = np.array(lq.lq_nf4_codebook(cb), dtype=np.float32)
+    assert np.array_equal(ours.view(np.uint32), onf4.nf4_codebook(cb).view(np.uint32))
+    assert lq.lib().lq_nf4_codebook(2, ctypes.cast((ctypes.c_float * 16)(), ctypes.c_void_p)) == -1
 
 
 def test_num_params_matches_oracle():
@@ -87,11 +89,14 @@ def test_argument_errors_launch_nothing():
     # M = 0 is a no-op
     assert _fwd(_weight(), M=0) == 0
     # bad quantise arguments
-    assert L.lq_nf4_quantize(None, 1, 10, 1, 0x1000, 0x1000, 0x1000, None, None) == -1
-    assert L.lq_nf4_quantize(0x1000, 1, 0, 1, 0x1000, 0x1000, 0x1000, None, None) == -1
-    assert L.lq_nf4_quantize(0x1000, 1, 10, 1, 0x1000, None, 0x1000, None, None) == -1
-    assert L.lq_nf4_quantize(0x1000, 7, 10, 1, 0x1000, 0x1000, 0x1000, None, None) == -1
-    assert L.lq_nf4_dequantize(0x1000, None, None, None, 0, 10, 0x1000, 1, None) == -1
+    assert L.lq_nf4_quantize(None, 1, 10, 1, 0, 0x1000, 0x1000, 0x1000, None, None) == -1
+    assert L.lq_nf4_quantize(0x1000, 1, 0, 1, 0, 0x1000, 0x1000, 0x1000, None, None) == -1
+    assert L.lq_nf4_quantize(0x1000, 1, 10, 1, 0, 0x1000, None, 0x1000, None, None) == -1
+    assert L.lq_nf4_quantize(0x1000, 7, 10, 1, 0, 0x1000, 0x1000, 0x1000, None, None) == -1
+    assert L.lq_nf4_quantize(0x1000, 1, 10, 3, 0, 0x1000, 0x1000, 0x1000, None, None) == -1
+    assert L.lq_nf4_quantize(0x1000, 1, 10, 2, 5, 0x1000, 0x1000, 0x1000, None, None) == -1
+    assert L.lq_nf4_dequantize(0x1000, None, None, None, 0, 0, 10, 0x1000, 1, None) == -1
+    assert L.lq_nf4_dequantize(0x1000, 0x1000, 0x1000, None, 2, 7, 10, 0x1000, 1, None) == -1
     # backward workspace
     w = _weight()
     assert L.lq_lora_bwd(0x1000, 0x1000, 64, ctypes.byref(w), 0x1000, 0x1000, 8, 2.0, 1, None,
@@ -123,10 +128,13 @@ def test_argument_errors_launch_nothing():
                                      0x1000, 0x1000, 1, 1, 0x1000, 0x1000, 1 << 20, None) == -1
     # merge
     assert L.lq_lora_merge(ctypes.byref(w), None, 0x1000, 8, 2.0, 1, 0x1000, None) == -1
-    # reserved field must be zero
+    # unknown codebook or constant format in the descriptor
     w2 = _weight()
-    w2.reserved = 1
+    w2.codebook = 2
     assert _fwd(w2) == -1
+    w3 = _weight(kind=1)
+    w3.double_quant = 3
+    assert _fwd(w3) == -1
 
 
 def test_adamw_argument_errors_launch_nothing():
