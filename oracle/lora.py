@@ -25,6 +25,14 @@ Y is M x N.  Every product is float64 from the exact input values.
   "2. Multi-Tenant Dynamic Multiplexing").
 * Trainable parameters per matrix r (d_in + d_out) ("Large Language Model
   Fine-tuning and LoRA", section "Choosing what to adapt: targets and rank").
+* LoRA-input dropout ("Lesson 26", the adapter configuration with
+  lora_dropout = 0.05; the pages give the setting, not its definition).
+  Reading: inverted dropout on the adapter branch's input only,
+  D(X) = X * keep / (1 - p) with keep a 0/1 mask drawn by the caller, so
+  Y = X W0^T + s (D(X) A^T) B^T and, by the chain rule, dX = dY W0 +
+  s ((dY B) A) * keep / (1 - p), dA = s (dY B)^T D(X), dB = s dY^T (D(X) A^T).
+  The mask arrives packed one bit per element of X in row-major order, bit j
+  of byte i standing for element 8 i + j (1 = kept).
 """
 from __future__ import annotations
 
@@ -111,3 +119,34 @@ def forward_loop(X, W0, A, B, s):
             bax = sum(float(B[n][j]) * ax[j] for j in range(r))
             Y[m][n] = base + s * bax
     return Y
+
+
+def unpack_keep(bits, M, K):
+    """Boolean M x K keep mask from its packed bits (bit j of byte i is element
+    8 i + j of the row-major M x K array)."""
+    b = np.asarray(bits, dtype=np.uint8).ravel()
+    flat = np.zeros(M * K, dtype=bool)
+    for e in range(M * K):
+        flat[e] = (int(b[e // 8]) >> (e % 8)) & 1
+    return flat.reshape(M, K)
+
+
+def lora_forward_dropout(X, W0, A, B, s, keep, p):
+    """Returns (Y, T) with T = D(X) A^T, D(X) = X * keep / (1 - p)."""
+    X, W0, A, B = map(_f64, (X, W0, A, B))
+    Xd = X * np.asarray(keep, dtype=np.float64) / (1.0 - p)
+    T = Xd @ A.T
+    Y = X @ W0.T + s * (T @ B.T)
+    return Y, T
+
+
+def lora_backward_dropout(dY, X, W0, A, B, s, keep, p):
+    """Returns (dX, dA, dB) of the dropout forward for the loss gradient dY."""
+    dY, X, W0, A, B = map(_f64, (dY, X, W0, A, B))
+    kf = np.asarray(keep, dtype=np.float64) / (1.0 - p)
+    Xd = X * kf
+    U = dY @ B
+    dX = dY @ W0 + s * ((U @ A) * kf)
+    dA = s * (U.T @ Xd)
+    dB = s * (dY.T @ (Xd @ A.T))
+    return dX, dA, dB

@@ -29,6 +29,7 @@ __all__ = [
     "small_case",
     "adamw_case",
     "config4_adapter_sizes",
+    "dropout_keep_bits",
 ]
 
 
@@ -242,3 +243,12 @@ def adamw_case(sizes, steps: int, seed: int = 11, zero_frac: float = 0.01):
             gs.append(g)
         grads.append(gs)
     return masters, grads
+
+
+def dropout_keep_bits(M: int, K: int, p: float, seed: int = 23) -> np.ndarray:
+    """A seeded dropout keep-mask for an M x K input, packed one bit per element
+    (bit j of byte i is element 8 i + j of the row-major array; 1 = kept).
+    Each element is kept independently with probability 1 - p."""
+    rng = np.random.default_rng(seed)
+    keep = rng.random(M * K) >= p
+    return np.packbits(keep, bitorder="little")

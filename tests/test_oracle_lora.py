@@ -179,3 +179,68 @@ def test_merge_flops_match_pages():
     assert round(32 * 2 * lora.merge_flops(d, d, 8) / 1e9, 2) == g["merge_gflops_qv_r8_32"]
     tot = 32 * (3 * lora.merge_flops(d, d, 16) + lora.merge_flops(d, ffn, 16))
     assert round(tot / 1e9, 2) == g["merge_gflops_qvo_down_r16"]
+
+
+# ------------------------------------------------------------ LoRA-input dropout
+
+def test_dropout_mask_bit_order():
+    # byte 0b00000101 keeps elements 0 and 2; the second byte's bit 7 is element 15
+    keep = lora.unpack_keep(np.array([0b00000101, 0b10000000], np.uint8), 2, 8)
+    assert keep[0].tolist() == [True, False, True, False, False, False, False, False]
+    assert keep[1].tolist() == [False] * 7 + [True]
+    rng = np.random.default_rng(1)
+    k = rng.random((3, 16)) < 0.7
+    assert np.array_equal(lora.unpack_keep(np.packbits(k.ravel(), bitorder="little"), 3, 16), k)
+
+
+def test_dropout_all_kept_p0_is_plain_lora():
+    X, W0, A, B, G = tiny(4)
+    keep = np.ones(X.shape, bool)
+    Y, T = lora.lora_forward_dropout(X, W0, A, B, 1.5, keep, 0.0)
+    Y0, _, T0 = lora.lora_forward(X, W0, A, B, 1.5)
+    assert np.array_equal(Y, Y0) and np.array_equal(T, T0)
+    for a, b in zip(lora.lora_backward_dropout(G, X, W0, A, B, 1.5, keep, 0.0),
+                    lora.lora_backward(G, X, W0, A, B, 1.5)):
+        assert np.array_equal(a, b)
+
+
+def test_dropout_all_dropped_is_base_and_no_adapter_grads():
+    X, W0, A, B, G = tiny(5)
+    keep = np.zeros(X.shape, bool)
+    Y, T = lora.lora_forward_dropout(X, W0, A, B, 2.0, keep, 0.3)
+    assert not T.any()
+    assert np.array_equal(Y, X @ W0.T)
+    dX, dA, dB = lora.lora_backward_dropout(G, X, W0, A, B, 2.0, keep, 0.3)
+    assert np.array_equal(dX, G @ W0) and not dA.any() and not dB.any()
+
+
+def test_dropout_expectation_over_all_masks_is_plain_lora():
+    # brute force over every mask of one row of K = 6: the keep-probability
+    # weighted mean of the adapter term is exactly the undropped one
+    rng = np.random.default_rng(2)
+    K, N, r, p, s = 6, 4, 2, 0.3, 2.0
+    X = rng.standard_normal((1, K))
+    W0 = rng.standard_normal((N, K))
+    A = rng.standard_normal((r, K))
+    B = rng.standard_normal((N, r))
+    mean = np.zeros((1, N))
+    for bits in range(2 ** K):
+        keep = np.array([[(bits >> k) & 1 for k in range(K)]], bool)
+        w = (1 - p) ** keep.sum() * p ** (K - keep.sum())
+        mean += w * lora.lora_forward_dropout(X, W0, A, B, s, keep, p)[0]
+    want = lora.lora_forward(X, W0, A, B, s)[0]
+    np.testing.assert_allclose(mean, want, rtol=1e-12, atol=1e-12)
+
+
+def test_dropout_gradients_match_finite_differences():
+    X, W0, A, B, G = tiny(6, M=3, N=4, K=5, r=2)
+    rng = np.random.default_rng(7)
+    keep = rng.random(X.shape) < 0.6
+    p, s = 0.4, 1.25
+
+    def f(X_, A_, B_):
+        return float(np.sum(G * lora.lora_forward_dropout(X_, W0, A_, B_, s, keep, p)[0]))
+    dX, dA, dB = lora.lora_backward_dropout(G, X, W0, A, B, s, keep, p)
+    np.testing.assert_allclose(dX, fd_grad(lambda P: f(P, A, B), X), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dA, fd_grad(lambda P: f(X, P, B), A), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dB, fd_grad(lambda P: f(X, A, P), B), rtol=1e-6, atol=1e-8)
