@@ -224,6 +224,48 @@ int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0,
                 int32_t accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Forward with LoRA-input dropout ([L26] "Putting It Together": the adapter
+ * configuration's lora_dropout; the pages give the setting, and the operation
+ * is read as inverted dropout on the adapter branch's input):
+ *   Y = X W0^T + s (D(X) A^T) B^T,   D(X) = X * keep / (1 - p)
+ * The base product sees the undropped X.
+ *   keep     device, ceil(M*K/8) bytes: the keep mask drawn by the caller, one
+ *            bit per element of X in row-major order, bit j of byte i for
+ *            element 8i + j (1 = kept; the caller draws it with probability
+ *            1 - p per element)
+ *   p        the dropout probability, 0 <= p < 1 (the factor 1/(1 - p) is
+ *            formed in double and rounded to float32)
+ *   T_out    optional device M x r float32: receives T = D(X) A^T, which
+ *            lq_lora_bwd_dropout takes as T_saved
+ *   ws       at least lq_workspace_size(LQ_OP_FWD_DROPOUT_FUSED, M, N, K, r, 0)
+ *            bytes; lq_workspace_size(LQ_OP_FWD_DROPOUT, ...) bytes select the
+ *            large-tile path where it applies (M >= 2048, N % 256 == 0).
+ * Other arguments, shape rules and errors as lq_lora_fwd; dt must be LQ_BF16
+ * (LQ_ERR_UNSUPPORTED otherwise).  M = 0 is a no-op.
+ */
+int lq_lora_fwd_dropout(const void* X, int64_t M, const lq_weight* W0, const void* A,
+                        const void* B, int64_t r, float scale, const uint8_t* keep, float p,
+                        lq_dtype dt, void* Y, float* T_out, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/*
+ * Backward of lq_lora_fwd_dropout for the same keep mask and p (the chain
+ * rule on its forward; W0 receives no gradient):
+ *   dX = dY W0 + s ((dY B) A) * keep / (1 - p)
+ *   dA = s (dY B)^T D(X)          (r x K float32)
+ *   dB = s dY^T T,  T = D(X) A^T  (N x r float32)
+ * T_saved: T_out of the forward with the same mask, or NULL to recompute.
+ * ws: at least lq_workspace_size(LQ_OP_BWD_DROPOUT_FUSED, ...) bytes;
+ * lq_workspace_size(LQ_OP_BWD_DROPOUT, ...) selects the large-tile dX path.
+ * dX / dA / dB / accumulate rules as lq_lora_bwd; dt must be LQ_BF16.
+ */
+int lq_lora_bwd_dropout(const void* dY, const void* X, int64_t M, const lq_weight* W0,
+                        const void* A, const void* B, int64_t r, float scale,
+                        const uint8_t* keep, float p, lq_dtype dt, const float* T_saved,
+                        void* dX, float* dA, float* dB, int32_t accumulate, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/*
  * Merge for deployment: W_out = deq(W0) + s B A, N x K of dt
  * ([MF] "1. Static Weight Merging"; [FT] "Merging adapters vs keeping them
  * separate"; [L26] "4. Merging Adapters").  The merged matrix has W0's shape
@@ -339,13 +381,18 @@ int lq_check_segments(const int32_t* h_offsets, const int32_t* h_adapter,
  * (at large M the large-tile path, whose part holds the bf16 copy of W0 and
  * the split-K slots); LQ_OP_FWD_FUSED, LQ_OP_BWD_FUSED and
  * LQ_OP_FWD_MULTI_FUSED: the smallest size each call accepts, with which the
- * fused kernels run. */
+ * fused kernels run.  LQ_OP_{FWD,BWD}_DROPOUT and their _FUSED forms: the same
+ * pair for lq_lora_fwd_dropout and lq_lora_bwd_dropout. */
 #define LQ_OP_FWD 0
 #define LQ_OP_BWD 1
 #define LQ_OP_FWD_MULTI 2
 #define LQ_OP_FWD_FUSED 3
 #define LQ_OP_BWD_FUSED 4
 #define LQ_OP_FWD_MULTI_FUSED 5
+#define LQ_OP_FWD_DROPOUT 6
+#define LQ_OP_FWD_DROPOUT_FUSED 7
+#define LQ_OP_BWD_DROPOUT 8
+#define LQ_OP_BWD_DROPOUT_FUSED 9
 size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
                          int32_t n_adapters);
 

@@ -25,8 +25,9 @@ Y is M x N.  Every product is float64 from the exact input values.
   "2. Multi-Tenant Dynamic Multiplexing").
 * Trainable parameters per matrix r (d_in + d_out) ("Large Language Model
   Fine-tuning and LoRA", section "Choosing what to adapt: targets and rank").
-* LoRA-input dropout ("Lesson 26", the adapter configuration with
-  lora_dropout = 0.05; the pages give the setting, not its definition).
+* LoRA-input dropout ("Lesson 26", section "Putting It Together": the adapter
+  configuration with lora_dropout = 0.05; the pages give the setting, not its
+  definition).
   Reading: inverted dropout on the adapter branch's input only,
   D(X) = X * keep / (1 - p) with keep a 0/1 mask drawn by the caller, so
   Y = X W0^T + s (D(X) A^T) B^T and, by the chain rule, dX = dY W0 +

@@ -108,6 +108,24 @@ size_t multi_big_bytes(int64_t T, int64_t N, int64_t K, int64_t rc) {
   return dispatch::big_fwd_eligible(T, N, K) ? dispatch::big_multi_ws_bytes(T, N, K, rc) : 0;
 }
 
+// Dropout workspaces: [X * keep, bf16 M x K][T, float32 M x r][the forward's
+// large-tile part, or the fused path's bf16 M x rp Tm]; backward: [X * keep]
+// [the backward's workspace][its large-tile part].
+size_t drop_fwd_bytes(int64_t M, int64_t N, int64_t K, int64_t r, bool big) {
+  const int64_t rp = r <= 32 ? 32 : 64;
+  const size_t head = align256((size_t)(M * K) * 2) + align256((size_t)(M * r) * 4);
+  return head + (big ? dispatch::big_fwd_ws_bytes(M, N, K, r) : (size_t)(M * rp) * 2);
+}
+
+size_t drop_bwd_bytes(int64_t M, int64_t N, int64_t K, int64_t r, bool big) {
+  const size_t head = align256((size_t)(M * K) * 2) + align256(bwd_ws_bytes(M, N, K, r));
+  return head + (big ? bwd_big_bytes(M, N, K) : 0);
+}
+
+bool drop_fwd_big(int64_t M, int64_t N, int64_t K) {
+  return M > kDecodeMaxM && dispatch::big_fwd_eligible(M, N, K);
+}
+
 // Column table of the multi-adapter forward from host rank offsets (n + 1
 // entries, checked by the caller) and per-adapter scales.
 MultiTab make_multi_tab(int32_t n, const int32_t* roff, const float* scales, int64_t N) {
@@ -233,6 +251,14 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
       const size_t big = multi_big_bytes(M, N, K, r * (n_adapters > 0 ? n_adapters : 1));
       return big > base ? big : base;
     }
+    case LQ_OP_FWD_DROPOUT:
+      return drop_fwd_bytes(M, N, K, r, drop_fwd_big(M, N, K));
+    case LQ_OP_FWD_DROPOUT_FUSED:
+      return drop_fwd_bytes(M, N, K, r, false);
+    case LQ_OP_BWD_DROPOUT:
+      return drop_bwd_bytes(M, N, K, r, bwd_big_bytes(M, N, K) != 0);
+    case LQ_OP_BWD_DROPOUT_FUSED:
+      return drop_bwd_bytes(M, N, K, r, false);
     case LQ_OP_FWD_FUSED:
       return (size_t)((M <= kDecodeMaxM ? kTParts : 1) * M * r) * 4;
     case LQ_OP_BWD_FUSED:
@@ -347,6 +373,77 @@ int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0, c
   if (big && ws_bytes >= align256(need) + big) big_ws = (char*)ws + align256(need);
   return dispatch::bf16_bwd(dY, X, M, *W0, A, B, r, scale, T_saved, dX, dA, dB, accumulate, ws,
                             big_ws, stream);
+}
+
+int lq_lora_fwd_dropout(const void* X, int64_t M, const lq_weight* W0, const void* A,
+                        const void* B, int64_t r, float scale, const uint8_t* keep, float p,
+                        lq_dtype dt, void* Y, float* T_out, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  REQUIRE(dt == LQ_F32 || dt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
+  REQUIRE(dt == LQ_BF16, LQ_ERR_UNSUPPORTED, "dropout is implemented for bf16 only");
+  int rc = check_weight(W0, dt);
+  if (rc) return rc;
+  REQUIRE(M >= 0, LQ_ERR_INVALID_ARG, "M = %lld", (long long)M);
+  REQUIRE(r >= 1 && r <= kMaxRank, LQ_ERR_UNSUPPORTED, "rank %lld outside [1, %lld]",
+          (long long)r, (long long)kMaxRank);
+  REQUIRE(std::isfinite(p) && p >= 0.0f && p < 1.0f, LQ_ERR_INVALID_ARG,
+          "dropout probability must be in [0, 1)");
+  if ((rc = check_bf16_shape(W0)) || (rc = check_bf16_rows(M, W0))) return rc;
+  if (M == 0) return LQ_OK;
+  REQUIRE(X && A && B && Y && keep, LQ_ERR_INVALID_ARG, "X, A, B, Y or keep is NULL");
+  const int64_t N = W0->N, K = W0->K;
+  const size_t need = drop_fwd_bytes(M, N, K, r, false);
+  REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu",
+          ws_bytes, need);
+  const bool big = drop_fwd_big(M, N, K) && ws_bytes >= drop_fwd_bytes(M, N, K, r, true);
+  char* w = (char*)ws;
+  void* Xd = w;
+  w += align256((size_t)(M * K) * 2);
+  float* T = T_out ? T_out : (float*)w;
+  w += align256((size_t)(M * r) * 4);
+  const float inv_keep = (float)(1.0 / (1.0 - (double)p));
+  if ((rc = dispatch::launch_keep_apply(X, keep, M, K, Xd, stream))) return rc;
+  if (big)
+    return dispatch::big_fwd(X, M, *W0, A, B, r, scale, Y, T, w, stream, Xd, inv_keep);
+  if ((rc = dispatch::t_only(Xd, M, K, A, r, T, stream, nullptr, 0))) return rc;
+  const int rp = r <= 32 ? 32 : 64;
+  if ((rc = dispatch::launch_t_finish(T, M, r, inv_keep, scale, w, rp, stream))) return rc;
+  return dispatch::bf16_fwd_given_t(X, M, *W0, B, r, w, Y, stream);
+}
+
+int lq_lora_bwd_dropout(const void* dY, const void* X, int64_t M, const lq_weight* W0,
+                        const void* A, const void* B, int64_t r, float scale,
+                        const uint8_t* keep, float p, lq_dtype dt, const float* T_saved,
+                        void* dX, float* dA, float* dB, int32_t accumulate, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  REQUIRE(dt == LQ_F32 || dt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
+  REQUIRE(dt == LQ_BF16, LQ_ERR_UNSUPPORTED, "dropout is implemented for bf16 only");
+  int rc = check_weight(W0, dt);
+  if (rc) return rc;
+  REQUIRE(M >= 0, LQ_ERR_INVALID_ARG, "M = %lld", (long long)M);
+  REQUIRE(r >= 1 && r <= kMaxRank, LQ_ERR_UNSUPPORTED, "rank %lld outside [1, %lld]",
+          (long long)r, (long long)kMaxRank);
+  REQUIRE(std::isfinite(p) && p >= 0.0f && p < 1.0f, LQ_ERR_INVALID_ARG,
+          "dropout probability must be in [0, 1)");
+  REQUIRE(A && B, LQ_ERR_INVALID_ARG, "A or B is NULL");
+  REQUIRE((dA == nullptr) == (dB == nullptr), LQ_ERR_INVALID_ARG,
+          "dA and dB must both be given or both be NULL");
+  REQUIRE(dA || dX, LQ_ERR_INVALID_ARG, "nothing to compute: dX, dA and dB are NULL");
+  REQUIRE(M == 0 || (dY && keep && (X || !dA)), LQ_ERR_INVALID_ARG, "dY, keep or X is NULL");
+  if ((rc = check_bf16_shape(W0)) || (rc = check_bf16_rows(M, W0))) return rc;
+  const int64_t N = W0->N, K = W0->K;
+  const size_t need = drop_bwd_bytes(M, N, K, r, false);
+  REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu",
+          ws_bytes, need);
+  char* w = (char*)ws;
+  void* Xd = w;
+  w += align256((size_t)(M * K) * 2);
+  void* big_ws = nullptr;
+  if (dX && bwd_big_bytes(M, N, K) && ws_bytes >= drop_bwd_bytes(M, N, K, r, true))
+    big_ws = w + align256(bwd_ws_bytes(M, N, K, r));
+  const float inv_keep = (float)(1.0 / (1.0 - (double)p));
+  return dispatch::bf16_bwd_dropout(dY, X, keep, inv_keep, M, *W0, A, B, r, scale, T_saved, dX,
+                                    dA, dB, accumulate, Xd, w, big_ws, stream);
 }
 
 int lq_lora_merge(const lq_weight* W0, const void* A, const void* B, int64_t r, float scale,

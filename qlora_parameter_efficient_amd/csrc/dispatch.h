@@ -72,8 +72,11 @@ bool big_fwd_eligible(int64_t M, int64_t N, int64_t K);
 bool big_dx_eligible(int64_t M, int64_t N, int64_t K);
 size_t big_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 size_t big_dx_ws_bytes(int64_t M, int64_t N, int64_t K);
+// Xa: the adapter branch's input when it differs from X (dropout), whose T is
+// then scaled by inv_keep.
 int big_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,
-            float s, void* Y, float* T_out, void* ws, hipStream_t st);
+            float s, void* Y, float* T_out, void* ws, hipStream_t st, const void* Xa = nullptr,
+            float inv_keep = 1.0f);
 // Multi-adapter forward at large T (same eligibility as the forward).
 size_t big_multi_ws_bytes(int64_t T, int64_t N, int64_t K, int64_t rc);
 int big_fwd_multi(const void* X, int64_t T, const lq_weight& W, const void* A_cat,
@@ -100,6 +103,24 @@ struct AdamHyper {
 };
 int adamw_step(const lq_adamw_tensor* ts, int32_t n_tensors, bool bf16_grad, const AdamHyper& h,
                hipStream_t st);
+
+// LoRA-input dropout (dropout.hip): X_d = X * keep; T *= inv_keep and
+// optionally Tm = bf16(s T) padded to rp columns; dX += s ((U A) * keep).
+int launch_keep_apply(const void* X, const uint8_t* keep, int64_t M, int64_t K, void* Xd,
+                      hipStream_t st);
+int launch_t_finish(float* T, int64_t M, int64_t r, float inv_keep, float s, void* Tm, int rp,
+                    hipStream_t st);
+int launch_dx_fixup(void* dX, const float* U, const void* A, const uint8_t* keep, int64_t M,
+                    int64_t K, int64_t r, float s, hipStream_t st);
+// The fused forward with the adapter factor given: Y = X W0^T + Tm B^T, Tm the
+// bf16 M x rp matrix s T (columns past r zero).
+int bf16_fwd_given_t(const void* X, int64_t M, const lq_weight& W, const void* B, int64_t r,
+                     const void* Tm, void* Y, hipStream_t st);
+// Dropout backward (lora_grad.hip); Xd is M x K bf16 scratch.
+int bf16_bwd_dropout(const void* dY, const void* X, const uint8_t* keep, float inv_keep,
+                     int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,
+                     float s, const float* T_saved, void* dX, float* dA, float* dB,
+                     int accumulate, void* Xd, void* ws, void* big_ws, hipStream_t st);
 
 }  // namespace dispatch
 }  // namespace lq

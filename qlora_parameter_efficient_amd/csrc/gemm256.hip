@@ -636,8 +636,10 @@ size_t big_dx_ws_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 int big_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,
-            float s, void* Y, float* T_out, void* ws, hipStream_t st) {
+            float s, void* Y, float* T_out, void* ws, hipStream_t st, const void* Xa,
+            float inv_keep) {
   const int64_t N = W.N, K = W.K;
+  const void* Z = Xa ? Xa : X;  // the adapter branch's input (dropped under dropout)
   char* w = (char*)ws;
   void* gws = w;
   w += align256(g256_ws_bytes(M, N));
@@ -647,9 +649,10 @@ int big_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const v
   const int nz = (int)(g256_flag_bytes(M, N) / 4);
   const void* Q = W.kind == LQ_WEIGHT_DENSE ? W.dense : (const void*)w;
   if (W.kind != LQ_WEIGHT_DENSE && shrink_eligible(false, r))
-    e = launch_prep(W, w, X, M, K, A, false, r, T, (int32_t*)gws, nz, st);
+    e = launch_prep(W, w, Z, M, K, A, false, r, T, (int32_t*)gws, nz, st);
   else if (!(e = W.kind == LQ_WEIGHT_DENSE ? 0 : bf16_weight(W, w, st)))
-    e = t_only(X, M, K, A, r, T, st, (int32_t*)gws, nz);
+    e = t_only(Z, M, K, A, r, T, st, (int32_t*)gws, nz);
+  if (!e && inv_keep != 1.0f) e = launch_t_finish(T, M, r, inv_keep, 0.0f, nullptr, 0, st);
   if (e) return e;
   return launch_g256(false, X, Q, T, B, M, N, K, r, s, Y, gws, st);
 }

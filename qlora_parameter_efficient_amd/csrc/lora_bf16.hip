@@ -1093,6 +1093,27 @@ size_t multi_ws_bytes(int64_t T_tokens, int64_t r, int32_t n_adapters) {
   return (size_t)T_tokens * 4 + (size_t)T_tokens * rp * 2 + 256;
 }
 
+int bf16_fwd_given_t(const void* X, int64_t M, const lq_weight& W, const void* B, int64_t r,
+                     const void* Tm, void* Y, hipStream_t st) {
+  FwdParams p{};
+  p.X = (const uint16_t*)X;
+  p.M = M;
+  p.W = weight_args(W);
+  p.Tm = (const uint16_t*)Tm;
+  p.Bstack = (const uint16_t*)B;
+  p.r = (int32_t)r;
+  p.n_ad = 1;
+  p.s = 1.0f;
+  p.rc = (int32_t)r;
+  for (int c = 0; c < kMaxRankCols; ++c) {  // B[n][c] = B[c + n r]; unused columns at 0
+    p.col_base[c] = c < r ? c : 0;
+    p.col_stride[c] = c < r ? (int32_t)r : 0;
+  }
+  p.Y = (uint16_t*)Y;
+  p.tab = nf4_table(W.codebook);
+  return fwd_dispatch<true>(p, W, r <= 32 ? 32 : 64, st);
+}
+
 int bf16_fwd_multi(const void* X, int64_t T_tokens, const lq_weight& W, const void* A_cat,
                    const void* B_cat, const MultiTab& mt, const int32_t* seg_offsets,
                    const int32_t* seg_adapter, int32_t n_seg, void* Y, void* ws, hipStream_t st) {

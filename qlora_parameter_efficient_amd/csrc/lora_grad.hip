@@ -350,5 +350,49 @@ int bf16_bwd(const void* dY, const void* X, int64_t M, const lq_weight& W, const
                    dA, dB, PA, PB, st);
 }
 
+// Backward of the dropout forward Y = X W0^T + s (D(X) A^T) B^T with
+// D(X) = X * keep * inv_keep:
+//   dX = dY W0 + s ((U' A) * keep),  U' = inv_keep (dY B)
+//   dA = s U'^T (X * keep),  dB = s dY^T T   (T = D(X) A^T, as the forward left it)
+// dX's base term comes from the product kernels run with s = 0 (which also
+// give U), its adapter term from the fix-up kernel.
+int bf16_bwd_dropout(const void* dY, const void* X, const uint8_t* keep, float inv_keep,
+                     int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,
+                     float s, const float* T_saved, void* dX, float* dA, float* dB,
+                     int accumulate, void* Xd, void* ws, void* big_ws, hipStream_t st) {
+  const int64_t N = W.N, K = W.K;
+  float* U = (float*)ws;
+  float* Tw = U + M * r;
+  uintptr_t pa = ((uintptr_t)(Tw + M * r) + 255) & ~(uintptr_t)255;
+  float* PA = (float*)pa;
+  float* PB = PA + (int64_t)pick_splits(M, K) * r * K;
+  int e;
+  const bool grads = dA != nullptr;
+  if (M == 0) {
+    if (accumulate || !grads) return LQ_OK;
+    if ((e = launch_zero_f32(dA, r * K, st))) return e;
+    return launch_zero_f32(dB, N * r, st);
+  }
+  if (dX) {
+    e = big_ws ? big_dx(dY, M, W, A, B, r, 0.0f, dX, U, big_ws, st)
+               : bf16_dx(dY, M, W, A, B, r, 0.0f, dX, U, st);
+  } else {
+    e = u_only(dY, M, N, B, r, U, st, nullptr, 0);
+  }
+  if (e) return e;
+  if ((e = launch_t_finish(U, M, r, inv_keep, 0.0f, nullptr, 0, st))) return e;
+  if (dX && (e = launch_dx_fixup(dX, U, A, keep, M, K, r, s, st))) return e;
+  if (!grads) return LQ_OK;
+  if ((e = launch_keep_apply(X, keep, M, K, Xd, st))) return e;
+  const float* T = T_saved;
+  if (!T) {
+    if ((e = t_only(Xd, M, K, A, r, Tw, st, nullptr, 0))) return e;
+    if ((e = launch_t_finish(Tw, M, r, inv_keep, 0.0f, nullptr, 0, st))) return e;
+    T = Tw;
+  }
+  return run_grads((const uint16_t*)Xd, U, (const uint16_t*)dY, T, M, N, K, (int)r, s, accumulate,
+                   dA, dB, PA, PB, st);
+}
+
 }  // namespace dispatch
 }  // namespace lq

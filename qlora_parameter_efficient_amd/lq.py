@@ -23,6 +23,7 @@ LQ_F32, LQ_BF16 = 0, 1
 LQ_WEIGHT_DENSE, LQ_WEIGHT_NF4 = 0, 1
 LQ_OP_FWD, LQ_OP_BWD, LQ_OP_FWD_MULTI, LQ_OP_FWD_FUSED, LQ_OP_BWD_FUSED = 0, 1, 2, 3, 4
 LQ_OP_FWD_MULTI_FUSED = 5
+LQ_OP_FWD_DROPOUT, LQ_OP_FWD_DROPOUT_FUSED, LQ_OP_BWD_DROPOUT, LQ_OP_BWD_DROPOUT_FUSED = 6, 7, 8, 9
 LQ_DQ_NONE, LQ_DQ_INT8, LQ_DQ_FP8 = 0, 1, 2
 LQ_CB_NF4, LQ_CB_NF4_SYMMETRIC = 0, 1
 DQ_FORMATS = {"int8": LQ_DQ_INT8, "fp8": LQ_DQ_FP8}
@@ -64,6 +65,10 @@ _SIGS = {
     "lq_lora_bwd": (ctypes.c_int, [_vp, _vp, _i64, _WP, _vp, _vp, _i64, _f32, _i32, _vp, _vp, _vp,
                                    _vp, _i32, _vp, _sz, _vp]),
     "lq_lora_merge": (ctypes.c_int, [_WP, _vp, _vp, _i64, _f32, _i32, _vp, _vp]),
+    "lq_lora_fwd_dropout": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i64, _f32, _vp, _f32, _i32,
+                                           _vp, _vp, _vp, _sz, _vp]),
+    "lq_lora_bwd_dropout": (ctypes.c_int, [_vp, _vp, _i64, _WP, _vp, _vp, _i64, _f32, _vp, _f32,
+                                           _i32, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "lq_lora_fwd_multi": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i32, _i64, _f32, _vp, _vp, _i32,
                                          _i32, _vp, _vp, _sz, _vp]),
     "lq_lora_fwd_multi_ranks": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
@@ -263,6 +268,51 @@ def lq_lora_bwd(dY, X, W0, A, B, scale, T_saved=None, need_dx=True, dA=None, dB=
     _check(lib().lq_lora_bwd(_ptr(dY), _ptr(X), M, ctypes.byref(w), _ptr(A), _ptr(B), r, scale, dt,
                              _ptr(T_saved), _ptr(dX), _ptr(dA), _ptr(dB), int(accumulate),
                              _ptr(ws), ws.numel(), _stream()))
+    return dX, dA, dB
+
+
+def lq_lora_fwd_dropout(X, W0, A, B, scale, keep, p, T_out=None, ws=None, Y=None, fused=False):
+    """Forward with LoRA-input dropout; ``keep`` is the packed uint8 keep mask
+    (one bit per element of X, bit j of byte i for element 8 i + j)."""
+    _dev(X, A, B, keep, T_out, ws, Y)
+    dt = _dt(X)
+    M = X.shape[0]
+    w = weight_struct(W0, dt)
+    r = A.shape[0]
+    if keep.dtype != torch.uint8 or keep.numel() * 8 < X.numel():
+        raise ValueError("keep must be a uint8 tensor of ceil(M*K/8) bytes")
+    if Y is None:
+        Y = torch.empty((M, w.N), dtype=X.dtype, device=X.device)
+    if ws is None:
+        op = LQ_OP_FWD_DROPOUT_FUSED if fused else LQ_OP_FWD_DROPOUT
+        ws = _ws(lq_workspace_size(op, M, w.N, w.K, r), X.device)
+    _check(lib().lq_lora_fwd_dropout(_ptr(X), M, ctypes.byref(w), _ptr(A), _ptr(B), r, scale,
+                                     _ptr(keep), p, dt, _ptr(Y), _ptr(T_out), _ptr(ws), ws.numel(),
+                                     _stream()))
+    return Y
+
+
+def lq_lora_bwd_dropout(dY, X, W0, A, B, scale, keep, p, T_saved=None, need_dx=True, dA=None,
+                        dB=None, accumulate=False, ws=None, dX=None, need_grads=True,
+                        fused=False):
+    _dev(dY, X, A, B, keep, T_saved, dA, dB, dX, ws)
+    dt = _dt(dY)
+    M = dY.shape[0]
+    w = weight_struct(W0, dt)
+    r = A.shape[0]
+    dev = dY.device
+    if dX is None and need_dx:
+        dX = torch.empty((M, w.K), dtype=dY.dtype, device=dev)
+    if need_grads and dA is None:
+        dA = torch.empty((r, w.K), dtype=torch.float32, device=dev)
+    if need_grads and dB is None:
+        dB = torch.empty((w.N, r), dtype=torch.float32, device=dev)
+    if ws is None:
+        op = LQ_OP_BWD_DROPOUT_FUSED if fused else LQ_OP_BWD_DROPOUT
+        ws = _ws(lq_workspace_size(op, M, w.N, w.K, r), dev)
+    _check(lib().lq_lora_bwd_dropout(_ptr(dY), _ptr(X), M, ctypes.byref(w), _ptr(A), _ptr(B), r,
+                                     scale, _ptr(keep), p, dt, _ptr(T_saved), _ptr(dX), _ptr(dA),
+                                     _ptr(dB), int(accumulate), _ptr(ws), ws.numel(), _stream()))
     return dX, dA, dB
 
 

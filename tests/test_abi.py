@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(lq.LIB_PATH),
 
 def test_exports_every_declared_symbol():
     declared = lq.declared_symbols()
-    assert len(declared) == 15
+    assert len(declared) == 17
     L = lq.lib()
     for name in declared:
         assert hasattr(L, name), name
@@ -155,6 +155,34 @@ def test_adamw_argument_errors_launch_nothing():
     assert step([ok, lq.LqAdamwTensor(0x1000, None, 0x3000, 0x4000, None, 5)]) == -1
     assert "tensor 1" in lq.lq_last_error()
     assert step([lq.LqAdamwTensor(0x1000, 0x2000, 0x3000, 0x4000, None, -1)]) == -1
+
+
+def test_dropout_argument_errors_launch_nothing():
+    L = lq.lib()
+    w = _weight()
+    big = 1 << 30
+
+    def fwd(keep=0x1000, p=0.05, dt=lq.LQ_BF16, ws=0x1000, wsb=big, M=64):
+        return L.lq_lora_fwd_dropout(0x1000, M, ctypes.byref(w), 0x1000, 0x1000, 8, 2.0, keep, p,
+                                     dt, 0x1000, None, ws, wsb, None)
+
+    def bwd(keep=0x1000, p=0.05, dA=0x1000, dB=0x1000, dX=0x1000, wsb=big):
+        return L.lq_lora_bwd_dropout(0x1000, 0x1000, 64, ctypes.byref(w), 0x1000, 0x1000, 8, 2.0,
+                                     keep, p, lq.LQ_BF16, None, dX, dA, dB, 0, 0x1000, wsb, None)
+    assert fwd(keep=None) == -1
+    assert fwd(p=1.0) == -1 and fwd(p=-0.1) == -1 and fwd(p=float("nan")) == -1
+    assert fwd(dt=lq.LQ_F32) == -2                       # bf16 only
+    assert fwd(wsb=100) == -3 and fwd(ws=None) == -3
+    assert fwd(M=0, keep=None) == 0                      # no-op
+    assert (lq.lq_workspace_size(lq.LQ_OP_FWD_DROPOUT, 2048, 4096, 4096, 16)
+            > lq.lq_workspace_size(lq.LQ_OP_FWD_DROPOUT_FUSED, 2048, 4096, 4096, 16)
+            >= 2048 * 4096 * 2)
+    assert (lq.lq_workspace_size(lq.LQ_OP_BWD_DROPOUT, 2048, 4096, 4096, 16)
+            > lq.lq_workspace_size(lq.LQ_OP_BWD_DROPOUT_FUSED, 2048, 4096, 4096, 16))
+    assert bwd(keep=None) == -1 and bwd(p=1.5) == -1
+    assert bwd(dA=None) == -1                            # dA and dB go together
+    assert bwd(dA=None, dB=None, dX=None) == -1
+    assert bwd(wsb=100) == -3
 
 
 def test_timing_read_without_launches():
