@@ -294,6 +294,23 @@ def secondary(S, torch):
     res["multi_adapter_config5"] = {"tokens": T5, "ms": round(t, 3),
                                     "TFLOPs": round(flop / (t * 1e-3) / 1e12, 1)}
     del X5, Y5, ws5
+    # the config-3 step with the pages' lora_dropout = 0.05 (seeded keep mask)
+    keep = torch.from_numpy(wl.dropout_keep_bits(M, K, 0.05, seed=99)).to(S["dev"])
+    wsdf = torch.empty(lq.lq_workspace_size(lq.LQ_OP_FWD_DROPOUT, M, N, K, R), dtype=torch.uint8,
+                       device=S["dev"])
+    wsdb = torch.empty(lq.lq_workspace_size(lq.LQ_OP_BWD_DROPOUT, M, N, K, R), dtype=torch.uint8,
+                       device=S["dev"])
+
+    def drop_step():
+        lq.lq_lora_fwd_dropout(S["X"], S["W"], S["A"], S["B"], S["s"], keep, 0.05, T_out=S["T"],
+                               Y=S["Y"], ws=wsdf)
+        lq.lq_lora_bwd_dropout(S["dY"], S["X"], S["W"], S["A"], S["B"], S["s"], keep, 0.05,
+                               T_saved=S["T"], dA=S["dA"], dB=S["dB"], ws=wsdb, dX=S["dX"])
+    drop_step()
+    t = cuda_time(drop_step, 20, torch)
+    res["dropout_step_config3_p005"] = {"ms": round(t, 4),
+                                        "TFLOPs": round(STEP_FLOP / (t * 1e-3) / 1e12, 1)}
+    del wsdf, wsdb
     # AdamW step on the adapters: float32 master, m, v and gradient, bf16 working
     # copy (16 bytes read and 14 written per parameter)
     for name, sizes in (("adamw_config4_block_r64", wl.config4_adapter_sizes()),
