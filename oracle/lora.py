@@ -34,6 +34,19 @@ Y is M x N.  Every product is float64 from the exact input values.
   s ((dY B) A) * keep / (1 - p), dA = s (dY B)^T D(X), dB = s dY^T (D(X) A^T).
   The mask arrives packed one bit per element of X in row-major order, bit j
   of byte i standing for element 8 i + j (1 = kept).
+* DoRA ("Large Language Model Fine-tuning and LoRA", section "Choosing what to
+  adapt": a trained magnitude vector of size d_out times a direction that gets
+  the low-rank update on top of the frozen base direction; "... Mathematical
+  Foundations ...", section "Advanced Variants: DoRA and LoRA+": W = m (V +
+  dW) / ||V + dW||, written there with m in R^{1 x d_in} and a Frobenius
+  norm).  The pages conflict on the size of m and on the norm.  Reading: m
+  has one entry per output row (d_out, as the first page states) and the norm
+  is the vector norm of each output row of V + dW, V = W0 and dW = s B A --
+  the per-vector norm of the cited paper in the d_out x d_in layout used here;
+  a whole-matrix Frobenius norm would make the normalisation one scalar and m
+  no magnitude per vector.  So W' = diag(m / c) (W0 + s B A) with
+  c_n = ||W0[n] + s B[n] A||_2 and Y = X W'^T.  Gradients are the exact chain
+  rule through the norm (the pages do not detach it).
 """
 from __future__ import annotations
 
@@ -151,3 +164,30 @@ def lora_backward_dropout(dY, X, W0, A, B, s, keep, p):
     dA = s * (U.T @ Xd)
     dB = s * (dY.T @ (Xd @ A.T))
     return dX, dA, dB
+
+
+def dora_forward(X, W0, A, B, s, m):
+    """Returns (Y, Z, c): Z = X (W0 + s B A)^T, c the row norms, Y = Z * (m / c)."""
+    X, W0, A, B, m = map(_f64, (X, W0, A, B, m))
+    W = W0 + s * (B @ A)
+    c = np.sqrt(np.sum(W * W, axis=1))
+    Z = X @ W.T
+    return Z * (m / c)[None, :], Z, c
+
+
+def dora_backward(dY, X, W0, A, B, s, m):
+    """Returns (dX, dA, dB, dm) of dora_forward for the loss gradient dY."""
+    dY, X, W0, A, B, m = map(_f64, (dY, X, W0, A, B, m))
+    W = W0 + s * (B @ A)
+    c = np.sqrt(np.sum(W * W, axis=1))
+    g = m / c
+    Z = X @ W.T
+    Gp = dY * g[None, :]               # gradient reaching Z
+    h = np.sum(dY * Z, axis=0)         # gradient reaching g, per output row
+    dm = h / c
+    kappa = -h * m / c ** 3            # gradient reaching c, times 1 / c
+    dW = Gp.T @ X + kappa[:, None] * W
+    dX = Gp @ W
+    dA = s * (B.T @ dW)
+    dB = s * (dW @ A.T)
+    return dX, dA, dB, dm

@@ -244,3 +244,46 @@ def test_dropout_gradients_match_finite_differences():
     np.testing.assert_allclose(dX, fd_grad(lambda P: f(P, A, B), X), rtol=1e-6, atol=1e-8)
     np.testing.assert_allclose(dA, fd_grad(lambda P: f(X, P, B), A), rtol=1e-6, atol=1e-8)
     np.testing.assert_allclose(dB, fd_grad(lambda P: f(X, A, P), B), rtol=1e-6, atol=1e-8)
+
+
+# ------------------------------------------------------------------ DoRA
+
+def test_dora_magnitude_at_row_norms_is_plain_lora():
+    # with m equal to the row norms of W0 + s B A the direction is rescaled
+    # back to itself: Y is the plain LoRA output
+    X, W0, A, B, G = tiny(8)
+    s = 1.7
+    W = W0 + s * (B @ A)
+    m = np.sqrt((W * W).sum(axis=1))
+    Y, Z, c = lora.dora_forward(X, W0, A, B, s, m)
+    np.testing.assert_allclose(Y, lora.lora_forward(X, W0, A, B, s)[0], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(c, m, rtol=1e-15)
+
+
+def test_dora_output_depends_only_on_direction():
+    # scaling W0 and B together scales every row of W0 + s B A: Y is unchanged
+    X, W0, A, B, G = tiny(9)
+    m = np.random.default_rng(9).uniform(0.5, 2.0, W0.shape[0])
+    Y1 = lora.dora_forward(X, W0, A, B, 0.8, m)[0]
+    Y2 = lora.dora_forward(X, 3.5 * W0, A, 3.5 * B, 0.8, m)[0]
+    np.testing.assert_allclose(Y1, Y2, rtol=1e-12, atol=1e-12)
+    # and row n of Y scales with m_n alone
+    m2 = m.copy()
+    m2[2] *= 4.0
+    Y3 = lora.dora_forward(X, W0, A, B, 0.8, m2)[0]
+    np.testing.assert_allclose(Y3[:, 2], 4.0 * Y1[:, 2], rtol=1e-12)
+    np.testing.assert_allclose(np.delete(Y3, 2, axis=1), np.delete(Y1, 2, axis=1), rtol=1e-15)
+
+
+def test_dora_gradients_match_finite_differences():
+    X, W0, A, B, G = tiny(10, M=3, N=4, K=5, r=2)
+    s = 1.3
+    m = np.random.default_rng(10).uniform(0.5, 2.0, 4)
+
+    def f(X_, A_, B_, m_):
+        return float(np.sum(G * lora.dora_forward(X_, W0, A_, B_, s, m_)[0]))
+    dX, dA, dB, dm = lora.dora_backward(G, X, W0, A, B, s, m)
+    np.testing.assert_allclose(dX, fd_grad(lambda P: f(P, A, B, m), X), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dA, fd_grad(lambda P: f(X, P, B, m), A), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dB, fd_grad(lambda P: f(X, A, P, m), B), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dm, fd_grad(lambda P: f(X, A, B, P), m), rtol=1e-6, atol=1e-8)
