@@ -266,6 +266,54 @@ int lq_lora_bwd_dropout(const void* dY, const void* X, int64_t M, const lq_weigh
                         size_t ws_bytes, hipStream_t stream);
 
 /*
+ * DoRA forward ([FT] "Choosing what to adapt": a trained magnitude vector of
+ * size d_out times a direction that receives the low-rank update; [MF]
+ * "Advanced Variants: DoRA and LoRA+": W = m (V + dW) / ||V + dW||).  The
+ * pages disagree on the size of m (d_out vs d_in) and write a Frobenius norm;
+ * the reading used is one magnitude per output row and the vector norm of
+ * each output row:
+ *   W' = diag(m / c) (W0 + s B A),  c_n = ||W0[n] + s B[n] A||_2,
+ *   Y = X W'^T = Z * (m / c) per output column,  Z = X (W0 + s B A)^T.
+ * W0 enters as the bf16 values the products use (an NF4 base dequantised).
+ *   magnitude  device float32[N], m (rows with c_n = 0 are outside the
+ *              contract)
+ *   Y          device M x N bf16
+ *   Z_out      optional device M x N bf16: receives Z, which lq_dora_bwd
+ *              needs as Z_saved
+ *   T_out      optional device M x r float32: T = X A^T, for lq_dora_bwd
+ *   norm_out   optional device float32[N]: receives c
+ *   ws         at least lq_workspace_size(LQ_OP_DORA_FWD_FUSED, M, N, K, r, 0)
+ *              bytes; lq_workspace_size(LQ_OP_DORA_FWD, ...) selects the
+ *              large-tile product where it applies
+ * Shape rules and errors as lq_lora_fwd; dt must be LQ_BF16.  M = 0: no-op.
+ */
+int lq_dora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, const void* B,
+                int64_t r, float scale, const float* magnitude, lq_dtype dt, void* Y,
+                void* Z_out, float* T_out, float* norm_out, void* ws, size_t ws_bytes,
+                hipStream_t stream);
+
+/*
+ * DoRA backward: the exact chain rule through the row norms (the norm is not
+ * held constant).  With g = m / c, G' = dY * g (per column) and
+ * h_n = sum_m dY[m][n] Z[m][n]:
+ *   dm = h / c,  dW = G'^T X + diag(-h m / c^3) (W0 + s B A),
+ *   dX = G' (W0 + s B A),  dA = s B^T dW,  dB = s dW A^T.
+ *   Z_saved   device M x N bf16, Z_out of lq_dora_fwd on the same inputs
+ *   T_saved   optional T_out of that forward (NULL: recomputed)
+ *   dX        optional device M x K bf16
+ *   dA, dB, dmag  required float32 outputs (r x K, N x r, N); accumulate = 1
+ *             adds into all three
+ *   ws        at least lq_workspace_size(LQ_OP_DORA_BWD_FUSED, ...) bytes;
+ *             lq_workspace_size(LQ_OP_DORA_BWD, ...) selects the large-tile dX
+ * Shape rules and errors as lq_lora_bwd; dt must be LQ_BF16.
+ */
+int lq_dora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0, const void* A,
+                const void* B, int64_t r, float scale, const float* magnitude, lq_dtype dt,
+                const void* Z_saved, const float* T_saved, void* dX, float* dA, float* dB,
+                float* dmag, int32_t accumulate, void* ws, size_t ws_bytes,
+                hipStream_t stream);
+
+/*
  * Merge for deployment: W_out = deq(W0) + s B A, N x K of dt
  * ([MF] "1. Static Weight Merging"; [FT] "Merging adapters vs keeping them
  * separate"; [L26] "4. Merging Adapters").  The merged matrix has W0's shape
@@ -381,8 +429,9 @@ int lq_check_segments(const int32_t* h_offsets, const int32_t* h_adapter,
  * (at large M the large-tile path, whose part holds the bf16 copy of W0 and
  * the split-K slots); LQ_OP_FWD_FUSED, LQ_OP_BWD_FUSED and
  * LQ_OP_FWD_MULTI_FUSED: the smallest size each call accepts, with which the
- * fused kernels run.  LQ_OP_{FWD,BWD}_DROPOUT and their _FUSED forms: the same
- * pair for lq_lora_fwd_dropout and lq_lora_bwd_dropout. */
+ * fused kernels run.  LQ_OP_{FWD,BWD}_DROPOUT and LQ_OP_DORA_{FWD,BWD} and
+ * their _FUSED forms: the same pair for the dropout and DoRA entry points
+ * (the DoRA sizes assume an NF4 base, whose bf16 copy they include). */
 #define LQ_OP_FWD 0
 #define LQ_OP_BWD 1
 #define LQ_OP_FWD_MULTI 2
@@ -393,6 +442,10 @@ int lq_check_segments(const int32_t* h_offsets, const int32_t* h_adapter,
 #define LQ_OP_FWD_DROPOUT_FUSED 7
 #define LQ_OP_BWD_DROPOUT 8
 #define LQ_OP_BWD_DROPOUT_FUSED 9
+#define LQ_OP_DORA_FWD 10
+#define LQ_OP_DORA_FWD_FUSED 11
+#define LQ_OP_DORA_BWD 12
+#define LQ_OP_DORA_BWD_FUSED 13
 size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
                          int32_t n_adapters);
 

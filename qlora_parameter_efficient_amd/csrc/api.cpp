@@ -126,6 +126,80 @@ bool drop_fwd_big(int64_t M, int64_t N, int64_t K) {
   return M > kDecodeMaxM && dispatch::big_fwd_eligible(M, N, K);
 }
 
+// Carves a caller workspace into 256-byte aligned pieces; with a null base it
+// only measures (the size is then the final offset).
+struct Bump {
+  char* base;
+  char* p;
+  explicit Bump(void* b) : base((char*)b), p((char*)b) {}
+  template <class T>
+  T* take(size_t bytes) {
+    T* r = (T*)p;
+    p += align256(bytes);
+    return r;
+  }
+  size_t used() const { return (size_t)(p - base); }
+};
+
+// DoRA weight side: [bf16 W0 (NF4 weights only)][w0sq][P0][Gram][c][g]
+void dora_side_take(Bump& b, bool nf4, int64_t N, int64_t K, int64_t r, float* norm_out,
+                    const void*& Wd, const void* dense, dispatch::DoraSide& d) {
+  Wd = nf4 ? (const void*)b.take<uint16_t>((size_t)(N * K) * 2) : dense;
+  d.w0sq = b.take<float>((size_t)N * 4);
+  d.P0 = b.take<float>((size_t)(N * r) * 4);
+  d.Gram = b.take<float>((size_t)(r * r) * 4);
+  d.c = norm_out ? norm_out : b.take<float>((size_t)N * 4);
+  d.g = b.take<float>((size_t)N * 4);
+}
+
+size_t plain_fwd_bytes(int64_t M, int64_t N, int64_t K, int64_t r, bool big) {
+  if (M <= kDecodeMaxM) return (size_t)(kTParts * M * r) * 4;
+  return big ? dispatch::big_fwd_ws_bytes(M, N, K, r) : 0;
+}
+
+bool dora_fwd_big(int64_t M, int64_t N, int64_t K) {
+  return M > kDecodeMaxM && dispatch::big_fwd_eligible(M, N, K);
+}
+
+size_t dora_fwd_bytes(int64_t M, int64_t N, int64_t K, int64_t r, bool nf4, bool big) {
+  Bump b(nullptr);
+  const void* Wd;
+  dispatch::DoraSide d;
+  dora_side_take(b, nf4, N, K, r, nullptr, Wd, nullptr, d);
+  b.take<uint16_t>((size_t)(M * N) * 2);  // Z when the caller keeps none
+  return b.used() + plain_fwd_bytes(M, N, K, r, big);
+}
+
+void dora_grad_take(Bump& b, int64_t M, int64_t N, int64_t K, int64_t r, dispatch::DoraGrad& q) {
+  q.Gp = b.take<uint16_t>((size_t)(M * N) * 2);
+  q.hpart = b.take<float>((size_t)(dispatch::dora_tiles(M) * N) * 4);
+  q.kappa = b.take<float>((size_t)N * 4);
+  q.KB = b.take<float>((size_t)(N * r) * 4);
+  q.R = b.take<float>((size_t)(r * r) * 4);
+  q.part = b.take<float>(dispatch::grad_one_bytes(N, K, r));
+}
+
+size_t dora_bwd_bytes(int64_t M, int64_t N, int64_t K, int64_t r, bool nf4, bool big) {
+  Bump b(nullptr);
+  const void* Wd;
+  dispatch::DoraSide d;
+  dispatch::DoraGrad q;
+  dora_side_take(b, nf4, N, K, r, nullptr, Wd, nullptr, d);
+  dora_grad_take(b, M, N, K, r, q);
+  b.take<char>(bwd_ws_bytes(M, N, K, r));
+  return b.used() + (big ? bwd_big_bytes(M, N, K) : 0);
+}
+
+lq_weight dense_view(const lq_weight& W, const void* Wd) {
+  lq_weight v{};
+  v.kind = LQ_WEIGHT_DENSE;
+  v.dtype = LQ_BF16;
+  v.N = W.N;
+  v.K = W.K;
+  v.dense = Wd;
+  return v;
+}
+
 // Column table of the multi-adapter forward from host rank offsets (n + 1
 // entries, checked by the caller) and per-adapter scales.
 MultiTab make_multi_tab(int32_t n, const int32_t* roff, const float* scales, int64_t N) {
@@ -259,6 +333,14 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
       return drop_bwd_bytes(M, N, K, r, bwd_big_bytes(M, N, K) != 0);
     case LQ_OP_BWD_DROPOUT_FUSED:
       return drop_bwd_bytes(M, N, K, r, false);
+    case LQ_OP_DORA_FWD:
+      return dora_fwd_bytes(M, N, K, r, true, dora_fwd_big(M, N, K));
+    case LQ_OP_DORA_FWD_FUSED:
+      return dora_fwd_bytes(M, N, K, r, true, false);
+    case LQ_OP_DORA_BWD:
+      return dora_bwd_bytes(M, N, K, r, true, bwd_big_bytes(M, N, K) != 0);
+    case LQ_OP_DORA_BWD_FUSED:
+      return dora_bwd_bytes(M, N, K, r, true, false);
     case LQ_OP_FWD_FUSED:
       return (size_t)((M <= kDecodeMaxM ? kTParts : 1) * M * r) * 4;
     case LQ_OP_BWD_FUSED:
@@ -444,6 +526,100 @@ int lq_lora_bwd_dropout(const void* dY, const void* X, int64_t M, const lq_weigh
   const float inv_keep = (float)(1.0 / (1.0 - (double)p));
   return dispatch::bf16_bwd_dropout(dY, X, keep, inv_keep, M, *W0, A, B, r, scale, T_saved, dX,
                                     dA, dB, accumulate, Xd, w, big_ws, stream);
+}
+
+int lq_dora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, const void* B,
+                int64_t r, float scale, const float* magnitude, lq_dtype dt, void* Y,
+                void* Z_out, float* T_out, float* norm_out, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  REQUIRE(dt == LQ_F32 || dt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
+  REQUIRE(dt == LQ_BF16, LQ_ERR_UNSUPPORTED, "DoRA is implemented for bf16 only");
+  int rc = check_weight(W0, dt);
+  if (rc) return rc;
+  REQUIRE(M >= 0, LQ_ERR_INVALID_ARG, "M = %lld", (long long)M);
+  REQUIRE(r >= 1 && r <= kMaxRank, LQ_ERR_UNSUPPORTED, "rank %lld outside [1, %lld]",
+          (long long)r, (long long)kMaxRank);
+  if ((rc = check_bf16_shape(W0)) || (rc = check_bf16_rows(M, W0))) return rc;
+  if (M == 0) return LQ_OK;
+  REQUIRE(X && A && B && Y && magnitude, LQ_ERR_INVALID_ARG, "X, A, B, Y or magnitude is NULL");
+  const int64_t N = W0->N, K = W0->K;
+  const bool nf4 = W0->kind == LQ_WEIGHT_NF4;
+  const size_t need = dora_fwd_bytes(M, N, K, r, nf4, false);
+  REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu",
+          ws_bytes, need);
+  const bool big = dora_fwd_big(M, N, K) && ws_bytes >= dora_fwd_bytes(M, N, K, r, nf4, true);
+  Bump b(ws);
+  const void* Wd;
+  dispatch::DoraSide d;
+  dora_side_take(b, nf4, N, K, r, norm_out, Wd, W0->dense, d);
+  void* Z = Z_out ? Z_out : (void*)b.take<uint16_t>((size_t)(M * N) * 2);
+  void* rest = b.p;
+  if (nf4 && (rc = launch_nf4_dequantize(W0->codes, W0->q8, W0->c2, W0->absmax,
+                                         W0->double_quant, W0->codebook, N * K, (void*)Wd,
+                                         LQ_BF16, stream)))
+    return rc;
+  if ((rc = dispatch::dora_weight_side(Wd, N, K, A, B, r, scale, magnitude, d, stream))) return rc;
+  const lq_weight Wv = dense_view(*W0, Wd);
+  if (M <= kDecodeMaxM)
+    rc = dispatch::decode_fwd(X, M, Wv, A, B, r, scale, Z, T_out, (float*)rest, stream);
+  else if (big)
+    rc = dispatch::big_fwd(X, M, Wv, A, B, r, scale, Z, T_out, rest, stream);
+  else
+    rc = dispatch::bf16_fwd(X, M, Wv, A, B, r, scale, Z, T_out, stream);
+  if (rc) return rc;
+  return dispatch::launch_col_scale(Z, d.g, M, N, Y, stream);
+}
+
+int lq_dora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0, const void* A,
+                const void* B, int64_t r, float scale, const float* magnitude, lq_dtype dt,
+                const void* Z_saved, const float* T_saved, void* dX, float* dA, float* dB,
+                float* dmag, int32_t accumulate, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  REQUIRE(dt == LQ_F32 || dt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
+  REQUIRE(dt == LQ_BF16, LQ_ERR_UNSUPPORTED, "DoRA is implemented for bf16 only");
+  int rc = check_weight(W0, dt);
+  if (rc) return rc;
+  REQUIRE(M >= 0, LQ_ERR_INVALID_ARG, "M = %lld", (long long)M);
+  REQUIRE(r >= 1 && r <= kMaxRank, LQ_ERR_UNSUPPORTED, "rank %lld outside [1, %lld]",
+          (long long)r, (long long)kMaxRank);
+  REQUIRE(A && B && magnitude && dA && dB && dmag, LQ_ERR_INVALID_ARG,
+          "A, B, magnitude, dA, dB and dmag are required");
+  REQUIRE(M == 0 || (dY && X && Z_saved), LQ_ERR_INVALID_ARG, "dY, X or Z_saved is NULL");
+  if ((rc = check_bf16_shape(W0)) || (rc = check_bf16_rows(M, W0))) return rc;
+  const int64_t N = W0->N, K = W0->K;
+  if (M == 0) {
+    if (accumulate) return LQ_OK;
+    if ((rc = launch_zero_f32(dA, r * K, stream)) || (rc = launch_zero_f32(dB, N * r, stream)))
+      return rc;
+    return launch_zero_f32(dmag, N, stream);
+  }
+  const bool nf4 = W0->kind == LQ_WEIGHT_NF4;
+  const size_t need = dora_bwd_bytes(M, N, K, r, nf4, false);
+  REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu",
+          ws_bytes, need);
+  const bool big = dX && bwd_big_bytes(M, N, K) &&
+                   ws_bytes >= dora_bwd_bytes(M, N, K, r, nf4, true);
+  Bump b(ws);
+  const void* Wd;
+  dispatch::DoraSide d;
+  dispatch::DoraGrad q;
+  dora_side_take(b, nf4, N, K, r, nullptr, Wd, W0->dense, d);
+  dora_grad_take(b, M, N, K, r, q);
+  void* bws = b.take<char>(bwd_ws_bytes(M, N, K, r));
+  void* big_ws = big ? (void*)b.p : nullptr;
+  if (nf4 && (rc = launch_nf4_dequantize(W0->codes, W0->q8, W0->c2, W0->absmax,
+                                         W0->double_quant, W0->codebook, N * K, (void*)Wd,
+                                         LQ_BF16, stream)))
+    return rc;
+  if ((rc = dispatch::dora_weight_side(Wd, N, K, A, B, r, scale, magnitude, d, stream))) return rc;
+  if ((rc = dispatch::dora_grad_side(dY, Z_saved, magnitude, B, M, N, r, d, q, dmag, accumulate,
+                                     stream)))
+    return rc;
+  const lq_weight Wv = dense_view(*W0, Wd);
+  if ((rc = dispatch::bf16_bwd(q.Gp, X, M, Wv, A, B, r, scale, T_saved, dX, dA, dB, accumulate,
+                               bws, big_ws, stream)))
+    return rc;
+  return dispatch::dora_fix(Wd, A, B, N, K, r, scale, d, q, dA, dB, stream);
 }
 
 int lq_lora_merge(const lq_weight* W0, const void* A, const void* B, int64_t r, float scale,

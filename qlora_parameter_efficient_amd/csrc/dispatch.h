@@ -122,5 +122,41 @@ int bf16_bwd_dropout(const void* dY, const void* X, const uint8_t* keep, float i
                      float s, const float* T_saved, void* dX, float* dA, float* dB,
                      int accumulate, void* Xd, void* ws, void* big_ws, hipStream_t st);
 
+// One gradient-style reduction (lora_grad.hip): out[j][c] += s sum_m
+// V[m][j] Z[m][c] over M rows (Z bf16 M x C, V float32 M x r); part holds
+// grad_one_bytes(M, C, r) bytes of split partials.
+size_t grad_one_bytes(int64_t M, int64_t C, int64_t r);
+int grad_one(const void* Z, const float* V, int64_t M, int64_t C, int r, float s, float* out,
+             float* part, hipStream_t st);
+
+// DoRA (dora.hip).  Weight side: row norms c of W0 + s B A (W0 given as the
+// bf16 matrix the products use) and g = m / c, with the pieces the backward
+// reuses.  Gradient side: G' = dY * g, h, dm, kappa and the kappa terms.
+struct DoraSide {
+  float* w0sq;  // N
+  float* P0;    // N x r, W0 A^T
+  float* Gram;  // r x r, A A^T
+  float* c;     // N
+  float* g;     // N
+};
+struct DoraGrad {
+  uint16_t* Gp;  // M x N bf16
+  float* hpart;  // tiles x N
+  float* kappa;  // N
+  float* KB;     // N x r
+  float* R;      // r x r
+  float* part;   // grad_one partials
+};
+int dora_tiles(int64_t M);
+int dora_weight_side(const void* Wd, int64_t N, int64_t K, const void* A, const void* B,
+                     int64_t r, float s, const float* m, const DoraSide& d, hipStream_t st);
+int launch_col_scale(const void* Z, const float* g, int64_t M, int64_t N, void* Y,
+                     hipStream_t st);
+int dora_grad_side(const void* dY, const void* Z, const float* m, const void* B, int64_t M,
+                   int64_t N, int64_t r, const DoraSide& d, const DoraGrad& q, float* dm,
+                   int accumulate, hipStream_t st);
+int dora_fix(const void* Wd, const void* A, const void* B, int64_t N, int64_t K, int64_t r,
+             float s, const DoraSide& d, const DoraGrad& q, float* dA, float* dB, hipStream_t st);
+
 }  // namespace dispatch
 }  // namespace lq

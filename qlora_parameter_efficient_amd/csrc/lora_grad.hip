@@ -308,6 +308,50 @@ int run_grads(const uint16_t* X, const float* U, const uint16_t* dY, const float
 
 namespace dispatch {
 
+size_t grad_one_bytes(int64_t M, int64_t C, int64_t r) {
+  return (size_t)(pick_splits(M, C) * r * C) * 4 + 512;
+}
+
+int grad_one(const void* Z, const float* V, int64_t M, int64_t C, int r, float s, float* out,
+             float* part, hipStream_t st) {
+  GradParams p;
+  p.job[0] = make_job((const uint16_t*)Z, V, M, C, part);
+  p.job[1] = p.job[0];  // unused: every workgroup belongs to job 0
+  p.M = M;
+  p.r = r;
+  p.blocks0 = p.job[0].c_tiles * p.job[0].splits;
+  const int blocks = p.blocks0;
+  const bool v4 = r % 4 == 0;
+  if (r <= 32) {
+    if (v4)
+      hipLaunchKernelGGL((grad_kernel<32, true>), dim3(blocks), dim3(kThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((grad_kernel<32, false>), dim3(blocks), dim3(kThreads), 0, st, p);
+  } else {
+    if (v4)
+      hipLaunchKernelGGL((grad_kernel<64, true>), dim3(blocks), dim3(kThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((grad_kernel<64, false>), dim3(blocks), dim3(kThreads), 0, st, p);
+  }
+  int e = hip_fail(hipGetLastError(), "grad_kernel launch");
+  if (e) return e;
+  ReduceParams q;
+  q.P[0] = part;
+  q.P[1] = part;
+  q.out[0] = out;
+  q.out[1] = out;
+  q.C[0] = C;
+  q.C[1] = 0;  // empty second part: the grid's rounding threads return at once
+  q.splits[0] = p.job[0].splits;
+  q.splits[1] = 0;
+  q.r = r;
+  q.s = s;
+  q.accumulate = 1;
+  const int64_t total = (int64_t)r * C;  // job 0's index space only
+  hipLaunchKernelGGL(grad_reduce_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, st, q);
+  return hip_fail(hipGetLastError(), "grad_reduce launch");
+}
+
 size_t grad_partial_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
   const int64_t sa = pick_splits(M, K), sb = pick_splits(M, N);
   return (size_t)(sa * r * K + sb * r * N) * 4 + 512;

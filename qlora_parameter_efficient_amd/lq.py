@@ -24,6 +24,7 @@ LQ_WEIGHT_DENSE, LQ_WEIGHT_NF4 = 0, 1
 LQ_OP_FWD, LQ_OP_BWD, LQ_OP_FWD_MULTI, LQ_OP_FWD_FUSED, LQ_OP_BWD_FUSED = 0, 1, 2, 3, 4
 LQ_OP_FWD_MULTI_FUSED = 5
 LQ_OP_FWD_DROPOUT, LQ_OP_FWD_DROPOUT_FUSED, LQ_OP_BWD_DROPOUT, LQ_OP_BWD_DROPOUT_FUSED = 6, 7, 8, 9
+LQ_OP_DORA_FWD, LQ_OP_DORA_FWD_FUSED, LQ_OP_DORA_BWD, LQ_OP_DORA_BWD_FUSED = 10, 11, 12, 13
 LQ_DQ_NONE, LQ_DQ_INT8, LQ_DQ_FP8 = 0, 1, 2
 LQ_CB_NF4, LQ_CB_NF4_SYMMETRIC = 0, 1
 DQ_FORMATS = {"int8": LQ_DQ_INT8, "fp8": LQ_DQ_FP8}
@@ -65,6 +66,10 @@ _SIGS = {
     "lq_lora_bwd": (ctypes.c_int, [_vp, _vp, _i64, _WP, _vp, _vp, _i64, _f32, _i32, _vp, _vp, _vp,
                                    _vp, _i32, _vp, _sz, _vp]),
     "lq_lora_merge": (ctypes.c_int, [_WP, _vp, _vp, _i64, _f32, _i32, _vp, _vp]),
+    "lq_dora_fwd": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i64, _f32, _vp, _i32, _vp, _vp, _vp,
+                                   _vp, _vp, _sz, _vp]),
+    "lq_dora_bwd": (ctypes.c_int, [_vp, _vp, _i64, _WP, _vp, _vp, _i64, _f32, _vp, _i32, _vp, _vp,
+                                   _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "lq_lora_fwd_dropout": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i64, _f32, _vp, _f32, _i32,
                                            _vp, _vp, _vp, _sz, _vp]),
     "lq_lora_bwd_dropout": (ctypes.c_int, [_vp, _vp, _i64, _WP, _vp, _vp, _i64, _f32, _vp, _f32,
@@ -314,6 +319,51 @@ def lq_lora_bwd_dropout(dY, X, W0, A, B, scale, keep, p, T_saved=None, need_dx=T
                                      scale, _ptr(keep), p, dt, _ptr(T_saved), _ptr(dX), _ptr(dA),
                                      _ptr(dB), int(accumulate), _ptr(ws), ws.numel(), _stream()))
     return dX, dA, dB
+
+
+def lq_dora_fwd(X, W0, A, B, scale, magnitude, Z_out=None, T_out=None, norm_out=None, ws=None,
+                Y=None, fused=False):
+    """DoRA forward; returns Y.  Pass Z_out (M x N bf16) to keep Z for lq_dora_bwd."""
+    _dev(X, A, B, magnitude, Z_out, T_out, norm_out, ws, Y)
+    dt = _dt(X)
+    M = X.shape[0]
+    w = weight_struct(W0, dt)
+    r = A.shape[0]
+    if Y is None:
+        Y = torch.empty((M, w.N), dtype=X.dtype, device=X.device)
+    if ws is None:
+        op = LQ_OP_DORA_FWD_FUSED if fused else LQ_OP_DORA_FWD
+        ws = _ws(lq_workspace_size(op, M, w.N, w.K, r), X.device)
+    _check(lib().lq_dora_fwd(_ptr(X), M, ctypes.byref(w), _ptr(A), _ptr(B), r, scale,
+                             _ptr(magnitude), dt, _ptr(Y), _ptr(Z_out), _ptr(T_out),
+                             _ptr(norm_out), _ptr(ws), ws.numel(), _stream()))
+    return Y
+
+
+def lq_dora_bwd(dY, X, W0, A, B, scale, magnitude, Z_saved, T_saved=None, need_dx=True, dA=None,
+                dB=None, dmag=None, accumulate=False, ws=None, dX=None, fused=False):
+    _dev(dY, X, A, B, magnitude, Z_saved, T_saved, dA, dB, dmag, ws, dX)
+    dt = _dt(dY)
+    M = dY.shape[0]
+    w = weight_struct(W0, dt)
+    r = A.shape[0]
+    dev = dY.device
+    if dX is None and need_dx:
+        dX = torch.empty((M, w.K), dtype=dY.dtype, device=dev)
+    if dA is None:
+        dA = torch.empty((r, w.K), dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty((w.N, r), dtype=torch.float32, device=dev)
+    if dmag is None:
+        dmag = torch.empty(w.N, dtype=torch.float32, device=dev)
+    if ws is None:
+        op = LQ_OP_DORA_BWD_FUSED if fused else LQ_OP_DORA_BWD
+        ws = _ws(lq_workspace_size(op, M, w.N, w.K, r), dev)
+    _check(lib().lq_dora_bwd(_ptr(dY), _ptr(X), M, ctypes.byref(w), _ptr(A), _ptr(B), r, scale,
+                             _ptr(magnitude), dt, _ptr(Z_saved), _ptr(T_saved), _ptr(dX),
+                             _ptr(dA), _ptr(dB), _ptr(dmag), int(accumulate), _ptr(ws),
+                             ws.numel(), _stream()))
+    return dX, dA, dB, dmag
 
 
 def lq_lora_merge(W0, A, B, scale, dtype=None, out=None):

@@ -30,6 +30,7 @@ __all__ = [
     "adamw_case",
     "config4_adapter_sizes",
     "dropout_keep_bits",
+    "dora_magnitude",
 ]
 
 
@@ -252,3 +253,11 @@ def dropout_keep_bits(M: int, K: int, p: float, seed: int = 23) -> np.ndarray:
     rng = np.random.default_rng(seed)
     keep = rng.random(M * K) >= p
     return np.packbits(keep, bitorder="little")
+
+
+def dora_magnitude(N: int, K: int, sigma_w: float = 0.02, seed: int = 29) -> np.ndarray:
+    """A seeded DoRA magnitude vector (float32, one entry per output row):
+    uniform in [0.5, 1.5] times sigma_w sqrt(K), the typical row norm of a
+    weight drawn with standard deviation sigma_w."""
+    rng = np.random.default_rng(seed)
+    return (rng.uniform(0.5, 1.5, N) * sigma_w * np.sqrt(K)).astype(np.float32)

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(lq.LIB_PATH),
 
 def test_exports_every_declared_symbol():
     declared = lq.declared_symbols()
-    assert len(declared) == 17
+    assert len(declared) == 19
     L = lq.lib()
     for name in declared:
         assert hasattr(L, name), name
@@ -183,6 +183,30 @@ def test_dropout_argument_errors_launch_nothing():
     assert bwd(dA=None) == -1                            # dA and dB go together
     assert bwd(dA=None, dB=None, dX=None) == -1
     assert bwd(wsb=100) == -3
+
+
+def test_dora_argument_errors_launch_nothing():
+    L = lq.lib()
+    w = _weight(kind=1)
+    big = 1 << 34
+
+    def fwd(mag=0x1000, dt=lq.LQ_BF16, wsb=big, M=64):
+        return L.lq_dora_fwd(0x1000, M, ctypes.byref(w), 0x1000, 0x1000, 8, 2.0, mag, dt, 0x1000,
+                             None, None, None, 0x1000, wsb, None)
+
+    def bwd(dmag=0x1000, Z=0x1000, wsb=big):
+        return L.lq_dora_bwd(0x1000, 0x1000, 64, ctypes.byref(w), 0x1000, 0x1000, 8, 2.0, 0x1000,
+                             lq.LQ_BF16, Z, None, 0x1000, 0x1000, 0x1000, dmag, 0, 0x1000, wsb,
+                             None)
+    assert fwd(mag=None) == -1
+    assert fwd(dt=lq.LQ_F32) == -2
+    assert fwd(wsb=1000) == -3
+    assert fwd(M=0, mag=None) == 0
+    assert bwd(dmag=None) == -1 and bwd(Z=None) == -1
+    assert bwd(wsb=1000) == -3
+    for op in (lq.LQ_OP_DORA_FWD, lq.LQ_OP_DORA_BWD):
+        assert (lq.lq_workspace_size(op, 2048, 4096, 4096, 16)
+                > lq.lq_workspace_size(op + 1, 2048, 4096, 4096, 16) > 4096 * 4096 * 2)
 
 
 def test_timing_read_without_launches():

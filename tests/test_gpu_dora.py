@@ -1,0 +1,125 @@
+"""DoRA on the GPU (lq_dora_fwd / lq_dora_bwd) against the oracle: fused and
+large-tile paths, decode-sized M, dense or NF4 base, odd and large ranks;
+Y, Z, dX, dA, dB and dm within the bf16 bar (2e-2 relative to max |oracle|),
+the row norms c within float32 rounding (1e-5).  With the magnitude set to
+the library's own row norms the output is the plain layer bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import lora as olora
+from oracle import nf4 as onf4
+from qlora_parameter_efficient_amd import lq
+from qlora_parameter_efficient_amd import workloads as wl
+
+from .gpu_helpers import BF16_TOL, DEV, F32_TOL, announce, f64, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def base_for(c, kind):
+    W0v = c["W0"].value
+    if kind == "nf4":
+        Wd = lq.lq_nf4_quantize(to_dev(c["W0"]))
+        q = onf4.nf4_quantize(W0v)
+        return Wd, onf4.bf16_bits_to_f64(onf4.nf4_dequantize_bf16(q)).reshape(W0v.shape)
+    return to_dev(c["W0"]), W0v.astype(np.float64)
+
+
+def run(c, kind, fused, label, rows=None):
+    M, K = c["X"].value.shape
+    N, r = c["W0"].value.shape[0], c["r"]
+    s = c["alpha"] / r
+    announce(f"dora {label} {kind} M={M} N={N} K={K} r={r} fused={fused}")
+    X, A, B, dY = to_dev(c["X"]), to_dev(c["A"]), to_dev(c["B"]), to_dev(c["dY"])
+    Wd, Wo = base_for(c, kind)
+    m_np = wl.dora_magnitude(N, K, seed=N + K)
+    m = torch.from_numpy(m_np).to(DEV)
+    Z = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    T = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    cn = torch.empty(N, dtype=torch.float32, device=DEV)
+    Y = lq.lq_dora_fwd(X, Wd, A, B, s, m, Z_out=Z, T_out=T, norm_out=cn, fused=fused)
+    dX, dA, dB, dm = lq.lq_dora_bwd(dY, X, Wd, A, B, s, m, Z, T_saved=T, fused=fused)
+    torch.cuda.synchronize()
+    Xo, Ao, Bo, dYo = c["X"].f64(), c["A"].f64(), c["B"].f64(), c["dY"].f64()
+    sel = np.arange(M) if rows is None else rows
+    Yo, Zo, co = olora.dora_forward(Xo[sel], Wo, Ao, Bo, s, m_np)
+    dXo, dAo, dBo, dmo = olora.dora_backward(dYo, Xo, Wo, Ao, Bo, s, m_np)
+    e = rel_err(f64(cn), co)
+    assert e <= F32_TOL, f"row norms rel err {e:.3e}"
+    for name, got, want in (("Y", f64(Y)[sel], Yo), ("Z", f64(Z)[sel], Zo),
+                            ("dX", f64(dX)[sel], dXo[sel]), ("dA", f64(dA), dAo),
+                            ("dB", f64(dB), dBo), ("dm", f64(dm), dmo)):
+        e = rel_err(got, want)
+        assert e <= BF16_TOL, f"{name} rel err {e:.3e}"
+    return dict(X=X, A=A, B=B, dY=dY, Wd=Wd, s=s, Y=Y, Z=Z, cn=cn, m=m, dA=dA, dB=dB, dm=dm, T=T)
+
+
+SHAPES = [
+    (300, 384, 512, 16, True),
+    (130, 192, 192, 5, True),
+    (700, 256, 320, 64, True),
+    (16, 256, 512, 8, True),
+    (2100, 256, 256, 16, False),
+    (2304, 512, 768, 64, False),
+]
+
+
+@pytest.mark.parametrize("kind", ["dense", "nf4"])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}r{r}{'' if f else '-large'}"
+                                               for m, n, k, r, f in SHAPES])
+def test_dora_layer(shape, kind):
+    M, N, K, r, fused = shape
+    c = wl.small_case(M, N, K, r, seed=M + N + K + r + 17)
+    run(c, kind, fused, "small")
+    if not fused:
+        run(c, kind, True, "small-fused")
+
+
+def test_magnitude_at_row_norms_gives_plain_output_exactly():
+    M, N, K, r = 300, 256, 512, 16
+    c = wl.small_case(M, N, K, r, seed=21)
+    o = run(c, "nf4", True, "identity")
+    Y = lq.lq_dora_fwd(o["X"], o["Wd"], o["A"], o["B"], o["s"], o["cn"])
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), o["Z"].view(torch.int16))
+
+
+def test_accumulate_adds_all_three_gradients():
+    M, N, K, r = 300, 256, 256, 8
+    c = wl.small_case(M, N, K, r, seed=22)
+    o = run(c, "dense", True, "accumulate")
+    dA, dB, dm = o["dA"].clone(), o["dB"].clone(), o["dm"].clone()
+    lq.lq_dora_bwd(o["dY"], o["X"], o["Wd"], o["A"], o["B"], o["s"], o["m"], o["Z"],
+                   T_saved=o["T"], dA=dA, dB=dB, dmag=dm, accumulate=True, need_dx=False)
+    torch.cuda.synchronize()
+    for name, got, once in (("dA", dA, o["dA"]), ("dB", dB, o["dB"]), ("dm", dm, o["dm"])):
+        e = rel_err(f64(got), 2 * f64(once))
+        assert e <= 1e-5, f"{name} accumulate rel err {e:.3e}"
+
+
+def test_config3_full_size():
+    c = wl.config3()
+    rows = np.random.default_rng(6).choice(2048, 64, replace=False)
+    run(c, "nf4", False, "config3", rows=rows)
+    run(c, "nf4", True, "config3-fused", rows=rows)
+
+
+def test_backward_is_deterministic():
+    # the gradient reductions add split partials in a fixed order and nothing
+    # else writes the outputs: repeated calls (with other allocations between
+    # them) give the same bits
+    M, N, K, r = 130, 192, 192, 5
+    c = wl.small_case(M, N, K, r, seed=23)
+    o = run(c, "dense", True, "determinism")
+    keep = []
+    for i in range(3):
+        pad = torch.empty(4096 * (i + 1), device=DEV)  # shift the allocator's placement
+        res = lq.lq_dora_bwd(o["dY"], o["X"], o["Wd"], o["A"], o["B"], o["s"], o["m"], o["Z"],
+                             T_saved=o["T"])
+        torch.cuda.synchronize()
+        keep.append([t.clone() for t in res])
+        del pad
+    for name, k in (("dX", 0), ("dA", 1), ("dB", 2), ("dm", 3)):
+        for other in keep[1:]:
+            assert torch.equal(keep[0][k], other[k]), f"{name} differs between calls"
