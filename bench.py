@@ -311,6 +311,25 @@ def secondary(S, torch):
     res["dropout_step_config3_p005"] = {"ms": round(t, 4),
                                         "TFLOPs": round(STEP_FLOP / (t * 1e-3) / 1e12, 1)}
     del wsdf, wsdb
+    # the config-3 step as DoRA (magnitude per output row, exact backward)
+    mag = torch.from_numpy(wl.dora_magnitude(N, K, seed=N + K)).to(S["dev"])
+    Zd = torch.empty((M, N), dtype=torch.bfloat16, device=S["dev"])
+    dmag = torch.empty(N, dtype=torch.float32, device=S["dev"])
+    wsof = torch.empty(lq.lq_workspace_size(lq.LQ_OP_DORA_FWD, M, N, K, R), dtype=torch.uint8,
+                       device=S["dev"])
+    wsob = torch.empty(lq.lq_workspace_size(lq.LQ_OP_DORA_BWD, M, N, K, R), dtype=torch.uint8,
+                       device=S["dev"])
+
+    def dora_step():
+        lq.lq_dora_fwd(S["X"], S["W"], S["A"], S["B"], S["s"], mag, Z_out=Zd, T_out=S["T"],
+                       Y=S["Y"], ws=wsof)
+        lq.lq_dora_bwd(S["dY"], S["X"], S["W"], S["A"], S["B"], S["s"], mag, Zd, T_saved=S["T"],
+                       dA=S["dA"], dB=S["dB"], dmag=dmag, ws=wsob, dX=S["dX"])
+    dora_step()
+    t = cuda_time(dora_step, 20, torch)
+    res["dora_step_config3"] = {"ms": round(t, 4),
+                                "TFLOPs": round(STEP_FLOP / (t * 1e-3) / 1e12, 1)}
+    del wsof, wsob, Zd
     # AdamW step on the adapters: float32 master, m, v and gradient, bf16 working
     # copy (16 bytes read and 14 written per parameter)
     for name, sizes in (("adamw_config4_block_r64", wl.config4_adapter_sizes()),
