@@ -315,6 +315,7 @@ def secondary(S, torch):
     mag = torch.from_numpy(wl.dora_magnitude(N, K, seed=N + K)).to(S["dev"])
     Zd = torch.empty((M, N), dtype=torch.bfloat16, device=S["dev"])
     dmag = torch.empty(N, dtype=torch.float32, device=S["dev"])
+    sv = torch.empty(lq.lq_dora_saved_floats(N, R), dtype=torch.float32, device=S["dev"])
     wsof = torch.empty(lq.lq_workspace_size(lq.LQ_OP_DORA_FWD, M, N, K, R), dtype=torch.uint8,
                        device=S["dev"])
     wsob = torch.empty(lq.lq_workspace_size(lq.LQ_OP_DORA_BWD, M, N, K, R), dtype=torch.uint8,
@@ -322,9 +323,9 @@ def secondary(S, torch):
 
     def dora_step():
         lq.lq_dora_fwd(S["X"], S["W"], S["A"], S["B"], S["s"], mag, Z_out=Zd, T_out=S["T"],
-                       Y=S["Y"], ws=wsof)
+                       saved_out=sv, Y=S["Y"], ws=wsof)
         lq.lq_dora_bwd(S["dY"], S["X"], S["W"], S["A"], S["B"], S["s"], mag, Zd, T_saved=S["T"],
-                       dA=S["dA"], dB=S["dB"], dmag=dmag, ws=wsob, dX=S["dX"])
+                       saved=sv, dA=S["dA"], dB=S["dB"], dmag=dmag, ws=wsob, dX=S["dX"])
     dora_step()
     t = cuda_time(dora_step, 20, torch)
     res["dora_step_config3"] = {"ms": round(t, 4),

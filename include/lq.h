@@ -281,7 +281,9 @@ int lq_lora_bwd_dropout(const void* dY, const void* X, int64_t M, const lq_weigh
  *   Z_out      optional device M x N bf16: receives Z, which lq_dora_bwd
  *              needs as Z_saved
  *   T_out      optional device M x r float32: T = X A^T, for lq_dora_bwd
- *   norm_out   optional device float32[N]: receives c
+ *   saved_out  optional device float32[lq_dora_saved_floats(N, r)]: receives
+ *              the weight-side results c[N], W0 A^T [N x r] and A A^T [r x r],
+ *              which lq_dora_bwd can take instead of recomputing them
  *   ws         at least lq_workspace_size(LQ_OP_DORA_FWD_FUSED, M, N, K, r, 0)
  *              bytes; lq_workspace_size(LQ_OP_DORA_FWD, ...) selects the
  *              large-tile product where it applies
@@ -289,8 +291,11 @@ int lq_lora_bwd_dropout(const void* dY, const void* X, int64_t M, const lq_weigh
  */
 int lq_dora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, const void* B,
                 int64_t r, float scale, const float* magnitude, lq_dtype dt, void* Y,
-                void* Z_out, float* T_out, float* norm_out, void* ws, size_t ws_bytes,
+                void* Z_out, float* T_out, float* saved_out, void* ws, size_t ws_bytes,
                 hipStream_t stream);
+
+/* Floats of lq_dora_fwd's saved_out buffer: N + N r + r^2. */
+int64_t lq_dora_saved_floats(int64_t N, int64_t r);
 
 /*
  * DoRA backward: the exact chain rule through the row norms (the norm is not
@@ -300,6 +305,8 @@ int lq_dora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
  *   dX = G' (W0 + s B A),  dA = s B^T dW,  dB = s dW A^T.
  *   Z_saved   device M x N bf16, Z_out of lq_dora_fwd on the same inputs
  *   T_saved   optional T_out of that forward (NULL: recomputed)
+ *   saved     optional saved_out of that forward, with the same W0, A, B and
+ *             scale (NULL: recomputed; the results are the same bits)
  *   dX        optional device M x K bf16
  *   dA, dB, dmag  required float32 outputs (r x K, N x r, N); accumulate = 1
  *             adds into all three
@@ -309,9 +316,9 @@ int lq_dora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
  */
 int lq_dora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0, const void* A,
                 const void* B, int64_t r, float scale, const float* magnitude, lq_dtype dt,
-                const void* Z_saved, const float* T_saved, void* dX, float* dA, float* dB,
-                float* dmag, int32_t accumulate, void* ws, size_t ws_bytes,
-                hipStream_t stream);
+                const void* Z_saved, const float* T_saved, const float* saved, void* dX,
+                float* dA, float* dB, float* dmag, int32_t accumulate, void* ws,
+                size_t ws_bytes, hipStream_t stream);
 
 /*
  * Merge for deployment: W_out = deq(W0) + s B A, N x K of dt

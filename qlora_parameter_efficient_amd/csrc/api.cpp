@@ -141,15 +141,20 @@ struct Bump {
   size_t used() const { return (size_t)(p - base); }
 };
 
-// DoRA weight side: [bf16 W0 (NF4 weights only)][w0sq][P0][Gram][c][g]
-void dora_side_take(Bump& b, bool nf4, int64_t N, int64_t K, int64_t r, float* norm_out,
+// DoRA weight side: [bf16 W0 (NF4 weights only)][w0sq][Gram partials][g] and,
+// unless the caller's saved buffer holds them, [c][P0][Gram] (the saved
+// buffer's layout: c[N], P0[N x r], Gram[r x r]).
+void dora_side_take(Bump& b, bool nf4, int64_t N, int64_t K, int64_t r, const float* saved,
                     const void*& Wd, const void* dense, dispatch::DoraSide& d) {
   Wd = nf4 ? (const void*)b.take<uint16_t>((size_t)(N * K) * 2) : dense;
   d.w0sq = b.take<float>((size_t)N * 4);
-  d.P0 = b.take<float>((size_t)(N * r) * 4);
-  d.Gram = b.take<float>((size_t)(r * r) * 4);
-  d.c = norm_out ? norm_out : b.take<float>((size_t)N * 4);
+  d.Gpart = b.take<float>((size_t)(dispatch::dora_gblocks(K) * r * r) * 4);
   d.g = b.take<float>((size_t)N * 4);
+  float* sv = saved ? const_cast<float*>(saved)
+                    : b.take<float>((size_t)(N + N * r + r * r) * 4);
+  d.c = sv;
+  d.P0 = sv + N;
+  d.Gram = sv + N + N * r;
 }
 
 size_t plain_fwd_bytes(int64_t M, int64_t N, int64_t K, int64_t r, bool big) {
@@ -175,6 +180,7 @@ void dora_grad_take(Bump& b, int64_t M, int64_t N, int64_t K, int64_t r, dispatc
   q.hpart = b.take<float>((size_t)(dispatch::dora_tiles(M) * N) * 4);
   q.kappa = b.take<float>((size_t)N * 4);
   q.KB = b.take<float>((size_t)(N * r) * 4);
+  q.Rpart = b.take<float>((size_t)(dispatch::dora_rblocks(N) * r * r) * 4);
   q.R = b.take<float>((size_t)(r * r) * 4);
   q.part = b.take<float>(dispatch::grad_one_bytes(N, K, r));
 }
@@ -528,9 +534,11 @@ int lq_lora_bwd_dropout(const void* dY, const void* X, int64_t M, const lq_weigh
                                     dA, dB, accumulate, Xd, w, big_ws, stream);
 }
 
+int64_t lq_dora_saved_floats(int64_t N, int64_t r) { return N + N * r + r * r; }
+
 int lq_dora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, const void* B,
                 int64_t r, float scale, const float* magnitude, lq_dtype dt, void* Y,
-                void* Z_out, float* T_out, float* norm_out, void* ws, size_t ws_bytes,
+                void* Z_out, float* T_out, float* saved_out, void* ws, size_t ws_bytes,
                 hipStream_t stream) {
   REQUIRE(dt == LQ_F32 || dt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
   REQUIRE(dt == LQ_BF16, LQ_ERR_UNSUPPORTED, "DoRA is implemented for bf16 only");
@@ -551,7 +559,7 @@ int lq_dora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
   Bump b(ws);
   const void* Wd;
   dispatch::DoraSide d;
-  dora_side_take(b, nf4, N, K, r, norm_out, Wd, W0->dense, d);
+  dora_side_take(b, nf4, N, K, r, saved_out, Wd, W0->dense, d);
   void* Z = Z_out ? Z_out : (void*)b.take<uint16_t>((size_t)(M * N) * 2);
   void* rest = b.p;
   if (nf4 && (rc = launch_nf4_dequantize(W0->codes, W0->q8, W0->c2, W0->absmax,
@@ -572,9 +580,9 @@ int lq_dora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
 
 int lq_dora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0, const void* A,
                 const void* B, int64_t r, float scale, const float* magnitude, lq_dtype dt,
-                const void* Z_saved, const float* T_saved, void* dX, float* dA, float* dB,
-                float* dmag, int32_t accumulate, void* ws, size_t ws_bytes,
-                hipStream_t stream) {
+                const void* Z_saved, const float* T_saved, const float* saved, void* dX,
+                float* dA, float* dB, float* dmag, int32_t accumulate, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
   REQUIRE(dt == LQ_F32 || dt == LQ_BF16, LQ_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
   REQUIRE(dt == LQ_BF16, LQ_ERR_UNSUPPORTED, "DoRA is implemented for bf16 only");
   int rc = check_weight(W0, dt);
@@ -603,7 +611,7 @@ int lq_dora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0, c
   const void* Wd;
   dispatch::DoraSide d;
   dispatch::DoraGrad q;
-  dora_side_take(b, nf4, N, K, r, nullptr, Wd, W0->dense, d);
+  dora_side_take(b, nf4, N, K, r, saved, Wd, W0->dense, d);
   dora_grad_take(b, M, N, K, r, q);
   void* bws = b.take<char>(bwd_ws_bytes(M, N, K, r));
   void* big_ws = big ? (void*)b.p : nullptr;
@@ -611,7 +619,9 @@ int lq_dora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0, c
                                          W0->double_quant, W0->codebook, N * K, (void*)Wd,
                                          LQ_BF16, stream)))
     return rc;
-  if ((rc = dispatch::dora_weight_side(Wd, N, K, A, B, r, scale, magnitude, d, stream))) return rc;
+  rc = saved ? dispatch::dora_g_from_c(magnitude, d, N, stream)
+             : dispatch::dora_weight_side(Wd, N, K, A, B, r, scale, magnitude, d, stream);
+  if (rc) return rc;
   if ((rc = dispatch::dora_grad_side(dY, Z_saved, magnitude, B, M, N, r, d, q, dmag, accumulate,
                                      stream)))
     return rc;

@@ -136,6 +136,7 @@ struct DoraSide {
   float* w0sq;  // N
   float* P0;    // N x r, W0 A^T
   float* Gram;  // r x r, A A^T
+  float* Gpart; // dora_gblocks(K) x r x r partials of A A^T
   float* c;     // N
   float* g;     // N
 };
@@ -144,12 +145,16 @@ struct DoraGrad {
   float* hpart;  // tiles x N
   float* kappa;  // N
   float* KB;     // N x r
+  float* Rpart;  // dora_rblocks(N) x r x r
   float* R;      // r x r
   float* part;   // grad_one partials
 };
 int dora_tiles(int64_t M);
+int dora_rblocks(int64_t N);
+int dora_gblocks(int64_t K);
 int dora_weight_side(const void* Wd, int64_t N, int64_t K, const void* A, const void* B,
                      int64_t r, float s, const float* m, const DoraSide& d, hipStream_t st);
+int dora_g_from_c(const float* m, const DoraSide& d, int64_t N, hipStream_t st);
 int launch_col_scale(const void* Z, const float* g, int64_t M, int64_t N, void* Y,
                      hipStream_t st);
 int dora_grad_side(const void* dY, const void* Z, const float* m, const void* B, int64_t M,

@@ -48,6 +48,10 @@ __global__ __launch_bounds__(256) void rowsumsq_kernel(const uint16_t* __restric
 }
 
 // c_n and g_n = m_n / c_n from the expansion of ||W0[n] + s B[n] A||^2.
+// RP lanes per row (RP = 16, 32 or 64 >= r, a power of two): lane i forms
+// b_i (Gram b)_i and P0[n][i] b_i, and the row's lanes add them with
+// shuffles.  Gram is staged in LDS.
+template <int RP>
 __global__ __launch_bounds__(256) void dora_norm_kernel(const float* __restrict__ w0sq,
                                                         const float* __restrict__ P0,
                                                         const float* __restrict__ Gram,
@@ -58,21 +62,61 @@ __global__ __launch_bounds__(256) void dora_norm_kernel(const float* __restrict_
   __shared__ float G[kMaxRankCols * kMaxRankCols];
   for (int i = threadIdx.x; i < r * r; i += 256) G[i] = Gram[i];
   __syncthreads();
-  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  const uint16_t* b = B + n * r;
+  const int i = threadIdx.x % RP;
+  const int64_t n = (int64_t)blockIdx.x * (256 / RP) + threadIdx.x / RP;
+  const int64_t nn = n < N ? n : N - 1;
+  const uint16_t* b = B + nn * r;
   float cross = 0.0f, quad = 0.0f;
-  for (int i = 0; i < r; ++i) {
+  if (i < r) {
     const float bi = bf16_to_f32(b[i]);
-    cross += P0[n * r + i] * bi;
     float gb = 0.0f;
     for (int j = 0; j < r; ++j) gb += G[i * r + j] * bf16_to_f32(b[j]);
-    quad += bi * gb;
+    quad = bi * gb;
+    cross = P0[nn * r + i] * bi;
   }
-  const float c2 = w0sq[n] + 2.0f * s * cross + s * s * quad;
-  const float cn = sqrtf(fmaxf(c2, 0.0f));
-  c[n] = cn;
-  g[n] = m[n] / cn;
+#pragma unroll
+  for (int o = RP / 2; o >= 1; o >>= 1) {
+    quad += __shfl_xor(quad, o);
+    cross += __shfl_xor(cross, o);
+  }
+  if (i == 0 && n < N) {
+    const float c2 = w0sq[n] + 2.0f * s * cross + s * s * quad;
+    const float cn = sqrtf(fmaxf(c2, 0.0f));
+    c[n] = cn;
+    g[n] = m[n] / cn;
+  }
+}
+
+// Partial Gram matrices A A^T over 256-column chunks of A (r x K, bf16): the
+// chunk is staged in LDS, and each thread forms whole entries of the r x r
+// partial.
+constexpr int kGramCols = 256;
+
+__global__ __launch_bounds__(256) void gram_part_kernel(const uint16_t* __restrict__ A, int r,
+                                                        int64_t K, float* __restrict__ part) {
+  __shared__ uint16_t As[kMaxRankCols][kGramCols + 2];
+  const int64_t k0 = (int64_t)blockIdx.x * kGramCols;
+  const int64_t cols = K - k0 < kGramCols ? K - k0 : kGramCols;
+  for (int e = threadIdx.x; e < r * kGramCols; e += 256) {
+    const int j = e / kGramCols, k = e % kGramCols;
+    As[j][k] = k < cols ? A[(int64_t)j * K + k0 + k] : (uint16_t)0;
+  }
+  __syncthreads();
+  float* out = part + (int64_t)blockIdx.x * r * r;
+  for (int p = threadIdx.x; p < r * r; p += 256) {
+    const int i = p / r, j = p - i * r;
+    float acc = 0.0f;
+    for (int k = 0; k < kGramCols; ++k) acc += bf16_to_f32(As[i][k]) * bf16_to_f32(As[j][k]);
+    out[p] = acc;
+  }
+}
+
+// g = m / c from saved row norms (the same division the norm kernel does).
+__global__ __launch_bounds__(256) void dora_g_kernel(const float* __restrict__ m,
+                                                     const float* __restrict__ c, int64_t N,
+                                                     float* __restrict__ g) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n < N) g[n] = m[n] / c[n];
 }
 
 // Y[m][n] = bf16(Z[m][n] g[n]), 16-byte chunks (N % 8 == 0).
@@ -100,9 +144,9 @@ __global__ __launch_bounds__(256) void col_scale_kernel(const uint16_t* __restri
 }
 
 // G'[m][n] = bf16(dY[m][n] g[n]) and the partial column sums
-// hpart[t][n] = sum over the 64 rows of tile t of dY[m][n] Z[m][n].
-// A workgroup covers 2048 columns (8 per thread) of one 64-row tile.
-constexpr int kHRows = 64, kHCols = 2048;
+// hpart[t][n] = sum over the 16 rows of tile t of dY[m][n] Z[m][n].
+// A workgroup covers 2048 columns (8 per thread) of one 16-row tile.
+constexpr int kHRows = 16, kHCols = 2048;
 
 __global__ __launch_bounds__(256) void dora_gprep_kernel(const uint16_t* __restrict__ dY,
                                                          const uint16_t* __restrict__ Z,
@@ -155,8 +199,9 @@ __global__ __launch_bounds__(256) void dora_gprep_kernel(const uint16_t* __restr
   *reinterpret_cast<f32x4*>(hp + 4) = f32x4{h[4], h[5], h[6], h[7]};
 }
 
-// h_n from the tile partials (fixed order), dm = h / c, kappa = -h g / c^2,
-// KB[n][j] = kappa_n B[n][j].
+// h_n from the tile partials, dm = h / c, kappa = -h g / c^2,
+// KB[n][j] = kappa_n B[n][j].  A workgroup owns 64 columns; its four thread
+// groups add every fourth tile, then the four sums are added in a fixed order.
 __global__ __launch_bounds__(256) void dora_hfin_kernel(const float* __restrict__ hpart,
                                                         int tiles, int64_t N,
                                                         const float* __restrict__ c,
@@ -165,47 +210,88 @@ __global__ __launch_bounds__(256) void dora_hfin_kernel(const float* __restrict_
                                                         float* __restrict__ dm, int accumulate,
                                                         float* __restrict__ kappa,
                                                         float* __restrict__ KB) {
-  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  float h = 0.0f;
-  for (int t = 0; t < tiles; ++t) h += hpart[(int64_t)t * N + n];
-  const float cn = c[n];
-  const float d = h / cn;
-  dm[n] = accumulate ? dm[n] + d : d;
-  const float k = -h * g[n] / (cn * cn);
-  kappa[n] = k;
-  for (int j = 0; j < r; ++j) KB[n * r + j] = k * bf16_to_f32(B[n * r + j]);
-}
-
-// R[j][i] = sum_n KB[n][j] B[n][i]: one workgroup per j, rows strided over
-// the threads, then a wave and a cross-wave reduction per i.
-__global__ __launch_bounds__(256) void dora_r_kernel(const float* __restrict__ KB,
-                                                     const uint16_t* __restrict__ B, int64_t N,
-                                                     int r, float* __restrict__ R) {
-  __shared__ float part[4][kMaxRankCols];
-  const int j = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float acc[kMaxRankCols];
-#pragma unroll
-  for (int i = 0; i < kMaxRankCols; ++i) acc[i] = 0.0f;
-  for (int64_t n = threadIdx.x; n < N; n += 256) {
-    const float kb = KB[n * r + j];
-#pragma unroll
-    for (int i = 0; i < kMaxRankCols; ++i)
-      if (i < r) acc[i] += kb * bf16_to_f32(B[n * r + i]);
+  __shared__ float part[4][64];
+  __shared__ float ks[64];
+  const int q = threadIdx.x >> 6, col = threadIdx.x & 63;
+  const int64_t n0 = (int64_t)blockIdx.x * 64;
+  const int64_t n = n0 + col;
+  float h0 = 0.0f, h1 = 0.0f, h2 = 0.0f, h3 = 0.0f;
+  if (n < N) {
+    int t = q;
+    for (; t + 12 < tiles; t += 16) {  // four independent chains of loads
+      h0 += hpart[(int64_t)t * N + n];
+      h1 += hpart[(int64_t)(t + 4) * N + n];
+      h2 += hpart[(int64_t)(t + 8) * N + n];
+      h3 += hpart[(int64_t)(t + 12) * N + n];
+    }
+    for (; t < tiles; t += 4) h0 += hpart[(int64_t)t * N + n];
   }
-#pragma unroll
-  for (int i = 0; i < kMaxRankCols; ++i) {
-    if (i >= r) break;
-    float v = acc[i];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    if (lane == 0) part[wave][i] = v;
+  part[q][col] = (h0 + h1) + (h2 + h3);
+  __syncthreads();
+  if (q == 0) {
+    float k = 0.0f;
+    if (n < N) {
+      const float hs = ((part[0][col] + part[1][col]) + part[2][col]) + part[3][col];
+      const float cn = c[n];
+      const float d = hs / cn;
+      dm[n] = accumulate ? dm[n] + d : d;
+      k = -hs * g[n] / (cn * cn);
+      kappa[n] = k;
+    }
+    ks[col] = k;
   }
   __syncthreads();
-  if (threadIdx.x < r)
-    R[j * r + threadIdx.x] = part[0][threadIdx.x] + part[1][threadIdx.x] +
-                             part[2][threadIdx.x] + part[3][threadIdx.x];
+  // KB for the workgroup's 64 rows: 64 r consecutive floats
+  const int64_t rows = N - n0 < 64 ? N - n0 : 64;
+  for (int64_t i = threadIdx.x; i < rows * r; i += 256)
+    KB[n0 * r + i] = ks[i / r] * bf16_to_f32(B[n0 * r + i]);
+}
+
+// R[j][i] = sum_n KB[n][j] B[n][i] in two steps: each workgroup stages 64
+// rows of KB and B in LDS and writes the partial r x r sum of its rows; a
+// second kernel adds the partials in block order.
+constexpr int kRRows = 64;
+
+__global__ __launch_bounds__(256) void dora_rpart_kernel(const float* __restrict__ KB,
+                                                         const uint16_t* __restrict__ B,
+                                                         int64_t N, int r,
+                                                         float* __restrict__ Rpart) {
+  __shared__ float Ks[kRRows][kMaxRankCols + 1];
+  __shared__ float Bs[kRRows][kMaxRankCols + 1];
+  const int64_t n0 = (int64_t)blockIdx.x * kRRows;
+  const int64_t rows = N - n0 < kRRows ? N - n0 : kRRows;
+  for (int i = threadIdx.x; i < kRRows * r; i += 256) {
+    const bool ok = i / r < rows;
+    Ks[i / r][i % r] = ok ? KB[n0 * r + i] : 0.0f;
+    Bs[i / r][i % r] = ok ? bf16_to_f32(B[n0 * r + i]) : 0.0f;
+  }
+  __syncthreads();
+  float* out = Rpart + (int64_t)blockIdx.x * r * r;
+  for (int p = threadIdx.x; p < r * r; p += 256) {
+    const int j = p / r, i = p - j * r;
+    float acc = 0.0f;
+    for (int k = 0; k < kRRows; ++k) acc += Ks[k][j] * Bs[k][i];
+    out[p] = acc;
+  }
+}
+
+// Sums blocks partial r x r matrices in a fixed order (also the Gram partials).
+__global__ __launch_bounds__(256) void dora_rsum_kernel(const float* __restrict__ Rpart,
+                                                        int blocks, int r,
+                                                        float* __restrict__ R) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= r * r) return;
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+  const int64_t rr = (int64_t)r * r;
+  int b = 0;
+  for (; b + 3 < blocks; b += 4) {  // four independent chains of loads
+    a0 += Rpart[b * rr + p];
+    a1 += Rpart[(b + 1) * rr + p];
+    a2 += Rpart[(b + 2) * rr + p];
+    a3 += Rpart[(b + 3) * rr + p];
+  }
+  for (; b < blocks; ++b) a0 += Rpart[b * rr + p];
+  R[p] = (a0 + a1) + (a2 + a3);
 }
 
 // The remaining kappa terms: index space r K (dA) then N r (dB).
@@ -249,10 +335,32 @@ int dora_weight_side(const void* Wd, int64_t N, int64_t K, const void* A, const 
                      (const uint16_t*)Wd, N, K, d.w0sq);
   if ((e = hip_fail(hipGetLastError(), "rowsumsq launch"))) return e;
   if ((e = t_only(Wd, N, K, A, r, d.P0, st, nullptr, 0))) return e;      // W0 A^T
-  if ((e = t_only(A, r, K, A, r, d.Gram, st, nullptr, 0))) return e;     // A A^T
-  hipLaunchKernelGGL(dora_norm_kernel, dim3((unsigned)cdiv(N, 256)), dim3(256), 0, st, d.w0sq,
-                     d.P0, d.Gram, (const uint16_t*)B, m, N, (int)r, s, d.c, d.g);
+  const int gblocks = dora_gblocks(K);  // A A^T: chunk partials, then their sum
+  hipLaunchKernelGGL(gram_part_kernel, dim3((unsigned)gblocks), dim3(256), 0, st,
+                     (const uint16_t*)A, (int)r, K, d.Gpart);
+  if ((e = hip_fail(hipGetLastError(), "gram_part launch"))) return e;
+  hipLaunchKernelGGL(dora_rsum_kernel, dim3((unsigned)cdiv(r * r, 256)), dim3(256), 0, st,
+                     d.Gpart, gblocks, (int)r, d.Gram);
+  if ((e = hip_fail(hipGetLastError(), "gram sum launch"))) return e;
+  const unsigned nb16 = (unsigned)cdiv(N, 16), nb8 = (unsigned)cdiv(N, 8),
+                 nb4 = (unsigned)cdiv(N, 4);
+  const uint16_t* Bh = (const uint16_t*)B;
+  if (r <= 16)
+    hipLaunchKernelGGL(dora_norm_kernel<16>, dim3(nb16), dim3(256), 0, st, d.w0sq, d.P0, d.Gram,
+                       Bh, m, N, (int)r, s, d.c, d.g);
+  else if (r <= 32)
+    hipLaunchKernelGGL(dora_norm_kernel<32>, dim3(nb8), dim3(256), 0, st, d.w0sq, d.P0, d.Gram,
+                       Bh, m, N, (int)r, s, d.c, d.g);
+  else
+    hipLaunchKernelGGL(dora_norm_kernel<64>, dim3(nb4), dim3(256), 0, st, d.w0sq, d.P0, d.Gram,
+                       Bh, m, N, (int)r, s, d.c, d.g);
   return hip_fail(hipGetLastError(), "dora_norm launch");
+}
+
+int dora_g_from_c(const float* m, const DoraSide& d, int64_t N, hipStream_t st) {
+  hipLaunchKernelGGL(dora_g_kernel, dim3((unsigned)cdiv(N, 256)), dim3(256), 0, st, m, d.c, N,
+                     d.g);
+  return hip_fail(hipGetLastError(), "dora_g launch");
 }
 
 int launch_col_scale(const void* Z, const float* g, int64_t M, int64_t N, void* Y,
@@ -266,6 +374,10 @@ int launch_col_scale(const void* Z, const float* g, int64_t M, int64_t N, void* 
 
 int dora_tiles(int64_t M) { return (int)cdiv(M, kHRows); }
 
+int dora_rblocks(int64_t N) { return (int)cdiv(N, kRRows); }
+
+int dora_gblocks(int64_t K) { return (int)cdiv(K, kGramCols); }
+
 int dora_grad_side(const void* dY, const void* Z, const float* m, const void* B, int64_t M,
                    int64_t N, int64_t r, const DoraSide& d, const DoraGrad& q, float* dm,
                    int accumulate, hipStream_t st) {
@@ -277,7 +389,7 @@ int dora_grad_side(const void* dY, const void* Z, const float* m, const void* B,
                      (const uint16_t*)dY, (const uint16_t*)Z, d.g, M, N, col_groups, q.Gp,
                      q.hpart);
   if ((e = hip_fail(hipGetLastError(), "dora_gprep launch"))) return e;
-  hipLaunchKernelGGL(dora_hfin_kernel, dim3((unsigned)cdiv(N, 256)), dim3(256), 0, st, q.hpart,
+  hipLaunchKernelGGL(dora_hfin_kernel, dim3((unsigned)cdiv(N, 64)), dim3(256), 0, st, q.hpart,
                      tiles, N, d.c, d.g, (const uint16_t*)B, (int)r, dm, accumulate, q.kappa, q.KB);
   return hip_fail(hipGetLastError(), "dora_hfin launch");
 }
@@ -285,9 +397,13 @@ int dora_grad_side(const void* dY, const void* Z, const float* m, const void* B,
 int dora_fix(const void* Wd, const void* A, const void* B, int64_t N, int64_t K, int64_t r,
              float s, const DoraSide& d, const DoraGrad& q, float* dA, float* dB, hipStream_t st) {
   int e;
-  hipLaunchKernelGGL(dora_r_kernel, dim3((unsigned)r), dim3(256), 0, st, q.KB,
-                     (const uint16_t*)B, N, (int)r, q.R);
-  if ((e = hip_fail(hipGetLastError(), "dora_r launch"))) return e;
+  const int rblocks = dora_rblocks(N);
+  hipLaunchKernelGGL(dora_rpart_kernel, dim3((unsigned)rblocks), dim3(256), 0, st, q.KB,
+                     (const uint16_t*)B, N, (int)r, q.Rpart);
+  if ((e = hip_fail(hipGetLastError(), "dora_rpart launch"))) return e;
+  hipLaunchKernelGGL(dora_rsum_kernel, dim3((unsigned)cdiv(r * r, 256)), dim3(256), 0, st,
+                     q.Rpart, rblocks, (int)r, q.R);
+  if ((e = hip_fail(hipGetLastError(), "dora_rsum launch"))) return e;
   // dA += s (kappa B)^T W0: the gradient reduction over the N rows of W0
   if ((e = grad_one(Wd, q.KB, N, K, (int)r, s, dA, q.part, st))) return e;
   const int64_t total = r * K + N * r;

@@ -69,7 +69,8 @@ _SIGS = {
     "lq_dora_fwd": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i64, _f32, _vp, _i32, _vp, _vp, _vp,
                                    _vp, _vp, _sz, _vp]),
     "lq_dora_bwd": (ctypes.c_int, [_vp, _vp, _i64, _WP, _vp, _vp, _i64, _f32, _vp, _i32, _vp, _vp,
-                                   _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
+                                   _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "lq_dora_saved_floats": (_i64, [_i64, _i64]),
     "lq_lora_fwd_dropout": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i64, _f32, _vp, _f32, _i32,
                                            _vp, _vp, _vp, _sz, _vp]),
     "lq_lora_bwd_dropout": (ctypes.c_int, [_vp, _vp, _i64, _WP, _vp, _vp, _i64, _f32, _vp, _f32,
@@ -321,10 +322,16 @@ def lq_lora_bwd_dropout(dY, X, W0, A, B, scale, keep, p, T_saved=None, need_dx=T
     return dX, dA, dB
 
 
-def lq_dora_fwd(X, W0, A, B, scale, magnitude, Z_out=None, T_out=None, norm_out=None, ws=None,
+def lq_dora_saved_floats(N, r):
+    return int(lib().lq_dora_saved_floats(N, r))
+
+
+def lq_dora_fwd(X, W0, A, B, scale, magnitude, Z_out=None, T_out=None, saved_out=None, ws=None,
                 Y=None, fused=False):
-    """DoRA forward; returns Y.  Pass Z_out (M x N bf16) to keep Z for lq_dora_bwd."""
-    _dev(X, A, B, magnitude, Z_out, T_out, norm_out, ws, Y)
+    """DoRA forward; returns Y.  Pass Z_out (M x N bf16) to keep Z for lq_dora_bwd, and
+    saved_out (lq_dora_saved_floats(N, r) float32; its first N entries are the row norms)
+    to hand the weight-side results to it."""
+    _dev(X, A, B, magnitude, Z_out, T_out, saved_out, ws, Y)
     dt = _dt(X)
     M = X.shape[0]
     w = weight_struct(W0, dt)
@@ -336,13 +343,14 @@ def lq_dora_fwd(X, W0, A, B, scale, magnitude, Z_out=None, T_out=None, norm_out=
         ws = _ws(lq_workspace_size(op, M, w.N, w.K, r), X.device)
     _check(lib().lq_dora_fwd(_ptr(X), M, ctypes.byref(w), _ptr(A), _ptr(B), r, scale,
                              _ptr(magnitude), dt, _ptr(Y), _ptr(Z_out), _ptr(T_out),
-                             _ptr(norm_out), _ptr(ws), ws.numel(), _stream()))
+                             _ptr(saved_out), _ptr(ws), ws.numel(), _stream()))
     return Y
 
 
-def lq_dora_bwd(dY, X, W0, A, B, scale, magnitude, Z_saved, T_saved=None, need_dx=True, dA=None,
-                dB=None, dmag=None, accumulate=False, ws=None, dX=None, fused=False):
-    _dev(dY, X, A, B, magnitude, Z_saved, T_saved, dA, dB, dmag, ws, dX)
+def lq_dora_bwd(dY, X, W0, A, B, scale, magnitude, Z_saved, T_saved=None, saved=None,
+                need_dx=True, dA=None, dB=None, dmag=None, accumulate=False, ws=None, dX=None,
+                fused=False):
+    _dev(dY, X, A, B, magnitude, Z_saved, T_saved, saved, dA, dB, dmag, ws, dX)
     dt = _dt(dY)
     M = dY.shape[0]
     w = weight_struct(W0, dt)
@@ -360,7 +368,8 @@ def lq_dora_bwd(dY, X, W0, A, B, scale, magnitude, Z_saved, T_saved=None, need_d
         op = LQ_OP_DORA_BWD_FUSED if fused else LQ_OP_DORA_BWD
         ws = _ws(lq_workspace_size(op, M, w.N, w.K, r), dev)
     _check(lib().lq_dora_bwd(_ptr(dY), _ptr(X), M, ctypes.byref(w), _ptr(A), _ptr(B), r, scale,
-                             _ptr(magnitude), dt, _ptr(Z_saved), _ptr(T_saved), _ptr(dX),
+                             _ptr(magnitude), dt, _ptr(Z_saved), _ptr(T_saved), _ptr(saved),
+                             _ptr(dX),
                              _ptr(dA), _ptr(dB), _ptr(dmag), int(accumulate), _ptr(ws),
                              ws.numel(), _stream()))
     return dX, dA, dB, dmag

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(lq.LIB_PATH),
 
 def test_exports_every_declared_symbol():
     declared = lq.declared_symbols()
-    assert len(declared) == 19
+    assert len(declared) == 20
     L = lq.lib()
     for name in declared:
         assert hasattr(L, name), name
@@ -196,14 +196,15 @@ def test_dora_argument_errors_launch_nothing():
 
     def bwd(dmag=0x1000, Z=0x1000, wsb=big):
         return L.lq_dora_bwd(0x1000, 0x1000, 64, ctypes.byref(w), 0x1000, 0x1000, 8, 2.0, 0x1000,
-                             lq.LQ_BF16, Z, None, 0x1000, 0x1000, 0x1000, dmag, 0, 0x1000, wsb,
-                             None)
+                             lq.LQ_BF16, Z, None, None, 0x1000, 0x1000, 0x1000, dmag, 0, 0x1000,
+                             wsb, None)
     assert fwd(mag=None) == -1
     assert fwd(dt=lq.LQ_F32) == -2
     assert fwd(wsb=1000) == -3
     assert fwd(M=0, mag=None) == 0
     assert bwd(dmag=None) == -1 and bwd(Z=None) == -1
     assert bwd(wsb=1000) == -3
+    assert lq.lq_dora_saved_floats(4096, 16) == 4096 + 4096 * 16 + 256
     for op in (lq.LQ_OP_DORA_FWD, lq.LQ_OP_DORA_BWD):
         assert (lq.lq_workspace_size(op, 2048, 4096, 4096, 16)
                 > lq.lq_workspace_size(op + 1, 2048, 4096, 4096, 16) > 4096 * 4096 * 2)

@@ -37,10 +37,15 @@ def run(c, kind, fused, label, rows=None):
     m = torch.from_numpy(m_np).to(DEV)
     Z = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     T = torch.empty((M, r), dtype=torch.float32, device=DEV)
-    cn = torch.empty(N, dtype=torch.float32, device=DEV)
-    Y = lq.lq_dora_fwd(X, Wd, A, B, s, m, Z_out=Z, T_out=T, norm_out=cn, fused=fused)
+    sv = torch.empty(lq.lq_dora_saved_floats(N, r), dtype=torch.float32, device=DEV)
+    cn = sv[:N]
+    Y = lq.lq_dora_fwd(X, Wd, A, B, s, m, Z_out=Z, T_out=T, saved_out=sv, fused=fused)
     dX, dA, dB, dm = lq.lq_dora_bwd(dY, X, Wd, A, B, s, m, Z, T_saved=T, fused=fused)
+    # with the forward's weight-side results the backward is the same bits
+    res = lq.lq_dora_bwd(dY, X, Wd, A, B, s, m, Z, T_saved=T, saved=sv, fused=fused)
     torch.cuda.synchronize()
+    for name, a, b in zip(("dX", "dA", "dB", "dm"), (dX, dA, dB, dm), res):
+        assert torch.equal(a, b), f"{name}: saved weight side gives other bits"
     Xo, Ao, Bo, dYo = c["X"].f64(), c["A"].f64(), c["B"].f64(), c["dY"].f64()
     sel = np.arange(M) if rows is None else rows
     Yo, Zo, co = olora.dora_forward(Xo[sel], Wo, Ao, Bo, s, m_np)
