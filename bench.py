@@ -9,7 +9,9 @@ Default run (python bench.py [--steps K] [--warmup W]):
   with the expand.  Backward: the same for dX (U = dY B), then the dA / dB
   reductions.  value = algorithmic fwd+bwd FLOPs / wall time per step, the
   step launched eagerly (the same step replayed from a HIP graph is reported
-  beside it: on this stack the replay is not faster).
+  beside it: on this stack the replay is not faster).  The default 200 timed
+  steps (about 40 ms) make the start-up of the timed region (about 1 ms in
+  all, measured) negligible; with 50 steps it would add 20 us to each.
 * roofline: the dominant kernel -- the large-tile product of the forward or
   of dX, whichever is slower (each does 2 M N K + 2 M N r FLOPs: the product
   and the rank-r expand) -- timed with HIP events that the library records
@@ -20,7 +22,8 @@ Default run (python bench.py [--steps K] [--warmup W]):
   on the current kernel source.
 * cpu_baseline: the CPU oracle (float64 NumPy) on the same step.
 * secondary lines in the same JSON object: NF4 decode (M = 1, 4, 16) GB/s on
-  the weight stream with cold weights, merge, quantise, multi-adapter.
+  the weight stream with cold weights, merge, quantise, multi-adapter, the
+  step with LoRA-input dropout and as DoRA, and the AdamW step.
 
 Profiling helpers (for rocprofv3): --mode fwd | dx | step | decode | copy | quant
 run only that part, a few iterations, and print one line.
@@ -354,8 +357,8 @@ def secondary(S, torch):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--mode", default="full",
                     choices=["full", "step", "fwd", "dx", "decode", "copy", "quant"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
