@@ -148,19 +148,17 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int r = p.r;
 
-  // expand inputs: element tid of T (M x r <= 1024) and of B rows n0.. (16 x r)
+  // expand inputs: element tid of T (M x r <= 1024) and of B rows n0.. (16 x r),
+  // loaded without branches (clamped index; threads past the end load a valid
+  // element and drop it), so that no wait for them is placed before the
+  // weight stream
   const int ET = (int)M * r, EB = 16 * r;
+  const int te = tid < ET ? tid : ET - 1, tb = tid < EB ? tid : EB - 1;
   float tp[kTParts];
-  uint32_t braw = 0u;
 #pragma unroll
-  for (int b = 0; b < kTParts; ++b) tp[b] = 0.0f;
-  if (tid < ET) {  // threads without an element issue no load
-#pragma unroll
-    for (int b = 0; b < kTParts; ++b) tp[b] = p.Tp[b * ET + tid];
-  }
-  if (tid < EB) braw = p.B[n0 * r + tid];
+  for (int b = 0; b < kTParts; ++b) tp[b] = p.Tp[b * ET + te];
+  const uint16_t braw = p.B[n0 * r + tb];
 
-  if (WK != kDense) build_lut(lut, p.tab);
   const int64_t n = n0 + l16;  // A-operand row of this lane (N % 16 == 0)
   const bool mrow = l16 < M;   // B-operand column (activation row) of this lane
   const int64_t xm = mrow ? l16 : 0;
@@ -169,13 +167,13 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
   for (int i = 0; i < CH; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const int64_t G = K / 32;
   const int64_t steps = (G + 3) / 4;
-  if (WK != kDense) __syncthreads();  // level table
-  for (int64_t base = wave; base < steps; base += kGemvWaves * CH) {
-    u32x4 wraw[CH][WK == kDense ? 4 : 1];
-    uint32_t sq[CH];
-    float sc2[CH];
-    u32x4 xf[CH][4];
-    bool ok[CH];
+  u32x4 wraw[CH][WK == kDense ? 4 : 1];
+  uint32_t sq[CH];
+  float sc2[CH];
+  u32x4 xf[CH][4];
+  bool ok[CH];
+  // one round of granule loads (clamped addresses; granules past the end masked)
+  auto load = [&](int64_t base) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int64_t t = base + kGemvWaves * i;
@@ -196,14 +194,24 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
           sq[i] = __float_as_uint(p.W.absmax[e >> 6]);
         }
       }
+      // every lane loads (lanes without an activation row read row 0 and are
+      // masked at the product): no branch, so no wait at a join
 #pragma unroll
-      for (int d = 0; d < 4; ++d) xf[i][d] = u32x4{0u, 0u, 0u, 0u};
-      if (mrow) {  // lanes without an activation row issue no load
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          xf[i][d] = *reinterpret_cast<const u32x4*>(p.X + xm * K + k + 8 * d);
-      }
+      for (int d = 0; d < 4; ++d)
+        xf[i][d] = *reinterpret_cast<const u32x4*>(p.X + xm * K + k + 8 * d);
+      ok[i] = ok[i] && mrow;
     }
+  };
+  // The first round's loads go out before the level table is built, so that
+  // their memory latency overlaps the table and its barrier (every wave
+  // issues them; a wave with no granule loads clamped addresses and masks).
+  load(wave);
+  if (WK != kDense) {
+    build_lut(lut, p.tab);
+    __syncthreads();  // level table
+  }
+  for (int64_t base = wave; base < steps; base += kGemvWaves * CH) {
+    if (base != wave) load(base);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       if (WK == kDense) {
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
   }
   if (tid < EB) {
     const int nn = tid / r, j = tid - nn * r;
-    tB[nn * 64 + j] = bf16_to_f32((uint16_t)braw);
+    tB[nn * 64 + j] = bf16_to_f32(braw);
   }
   // acc lane l: rows n0 + 4 q + i, column m = l16 (16x16 accumulator layout)
   f32x4 a0 = acc[0];
@@ -297,12 +305,12 @@ __global__ __launch_bounds__(kThreads) void tpart_kernel(const uint16_t* __restr
         const int j = 16 * jt + l16;
         af[i][jt] = *reinterpret_cast<const u32x4*>(A + (int64_t)(j < r ? j : 0) * K + k);
       }
-      xf[i] = u32x4{0u, 0u, 0u, 0u};
-      if (mrow) xf[i] = *reinterpret_cast<const u32x4*>(X + xm * K + k);
+      // every lane loads (rows past M read row 0, masked below): no branch
+      xf[i] = *reinterpret_cast<const u32x4*>(X + xm * K + k);
     }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const u32x4 x = sel4(ok[i], xf[i]);
+      const u32x4 x = sel4(ok[i] && mrow, xf[i]);
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
         acc[jt] = mfma16(sel4(16 * jt + l16 < r, af[i][jt]), x, acc[jt]);
