@@ -204,7 +204,8 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(GradParams p) {
 }
 
 // Both reductions' finishing pass: out = s * sum_split P[split] (+ out if
-// accumulate), the split partials added in a fixed order.  Index space: dA
+// accumulate), the split partials added in a fixed order (four interleaved
+// chains, then their pairwise sum).  Index space: dA
 // (r x K, out[j][c]) then dB (N x r, out[c][j]).
 struct ReduceParams {
   const float* P[2];
@@ -232,9 +233,19 @@ __global__ void grad_reduce_kernel(ReduceParams p) {
     j = i / C;
     c = i - j * C;
   }
-  const float* P = p.P[jb];
-  float sum = 0.0f;
-  for (int t = 0; t < p.splits[jb]; ++t) sum += P[(int64_t)t * total + j * C + c];
+  const float* P = p.P[jb] + j * C + c;
+  const int ns = p.splits[jb];
+  // four independent chains of loads, added in a fixed order
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  int t = 0;
+  for (; t + 3 < ns; t += 4) {
+    s0 += P[(int64_t)t * total];
+    s1 += P[(int64_t)(t + 1) * total];
+    s2 += P[(int64_t)(t + 2) * total];
+    s3 += P[(int64_t)(t + 3) * total];
+  }
+  for (; t < ns; ++t) s0 += P[(int64_t)t * total];
+  const float sum = (s0 + s1) + (s2 + s3);
   float v = p.s * sum;
   if (p.accumulate) v += p.out[jb][i];
   p.out[jb][i] = v;

@@ -223,6 +223,128 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs pa, const uint16_t* 
     shrink_rows<JT, GT, 4>((int64_t)blockIdx.x - pa.nd, Z, M, K, G, r, out, row_ad, mt);
 }
 
+// Wide shrink (out = Z G^T with G = A, 16 < r <= 64) for many rows: a
+// workgroup of four waves owns 128 rows and all RC = 32 JC rank columns.  Per
+// 64-wide reduction step the rank tile (RC rows of 128 bytes) is staged in LDS
+// once and shared by the four waves -- the rows-per-workgroup of the kernel
+// above would re-read all of A for every 16 rows.  Each wave loads its 32
+// activation rows straight into MFMA registers: lane (h, l32) takes row l32
+// and the 64 contiguous bytes 64 h .. of the step, so substep s of
+// v_mfma_f32_32x32x16_bf16 reduces elements 32 h + 8 s .. + 7 on both operands
+// (the rank tile is read with the same relabelling).  Rank-tile chunk c of
+// row j sits at chunk c ^ (j & 7) in LDS, so the 32 lanes of one read hit
+// distinct bank groups.  The next step's tiles are loaded into registers
+// before the current step's products.
+constexpr int kWRows = 128;
+
+template <int JC>
+__global__ __launch_bounds__(256) void shrink_wide_kernel(const uint16_t* __restrict__ Z,
+                                                          int64_t M, int64_t K,
+                                                          const uint16_t* __restrict__ G, int r,
+                                                          float* __restrict__ out,
+                                                          int32_t* __restrict__ zero, int nzero,
+                                                          const int32_t* __restrict__ row_ad,
+                                                          MultiTab mt) {
+  constexpr int RC = 32 * JC;
+  constexpr int GL = RC * 8 / 256;  // 16-byte rank-tile loads per thread per step
+  __shared__ __attribute__((aligned(16))) uint16_t gt[2][RC * 64];
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nzero; i += 256) zero[i] = 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t m0 = (int64_t)blockIdx.x * kWRows + 32 * wave;
+  const int64_t mz = m0 + l32 < M ? m0 + l32 : M - 1;
+  const uint16_t* zrow = Z + mz * K + 32 * h;
+  // rank-tile loads: piece e = tid + 256 i -> row e / 8 (clamped to r - 1), chunk e % 8
+  const uint16_t* grow[GL];
+  uint32_t gst[GL];
+#pragma unroll
+  for (int i = 0; i < GL; ++i) {
+    const int e = tid + 256 * i, row = e >> 3, ch = e & 7;
+    grow[i] = G + (int64_t)(row < r ? row : r - 1) * K + 8 * ch;
+    gst[i] = (uint32_t)(row * 64 + 8 * (ch ^ (row & 7)));
+  }
+  f32x16 acc[JC];
+#pragma unroll
+  for (int jc = 0; jc < JC; ++jc)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[jc][v] = 0.0f;
+  const int64_t steps = K / 64;
+  u32x4 zc[4], zn[4], gc[GL];
+  auto zload = [&](int64_t kt, u32x4 (&z)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) z[s] = *reinterpret_cast<const u32x4*>(zrow + kt * 64 + 8 * s);
+  };
+  auto gload = [&](int64_t kt) {
+#pragma unroll
+    for (int i = 0; i < GL; ++i) gc[i] = *reinterpret_cast<const u32x4*>(grow[i] + kt * 64);
+  };
+  auto gstore = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < GL; ++i) *reinterpret_cast<u32x4*>(&gt[b][gst[i]]) = gc[i];
+  };
+  zload(0, zc);
+  gload(0);
+  gstore(0);
+  __syncthreads();
+  for (int64_t kt = 0; kt < steps; ++kt) {
+    const int b = (int)(kt & 1);
+    const bool more = kt + 1 < steps;
+    if (more) {
+      zload(kt + 1, zn);
+      gload(kt + 1);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int jc = 0; jc < JC; ++jc) {
+        const int j = 32 * jc + l32;
+        const u32x4 gf = *reinterpret_cast<const u32x4*>(&gt[b][j * 64 + 8 * ((4 * h + s) ^ (j & 7))]);
+        acc[jc] = mfma32(zc[s], gf, acc[jc]);
+      }
+    }
+    if (more) {
+      gstore(b ^ 1);  // the other buffer: its last reads were the previous step's
+#pragma unroll
+      for (int s = 0; s < 4; ++s) zc[s] = zn[s];
+    }
+    __syncthreads();
+  }
+  // acc[jc] lane l: rows m0 + 8 (v / 4) + 4 h + v % 4, column 32 jc + l32
+#pragma unroll
+  for (int jc = 0; jc < JC; ++jc) {
+    const int j = 32 * jc + l32;
+    if (j >= r) continue;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t m = m0 + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (m >= M) continue;
+      float val = acc[jc][v];
+      if (row_ad) {
+        int a = row_ad[m];  // clamped: ids are in range by precondition
+        a = a < 0 ? 0 : (a >= mt.n_ad ? mt.n_ad - 1 : a);
+        val = (j >= mt.roff[a] && j < mt.roff[a + 1]) ? val * mt.scale[a] : 0.0f;
+      }
+      out[m * r + j] = val;
+    }
+  }
+}
+
+bool wide_ok(bool gt, int64_t M, int64_t r) { return !gt && r > 16 && M >= kWRows; }
+
+int launch_wide(const uint16_t* Z, int64_t M, int64_t K, const uint16_t* G, int64_t r, float* out,
+                int32_t* zero, int nzero, const int32_t* row_ad, const MultiTab& mt,
+                hipStream_t st) {
+  const dim3 grid((unsigned)cdiv(M, kWRows)), block(256);
+  if (r <= 32)
+    hipLaunchKernelGGL((shrink_wide_kernel<1>), grid, block, 0, st, Z, M, K, G, (int)r, out, zero,
+                       nzero, row_ad, mt);
+  else
+    hipLaunchKernelGGL((shrink_wide_kernel<2>), grid, block, 0, st, Z, M, K, G, (int)r, out, zero,
+                       nzero, row_ad, mt);
+  return hip_fail(hipGetLastError(), "shrink_wide launch");
+}
+
 template <bool GT>
 int launch(const uint16_t* Z, int64_t M, int64_t K, const uint16_t* G, int64_t r, float* out,
            int32_t* zero, int nzero, const int32_t* row_ad, const MultiTab& mt, hipStream_t st) {
@@ -255,6 +377,9 @@ int launch_shrink(const void* Z, int64_t M, int64_t K, const void* G, bool gt, i
                   const MultiTab* mt) {
   const MultiTab none{};
   const MultiTab& t = mt ? *mt : none;
+  if (wide_ok(gt, M, r))
+    return launch_wide((const uint16_t*)Z, M, K, (const uint16_t*)G, r, out, zero, nzero, row_ad,
+                       t, st);
   if (gt)
     return launch<true>((const uint16_t*)Z, M, K, (const uint16_t*)G, r, out, zero, nzero, row_ad,
                         t, st);
@@ -277,6 +402,17 @@ int launch_prep(const lq_weight& W, void* wout, const void* Z, int64_t M, int64_
   pa.nd = (int32_t)cdiv(pa.n, kDeqSpan);
   pa.wout = (uint16_t*)wout;
   pa.tab = nf4_table(W.codebook);
+  if (wide_ok(gt, M, r)) {
+    // wide rank: the prep launch only dequantises (and clears the flags); the
+    // shrink runs as the wide kernel, which shares the rank tile across 128 rows
+    hipLaunchKernelGGL((prep_kernel<1, false>), dim3((unsigned)pa.nd), dim3(256), 0, st, pa,
+                       (const uint16_t*)Z, (int64_t)0, K, (const uint16_t*)G, (int)r, out, zero,
+                       nzero, row_ad, mtab);
+    int e = hip_fail(hipGetLastError(), "prep launch");
+    if (e) return e;
+    return launch_wide((const uint16_t*)Z, M, K, (const uint16_t*)G, r, out, nullptr, 0, row_ad,
+                       mtab, st);
+  }
   const dim3 grid((unsigned)(pa.nd + cdiv(M, 16))), block(256);
   const uint16_t* Zh = (const uint16_t*)Z;
   const uint16_t* Gh = (const uint16_t*)G;
