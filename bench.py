@@ -23,7 +23,9 @@ Default run (python bench.py [--steps K] [--warmup W]):
 * cpu_baseline: the CPU oracle (float64 NumPy) on the same step.
 * secondary lines in the same JSON object: NF4 decode (M = 1, 4, 16) GB/s on
   the weight stream with cold weights, merge, quantise, multi-adapter, the
-  step with LoRA-input dropout and as DoRA, and the AdamW step.
+  step with LoRA-input dropout and as DoRA, the AdamW step, and forward +
+  backward of config 2 (q and v, bf16, M = 4096, r = 8) and of config 4 (the
+  seven projections of a block, NF4, M = 8192, r = 64).
 
 Profiling helpers (for rocprofv3): --mode fwd | dx | step | decode | copy | quant
 run only that part, a few iterations, and print one line.
@@ -334,6 +336,53 @@ def secondary(S, torch):
     res["dora_step_config3"] = {"ms": round(t, 4),
                                 "TFLOPs": round(STEP_FLOP / (t * 1e-3) / 1e12, 1)}
     del wsof, wsob, Zd
+    # configs 2 and 4 as steps: forward + backward of every linear, inputs drawn on the GPU
+    # from a seeded generator with the workloads' shapes and standard deviations
+    gen = torch.Generator(device=S["dev"]).manual_seed(2024)
+
+    def normal(shape, sigma):
+        return (torch.randn(shape, generator=gen, device=S["dev"]) * sigma).to(torch.bfloat16)
+
+    def linear_step(Mx, Nx, Kx, rx, alpha, nf4):
+        W0 = normal((Nx, Kx), 0.02)
+        Wl = lq.lq_nf4_quantize(W0) if nf4 else W0
+        Al, Bl = normal((rx, Kx), 1.0 / rx ** 0.5), normal((Nx, rx), 0.01)
+        Xl, dYl = normal((Mx, Kx), 1.0), normal((Mx, Nx), 1.0)
+        bufs = dict(Y=torch.empty((Mx, Nx), dtype=torch.bfloat16, device=S["dev"]),
+                    T=torch.empty((Mx, rx), device=S["dev"]),
+                    dX=torch.empty((Mx, Kx), dtype=torch.bfloat16, device=S["dev"]),
+                    dA=torch.empty((rx, Kx), device=S["dev"]),
+                    dB=torch.empty((Nx, rx), device=S["dev"]),
+                    wf=torch.empty(lq.lq_workspace_size(lq.LQ_OP_FWD, Mx, Nx, Kx, rx),
+                                   dtype=torch.uint8, device=S["dev"]),
+                    wb=torch.empty(lq.lq_workspace_size(lq.LQ_OP_BWD, Mx, Nx, Kx, rx),
+                                   dtype=torch.uint8, device=S["dev"]))
+        sl = alpha / rx
+
+        def run():
+            lq.lq_lora_fwd(Xl, Wl, Al, Bl, sl, T_out=bufs["T"], Y=bufs["Y"], ws=bufs["wf"])
+            lq.lq_lora_bwd(dYl, Xl, Wl, Al, Bl, sl, T_saved=bufs["T"], dA=bufs["dA"],
+                           dB=bufs["dB"], ws=bufs["wb"], dX=bufs["dX"])
+        flop = 2 * (2 * Mx * Nx * Kx) + 6 * Mx * rx * (Nx + Kx)
+        return run, flop, (W0, Wl, Al, Bl, Xl, dYl, bufs)
+
+    for name, layers, Mx, rx, alpha, nf4 in (
+            ("config2_qv_bf16_M4096_r8", [(4096, 4096)] * 2, 4096, 8, 16.0, False),
+            ("config4_block_nf4_M8192_r64",
+             [(n, k) for _, n, k in wl.LLAMA_BLOCK], 8192, 64, 128.0, True)):
+        runs, keep, flop = [], [], 0
+        for Nx, Kx in layers:
+            run, f, k = linear_step(Mx, Nx, Kx, rx, alpha, nf4)
+            runs.append(run)
+            keep.append(k)
+            flop += f
+        step_all = lambda: [f() for f in runs]  # noqa: E731
+        step_all()
+        t = cuda_time(step_all, 5, torch)
+        res[name] = {"linears": len(layers), "ms": round(t, 3),
+                     "TFLOPs": round(flop / (t * 1e-3) / 1e12, 1)}
+        del runs, keep
+    torch.cuda.empty_cache()
     # AdamW step on the adapters: float32 master, m, v and gradient, bf16 working
     # copy (16 bytes read and 14 written per parameter)
     for name, sizes in (("adamw_config4_block_r64", wl.config4_adapter_sizes()),
