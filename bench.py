@@ -9,9 +9,10 @@ Default run (python bench.py [--steps K] [--warmup W]):
   with the expand.  Backward: the same for dX (U = dY B), then the dA / dB
   reductions.  value = algorithmic fwd+bwd FLOPs / wall time per step, the
   step launched eagerly (the same step replayed from a HIP graph is reported
-  beside it: on this stack the replay is not faster).  The default 200 timed
-  steps (about 40 ms) make the start-up of the timed region (about 1 ms in
-  all, measured) negligible; with 50 steps it would add 20 us to each.
+  beside it: on this stack the replay is not faster).  The default 1000 timed
+  steps (about 0.2 s) spread the start-up of the timed region (about 1 ms in
+  all, measured) to about 1 us per step; with 50 steps it would add 20 us to
+  each.
 * roofline: the dominant kernel -- the large-tile product of the forward or
   of dX, whichever is slower (each does 2 M N K + 2 M N r FLOPs: the product
   and the rank-r expand) -- timed with HIP events that the library records
@@ -406,8 +407,8 @@ def secondary(S, torch):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--mode", default="full",
                     choices=["full", "step", "fwd", "dx", "decode", "copy", "quant"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")

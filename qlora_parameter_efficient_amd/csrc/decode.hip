@@ -1,15 +1,15 @@
 // Decode-sized forward (M <= 16) and the skinny rank-r products.
 //
-// Decode: Y = X deq(W0)^T + s T B^T with T = X A^T computed first by the
-// skinny kernel.  With at most 16 activation rows the layer is bound by
-// streaming W0 from HBM (4.127 bits per weight in NF4 with double
+// Decode: Y = X deq(W0)^T + s T B^T, with the partial sums of T = X A^T
+// formed first by tpart_kernel.  With at most 16 activation rows the layer is
+// bound by streaming W0 from HBM (4.127 bits per weight in NF4 with double
 // quantisation: "Large Language Model Fine-tuning and LoRA", section
-// "Quantizing the frozen weights"), so the kernel is organised around that
-// stream: a workgroup owns 16 output rows n and its four waves split K; each
-// lane loads 16 code bytes (32 weights, half a block) per step, dequantises
-// them in registers through the LDS level table and feeds four
-// v_mfma_f32_16x16x32_bf16 (X padded to 16 rows).  The four partial sums are
-// combined through LDS; the rank-r expand is a few scalar FMAs per output.
+// "Quantizing the frozen weights"), so gemv_kernel is organised around that
+// stream: a workgroup owns 16 output rows n and its sixteen waves split K;
+// each lane loads 16 code bytes (32 weights, half a block) per granule,
+// dequantises them in registers through the LDS level table and feeds four
+// v_mfma_f32_16x16x32_bf16 (X padded to 16 rows).  The wave partial sums are
+// combined through LDS; the rank-r expand is r scalar FMAs per output.
 //
 // Skinny: out[m][j] = sum_k Z[m][k] G[j][k] for j < r <= 64, G = A (r x K)
 // or B^T (B is K x r here, i.e. the reduction runs over B's rows).  Each wave

@@ -1,4 +1,5 @@
-"""HIP graph capture of the dropout, DoRA and AdamW entry points: every replay
+"""HIP graph capture of the plain forward + backward (decode, fused and
+large-tile paths, dense or NF4 base), dropout, DoRA and AdamW entry points: every replay
 (with eager calls and synchronisation between replays) gives the eager
 result bit for bit.  None of these calls records a memset; the flags and
 partial sums they use are written by kernels."""
@@ -40,6 +41,31 @@ def check_replays(run, outs, names, label):
             assert torch.equal(got, want), f"{label} replay {i}: {name} differs from eager"
         run()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M", [8, 300, 2100], ids=["decode", "fused", "large"])
+@pytest.mark.parametrize("kind", ["dense", "nf4"])
+def test_plain_step_replays(M, kind):
+    N, K, r = 256, 512, 16
+    announce(f"graph plain {kind} M={M}")
+    c = wl.small_case(M, N, K, r, seed=30)
+    s = c["alpha"] / r
+    X, A, B, dY = to_dev(c["X"]), to_dev(c["A"]), to_dev(c["B"]), to_dev(c["dY"])
+    Wd = lq.lq_nf4_quantize(to_dev(c["W0"])) if kind == "nf4" else to_dev(c["W0"])
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    T = torch.empty((M, r), dtype=torch.float32, device=DEV)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    dA = torch.empty((r, K), dtype=torch.float32, device=DEV)
+    dB = torch.empty((N, r), dtype=torch.float32, device=DEV)
+    wsf = torch.empty(lq.lq_workspace_size(lq.LQ_OP_FWD, M, N, K, r), dtype=torch.uint8,
+                      device=DEV)
+    wsb = torch.empty(lq.lq_workspace_size(lq.LQ_OP_BWD, M, N, K, r), dtype=torch.uint8,
+                      device=DEV)
+
+    def run():
+        lq.lq_lora_fwd(X, Wd, A, B, s, T_out=T, Y=Y, ws=wsf)
+        lq.lq_lora_bwd(dY, X, Wd, A, B, s, T_saved=T, dA=dA, dB=dB, ws=wsb, dX=dX)
+    check_replays(run, (Y, T, dX, dA, dB), ("Y", "T", "dX", "dA", "dB"), "plain")
 
 
 @pytest.mark.parametrize("M", [300, 2100], ids=["fused", "large"])
