@@ -28,8 +28,9 @@ decided by float32 comparisons and roundings on both sides.
 
 Modules:
     nf4   -- codebook, quantize / dequantize with double quantization
-    lora  -- forward, backward, merge, segmented multi-adapter forward,
-             trainable-parameter counts
+    lora  -- forward, backward, merge, segmented multi-adapter forward
+             (uniform or per-adapter ranks and scales), LoRA-input dropout,
+             DoRA forward and backward, trainable-parameter counts
     optim -- AdamW step on the adapter factors (float32 master, m, v)
 
 Parity unpinned: none of the functions here is without a pin; what pins
