@@ -132,12 +132,19 @@ struct GemvParams {
 // sums and this workgroup's 16 rows of B) are loaded into registers before
 // the weight stream and only summed and staged in LDS after it; the 16 wave
 // partials are added through LDS.
+// With few activation rows (M K <= 16384 elements, XL) the activations are
+// staged in LDS once per workgroup: loaded straight from global memory, the
+// lanes of a 16-lane group whose row is past M would otherwise all load row 0
+// again, 16 times the bytes of X through each compute unit's load path.
 constexpr int kGemvWaves = 16;
+constexpr int64_t kXStage = 16384;  // bf16 elements of X staged in LDS
 
-template <int WK>
+template <int WK, bool XL>
 __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
   constexpr int CH = 2;
   constexpr int NT = 64 * kGemvWaves;
+  constexpr int XC = XL ? (int)(kXStage / 8 / NT) : 1;  // 16-byte X chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t xs[XL ? kXStage : 8];
   __shared__ float2 lut[256];
   __shared__ f32x4 part[kGemvWaves][64];
   __shared__ float tT[16 * 64];
@@ -147,6 +154,18 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
   const int64_t N = p.W.N, K = p.W.K, M = p.M;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int r = p.r;
+
+  // XL: the chunks of X, issued first so that the wait before their LDS store
+  // does not wait for the weight stream (clamped to the last chunk)
+  const int64_t nxc = M * K / 8;
+  u32x4 xc[XC];
+  if (XL) {
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int64_t c = tid + (int64_t)NT * i;
+      xc[i] = *reinterpret_cast<const u32x4*>(p.X + 8 * (c < nxc ? c : nxc - 1));
+    }
+  }
 
   // expand inputs: element tid of T (M x r <= 1024) and of B rows n0.. (16 x r),
   // loaded without branches (clamped index; threads past the end load a valid
@@ -171,6 +190,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
   uint32_t sq[CH];
   float sc2[CH];
   u32x4 xf[CH][4];
+  int64_t kx[CH];
   bool ok[CH];
   // one round of granule loads (clamped addresses; granules past the end masked)
   auto load = [&](int64_t base) {
@@ -196,9 +216,11 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
       }
       // every lane loads (lanes without an activation row read row 0 and are
       // masked at the product): no branch, so no wait at a join
+      kx[i] = xm * K + k;
+      if (!XL)
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
-        xf[i][d] = *reinterpret_cast<const u32x4*>(p.X + xm * K + k + 8 * d);
+        for (int d = 0; d < 4; ++d)
+          xf[i][d] = *reinterpret_cast<const u32x4*>(p.X + kx[i] + 8 * d);
       ok[i] = ok[i] && mrow;
     }
   };
@@ -206,14 +228,22 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
   // their memory latency overlaps the table and its barrier (every wave
   // issues them; a wave with no granule loads clamped addresses and masks).
   load(wave);
-  if (WK != kDense) {
-    build_lut(lut, p.tab);
-    __syncthreads();  // level table
+  if (XL) {
+    // every thread stores (chunks past M K land in the unread rest of xs):
+    // no branch, so the loads of X stay ahead of the weight stream
+#pragma unroll
+    for (int i = 0; i < XC; ++i) *reinterpret_cast<u32x4*>(xs + 8 * (tid + NT * i)) = xc[i];
   }
+  if (WK != kDense) build_lut(lut, p.tab);
+  if (XL || WK != kDense) __syncthreads();  // level table, staged X
   for (int64_t base = wave; base < steps; base += kGemvWaves * CH) {
     if (base != wave) load(base);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
+      if (XL)
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          xf[i][d] = *reinterpret_cast<const u32x4*>(xs + kx[i] + 8 * d);
       if (WK == kDense) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) acc[i] = mfma16(wraw[i][d], sel4(ok[i], xf[i][d]), acc[i]);
@@ -393,15 +423,19 @@ int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, cons
   p.Y = (uint16_t*)Y;
   p.tab = nf4_table(W.codebook);
   const dim3 grid((unsigned)(W.N / 16)), block(64 * kGemvWaves);
+  const bool xl = M * W.K <= kXStage;
   switch (weight_format(W)) {
     case kDense:
-      hipLaunchKernelGGL(gemv_kernel<kDense>, grid, block, 0, st, p);
+      if (xl) hipLaunchKernelGGL((gemv_kernel<kDense, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gemv_kernel<kDense, false>), grid, block, 0, st, p);
       break;
     case kNF4DQ:
-      hipLaunchKernelGGL(gemv_kernel<kNF4DQ>, grid, block, 0, st, p);
+      if (xl) hipLaunchKernelGGL((gemv_kernel<kNF4DQ, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gemv_kernel<kNF4DQ, false>), grid, block, 0, st, p);
       break;
     default:
-      hipLaunchKernelGGL(gemv_kernel<kNF4>, grid, block, 0, st, p);
+      if (xl) hipLaunchKernelGGL((gemv_kernel<kNF4, true>), grid, block, 0, st, p);
+      else hipLaunchKernelGGL((gemv_kernel<kNF4, false>), grid, block, 0, st, p);
       break;
   }
   return hip_fail(hipGetLastError(), "gemv launch");
