@@ -132,19 +132,24 @@ struct GemvParams {
 // sums and this workgroup's 16 rows of B) are loaded into registers before
 // the weight stream and only summed and staged in LDS after it; the 16 wave
 // partials are added through LDS.
-// With few activation rows (M K <= 16384 elements, XL) the activations are
-// staged in LDS once per workgroup: loaded straight from global memory, the
-// lanes of a 16-lane group whose row is past M would otherwise all load row 0
-// again, 16 times the bytes of X through each compute unit's load path.
+// The activations are staged in LDS once per workgroup (XS > 0: up to XS
+// elements; M K <= 16384 keeps two workgroups per compute unit, up to 65536
+// when the grid has no more workgroups than compute units).  Loaded per lane
+// straight from global memory, the lanes of a 16-lane group whose row is past
+// M would all load row 0 again (16 times the bytes of X through each compute
+// unit's load path at M = 1), and at M = 16 the per-lane 16-byte pieces are
+// scattered over 16 rows.  Staged row m, 16-byte chunk c sits at chunk
+// c ^ (m & 15) of its row (needs K % 128 == 0), so the 16 rows read by one
+// lane group hit 16 distinct bank groups.
 constexpr int kGemvWaves = 16;
-constexpr int64_t kXStage = 16384;  // bf16 elements of X staged in LDS
 
-template <int WK, bool XL>
+template <int WK, int XS>
 __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
+  constexpr bool XL = XS > 0;
   constexpr int CH = 2;
   constexpr int NT = 64 * kGemvWaves;
-  constexpr int XC = XL ? (int)(kXStage / 8 / NT) : 1;  // 16-byte X chunks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t xs[XL ? kXStage : 8];
+  constexpr int XC = XL ? XS / 8 / NT : 1;  // 16-byte X chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t xs[XL ? XS : 8];
   __shared__ float2 lut[256];
   __shared__ f32x4 part[kGemvWaves][64];
   __shared__ float tT[16 * 64];
@@ -156,14 +161,19 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
   const int r = p.r;
 
   // XL: the chunks of X, issued first so that the wait before their LDS store
-  // does not wait for the weight stream (clamped to the last chunk)
-  const int64_t nxc = M * K / 8;
+  // does not wait for the weight stream (clamped to the last chunk; a clamped
+  // thread stores the same value to the same place as the last chunk's owner)
+  const int64_t nxc = M * K / 8, rowc = K / 8;
   u32x4 xc[XC];
+  uint32_t xsto[XC];
   if (XL) {
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
-      const int64_t c = tid + (int64_t)NT * i;
-      xc[i] = *reinterpret_cast<const u32x4*>(p.X + 8 * (c < nxc ? c : nxc - 1));
+      int64_t c = tid + (int64_t)NT * i;
+      c = c < nxc ? c : nxc - 1;
+      xc[i] = *reinterpret_cast<const u32x4*>(p.X + 8 * c);
+      const int64_t m = c / rowc, ch = c - m * rowc;
+      xsto[i] = (uint32_t)(m * K + 8 * (ch ^ (m & 15)));
     }
   }
 
@@ -221,6 +231,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
 #pragma unroll
         for (int d = 0; d < 4; ++d)
           xf[i][d] = *reinterpret_cast<const u32x4*>(p.X + kx[i] + 8 * d);
+      else  // staged: the chunk index of k, before the row swizzle
+        kx[i] = k >> 3;
       ok[i] = ok[i] && mrow;
     }
   };
@@ -228,13 +240,13 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
   // their memory latency overlaps the table and its barrier (every wave
   // issues them; a wave with no granule loads clamped addresses and masks).
   load(wave);
-  if (XL) {
-    // every thread stores (chunks past M K land in the unread rest of xs):
-    // no branch, so the loads of X stay ahead of the weight stream
-#pragma unroll
-    for (int i = 0; i < XC; ++i) *reinterpret_cast<u32x4*>(xs + 8 * (tid + NT * i)) = xc[i];
-  }
   if (WK != kDense) build_lut(lut, p.tab);
+  if (XL) {
+    // every thread stores: no branch, so the loads of X stay ahead of the
+    // weight stream
+#pragma unroll
+    for (int i = 0; i < XC; ++i) *reinterpret_cast<u32x4*>(xs + xsto[i]) = xc[i];
+  }
   if (XL || WK != kDense) __syncthreads();  // level table, staged X
   for (int64_t base = wave; base < steps; base += kGemvWaves * CH) {
     if (base != wave) load(base);
@@ -243,7 +255,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
       if (XL)
 #pragma unroll
         for (int d = 0; d < 4; ++d)
-          xf[i][d] = *reinterpret_cast<const u32x4*>(xs + kx[i] + 8 * d);
+          xf[i][d] = *reinterpret_cast<const u32x4*>(
+              xs + xm * K + 8 * ((kx[i] + d) ^ (xm & 15)));
       if (WK == kDense) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) acc[i] = mfma16(wraw[i][d], sel4(ok[i], xf[i][d]), acc[i]);
@@ -423,20 +436,20 @@ int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, cons
   p.Y = (uint16_t*)Y;
   p.tab = nf4_table(W.codebook);
   const dim3 grid((unsigned)(W.N / 16)), block(64 * kGemvWaves);
-  const bool xl = M * W.K <= kXStage;
-  switch (weight_format(W)) {
-    case kDense:
-      if (xl) hipLaunchKernelGGL((gemv_kernel<kDense, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gemv_kernel<kDense, false>), grid, block, 0, st, p);
-      break;
-    case kNF4DQ:
-      if (xl) hipLaunchKernelGGL((gemv_kernel<kNF4DQ, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gemv_kernel<kNF4DQ, false>), grid, block, 0, st, p);
-      break;
-    default:
-      if (xl) hipLaunchKernelGGL((gemv_kernel<kNF4, true>), grid, block, 0, st, p);
-      else hipLaunchKernelGGL((gemv_kernel<kNF4, false>), grid, block, 0, st, p);
-      break;
+  // staged X: 16384 elements keep two workgroups per compute unit; 65536 only
+  // when the grid has at most one workgroup per compute unit
+  const int64_t mk = M * W.K;
+  const int xs = W.K % 128 ? 0 : mk <= 16384 ? 1 : (mk <= 65536 && W.N / 16 <= 256) ? 2 : 0;
+  switch (weight_format(W) * 3 + xs) {
+    case kDense * 3 + 0: hipLaunchKernelGGL((gemv_kernel<kDense, 0>), grid, block, 0, st, p); break;
+    case kDense * 3 + 1: hipLaunchKernelGGL((gemv_kernel<kDense, 16384>), grid, block, 0, st, p); break;
+    case kDense * 3 + 2: hipLaunchKernelGGL((gemv_kernel<kDense, 65536>), grid, block, 0, st, p); break;
+    case kNF4DQ * 3 + 0: hipLaunchKernelGGL((gemv_kernel<kNF4DQ, 0>), grid, block, 0, st, p); break;
+    case kNF4DQ * 3 + 1: hipLaunchKernelGGL((gemv_kernel<kNF4DQ, 16384>), grid, block, 0, st, p); break;
+    case kNF4DQ * 3 + 2: hipLaunchKernelGGL((gemv_kernel<kNF4DQ, 65536>), grid, block, 0, st, p); break;
+    case kNF4 * 3 + 0: hipLaunchKernelGGL((gemv_kernel<kNF4, 0>), grid, block, 0, st, p); break;
+    case kNF4 * 3 + 1: hipLaunchKernelGGL((gemv_kernel<kNF4, 16384>), grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL((gemv_kernel<kNF4, 65536>), grid, block, 0, st, p); break;
   }
   return hip_fail(hipGetLastError(), "gemv launch");
 }
