@@ -24,7 +24,8 @@ Default run (python bench.py [--steps K] [--warmup W]):
 * cpu_baseline: the CPU oracle (float64 NumPy) on the same step.
 * secondary lines in the same JSON object: NF4 decode (M = 1, 4, 16) GB/s on
   the weight stream with cold weights, merge, quantise, multi-adapter, the
-  step with LoRA-input dropout and as DoRA, the AdamW step, and forward +
+  step with LoRA-input dropout and as DoRA, the AdamW step, the plain bf16
+  GEMMs of the product kernel's shape through torch (context), and forward +
   backward of config 2 (q and v, bf16, M = 4096, r = 8) and of config 4 (the
   seven projections of a block, NF4, M = 8192, r = 64).
 
@@ -279,6 +280,23 @@ def secondary(S, torch):
     t = graph_time(lambda: lq.lq_nf4_dequantize(S["W"], dtype=torch.bfloat16), torch)
     res["nf4_dequantize_bf16"] = {"us": round(t * 1e3, 2),
                                   "GBs": round(qbytes / (t * 1e-3) / 1e9, 1)}
+    # context for the product kernel: the plain bf16 GEMMs of the same shape through torch
+    # (hipBLASLt), without the expand, on the dequantised weight
+    Wb = lq.lq_nf4_dequantize(S["W"], dtype=torch.bfloat16).view(N, K)
+    Yb = torch.empty((M, N), dtype=torch.bfloat16, device=S["dev"])
+    dXb = torch.empty((M, K), dtype=torch.bfloat16, device=S["dev"])
+    gf = lambda: torch.matmul(S["X"], Wb.t(), out=Yb)  # noqa: E731
+    gd = lambda: torch.matmul(S["dY"], Wb, out=dXb)  # noqa: E731
+    for _ in range(10):  # library handle, workspace and kernel selection
+        gf()
+        gd()
+    t_f = cuda_time(gf, 50, torch)
+    t_d = cuda_time(gd, 50, torch)
+    res["torch_bf16_gemm_same_shape"] = {
+        "fwd_us": round(t_f * 1e3, 2), "dx_us": round(t_d * 1e3, 2),
+        "TFLOPs_fwd": round(2 * M * N * K / (t_f * 1e-3) / 1e12, 1),
+        "TFLOPs_dx": round(2 * M * N * K / (t_d * 1e-3) / 1e12, 1)}
+    del Wb, Yb, dXb
     # multi-adapter serving workload: 4 adapters r=16 over 256 requests, 4096^2 bf16 base
     from qlora_parameter_efficient_amd import workloads as wl
     c5 = wl.config5()
