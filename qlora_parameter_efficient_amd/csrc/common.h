@@ -33,6 +33,7 @@ struct MultiTab {
   float scale[kMaxRankCols];
   int32_t col_base[kMaxRankCols];
   int32_t col_stride[kMaxRankCols];
+  float oscale = 1.0f;  // skinny products: every stored result times this (dropout's 1 / (1 - p))
 };
 
 // Per-thread error reporting used by the ABI layer.

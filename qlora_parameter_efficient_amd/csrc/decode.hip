@@ -389,17 +389,27 @@ __global__ __launch_bounds__(kThreads) void tpart_kernel(const uint16_t* __restr
 namespace dispatch {
 
 int t_only(const void* X, int64_t M, int64_t K, const void* A, int64_t r, float* T,
-           hipStream_t st, int32_t* zero, int nzero) {
-  if (shrink_eligible(false, r)) return launch_shrink(X, M, K, A, false, r, T, zero, nzero, st);
-  return launch_skinny((const uint16_t*)X, M, K, (const uint16_t*)A, false, r, T, zero, nzero,
-                       st);
+           hipStream_t st, int32_t* zero, int nzero, float oscale) {
+  MultiTab sc{};
+  sc.oscale = oscale;
+  if (shrink_eligible(false, r))
+    return launch_shrink(X, M, K, A, false, r, T, zero, nzero, st, nullptr, &sc);
+  const int e = launch_skinny((const uint16_t*)X, M, K, (const uint16_t*)A, false, r, T, zero,
+                              nzero, st);
+  if (e || oscale == 1.0f) return e;
+  return launch_t_finish(T, M, r, oscale, 0.0f, nullptr, 0, st);
 }
 
 int u_only(const void* dY, int64_t M, int64_t N, const void* B, int64_t r, float* U,
-           hipStream_t st, int32_t* zero, int nzero) {
-  if (shrink_eligible(true, r)) return launch_shrink(dY, M, N, B, true, r, U, zero, nzero, st);
-  return launch_skinny((const uint16_t*)dY, M, N, (const uint16_t*)B, true, r, U, zero, nzero,
-                       st);
+           hipStream_t st, int32_t* zero, int nzero, float oscale) {
+  MultiTab sc{};
+  sc.oscale = oscale;
+  if (shrink_eligible(true, r))
+    return launch_shrink(dY, M, N, B, true, r, U, zero, nzero, st, nullptr, &sc);
+  const int e = launch_skinny((const uint16_t*)dY, M, N, (const uint16_t*)B, true, r, U, zero,
+                              nzero, st);
+  if (e || oscale == 1.0f) return e;
+  return launch_t_finish(U, M, r, oscale, 0.0f, nullptr, 0, st);
 }
 
 int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,

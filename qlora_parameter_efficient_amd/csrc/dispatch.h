@@ -44,17 +44,19 @@ int bf16_bwd(const void* dY, const void* X, int64_t M, const lq_weight& W, const
 int bf16_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B,
             int64_t r, float s, void* dX, float* U_out, hipStream_t st);
 
-// Skinny products T = X A^T and U = dY B (float32, M x r).  zero / nzero: int
-// words cleared by the first workgroup as a side job (the split-K flags of the
-// large-tile kernel that follows), or NULL / 0.
+// Skinny products T = X A^T and U = dY B (float32, M x r), each result times
+// oscale (a single float32 product).  zero / nzero: int words cleared by the
+// first workgroup as a side job (the split-K flags of the large-tile kernel
+// that follows), or NULL / 0.
 int t_only(const void* X, int64_t M, int64_t K, const void* A, int64_t r, float* T,
-           hipStream_t st, int32_t* zero, int nzero);
+           hipStream_t st, int32_t* zero, int nzero, float oscale = 1.0f);
 int u_only(const void* dY, int64_t M, int64_t N, const void* B, int64_t r, float* U,
-           hipStream_t st, int32_t* zero, int nzero);
+           hipStream_t st, int32_t* zero, int nzero, float oscale = 1.0f);
 // The 8-wave shrink kernel behind t_only / u_only (gt: G is B, K x r; needs
 // r % 4 == 0), with the older one-pass kernel as the fallback.
 // row_ad / mt (optional, multi-adapter T): column j of row m kept, times the
-// adapter's scale, only inside the columns of adapter row_ad[m], else 0.
+// adapter's scale, only inside the columns of adapter row_ad[m], else 0;
+// every stored result is then multiplied by mt->oscale.
 bool shrink_eligible(bool gt, int64_t r);
 // One launch: the NF4 weight W dequantised to bf16 at wout, and the shrink of
 // launch_shrink (same arguments), the flag words cleared as well.
@@ -85,9 +87,9 @@ int big_fwd_multi(const void* X, int64_t T, const lq_weight& W, const void* A_ca
 // row_ad[m] = adapter of the segment holding row m
 int launch_rowmap(const int32_t* seg_off, const int32_t* seg_ad, int32_t n_seg, int64_t T,
                   int32_t* row_ad, hipStream_t st);
-// U (M x r float32) is written as well: the expand needs it.
+// U (M x r float32) is written as well, times uscale: the expand needs it.
 int big_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,
-           float s, void* dX, float* U, void* ws, hipStream_t st);
+           float s, void* dX, float* U, void* ws, hipStream_t st, float uscale = 1.0f);
 int bf16_merge(const lq_weight& W, const void* A, const void* B, int64_t r, float s, void* Wout,
                hipStream_t st);
 int bf16_fwd_multi(const void* X, int64_t T_tokens, const lq_weight& W, const void* A_cat,

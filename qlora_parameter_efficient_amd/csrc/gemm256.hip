@@ -648,17 +648,18 @@ int big_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const v
   int e = 0;
   const int nz = (int)(g256_flag_bytes(M, N) / 4);
   const void* Q = W.kind == LQ_WEIGHT_DENSE ? W.dense : (const void*)w;
+  MultiTab sc{};  // T times 1 / (1 - p) under dropout, in the shrink's stores
+  sc.oscale = inv_keep;
   if (W.kind != LQ_WEIGHT_DENSE && shrink_eligible(false, r))
-    e = launch_prep(W, w, Z, M, K, A, false, r, T, (int32_t*)gws, nz, st);
+    e = launch_prep(W, w, Z, M, K, A, false, r, T, (int32_t*)gws, nz, st, nullptr, &sc);
   else if (!(e = W.kind == LQ_WEIGHT_DENSE ? 0 : bf16_weight(W, w, st)))
-    e = t_only(Z, M, K, A, r, T, st, (int32_t*)gws, nz);
-  if (!e && inv_keep != 1.0f) e = launch_t_finish(T, M, r, inv_keep, 0.0f, nullptr, 0, st);
+    e = t_only(Z, M, K, A, r, T, st, (int32_t*)gws, nz, inv_keep);
   if (e) return e;
   return launch_g256(false, X, Q, T, B, M, N, K, r, s, Y, gws, st);
 }
 
 int big_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,
-           float s, void* dX, float* U, void* ws, hipStream_t st) {
+           float s, void* dX, float* U, void* ws, hipStream_t st, float uscale) {
   const int64_t N = W.N, K = W.K;
   char* w = (char*)ws;
   void* gws = w;
@@ -666,10 +667,12 @@ int big_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const v
   int e = 0;
   const int nz = (int)(g256_flag_bytes(M, K) / 4);
   const void* Q = W.kind == LQ_WEIGHT_DENSE ? W.dense : (const void*)w;
+  MultiTab sc{};
+  sc.oscale = uscale;
   if (W.kind != LQ_WEIGHT_DENSE && shrink_eligible(true, r))
-    e = launch_prep(W, w, dY, M, N, B, true, r, U, (int32_t*)gws, nz, st);
+    e = launch_prep(W, w, dY, M, N, B, true, r, U, (int32_t*)gws, nz, st, nullptr, &sc);
   else if (!(e = W.kind == LQ_WEIGHT_DENSE ? 0 : bf16_weight(W, w, st)))
-    e = u_only(dY, M, N, B, r, U, st, (int32_t*)gws, nz);
+    e = u_only(dY, M, N, B, r, U, st, (int32_t*)gws, nz, uscale);
   if (e) return e;
   return launch_g256(true, dY, Q, U, A, M, K, N, r, s, dX, gws, st);
 }

@@ -428,21 +428,22 @@ int bf16_bwd_dropout(const void* dY, const void* X, const uint8_t* keep, float i
     if ((e = launch_zero_f32(dA, r * K, st))) return e;
     return launch_zero_f32(dB, N * r, st);
   }
-  if (dX) {
-    e = big_ws ? big_dx(dY, M, W, A, B, r, 0.0f, dX, U, big_ws, st)
-               : bf16_dx(dY, M, W, A, B, r, 0.0f, dX, U, st);
+  // U' = inv_keep U: in the shrink's stores, except after the fused dX kernel
+  if (dX && big_ws) {
+    e = big_dx(dY, M, W, A, B, r, 0.0f, dX, U, big_ws, st, inv_keep);
+  } else if (dX) {
+    if (!(e = bf16_dx(dY, M, W, A, B, r, 0.0f, dX, U, st)))
+      e = launch_t_finish(U, M, r, inv_keep, 0.0f, nullptr, 0, st);
   } else {
-    e = u_only(dY, M, N, B, r, U, st, nullptr, 0);
+    e = u_only(dY, M, N, B, r, U, st, nullptr, 0, inv_keep);
   }
   if (e) return e;
-  if ((e = launch_t_finish(U, M, r, inv_keep, 0.0f, nullptr, 0, st))) return e;
   if (dX && (e = launch_dx_fixup(dX, U, A, keep, M, K, r, s, st))) return e;
   if (!grads) return LQ_OK;
   if ((e = launch_keep_apply(X, keep, M, K, Xd, st))) return e;
   const float* T = T_saved;
   if (!T) {
-    if ((e = t_only(Xd, M, K, A, r, Tw, st, nullptr, 0))) return e;
-    if ((e = launch_t_finish(Tw, M, r, inv_keep, 0.0f, nullptr, 0, st))) return e;
+    if ((e = t_only(Xd, M, K, A, r, Tw, st, nullptr, 0, inv_keep))) return e;
     T = Tw;
   }
   return run_grads((const uint16_t*)Xd, U, (const uint16_t*)dY, T, M, N, K, (int)r, s, accumulate,

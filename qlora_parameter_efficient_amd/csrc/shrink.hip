@@ -169,7 +169,7 @@ __device__ __forceinline__ void shrink_rows(int64_t rb, const uint16_t* __restri
             a = a < 0 ? 0 : (a >= mt.n_ad ? mt.n_ad - 1 : a);
             v = (j >= mt.roff[a] && j < mt.roff[a + 1]) ? v * mt.scale[a] : 0.0f;
           }
-          out[m * r + j] = v;
+          out[m * r + j] = v * mt.oscale;
         }
       }
     }
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(256) void shrink_wide_kernel(const uint16_t* __rest
         a = a < 0 ? 0 : (a >= mt.n_ad ? mt.n_ad - 1 : a);
         val = (j >= mt.roff[a] && j < mt.roff[a + 1]) ? val * mt.scale[a] : 0.0f;
       }
-      out[m * r + j] = val;
+      out[m * r + j] = val * mt.oscale;
     }
   }
 }
