@@ -184,7 +184,7 @@ int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
  *   of partial sums of T, the float32 path M r floats of T when T_out is
  *   NULL; otherwise ws may be NULL.
  *   dt = LQ_BF16: bf16 inputs, float32 accumulation, bf16 RNE output; W0 dense
- *   bf16 or NF4.  With the LQ_OP_FWD size at M >= 2048 and N % 256 == 0 the
+ *   bf16 or NF4.  With the LQ_OP_FWD size at M > 16 and N % 256 == 0 the
  *   large-tile path runs: NF4 W0 is first dequantised (bit-exactly, as
  *   lq_nf4_dequantize) to a bf16 copy inside ws, then multiplied; otherwise
  *   the fused kernels dequantise NF4 in registers / LDS and never write a
@@ -214,8 +214,8 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A,
  *   micro-batches); 0 overwrites them.
  *   ws / ws_bytes: device workspace of at least
  *   lq_workspace_size(LQ_OP_BWD_FUSED, M, N, K, r, 0) bytes (caller-owned);
- *   with lq_workspace_size(LQ_OP_BWD, ...) bytes at M >= 2048 and
- *   K % 256 == 0, dX takes the large-tile path (bf16 copy of W0 in ws).
+ *   with lq_workspace_size(LQ_OP_BWD, ...) bytes and K % 256 == 0, dX takes
+ *   the large-tile path (bf16 copy of W0 in ws).
  * Same shape rules as lq_lora_fwd.
  */
 int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0,
@@ -239,7 +239,7 @@ int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0,
  *            lq_lora_bwd_dropout takes as T_saved
  *   ws       at least lq_workspace_size(LQ_OP_FWD_DROPOUT_FUSED, M, N, K, r, 0)
  *            bytes; lq_workspace_size(LQ_OP_FWD_DROPOUT, ...) bytes select the
- *            large-tile path where it applies (M >= 2048, N % 256 == 0).
+ *            large-tile path where it applies (M > 16, N % 256 == 0).
  * Other arguments, shape rules and errors as lq_lora_fwd; dt must be LQ_BF16
  * (LQ_ERR_UNSUPPORTED otherwise).  M = 0 is a no-op.
  */
@@ -341,8 +341,8 @@ int lq_lora_merge(const lq_weight* W0, const void* A, const void* B, int64_t r,
  *   (preconditions: offsets non-decreasing from 0 to T_tokens, ids in
  *   [0, n_adapters); lq_check_segments verifies host copies).
  *   ws: at least lq_workspace_size(LQ_OP_FWD_MULTI_FUSED, T_tokens, N, K, r,
- *   n_adapters) bytes; with lq_workspace_size(LQ_OP_FWD_MULTI, ...) bytes at
- *   T_tokens >= 2048 and N % 256 == 0 the large-tile path runs (adapter-masked
+ *   n_adapters) bytes; with lq_workspace_size(LQ_OP_FWD_MULTI, ...) bytes and
+ *   N % 256 == 0 the large-tile path runs (adapter-masked
  *   T, then the large product whose expand reads the stacked B).
  *   Requires dt = LQ_BF16, K % 64 == 0, N % 64 == 0, r * n_adapters <= 64.
  */

@@ -319,6 +319,7 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
   switch (op) {
     case LQ_OP_FWD: {  // float32 T, or the decode path's partial sums of T
       const size_t base = (size_t)((M <= kDecodeMaxM ? kTParts : 1) * M * r) * 4;
+      if (M <= kDecodeMaxM) return base;  // decode never takes the large-tile path
       const size_t big = fwd_big_bytes(M, N, K, r);
       return big > base ? big : base;
     }

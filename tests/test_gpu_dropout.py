@@ -80,9 +80,10 @@ def test_dropout_layer(shape, kind, p):
     M, N, K, r, fused = shape
     c = wl.small_case(M, N, K, r, seed=M + N + K + r + 11)
     bits = wl.dropout_keep_bits(M, K, p, seed=M + K)
-    run(c, kind, p, bits, fused, "small")
-    if not fused:  # the fused kernels with the smaller workspace, same inputs
-        run(c, kind, p, bits, True, "small-fused")
+    # the default workspace (the large-tile path where the shapes allow it) and
+    # the fused kernels with the smaller workspace, same inputs
+    run(c, kind, p, bits, False, "small")
+    run(c, kind, p, bits, True, "small-fused")
 
 
 def test_all_dropped_is_base_output_and_zero_adapter_grads():

@@ -87,9 +87,12 @@ SMALL = [
 @pytest.mark.parametrize("kind", ["dense", "nf4"])
 @pytest.mark.parametrize("shape", SMALL, ids=[f"{m}x{n}x{k}r{r}" for m, n, k, r in SMALL])
 def test_small(shape, kind):
+    # the default workspace (the large-tile path where N or K is a multiple of
+    # 256) and the fused kernels with the smallest workspace
     M, N, K, r = shape
     c = wl.small_case(M, N, K, r, seed=M + N + K + r)
     check_layer(c, kind, label="small")
+    check_layer(c, kind, merge=False, label="small-fused", fused=True)
 
 
 # Shapes that take the large-tile path (256 x 256 tiles, bf16 weight copy in

@@ -83,6 +83,7 @@ def test_small_segments(n_ad, r):
     ids = rng.integers(0, n_ad, len(counts))
     X, W0, A, B, off, ids = small_multi(counts, ids, n_ad, r)
     run_multi(X, W0, A, B, off, ids, 2.0, label="small")
+    run_multi(X, W0, A, B, off, ids, 2.0, label="small-fused", fused=True)
 
 
 def test_single_adapter_equals_single_forward():
@@ -107,8 +108,9 @@ def test_config5_full():
 
 @pytest.mark.parametrize("n_ad,r", [(3, 8), (4, 5), (2, 32)])
 def test_large_segments(n_ad, r):
-    """T >= 2048 with N = 256: the large-tile path (masked T from the shrink
-    kernel, expand over the stacked B), including an odd rank."""
+    """T >= 2048 with N = 256: the large-tile path with several row tiles
+    (masked T from the shrink kernel, expand over the stacked B), including an
+    odd rank."""
     counts = [0, 700, 1, 513, 0, 900, 129, 64]
     T = sum(counts)
     assert (lq.lq_workspace_size(lq.LQ_OP_FWD_MULTI, T, 256, 256, r, n_ad)
@@ -123,12 +125,13 @@ def test_large_segments(n_ad, r):
 @pytest.mark.parametrize("counts", [[0, 37, 129, 300, 2], [0, 700, 1, 513, 0, 900, 129, 64]],
                          ids=["fused", "large"])
 def test_nf4_shared_base(counts):
-    """Segmented forward over one NF4 + DQ base (the fused kernel at small T;
-    the prep kernel's bf16 copy and masked T at T >= 2048)."""
+    """Segmented forward over one NF4 + DQ base: the prep kernel's bf16 copy
+    and masked T with the default workspace, the fused kernel with the smallest."""
     rng = np.random.default_rng(len(counts))
     ids = rng.integers(0, 3, len(counts))
     X, W0, A, B, off, ids = small_multi(counts, ids, 3, 16, seed=7)
     run_multi(X, W0, A, B, off, ids, 2.0, label="nf4 base", nf4=True)
+    run_multi(X, W0, A, B, off, ids, 2.0, label="nf4 base fused", nf4=True, fused=True)
 
 
 def run_multi_ranks(counts, ids, ranks, scales, N=256, K=256, seed=13, nf4=False, fused=False,
