@@ -42,6 +42,10 @@ namespace {
 
 constexpr int64_t kMaxRank = 64;
 constexpr int64_t kDecodeMaxM = 16;
+// Forward rows run as 16-row decode chunks up to here: a chunk re-reads the
+// weights but costs ≈10 µs, against ≈52 µs for a large-tile call at these
+// sizes (W0 4096^2 NF4), which leaves most compute units idle.
+constexpr int64_t kDecodeChunkMaxM = 64;
 
 int check_weight(const lq_weight* w, lq_dtype dt) {
   REQUIRE(w != nullptr, LQ_ERR_INVALID_ARG, "W0 descriptor is NULL");
@@ -317,9 +321,10 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
                          int32_t n_adapters) {
   if (M < 0 || N < 0 || K < 0 || r < 0) return 0;
   switch (op) {
-    case LQ_OP_FWD: {  // float32 T, or the decode path's partial sums of T
-      const size_t base = (size_t)((M <= kDecodeMaxM ? kTParts : 1) * M * r) * 4;
-      if (M <= kDecodeMaxM) return base;  // decode never takes the large-tile path
+    case LQ_OP_FWD: {  // the decode path's partial sums of T, or float32 T
+      if (M <= kDecodeChunkMaxM)  // decode (chunks): never the large-tile path
+        return (size_t)(kTParts * (M < kDecodeMaxM ? M : kDecodeMaxM) * r) * 4;
+      const size_t base = (size_t)(M * r) * 4;
       const size_t big = fwd_big_bytes(M, N, K, r);
       return big > base ? big : base;
     }
@@ -349,7 +354,8 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
     case LQ_OP_DORA_BWD_FUSED:
       return dora_bwd_bytes(M, N, K, r, true, false);
     case LQ_OP_FWD_FUSED:
-      return (size_t)((M <= kDecodeMaxM ? kTParts : 1) * M * r) * 4;
+      if (M <= kDecodeChunkMaxM) return (size_t)(kTParts * (M < kDecodeMaxM ? M : kDecodeMaxM) * r) * 4;
+      return (size_t)(M * r) * 4;
     case LQ_OP_BWD_FUSED:
       return bwd_ws_bytes(M, N, K, r);
     case LQ_OP_FWD_MULTI_FUSED:
@@ -420,11 +426,20 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
     return f32_lora_fwd((const float*)X, M, *W0, (const float*)A, (const float*)B, r, scale,
                         (float*)Y, T, stream);
   }
-  if (M <= kDecodeMaxM) {  // partial sums of T cross two kernels
-    const size_t need = (size_t)(kTParts * M * r) * 4;
+  if (M <= kDecodeChunkMaxM) {  // partial sums of T cross two kernels, per 16-row chunk
+    const int64_t mc = M < kDecodeMaxM ? M : kDecodeMaxM;
+    const size_t need = (size_t)(kTParts * mc * r) * 4;
     REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE,
             "workspace %zu bytes, need %zu", ws_bytes, need);
-    return dispatch::decode_fwd(X, M, *W0, A, B, r, scale, Y, T_out, (float*)ws, stream);
+    const int64_t K = W0->K, N = W0->N;
+    for (int64_t m0 = 0; m0 < M; m0 += kDecodeMaxM) {
+      const int64_t m = M - m0 < kDecodeMaxM ? M - m0 : kDecodeMaxM;
+      if ((rc = dispatch::decode_fwd((const char*)X + m0 * K * 2, m, *W0, A, B, r, scale,
+                                     (char*)Y + m0 * N * 2, T_out ? T_out + m0 * r : nullptr,
+                                     (float*)ws, stream)))
+        return rc;
+    }
+    return LQ_OK;
   }
   const size_t big = fwd_big_bytes(M, W0->N, W0->K, r);
   if (big && ws && ws_bytes >= big)

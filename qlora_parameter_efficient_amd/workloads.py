@@ -127,7 +127,7 @@ def config3(M: int = 2048):
 
 
 def decode_inputs(M: int):
-    """Decode-sized activations for the config-3 weight, M in {1, 4, 16}."""
+    """Decode-sized activations for the config-3 weight (M = 1, 4, 16 in the bench)."""
     rng = np.random.default_rng(2003 + M)
     return _normal(rng, (M, 4096), 1.0, "bf16")
 

@@ -49,10 +49,13 @@ def test_check_segments():
 
 
 def test_workspace_sizes():
-    assert lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, 64, 256, 256, 8) == 64 * 8 * 4
-    # the default size also holds the large-tile path's bf16 copy of W0
-    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 64, 256, 256, 8) >= 64 * 8 * 4 + 256 * 256 * 2
-    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 16, 256, 256, 8) == 8 * 16 * 8 * 4  # decode partials
+    # up to 64 rows: 16-row decode chunks, 8 partial sums of T per chunk row
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 16, 256, 256, 8) == 8 * 16 * 8 * 4
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 64, 256, 256, 8) == 8 * 16 * 8 * 4
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, 5, 256, 256, 8) == 8 * 5 * 8 * 4
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, 65, 256, 256, 8) == 65 * 8 * 4
+    # beyond: the default size also holds the large-tile path's bf16 copy of W0
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 65, 256, 256, 8) >= 65 * 8 * 4 + 256 * 256 * 2
     assert lq.lq_workspace_size(lq.LQ_OP_BWD, 2048, 4096, 4096, 16) >= 2 * 2048 * 16 * 4
     assert lq.lq_workspace_size(lq.LQ_OP_FWD_MULTI, 1000, 4096, 4096, 16, 4) >= 1000 * 4
 

@@ -120,7 +120,7 @@ def test_large_tile_path(shape, kind):
 
 
 @pytest.mark.parametrize("kind", ["dense", "nf4"])
-@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("M", [1, 4, 16, 33, 64])  # 33, 64: 16-row decode chunks
 def test_decode_small(M, kind):
     c = wl.small_case(M, 256, 512, 16, seed=100 + M)
     check_layer(c, kind, label="decode", bwd=True, merge=False)
@@ -159,7 +159,7 @@ def test_config3_qlora_full():
     check_layer(c, "nf4", rows=sample_rows(2048), label="config3")
 
 
-@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("M", [1, 4, 16, 48])
 def test_config3_decode(M):
     c = wl.config3(M=32)
     c["X"] = wl.decode_inputs(M)
