@@ -161,13 +161,32 @@ void dora_side_take(Bump& b, bool nf4, int64_t N, int64_t K, int64_t r, const fl
   d.Gram = sv + N + N * r;
 }
 
+// Partial sums of T for the decode kernels, one 16-row chunk at a time.
+size_t decode_bytes(int64_t M, int64_t r) {
+  return (size_t)(kTParts * (M < kDecodeMaxM ? M : kDecodeMaxM) * r) * 4;
+}
+
+// The bf16 forward of up to kDecodeChunkMaxM rows by the decode kernels, in
+// 16-row chunks on the caller's stream (Tp: decode_bytes of workspace).
+int decode_chunks(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
+                  int64_t r, float s, void* Y, float* T_out, float* Tp, hipStream_t st) {
+  for (int64_t m0 = 0; m0 < M; m0 += kDecodeMaxM) {
+    const int64_t m = M - m0 < kDecodeMaxM ? M - m0 : kDecodeMaxM;
+    const int rc = dispatch::decode_fwd((const char*)X + m0 * W.K * 2, m, W, A, B, r, s,
+                                        (char*)Y + m0 * W.N * 2, T_out ? T_out + m0 * r : nullptr,
+                                        Tp, st);
+    if (rc) return rc;
+  }
+  return LQ_OK;
+}
+
 size_t plain_fwd_bytes(int64_t M, int64_t N, int64_t K, int64_t r, bool big) {
-  if (M <= kDecodeMaxM) return (size_t)(kTParts * M * r) * 4;
+  if (M <= kDecodeChunkMaxM) return decode_bytes(M, r);
   return big ? dispatch::big_fwd_ws_bytes(M, N, K, r) : 0;
 }
 
 bool dora_fwd_big(int64_t M, int64_t N, int64_t K) {
-  return M > kDecodeMaxM && dispatch::big_fwd_eligible(M, N, K);
+  return M > kDecodeChunkMaxM && dispatch::big_fwd_eligible(M, N, K);
 }
 
 size_t dora_fwd_bytes(int64_t M, int64_t N, int64_t K, int64_t r, bool nf4, bool big) {
@@ -322,8 +341,7 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
   if (M < 0 || N < 0 || K < 0 || r < 0) return 0;
   switch (op) {
     case LQ_OP_FWD: {  // the decode path's partial sums of T, or float32 T
-      if (M <= kDecodeChunkMaxM)  // decode (chunks): never the large-tile path
-        return (size_t)(kTParts * (M < kDecodeMaxM ? M : kDecodeMaxM) * r) * 4;
+      if (M <= kDecodeChunkMaxM) return decode_bytes(M, r);  // never the large-tile path
       const size_t base = (size_t)(M * r) * 4;
       const size_t big = fwd_big_bytes(M, N, K, r);
       return big > base ? big : base;
@@ -354,7 +372,7 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
     case LQ_OP_DORA_BWD_FUSED:
       return dora_bwd_bytes(M, N, K, r, true, false);
     case LQ_OP_FWD_FUSED:
-      if (M <= kDecodeChunkMaxM) return (size_t)(kTParts * (M < kDecodeMaxM ? M : kDecodeMaxM) * r) * 4;
+      if (M <= kDecodeChunkMaxM) return decode_bytes(M, r);
       return (size_t)(M * r) * 4;
     case LQ_OP_BWD_FUSED:
       return bwd_ws_bytes(M, N, K, r);
@@ -427,19 +445,10 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
                         (float*)Y, T, stream);
   }
   if (M <= kDecodeChunkMaxM) {  // partial sums of T cross two kernels, per 16-row chunk
-    const int64_t mc = M < kDecodeMaxM ? M : kDecodeMaxM;
-    const size_t need = (size_t)(kTParts * mc * r) * 4;
+    const size_t need = decode_bytes(M, r);
     REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE,
             "workspace %zu bytes, need %zu", ws_bytes, need);
-    const int64_t K = W0->K, N = W0->N;
-    for (int64_t m0 = 0; m0 < M; m0 += kDecodeMaxM) {
-      const int64_t m = M - m0 < kDecodeMaxM ? M - m0 : kDecodeMaxM;
-      if ((rc = dispatch::decode_fwd((const char*)X + m0 * K * 2, m, *W0, A, B, r, scale,
-                                     (char*)Y + m0 * N * 2, T_out ? T_out + m0 * r : nullptr,
-                                     (float*)ws, stream)))
-        return rc;
-    }
-    return LQ_OK;
+    return decode_chunks(X, M, *W0, A, B, r, scale, Y, T_out, (float*)ws, stream);
   }
   const size_t big = fwd_big_bytes(M, W0->N, W0->K, r);
   if (big && ws && ws_bytes >= big)
@@ -584,8 +593,8 @@ int lq_dora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
     return rc;
   if ((rc = dispatch::dora_weight_side(Wd, N, K, A, B, r, scale, magnitude, d, stream))) return rc;
   const lq_weight Wv = dense_view(*W0, Wd);
-  if (M <= kDecodeMaxM)
-    rc = dispatch::decode_fwd(X, M, Wv, A, B, r, scale, Z, T_out, (float*)rest, stream);
+  if (M <= kDecodeChunkMaxM)
+    rc = decode_chunks(X, M, Wv, A, B, r, scale, Z, T_out, (float*)rest, stream);
   else if (big)
     rc = dispatch::big_fwd(X, M, Wv, A, B, r, scale, Z, T_out, rest, stream);
   else

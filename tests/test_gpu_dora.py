@@ -65,6 +65,7 @@ SHAPES = [
     (130, 192, 192, 5, True),
     (700, 256, 320, 64, True),
     (16, 256, 512, 8, True),
+    (40, 256, 512, 16, True),   # three 16-row decode chunks
     (2100, 256, 256, 16, False),
     (2304, 512, 768, 64, False),
 ]
