@@ -24,7 +24,8 @@ Default run (python bench.py [--steps K] [--warmup W]):
 * cpu_baseline: the CPU oracle (float64 NumPy) on the same step.
 * secondary lines in the same JSON object: NF4 decode (M = 1, 4, 16) GB/s on
   the weight stream with cold weights, merge, quantise, multi-adapter, the
-  step with LoRA-input dropout and as DoRA, the AdamW step, the plain bf16
+  forwards of 32 and 64 rows (16-row decode chunks), the step with LoRA-input
+  dropout and as DoRA, the AdamW step, the plain bf16
   GEMMs of the product kernel's shape through torch (context), and forward +
   backward of config 2 (q and v, bf16, M = 4096, r = 8) and of config 4 (the
   seven projections of a block, NF4, M = 8192, r = 64).
@@ -267,6 +268,19 @@ def secondary(S, torch):
     lq = S["lq"]
     res = {}
     res["decode_nf4"] = decode_bench(S, torch)
+    # forwards of 32 and 64 rows (16-row decode chunks), graph-launched, warm weights
+    from qlora_parameter_efficient_amd import workloads as wlc
+    chunks = {}
+    for m in (32, 64):
+        Xm = torch.from_numpy(wlc.decode_inputs(m).bits.view(np.int16).copy()).view(
+            torch.bfloat16).to(S["dev"])
+        Ym = torch.empty((m, N), dtype=torch.bfloat16, device=S["dev"])
+        wsm = torch.empty(lq.lq_workspace_size(lq.LQ_OP_FWD, m, N, K, R), dtype=torch.uint8,
+                          device=S["dev"])
+        t = graph_time(lambda: lq.lq_lora_fwd(Xm, S["W"], S["A"], S["B"], S["s"], ws=wsm, Y=Ym),
+                       torch)
+        chunks[f"M{m}"] = {"us_per_call_graph": round(t * 1e3, 2)}
+    res["forward_nf4_decode_chunks"] = chunks
     # one-time ops, HBM-bound: GPU time per call from graph-captured sequences
     Wm = torch.empty((N, K), dtype=torch.bfloat16, device=S["dev"])
     t = graph_time(lambda: lq.lq_lora_merge(S["W"], S["A"], S["B"], S["s"],
