@@ -161,23 +161,18 @@ void dora_side_take(Bump& b, bool nf4, int64_t N, int64_t K, int64_t r, const fl
   d.Gram = sv + N + N * r;
 }
 
-// Partial sums of T for the decode kernels, one 16-row chunk at a time.
+// Partial sums of T for the decode kernels: kTParts per row, 16-row chunks
+// padded past 16 rows.
 size_t decode_bytes(int64_t M, int64_t r) {
-  return (size_t)(kTParts * (M < kDecodeMaxM ? M : kDecodeMaxM) * r) * 4;
+  const int64_t rows = M <= kDecodeMaxM ? M : (M + kDecodeMaxM - 1) / kDecodeMaxM * kDecodeMaxM;
+  return (size_t)(kTParts * rows * r) * 4;
 }
 
-// The bf16 forward of up to kDecodeChunkMaxM rows by the decode kernels, in
-// 16-row chunks on the caller's stream (Tp: decode_bytes of workspace).
+// The bf16 forward of up to kDecodeChunkMaxM rows by the decode kernels (one
+// launch each, 16-row chunks along the grid's second dimension).
 int decode_chunks(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
                   int64_t r, float s, void* Y, float* T_out, float* Tp, hipStream_t st) {
-  for (int64_t m0 = 0; m0 < M; m0 += kDecodeMaxM) {
-    const int64_t m = M - m0 < kDecodeMaxM ? M - m0 : kDecodeMaxM;
-    const int rc = dispatch::decode_fwd((const char*)X + m0 * W.K * 2, m, W, A, B, r, s,
-                                        (char*)Y + m0 * W.N * 2, T_out ? T_out + m0 * r : nullptr,
-                                        Tp, st);
-    if (rc) return rc;
-  }
-  return LQ_OK;
+  return dispatch::decode_fwd(X, M, W, A, B, r, s, Y, T_out, Tp, st);
 }
 
 size_t plain_fwd_bytes(int64_t M, int64_t N, int64_t K, int64_t r, bool big) {

@@ -145,6 +145,16 @@ constexpr int kGemvWaves = 16;
 
 template <int WK, int XS>
 __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
+  // 16-row chunk blockIdx.y of a call with up to 64 rows: its rows of X, Y and
+  // T_out, and its own partial sums of T
+  {
+    const int64_t m0 = 16 * (int64_t)blockIdx.y;
+    p.X += m0 * p.W.K;
+    p.Y += m0 * p.W.N;
+    if (p.T_out) p.T_out += m0 * p.r;
+    p.Tp += (int64_t)blockIdx.y * kTParts * 16 * p.r;
+    p.M = p.M - m0 < 16 ? p.M - m0 : 16;
+  }
   constexpr bool XL = XS > 0;
   constexpr int CH = 2;
   constexpr int NT = 64 * kGemvWaves;
@@ -313,7 +323,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
       u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
 }
 
-// Partial sums of T = X A^T for M <= 16 rows: workgroup b reduces granules
+// Partial sums of T = X A^T for one 16-row chunk (blockIdx.y) of up to 64
+// rows, kTParts x 16 x r floats per chunk: workgroup b reduces granules
 // [b G / kTParts, (b + 1) G / kTParts) of the G = K / 32 granules of 32
 // reduction elements; its four waves take every fourth granule and run
 // v_mfma_f32_16x16x32_bf16 with A rows as the A operand (16 per tile, JT
@@ -326,6 +337,12 @@ __global__ __launch_bounds__(kThreads) void tpart_kernel(const uint16_t* __restr
                                                          int r, float* __restrict__ Tp) {
   constexpr int CH = 4;
   __shared__ f32x4 part[4][JT][64];
+  {  // 16-row chunk blockIdx.y (the decode GEMV reads this chunk's partials)
+    const int64_t m0 = 16 * (int64_t)blockIdx.y;
+    X += m0 * K;
+    M = M - m0 < 16 ? M - m0 : 16;
+    Tp += (int64_t)blockIdx.y * kTParts * 16 * r;
+  }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, q = lane >> 4;
   const bool mrow = l16 < M;
@@ -417,7 +434,8 @@ int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, cons
   const int jt = (int)((r + 15) / 16);
   const uint16_t* Xh = (const uint16_t*)X;
   const uint16_t* Ah = (const uint16_t*)A;
-  const dim3 tg(kTParts), tb(kThreads);
+  const unsigned chunks = (unsigned)((M + 15) / 16);  // 16-row chunks, grid dimension y
+  const dim3 tg(kTParts, chunks), tb(kThreads);
   switch (jt) {
     case 1:
       hipLaunchKernelGGL(tpart_kernel<1>, tg, tb, 0, st, Xh, M, W.K, Ah, (int)r, Tp);
@@ -445,11 +463,14 @@ int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, cons
   p.s = s;
   p.Y = (uint16_t*)Y;
   p.tab = nf4_table(W.codebook);
-  const dim3 grid((unsigned)(W.N / 16)), block(64 * kGemvWaves);
-  // staged X: 16384 elements keep two workgroups per compute unit; 65536 only
-  // when the grid has at most one workgroup per compute unit
-  const int64_t mk = M * W.K;
-  const int xs = W.K % 128 ? 0 : mk <= 16384 ? 1 : (mk <= 65536 && W.N / 16 <= 256) ? 2 : 0;
+  const dim3 grid((unsigned)(W.N / 16), chunks), block(64 * kGemvWaves);
+  // staged X (one chunk's rows): 16384 elements keep two workgroups per
+  // compute unit; 65536 only when the grid has at most one workgroup per
+  // compute unit
+  const int64_t mk = (M < 16 ? M : 16) * W.K;
+  const int xs = W.K % 128 ? 0
+                 : mk <= 16384 ? 1
+                 : (mk <= 65536 && W.N / 16 * (int64_t)chunks <= 256) ? 2 : 0;
   switch (weight_format(W) * 3 + xs) {
     case kDense * 3 + 0: hipLaunchKernelGGL((gemv_kernel<kDense, 0>), grid, block, 0, st, p); break;
     case kDense * 3 + 1: hipLaunchKernelGGL((gemv_kernel<kDense, 16384>), grid, block, 0, st, p); break;

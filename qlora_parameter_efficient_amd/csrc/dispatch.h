@@ -32,8 +32,9 @@ size_t multi_ws_bytes(int64_t T_tokens, int64_t r, int32_t n_adapters);
 
 int bf16_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
              int64_t r, float s, void* Y, float* T_out, hipStream_t st);
-// Decode path (M <= 16): T partial sums (kTParts x M x r floats) go to Tp;
-// T_out (optional) receives T.
+// Decode path (M <= 64, as 16-row chunks in one launch of each kernel): T
+// partial sums (kTParts x M x r floats, M padded to a multiple of 16 past 16
+// rows) go to Tp; T_out (optional) receives T.
 int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
                int64_t r, float s, void* Y, float* T_out, float* Tp, hipStream_t st);
 // big_ws: workspace of the large-tile dX path (big_dx_ws_bytes), or NULL for

@@ -49,9 +49,11 @@ def test_check_segments():
 
 
 def test_workspace_sizes():
-    # up to 64 rows: 16-row decode chunks, 8 partial sums of T per chunk row
+    # up to 64 rows: the decode kernels, 8 partial sums of T per row (16-row
+    # chunks, rows padded to a multiple of 16 past 16)
     assert lq.lq_workspace_size(lq.LQ_OP_FWD, 16, 256, 256, 8) == 8 * 16 * 8 * 4
-    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 64, 256, 256, 8) == 8 * 16 * 8 * 4
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 33, 256, 256, 8) == 8 * 48 * 8 * 4
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 64, 256, 256, 8) == 8 * 64 * 8 * 4
     assert lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, 5, 256, 256, 8) == 8 * 5 * 8 * 4
     assert lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, 65, 256, 256, 8) == 65 * 8 * 4
     # beyond: the default size also holds the large-tile path's bf16 copy of W0
