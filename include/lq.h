@@ -180,9 +180,10 @@ int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
  *   ws / ws_bytes: device workspace (caller-owned, contents not preserved).
  *   lq_workspace_size(LQ_OP_FWD, M, N, K, r, 0) bytes select the fastest
  *   path; lq_workspace_size(LQ_OP_FWD_FUSED, ...) is the smallest workspace
- *   that works.  The decode path (dt = LQ_BF16, M <= 64, run as chunks of up
- *   to 16 rows) needs 8 min(M, 16) r floats of partial sums of T, the float32
- *   path M r floats of T when T_out is NULL; otherwise ws may be NULL.
+ *   that works.  The decode path (dt = LQ_BF16, M <= 80, run as chunks of up
+ *   to 16 rows) needs 8 M' r floats of partial sums of T (M' = M up to 16,
+ *   else M rounded up to a multiple of 16), the float32 path M r floats of T
+ *   when T_out is NULL; otherwise ws may be NULL.
  *   dt = LQ_BF16: bf16 inputs, float32 accumulation, bf16 RNE output; W0 dense
  *   bf16 or NF4.  With the LQ_OP_FWD size at M > 16 and N % 256 == 0 the
  *   large-tile path runs: NF4 W0 is first dequantised (bit-exactly, as
@@ -190,7 +191,7 @@ int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
  *   the fused kernels dequantise NF4 in registers / LDS and never write a
  *   dense W0.  Both give "dequantise, then multiply in bf16".
  *   Requires K % 64 == 0, N % 64 == 0, N, K <= 65536, M*K and M*N < 2^31,
- *   1 <= r <= 64.  M <= 64 takes the memory-bound decode path, 16 rows at a
+ *   1 <= r <= 64.  M <= 80 takes the memory-bound decode path, 16 rows at a
  *   time (each chunk streams W0 once).
  *   dt = LQ_F32: float32 throughout (W0 dense f32 or NF4), 1 <= r <= 64.
  * M = 0 is a no-op returning LQ_OK.
