@@ -180,7 +180,7 @@ int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
  *   ws / ws_bytes: device workspace (caller-owned, contents not preserved).
  *   lq_workspace_size(LQ_OP_FWD, M, N, K, r, 0) bytes select the fastest
  *   path; lq_workspace_size(LQ_OP_FWD_FUSED, ...) is the smallest workspace
- *   that works.  The decode path (dt = LQ_BF16, M <= 80, run as chunks of up
+ *   that works.  The decode path (dt = LQ_BF16, M <= 96, run as chunks of up
  *   to 16 rows) needs 8 M' r floats of partial sums of T (M' = M up to 16,
  *   else M rounded up to a multiple of 16), the float32 path M r floats of T
  *   when T_out is NULL; otherwise ws may be NULL.
@@ -191,7 +191,7 @@ int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
  *   the fused kernels dequantise NF4 in registers / LDS and never write a
  *   dense W0.  Both give "dequantise, then multiply in bf16".
  *   Requires K % 64 == 0, N % 64 == 0, N, K <= 65536, M*K and M*N < 2^31,
- *   1 <= r <= 64.  M <= 80 takes the memory-bound decode path, 16 rows at a
+ *   1 <= r <= 64.  M <= 96 takes the memory-bound decode path, 16 rows at a
  *   time (each chunk streams W0 once).
  *   dt = LQ_F32: float32 throughout (W0 dense f32 or NF4), 1 <= r <= 64.
  * M = 0 is a no-op returning LQ_OK.

@@ -43,10 +43,10 @@ namespace {
 constexpr int64_t kMaxRank = 64;
 constexpr int64_t kDecodeMaxM = 16;
 // Forward rows run as 16-row decode chunks up to here: each chunk re-reads
-// the weights, and five chunks (80 rows, 44.5 µs for W0 4096^2 NF4) still beat
+// the weights, and six chunks (96 rows, 45.5 µs for W0 4096^2 NF4) still beat
 // a large-tile call at these sizes (≈52 µs), which leaves most compute units
-// idle; six tie and seven lose.
-constexpr int64_t kDecodeChunkMaxM = 80;
+// idle; seven tie and eight lose.
+constexpr int64_t kDecodeChunkMaxM = 96;
 
 int check_weight(const lq_weight* w, lq_dtype dt) {
   REQUIRE(w != nullptr, LQ_ERR_INVALID_ARG, "W0 descriptor is NULL");

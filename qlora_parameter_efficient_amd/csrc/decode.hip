@@ -133,8 +133,8 @@ struct GemvParams {
 // the weight stream and only summed and staged in LDS after it; the 16 wave
 // partials are added through LDS.
 // The activations are staged in LDS once per workgroup (XS > 0: up to XS
-// elements; M K <= 16384 keeps two workgroups per compute unit, up to 65536
-// when the grid has no more workgroups than compute units).  Loaded per lane
+// elements of one chunk's rows; 16384 keeps two workgroups per compute unit,
+// 65536 one).  Loaded per lane
 // straight from global memory, the lanes of a 16-lane group whose row is past
 // M would all load row 0 again (16 times the bytes of X through each compute
 // unit's load path at M = 1), and at M = 16 the per-lane 16-byte pieces are
@@ -465,12 +465,10 @@ int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, cons
   p.tab = nf4_table(W.codebook);
   const dim3 grid((unsigned)(W.N / 16), chunks), block(64 * kGemvWaves);
   // staged X (one chunk's rows): 16384 elements keep two workgroups per
-  // compute unit; 65536 only when the grid has at most one workgroup per
-  // compute unit
+  // compute unit; 65536 allows one, and still measured faster than loading X
+  // per lane with grids of up to six workgroups per compute unit
   const int64_t mk = (M < 16 ? M : 16) * W.K;
-  const int xs = W.K % 128 ? 0
-                 : mk <= 16384 ? 1
-                 : (mk <= 65536 && W.N / 16 * (int64_t)chunks <= 256) ? 2 : 0;
+  const int xs = W.K % 128 ? 0 : mk <= 16384 ? 1 : mk <= 65536 ? 2 : 0;
   switch (weight_format(W) * 3 + xs) {
     case kDense * 3 + 0: hipLaunchKernelGGL((gemv_kernel<kDense, 0>), grid, block, 0, st, p); break;
     case kDense * 3 + 1: hipLaunchKernelGGL((gemv_kernel<kDense, 16384>), grid, block, 0, st, p); break;

@@ -53,11 +53,11 @@ def test_workspace_sizes():
     # chunks, rows padded to a multiple of 16 past 16)
     assert lq.lq_workspace_size(lq.LQ_OP_FWD, 16, 256, 256, 8) == 8 * 16 * 8 * 4
     assert lq.lq_workspace_size(lq.LQ_OP_FWD, 33, 256, 256, 8) == 8 * 48 * 8 * 4
-    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 80, 256, 256, 8) == 8 * 80 * 8 * 4
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 90, 256, 256, 8) == 8 * 96 * 8 * 4
     assert lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, 5, 256, 256, 8) == 8 * 5 * 8 * 4
-    assert lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, 81, 256, 256, 8) == 81 * 8 * 4
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, 97, 256, 256, 8) == 97 * 8 * 4
     # beyond: the default size also holds the large-tile path's bf16 copy of W0
-    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 81, 256, 256, 8) >= 81 * 8 * 4 + 256 * 256 * 2
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 97, 256, 256, 8) >= 97 * 8 * 4 + 256 * 256 * 2
     assert lq.lq_workspace_size(lq.LQ_OP_BWD, 2048, 4096, 4096, 16) >= 2 * 2048 * 16 * 4
     assert lq.lq_workspace_size(lq.LQ_OP_FWD_MULTI, 1000, 4096, 4096, 16, 4) >= 1000 * 4
 

@@ -120,7 +120,7 @@ def test_large_tile_path(shape, kind):
 
 
 @pytest.mark.parametrize("kind", ["dense", "nf4"])
-@pytest.mark.parametrize("M", [1, 4, 16, 33, 80])  # 33, 80: 16-row decode chunks
+@pytest.mark.parametrize("M", [1, 4, 16, 33, 96])  # 33, 96: 16-row decode chunks
 def test_decode_small(M, kind):
     c = wl.small_case(M, 256, 512, 16, seed=100 + M)
     check_layer(c, kind, label="decode", bwd=True, merge=False)
