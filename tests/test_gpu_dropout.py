@@ -110,11 +110,10 @@ def test_all_kept_p0_matches_plain_layer():
 
 
 def test_config3_full_size_p005():
-    # the benchmark workload with the pages' lora_dropout = 0.05, both paths;
-    # Y and dX checked on sampled rows, T / dA / dB in full
+    # the benchmark workload with the pages' lora_dropout = 0.05, both paths,
+    # every output in full
     c = wl.config3()
     M, K = c["X"].value.shape
     bits = wl.dropout_keep_bits(M, K, 0.05, seed=99)
-    rows = np.random.default_rng(5).choice(M, 64, replace=False)
-    run(c, "nf4", 0.05, bits, False, "config3", rows=rows)
-    run(c, "nf4", 0.05, bits, True, "config3-fused", rows=rows)
+    run(c, "nf4", 0.05, bits, False, "config3")
+    run(c, "nf4", 0.05, bits, True, "config3-fused")

@@ -1,6 +1,6 @@
-"""NF4 format variants on the GPU against the oracle: FP8 (E4M3) second-level
-constants, the symmetric zero-free codebook, and single-level constants with
-either codebook.
+"""NF4 formats on the GPU against the oracle: the default format (NF4 codebook,
+int8 second-level constants), FP8 (E4M3) second-level constants, the
+symmetric zero-free codebook, and single-level constants with either codebook.
 
 * The codec is bit-exact: packed codes, 8-bit constants, c2 / absmax and both
   dequantised outputs, on the config-3 weight, ragged lengths and constants
@@ -25,14 +25,17 @@ from .gpu_helpers import BF16_TOL, DEV, F32_TOL, announce, bits, f64, rel_err, t
 
 pytestmark = pytest.mark.gpu
 
-# (double_quant, dq_format, codebook)
+# (double_quant, dq_format, codebook); the first entry is the default format
+# every workload uses (NF4 codebook, int8 second-level constants)
 VARIANTS = [
+    (True, "int8", "nf4"),
+    (False, "int8", "nf4"),
     (True, "fp8", "nf4"),
     (True, "int8", "nf4_symmetric"),
     (True, "fp8", "nf4_symmetric"),
     (False, "int8", "nf4_symmetric"),
 ]
-VIDS = ["fp8", "sym", "fp8-sym", "single-sym"]
+VIDS = ["default", "single", "fp8", "sym", "fp8-sym", "single-sym"]
 
 
 def quant_both(w_values, W_dev, v):
@@ -114,14 +117,19 @@ def one_hot_rows(M, K, ks):
 
 
 @pytest.mark.parametrize("v", VARIANTS, ids=VIDS)
-@pytest.mark.parametrize("M,fused", [(300, True), (2100, False), (4, True)],
-                         ids=["fused", "large", "decode"])
-def test_in_register_dequant_is_exact(v, M, fused):
+@pytest.mark.parametrize("M,N,K,fused", [(300, 512, 768, True), (300, 256, 4096, True),
+                                         (2100, 512, 768, False), (2048, 256, 4096, False),
+                                         (4, 512, 768, True), (16, 256, 4096, True)],
+                         ids=["fused", "fused-k4096", "large", "large-k4096", "decode",
+                              "decode-k4096"])
+def test_in_register_dequant_is_exact(v, M, N, K, fused):
     """Y = onehot(k) W'^T with B = 0 returns column k of the dequantised W'
-    (bf16) exactly; dX = onehot(n) W' returns row n."""
-    N, K, r = 512, 768, 16
+    (bf16) exactly; dX = onehot(n) W' returns row n.  K = 4096 walks the
+    config-3 reduction length (64 blocks per row, four second-level groups
+    per row)."""
+    r = 16
     announce(f"formats exact dequant M={M} fused={fused} {v}")
-    rng = np.random.default_rng(M)
+    rng = np.random.default_rng(M + K)
     W = wl.Tensor((rng.standard_normal((N, K)) * 0.02).astype(np.float32), "bf16")
     q, o = quant_both(W.value, to_dev(W), v)
     Wp = onf4.nf4_dequantize_bf16(o).reshape(N, K)          # bf16 bits of W'

@@ -1,10 +1,14 @@
 """bf16 path (MFMA kernels) against the float64 oracle, 2e-2 relative max error.
 
-Small cases span several tiles with ragged edges (M not a multiple of the
-128/256-row tiles, N with a partial 128-column tile and a partial 64-row
-reduction step, odd ranks); full workload sizes are checked on sampled rows
-for Y and dX (each row computed by the oracle on its own) and in full for dA,
-dB and the merged weight."""
+Every comparison covers the whole output tensor (Y, T, dX, dA, dB and the
+merged weight), with the reference from the oracle's own forward, backward
+and merge.  Small cases span several tiles with ragged edges (M not a
+multiple of the 128/256-row tiles, N with a partial 128-column tile and a
+partial 64-row reduction step, odd ranks).  The workload sizes (configs 2, 3
+and 4) run through both the default workspace and the smaller fused-kernel
+workspace, with the dense and the NF4 base where the workload names both."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -30,49 +34,64 @@ def base_for(c, kind):
     return to_dev(c["W0"]), W0v.astype(np.float64)
 
 
-def check_layer(c, kind, rows=None, bwd=True, merge=True, label="", fused=False):
+def oracle_ref(c, Wo, bwd=True):
+    """The oracle's forward (Y, T) and backward (dX, dA, dB) on the whole batch."""
+    s = c["alpha"] / c["r"]
+    Xo, Ao, Bo = c["X"].f64(), c["A"].f64(), c["B"].f64()
+    Yo, _, To = olora.lora_forward(Xo, Wo, Ao, Bo, s)
+    ref = dict(Y=Yo, T=To)
+    if bwd:
+        ref["dX"], ref["dA"], ref["dB"] = olora.lora_backward(c["dY"].f64(), Xo, Wo, Ao, Bo, s)
+    return ref
+
+
+def check_gpu(c, Wd, ref, label="", fused=False):
+    """The GPU layer on the same inputs against ``ref`` over whole tensors."""
     s = c["alpha"] / c["r"]
     X, A, B = to_dev(c["X"]), to_dev(c["A"]), to_dev(c["B"])
-    Wd, Wo = base_for(c, kind)
     M, r = X.shape[0], A.shape[0]
-    Xo, Ao, Bo = c["X"].f64(), c["A"].f64(), c["B"].f64()
-    sel = np.arange(M) if rows is None else rows
-    announce(f"bf16 fwd {label} {kind} M={M} N={Wo.shape[0]} K={Wo.shape[1]} r={r}")
+    announce(f"bf16 fwd {label} fused={fused} M={M} N={ref['Y'].shape[1]} K={X.shape[1]} r={r}")
     T = torch.empty((M, r), dtype=torch.float32, device=X.device)
     Y = lq.lq_lora_fwd(X, Wd, A, B, s, T_out=T, fused=fused)
     torch.cuda.synchronize()
-    Yo, _, To = olora.lora_forward(Xo[sel], Wo, Ao, Bo, s)
-    e = rel_err(f64(Y)[sel], Yo)
-    assert e <= BF16_TOL, f"Y rel err {e:.3e}"
-    e = rel_err(f64(T)[sel], To)
-    assert e <= BF16_TOL, f"T rel err {e:.3e}"
-    if bwd:
-        announce(f"bf16 bwd {label} {kind} M={M}")
-        dY = to_dev(c["dY"])
-        dX, dA, dB = lq.lq_lora_bwd(dY, X, Wd, A, B, s, T_saved=T if M > 16 else None,
-                                    fused=fused)
-        torch.cuda.synchronize()
-        dYo = c["dY"].f64()
-        dXo = dYo[sel] @ Wo + s * ((dYo[sel] @ Bo) @ Ao)
-        e = rel_err(f64(dX)[sel], dXo)
-        assert e <= BF16_TOL, f"dX rel err {e:.3e}"
-        U = dYo @ Bo
-        dAo = s * (U.T @ Xo)
-        dBo = s * (dYo.T @ (Xo @ Ao.T))
-        for name, got, want in (("dA", dA, dAo), ("dB", dB, dBo)):
-            e = rel_err(f64(got), want)
-            assert e <= BF16_TOL, f"{name} rel err {e:.3e}"
-        # dX alone (dA = dB = NULL) runs the same kernel: bit-identical dX
-        dX2, dA2, dB2 = lq.lq_lora_bwd(dY, X, Wd, A, B, s, need_grads=False, fused=fused)
-        torch.cuda.synchronize()
-        assert dA2 is None and dB2 is None
-        assert torch.equal(dX2, dX), "dX-only call differs from the full backward"
+    for name, got, want in (("Y", Y, ref["Y"]), ("T", T, ref["T"])):
+        e = rel_err(f64(got), want)
+        assert e <= BF16_TOL, f"{name} rel err {e:.3e}"
+    del Y
+    if "dX" not in ref:
+        return
+    announce(f"bf16 bwd {label} fused={fused} M={M}")
+    dY = to_dev(c["dY"])
+    dX, dA, dB = lq.lq_lora_bwd(dY, X, Wd, A, B, s, T_saved=T if M > 16 else None, fused=fused)
+    torch.cuda.synchronize()
+    for name, got in (("dX", dX), ("dA", dA), ("dB", dB)):
+        e = rel_err(f64(got), ref[name])
+        assert e <= BF16_TOL, f"{name} rel err {e:.3e}"
+    # dX alone (dA = dB = NULL) runs the same kernel: bit-identical dX
+    dX2, dA2, dB2 = lq.lq_lora_bwd(dY, X, Wd, A, B, s, need_grads=False, fused=fused)
+    torch.cuda.synchronize()
+    assert dA2 is None and dB2 is None
+    assert torch.equal(dX2, dX), "dX-only call differs from the full backward"
+
+
+def check_layer(c, kind, bwd=True, merge=True, label="", fused=False):
+    Wd, Wo = base_for(c, kind)
+    check_gpu(c, Wd, oracle_ref(c, Wo, bwd=bwd), label=f"{label} {kind}", fused=fused)
     if merge:
         announce(f"bf16 merge {label} {kind}")
-        Wm = lq.lq_lora_merge(Wd, A, B, s, dtype=torch.bfloat16)
+        s = c["alpha"] / c["r"]
+        Wm = lq.lq_lora_merge(Wd, to_dev(c["A"]), to_dev(c["B"]), s, dtype=torch.bfloat16)
         torch.cuda.synchronize()
-        e = rel_err(f64(Wm), olora.lora_merge(Wo, Ao, Bo, s))
+        e = rel_err(f64(Wm), olora.lora_merge(Wo, c["A"].f64(), c["B"].f64(), s))
         assert e <= BF16_TOL, f"merge rel err {e:.3e}"
+
+
+def check_both_paths(c, kind, label):
+    """Default and fused-kernel workspaces on one oracle reference."""
+    Wd, Wo = base_for(c, kind)
+    ref = oracle_ref(c, Wo)
+    for fused in (False, True):
+        check_gpu(c, Wd, ref, label=f"{label} {kind}", fused=fused)
 
 
 SMALL = [
@@ -80,7 +99,8 @@ SMALL = [
     (2100, 256, 256, 16),    # 256-row tiles, ragged
     (700, 256, 320, 64),     # rank 64 (two 32-row shrink blocks)
     (130, 192, 192, 5),      # odd rank, partial column tile, partial k tile
-    (17, 128, 128, 8),       # smallest non-decode M
+    (17, 128, 128, 8),       # forward on the decode kernels (one 16-row chunk and one row)
+    (97, 256, 512, 16),      # smallest forward past the decode chunks
 ]
 
 
@@ -115,8 +135,7 @@ def test_large_tile_path(shape, kind):
     assert (lq.lq_workspace_size(lq.LQ_OP_BWD, M, N, K, r)
             > lq.lq_workspace_size(lq.LQ_OP_BWD_FUSED, M, N, K, r))
     c = wl.small_case(M, N, K, r, seed=M + N + K + r + 7)
-    check_layer(c, kind, merge=False, label="large")
-    check_layer(c, kind, merge=False, bwd=kind == "nf4", label="large-fused", fused=True)
+    check_both_paths(c, kind, label="large")
 
 
 @pytest.mark.parametrize("kind", ["dense", "nf4"])
@@ -126,6 +145,14 @@ def test_decode_small(M, kind):
     check_layer(c, kind, label="decode", bwd=True, merge=False)
     c = wl.small_case(M, 192, 192, 5, seed=200 + M)
     check_layer(c, kind, label="decode-odd", bwd=False, merge=False)
+
+
+@pytest.mark.parametrize("kind", ["dense", "nf4"])
+@pytest.mark.parametrize("M", [1, 16, 96])
+def test_decode_rank64(M, kind):
+    """Ranks past 32 on the decode kernels (the widest T partial layout)."""
+    c = wl.small_case(M, 256, 512, 64, seed=300 + M)
+    check_layer(c, kind, label="decode-r64", bwd=False, merge=False)
 
 
 @pytest.mark.parametrize("kind", ["dense", "nf4"])
@@ -147,16 +174,15 @@ def test_zero_b_is_base_output(M, kind):
     assert torch.count_nonzero(dA).item() == 0
 
 
-def sample_rows(M, n=48, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = rng.choice(M, size=min(n, M), replace=False)
-    return np.unique(np.concatenate([rows, [0, M - 1]]))
-
-
-def test_config3_qlora_full():
-    """QLoRA linear 4096^2, NF4 + DQ base, r = 16, alpha = 32, M = 2048."""
+@pytest.mark.parametrize("kind", ["nf4", "dense"])
+def test_config3_qlora_full(kind):
+    """QLoRA linear 4096^2, r = 16, alpha = 32, M = 2048: the NF4 + DQ base of
+    the workload and, for the fused kernels' dense form, the same weight in
+    bf16; whole tensors through both workspaces and the merge."""
     c = wl.config3()
-    check_layer(c, "nf4", rows=sample_rows(2048), label="config3")
+    check_both_paths(c, kind, label="config3")
+    if kind == "nf4":
+        check_layer(c, kind, bwd=False, label="config3-merge")
 
 
 @pytest.mark.parametrize("M", [1, 4, 16, 48])
@@ -172,19 +198,25 @@ def test_config2_lora_bf16(proj):
     c2 = wl.config2(projections=(proj,))
     p = c2["proj"][proj]
     c = dict(W0=p["W0"], A=p["A"], B=p["B"], dY=p["dY"], X=c2["X"], r=8, alpha=16.0)
-    check_layer(c, "dense", rows=sample_rows(4096, seed=1), label=f"config2-{proj}", merge=False)
+    check_both_paths(c, "dense", label=f"config2-{proj}")
 
 
+@functools.lru_cache(maxsize=1)
+def _config4():
+    return wl.config4(only=("q", "gate", "down"))
+
+
+@pytest.mark.parametrize("kind", ["nf4", "dense"])
 @pytest.mark.parametrize("proj", ["q", "gate", "down"])
-def test_config4_block(proj):
-    """One Llama-2-7B-shaped block, NF4 + DQ base, r = 64, alpha = 128, M = 8192:
-    the three distinct shapes (4096 x 4096, 11008 x 4096, 4096 x 11008)."""
-    c4 = wl.config4(only=(proj,))
+def test_config4_block(proj, kind):
+    """One Llama-2-7B-shaped block, r = 64, alpha = 128, M = 8192: the three
+    distinct shapes (4096 x 4096, 11008 x 4096, 4096 x 11008), with the
+    workload's NF4 + DQ base and the same weight in bf16."""
+    c4 = _config4()
     p = c4["proj"][proj]
     X = c4["X_down"] if proj == "down" else c4["X"]
     c = dict(W0=p["W0"], A=p["A"], B=p["B"], dY=p["dY"], X=X, r=64, alpha=128.0)
-    check_layer(c, "nf4", rows=sample_rows(8192, n=32, seed=4), label=f"config4-{proj}",
-                merge=False)
+    check_both_paths(c, kind, label=f"config4-{proj}")
 
 
 @pytest.mark.parametrize("shape", [(2100, 256, 256, 16), (2048, 5376, 256, 64)],
