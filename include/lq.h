@@ -479,6 +479,16 @@ const char* lq_last_error(void);
 int lq_timing_enable(int32_t on);
 int lq_timing_read(const char* name, double* total_ms, int64_t* launches);
 
+/*
+ * Test aid: the bound, in polls, of every wait in which one workgroup waits
+ * for another inside a kernel (the decode kernel's wait for T; the split-K
+ * partner wait of the large-tile path).  polls <= 0 restores the default
+ * (2^20 polls, tens of milliseconds).  A wait that gives up takes the
+ * fallback its kernel documents.  Applies to launches made after the call.
+ * Returns LQ_OK.
+ */
+int lq_debug_set_wait_limit(int32_t polls);
+
 #ifdef __cplusplus
 }
 #endif

@@ -164,20 +164,25 @@ void dora_side_take(Bump& b, bool nf4, int64_t N, int64_t K, int64_t r, const fl
 
 // Partial sums of T for the decode kernels: kTParts per row, 16-row chunks
 // padded past 16 rows.
-size_t decode_bytes(int64_t M, int64_t r) {
-  const int64_t rows = M <= kDecodeMaxM ? M : (M + kDecodeMaxM - 1) / kDecodeMaxM * kDecodeMaxM;
+// Up to 16 rows: the one-launch decode kernel's partial sums and T; past 16
+// rows: kTParts partial sums per row, 16-row chunks.
+size_t decode_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+  if (M <= kDecodeMaxM) return dispatch::decode1_floats(M, N, K, r) * 4;
+  const int64_t rows = (M + kDecodeMaxM - 1) / kDecodeMaxM * kDecodeMaxM;
   return (size_t)(kTParts * rows * r) * 4;
 }
 
-// The bf16 forward of up to kDecodeChunkMaxM rows by the decode kernels (one
-// launch each, 16-row chunks along the grid's second dimension).
+// The bf16 forward of up to kDecodeChunkMaxM rows by the decode kernels: one
+// launch up to 16 rows, else one launch each of the two chunk kernels, 16-row
+// chunks along the grid's second dimension.
 int decode_chunks(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
                   int64_t r, float s, void* Y, float* T_out, float* Tp, hipStream_t st) {
+  if (M <= kDecodeMaxM) return dispatch::decode_fwd1(X, M, W, A, B, r, s, Y, T_out, Tp, st);
   return dispatch::decode_fwd(X, M, W, A, B, r, s, Y, T_out, Tp, st);
 }
 
 size_t plain_fwd_bytes(int64_t M, int64_t N, int64_t K, int64_t r, bool big) {
-  if (M <= kDecodeChunkMaxM) return decode_bytes(M, r);
+  if (M <= kDecodeChunkMaxM) return decode_bytes(M, N, K, r);
   return big ? dispatch::big_fwd_ws_bytes(M, N, K, r) : 0;
 }
 
@@ -275,6 +280,11 @@ extern "C" {
 
 const char* lq_last_error(void) { return g_err; }
 
+int lq_debug_set_wait_limit(int32_t polls) {
+  dispatch::set_wait_limit(polls);
+  return LQ_OK;
+}
+
 int lq_nf4_codebook(int32_t codebook, float* out) {
   REQUIRE(out != nullptr, LQ_ERR_INVALID_ARG, "out is NULL");
   REQUIRE(codebook == LQ_CB_NF4 || codebook == LQ_CB_NF4_SYMMETRIC, LQ_ERR_INVALID_ARG,
@@ -337,7 +347,7 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
   if (M < 0 || N < 0 || K < 0 || r < 0) return 0;
   switch (op) {
     case LQ_OP_FWD: {  // the decode path's partial sums of T, or float32 T
-      if (M <= kDecodeChunkMaxM) return decode_bytes(M, r);  // never the large-tile path
+      if (M <= kDecodeChunkMaxM) return decode_bytes(M, N, K, r);  // never the large-tile path
       const size_t base = (size_t)(M * r) * 4;
       const size_t big = fwd_big_bytes(M, N, K, r);
       return big > base ? big : base;
@@ -368,7 +378,7 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
     case LQ_OP_DORA_BWD_FUSED:
       return dora_bwd_bytes(M, N, K, r, true, false);
     case LQ_OP_FWD_FUSED:
-      if (M <= kDecodeChunkMaxM) return decode_bytes(M, r);
+      if (M <= kDecodeChunkMaxM) return decode_bytes(M, N, K, r);
       return (size_t)(M * r) * 4;
     case LQ_OP_BWD_FUSED:
       return bwd_ws_bytes(M, N, K, r);
@@ -441,8 +451,8 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
                         (float*)Y, T, stream);
   }
   if (M <= kDecodeChunkMaxM) {  // partial sums of T cross two kernels, per 16-row chunk
-    const size_t need = decode_bytes(M, r);
-    REQUIRE(ws != nullptr && ws_bytes >= need, LQ_ERR_WORKSPACE,
+    const size_t need = decode_bytes(M, W0->N, W0->K, r);
+    REQUIRE(need == 0 || (ws != nullptr && ws_bytes >= need), LQ_ERR_WORKSPACE,
             "workspace %zu bytes, need %zu", ws_bytes, need);
     return decode_chunks(X, M, *W0, A, B, r, scale, Y, T_out, (float*)ws, stream);
   }

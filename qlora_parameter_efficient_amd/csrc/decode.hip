@@ -15,6 +15,10 @@
 // or B^T (B is K x r here, i.e. the reduction runs over B's rows).  Each wave
 // takes 32 rows of Z straight into MFMA registers; the small G tile of each
 // step is staged in LDS (transposed for B).
+#include <atomic>
+#include <map>
+#include <mutex>
+
 #include "device_util.h"
 #include "dispatch.h"
 
@@ -323,6 +327,345 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
       u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
 }
 
+// ------------------------------------------------------------ decode, one launch
+//
+// dq_kernel runs the decode forward (M <= 16) in one launch.  Workgroup b owns
+// output rows 16 b .. 16 b + 15 and streams their NF4 codes as gemv_kernel
+// does (each lane two 32-weight granules per round, every load issued before
+// any is used, dequantised in registers through the LDS level table into
+// v_mfma_f32_16x16x32_bf16, activations staged in LDS).  T = X A^T is formed
+// in the same launch: the first P workgroups ("producers") also reduce one
+// contiguous range of the reduction each (one granule per wave, A fragments
+// loaded with the first weight loads, activations from LDS) and publish their
+// partial sums; after its own weight stream every workgroup adds the P
+// partials in producer order and applies the rank-r expand.
+// Publication without fences: every published float travels as one 64-bit
+// word (call tag, value), written and read with relaxed agent-scope atomics
+// (single-copy atomic, coherent across the XCDs).  A reader accepts a word
+// only when its tag is this call's, so it never needs the writer's other
+// stores to be visible and no ordering between words is required.  The call
+// tag is epoch + 1, with the epoch a word of the stream's slot in library
+// memory that every workgroup reads as its first load.  Each workgroup counts
+// itself in (one of eight counters, by XCD) once that load has returned;
+// workgroup 0, at its end, waits until all have counted in, returns the
+// counters to zero and advances the epoch.  So every workgroup of a call sees
+// the same tag, each call (also each replay of a captured graph) has a new
+// one, and nothing needs clearing between calls.  Every wait is bounded; a
+// workgroup that gives up on the partials computes T itself from X and A (the
+// same value up to summation order), so a call stays correct even then.
+constexpr int kDecSlots = 32;        // streams with their own slot, per device
+constexpr int kDecMaxP = 16;         // producer workgroups at most
+constexpr int kDecMaxT = 16 * 64;    // elements of T at most (M <= 16, r <= 64)
+struct DecSlot {
+  uint32_t epoch;
+  uint32_t pad[31];
+  uint32_t started[8][32];  // workgroups counted in this call, by XCD (one line each)
+  uint64_t part[kDecMaxP * kDecMaxT];  // (tag, partial sum of T) of producer p, element e
+};
+__device__ DecSlot g_dec_slot[kDecSlots];
+
+struct DecParams {
+  const uint16_t* X;  // M x K, M <= 16
+  int64_t M;
+  WeightArgs W;
+  const uint16_t* A;  // r x K
+  const uint16_t* B;  // N x r
+  float* T_out;       // M x r or NULL
+  int32_t r;
+  float s;
+  uint16_t* Y;        // M x N
+  NF4Table tab;
+  int32_t P;          // producer workgroups
+  int32_t slot;
+  int32_t spin;       // bound of a wait for a word, in polls
+};
+
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, float v) {
+  return ((uint64_t)tag << 32) | __float_as_uint(v);
+}
+
+// T straight from X and A in float32 by the 64 lanes of one wave (the fallback
+// of a wait that gave up): element e = m r + j goes to T[64 m + j]
+__device__ __forceinline__ void dec_t_direct(const DecParams& p, float* T) {
+  const int lane = threadIdx.x & 63;
+  const int64_t K = p.W.K;
+  for (int e = lane; e < (int)p.M * p.r; e += 64) {
+    const int m = e / p.r, j = e - m * p.r;
+    float acc = 0.0f;
+    for (int64_t k = 0; k < K; ++k)
+      acc = fmaf(bf16_to_f32(p.X[m * K + k]), bf16_to_f32(p.A[(int64_t)j * K + k]), acc);
+    T[64 * m + j] = acc;
+  }
+}
+
+template <int WK, int XS, int JT>
+__global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
+  constexpr bool XL = XS > 0;
+  constexpr int CH = 2;
+  constexpr int NT = 64 * kGemvWaves;
+  constexpr int XC = XL ? XS / 8 / NT : 1;  // 16-byte X chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t xs[XL ? XS : 8];
+  __shared__ float2 lut[256];
+  __shared__ f32x4 part[kGemvWaves][64];
+  __shared__ float tB[16 * 64];
+  __shared__ float tT[16 * 64];
+  DecSlot* sl = g_dec_slot + p.slot;
+  // the call tag: this call's epoch + 1, read before anything else
+  const uint32_t tag =
+      __hip_atomic_load(&sl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  asm volatile("" ::: "memory");  // keep the epoch load first
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, q = lane >> 4;
+  const int64_t N = p.W.N, K = p.W.K, M = p.M;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int r = p.r, ET = (int)M * r;
+  const int64_t G = K / 32;
+
+  // X chunks first, as gemv_kernel (clamped, branchless)
+  const int64_t nxc = M * K / 8, rowc = K / 8;
+  u32x4 xc[XC];
+  uint32_t xsto[XC];
+  if (XL) {
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      int64_t c = tid + (int64_t)NT * i;
+      c = c < nxc ? c : nxc - 1;
+      xc[i] = *reinterpret_cast<const u32x4*>(p.X + 8 * c);
+      const int64_t m = c / rowc, ch = c - m * rowc;
+      xsto[i] = (uint32_t)(m * K + 8 * (ch ^ (m & 15)));
+    }
+  }
+  // producers: granule g0 + wave of the range [g0, g1) (at most one per wave)
+  const bool producer = (int)blockIdx.x < p.P;
+  const int64_t g0 = producer ? (int64_t)blockIdx.x * G / p.P : 0;
+  const int64_t g1 = producer ? (int64_t)(blockIdx.x + 1) * G / p.P : 0;
+  const bool twave = producer && g0 + wave < g1;  // wave-uniform
+  u32x4 af[JT];
+  if (twave) {
+    const int64_t k = 32 * (g0 + wave) + 8 * q;
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      const int j = 16 * jt + l16;
+      af[jt] = *reinterpret_cast<const u32x4*>(p.A + (int64_t)(j < r ? j : 0) * K + k);
+    }
+  }
+  const int EB = 16 * r;
+  const int tb = tid < EB ? tid : EB - 1;
+  const uint16_t braw = p.B[n0 * r + tb];
+
+  const int64_t n = n0 + l16;
+  const bool mrow = l16 < M;
+  const int64_t xm = mrow ? l16 : 0;
+  f32x4 acc[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const int64_t steps = (G + 3) / 4;
+  u32x4 wraw[CH][WK == kDense ? 4 : 1];
+  uint32_t sq[CH];
+  float sc2[CH];
+  u32x4 xf[CH][4];
+  int64_t kx[CH];
+  bool ok[CH];
+  auto load = [&](int64_t base) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int64_t t = base + kGemvWaves * i;
+      const int64_t g = 4 * t + q;
+      ok[i] = t < steps && g < G;
+      const int64_t k = ok[i] ? 32 * g : 0;
+      const int64_t e = n * K + k;
+      if (WK == kDense) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          wraw[i][d] = *reinterpret_cast<const u32x4*>(p.W.dense + e + 8 * d);
+      } else {
+        wraw[i][0] = *reinterpret_cast<const u32x4*>(p.W.codes + (e >> 1));
+        if (WK == kNF4DQ) {
+          sq[i] = p.W.q8[e >> 6];
+          sc2[i] = p.W.c2[e >> 14];
+        } else {
+          sq[i] = __float_as_uint(p.W.absmax[e >> 6]);
+        }
+      }
+      kx[i] = xm * K + k;
+      if (!XL)
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          xf[i][d] = *reinterpret_cast<const u32x4*>(p.X + kx[i] + 8 * d);
+      else
+        kx[i] = k >> 3;
+      ok[i] = ok[i] && mrow;
+    }
+  };
+  load(wave);
+  if (WK != kDense) build_lut(lut, p.tab);
+  if (XL) {
+#pragma unroll
+    for (int i = 0; i < XC; ++i) *reinterpret_cast<u32x4*>(xs + xsto[i]) = xc[i];
+  }
+  if (tid < EB) {
+    const int nn = tid / r, j = tid - nn * r;
+    tB[nn * 64 + j] = bf16_to_f32(braw);
+  }
+  __syncthreads();  // level table, staged X, B rows
+  // count this workgroup in: its epoch load, issued before the loads waited
+  // for above, has returned (loads complete in order)
+  if (tid == 0)
+    __hip_atomic_fetch_add(&sl->started[blockIdx.x & 7][0], 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+
+  // ---- producers: the partial sums of T over [g0, g1), added over the waves
+  // through LDS one rank tile at a time; lane (q, l16) of a wave holds
+  // T[m = l16][j = 16 jt + 4 q + i]
+  if (producer) {
+    f32x4 ta[JT];
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) ta[jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (twave) {
+      // granules g0 + wave, g0 + wave + 16, ... (the first one's A fragments
+      // were loaded up front)
+      for (int64_t g = g0 + wave; g < g1; g += kGemvWaves) {
+        const int64_t k = 32 * g + 8 * q;
+        u32x4 x;
+        if (XL)
+          x = *reinterpret_cast<const u32x4*>(xs + xm * K + 8 * ((k >> 3) ^ (xm & 15)));
+        else
+          x = *reinterpret_cast<const u32x4*>(p.X + xm * K + k);
+        x = sel4(mrow, x);
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          const int j = 16 * jt + l16;
+          const u32x4 a = g == g0 + wave
+                              ? af[jt]
+                              : *reinterpret_cast<const u32x4*>(p.A + (int64_t)(j < r ? j : 0) * K + k);
+          ta[jt] = mfma16(sel4(j < r, a), x, ta[jt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      part[wave][lane] = ta[jt];
+      __syncthreads();
+      if (wave == 0 && mrow) {
+        f32x4 s4 = part[0][lane];
+        for (int w = 1; w < kGemvWaves; ++w) {
+          const f32x4 o = part[w][lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s4[i] += o[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 16 * jt + 4 * q + i;
+          if (j < r)
+            __hip_atomic_store(&sl->part[blockIdx.x * kDecMaxT + l16 * r + j], tagged(tag, s4[i]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- the weight stream
+  for (int64_t base = wave; base < steps; base += kGemvWaves * CH) {
+    if (base != wave) load(base);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if (XL)
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          xf[i][d] = *reinterpret_cast<const u32x4*>(
+              xs + xm * K + 8 * ((kx[i] + d) ^ (xm & 15)));
+      if (WK == kDense) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) acc[i] = mfma16(wraw[i][d], sel4(ok[i], xf[i][d]), acc[i]);
+      } else {
+        const float a =
+            WK == kNF4DQ ? dq_q_rt(p.W.dq, sq[i]) * dq_step(sc2[i]) : __uint_as_float(sq[i]);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          acc[i] = mfma16(deq8(wraw[i][0][d], a, lut), sel4(ok[i], xf[i][d]), acc[i]);
+      }
+    }
+  }
+  f32x4 a0 = acc[0];
+#pragma unroll
+  for (int i = 1; i < CH; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) a0[v] += acc[i][v];
+  part[wave][lane] = a0;
+
+  // ---- T: thread e < M r reads element e's P partial words (all loads in
+  // flight together), re-reads any that is not yet this call's (bounded), and
+  // adds them in producer order
+  bool got = true;
+  if (tid < ET) {
+    uint64_t v[kDecMaxP];
+#pragma unroll
+    for (int b = 0; b < kDecMaxP; ++b)
+      if (b < p.P)
+        v[b] = __hip_atomic_load(&sl->part[b * kDecMaxT + tid], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    float t = 0.0f;
+#pragma unroll
+    for (int b = 0; b < kDecMaxP; ++b) {
+      if (b < p.P) {
+        int it = 0;
+        while ((uint32_t)(v[b] >> 32) != tag && got) {
+          if (++it > p.spin) got = false;
+          __builtin_amdgcn_s_sleep(1);
+          v[b] = __hip_atomic_load(&sl->part[b * kDecMaxT + tid], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        t += __uint_as_float((uint32_t)v[b]);
+      }
+    }
+    tT[64 * (tid / r) + tid % r] = t;
+  }
+  const bool gave_up = __syncthreads_or(!got);
+  if (wave != 0) return;
+  if (gave_up) dec_t_direct(p, tT);
+  if (blockIdx.x == 0 && p.T_out)
+    for (int e = lane; e < ET; e += 64) p.T_out[e] = tT[64 * (e / r) + e % r];
+  f32x4 sum = part[0][lane];
+#pragma unroll
+  for (int w = 1; w < kGemvWaves; ++w) {
+    const f32x4 o = part[w][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum[i] += o[i];
+  }
+  if (mrow) {
+    const int m = l16;
+    float d[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < r; ++j) {
+      const float t = tT[m * 64 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = fmaf(t, tB[(4 * q + i) * 64 + j], d[i]);
+    }
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = sum[i] + p.s * d[i];
+    *reinterpret_cast<u32x2*>(p.Y + m * N + n0 + 4 * q) =
+        u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+  }
+  // ---- workgroup 0, last: once every workgroup has read the epoch, move it on
+  if (blockIdx.x == 0 && lane == 0) {
+    int it = 0;
+    for (;;) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+        c += __hip_atomic_load(&sl->started[x][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (c >= gridDim.x || ++it > p.spin) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      __hip_atomic_store(&sl->started[x][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&sl->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Partial sums of T = X A^T for one 16-row chunk (blockIdx.y) of up to 64
 // rows, kTParts x 16 x r floats per chunk: workgroup b reduces granules
 // [b G / kTParts, (b + 1) G / kTParts) of the G = K / 32 granules of 32
@@ -427,6 +770,79 @@ int u_only(const void* dY, int64_t M, int64_t N, const void* B, int64_t r, float
                               nzero, st);
   if (e || oscale == 1.0f) return e;
   return launch_t_finish(U, M, r, oscale, 0.0f, nullptr, 0, st);
+}
+
+// Slot of a stream on the current device: one per (device, stream) pair,
+// given out in order of first use; past kDecSlots streams on one device the
+// slots are shared (stream index modulo kDecSlots), so two such streams must
+// not run decode calls at the same time.
+static int stream_slot(hipStream_t st) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, int> slots;
+  static std::map<int, int> used;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lk(mu);
+  const auto key = std::make_pair(dev, st);
+  auto it = slots.find(key);
+  if (it != slots.end()) return it->second;
+  const int id = used[dev]++ % kDecSlots;
+  slots.emplace(key, id);
+  return id;
+}
+
+// producers: enough that each reduces at most one granule per wave (up to
+// kDecMaxP; past that a wave takes several), and at most the grid
+static int dec_producers(int64_t N, int64_t K) {
+  int64_t P = cdiv(K / 32, kGemvWaves);
+  P = P < kDecMaxP ? P : kDecMaxP;
+  return (int)(P < N / 16 ? P : N / 16);
+}
+
+size_t decode1_floats(int64_t, int64_t, int64_t, int64_t) { return 0; }
+
+int decode_fwd1(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
+                int64_t r, float s, void* Y, float* T_out, float*, hipStream_t st) {
+  DecParams p;
+  p.X = (const uint16_t*)X;
+  p.M = M;
+  p.W = weight_args(W);
+  p.A = (const uint16_t*)A;
+  p.B = (const uint16_t*)B;
+  p.T_out = T_out;
+  p.r = (int32_t)r;
+  p.s = s;
+  p.Y = (uint16_t*)Y;
+  p.tab = nf4_table(W.codebook);
+  p.P = dec_producers(W.N, W.K);
+  p.slot = stream_slot(st);
+  p.spin = wait_limit();
+  const dim3 grid((unsigned)(W.N / 16)), block(64 * kGemvWaves);
+  const int64_t mk = M * W.K;
+  const int xs = W.K % 128 ? 0 : mk <= 16384 ? 1 : mk <= 65536 ? 2 : 0;
+  const int jt = r <= 16 ? 0 : r <= 32 ? 1 : 2;
+  const int sel = (weight_format(W) * 3 + xs) * 3 + jt;
+#define LQ_DEC(WKv, XSv, JTv, idx)                                            \
+  case idx:                                                                   \
+    hipLaunchKernelGGL((dq_kernel<WKv, XSv, JTv>), grid, block, 0, st, p);    \
+    break;
+#define LQ_DEC3(WKv, XSv, base) \
+  LQ_DEC(WKv, XSv, 1, base) LQ_DEC(WKv, XSv, 2, base + 1) LQ_DEC(WKv, XSv, 4, base + 2)
+  switch (sel) {
+    LQ_DEC3(kDense, 0, 0)
+    LQ_DEC3(kDense, 16384, 3)
+    LQ_DEC3(kDense, 65536, 6)
+    LQ_DEC3(kNF4DQ, 0, 9)
+    LQ_DEC3(kNF4DQ, 16384, 12)
+    LQ_DEC3(kNF4DQ, 65536, 15)
+    LQ_DEC3(kNF4, 0, 18)
+    LQ_DEC3(kNF4, 16384, 21)
+    LQ_DEC3(kNF4, 65536, 24)
+    default: break;
+  }
+#undef LQ_DEC3
+#undef LQ_DEC
+  return hip_fail(hipGetLastError(), "decode launch");
 }
 
 int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,

@@ -32,11 +32,20 @@ size_t multi_ws_bytes(int64_t T_tokens, int64_t r, int32_t n_adapters);
 
 int bf16_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
              int64_t r, float s, void* Y, float* T_out, hipStream_t st);
-// Decode path (M <= 64, as 16-row chunks in one launch of each kernel): T
-// partial sums (kTParts x M x r floats, M padded to a multiple of 16 past 16
-// rows) go to Tp; T_out (optional) receives T.
+// Chunked decode path (16 < M <= 96, as 16-row chunks in one launch of each
+// of two kernels): T partial sums (kTParts x M x r floats, M padded to a
+// multiple of 16) go to Tp; T_out (optional) receives T.
 int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
                int64_t r, float s, void* Y, float* T_out, float* Tp, hipStream_t st);
+// Decode forward for M <= 16 in one launch (the reduction split over
+// workgroups, T formed inside): part holds decode1_floats(M, N, K, r) floats
+// of partial outputs and partial sums of T.
+size_t decode1_floats(int64_t M, int64_t N, int64_t K, int64_t r);
+int decode_fwd1(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
+                int64_t r, float s, void* Y, float* T_out, float* part, hipStream_t st);
+// Bound (in polls) of the waits for another workgroup; <= 0 restores the default.
+void set_wait_limit(int32_t polls);
+int32_t wait_limit();
 // big_ws: workspace of the large-tile dX path (big_dx_ws_bytes), or NULL for
 // the fused kernel
 int bf16_bwd(const void* dY, const void* X, int64_t M, const lq_weight& W, const void* A,

@@ -50,6 +50,7 @@
 // accumulators (V = T or U rounded to bf16 after scaling by s, E = B or A),
 // then the tile is staged in LDS as bf16 and written with 16-byte stores that
 // cover whole output lines.
+#include <atomic>
 #include <type_traits>
 
 #include "device_util.h"
@@ -74,7 +75,6 @@ struct Shape {
   static constexpr int NST = 2;                           // LDS stages (3 measured no faster)
   static constexpr int DMA = 8 + 2 * JM;                  // loads per wave per step
 };
-constexpr int kSpinLimit = 1 << 22;          // split-K wait bound (s_sleep 2 each)
 
 struct G256Params {
   const uint16_t* P;  // activations, M x KR (X or dY)
@@ -90,6 +90,7 @@ struct G256Params {
   float s;
   int32_t ti, tj, splits, ksteps;
   int32_t tpx;  // split K: tiles per XCD
+  int32_t spin;  // split K: bound of the partner wait, in polls
   int32_t multi;  // multi-adapter forward: E is the concatenated B, read through col_*
   int32_t col_base[kMaxRankCols];
   int32_t col_stride[kMaxRankCols];
@@ -443,7 +444,7 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
     if (tid == 0) {
       int it = 0, rd;
       while ((rd = __hip_atomic_load(fl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
-        if (++it > kSpinLimit) {
+        if (++it > p.spin) {
           __hip_atomic_store(p.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
@@ -524,6 +525,13 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
 
 namespace dispatch {
 
+// The bound of the in-kernel waits between workgroups (polls of s_sleep 2,
+// about 8 ms at the default).
+static std::atomic<int32_t> g_wait_limit{1 << 22};
+
+void set_wait_limit(int32_t polls) { g_wait_limit.store(polls > 0 ? polls : (1 << 22)); }
+int32_t wait_limit() { return g_wait_limit.load(); }
+
 namespace {
 
 // Any M: with the bf16 weight copy in the workspace this path measured faster
@@ -602,6 +610,7 @@ int launch_g256(bool tr, const void* P, const void* Q, const float* V, const voi
   p.flags = (int32_t*)(w + 256);
   p.part = (float*)(w + g256_flag_bytes(M, NI));
   p.tpx = (int32_t)cdiv(pl.tiles, 8);
+  p.spin = wait_limit();
   const unsigned blocks = (unsigned)(p.splits == 2 ? 16 * (int64_t)p.tpx : pl.tiles);
   timing_begin(tr ? "g256_dx" : "g256_fwd", st);
   if (tr) {

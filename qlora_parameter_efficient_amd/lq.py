@@ -86,6 +86,7 @@ _SIGS = {
     "lq_lora_num_params": (_i64, [_i64, _i64, _i64]),
     "lq_last_error": (ctypes.c_char_p, []),
     "lq_timing_enable": (ctypes.c_int, [_i32]),
+    "lq_debug_set_wait_limit": (ctypes.c_int, [_i32]),
     "lq_timing_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_int64)]),
 }
@@ -491,3 +492,8 @@ def lq_timing_read(name):
     ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
     _check(lib().lq_timing_read(name.encode(), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def lq_debug_set_wait_limit(polls):
+    """Bound (in polls) of the in-kernel waits between workgroups; <= 0 restores the default."""
+    _check(lib().lq_debug_set_wait_limit(int(polls)))

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(lq.LIB_PATH),
 
 def test_exports_every_declared_symbol():
     declared = lq.declared_symbols()
-    assert len(declared) == 20
+    assert len(declared) == 21
     L = lq.lib()
     for name in declared:
         assert hasattr(L, name), name
@@ -49,12 +49,15 @@ def test_check_segments():
 
 
 def test_workspace_sizes():
-    # up to 64 rows: the decode kernels, 8 partial sums of T per row (16-row
-    # chunks, rows padded to a multiple of 16 past 16)
-    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 16, 256, 256, 8) == 8 * 16 * 8 * 4
+    # up to 16 rows: the one-launch decode kernel needs no workspace (its
+    # handoff of T lives in the library's per-stream slot)
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 16, 256, 256, 8) == 0
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 4, 4096, 4096, 16) == 0
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, 5, 256, 256, 8) == 0
+    # 17 to 96 rows: the chunk kernels, 8 partial sums of T per row (16-row
+    # chunks, rows padded to a multiple of 16)
     assert lq.lq_workspace_size(lq.LQ_OP_FWD, 33, 256, 256, 8) == 8 * 48 * 8 * 4
     assert lq.lq_workspace_size(lq.LQ_OP_FWD, 90, 256, 256, 8) == 8 * 96 * 8 * 4
-    assert lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, 5, 256, 256, 8) == 8 * 5 * 8 * 4
     assert lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, 97, 256, 256, 8) == 97 * 8 * 4
     # beyond: the default size also holds the large-tile path's bf16 copy of W0
     assert lq.lq_workspace_size(lq.LQ_OP_FWD, 97, 256, 256, 8) >= 97 * 8 * 4 + 256 * 256 * 2
@@ -91,7 +94,7 @@ def test_argument_errors_launch_nothing():
     # dtype mismatch between descriptor and call
     assert _fwd(_weight(dtype=lq.LQ_F32)) == -1
     # missing workspace when T_out is NULL (M > 0)
-    assert _fwd(_weight(), M=8) == -3               # decode path keeps partial sums of T in ws
+    assert _fwd(_weight(), M=40) == -3              # 16-row decode chunks keep partial sums of T in ws
     assert "workspace" in lq.lq_last_error()
     # M = 0 is a no-op
     assert _fwd(_weight(), M=0) == 0
