@@ -4,23 +4,28 @@
 Default run (python bench.py [--steps K] [--warmup W]):
 
 * step = one forward + backward of the QLoRA linear at 4096 x 4096, NF4 base
-  with double quantisation, r = 16, alpha = 32, M = 2048 tokens, bf16 compute.
-  Forward: NF4 -> bf16 weight copy, T = X A^T, then the large-tile product
-  with the expand.  Backward: the same for dX (U = dY B), then the dA / dB
-  reductions.  value = algorithmic fwd+bwd FLOPs / wall time per step, the
-  step launched eagerly (the same step replayed from a HIP graph is reported
-  beside it: on this stack the replay is not faster).  The default 1000 timed
-  steps (about 0.2 s) spread the start-up of the timed region (about 1 ms in
-  all, measured) to about 1 us per step; with 50 steps it would add 20 us to
-  each.
+  with double quantisation, r = 16, alpha = 32, M = 2048 tokens, bf16 compute,
+  with the workspaces that select the fastest path.  Forward: one launch
+  dequantises NF4 to a bf16 copy in the workspace and forms T = X A^T, then
+  the large-tile product with the expand.  Backward: the same for dX (U =
+  dY B), then the dA / dB reductions.  value = algorithmic fwd+bwd FLOPs /
+  wall time per step, the step launched eagerly; the GPU-event time of the
+  same timed region and the step replayed from a HIP graph are reported
+  beside it.  The step first runs untimed for CLOCK_WARMUP_S seconds so that
+  the clocks have settled, and the shader clock is sampled from sysfs during
+  the timed region.
 * roofline: the dominant kernel -- the large-tile product of the forward or
   of dX, whichever is slower (each does 2 M N K + 2 M N r FLOPs: the product
   and the rank-r expand) -- timed with HIP events that the library records
   around its launches on the launch stream (lq_timing_enable), algorithmic
-  FLOPs per launch / average duration, against the bf16 dense MFMA peak;
-  traffic (HBM bytes per launch) from rocprofv3 FETCH_SIZE / WRITE_SIZE
-  counters scaled by the same counters on a plain copy, when they were taken
-  on the current kernel source.
+  FLOPs per launch / average duration, against the bf16 dense MFMA peak, and
+  against that peak scaled to the sampled clock; traffic (HBM bytes per
+  launch) from rocprofv3 FETCH_SIZE / WRITE_SIZE counters scaled by the same
+  counters on a plain copy, when they were taken on the current kernel
+  source.  Beside it: the forward with the smaller workspace (NF4 dequantised
+  inside the product's K loop, no bf16 copy of W0) and with none (the fused
+  kernel), and roofline["decode"]: NF4 decode at M = 1, weight-stream bytes
+  per graph-replayed call over 40 cold weight copies, against the HBM peak.
 * cpu_baseline: the CPU oracle (float64 NumPy) on the same step.
 * secondary lines in the same JSON object: NF4 decode (M = 1, 4, 16) GB/s on
   the weight stream with cold weights, merge, quantise, multi-adapter, the
@@ -30,8 +35,8 @@ Default run (python bench.py [--steps K] [--warmup W]):
   backward of config 2 (q and v, bf16, M = 4096, r = 8) and of config 4 (the
   seven projections of a block, NF4, M = 8192, r = 64).
 
-Profiling helpers (for rocprofv3): --mode fwd | dx | step | decode | copy | quant
-run only that part, a few iterations, and print one line.
+Profiling helpers (for rocprofv3): --mode fwd | fwd_inloop | dx | step | decode
+| copy | quant run only that part, a few iterations, and print one line.
 """
 from __future__ import annotations
 
@@ -99,6 +104,57 @@ def cuda_time(fn, iters, torch):
 
 
 CLOCK_WARMUP_S = 0.5
+PEAK_SCLK_MHZ = 2400.0         # the clock the peak figures assume
+
+
+class SclkSampler:
+    """Samples the shader clock the driver reports (the starred level of
+    pp_dpm_sclk in sysfs, which carries the current frequency) every few
+    milliseconds from a background thread while the block runs; ``mhz`` is
+    the median of the samples, or None where the file is unreadable."""
+
+    def __init__(self, period_s=0.005):
+        import glob
+        import threading
+        self.files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def read(self):
+        import re
+        for f in self.files:
+            try:
+                with open(f) as fh:
+                    for line in fh:
+                        if line.rstrip().endswith("*"):
+                            m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                            if m:
+                                return float(m.group(1))
+            except OSError:
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self.read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+        return False
+
+    @property
+    def mhz(self):
+        return statistics.median(self.samples) if self.samples else None
 
 
 def spin_sync(ev, torch):
@@ -135,6 +191,8 @@ def setup(torch):
                           device=dev)
     S["wsf"] = torch.empty(lq.lq_workspace_size(lq.LQ_OP_FWD, M, N, K, R), dtype=torch.uint8,
                            device=dev)
+    S["wsi"] = torch.empty(lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, M, N, K, R),
+                           dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     return S
 
@@ -142,6 +200,19 @@ def setup(torch):
 def fwd(S):
     lq = S["lq"]
     lq.lq_lora_fwd(S["X"], S["W"], S["A"], S["B"], S["s"], T_out=S["T"], Y=S["Y"], ws=S["wsf"])
+
+
+def fwd_inloop(S):
+    """The forward with the smaller workspace: NF4 dequantised inside the
+    product's K loop, no bf16 copy of W0."""
+    lq = S["lq"]
+    lq.lq_lora_fwd(S["X"], S["W"], S["A"], S["B"], S["s"], T_out=S["T"], Y=S["Y"], ws=S["wsi"])
+
+
+def fwd_fused(S):
+    """The forward with no workspace: the fused kernel (T in the same K loop)."""
+    lq = S["lq"]
+    lq.lq_lora_fwd(S["X"], S["W"], S["A"], S["B"], S["s"], T_out=S["T"], Y=S["Y"], no_ws=True)
 
 
 def bwd(S):
@@ -279,11 +350,11 @@ def graph_time(fn, torch, calls=20, replays=10):
     return t
 
 
-def secondary(S, torch):
+def secondary(S, torch, dec=None):
     import numpy as np
     lq = S["lq"]
     res = {}
-    res["decode_nf4"] = decode_bench(S, torch)
+    res["decode_nf4"] = dec if dec is not None else decode_bench(S, torch)
     # forwards of 32 and 64 rows (16-row decode chunks), graph-launched, warm weights
     from qlora_parameter_efficient_amd import workloads as wlc
     chunks = {}
@@ -458,7 +529,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--mode", default="full",
-                    choices=["full", "step", "fwd", "dx", "decode", "copy", "quant"])
+                    choices=["full", "step", "fwd", "fwd_inloop", "dx", "decode", "copy", "quant"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-secondary", action="store_true")
     a = ap.parse_args(argv)
@@ -492,6 +563,12 @@ def main(argv=None):
             fwd(S)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "fwd", "launches": a.steps}))
+        return 0
+    if a.mode == "fwd_inloop":
+        for _ in range(a.steps):
+            fwd_inloop(S)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "fwd_inloop", "launches": a.steps}))
         return 0
     if a.mode == "dx":
         for _ in range(a.steps):
@@ -531,13 +608,14 @@ def main(argv=None):
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(a.steps):
-        step(S)
-    ev1.record()
-    spin_sync(ev1, torch)
-    wall = time.perf_counter() - t0
+    with SclkSampler() as clk:
+        t0 = time.perf_counter()
+        ev0.record()
+        for _ in range(a.steps):
+            step(S)
+        ev1.record()
+        spin_sync(ev1, torch)
+        wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / a.steps
     ev_ms_per_step = ev0.elapsed_time(ev1) / a.steps
     value = STEP_FLOP / (wall / a.steps) / 1e12
@@ -559,18 +637,23 @@ def main(argv=None):
     lq = S["lq"]
     t_fwd_call = cuda_time(lambda: fwd(S), 50, torch)
     t_dx_call = cuda_time(lambda: dx_only(S), 50, torch)
+    t_inloop_call = cuda_time(lambda: fwd_inloop(S), 50, torch)
+    t_fused_call = cuda_time(lambda: fwd_fused(S), 20, torch)
     t_step_ev = cuda_time(lambda: step(S), 20, torch)
     lq.lq_timing_enable(True)
-    lq.lq_timing_read("g256_fwd")
-    lq.lq_timing_read("g256_dx")
-    for _ in range(50):
-        fwd(S)
-        dx_only(S)
-    torch.cuda.synchronize()
+    for k in ("g256_fwd", "g256_dx", "q256_fwd"):
+        lq.lq_timing_read(k)
+    with SclkSampler() as kclk:
+        for _ in range(50):
+            fwd(S)
+            dx_only(S)
+            fwd_inloop(S)
+        torch.cuda.synchronize()
     ms_f, n_f = lq.lq_timing_read("g256_fwd")
     ms_d, n_d = lq.lq_timing_read("g256_dx")
+    ms_q, n_q = lq.lq_timing_read("q256_fwd")
     lq.lq_timing_enable(False)
-    t_fwd, t_dx = ms_f / max(n_f, 1), ms_d / max(n_d, 1)
+    t_fwd, t_dx, t_q = ms_f / max(n_f, 1), ms_d / max(n_d, 1), ms_q / max(n_q, 1)
     if t_dx > t_fwd:
         name, t_dom = "g256_kernel<dX> (bf16 product dY Wd + expand, 256x128 tiles)", t_dx
         traffic = traffic_for("g256_dx", G256_SOURCES)
@@ -582,9 +665,25 @@ def main(argv=None):
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "flop_per_launch": G256_FLOP, "us_per_launch": round(t_dom * 1e3, 2),
+            "sclk_mhz": kclk.mhz,
+            "frac_at_sclk": (round(achieved / (PEAK_BF16_TFLOPS * kclk.mhz / PEAK_SCLK_MHZ), 4)
+                             if kclk.mhz else None),
             "launches_timed": min(n_f, n_d),
             "us_fwd_kernel": round(t_fwd * 1e3, 2), "us_dx_kernel": round(t_dx * 1e3, 2),
-            "us_fwd_call": round(t_fwd_call * 1e3, 2), "us_dx_call": round(t_dx_call * 1e3, 2)}
+            "us_fwd_call": round(t_fwd_call * 1e3, 2), "us_dx_call": round(t_dx_call * 1e3, 2),
+            "us_fwd_inloop_kernel": round(t_q * 1e3, 2),
+            "us_fwd_inloop_call": round(t_inloop_call * 1e3, 2),
+            "us_fwd_fused_call": round(t_fused_call * 1e3, 2)}
+    # NF4 decode at M = 1: weight-stream bytes per call over the graph-replayed
+    # call time with cold weights, against the HBM peak
+    dec = decode_bench(S, torch)
+    d1 = dec["M1"]
+    roof["decode"] = {"kernel": "dq_kernel (NF4 decode, T formed in the same launch), M=1",
+                      "bound": "hbm", "achieved": d1["weight_stream_GBs_graph_cold"],
+                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(d1["weight_stream_GBs_graph_cold"] / PEAK_HBM_GBS, 4),
+                      "bytes_per_call": NF4_STREAM_BYTES,
+                      "us_per_call": d1["us_per_call_graph_cold"], "traffic": None}
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -596,13 +695,14 @@ def main(argv=None):
            "gpu_event_ms_per_step_steady": round(t_step_ev, 4),
            "clock_warmup_steps": n_clock,
            "graph_ms_per_step": round(ms_graph, 4),
+           "sclk_mhz_timed_region": clk.mhz, "sclk_samples": len(clk.samples),
            "roofline": roof}
     if not a.no_cpu:
         log("timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(S)
     if not a.no_secondary:
         log("secondary measurements ...")
-        out["secondary"] = secondary(S, torch)
+        out["secondary"] = secondary(S, torch, dec)
     print(json.dumps(out), flush=True)
     return 0
 

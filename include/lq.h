@@ -180,16 +180,24 @@ int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
  *   ws / ws_bytes: device workspace (caller-owned, contents not preserved).
  *   lq_workspace_size(LQ_OP_FWD, M, N, K, r, 0) bytes select the fastest
  *   path; lq_workspace_size(LQ_OP_FWD_FUSED, ...) is the smallest workspace
- *   that works.  The decode path (dt = LQ_BF16, M <= 96, run as chunks of up
- *   to 16 rows) needs 8 M' r floats of partial sums of T (M' = M up to 16,
- *   else M rounded up to a multiple of 16), the float32 path M r floats of T
- *   when T_out is NULL; otherwise ws may be NULL.
+ *   that works.  The decode path (dt = LQ_BF16, M <= 96) needs no workspace
+ *   up to 16 rows (one launch; T is formed inside it); 17 to 96 rows run as
+ *   16-row chunks and need 8 M' r floats of partial sums of T (M' = M rounded
+ *   up to a multiple of 16).  The float32 path needs M r floats of T when
+ *   T_out is NULL; otherwise ws may be NULL.
  *   dt = LQ_BF16: bf16 inputs, float32 accumulation, bf16 RNE output; W0 dense
- *   bf16 or NF4.  With the LQ_OP_FWD size at M > 16 and N % 256 == 0 the
- *   large-tile path runs: NF4 W0 is first dequantised (bit-exactly, as
- *   lq_nf4_dequantize) to a bf16 copy inside ws, then multiplied; otherwise
- *   the fused kernels dequantise NF4 in registers / LDS and never write a
- *   dense W0.  Both give "dequantise, then multiply in bf16".
+ *   bf16 or NF4.  Past the decode rows, the path follows the workspace:
+ *     - at least the LQ_OP_FWD size, N % 256 == 0: the large-tile path; an
+ *       NF4 W0 is first dequantised (bit-exactly, as lq_nf4_dequantize) to a
+ *       bf16 copy inside ws, then multiplied (fastest);
+ *     - at least M r floats (the LQ_OP_FWD_FUSED size), NF4 W0 with
+ *       N % 128 == 0, K % 256 == 0 and at least 192 tiles of 128 x 256: T
+ *       into T_out (or ws), then a product that dequantises the codes inside
+ *       its K loop; no dense W0 is ever written;
+ *     - otherwise the fused kernels (T in the same K loop, NF4 dequantised in
+ *       registers / LDS, no dense W0 either).
+ *   All three give "dequantise, then multiply in bf16" with identical
+ *   dequantised values.
  *   Requires K % 64 == 0, N % 64 == 0, N, K <= 65536, M*K and M*N < 2^31,
  *   1 <= r <= 64.  M <= 96 takes the memory-bound decode path, 16 rows at a
  *   time (each chunk streams W0 once).

@@ -459,6 +459,8 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
   const size_t big = fwd_big_bytes(M, W0->N, W0->K, r);
   if (big && ws && ws_bytes >= big)
     return dispatch::big_fwd(X, M, *W0, A, B, r, scale, Y, T_out, ws, stream);
+  if (ws && ws_bytes >= (size_t)(M * r) * 4 && dispatch::inloop_fwd_eligible(*W0, M))
+    return dispatch::inloop_fwd(X, M, *W0, A, B, r, scale, Y, T_out ? T_out : (float*)ws, stream);
   return dispatch::bf16_fwd(X, M, *W0, A, B, r, scale, Y, T_out, stream);
 }
 

@@ -89,6 +89,13 @@ size_t big_dx_ws_bytes(int64_t M, int64_t N, int64_t K);
 int big_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,
             float s, void* Y, float* T_out, void* ws, hipStream_t st, const void* Xa = nullptr,
             float inv_keep = 1.0f);
+// Large-M NF4 forward with no copy of W0: T (M x r float32, written to T),
+// then the 128 x 256-tile product that dequantises the codes inside its K loop
+// and adds the expand in its epilogue.  Eligible for an NF4 weight with
+// N % 128 == 0, K % 256 == 0 and at least 192 tiles.
+bool inloop_fwd_eligible(const lq_weight& W, int64_t M);
+int inloop_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
+               int64_t r, float s, void* Y, float* T, hipStream_t st);
 // Multi-adapter forward at large T (same eligibility as the forward).
 size_t big_multi_ws_bytes(int64_t T, int64_t N, int64_t K, int64_t rc);
 int big_fwd_multi(const void* X, int64_t T, const lq_weight& W, const void* A_cat,

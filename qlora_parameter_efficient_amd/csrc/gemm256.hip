@@ -118,6 +118,18 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t l
       : "memory");
 }
 
+// 4 bytes per lane from global memory (base + off) straight into LDS at
+// m0 + 4 * lane (same rules as dma16).
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory");
+}
+
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // wait until at most N of this wave's loads are outstanding
@@ -521,6 +533,357 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Forward with the NF4 weight dequantised inside the K loop (no bf16 copy of
+// W0 anywhere): Y = X deq(W0)^T + (s T) B^T.
+//
+// Tile 128 (weight rows n) x 256 (activation rows m); wave (wi, wj) owns the
+// 64 x 128 block at (64 wi, 128 wj): 2 x 4 accumulators of 32 x 32 (128
+// registers).  Per 64-wide reduction step (one NF4 block per weight row):
+//   * the activation tile (256 rows x 128 bytes) goes straight into LDS by
+//     direct-to-LDS loads, as in g256_kernel;
+//   * the NF4 codes of the weight tile, the blocks' 8-bit constants and c2
+//     come by direct-to-LDS loads too, in groups of four steps (a whole
+//     128-byte line of codes per row), one group ahead, into two code
+//     buffers; during the step before the one that uses them, thread t
+//     forms the block's 16 possible bf16 values RNE(fl32(cb[i] a')), a' =
+//     fl32(q8 fl32(c2 / 127)), as byte planes in registers, looks its 32
+//     weights up with v_perm_b32 (four codes per instruction, one code word
+//     per substep; no LDS traffic for the table) and stores them as bf16 into
+//     the weight tile of the other LDS stage (128-byte rows, the same chunk
+//     swizzle as the activations).  With every global load issued by the
+//     kernel itself, the waits are its own: the end of a step waits until
+//     only the code group loads issued in it (if any) are outstanding.
+//     Whole-line code loads keep the lines the load path touches per step
+//     below those of a bf16 weight tile.
+// Each code is thus dequantised once per 256 activation rows, in registers,
+// and fed to bf16 MFMA from LDS.  The expand runs in the epilogue as in
+// g256_kernel; the tile is staged in LDS as bf16 and written with 16-byte
+// stores.
+constexpr int kQI = 128, kQJ = 256;
+constexpr int kQWT = kQI * kGK * 2;  // weight tile of one step: 16 KB
+constexpr int kQAT = kQJ * kGK * 2;  // activation tile: 32 KB
+constexpr int kQStage = kQWT + kQAT;
+
+struct Q256Params {
+  const uint16_t* P;  // X, M x K
+  WeightArgs W;       // NF4 weight, N x K
+  const float* V;     // T, M x r
+  const uint16_t* E;  // B, N x r
+  uint16_t* Y;        // M x N
+  int64_t M, N, K;
+  int32_t r;
+  float s;
+  int32_t ti, tj;
+  NF4Table tab;
+};
+
+// Per-block level table in registers: the 16 bf16 results t_i =
+// RNE(fl32(cb[i] a')) of one NF4 block, as byte planes (lo[k] holds the low
+// bytes of t_4k .. t_4k+3, hi[k] the high bytes), so that one v_perm_b32
+// looks up four codes at once.
+struct PermTable {
+  uint32_t lo[4], hi[4];
+};
+
+__device__ __forceinline__ PermTable perm_table(const NF4Table& tab, float a) {
+  uint32_t pr[8];  // bf16 pairs (t_2k, t_2k+1)
+#pragma unroll
+  for (int k = 0; k < 8; ++k) pr[k] = pack_bf16x2(tab.cb[2 * k] * a, tab.cb[2 * k + 1] * a);
+  PermTable t;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // bytes 0, 2 of pr[2k] and of pr[2k + 1]; bytes 1, 3 for the high plane
+    t.lo[k] = __builtin_amdgcn_perm(pr[2 * k + 1], pr[2 * k], 0x06040200u);
+    t.hi[k] = __builtin_amdgcn_perm(pr[2 * k + 1], pr[2 * k], 0x07050301u);
+  }
+  return t;
+}
+
+// one byte plane for four codes (one per byte of c, values 0..15): the byte
+// of t_code for each
+__device__ __forceinline__ uint32_t perm_plane(const uint32_t (&pl)[4], uint32_t c7, uint32_t s2) {
+  const uint32_t a = __builtin_amdgcn_perm(pl[1], pl[0], c7);  // codes 0..7
+  const uint32_t b = __builtin_amdgcn_perm(pl[3], pl[2], c7);  // codes 8..15
+  return __builtin_amdgcn_perm(b, a, s2);                       // by bit 3 of each code
+}
+
+// Eight codes (element e in bits 4e .. 4e + 3) -> the eight bf16 values t_code
+// in natural element order (bit-identical to deq8 with the same a')
+__device__ __forceinline__ u32x4 perm_deq8(uint32_t w, const PermTable& t) {
+  const uint32_t ce = w & 0x0F0F0F0Fu, co = (w >> 4) & 0x0F0F0F0Fu;  // elements 0,2,4,6 / 1,3,5,7
+  const uint32_t ce7 = ce & 0x07070707u, co7 = co & 0x07070707u;
+  const uint32_t es2 = ((ce >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t os2 = ((co >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t le = perm_plane(t.lo, ce7, es2), he = perm_plane(t.hi, ce7, es2);
+  const uint32_t lo = perm_plane(t.lo, co7, os2), ho = perm_plane(t.hi, co7, os2);
+  const uint32_t x01 = __builtin_amdgcn_perm(he, le, 0x05010400u);  // (e0, e2)
+  const uint32_t x23 = __builtin_amdgcn_perm(he, le, 0x07030602u);  // (e4, e6)
+  const uint32_t y01 = __builtin_amdgcn_perm(ho, lo, 0x05010400u);  // (e1, e3)
+  const uint32_t y23 = __builtin_amdgcn_perm(ho, lo, 0x07030602u);  // (e5, e7)
+  return u32x4{__builtin_amdgcn_perm(y01, x01, 0x05040100u), __builtin_amdgcn_perm(y01, x01, 0x07060302u),
+               __builtin_amdgcn_perm(y23, x23, 0x05040100u), __builtin_amdgcn_perm(y23, x23, 0x07060302u)};
+}
+
+__device__ __forceinline__ void write16(uint32_t addr, const u32x4& v) {
+  typedef __attribute__((address_space(3))) u32x4* lds_ptr;
+  *(lds_ptr)(uintptr_t)addr = v;
+}
+
+template <int WK>
+__global__ __launch_bounds__(kGThreads) void q256_fwd_kernel(Q256Params p) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kQStage];
+  __shared__ __attribute__((aligned(1024))) char cst[2 * (16384 + 1024 + 2048)];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wi = wave & 1, wj = wave >> 1;
+  const int h = lane >> 5, l32 = lane & 31;
+  // tiles in activation-row order, so that an XCD's contiguous range of
+  // tiles shares one activation tile (its rows stay in that XCD's L2)
+  const int t = xcd_tile(blockIdx.x, p.ti * p.tj);
+  const int tile_j = t / p.ti, tile_i = t - tile_j * p.ti;
+  const int64_t i0 = (int64_t)tile_i * kQI, j0 = (int64_t)tile_j * kQJ;
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int KT = (int)(K / kGK);
+  const uint32_t sbase = lds_addr(smem);
+
+  // activation DMA: wave w fills rows 64 w .. 64 w + 63, 8 rows per instruction
+  uint32_t poff[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int row = 64 * wave + 8 * u + (lane >> 3);
+    int64_t m = j0 + row;
+    m = m < M ? m : M - 1;
+    poff[u] = (uint32_t)((m * K + 8 * ((lane & 7) ^ rswz(row))) * 2);
+  }
+  const char* pbase0 = reinterpret_cast<const char*>(p.P);
+  auto issue_act = [&](int kt, int b) {
+    const uint32_t at = sbase + b * kQStage + kQWT;
+    const char* pb = pbase0 + (int64_t)kt * kGK * 2;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dma16(pb, poff[u], at + (64 * wave + 8 * u) * 128);
+  };
+  // Weight codes and block constants arrive by direct-to-LDS loads as well,
+  // in groups of four steps (one 128-byte line of codes per row): the
+  // group's codes (128 rows x 128 bytes; chunk c of row x at physical chunk
+  // c ^ (x & 7)), the dword of 8-bit constants of each row that holds the
+  // group's four blocks, and each row's c2 (or float32 absmax) for the four
+  // steps.  Group g + 1 is loaded during step 4 g + 1 into the other of two
+  // code buffers; thread t then dequantises row t / 2, weights 32 (t & 1) ..
+  // + 31 of each block, from LDS.
+  constexpr int kCB = 16384 + 1024 + 2048;  // code buffer: codes, constants, c2 [step][row]
+  constexpr int NGD = (WK == kNF4DQ ? 1 : 0) + 6;  // group loads per wave
+  const uint32_t cbase = lds_addr(cst);
+  const int64_t KB = K / 64;
+  const int NG = KT / 4;
+  const int wx = tid >> 1, wh = tid & 1;
+  uint32_t coff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = 32 * wave + 8 * u + (lane >> 3);
+    coff[u] = (uint32_t)((((i0 + row) * K) >> 1) + 16 * ((lane & 7) ^ (row & 7)));
+  }
+  const int crow = (64 * wave + lane) & (kQI - 1);
+  const uint32_t qoff = (uint32_t)((i0 + crow) * KB);
+  int64_t sblk[2];  // block of the c2 entry this lane brings for group 0: (row, step j)
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int e = (2 * wave + v) * 64 + lane;
+    sblk[v] = (i0 + (e & 127)) * KB + (e >> 7);
+  }
+  uint32_t wdst[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) wdst[d] = (uint32_t)(wx * 128 + (((4 * wh + d) ^ rswz(wx)) << 4));
+  auto issue_group = [&](int g, int buf) {
+    const uint32_t cb = cbase + buf * kCB;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      dma16(reinterpret_cast<const char*>(p.W.codes) + (int64_t)g * 128, coff[u],
+            cb + (32 * wave + 8 * u) * 128);
+    if (WK == kNF4DQ) dma4(p.W.q8 + 4 * g, qoff, cb + 16384 + 256 * wave);
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int64_t blk = sblk[v] + 4 * g;
+      const uint32_t at = cb + 17408 + 256 * (2 * wave + v);
+      if (WK == kNF4DQ)
+        dma4(p.W.c2, (uint32_t)((blk >> 8) * 4), at);
+      else
+        dma4(p.W.absmax, (uint32_t)(blk * 4), at);
+    }
+  };
+  // this thread's code words (one per substep) and block scale for the step
+  // at position pos of the group in code buffer buf
+  auto codes_at = [&](int buf, int pos) {
+    typedef __attribute__((address_space(3))) const u32x4* lp;
+    const int ch = (2 * pos + wh) ^ (wx & 7);
+    return *(lp)(uintptr_t)(cbase + buf * kCB + wx * 128 + ch * 16);
+  };
+  auto scale_at = [&](int buf, int pos) {
+    typedef __attribute__((address_space(3))) const uint32_t* lp;
+    const uint32_t cb = cbase + buf * kCB;
+    const float v = __uint_as_float(*(lp)(uintptr_t)(cb + 17408 + 4 * (128 * pos + wx)));
+    if (WK == kNF4DQ) {
+      const uint32_t qw = *(lp)(uintptr_t)(cb + 16384 + 4 * wx);
+      return dq_q_rt(p.W.dq, (qw >> (8 * pos)) & 0xFFu) * dq_step(v);
+    }
+    return v;
+  };
+
+  // operand reads (128-byte-row tiles, as g256_kernel)
+  const int sw = rswz(l32);
+  uint32_t pcx[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) pcx[s] = (uint32_t)(((2 * s + h) ^ sw) << 4);
+  const uint32_t prow = (uint32_t)((128 * wj + l32) * 128);
+  const uint32_t qrow = (uint32_t)((64 * wi + l32) * 128);
+  auto load_frags = [&](uint32_t st, int s, u32x4 (&wf)[2], u32x4 (&xf)[4]) {
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) xf[ms] = read16(st + kQWT + prow + ms * 32 * 128 + pcx[s]);
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns) wf[ns] = read16(st + qrow + ns * 32 * 128 + pcx[s]);
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+  // prologue: step 0's tiles in stage 0, group 0's codes in code buffer 0
+  issue_act(0, 0);
+  issue_group(0, 0);
+  wait_dma();
+  __syncthreads();
+  {
+    const u32x4 cw = codes_at(0, 0);
+    const PermTable pt = perm_table(p.tab, scale_at(0, 0));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) write16(sbase + wdst[d], perm_deq8(cw[d], pt));
+  }
+  __syncthreads();
+
+  // Step kt (J = kt mod 8: stage J & 1, code buffer J >> 2, position J & 3):
+  // the activation loads of step kt + 1, in position 1 the loads of the next
+  // code group, the words of step kt + 1 dequantised (one word per substep,
+  // after the substep's MFMAs) into the other weight tile, the MFMAs of step
+  // kt; at the end, wait for everything but the code group loads issued in
+  // this step.  Unrolled by eight so that every LDS address is a base plus an
+  // immediate.
+  auto step = [&](int kt, auto jj) {
+    constexpr int J = decltype(jj)::value;
+    constexpr int B = J & 1, POS = J & 3, BUF = J >> 2;
+    constexpr int NPOS = (POS + 1) & 3, NBUF = POS == 3 ? BUF ^ 1 : BUF;  // step kt + 1
+    const bool more = kt + 1 < KT;
+    if (more) issue_act(kt + 1, B ^ 1);
+    const bool grp = POS == 1 && (kt >> 2) + 1 < NG;
+    if (grp) issue_group((kt >> 2) + 1, BUF ^ 1);
+    const uint32_t st = sbase + B * kQStage;
+    const uint32_t wt = sbase + (B ^ 1) * kQStage;
+    u32x4 cw = u32x4{0u, 0u, 0u, 0u};
+    float a = 0.0f;
+    if (more) {
+      cw = codes_at(NBUF, NPOS);
+      a = scale_at(NBUF, NPOS);
+    }
+    u32x4 wf[2][2], xf[2][4];
+    load_frags(st, 0, wf[0], xf[0]);
+    const PermTable pt = perm_table(p.tab, a);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c = s & 1;
+      if (s < 3) load_frags(st, s + 1, wf[c ^ 1], xf[c ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);  // next substep's reads ahead of this one's work
+#pragma unroll
+      for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf[c][ms], acc[ns][ms]);
+      if (more) write16(wt + wdst[s], perm_deq8(cw[s], pt));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (grp)
+      wait_dma_but<NGD>();
+    else
+      wait_dma();
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  using I6 = std::integral_constant<int, 6>;
+  using I7 = std::integral_constant<int, 7>;
+  int kt = 0;
+  for (; kt + 8 <= KT; kt += 8) {
+    step(kt, I0{});
+    step(kt + 1, I1{});
+    step(kt + 2, I2{});
+    step(kt + 3, I3{});
+    step(kt + 4, I4{});
+    step(kt + 5, I5{});
+    step(kt + 6, I6{});
+    step(kt + 7, I7{});
+  }
+  if (kt < KT) {  // KT % 4 == 0: one more group of four
+    step(kt, I0{});
+    step(kt + 1, I1{});
+    step(kt + 2, I2{});
+    step(kt + 3, I3{});
+  }
+
+  // ---- expand: acc += B rows x bf16(s T) over rank chunks of 16
+  const int r = p.r;
+  for (int c = 0; c < r; c += 16) {
+    const int jr = c + 8 * h;
+    u32x4 ef[2], vf[4];
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns) {
+      const int64_t i = i0 + 64 * wi + 32 * ns + l32;
+      ef[ns] = e_operand_row(p.E + i * r, jr, r);
+    }
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) {
+      int64_t m = j0 + 128 * wj + 32 * ms + l32;
+      m = m < M ? m : M - 1;
+      vf[ms] = v_operand(p.V + m * r, jr, r, p.s);
+    }
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) acc[ns][ms] = mfma32(ef[ns], vf[ms], acc[ns][ms]);
+  }
+
+  // ---- store: bf16 tile in LDS (row j of 256 bytes; chunk c at c ^ (j & 15)),
+  // then whole 256-byte output row segments with 16-byte stores
+  __syncthreads();
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) {
+    const int j = 128 * wj + 32 * ms + l32;
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 64 * wi + 32 * ns + 8 * q + 4 * h;  // 4 outputs i .. i + 3
+        const uint32_t a = sbase + (uint32_t)(j * 256 + (((i >> 3) ^ (j & 15)) << 4) + (i & 7) * 2);
+        typedef __attribute__((address_space(3))) u32x2* lds_ptr;
+        *(lds_ptr)(uintptr_t)a = u32x2{pack_bf16x2(acc[ns][ms][4 * q], acc[ns][ms][4 * q + 1]),
+                                       pack_bf16x2(acc[ns][ms][4 * q + 2], acc[ns][ms][4 * q + 3])};
+      }
+  }
+  __syncthreads();
+  const int cl = tid & 15;
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int j = 16 * it + (tid >> 4);
+    const int64_t m = j0 + j;
+    const u32x4 v = read16(sbase + (uint32_t)(j * 256 + ((cl ^ (j & 15)) << 4)));
+    if (m < M) *reinterpret_cast<u32x4*>(p.Y + m * N + i0 + 8 * cl) = v;
+  }
+}
+
 }  // namespace
 
 namespace dispatch {
@@ -624,6 +987,39 @@ int launch_g256(bool tr, const void* P, const void* Q, const float* V, const voi
   return hip_fail(hipGetLastError(), "g256 launch");
 }
 
+// The NF4 forward with the dequantisation in the K loop: enough 128 x 256
+// tiles to fill the chip, whole 128-row weight tiles.
+bool q256_fwd_fits(const lq_weight& W, int64_t M) {
+  return W.kind == LQ_WEIGHT_NF4 && W.N % kQI == 0 && W.K % 256 == 0 &&
+         (W.N / kQI) * cdiv(M, kQJ) >= 192 && (double)M * W.K * 2 < 4294967296.0;
+}
+
+int launch_q256_fwd(const void* X, int64_t M, const lq_weight& W, const float* T, const void* B,
+                    int64_t r, float s, void* Y, hipStream_t st) {
+  Q256Params p{};
+  p.P = (const uint16_t*)X;
+  p.W = weight_args(W);
+  p.V = T;
+  p.E = (const uint16_t*)B;
+  p.Y = (uint16_t*)Y;
+  p.M = M;
+  p.N = W.N;
+  p.K = W.K;
+  p.r = (int32_t)r;
+  p.s = s;
+  p.ti = (int32_t)(W.N / kQI);
+  p.tj = (int32_t)cdiv(M, kQJ);
+  p.tab = nf4_table(W.codebook);
+  const unsigned blocks = (unsigned)(p.ti * p.tj);
+  timing_begin("q256_fwd", st);
+  if (W.double_quant)
+    hipLaunchKernelGGL((q256_fwd_kernel<kNF4DQ>), dim3(blocks), dim3(kGThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((q256_fwd_kernel<kNF4>), dim3(blocks), dim3(kGThreads), 0, st, p);
+  timing_end(st);
+  return hip_fail(hipGetLastError(), "q256 launch");
+}
+
 // the NF4 weight dequantised to bf16 into the workspace at q (when the prep
 // kernel cannot take the shrink as well)
 int bf16_weight(const lq_weight& W, void* q, hipStream_t st) {
@@ -667,6 +1063,15 @@ int big_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const v
     e = t_only(Z, M, K, A, r, T, st, (int32_t*)gws, nz, inv_keep);
   if (e) return e;
   return launch_g256(false, X, Q, T, B, M, N, K, r, s, Y, gws, st);
+}
+
+bool inloop_fwd_eligible(const lq_weight& W, int64_t M) { return q256_fwd_fits(W, M); }
+
+int inloop_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
+               int64_t r, float s, void* Y, float* T, hipStream_t st) {
+  int e = t_only(X, M, W.K, A, r, T, st, nullptr, 0, 1.0f);
+  if (e) return e;
+  return launch_q256_fwd(X, M, W, T, B, r, s, Y, st);
 }
 
 int big_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,

@@ -237,7 +237,9 @@ def _ws(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def lq_lora_fwd(X, W0, A, B, scale, T_out=None, ws=None, Y=None, fused=False):
+def lq_lora_fwd(X, W0, A, B, scale, T_out=None, ws=None, Y=None, fused=False, no_ws=False):
+    """``fused``: allocate the LQ_OP_FWD_FUSED workspace instead of the
+    LQ_OP_FWD one; ``no_ws``: pass no workspace at all."""
     _dev(X, A, B, T_out)
     dt = _dt(X)
     M = X.shape[0]
@@ -245,7 +247,7 @@ def lq_lora_fwd(X, W0, A, B, scale, T_out=None, ws=None, Y=None, fused=False):
     if Y is None:
         Y = torch.empty((M, ws_struct.N), dtype=X.dtype, device=X.device)
     r = A.shape[0]
-    if ws is None:
+    if ws is None and not no_ws:
         need = lq_workspace_size(LQ_OP_FWD_FUSED if fused else LQ_OP_FWD, M, ws_struct.N,
                                  ws_struct.K, r)
         if need:

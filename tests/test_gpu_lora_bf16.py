@@ -45,14 +45,18 @@ def oracle_ref(c, Wo, bwd=True):
     return ref
 
 
-def check_gpu(c, Wd, ref, label="", fused=False):
-    """The GPU layer on the same inputs against ``ref`` over whole tensors."""
+def check_gpu(c, Wd, ref, label="", fused=False, no_ws=False):
+    """The GPU layer on the same inputs against ``ref`` over whole tensors.
+    ``fused``: the LQ_OP_*_FUSED workspaces (for an NF4 forward at large M,
+    the product that dequantises in its K loop); ``no_ws``: a forward with no
+    workspace (the fused forward kernel)."""
     s = c["alpha"] / c["r"]
     X, A, B = to_dev(c["X"]), to_dev(c["A"]), to_dev(c["B"])
     M, r = X.shape[0], A.shape[0]
-    announce(f"bf16 fwd {label} fused={fused} M={M} N={ref['Y'].shape[1]} K={X.shape[1]} r={r}")
+    announce(f"bf16 fwd {label} fused={fused} no_ws={no_ws} M={M} N={ref['Y'].shape[1]} "
+             f"K={X.shape[1]} r={r}")
     T = torch.empty((M, r), dtype=torch.float32, device=X.device)
-    Y = lq.lq_lora_fwd(X, Wd, A, B, s, T_out=T, fused=fused)
+    Y = lq.lq_lora_fwd(X, Wd, A, B, s, T_out=T, fused=fused, no_ws=no_ws)
     torch.cuda.synchronize()
     for name, got, want in (("Y", Y, ref["Y"]), ("T", T, ref["T"])):
         e = rel_err(f64(got), want)
@@ -87,11 +91,15 @@ def check_layer(c, kind, bwd=True, merge=True, label="", fused=False):
 
 
 def check_both_paths(c, kind, label):
-    """Default and fused-kernel workspaces on one oracle reference."""
+    """Default and fused-kernel workspaces on one oracle reference; for an NF4
+    base also the forward with no workspace (the fused kernel where the
+    smaller workspace selects the K-loop dequantising product)."""
     Wd, Wo = base_for(c, kind)
     ref = oracle_ref(c, Wo)
     for fused in (False, True):
         check_gpu(c, Wd, ref, label=f"{label} {kind}", fused=fused)
+    if kind == "nf4":
+        check_gpu(c, Wd, dict(Y=ref["Y"], T=ref["T"]), label=f"{label} {kind}", no_ws=True)
 
 
 SMALL = [
@@ -116,13 +124,18 @@ def test_small(shape, kind):
 
 
 # Shapes that take the large-tile path (256 x 256 tiles, bf16 weight copy in
-# the workspace) with the default workspace, and the fused kernels with the
-# smaller LQ_OP_*_FUSED workspace.
+# the workspace) with the default workspace; with the smaller LQ_OP_*_FUSED
+# workspace the fused kernels, or for an NF4 forward with enough 128 x 256
+# tiles the product that dequantises in its K loop.
 LARGE = [
     (2100, 256, 256, 16),    # split K (9 tiles), ragged last row tile
     (2304, 512, 768, 5),     # split K, odd rank, three 256-wide dX tiles
     (2048, 5376, 256, 64),   # 256 x 128 forward tiles, no split; rank 64
     (4096, 3072, 256, 16),   # 256 x 256 forward tiles
+    (2100, 3072, 768, 16),   # NF4, small workspace: 128 x 256 tiles dequantised in the K
+                             # loop, ragged M, three four-step code groups
+    (2048, 3072, 256, 64),   # NF4 in the K loop at rank 64 (four expand chunks of 16)
+    (2100, 3072, 320, 16),   # reduction not a multiple of 256: fused kernels instead
 ]
 
 
@@ -132,8 +145,9 @@ def test_large_tile_path(shape, kind):
     M, N, K, r = shape
     assert (lq.lq_workspace_size(lq.LQ_OP_FWD, M, N, K, r)
             > lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, M, N, K, r))
-    assert (lq.lq_workspace_size(lq.LQ_OP_BWD, M, N, K, r)
-            > lq.lq_workspace_size(lq.LQ_OP_BWD_FUSED, M, N, K, r))
+    if K % 256 == 0:  # dX on the large-tile path: output width K in 256-wide tiles
+        assert (lq.lq_workspace_size(lq.LQ_OP_BWD, M, N, K, r)
+                > lq.lq_workspace_size(lq.LQ_OP_BWD_FUSED, M, N, K, r))
     c = wl.small_case(M, N, K, r, seed=M + N + K + r + 7)
     check_both_paths(c, kind, label="large")
 
