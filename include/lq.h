@@ -234,6 +234,28 @@ int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0,
                 int32_t accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * lq_lora_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as lq_lora_bwd with a workspace of exactly
+ * LQ_NOALLOC_SCRATCH_BYTES bytes, except that the workspace is a static
+ * device array of that size inside the library (one per GPU, held from the
+ * library's load until the process ends) rather than a caller buffer.  The
+ * call allocates nothing (no hipMalloc / hipFree, no allocating library
+ * routine); its first call on a device looks up that device's address of the
+ * array once.  A backward whose smallest workspace (the LQ_OP_BWD_FUSED size)
+ * exceeds LQ_NOALLOC_SCRATCH_BYTES returns LQ_ERR_WORKSPACE before any
+ * launch; where the LQ_OP_BWD size fits as well, dX takes the large-tile
+ * path.  All calls on one GPU share the array: calls that overlap in time on
+ * one GPU (several streams, several host threads) race and must be ordered
+ * by the caller.  Timing (lq_timing_enable) must be off.
+ */
+#define LQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int lq_lora_bwd_noalloc(const void* dY, const void* X, int64_t M, const lq_weight* W0,
+                        const void* A, const void* B, int64_t r, float scale, lq_dtype dt,
+                        const float* T_saved, void* dX, float* dA, float* dB,
+                        int32_t accumulate, hipStream_t stream);
+
+/*
  * Forward with LoRA-input dropout ([L26] "Putting It Together": the adapter
  * configuration's lora_dropout; the pages give the setting, and the operation
  * is read as inverted dropout on the adapter branch's input):

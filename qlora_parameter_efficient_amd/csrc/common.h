@@ -43,6 +43,7 @@ int hip_fail(hipError_t e, const char* where);
 // Event brackets around a kernel launch (no-ops unless lq_timing_enable).
 void timing_begin(const char* name, hipStream_t st);
 void timing_end(hipStream_t st);
+bool timing_enabled();
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

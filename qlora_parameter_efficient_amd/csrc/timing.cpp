@@ -57,6 +57,11 @@ void timing_end(hipStream_t st) {
   g_pending = nullptr;
 }
 
+bool timing_enabled() {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return g_on;
+}
+
 }  // namespace lq
 
 extern "C" {

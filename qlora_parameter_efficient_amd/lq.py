@@ -26,6 +26,7 @@ LQ_OP_FWD_MULTI_FUSED = 5
 LQ_OP_FWD_DROPOUT, LQ_OP_FWD_DROPOUT_FUSED, LQ_OP_BWD_DROPOUT, LQ_OP_BWD_DROPOUT_FUSED = 6, 7, 8, 9
 LQ_OP_DORA_FWD, LQ_OP_DORA_FWD_FUSED, LQ_OP_DORA_BWD, LQ_OP_DORA_BWD_FUSED = 10, 11, 12, 13
 LQ_DQ_NONE, LQ_DQ_INT8, LQ_DQ_FP8 = 0, 1, 2
+LQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 LQ_CB_NF4, LQ_CB_NF4_SYMMETRIC = 0, 1
 DQ_FORMATS = {"int8": LQ_DQ_INT8, "fp8": LQ_DQ_FP8}
 CODEBOOKS = {"nf4": LQ_CB_NF4, "nf4_symmetric": LQ_CB_NF4_SYMMETRIC}
@@ -65,6 +66,8 @@ _SIGS = {
     "lq_lora_fwd": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i64, _f32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "lq_lora_bwd": (ctypes.c_int, [_vp, _vp, _i64, _WP, _vp, _vp, _i64, _f32, _i32, _vp, _vp, _vp,
                                    _vp, _i32, _vp, _sz, _vp]),
+    "lq_lora_bwd_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _WP, _vp, _vp, _i64, _f32, _i32, _vp,
+                                           _vp, _vp, _vp, _i32, _vp]),
     "lq_lora_merge": (ctypes.c_int, [_WP, _vp, _vp, _i64, _f32, _i32, _vp, _vp]),
     "lq_dora_fwd": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i64, _f32, _vp, _i32, _vp, _vp, _vp,
                                    _vp, _vp, _sz, _vp]),
@@ -277,6 +280,20 @@ def lq_lora_bwd(dY, X, W0, A, B, scale, T_saved=None, need_dx=True, dA=None, dB=
     _check(lib().lq_lora_bwd(_ptr(dY), _ptr(X), M, ctypes.byref(w), _ptr(A), _ptr(B), r, scale, dt,
                              _ptr(T_saved), _ptr(dX), _ptr(dA), _ptr(dB), int(accumulate),
                              _ptr(ws), ws.numel(), _stream()))
+    return dX, dA, dB
+
+
+def lq_lora_bwd_noalloc(dY, X, W0, A, B, scale, dX, dA=None, dB=None, T_saved=None,
+                        accumulate=False):
+    """lq_lora_bwd with the library's static workspace: the outputs are the
+    caller's (dX required; dA and dB both or neither) and nothing is
+    allocated."""
+    _dev(dY, X, A, B, T_saved, dA, dB, dX)
+    dt = _dt(dY)
+    w = weight_struct(W0, dt)
+    _check(lib().lq_lora_bwd_noalloc(_ptr(dY), _ptr(X), dY.shape[0], ctypes.byref(w), _ptr(A),
+                                     _ptr(B), A.shape[0], scale, dt, _ptr(T_saved), _ptr(dX),
+                                     _ptr(dA), _ptr(dB), int(accumulate), _stream()))
     return dX, dA, dB
 
 

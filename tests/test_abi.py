@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(lq.LIB_PATH),
 
 def test_exports_every_declared_symbol():
     declared = lq.declared_symbols()
-    assert len(declared) == 21
+    assert len(declared) == 22
     L = lq.lib()
     for name in declared:
         assert hasattr(L, name), name
@@ -225,3 +225,28 @@ def test_timing_read_without_launches():
     assert lq.lq_timing_read("g256_fwd") == (0.0, 0)
     lq.lq_timing_enable(False)
     assert lq.lib().lq_timing_read(None, None, None) == -1
+
+
+def test_noalloc_backward_rejects_past_the_static_size():
+    """The backward on the library's static workspace refuses a layer whose
+    smallest workspace exceeds LQ_NOALLOC_SCRATCH_BYTES, before any HIP call
+    (the pointers here are never dereferenced)."""
+    N = K = 8192
+    M, r = 65536, 64
+    need = lq.lq_workspace_size(lq.LQ_OP_BWD_FUSED, M, N, K, r)
+    assert need > lq.LQ_NOALLOC_SCRATCH_BYTES
+    w = lq.LqWeightStruct()
+    w.kind, w.dtype, w.N, w.K = lq.LQ_WEIGHT_DENSE, lq.LQ_BF16, N, K
+    w.dense = 256
+    rc = lq.lib().lq_lora_bwd_noalloc(256, 256, M, w, 256, 256, r, 1.0, lq.LQ_BF16, None, 256, 256,
+                                      256, 0, None)
+    assert rc == -3
+    assert "static workspace" in lq.lib().lq_last_error().decode()
+    assert lq.lib().lq_lora_bwd_noalloc(256, 256, M, None, 256, 256, r, 1.0, lq.LQ_BF16, None,
+                                        256, 256, 256, 0, None) == -1
+
+
+def test_noalloc_size_matches_header():
+    text = open(lq.HEADER).read()
+    assert "#define LQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert lq.LQ_NOALLOC_SCRATCH_BYTES == 64 << 20
