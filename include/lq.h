@@ -510,14 +510,26 @@ int lq_timing_enable(int32_t on);
 int lq_timing_read(const char* name, double* total_ms, int64_t* launches);
 
 /*
- * Test aid: the bound, in polls, of every wait in which one workgroup waits
- * for another inside a kernel (the decode kernel's wait for T; the split-K
- * partner wait of the large-tile path).  polls <= 0 restores the default
- * (2^20 polls, tens of milliseconds).  A wait that gives up takes the
- * fallback its kernel documents.  Applies to launches made after the call.
- * Returns LQ_OK.
+ * Test aids for the waits in which one workgroup waits for data another
+ * workgroup of the same launch publishes: the decode kernel's wait for the
+ * partial sums of T, and the split-K partner wait of the large-tile path.
+ * Every such wait is bounded, and one that gives up is counted on the device.
+ * A decode workgroup that gives up computes T itself from X and A, so the
+ * output stays correct.  A split-K workgroup that gives up leaves its
+ * partner's partial sums unread, so its output tile holds half of the
+ * reduction: a nonzero count means such a call's output is not to be used.
+ * Neither happens in normal operation (the partner is already past its own
+ * reduction when the wait starts).
+ * lq_debug_set_wait_limit: the bound, in polls, for launches made after the
+ * call.  polls > 0 sets it; 0 restores the default (2^22 polls, about a tenth
+ * of a second); polls < 0 makes every such wait give up at once, which runs
+ * the fallbacks deterministically.  Returns LQ_OK.
+ * lq_debug_wait_giveups: synchronises the current device, stores in *count
+ * the number of waits that gave up on it since the last call, and clears that
+ * number.  LQ_ERR_INVALID_ARG if count is NULL; LQ_ERR_HIP on a HIP error.
  */
 int lq_debug_set_wait_limit(int32_t polls);
+int lq_debug_wait_giveups(int64_t* count);
 
 #ifdef __cplusplus
 }

@@ -285,6 +285,16 @@ int lq_debug_set_wait_limit(int32_t polls) {
   return LQ_OK;
 }
 
+int lq_debug_wait_giveups(int64_t* count) {
+  REQUIRE(count != nullptr, LQ_ERR_INVALID_ARG, "count is NULL");
+  int rc = hip_fail(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  uint64_t a = 0, b = 0;
+  if (!rc) rc = dispatch::take_g256_giveups(&a);
+  if (!rc) rc = dispatch::take_decode_giveups(&b);
+  *count = rc ? 0 : (int64_t)(a + b);
+  return rc;
+}
+
 int lq_nf4_codebook(int32_t codebook, float* out) {
   REQUIRE(out != nullptr, LQ_ERR_INVALID_ARG, "out is NULL");
   REQUIRE(codebook == LQ_CB_NF4 || codebook == LQ_CB_NF4_SYMMETRIC, LQ_ERR_INVALID_ARG,

@@ -351,8 +351,12 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
 // counters to zero and advances the epoch.  So every workgroup of a call sees
 // the same tag, each call (also each replay of a captured graph) has a new
 // one, and nothing needs clearing between calls.  Every wait is bounded; a
-// workgroup that gives up on the partials computes T itself from X and A (the
-// same value up to summation order), so a call stays correct even then.
+// workgroup that gives up on the partials counts the give-up
+// (lq_debug_wait_giveups) and computes T itself from X and A (the same value
+// up to summation order), so a call stays correct even then.  The bound set
+// by lq_debug_set_wait_limit applies to that wait only; workgroup 0's wait
+// before it advances the epoch keeps the default bound, since advancing early
+// would hand a late workgroup the next call's tag.
 constexpr int kDecSlots = 32;        // streams with their own slot, per device
 constexpr int kDecMaxP = 16;         // producer workgroups at most
 constexpr int kDecMaxT = 16 * 64;    // elements of T at most (M <= 16, r <= 64)
@@ -363,6 +367,8 @@ struct DecSlot {
   uint64_t part[kDecMaxP * kDecMaxT];  // (tag, partial sum of T) of producer p, element e
 };
 __device__ DecSlot g_dec_slot[kDecSlots];
+// waits for T words that gave up since the host last read the count
+__device__ unsigned long long g_dec_giveups;
 
 struct DecParams {
   const uint16_t* X;  // M x K, M <= 16
@@ -377,7 +383,7 @@ struct DecParams {
   NF4Table tab;
   int32_t P;          // producer workgroups
   int32_t slot;
-  int32_t spin;       // bound of a wait for a word, in polls
+  int32_t spin;       // bound of a wait for a word, in polls (< 0: give up at once)
 };
 
 __device__ __forceinline__ uint64_t tagged(uint32_t tag, float v) {
@@ -598,8 +604,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
   // ---- T: thread e < M r reads element e's P partial words (all loads in
   // flight together), re-reads any that is not yet this call's (bounded), and
   // adds them in producer order
-  bool got = true;
-  if (tid < ET) {
+  bool got = p.spin >= 0;
+  if (tid < ET && got) {
     uint64_t v[kDecMaxP];
 #pragma unroll
     for (int b = 0; b < kDecMaxP; ++b)
@@ -624,7 +630,11 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
   }
   const bool gave_up = __syncthreads_or(!got);
   if (wave != 0) return;
-  if (gave_up) dec_t_direct(p, tT);
+  if (gave_up) {
+    if (lane == 0)
+      __hip_atomic_fetch_add(&g_dec_giveups, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    dec_t_direct(p, tT);
+  }
   if (blockIdx.x == 0 && p.T_out)
     for (int e = lane; e < ET; e += 64) p.T_out[e] = tT[64 * (e / r) + e % r];
   f32x4 sum = part[0][lane];
@@ -656,7 +666,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
 #pragma unroll
       for (int x = 0; x < 8; ++x)
         c += __hip_atomic_load(&sl->started[x][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (c >= gridDim.x || ++it > p.spin) break;
+      if (c >= gridDim.x || ++it > dispatch::kDefaultWaitPolls) break;
       __builtin_amdgcn_s_sleep(1);
     }
 #pragma unroll
@@ -800,6 +810,14 @@ static int dec_producers(int64_t N, int64_t K) {
 }
 
 size_t decode1_floats(int64_t, int64_t, int64_t, int64_t) { return 0; }
+
+int take_decode_giveups(uint64_t* n) {
+  unsigned long long v = 0, z = 0;
+  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_dec_giveups), sizeof(v));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(g_dec_giveups), &z, sizeof(z));
+  *n = v;
+  return hip_fail(e, "decode give-up count");
+}
 
 int decode_fwd1(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
                 int64_t r, float s, void* Y, float* T_out, float*, hipStream_t st) {

@@ -38,14 +38,21 @@ int bf16_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const 
 int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
                int64_t r, float s, void* Y, float* T_out, float* Tp, hipStream_t st);
 // Decode forward for M <= 16 in one launch (the reduction split over
-// workgroups, T formed inside): part holds decode1_floats(M, N, K, r) floats
-// of partial outputs and partial sums of T.
+// workgroups, T formed inside; no workspace: decode1_floats is 0).
 size_t decode1_floats(int64_t M, int64_t N, int64_t K, int64_t r);
 int decode_fwd1(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
                 int64_t r, float s, void* Y, float* T_out, float* part, hipStream_t st);
-// Bound (in polls) of the waits for another workgroup; <= 0 restores the default.
+// Bound (in polls) of a workgroup's wait for data another workgroup publishes
+// (the decode kernel's T words, the split-K partner's partial sums): polls > 0
+// sets it, 0 restores the default, < 0 makes every such wait give up at once
+// (wait_limit() is then -1).  Every wait that gives up takes its kernel's
+// fallback and is counted; take_*_giveups return the device's count since the
+// last read and clear it.
+constexpr int32_t kDefaultWaitPolls = 1 << 22;
 void set_wait_limit(int32_t polls);
 int32_t wait_limit();
+int take_g256_giveups(uint64_t* n);
+int take_decode_giveups(uint64_t* n);
 // big_ws: workspace of the large-tile dX path (big_dx_ws_bytes), or NULL for
 // the fused kernel
 int bf16_bwd(const void* dY, const void* X, int64_t M, const lq_weight& W, const void* A,

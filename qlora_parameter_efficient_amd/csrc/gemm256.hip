@@ -40,11 +40,13 @@
 //
 // Split K.  When there are fewer tiles than compute units, each tile's
 // reduction is split between two workgroups.  The first to finish publishes
-// its float32 accumulators to a per-tile slot and a ready flag; the second
-// adds them to its own and finishes the tile.  The second only ever waits for
-// a workgroup that is already past its main loop, so the wait cannot
-// deadlock; it is also bounded, and a timeout is recorded in an error word.
-// The flags return to zero before the kernel ends, ready for the next call.
+// its float32 accumulators to a per-tile slot (device-scope release) and a
+// ready flag; the second acquires them, adds them to its own and finishes the
+// tile.  The second only ever waits for a workgroup that is already past its
+// main loop, so the wait cannot deadlock; it is also bounded, and a wait that
+// gives up is counted on the device (lq_debug_wait_giveups), the tile then
+// being incomplete.  The kernel that forms T or U clears the flags before each
+// launch.
 //
 // Epilogue.  The expand adds (s V) E as extra MFMAs on the finished
 // accumulators (V = T or U rounded to bf16 after scaling by s, E = B or A),
@@ -84,7 +86,6 @@ struct G256Params {
   uint16_t* Y;        // M x NI
   float* part;        // split-K slots, Shape<JM>::Slot floats per tile
   int32_t* flags;     // split-K (arrivals, ready) per tile, zero between calls
-  int32_t* err;       // set to 1 if a split-K wait gave up
   int64_t M, NI, KR;
   int32_t r;
   float s;
@@ -95,6 +96,10 @@ struct G256Params {
   int32_t col_base[kMaxRankCols];
   int32_t col_stride[kMaxRankCols];
 };
+
+// split-K waits that gave up since the host last read the count (one
+// counter per device)
+__device__ unsigned long long g_wait_giveups;
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
@@ -256,8 +261,9 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
   const int64_t i0 = (int64_t)tile_i * kGT, j0 = (int64_t)tile_j * S::TJ;
   const int64_t M = p.M, NI = p.NI, KR = p.KR;
   const int KT = (int)(KR / kGK);
-  const int kt0 = split * p.ksteps;
-  const int kt1 = (kt0 + p.ksteps) < KT ? (kt0 + p.ksteps) : KT;
+  // this split's reduction steps [ka, kb)
+  const int ka = split * p.ksteps;
+  const int kb = (ka + p.ksteps) < KT ? (ka + p.ksteps) : KT;
 
   const uint32_t sbase = lds_addr(smem);
   // stage b: weight tile at sbase + b * S::Stage, activation tile + kTileBytes
@@ -367,7 +373,7 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
   constexpr int NST = S::NST;
   auto step = [&](int kt, auto stage) {
     constexpr int B = decltype(stage)::value;
-    const bool more = kt + NST - 1 < kt1;
+    const bool more = kt + NST - 1 < kb;
     if (more && JM == 2) issue(kt + NST - 1, (B + NST - 1) % NST);
     const uint32_t st = sbase + B * S::Stage;
     u32x4 wf[2][4], xf[2][JM];
@@ -392,40 +398,51 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  if (kt0 < kt1) {
-    issue(kt0, 0);
-    if (NST > 2 && kt0 + 1 < kt1) {
-      issue(kt0 + 1, 1);
+  if (ka < kb) {
+    issue(ka, 0);
+    if (NST > 2 && ka + 1 < kb) {
+      issue(ka + 1, 1);
       wait_dma_but<S::DMA>();
     } else {
       wait_dma();
     }
     __syncthreads();
-    int kt = kt0;
+    int kt = ka;
     if (NST == 2) {
-      for (; kt + 1 < kt1; kt += 2) {
+      for (; kt + 1 < kb; kt += 2) {
         step(kt, I0{});
         step(kt + 1, I1{});
       }
-      if (kt < kt1) step(kt, I0{});
+      if (kt < kb) step(kt, I0{});
     } else {
-      for (; kt + 2 < kt1; kt += 3) {
+      for (; kt + 2 < kb; kt += 3) {
         step(kt, I0{});
         step(kt + 1, I1{});
         step(kt + 2, I2{});
       }
-      if (kt < kt1) step(kt, I0{});
-      if (kt + 1 < kt1) step(kt + 1, I1{});
+      if (kt < kb) step(kt, I0{});
+      if (kt + 1 < kb) step(kt + 1, I1{});
     }
   }
 
-  // ---- split-K: the second workgroup of a tile to finish completes it.
-  // Only relaxed device-scope atomics touch the flags, so no whole-L2
-  // write-back or invalidation is needed.  When the partner is known to run on
-  // this XCD (its XCD published at its start), the partial sums stay in the
-  // shared L2: plain stores, a wait for their completion, then the ready flag
-  // (1).  Otherwise (partner elsewhere or not started) they are published with
-  // a device-scope release (ready = 2) and read after an acquire.
+  // ---- split K: the second workgroup of a tile to arrive completes it.
+  // Only device-scope atomics touch the flags.  The first to arrive publishes
+  // its float32 accumulators to the tile's slot.  When its partner is known
+  // to run on this XCD (each workgroup publishes its XCD at its start), the
+  // two share one L2: plain stores, a wait until every store has reached that
+  // L2 (vmcnt 0 in every wave), a barrier, then ready = 1 -- a device-scope
+  // release would also write back every dirty line of the XCD's L2, which
+  // measured far slower.  Otherwise every thread releases at device scope
+  // before the barrier and ready = 2.  The second workgroup polls ready
+  // (relaxed loads, bounded) and then acquires at device scope in either
+  // case, which orders its reads of the slot after the flag and drops stale
+  // L1 lines; a barrier then hands the slot to all its threads.  The first to
+  // arrive is already past its main loop, so the wait is short and cannot
+  // deadlock.  A wait that still gives up (or that the host forced to give
+  // up) is counted on the device (lq_debug_wait_giveups) and the slot is left
+  // unread: the tile then holds this workgroup's half of the reduction only,
+  // and the nonzero count tells the caller so.  The kernel that forms T / U
+  // clears the flags before every launch.
   if (p.splits > 1) {
     if (tid == 0) {
       const int old = __hip_atomic_fetch_add(fl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -448,36 +465,36 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
       if (mode == 1)
         wait_dma();  // the stores have reached the L2 shared with the partner
       else
-        __threadfence();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __syncthreads();
       if (tid == 0) __hip_atomic_store(fl + 1, mode, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
     if (tid == 0) {
-      int it = 0, rd;
-      while ((rd = __hip_atomic_load(fl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
-        if (++it > p.spin) {
-          __hip_atomic_store(p.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
+      bool ok = p.spin >= 0;  // a negative bound: give up at once (test aid)
+      int it = 0;
+      while (ok && __hip_atomic_load(fl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        if (++it > p.spin) ok = false;
         __builtin_amdgcn_s_sleep(2);
       }
-      s_ready = rd;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __hip_atomic_store(fl + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (ok)
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      else
+        __hip_atomic_fetch_add(&g_wait_giveups, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_ready = ok;
     }
     __syncthreads();
-    if (s_ready == 2) __threadfence();
+    if (s_ready) {
 #pragma unroll
-    for (int a = 0; a < 4 * JM; ++a)
+      for (int a = 0; a < 4 * JM; ++a)
 #pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const f32x4 y = slot[((wave * 4 * JM + a) * 4 + v4) * 64 + lane];
-        f32x16& x = acc[a / JM][a % JM];
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const f32x4 y = slot[((wave * 4 * JM + a) * 4 + v4) * 64 + lane];
+          f32x16& x = acc[a / JM][a % JM];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * v4 + e] += y[e];
-      }
+          for (int e = 0; e < 4; ++e) x[4 * v4 + e] += y[e];
+        }
+    }
   }
 
   // ---- expand: acc += E-operand x (s V)-operand over rank chunks of 16
@@ -890,10 +907,20 @@ namespace dispatch {
 
 // The bound of the in-kernel waits between workgroups (polls of s_sleep 2,
 // about 8 ms at the default).
-static std::atomic<int32_t> g_wait_limit{1 << 22};
+static std::atomic<int32_t> g_wait_limit{kDefaultWaitPolls};
 
-void set_wait_limit(int32_t polls) { g_wait_limit.store(polls > 0 ? polls : (1 << 22)); }
+void set_wait_limit(int32_t polls) {
+  g_wait_limit.store(polls > 0 ? polls : polls == 0 ? kDefaultWaitPolls : -1);
+}
 int32_t wait_limit() { return g_wait_limit.load(); }
+
+int take_g256_giveups(uint64_t* n) {
+  unsigned long long v = 0, z = 0;
+  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_wait_giveups), sizeof(v));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(g_wait_giveups), &z, sizeof(z));
+  *n = v;
+  return hip_fail(e, "split-K give-up count");
+}
 
 namespace {
 
@@ -969,7 +996,6 @@ int launch_g256(bool tr, const void* P, const void* Q, const float* V, const voi
   p.splits = pl.splits;
   p.ksteps = (int32_t)cdiv(KR / kGK, p.splits);
   char* w = (char*)ws;
-  p.err = (int32_t*)w;
   p.flags = (int32_t*)(w + 256);
   p.part = (float*)(w + g256_flag_bytes(M, NI));
   p.tpx = (int32_t)cdiv(pl.tiles, 8);

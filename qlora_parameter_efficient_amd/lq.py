@@ -90,6 +90,7 @@ _SIGS = {
     "lq_last_error": (ctypes.c_char_p, []),
     "lq_timing_enable": (ctypes.c_int, [_i32]),
     "lq_debug_set_wait_limit": (ctypes.c_int, [_i32]),
+    "lq_debug_wait_giveups": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int64)]),
     "lq_timing_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_int64)]),
 }
@@ -514,5 +515,13 @@ def lq_timing_read(name):
 
 
 def lq_debug_set_wait_limit(polls):
-    """Bound (in polls) of the in-kernel waits between workgroups; <= 0 restores the default."""
+    """Bound (in polls) of the in-kernel waits between workgroups: > 0 sets it,
+    0 restores the default, < 0 makes every such wait give up at once."""
     _check(lib().lq_debug_set_wait_limit(int(polls)))
+
+
+def lq_debug_wait_giveups():
+    """Waits that gave up on the current device since the last call (synchronises)."""
+    n = ctypes.c_int64(0)
+    _check(lib().lq_debug_wait_giveups(ctypes.byref(n)))
+    return n.value

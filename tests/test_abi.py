@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(lq.LIB_PATH),
 
 def test_exports_every_declared_symbol():
     declared = lq.declared_symbols()
-    assert len(declared) == 22
+    assert len(declared) == 23
     L = lq.lib()
     for name in declared:
         assert hasattr(L, name), name
