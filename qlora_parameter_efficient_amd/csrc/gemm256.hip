@@ -554,25 +554,26 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
 // Forward with the NF4 weight dequantised inside the K loop (no bf16 copy of
 // W0 anywhere): Y = X deq(W0)^T + (s T) B^T.
 //
-// Tile 128 (weight rows n) x 256 (activation rows m); wave (wi, wj) owns the
-// 64 x 128 block at (64 wi, 128 wj): 2 x 4 accumulators of 32 x 32 (128
-// registers).  Per 64-wide reduction step (one NF4 block per weight row):
+// Tile 128 (weight rows n) x 256 (activation rows m), eight waves (two per
+// SIMD); wave (wi, wj) owns the 64 x 64 block at (64 wi, 64 wj): 2 x 2
+// accumulators of 32 x 32.  Per 64-wide reduction step (one NF4 block per
+// weight row):
 //   * the activation tile (256 rows x 128 bytes) goes straight into LDS by
 //     direct-to-LDS loads, as in g256_kernel;
 //   * the NF4 codes of the weight tile, the blocks' 8-bit constants and c2
 //     come by direct-to-LDS loads too, in groups of four steps (a whole
 //     128-byte line of codes per row), one group ahead, into two code
 //     buffers; during the step before the one that uses them, thread t
-//     forms the block's 16 possible bf16 values RNE(fl32(cb[i] a')), a' =
-//     fl32(q8 fl32(c2 / 127)), as byte planes in registers, looks its 32
-//     weights up with v_perm_b32 (four codes per instruction, one code word
-//     per substep; no LDS traffic for the table) and stores them as bf16 into
-//     the weight tile of the other LDS stage (128-byte rows, the same chunk
-//     swizzle as the activations).  With every global load issued by the
-//     kernel itself, the waits are its own: the end of a step waits until
-//     only the code group loads issued in it (if any) are outstanding.
-//     Whole-line code loads keep the lines the load path touches per step
-//     below those of a bf16 weight tile.
+//     forms its block's 16 possible bf16 values RNE(fl32(cb[i] a')), a' =
+//     fl32(q8 fl32(c2 / 127)), as byte planes in registers, looks its 16
+//     weights up with v_perm_b32 (four codes per instruction; no LDS traffic
+//     for the table) and stores them as bf16 into the weight tile of the
+//     other LDS stage (128-byte rows, the same chunk swizzle as the
+//     activations).  The dequantisation is scheduled between the step's
+//     MFMAs (sched_group_barrier), so it runs while the matrix cores work.
+//     With every global load issued by the kernel itself, the waits are its
+//     own: the end of a step waits until only the code group loads issued in
+//     it (if any) are outstanding.
 // Each code is thus dequantised once per 256 activation rows, in registers,
 // and fed to bf16 MFMA from LDS.  The expand runs in the epilogue as in
 // g256_kernel; the tile is staged in LDS as bf16 and written with 16-byte
@@ -581,6 +582,10 @@ constexpr int kQI = 128, kQJ = 256;
 constexpr int kQWT = kQI * kGK * 2;  // weight tile of one step: 16 KB
 constexpr int kQAT = kQJ * kGK * 2;  // activation tile: 32 KB
 constexpr int kQStage = kQWT + kQAT;
+constexpr int kQThreads = 512;  // 8 waves: two per SIMD
+// code buffer: codes (128 rows x 128 bytes), 8-bit constants (one dword per
+// row and wave), c2 / absmax [step][row]
+constexpr int kQCQ8 = 16384, kQCC2 = 16384 + 2048, kQCB = 16384 + 2048 + 2048;
 
 struct Q256Params {
   const uint16_t* P;  // X, M x K
@@ -647,10 +652,10 @@ __device__ __forceinline__ void write16(uint32_t addr, const u32x4& v) {
   *(lds_ptr)(uintptr_t)addr = v;
 }
 
-template <int WK>
-__global__ __launch_bounds__(kGThreads) void q256_fwd_kernel(Q256Params p) {
+template <int WK, bool FP8>
+__global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * kQStage];
-  __shared__ __attribute__((aligned(1024))) char cst[2 * (16384 + 1024 + 2048)];
+  __shared__ __attribute__((aligned(1024))) char cst[2 * kQCB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = wave & 1, wj = wave >> 1;
@@ -664,11 +669,11 @@ __global__ __launch_bounds__(kGThreads) void q256_fwd_kernel(Q256Params p) {
   const int KT = (int)(K / kGK);
   const uint32_t sbase = lds_addr(smem);
 
-  // activation DMA: wave w fills rows 64 w .. 64 w + 63, 8 rows per instruction
-  uint32_t poff[8];
+  // activation DMA: wave w fills rows 32 w .. 32 w + 31, 8 rows per instruction
+  uint32_t poff[4];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int row = 64 * wave + 8 * u + (lane >> 3);
+  for (int u = 0; u < 4; ++u) {
+    const int row = 32 * wave + 8 * u + (lane >> 3);
     int64_t m = j0 + row;
     m = m < M ? m : M - 1;
     poff[u] = (uint32_t)((m * K + 8 * ((lane & 7) ^ rswz(row))) * 2);
@@ -678,72 +683,67 @@ __global__ __launch_bounds__(kGThreads) void q256_fwd_kernel(Q256Params p) {
     const uint32_t at = sbase + b * kQStage + kQWT;
     const char* pb = pbase0 + (int64_t)kt * kGK * 2;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) dma16(pb, poff[u], at + (64 * wave + 8 * u) * 128);
+    for (int u = 0; u < 4; ++u) dma16(pb, poff[u], at + (32 * wave + 8 * u) * 128);
   };
   // Weight codes and block constants arrive by direct-to-LDS loads as well,
-  // in groups of four steps (one 128-byte line of codes per row): the
-  // group's codes (128 rows x 128 bytes; chunk c of row x at physical chunk
-  // c ^ (x & 7)), the dword of 8-bit constants of each row that holds the
-  // group's four blocks, and each row's c2 (or float32 absmax) for the four
-  // steps.  Group g + 1 is loaded during step 4 g + 1 into the other of two
-  // code buffers; thread t then dequantises row t / 2, weights 32 (t & 1) ..
-  // + 31 of each block, from LDS.
-  constexpr int kCB = 16384 + 1024 + 2048;  // code buffer: codes, constants, c2 [step][row]
-  constexpr int NGD = (WK == kNF4DQ ? 1 : 0) + 6;  // group loads per wave
+  // in groups of four steps (one 128-byte line of codes per row), into one of
+  // two code buffers: the group's codes (128 rows x 128 bytes; chunk c of row
+  // x at physical chunk c ^ (x & 7)), the dword of 8-bit constants of each row
+  // that holds the group's four blocks (waves 0 and 1; the other waves load
+  // copies into unused space, so that every wave issues the same loads), and
+  // each row's c2 (or float32 absmax) for the four steps, [step][row].  Group
+  // g + 1 is loaded during step 4 g + 1.  Thread t dequantises row t / 4,
+  // weights 16 (t & 3) .. + 15 of each block, from LDS.
+  constexpr int NGD = (WK == kNF4DQ ? 1 : 0) + 3;  // group loads per wave
   const uint32_t cbase = lds_addr(cst);
   const int64_t KB = K / 64;
   const int NG = KT / 4;
-  const int wx = tid >> 1, wh = tid & 1;
-  uint32_t coff[4];
+  const int wx = tid >> 2, wq = tid & 3;
+  uint32_t coff[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row = 32 * wave + 8 * u + (lane >> 3);
+  for (int u = 0; u < 2; ++u) {
+    const int row = 16 * wave + 8 * u + (lane >> 3);
     coff[u] = (uint32_t)((((i0 + row) * K) >> 1) + 16 * ((lane & 7) ^ (row & 7)));
   }
-  const int crow = (64 * wave + lane) & (kQI - 1);
-  const uint32_t qoff = (uint32_t)((i0 + crow) * KB);
-  int64_t sblk[2];  // block of the c2 entry this lane brings for group 0: (row, step j)
+  const uint32_t qoff = (uint32_t)((i0 + ((64 * wave + lane) & (kQI - 1))) * KB);
+  const int ce = 64 * wave + lane;  // the c2 entry this lane brings: step ce / 128, row ce % 128
+  const int64_t sblk = (i0 + (ce & 127)) * KB + (ce >> 7);
+  uint32_t wdst[2];
 #pragma unroll
-  for (int v = 0; v < 2; ++v) {
-    const int e = (2 * wave + v) * 64 + lane;
-    sblk[v] = (i0 + (e & 127)) * KB + (e >> 7);
-  }
-  uint32_t wdst[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) wdst[d] = (uint32_t)(wx * 128 + (((4 * wh + d) ^ rswz(wx)) << 4));
+  for (int d = 0; d < 2; ++d) wdst[d] = (uint32_t)(wx * 128 + (((2 * wq + d) ^ rswz(wx)) << 4));
   auto issue_group = [&](int g, int buf) {
-    const uint32_t cb = cbase + buf * kCB;
+    const uint32_t cb = cbase + buf * kQCB;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 2; ++u)
       dma16(reinterpret_cast<const char*>(p.W.codes) + (int64_t)g * 128, coff[u],
-            cb + (32 * wave + 8 * u) * 128);
-    if (WK == kNF4DQ) dma4(p.W.q8 + 4 * g, qoff, cb + 16384 + 256 * wave);
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const int64_t blk = sblk[v] + 4 * g;
-      const uint32_t at = cb + 17408 + 256 * (2 * wave + v);
-      if (WK == kNF4DQ)
-        dma4(p.W.c2, (uint32_t)((blk >> 8) * 4), at);
-      else
-        dma4(p.W.absmax, (uint32_t)(blk * 4), at);
-    }
+            cb + (16 * wave + 8 * u) * 128);
+    if (WK == kNF4DQ) dma4(p.W.q8 + 4 * g, qoff, cb + kQCQ8 + 256 * wave);
+    const int64_t blk = sblk + 4 * g;
+    if (WK == kNF4DQ)
+      dma4(p.W.c2, (uint32_t)((blk >> 8) * 4), cb + kQCC2 + 256 * wave);
+    else
+      dma4(p.W.absmax, (uint32_t)(blk * 4), cb + kQCC2 + 256 * wave);
   };
-  // this thread's code words (one per substep) and block scale for the step
-  // at position pos of the group in code buffer buf
+  // this thread's 16 codes of the step at position pos of the group in code
+  // buffer buf (two words), and the raw constants of its block: (c2 or float32
+  // absmax bits, the row's word of 8-bit constants); then the block scale a'
   auto codes_at = [&](int buf, int pos) {
-    typedef __attribute__((address_space(3))) const u32x4* lp;
-    const int ch = (2 * pos + wh) ^ (wx & 7);
-    return *(lp)(uintptr_t)(cbase + buf * kCB + wx * 128 + ch * 16);
+    typedef __attribute__((address_space(3))) const u32x2* lp;
+    const int ch = (2 * pos + (wq >> 1)) ^ (wx & 7);
+    return *(lp)(uintptr_t)(cbase + buf * kQCB + wx * 128 + ch * 16 + 8 * (wq & 1));
   };
-  auto scale_at = [&](int buf, int pos) {
+  auto raw_at = [&](int buf, int pos) {
     typedef __attribute__((address_space(3))) const uint32_t* lp;
-    const uint32_t cb = cbase + buf * kCB;
-    const float v = __uint_as_float(*(lp)(uintptr_t)(cb + 17408 + 4 * (128 * pos + wx)));
-    if (WK == kNF4DQ) {
-      const uint32_t qw = *(lp)(uintptr_t)(cb + 16384 + 4 * wx);
-      return dq_q_rt(p.W.dq, (qw >> (8 * pos)) & 0xFFu) * dq_step(v);
-    }
+    const uint32_t cb = cbase + buf * kQCB;
+    u32x2 v;
+    v[0] = *(lp)(uintptr_t)(cb + kQCC2 + 4 * (128 * pos + wx));
+    v[1] = WK == kNF4DQ ? *(lp)(uintptr_t)(cb + kQCQ8 + 4 * wx) : 0u;
     return v;
+  };
+  auto scale_of = [&](const u32x2& v, int pos) {
+    if (WK == kNF4DQ)
+      return dq_value<FP8>((v[1] >> (8 * pos)) & 0xFFu) * dq_step(__uint_as_float(v[0]));
+    return __uint_as_float(v[0]);
   };
 
   // operand reads (128-byte-row tiles, as g256_kernel)
@@ -751,20 +751,20 @@ __global__ __launch_bounds__(kGThreads) void q256_fwd_kernel(Q256Params p) {
   uint32_t pcx[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) pcx[s] = (uint32_t)(((2 * s + h) ^ sw) << 4);
-  const uint32_t prow = (uint32_t)((128 * wj + l32) * 128);
+  const uint32_t prow = (uint32_t)((64 * wj + l32) * 128);
   const uint32_t qrow = (uint32_t)((64 * wi + l32) * 128);
-  auto load_frags = [&](uint32_t st, int s, u32x4 (&wf)[2], u32x4 (&xf)[4]) {
+  auto load_frags = [&](uint32_t st, int s, u32x4 (&wf)[2], u32x4 (&xf)[2]) {
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms) xf[ms] = read16(st + kQWT + prow + ms * 32 * 128 + pcx[s]);
+    for (int ms = 0; ms < 2; ++ms) xf[ms] = read16(st + kQWT + prow + ms * 32 * 128 + pcx[s]);
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) wf[ns] = read16(st + qrow + ns * 32 * 128 + pcx[s]);
   };
 
-  f32x16 acc[2][4];
+  f32x16 acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
@@ -774,20 +774,20 @@ __global__ __launch_bounds__(kGThreads) void q256_fwd_kernel(Q256Params p) {
   wait_dma();
   __syncthreads();
   {
-    const u32x4 cw = codes_at(0, 0);
-    const PermTable pt = perm_table(p.tab, scale_at(0, 0));
+    const u32x2 cw = codes_at(0, 0);
+    const PermTable pt = perm_table(p.tab, scale_of(raw_at(0, 0), 0));
 #pragma unroll
-    for (int d = 0; d < 4; ++d) write16(sbase + wdst[d], perm_deq8(cw[d], pt));
+    for (int d = 0; d < 2; ++d) write16(sbase + wdst[d], perm_deq8(cw[d], pt));
   }
   __syncthreads();
 
   // Step kt (J = kt mod 8: stage J & 1, code buffer J >> 2, position J & 3):
   // the activation loads of step kt + 1, in position 1 the loads of the next
-  // code group, the words of step kt + 1 dequantised (one word per substep,
-  // after the substep's MFMAs) into the other weight tile, the MFMAs of step
-  // kt; at the end, wait for everything but the code group loads issued in
-  // this step.  Unrolled by eight so that every LDS address is a base plus an
-  // immediate.
+  // code group, the MFMAs of step kt with the dequantisation of step kt + 1
+  // (level table, then one code word in each of the next two substeps) into
+  // the other weight tile scheduled between them; at the end, wait for
+  // everything but the code group loads issued in this step.  Unrolled by
+  // eight so that every LDS address is a base plus an immediate.
   auto step = [&](int kt, auto jj) {
     constexpr int J = decltype(jj)::value;
     constexpr int B = J & 1, POS = J & 3, BUF = J >> 2;
@@ -798,25 +798,42 @@ __global__ __launch_bounds__(kGThreads) void q256_fwd_kernel(Q256Params p) {
     if (grp) issue_group((kt >> 2) + 1, BUF ^ 1);
     const uint32_t st = sbase + B * kQStage;
     const uint32_t wt = sbase + (B ^ 1) * kQStage;
-    u32x4 cw = u32x4{0u, 0u, 0u, 0u};
-    float a = 0.0f;
-    if (more) {
-      cw = codes_at(NBUF, NPOS);
-      a = scale_at(NBUF, NPOS);
-    }
-    u32x4 wf[2][2], xf[2][4];
+    // (after the last step the words read here are stale and their
+    // dequantised values land in a tile nobody reads: no branch, so that the
+    // dequantisation can be scheduled between the MFMAs)
+    u32x4 wf[2][2], xf[2][2];
     load_frags(st, 0, wf[0], xf[0]);
-    const PermTable pt = perm_table(p.tab, a);
+    const u32x2 cw = codes_at(NBUF, NPOS);
+    const u32x2 raw = raw_at(NBUF, NPOS);
+    __builtin_amdgcn_sched_barrier(0);
+    PermTable pt;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c = s & 1;
       if (s < 3) load_frags(st, s + 1, wf[c ^ 1], xf[c ^ 1]);
-      __builtin_amdgcn_sched_barrier(0);  // next substep's reads ahead of this one's work
+      if (s == 0) pt = perm_table(p.tab, scale_of(raw, NPOS));
 #pragma unroll
       for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf[c][ms], acc[ns][ms]);
-      if (more) write16(wt + wdst[s], perm_deq8(cw[s], pt));
+        for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf[c][ms], acc[ns][ms]);
+      if (s == 1 || s == 2) write16(wt + wdst[s - 1], perm_deq8(cw[s - 1], pt));
+      // the next substep's reads first, then each MFMA followed by a share of
+      // the dequantisation, then the store of the dequantised word
+      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      if (s == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        }
+      } else if (s < 3) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (grp)
@@ -855,30 +872,30 @@ __global__ __launch_bounds__(kGThreads) void q256_fwd_kernel(Q256Params p) {
   const int r = p.r;
   for (int c = 0; c < r; c += 16) {
     const int jr = c + 8 * h;
-    u32x4 ef[2], vf[4];
+    u32x4 ef[2], vf[2];
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
       const int64_t i = i0 + 64 * wi + 32 * ns + l32;
       ef[ns] = e_operand_row(p.E + i * r, jr, r);
     }
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms) {
-      int64_t m = j0 + 128 * wj + 32 * ms + l32;
+    for (int ms = 0; ms < 2; ++ms) {
+      int64_t m = j0 + 64 * wj + 32 * ms + l32;
       m = m < M ? m : M - 1;
       vf[ms] = v_operand(p.V + m * r, jr, r, p.s);
     }
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms) acc[ns][ms] = mfma32(ef[ns], vf[ms], acc[ns][ms]);
+      for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(ef[ns], vf[ms], acc[ns][ms]);
   }
 
   // ---- store: bf16 tile in LDS (row j of 256 bytes; chunk c at c ^ (j & 15)),
   // then whole 256-byte output row segments with 16-byte stores
   __syncthreads();
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms) {
-    const int j = 128 * wj + 32 * ms + l32;
+  for (int ms = 0; ms < 2; ++ms) {
+    const int j = 64 * wj + 32 * ms + l32;
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
@@ -893,8 +910,8 @@ __global__ __launch_bounds__(kGThreads) void q256_fwd_kernel(Q256Params p) {
   __syncthreads();
   const int cl = tid & 15;
 #pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int j = 16 * it + (tid >> 4);
+  for (int it = 0; it < 8; ++it) {
+    const int j = 32 * it + (tid >> 4);
     const int64_t m = j0 + j;
     const u32x4 v = read16(sbase + (uint32_t)(j * 256 + ((cl ^ (j & 15)) << 4)));
     if (m < M) *reinterpret_cast<u32x4*>(p.Y + m * N + i0 + 8 * cl) = v;
@@ -1038,10 +1055,12 @@ int launch_q256_fwd(const void* X, int64_t M, const lq_weight& W, const float* T
   p.tab = nf4_table(W.codebook);
   const unsigned blocks = (unsigned)(p.ti * p.tj);
   timing_begin("q256_fwd", st);
-  if (W.double_quant)
-    hipLaunchKernelGGL((q256_fwd_kernel<kNF4DQ>), dim3(blocks), dim3(kGThreads), 0, st, p);
+  if (W.double_quant == LQ_DQ_FP8)
+    hipLaunchKernelGGL((q256_fwd_kernel<kNF4DQ, true>), dim3(blocks), dim3(kQThreads), 0, st, p);
+  else if (W.double_quant)
+    hipLaunchKernelGGL((q256_fwd_kernel<kNF4DQ, false>), dim3(blocks), dim3(kQThreads), 0, st, p);
   else
-    hipLaunchKernelGGL((q256_fwd_kernel<kNF4>), dim3(blocks), dim3(kGThreads), 0, st, p);
+    hipLaunchKernelGGL((q256_fwd_kernel<kNF4, false>), dim3(blocks), dim3(kQThreads), 0, st, p);
   timing_end(st);
   return hip_fail(hipGetLastError(), "q256 launch");
 }
