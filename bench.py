@@ -35,8 +35,8 @@ Default run (python bench.py [--steps K] [--warmup W]):
   backward of config 2 (q and v, bf16, M = 4096, r = 8) and of config 4 (the
   seven projections of a block, NF4, M = 8192, r = 64).
 
-Profiling helpers (for rocprofv3): --mode fwd | fwd_inloop | dx | step | decode
-| copy | quant run only that part, a few iterations, and print one line.
+Profiling helpers (for rocprofv3): --mode fwd | fwd_inloop | fwd_fused | dx | step
+| decode | copy | quant run only that part, a few iterations, and print one line.
 """
 from __future__ import annotations
 
@@ -529,7 +529,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--mode", default="full",
-                    choices=["full", "step", "fwd", "fwd_inloop", "dx", "decode", "copy", "quant"])
+                    choices=["full", "step", "fwd", "fwd_inloop", "fwd_fused", "dx", "decode", "copy",
+                             "quant"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-secondary", action="store_true")
     a = ap.parse_args(argv)
@@ -564,11 +565,12 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"mode": "fwd", "launches": a.steps}))
         return 0
-    if a.mode == "fwd_inloop":
+    if a.mode in ("fwd_inloop", "fwd_fused"):
+        f = fwd_inloop if a.mode == "fwd_inloop" else fwd_fused
         for _ in range(a.steps):
-            fwd_inloop(S)
+            f(S)
         torch.cuda.synchronize()
-        print(json.dumps({"mode": "fwd_inloop", "launches": a.steps}))
+        print(json.dumps({"mode": a.mode, "launches": a.steps}))
         return 0
     if a.mode == "dx":
         for _ in range(a.steps):
