@@ -36,7 +36,8 @@ Default run (python bench.py [--steps K] [--warmup W]):
   seven projections of a block, NF4, M = 8192, r = 64).
 
 Profiling helpers (for rocprofv3): --mode fwd | fwd_inloop | fwd_fused | dx | step
-| decode | copy | quant run only that part, a few iterations, and print one line.
+| decode | copy | quant run only that part, a few iterations (after CLOCK_WARMUP_S seconds of
+the same work for the first five), and print one line.
 """
 from __future__ import annotations
 
@@ -90,10 +91,14 @@ def traffic_for(kernel, sources):
     return e.get("bytes_per_launch")
 
 
-def cuda_time(fn, iters, torch):
-    """Average GPU time (ms) of fn() over iters back-to-back calls (HIP events)."""
+def cuda_time(fn, iters, torch, warm=3):
+    """Average GPU time (ms) of fn() over iters back-to-back calls (HIP events),
+    after `warm` untimed calls (the first launch of a kernel in a process also
+    loads its code)."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(warm):
+        fn()
     torch.cuda.synchronize()
     e0.record()
     for _ in range(iters):
@@ -559,6 +564,19 @@ def main(argv=None):
         return 0
 
     S = setup(torch)
+
+    def settle(fn):
+        """Run fn untimed for CLOCK_WARMUP_S seconds so that a profiled run sees the
+        clocks of steady work (see the timed region below)."""
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < CLOCK_WARMUP_S:
+            for _ in range(20):
+                fn(S)
+            torch.cuda.synchronize()
+
+    if a.mode in ("fwd", "dx", "step", "fwd_inloop", "fwd_fused"):
+        settle({"fwd": fwd, "dx": dx_only, "step": step, "fwd_inloop": fwd_inloop,
+                "fwd_fused": fwd_fused}[a.mode])
     if a.mode == "fwd":
         for _ in range(a.steps):
             fwd(S)
