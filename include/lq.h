@@ -183,7 +183,9 @@ int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
  *   that works.  The decode path (dt = LQ_BF16, M <= 96) needs no workspace
  *   up to 16 rows (one launch; T is formed inside it); 17 to 96 rows run as
  *   16-row chunks and need 8 M' r floats of partial sums of T (M' = M rounded
- *   up to a multiple of 16).  The float32 path needs M r floats of T when
+ *   up to a multiple of 16).  With the LQ_OP_FWD workspace and N > 4096 the
+ *   chunks stop at 32 rows for an NF4 W0 and at 16 for a bf16 one (the
+ *   large-tile path is faster past those).  The float32 path needs M r floats of T when
  *   T_out is NULL; otherwise ws may be NULL.
  *   dt = LQ_BF16: bf16 inputs, float32 accumulation, bf16 RNE output; W0 dense
  *   bf16 or NF4.  Past the decode rows, the path follows the workspace:

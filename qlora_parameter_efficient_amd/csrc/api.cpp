@@ -42,11 +42,22 @@ namespace {
 
 constexpr int64_t kMaxRank = 64;
 constexpr int64_t kDecodeMaxM = 16;
-// Forward rows run as 16-row decode chunks up to here: each chunk re-reads
-// the weights, and six chunks (96 rows, 45.5 µs for W0 4096^2 NF4) still beat
-// a large-tile call at these sizes (≈52 µs), which leaves most compute units
-// idle; seven tie and eight lose.
+// Forward rows that may run as 16-row decode chunks (one launch of each chunk
+// kernel): each chunk streams W0 again, while the large-tile path's time
+// barely grows with M at these sizes but leaves most compute units idle.
 constexpr int64_t kDecodeChunkMaxM = 96;
+
+// Where the chunks stop when the large-tile path is available (the LQ_OP_FWD
+// workspace).  Measured, µs per graph-launched call at r = 16 (chunks / large
+// tile): 4096 x 4096 NF4 M = 64 29.6 / 51.6, M = 96 42.1 / 51.6; 4096 x 4096
+// bf16 M = 64 30.6 / 45.1, M = 96 43.4 / 45.4; 4096 x 11008 NF4 M = 96
+// 107.4 / 116.7; 11008 x 4096 NF4 M = 32 41.9 / 58.7, M = 48 60.2 / 59.3,
+// M = 64 73.4 / 59.6; 11008 x 4096 bf16 M = 17 47.4 / 46.0.  A wider output
+// gives the large-tile path more tiles, while every chunk costs more.
+int64_t chunk_max_m(int64_t N, bool nf4) {
+  if (N <= 4096) return kDecodeChunkMaxM;
+  return nf4 ? 32 : kDecodeMaxM;
+}
 
 int check_weight(const lq_weight* w, lq_dtype dt) {
   REQUIRE(w != nullptr, LQ_ERR_INVALID_ARG, "W0 descriptor is NULL");
@@ -357,8 +368,9 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
   if (M < 0 || N < 0 || K < 0 || r < 0) return 0;
   switch (op) {
     case LQ_OP_FWD: {  // the decode path's partial sums of T, or float32 T
-      if (M <= kDecodeChunkMaxM) return decode_bytes(M, N, K, r);  // never the large-tile path
-      const size_t base = (size_t)(M * r) * 4;
+      // up to chunk_max_m rows (either format) never the large-tile path
+      if (M <= kDecodeMaxM || M <= chunk_max_m(N, true)) return decode_bytes(M, N, K, r);
+      const size_t base = M <= kDecodeChunkMaxM ? decode_bytes(M, N, K, r) : (size_t)(M * r) * 4;
       const size_t big = fwd_big_bytes(M, N, K, r);
       return big > base ? big : base;
     }
@@ -460,15 +472,17 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
     return f32_lora_fwd((const float*)X, M, *W0, (const float*)A, (const float*)B, r, scale,
                         (float*)Y, T, stream);
   }
-  if (M <= kDecodeChunkMaxM) {  // partial sums of T cross two kernels, per 16-row chunk
+  const size_t big = fwd_big_bytes(M, W0->N, W0->K, r);
+  const bool big_ok = big && ws && ws_bytes >= big;
+  if (M <= kDecodeMaxM ||
+      (M <= kDecodeChunkMaxM && (!big_ok || M <= chunk_max_m(W0->N, W0->kind == LQ_WEIGHT_NF4)))) {
+    // partial sums of T cross two kernels, per 16-row chunk (none up to 16 rows)
     const size_t need = decode_bytes(M, W0->N, W0->K, r);
     REQUIRE(need == 0 || (ws != nullptr && ws_bytes >= need), LQ_ERR_WORKSPACE,
             "workspace %zu bytes, need %zu", ws_bytes, need);
     return decode_chunks(X, M, *W0, A, B, r, scale, Y, T_out, (float*)ws, stream);
   }
-  const size_t big = fwd_big_bytes(M, W0->N, W0->K, r);
-  if (big && ws && ws_bytes >= big)
-    return dispatch::big_fwd(X, M, *W0, A, B, r, scale, Y, T_out, ws, stream);
+  if (big_ok) return dispatch::big_fwd(X, M, *W0, A, B, r, scale, Y, T_out, ws, stream);
   if (ws && ws_bytes >= (size_t)(M * r) * 4 && dispatch::inloop_fwd_eligible(*W0, M))
     return dispatch::inloop_fwd(X, M, *W0, A, B, r, scale, Y, T_out ? T_out : (float*)ws, stream);
   return dispatch::bf16_fwd(X, M, *W0, A, B, r, scale, Y, T_out, stream);

@@ -58,6 +58,11 @@ def test_workspace_sizes():
     # chunks, rows padded to a multiple of 16)
     assert lq.lq_workspace_size(lq.LQ_OP_FWD, 33, 256, 256, 8) == 8 * 48 * 8 * 4
     assert lq.lq_workspace_size(lq.LQ_OP_FWD, 90, 256, 256, 8) == 8 * 96 * 8 * 4
+    # wider than 4096 outputs: past 32 rows the LQ_OP_FWD size also holds the large-tile
+    # path's part (bf16 weight copy), which then runs; the fused size stays the chunks'
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 32, 4352, 256, 16) == 8 * 32 * 16 * 4
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD, 48, 4352, 256, 16) > 4352 * 256 * 2
+    assert lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, 48, 4352, 256, 16) == 8 * 48 * 16 * 4
     assert lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, 97, 256, 256, 8) == 97 * 8 * 4
     # beyond: the default size also holds the large-tile path's bf16 copy of W0
     assert lq.lq_workspace_size(lq.LQ_OP_FWD, 97, 256, 256, 8) >= 97 * 8 * 4 + 256 * 256 * 2
