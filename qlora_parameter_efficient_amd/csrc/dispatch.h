@@ -45,8 +45,9 @@ int decode_fwd1(const void* X, int64_t M, const lq_weight& W, const void* A, con
 // Bound (in polls) of a workgroup's wait for data another workgroup publishes
 // (the decode kernel's T words, the split-K partner's partial sums): polls > 0
 // sets it, 0 restores the default, < 0 makes every such wait give up at once
-// (wait_limit() is then -1).  Every wait that gives up takes its kernel's
-// fallback and is counted; take_*_giveups return the device's count since the
+// (wait_limit() is then -1).  Every wait that gives up is counted (a decode
+// workgroup then forms T itself; a split-K workgroup leaves its partner's
+// partial sums unread); take_*_giveups return the device's count since the
 // last read and clear it.
 constexpr int32_t kDefaultWaitPolls = 1 << 22;
 void set_wait_limit(int32_t polls);

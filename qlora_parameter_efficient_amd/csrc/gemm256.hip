@@ -970,7 +970,7 @@ G256Plan g256_plan(int64_t M, int64_t NI) {
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// error word, then four flag words per tile
+// a 256-byte header (unused), then four flag words per tile
 size_t g256_flag_bytes(int64_t M, int64_t NI) {
   return 256 + align256((size_t)g256_plan(M, NI).tiles * 16);
 }
@@ -1077,12 +1077,12 @@ int bf16_weight(const lq_weight& W, void* q, hipStream_t st) {
 bool big_fwd_eligible(int64_t M, int64_t N, int64_t K) { return g256_fits(M, N, K); }
 bool big_dx_eligible(int64_t M, int64_t N, int64_t K) { return g256_fits(M, K, N); }
 
-// [g256: error word, flags, split-K slots] [T when T_out is NULL] [bf16 W0]
+// [g256: header, flags, split-K slots] [T when T_out is NULL] [bf16 W0]
 size_t big_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
   return align256(g256_ws_bytes(M, N)) + align256((size_t)(M * r) * 4) + (size_t)(N * K) * 2;
 }
 
-// [g256: error word, flags, split-K slots] [bf16 W0]
+// [g256: header, flags, split-K slots] [bf16 W0]
 size_t big_dx_ws_bytes(int64_t M, int64_t N, int64_t K) {
   return align256(g256_ws_bytes(M, K)) + (size_t)(N * K) * 2;
 }

@@ -9,7 +9,7 @@
 // host it is only a stand-in for the symbol): the first call on a device asks
 // the runtime for that device's address once and keeps it.  Calls on one GPU
 // share the array; the backward's kernels clear what must start at zero (the
-// split-K flags and error word) themselves on every call, and every other
+// split-K flags) themselves on every call, and every other
 // part of the workspace is written before it is read, so stale contents from
 // an earlier call do no harm.  Calls that overlap in time on one GPU race.
 #include <mutex>
