@@ -214,6 +214,15 @@ def small_case(M, N, K, r, dtype="bf16", seed=7, sw=0.02, sa=None, sb=0.01, zero
     return dict(W0=W0, A=A, B=B, X=X, dY=dY, r=r, alpha=2.0 * r)
 
 
+def device_normal(shape, sigma, seed, device):
+    """A bf16 tensor ~ N(0, sigma^2) drawn on the device from a seeded torch
+    generator: for inputs too large to draw and move from the host (the
+    largest activation tensor the boundary accepts)."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=device) * sigma).to(torch.bfloat16)
+
+
 def config4_adapter_sizes(r: int = 64):
     """Element counts of the trainable A (r x K) and B (N x r) of config 4's
     seven projections, in block order: 14 tensors, 4,997,120 parameters."""
