@@ -347,8 +347,9 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(GemvParams p) {
 // tag is epoch + 1, with the epoch a word of the stream's slot in library
 // memory that every workgroup reads as its first load.  Each workgroup counts
 // itself in (one of eight counters, by XCD) once that load has returned;
-// workgroup 0, at its end, waits until all have counted in, returns the
-// counters to zero and advances the epoch.  So every workgroup of a call sees
+// workgroup 0 reads the counters after its weight stream and, at its end
+// (re-reading while they are short), returns them to zero and advances the
+// epoch.  So every workgroup of a call sees
 // the same tag, each call (also each replay of a captured graph) has a new
 // one, and nothing needs clearing between calls.  Every wait is bounded; a
 // workgroup that gives up on the partials counts the give-up
@@ -404,7 +405,7 @@ __device__ __forceinline__ void dec_t_direct(const DecParams& p, float* T) {
   }
 }
 
-template <int WK, int XS, int JT>
+template <int WK, int XS, int JT, bool SS>
 __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
   constexpr bool XL = XS > 0;
   constexpr int CH = 2;
@@ -415,6 +416,10 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
   __shared__ f32x4 part[kGemvWaves][64];
   __shared__ float tB[16 * 64];
   __shared__ float tT[16 * 64];
+  // SS (NF4, K <= 4096): the block scales a' of the workgroup's 16 rows, formed
+  // once per block by the workgroup (row stride 65 words: the 16 rows one
+  // lane group reads sit in distinct banks)
+  __shared__ float sa[SS ? 16 * 65 : 1];
   DecSlot* sl = g_dec_slot + p.slot;
   // the call tag: this call's epoch + 1, read before anything else
   const uint32_t tag =
@@ -459,6 +464,21 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
   const int EB = 16 * r;
   const int tb = tid < EB ? tid : EB - 1;
   const uint16_t braw = p.B[n0 * r + tb];
+  // SS: thread t < 16 KB loads the constants of block t of the 16 rows (row
+  // t / KB, block t % KB; consecutive threads read consecutive bytes)
+  const int KB = (int)(K / 64);
+  uint32_t sraw = 0;
+  float sc2raw = 1.0f;
+  if (SS) {
+    const int tq = tid < 16 * KB ? tid : 16 * KB - 1;
+    const int64_t e = n0 * KB + tq;
+    if (WK == kNF4DQ) {
+      sraw = p.W.q8[e];
+      sc2raw = p.W.c2[e >> 8];
+    } else {
+      sraw = __float_as_uint(p.W.absmax[e]);
+    }
+  }
 
   const int64_t n = n0 + l16;
   const bool mrow = l16 < M;
@@ -487,7 +507,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
           wraw[i][d] = *reinterpret_cast<const u32x4*>(p.W.dense + e + 8 * d);
       } else {
         wraw[i][0] = *reinterpret_cast<const u32x4*>(p.W.codes + (e >> 1));
-        if (WK == kNF4DQ) {
+        if (SS) {
+        } else if (WK == kNF4DQ) {
           sq[i] = p.W.q8[e >> 6];
           sc2[i] = p.W.c2[e >> 14];
         } else {
@@ -514,7 +535,12 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
     const int nn = tid / r, j = tid - nn * r;
     tB[nn * 64 + j] = bf16_to_f32(braw);
   }
-  __syncthreads();  // level table, staged X, B rows
+  if (SS && tid < 16 * KB) {
+    const int rr = tid / KB;
+    sa[rr * 65 + (tid - rr * KB)] =
+        WK == kNF4DQ ? dq_q_rt(p.W.dq, sraw) * dq_step(sc2raw) : __uint_as_float(sraw);
+  }
+  __syncthreads();  // level table, staged X, B rows, block scales
   // count this workgroup in: its epoch load, issued before the loads waited
   // for above, has returned (loads complete in order)
   if (tid == 0)
@@ -586,8 +612,10 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) acc[i] = mfma16(wraw[i][d], sel4(ok[i], xf[i][d]), acc[i]);
       } else {
-        const float a =
-            WK == kNF4DQ ? dq_q_rt(p.W.dq, sq[i]) * dq_step(sc2[i]) : __uint_as_float(sq[i]);
+        // SS: the granule's block within its row, (4 t + q) / 2
+        const float a = SS ? sa[l16 * 65 + (int)((4 * (base + kGemvWaves * i) + q) >> 1)]
+                        : WK == kNF4DQ ? dq_q_rt(p.W.dq, sq[i]) * dq_step(sc2[i])
+                                       : __uint_as_float(sq[i]);
 #pragma unroll
         for (int d = 0; d < 4; ++d)
           acc[i] = mfma16(deq8(wraw[i][0][d], a, lut), sel4(ok[i], xf[i][d]), acc[i]);
@@ -600,6 +628,14 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) a0[v] += acc[i][v];
   part[wave][lane] = a0;
+
+  // workgroup 0, wave 0: read the eight started counters now (lane x reads
+  // counter x & 7), while the T words, the expand and the stores are still
+  // ahead; the values are used at the end
+  const bool ep = blockIdx.x == 0 && wave == 0;
+  uint32_t cv = 0;
+  if (ep)
+    cv = __hip_atomic_load(&sl->started[lane & 7][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- T: thread e < M r reads element e's P partial words (all loads in
   // flight together), re-reads any that is not yet this call's (bounded), and
@@ -658,21 +694,26 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
     *reinterpret_cast<u32x2*>(p.Y + m * N + n0 + 4 * q) =
         u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
   }
-  // ---- workgroup 0, last: once every workgroup has read the epoch, move it on
-  if (blockIdx.x == 0 && lane == 0) {
-    int it = 0;
-    for (;;) {
-      uint32_t c = 0;
+  // ---- workgroup 0, last: once every workgroup has read the epoch (the
+  // counters read above, re-read while short), move it on
+  if (ep) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) c += (uint32_t)__shfl((int)cv, x);
+    if (lane == 0) {
+      int it = 0;
+      while (c < gridDim.x && ++it <= dispatch::kDefaultWaitPolls) {
+        __builtin_amdgcn_s_sleep(1);
+        c = 0;
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+          c += __hip_atomic_load(&sl->started[x][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
 #pragma unroll
       for (int x = 0; x < 8; ++x)
-        c += __hip_atomic_load(&sl->started[x][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (c >= gridDim.x || ++it > dispatch::kDefaultWaitPolls) break;
-      __builtin_amdgcn_s_sleep(1);
+        __hip_atomic_store(&sl->started[x][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&sl->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-#pragma unroll
-    for (int x = 0; x < 8; ++x)
-      __hip_atomic_store(&sl->started[x][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_add(&sl->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -839,25 +880,33 @@ int decode_fwd1(const void* X, int64_t M, const lq_weight& W, const void* A, con
   const int64_t mk = M * W.K;
   const int xs = W.K % 128 ? 0 : mk <= 16384 ? 1 : mk <= 65536 ? 2 : 0;
   const int jt = r <= 16 ? 0 : r <= 32 ? 1 : 2;
-  const int sel = (weight_format(W) * 3 + xs) * 3 + jt;
-#define LQ_DEC(WKv, XSv, JTv, idx)                                            \
-  case idx:                                                                   \
-    hipLaunchKernelGGL((dq_kernel<WKv, XSv, JTv>), grid, block, 0, st, p);    \
+  // block scales staged per workgroup for an NF4 weight with K <= 4096
+  const bool ss = W.kind == LQ_WEIGHT_NF4 && W.K <= 4096;
+  const int sel = ((weight_format(W) * 3 + xs) * 3 + jt) * 2 + (ss ? 1 : 0);
+#define LQ_DEC(WKv, XSv, JTv, SSv, idx)                                            \
+  case idx:                                                                        \
+    hipLaunchKernelGGL((dq_kernel<WKv, XSv, JTv, SSv>), grid, block, 0, st, p);    \
     break;
-#define LQ_DEC3(WKv, XSv, base) \
-  LQ_DEC(WKv, XSv, 1, base) LQ_DEC(WKv, XSv, 2, base + 1) LQ_DEC(WKv, XSv, 4, base + 2)
+#define LQ_DEC3(WKv, XSv, base)                                                    \
+  LQ_DEC(WKv, XSv, 1, false, 2 * (base)) LQ_DEC(WKv, XSv, 2, false, 2 * (base) + 2) \
+  LQ_DEC(WKv, XSv, 4, false, 2 * (base) + 4)
+#define LQ_DEC3S(WKv, XSv, base)                                                   \
+  LQ_DEC3(WKv, XSv, base)                                                          \
+  LQ_DEC(WKv, XSv, 1, true, 2 * (base) + 1) LQ_DEC(WKv, XSv, 2, true, 2 * (base) + 3) \
+  LQ_DEC(WKv, XSv, 4, true, 2 * (base) + 5)
   switch (sel) {
     LQ_DEC3(kDense, 0, 0)
     LQ_DEC3(kDense, 16384, 3)
     LQ_DEC3(kDense, 65536, 6)
-    LQ_DEC3(kNF4DQ, 0, 9)
-    LQ_DEC3(kNF4DQ, 16384, 12)
-    LQ_DEC3(kNF4DQ, 65536, 15)
-    LQ_DEC3(kNF4, 0, 18)
-    LQ_DEC3(kNF4, 16384, 21)
-    LQ_DEC3(kNF4, 65536, 24)
+    LQ_DEC3S(kNF4DQ, 0, 9)
+    LQ_DEC3S(kNF4DQ, 16384, 12)
+    LQ_DEC3S(kNF4DQ, 65536, 15)
+    LQ_DEC3S(kNF4, 0, 18)
+    LQ_DEC3S(kNF4, 16384, 21)
+    LQ_DEC3S(kNF4, 65536, 24)
     default: break;
   }
+#undef LQ_DEC3S
 #undef LQ_DEC3
 #undef LQ_DEC
   return hip_fail(hipGetLastError(), "decode launch");
