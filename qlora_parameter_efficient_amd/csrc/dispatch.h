@@ -112,6 +112,15 @@ int big_fwd_multi(const void* X, int64_t T, const lq_weight& W, const void* A_ca
 // row_ad[m] = adapter of the segment holding row m
 int launch_rowmap(const int32_t* seg_off, const int32_t* seg_ad, int32_t n_seg, int64_t T,
                   int32_t* row_ad, hipStream_t st);
+// dX for at most 64 rows with an NF4 weight (K % 128 == 0, N % 64 == 0,
+// r <= 64): the weight streamed once by (128-column, 512-row) pieces, float32
+// partial sums of dY Wd and of U = dY B per row range in ws
+// (small_dx_ws_bytes, carved from the large-tile dX workspace), added in a
+// second launch that also writes U (M x r float32, when U is not NULL).
+bool small_dx_eligible(const lq_weight& W, int64_t M, int64_t r);
+size_t small_dx_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+int small_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B,
+             int64_t r, float s, float* U, void* dX, void* ws, hipStream_t st);
 // U (M x r float32) is written as well, times uscale: the expand needs it.
 int big_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,
            float s, void* dX, float* U, void* ws, hipStream_t st, float uscale = 1.0f);

@@ -171,6 +171,27 @@ def test_mid_rows_wide_output(M, kind):
     check_both_paths(c, kind, label="mid-wide")
 
 
+@pytest.mark.parametrize("M", [1, 31, 33, 64])
+def test_small_rows_nf4_dx(M):
+    """dX for at most 64 rows with an NF4 weight and the default workspace:
+    the weight-streaming kernel (128-column x 512-row pieces of the codes,
+    float32 partial sums of dY W' and of U per row range, added in order by a
+    second launch).  The config-3 weight at 4096^2 (8 row ranges, 32 column
+    slabs, one rank column per slab); 1088 x 256 at rank 64 (a last row range
+    of 64 rows, two column slabs holding 32 rank columns each); 320 x 768 with
+    single-level constants (one ragged row range)."""
+    c = wl.config3(M=M)
+    check_layer(c, "nf4", merge=False, label="small-rows-dx config3")
+    c = wl.small_case(M, 1088, 256, 64, seed=600 + M)
+    check_layer(c, "nf4", merge=False, label="small-rows-dx r64")
+    c = wl.small_case(M, 320, 768, 8, seed=500 + M)
+    Wd = lq.lq_nf4_quantize(to_dev(c["W0"]), double_quant=False)
+    W0v = c["W0"].value
+    Wo = onf4.bf16_bits_to_f64(onf4.nf4_dequantize_bf16(
+        onf4.nf4_quantize(W0v, double_quant=False))).reshape(W0v.shape)
+    check_gpu(c, Wd, oracle_ref(c, Wo), label="small-rows-dx single-level")
+
+
 @pytest.mark.parametrize("kind", ["dense", "nf4"])
 @pytest.mark.parametrize("M", [1, 16, 96])
 def test_decode_rank64(M, kind):
