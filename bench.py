@@ -4,27 +4,28 @@
 Default run (python bench.py [--steps K] [--warmup W]):
 
 * step = one forward + backward of the QLoRA linear at 4096 x 4096, NF4 base
-  with double quantisation, r = 16, alpha = 32, M = 2048 tokens, bf16 compute,
-  with the workspaces that select the fastest path.  Forward: one launch
-  dequantises NF4 to a bf16 copy in the workspace and forms T = X A^T, then
-  the large-tile product with the expand.  Backward: the same for dX (U =
-  dY B), then the dA / dB reductions.  value = algorithmic fwd+bwd FLOPs /
+  with double quantisation, r = 16, alpha = 32, M = 2048 tokens, bf16 compute.
+  Forward: one launch, the product that dequantises NF4 inside its K loop,
+  forms T = X A^T in the same loop and adds the expand (no bf16 copy of W0
+  anywhere).  Backward: the same for dX (U = dY B in the K loop, expand
+  (s U) A), then the dA / dB reductions.  value = algorithmic fwd+bwd FLOPs /
   wall time per step, the step launched eagerly; the GPU-event time of the
   same timed region and the step replayed from a HIP graph are reported
   beside it.  The step first runs untimed for CLOCK_WARMUP_S seconds so that
   the clocks have settled, and the shader clock is sampled from sysfs during
   the timed region.
-* roofline: the dominant kernel -- the large-tile product of the forward or
-  of dX, whichever is slower (each does 2 M N K + 2 M N r FLOPs: the product
-  and the rank-r expand) -- timed with HIP events that the library records
+* roofline: the dominant kernel -- the K-loop product of the forward or of
+  dX, whichever is slower (each does 2 M N K + 2 M K r + 2 M N r FLOPs: the
+  product, the rank-r shrink and the expand) -- timed with HIP events that
+  the library records
   around its launches on the launch stream (lq_timing_enable), algorithmic
   FLOPs per launch / average duration, against the bf16 dense MFMA peak, and
   against that peak scaled to the sampled clock; traffic (HBM bytes per
   launch) from rocprofv3 FETCH_SIZE / WRITE_SIZE counters scaled by the same
   counters on a plain copy, when they were taken on the current kernel
-  source.  Beside it: the forward with the smaller workspace (NF4 dequantised
-  inside the product's K loop, no bf16 copy of W0) and with none (the fused
-  kernel), and roofline["decode"]: NF4 decode at M = 1, weight-stream bytes
+  source.  Beside it: the forward and dX calls, the forward through the
+  older fused kernel (the weight dense bf16, as its only K-loop form here),
+  and roofline["decode"]: NF4 decode at M = 1, weight-stream bytes
   per graph-replayed call over 40 cold weight copies, against the HBM peak.
 * cpu_baseline: the CPU oracle (float64 NumPy) on the same step.
 * secondary lines in the same JSON object: NF4 decode (M = 1, 4, 16) GB/s on
@@ -35,7 +36,7 @@ Default run (python bench.py [--steps K] [--warmup W]):
   backward of config 2 (q and v, bf16, M = 4096, r = 8) and of config 4 (the
   seven projections of a block, NF4, M = 8192, r = 64).
 
-Profiling helpers (for rocprofv3): --mode fwd | fwd_inloop | fwd_fused | dx | step
+Profiling helpers (for rocprofv3): --mode fwd | fwd_fused | dx | step
 | decode | copy | quant run only that part, a few iterations (after CLOCK_WARMUP_S seconds of
 the same work for the first five), and print one line.
 """
@@ -56,7 +57,7 @@ METRIC = "QLoRA linear fwd+bwd TFLOP/s (4096²,r=16,M=2048); NF4 decode HBM GB/s
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 FLOP/clk)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 M, N, K, R = 2048, 4096, 4096, 16
-G256_FLOP = 2 * M * N * K + 2 * M * N * R                         # product + expand kernel
+PROD_FLOP = 2 * M * N * K + 2 * M * K * R + 2 * M * N * R       # product + shrink + expand
 STEP_FLOP = 2 * (2 * M * N * K) + 6 * M * R * (N + K)             # fwd + bwd, algorithmic
 NF4_STREAM_BYTES = N * K // 2 + N * K // 64 + 4 * (N * K // 64 // 256)   # 8,654,848
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -75,7 +76,7 @@ def src_hash(files):
     return h.hexdigest()[:16]
 
 
-G256_SOURCES = ["gemm256.hip", "device_util.h", "common.h"]
+PROD_SOURCES = ["gemm256.hip", "device_util.h", "common.h"]
 
 
 def traffic_for(kernel, sources):
@@ -196,8 +197,6 @@ def setup(torch):
                           device=dev)
     S["wsf"] = torch.empty(lq.lq_workspace_size(lq.LQ_OP_FWD, M, N, K, R), dtype=torch.uint8,
                            device=dev)
-    S["wsi"] = torch.empty(lq.lq_workspace_size(lq.LQ_OP_FWD_FUSED, M, N, K, R),
-                           dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     return S
 
@@ -207,17 +206,12 @@ def fwd(S):
     lq.lq_lora_fwd(S["X"], S["W"], S["A"], S["B"], S["s"], T_out=S["T"], Y=S["Y"], ws=S["wsf"])
 
 
-def fwd_inloop(S):
-    """The forward with the smaller workspace: NF4 dequantised inside the
-    product's K loop, no bf16 copy of W0."""
-    lq = S["lq"]
-    lq.lq_lora_fwd(S["X"], S["W"], S["A"], S["B"], S["s"], T_out=S["T"], Y=S["Y"], ws=S["wsi"])
-
-
 def fwd_fused(S):
-    """The forward with no workspace: the fused kernel (T in the same K loop)."""
+    """The forward of the same layer with the weight dense bf16 and no
+    workspace: the older fused kernel (T in the same K loop, bf16 operands
+    from LDS), for comparison with the K-loop NF4 product."""
     lq = S["lq"]
-    lq.lq_lora_fwd(S["X"], S["W"], S["A"], S["B"], S["s"], T_out=S["T"], Y=S["Y"], no_ws=True)
+    lq.lq_lora_fwd(S["X"], S["W0d"], S["A"], S["B"], S["s"], T_out=S["T"], Y=S["Y"], no_ws=True)
 
 
 def bwd(S):
@@ -534,8 +528,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--mode", default="full",
-                    choices=["full", "step", "fwd", "fwd_inloop", "fwd_fused", "dx", "decode", "copy",
-                             "quant"])
+                    choices=["full", "step", "fwd", "fwd_fused", "dx", "decode", "copy", "quant"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-secondary", action="store_true")
     a = ap.parse_args(argv)
@@ -574,19 +567,17 @@ def main(argv=None):
                 fn(S)
             torch.cuda.synchronize()
 
-    if a.mode in ("fwd", "dx", "step", "fwd_inloop", "fwd_fused"):
-        settle({"fwd": fwd, "dx": dx_only, "step": step, "fwd_inloop": fwd_inloop,
-                "fwd_fused": fwd_fused}[a.mode])
+    if a.mode in ("fwd", "dx", "step", "fwd_fused"):
+        settle({"fwd": fwd, "dx": dx_only, "step": step, "fwd_fused": fwd_fused}[a.mode])
     if a.mode == "fwd":
         for _ in range(a.steps):
             fwd(S)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "fwd", "launches": a.steps}))
         return 0
-    if a.mode in ("fwd_inloop", "fwd_fused"):
-        f = fwd_inloop if a.mode == "fwd_inloop" else fwd_fused
+    if a.mode == "fwd_fused":
         for _ in range(a.steps):
-            f(S)
+            fwd_fused(S)
         torch.cuda.synchronize()
         print(json.dumps({"mode": a.mode, "launches": a.steps}))
         return 0
@@ -651,49 +642,46 @@ def main(argv=None):
     ms_graph = (time.perf_counter() - t0) * 1e3 / a.steps
     del g
 
-    # dominant kernel: the large-tile product of the forward or of dX (the
-    # same algorithmic FLOPs); event pairs recorded by the library around each
+    # dominant kernel: the K-loop product of the forward or of dX (the same
+    # algorithmic FLOPs); event pairs recorded by the library around each
     # launch, on the stream it is launched on
     lq = S["lq"]
     t_fwd_call = cuda_time(lambda: fwd(S), 50, torch)
     t_dx_call = cuda_time(lambda: dx_only(S), 50, torch)
-    t_inloop_call = cuda_time(lambda: fwd_inloop(S), 50, torch)
     t_fused_call = cuda_time(lambda: fwd_fused(S), 20, torch)
     t_step_ev = cuda_time(lambda: step(S), 20, torch)
     lq.lq_timing_enable(True)
-    for k in ("g256_fwd", "g256_dx", "q256_fwd"):
+    for k in ("q256_fwd", "q256_dx"):
         lq.lq_timing_read(k)
     with SclkSampler() as kclk:
         for _ in range(50):
             fwd(S)
             dx_only(S)
-            fwd_inloop(S)
         torch.cuda.synchronize()
-    ms_f, n_f = lq.lq_timing_read("g256_fwd")
-    ms_d, n_d = lq.lq_timing_read("g256_dx")
-    ms_q, n_q = lq.lq_timing_read("q256_fwd")
+    ms_f, n_f = lq.lq_timing_read("q256_fwd")
+    ms_d, n_d = lq.lq_timing_read("q256_dx")
     lq.lq_timing_enable(False)
-    t_fwd, t_dx, t_q = ms_f / max(n_f, 1), ms_d / max(n_d, 1), ms_q / max(n_q, 1)
+    t_fwd, t_dx = ms_f / max(n_f, 1), ms_d / max(n_d, 1)
     if t_dx > t_fwd:
-        name, t_dom = "g256_kernel<dX> (bf16 product dY Wd + expand, 256x128 tiles)", t_dx
-        traffic = traffic_for("g256_dx", G256_SOURCES)
+        name, t_dom = ("q256_dx_kernel (dY deq(W0) with NF4 dequantised in the K loop, U = dY B "
+                       "in the same loop, expand; 128x256 tiles)"), t_dx
+        traffic = traffic_for("q256_dx", PROD_SOURCES)
     else:
-        name, t_dom = "g256_kernel<fwd> (bf16 product X Wd^T + expand, 256x128 tiles)", t_fwd
-        traffic = traffic_for("g256_fwd", G256_SOURCES)
-    achieved = G256_FLOP / (t_dom * 1e-3) / 1e12
+        name, t_dom = ("q256_fwd_kernel (X deq(W0)^T with NF4 dequantised in the K loop, T = X A^T "
+                       "in the same loop, expand; 128x256 tiles)"), t_fwd
+        traffic = traffic_for("q256_fwd", PROD_SOURCES)
+    achieved = PROD_FLOP / (t_dom * 1e-3) / 1e12
     roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 1),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-            "flop_per_launch": G256_FLOP, "us_per_launch": round(t_dom * 1e3, 2),
+            "flop_per_launch": PROD_FLOP, "us_per_launch": round(t_dom * 1e3, 2),
             "sclk_mhz": kclk.mhz,
             "frac_at_sclk": (round(achieved / (PEAK_BF16_TFLOPS * kclk.mhz / PEAK_SCLK_MHZ), 4)
                              if kclk.mhz else None),
             "launches_timed": min(n_f, n_d),
             "us_fwd_kernel": round(t_fwd * 1e3, 2), "us_dx_kernel": round(t_dx * 1e3, 2),
             "us_fwd_call": round(t_fwd_call * 1e3, 2), "us_dx_call": round(t_dx_call * 1e3, 2),
-            "us_fwd_inloop_kernel": round(t_q * 1e3, 2),
-            "us_fwd_inloop_call": round(t_inloop_call * 1e3, 2),
-            "us_fwd_fused_call": round(t_fused_call * 1e3, 2)}
+            "us_fwd_fused_dense_call": round(t_fused_call * 1e3, 2)}
     # NF4 decode at M = 1: weight-stream bytes per call over the graph-replayed
     # call time with cold weights, against the HBM peak
     dec = decode_bench(S, torch)

@@ -482,9 +482,12 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
             "workspace %zu bytes, need %zu", ws_bytes, need);
     return decode_chunks(X, M, *W0, A, B, r, scale, Y, T_out, (float*)ws, stream);
   }
+  // an NF4 weight with enough 128 x 256 tiles: the product that dequantises
+  // in its K loop and forms T in the same loop (no bf16 copy of W0, no
+  // workspace), whatever workspace was given
+  if (dispatch::inloop_fwd_eligible(*W0, M))
+    return dispatch::inloop_fwd(X, M, *W0, A, B, r, scale, Y, T_out, stream);
   if (big_ok) return dispatch::big_fwd(X, M, *W0, A, B, r, scale, Y, T_out, ws, stream);
-  if (ws && ws_bytes >= (size_t)(M * r) * 4 && dispatch::inloop_fwd_eligible(*W0, M))
-    return dispatch::inloop_fwd(X, M, *W0, A, B, r, scale, Y, T_out ? T_out : (float*)ws, stream);
   return dispatch::bf16_fwd(X, M, *W0, A, B, r, scale, Y, T_out, stream);
 }
 

@@ -97,13 +97,22 @@ size_t big_dx_ws_bytes(int64_t M, int64_t N, int64_t K);
 int big_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,
             float s, void* Y, float* T_out, void* ws, hipStream_t st, const void* Xa = nullptr,
             float inv_keep = 1.0f);
-// Large-M NF4 forward with no copy of W0: T (M x r float32, written to T),
-// then the 128 x 256-tile product that dequantises the codes inside its K loop
-// and adds the expand in its epilogue.  Eligible for an NF4 weight with
-// N % 128 == 0, K % 256 == 0 and at least 192 tiles.
+// Large-M NF4 forward with no copy of W0, in one launch: the 128 x 256-tile
+// product that dequantises the codes inside its K loop, forms T = X A^T in the
+// same loop (stored to T_out, M x r float32, when not NULL) and adds the
+// expand in its epilogue.  Eligible for an NF4 weight with N % 128 == 0,
+// K % 256 == 0 and at least 192 tiles.
 bool inloop_fwd_eligible(const lq_weight& W, int64_t M);
 int inloop_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
-               int64_t r, float s, void* Y, float* T, hipStream_t st);
+               int64_t r, float s, void* Y, float* T_out, hipStream_t st);
+// Large-M NF4 dX with no copy of W0, in one launch: the 128 x 256-tile product
+// that dequantises the codes inside its K loop (read back transposed), forms
+// U = dY B in the same loop (stored to U_out, M x r float32, when not NULL)
+// and adds the expand (s U) A in its epilogue.  Eligible for an NF4 weight
+// with K % 256 == 0, N % 128 == 0, r % 8 == 0 and at least 192 tiles.
+bool inloop_dx_eligible(const lq_weight& W, int64_t M, int64_t r);
+int inloop_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B,
+              int64_t r, float s, void* dX, float* U_out, hipStream_t st);
 // Multi-adapter forward at large T (same eligibility as the forward).
 size_t big_multi_ws_bytes(int64_t T, int64_t N, int64_t K, int64_t rc);
 int big_fwd_multi(const void* X, int64_t T, const lq_weight& W, const void* A_cat,

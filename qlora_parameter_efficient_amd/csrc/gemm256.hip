@@ -551,15 +551,17 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// Forward with the NF4 weight dequantised inside the K loop (no bf16 copy of
-// W0 anywhere): Y = X deq(W0)^T + (s T) B^T.
+// Forward with the NF4 weight dequantised inside the K loop and the rank-r
+// shrink in the same loop (no bf16 copy of W0 anywhere, no separate launch
+// for T): Y = X deq(W0)^T + (s T) B^T with T = X A^T formed on the way.
 //
 // Tile 128 (weight rows n) x 256 (activation rows m), eight waves (two per
 // SIMD); wave (wi, wj) owns the 64 x 64 block at (64 wi, 64 wj): 2 x 2
 // accumulators of 32 x 32.  Per 64-wide reduction step (one NF4 block per
 // weight row):
 //   * the activation tile (256 rows x 128 bytes) goes straight into LDS by
-//     direct-to-LDS loads, as in g256_kernel;
+//     direct-to-LDS loads, as in g256_kernel, and so does the step's slice of
+//     A (r rows x 128 bytes, same swizzle);
 //   * the NF4 codes of the weight tile, the blocks' 8-bit constants and c2
 //     come by direct-to-LDS loads too, in groups of four steps (a whole
 //     128-byte line of codes per row), one group ahead, into two code
@@ -574,8 +576,15 @@ __global__ __launch_bounds__(kGThreads) void g256_kernel(G256Params p) {
 //     With every global load issued by the kernel itself, the waits are its
 //     own: the end of a step waits until only the code group loads issued in
 //     it (if any) are outstanding.
+//   * the shrink: the two waves that hold the same 64 activation rows split
+//     them, wave wi taking the 32 rows of its operand ms = wi, and add A-slice
+//     x activation products (one 32 x 32 x 16 MFMA per 32 ranks and substep,
+//     ranks past r reading zero or a repeated row of A whose results are never
+//     used) to a T accumulator.  Every column tile of a row block forms the
+//     same T; the one with tile_i = 0 stores it (T_out).
 // Each code is thus dequantised once per 256 activation rows, in registers,
-// and fed to bf16 MFMA from LDS.  The expand runs in the epilogue as in
+// and fed to bf16 MFMA from LDS.  After the loop T goes through LDS as
+// bf16(s T) to the waves that need its rows for the expand, which runs as in
 // g256_kernel; the tile is staged in LDS as bf16 and written with 16-byte
 // stores.
 constexpr int kQI = 128, kQJ = 256;
@@ -586,11 +595,14 @@ constexpr int kQThreads = 512;  // 8 waves: two per SIMD
 // code buffer: codes (128 rows x 128 bytes), 8-bit constants (one dword per
 // row and wave), c2 / absmax [step][row]
 constexpr int kQCQ8 = 16384, kQCC2 = 16384 + 2048, kQCB = 16384 + 2048 + 2048;
+// slice of A (or of B^T) for one step: up to 64 rank rows x 128 bytes
+constexpr int kQAS = 64 * 128;
 
 struct Q256Params {
   const uint16_t* P;  // X, M x K
   WeightArgs W;       // NF4 weight, N x K
-  const float* V;     // T, M x r
+  const uint16_t* A;  // A, r x K
+  float* T_out;       // T, M x r float32, or NULL
   const uint16_t* E;  // B, N x r
   uint16_t* Y;        // M x N
   int64_t M, N, K;
@@ -652,10 +664,12 @@ __device__ __forceinline__ void write16(uint32_t addr, const u32x4& v) {
   *(lds_ptr)(uintptr_t)addr = v;
 }
 
-template <int WK, bool FP8>
+// RQ: 32-rank blocks of the shrink (1 for r <= 32, 2 for r <= 64)
+template <int WK, bool FP8, int RQ>
 __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * kQStage];
   __shared__ __attribute__((aligned(1024))) char cst[2 * kQCB];
+  __shared__ __attribute__((aligned(1024))) char aslc[2 * kQAS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = wave & 1, wj = wave >> 1;
@@ -685,6 +699,29 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) dma16(pb, poff[u], at + (32 * wave + 8 * u) * 128);
   };
+  // A slice of a step: wave w brings rank rows 8 w .. 8 w + 7 when 8 w < r
+  // (rows past r repeat row r - 1); rows from the next multiple of 8 up to
+  // 32 RQ are zero, written once below
+  const int r = p.r;
+  const uint32_t abase = lds_addr(aslc);
+  const bool a_rows = 8 * wave < r;
+  uint32_t aoff;
+  {
+    const int row = 8 * wave + (lane >> 3);
+    const int srow = row < r ? row : r - 1;
+    aoff = (uint32_t)(((int64_t)srow * K + 8 * ((lane & 7) ^ rswz(row))) * 2);
+  }
+  const char* abase0 = reinterpret_cast<const char*>(p.A);
+  auto issue_a = [&](int kt, int b) {
+    if (a_rows) dma16(abase0 + (int64_t)kt * kGK * 2, aoff, abase + b * kQAS + 8 * wave * 128);
+  };
+  {
+    const int rp = (r + 7) & ~7;
+    for (int i = tid; i < 2 * (32 * RQ - rp) * 8; i += kQThreads) {
+      const int b = i / ((32 * RQ - rp) * 8), rem = i - b * (32 * RQ - rp) * 8;
+      write16(abase + b * kQAS + rp * 128 + rem * 16, u32x4{0u, 0u, 0u, 0u});
+    }
+  }
   // Weight codes and block constants arrive by direct-to-LDS loads as well,
   // in groups of four steps (one 128-byte line of codes per row), into one of
   // two code buffers: the group's codes (128 rows x 128 bytes; chunk c of row
@@ -753,23 +790,32 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
   for (int s = 0; s < 4; ++s) pcx[s] = (uint32_t)(((2 * s + h) ^ sw) << 4);
   const uint32_t prow = (uint32_t)((64 * wj + l32) * 128);
   const uint32_t qrow = (uint32_t)((64 * wi + l32) * 128);
-  auto load_frags = [&](uint32_t st, int s, u32x4 (&wf)[2], u32x4 (&xf)[2]) {
+  const uint32_t arow = (uint32_t)(l32 * 128);
+  auto load_frags = [&](uint32_t st, uint32_t as, int s, u32x4 (&wf)[2], u32x4 (&xf)[2],
+                        u32x4 (&af)[RQ]) {
 #pragma unroll
     for (int ms = 0; ms < 2; ++ms) xf[ms] = read16(st + kQWT + prow + ms * 32 * 128 + pcx[s]);
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) wf[ns] = read16(st + qrow + ns * 32 * 128 + pcx[s]);
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) af[q] = read16(as + arow + q * 32 * 128 + pcx[s]);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][2], tacc[RQ];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+#pragma unroll
+  for (int q = 0; q < RQ; ++q)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tacc[q][v] = 0.0f;
 
   // prologue: step 0's tiles in stage 0, group 0's codes in code buffer 0
   issue_act(0, 0);
+  issue_a(0, 0);
   issue_group(0, 0);
   wait_dma();
   __syncthreads();
@@ -793,16 +839,20 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
     constexpr int B = J & 1, POS = J & 3, BUF = J >> 2;
     constexpr int NPOS = (POS + 1) & 3, NBUF = POS == 3 ? BUF ^ 1 : BUF;  // step kt + 1
     const bool more = kt + 1 < KT;
-    if (more) issue_act(kt + 1, B ^ 1);
+    if (more) {
+      issue_act(kt + 1, B ^ 1);
+      issue_a(kt + 1, B ^ 1);
+    }
     const bool grp = POS == 1 && (kt >> 2) + 1 < NG;
     if (grp) issue_group((kt >> 2) + 1, BUF ^ 1);
     const uint32_t st = sbase + B * kQStage;
+    const uint32_t as = abase + B * kQAS;
     const uint32_t wt = sbase + (B ^ 1) * kQStage;
     // (after the last step the words read here are stale and their
     // dequantised values land in a tile nobody reads: no branch, so that the
     // dequantisation can be scheduled between the MFMAs)
-    u32x4 wf[2][2], xf[2][2];
-    load_frags(st, 0, wf[0], xf[0]);
+    u32x4 wf[2][2], xf[2][2], af[2][RQ];
+    load_frags(st, as, 0, wf[0], xf[0], af[0]);
     const u32x2 cw = codes_at(NBUF, NPOS);
     const u32x2 raw = raw_at(NBUF, NPOS);
     __builtin_amdgcn_sched_barrier(0);
@@ -810,27 +860,30 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c = s & 1;
-      if (s < 3) load_frags(st, s + 1, wf[c ^ 1], xf[c ^ 1]);
+      if (s < 3) load_frags(st, as, s + 1, wf[c ^ 1], xf[c ^ 1], af[c ^ 1]);
       if (s == 0) pt = perm_table(p.tab, scale_of(raw, NPOS));
 #pragma unroll
       for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf[c][ms], acc[ns][ms]);
+      const u32x4 xt = wi ? xf[c][1] : xf[c][0];
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) tacc[q] = mfma32(af[c][q], xt, tacc[q]);
       if (s == 1 || s == 2) write16(wt + wdst[s - 1], perm_deq8(cw[s - 1], pt));
       // the next substep's reads first, then each MFMA followed by a share of
       // the dequantisation, then the store of the dequantised word
-      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 4 + RQ, 0);
       if (s == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4 + RQ; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 52 / (4 + RQ), 0);
         }
       } else if (s < 3) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4 + RQ; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 32 / (4 + RQ), 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
       }
@@ -868,8 +921,49 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
     step(kt + 3, I3{});
   }
 
+  // ---- T: lane (l32, h) of wave (wi, wj) holds T[m][32 q + 8 v + 4 h + e]
+  // in tacc[q][4 v + e], m = 64 wj + 32 wi + l32 of the tile.  The column
+  // tile 0 stores it; every tile passes bf16(s T) (zero past r) through LDS
+  // (row m, 128 bytes, after the stages' 64 KB of output staging) to the
+  // waves of the expand.
+  const int64_t mt = j0 + 64 * wj + 32 * wi + l32;
+  if (tile_i == 0 && p.T_out && mt < M) {
+    float* trow = p.T_out + mt * r;
+#pragma unroll
+    for (int q = 0; q < RQ; ++q)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 32 * q + 8 * v + 4 * h;
+        if (j + 4 <= r && (r & 3) == 0) {
+          *reinterpret_cast<f32x4*>(trow + j) =
+              f32x4{tacc[q][4 * v], tacc[q][4 * v + 1], tacc[q][4 * v + 2], tacc[q][4 * v + 3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j + e < r) trow[j + e] = tacc[q][4 * v + e];
+        }
+      }
+  }
+  const uint32_t tl = sbase + 65536;
+  {
+    const uint32_t trow = tl + (uint32_t)((64 * wj + 32 * wi + l32) * 128);
+    const float sc = p.s;
+#pragma unroll
+    for (int q = 0; q < RQ; ++q)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 32 * q + 8 * v + 4 * h;
+        float e4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) e4[e] = j + e < r ? sc * tacc[q][4 * v + e] : 0.0f;
+        typedef __attribute__((address_space(3))) u32x2* lds_ptr;
+        *(lds_ptr)(uintptr_t)(trow + 2 * j) =
+            u32x2{pack_bf16x2(e4[0], e4[1]), pack_bf16x2(e4[2], e4[3])};
+      }
+  }
+  __syncthreads();
+
   // ---- expand: acc += B rows x bf16(s T) over rank chunks of 16
-  const int r = p.r;
   for (int c = 0; c < r; c += 16) {
     const int jr = c + 8 * h;
     u32x4 ef[2], vf[2];
@@ -879,11 +973,8 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
       ef[ns] = e_operand_row(p.E + i * r, jr, r);
     }
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
-      int64_t m = j0 + 64 * wj + 32 * ms + l32;
-      m = m < M ? m : M - 1;
-      vf[ms] = v_operand(p.V + m * r, jr, r, p.s);
-    }
+    for (int ms = 0; ms < 2; ++ms)
+      vf[ms] = read16(tl + (uint32_t)((64 * wj + 32 * ms + l32) * 128 + 2 * jr));
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
@@ -915,6 +1006,371 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
     const int64_t m = j0 + j;
     const u32x4 v = read16(sbase + (uint32_t)(j * 256 + ((cl ^ (j & 15)) << 4)));
     if (m < M) *reinterpret_cast<u32x4*>(p.Y + m * N + i0 + 8 * cl) = v;
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// dX with the NF4 weight dequantised inside the K loop and U = dY B formed in
+// the same loop (no bf16 copy of W0 anywhere, no separate launch for U):
+// dX = dY deq(W0) + (s U) A.
+//
+// Tile 128 (outputs k) x 256 (activation rows m), eight waves (two per SIMD);
+// wave (wi, wj) owns the 64 x 64 block at (64 wi, 64 wj).  The reduction runs
+// over the weight's rows n, 64 per step:
+//   * the dY tile (256 rows x 128 bytes) and the step's rows of B (64 x r
+//     bf16, contiguous in B) arrive by direct-to-LDS loads;
+//   * the weight tile is W0's rows n0 .. n0 + 63 over the tile's 128 columns:
+//     64 code bytes per row and two NF4 blocks, which share one 8-bit
+//     constant word and one c2 (the blocks are an even-odd pair, so they sit
+//     in one dword of constants and one group of 256).  Codes and constants
+//     come by direct-to-LDS loads in groups of two steps (128 rows), issued
+//     two steps before the step that dequantises them, into two code buffers.
+//     Thread t dequantises row t / 8, columns 16 (t & 7) .. + 15 of the next
+//     step (one block: the same byte-plane table and v_perm_b32 lookups as
+//     the forward), between the current step's MFMAs, and stores them into
+//     the other stage's weight tile in storage order (row n of 256 bytes,
+//     16-byte chunk c at c ^ 4 (n & 3));
+//   * the weight operand (one output column, eight consecutive n) is read
+//     with the transposing ds_read_b64_tr_b16; with the swizzle above the 32
+//     lanes of a read touch 16 distinct 16-byte bank groups;
+//   * U: the waves holding the same 64 dY rows split them as in the forward;
+//     the B operand (one rank, eight consecutive n) is read from the step's
+//     rows of B with the same transposing read (ranks past r read
+//     neighbouring rows; those results are never used).
+// Needs r % 8 == 0 (the transposing read's 8-byte alignment in rows of 2r
+// bytes).  The column tile 0 stores U; the expand adds (s U) A in the
+// epilogue as in g256_kernel.
+constexpr int kDCodes = 128 * 64;                 // codes of a group: 128 rows x 64 bytes
+constexpr int kDCB = kDCodes + 512 + 512;         // + constant words, + c2 (per row)
+constexpr int kDBS = 64 * 128 + 256;              // step's rows of B (up to 64 x 64), padded
+
+struct Q256DxParams {
+  const uint16_t* P;  // dY, M x N
+  WeightArgs W;       // NF4 weight, N x K
+  const uint16_t* G;  // B, N x r
+  float* U_out;       // U, M x r float32 (column tile 0 stores it)
+  const uint16_t* E;  // A, r x K
+  uint16_t* Y;        // dX, M x K
+  int64_t M, N, K;
+  int32_t r;
+  float s;
+  int32_t ti, tj;
+  NF4Table tab;
+};
+
+template <int WK, bool FP8, int RQ>
+__global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kQStage];
+  __shared__ __attribute__((aligned(1024))) char cst[2 * kDCB];
+  __shared__ __attribute__((aligned(1024))) char bslc[2 * kDBS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wi = wave & 1, wj = wave >> 1;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int t = xcd_tile(blockIdx.x, p.ti * p.tj);
+  const int tile_j = t / p.ti, tile_i = t - tile_j * p.ti;
+  const int64_t i0 = (int64_t)tile_i * kQI, j0 = (int64_t)tile_j * kQJ;
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int KT = (int)(N / kGK);  // even
+  const int NG = KT / 2;
+  const int r = p.r;
+  const uint32_t sbase = lds_addr(smem);
+  const uint32_t cbase = lds_addr(cst);
+  const uint32_t bbase = lds_addr(bslc);
+
+  // dY DMA: wave w fills rows 32 w .. 32 w + 31, 8 rows per instruction
+  uint32_t poff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = 32 * wave + 8 * u + (lane >> 3);
+    int64_t m = j0 + row;
+    m = m < M ? m : M - 1;
+    poff[u] = (uint32_t)((m * N + 8 * ((lane & 7) ^ rswz(row))) * 2);
+  }
+  const char* pbase0 = reinterpret_cast<const char*>(p.P);
+  auto issue_act = [&](int kt, int b) {
+    const uint32_t at = sbase + b * kQStage + kQWT;
+    const char* pb = pbase0 + (int64_t)kt * kGK * 2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dma16(pb, poff[u], at + (32 * wave + 8 * u) * 128);
+  };
+  // the step's rows of B: 128 r contiguous bytes, wave w brings the w-th KB
+  const bool b_part = 8 * wave < r;
+  const char* gbase0 = reinterpret_cast<const char*>(p.G);
+  auto issue_b = [&](int kt, int b) {
+    if (b_part)
+      dma16(gbase0 + (int64_t)kt * kGK * r * 2, (uint32_t)(1024 * wave + 16 * lane),
+            bbase + b * kDBS + 1024 * wave);
+  };
+  // Group g (steps 2 g, 2 g + 1: weight rows 128 g .. + 127): codes, wave w
+  // rows 16 w .. + 15 (four lanes per 64-byte row); waves 0 and 1 the dwords
+  // of 8-bit constants (float32 absmax of the even block without a second
+  // level) of rows 0 .. 63 and 64 .. 127, waves 2 and 3 the rows' c2 (the odd
+  // block's absmax).
+  const int64_t KB = K / 64;
+  const int64_t cb0 = i0 / 64;  // the tile's first block within a row (even)
+  const uint32_t coff = (uint32_t)((16 * wave + (lane >> 2)) * (K / 2) + i0 / 2 + 16 * (lane & 3));
+  const int crow = 64 * (wave & 1) + lane;  // constants row of waves 0 .. 3
+  const bool c_part = wave < 4;
+  auto issue_group = [&](int g, int buf) {
+    const uint32_t cb = cbase + buf * kDCB;
+    dma16(reinterpret_cast<const char*>(p.W.codes) + (int64_t)g * 128 * (K / 2), coff,
+          cb + 16 * wave * 64);
+    if (c_part) {
+      const int64_t blk = (128 * (int64_t)g + crow) * KB + cb0;
+      const uint32_t dst = cb + kDCodes + (wave >> 1) * 512 + 256 * (wave & 1);
+      if (WK == kNF4DQ) {
+        if (wave < 2) dma4(p.W.q8, (uint32_t)(blk & ~(int64_t)3), dst);
+        else dma4(p.W.c2, (uint32_t)((blk >> 8) * 4), dst);
+      } else {
+        dma4(p.W.absmax, (uint32_t)((blk + (wave >> 1)) * 4), dst);
+      }
+    }
+  };
+  auto wait_but_group = [&]() {
+    if (c_part) wait_dma_but<2>();
+    else wait_dma_but<1>();
+  };
+  // dequantisation: thread t, row t / 8 of the step, columns 16 (t & 7) .. + 15
+  const int dx_row = tid >> 3, dx_j = tid & 7;
+  auto codes_at = [&](int buf, int pos) {
+    typedef __attribute__((address_space(3))) const u32x2* lp;
+    return *(lp)(uintptr_t)(cbase + buf * kDCB + (64 * pos + dx_row) * 64 + 8 * dx_j);
+  };
+  auto raw_at = [&](int buf, int pos) {
+    typedef __attribute__((address_space(3))) const uint32_t* lp;
+    const uint32_t cb = cbase + buf * kDCB + kDCodes + 4 * (64 * pos + dx_row);
+    return u32x2{*(lp)(uintptr_t)cb, *(lp)(uintptr_t)(cb + 512)};
+  };
+  const int qsh = 8 * ((int)(cb0 & 3) + (dx_j >> 2));  // the block's byte in the dword
+  auto scale_of = [&](const u32x2& v) {
+    if (WK == kNF4DQ) return dq_value<FP8>((v[0] >> qsh) & 0xFFu) * dq_step(__uint_as_float(v[1]));
+    return __uint_as_float((dx_j >> 2) ? v[1] : v[0]);
+  };
+  uint32_t wdst[2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+    wdst[d] = (uint32_t)(dx_row * 256 + (((2 * dx_j + d) ^ (4 * (dx_row & 3))) << 4));
+
+  // operand reads: dY as the forward's activations; the weight and B
+  // operands transposed (lane group of 16: rows nlo = gc / 4 and nlo + 4,
+  // four columns 4 (gc & 3) .. + 3 of its 16-column half)
+  const int sw = rswz(l32);
+  uint32_t pcx[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) pcx[s] = (uint32_t)(((2 * s + h) ^ sw) << 4);
+  const uint32_t prow = (uint32_t)((64 * wj + l32) * 128);
+  const int gc = l32 & 15, half = l32 >> 4, nlo = gc >> 2;
+  uint32_t qtr[2];
+#pragma unroll
+  for (int ns = 0; ns < 2; ++ns) {
+    const int col = 64 * wi + 32 * ns + 16 * half + 4 * (gc & 3);
+    qtr[ns] = (uint32_t)((8 * h + nlo) * 256 + (((col >> 3) ^ (4 * nlo)) << 4) + (col & 7) * 2);
+  }
+  const uint32_t btr = (uint32_t)((8 * h + nlo) * 2 * r + 2 * (16 * half + 4 * (gc & 3)));
+  auto load_frags = [&](uint32_t st, uint32_t bs, int s, u32x4 (&wf)[2], u32x4 (&xf)[2],
+                        u32x4 (&bf)[RQ]) {
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms) xf[ms] = read16(st + kQWT + prow + ms * 32 * 128 + pcx[s]);
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns) {
+      const uint32_t a = st + (uint32_t)(16 * s * 256) + qtr[ns];
+      const u32x2 lo = read_tr(a), hi = read_tr(a + 4 * 256);
+      wf[ns] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      const uint32_t a = bs + (uint32_t)(16 * s * 2 * r + 64 * q) + btr;
+      const u32x2 lo = read_tr(a), hi = read_tr(a + (uint32_t)(8 * r));
+      bf[q] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
+
+  f32x16 acc[2][2], uacc[RQ];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+#pragma unroll
+  for (int q = 0; q < RQ; ++q)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) uacc[q][v] = 0.0f;
+
+  // prologue: step 0's tiles in stage 0, groups 0 and 1 in code buffers 0, 1;
+  // step 0 dequantised into stage 0
+  issue_act(0, 0);
+  issue_b(0, 0);
+  issue_group(0, 0);
+  if (NG > 1) issue_group(1, 1);
+  wait_dma();
+  __syncthreads();
+  {
+    const u32x2 cw = codes_at(0, 0);
+    const PermTable pt = perm_table(p.tab, scale_of(raw_at(0, 0)));
+#pragma unroll
+    for (int d = 0; d < 2; ++d) write16(sbase + wdst[d], perm_deq8(cw[d], pt));
+  }
+  __syncthreads();
+
+  // Step kt (J = kt mod 4: stage and position in the group J & 1, code
+  // buffer J >> 1): the dY and B loads of step kt + 1; in position 1 the
+  // loads of group kt / 2 + 2 into this step's (now free) code buffer; the
+  // MFMAs of step kt with the dequantisation of step kt + 1 between them; at
+  // the end, wait for everything but the group loads issued in this step.
+  auto step = [&](int kt, auto jj) {
+    constexpr int J = decltype(jj)::value;
+    constexpr int B = J & 1, POS = J & 1, BUF = J >> 1;
+    constexpr int NPOS = POS ^ 1, NBUF = POS == 1 ? BUF ^ 1 : BUF;  // step kt + 1
+    const bool more = kt + 1 < KT;
+    if (more) {
+      issue_act(kt + 1, B ^ 1);
+      issue_b(kt + 1, B ^ 1);
+    }
+    const bool grp = POS == 1 && (kt >> 1) + 2 < NG;
+    if (grp) issue_group((kt >> 1) + 2, BUF);
+    const uint32_t st = sbase + B * kQStage;
+    const uint32_t bs = bbase + B * kDBS;
+    const uint32_t wt = sbase + (B ^ 1) * kQStage;
+    // (after the last step the words read here are stale and their
+    // dequantised values land in a tile nobody reads)
+    u32x4 wf[2][2], xf[2][2], bf[2][RQ];
+    load_frags(st, bs, 0, wf[0], xf[0], bf[0]);
+    const u32x2 cw = codes_at(NBUF, NPOS);
+    const u32x2 raw = raw_at(NBUF, NPOS);
+    __builtin_amdgcn_sched_barrier(0);
+    PermTable pt;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c = s & 1;
+      if (s < 3) load_frags(st, bs, s + 1, wf[c ^ 1], xf[c ^ 1], bf[c ^ 1]);
+      if (s == 0) pt = perm_table(p.tab, scale_of(raw));
+#pragma unroll
+      for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf[c][ms], acc[ns][ms]);
+      const u32x4 xt = wi ? xf[c][1] : xf[c][0];
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) uacc[q] = mfma32(bf[c][q], xt, uacc[q]);
+      if (s == 1 || s == 2) write16(wt + wdst[s - 1], perm_deq8(cw[s - 1], pt));
+      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6 + 2 * RQ, 0);
+      if (s == 0) {
+#pragma unroll
+        for (int i = 0; i < 4 + RQ; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 52 / (4 + RQ), 0);
+        }
+      } else if (s < 3) {
+#pragma unroll
+        for (int i = 0; i < 4 + RQ; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 32 / (4 + RQ), 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (grp)
+      wait_but_group();
+    else
+      wait_dma();
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  int kt = 0;
+  for (; kt + 4 <= KT; kt += 4) {
+    step(kt, I0{});
+    step(kt + 1, I1{});
+    step(kt + 2, I2{});
+    step(kt + 3, I3{});
+  }
+  if (kt < KT) {  // KT even: one more group of two
+    step(kt, I0{});
+    step(kt + 1, I1{});
+  }
+
+  // ---- U as T in the forward: column tile 0 stores it, bf16(s U) (zero
+  // past r) goes through LDS to the waves of the expand
+  const int64_t mt = j0 + 64 * wj + 32 * wi + l32;
+  if (tile_i == 0 && p.U_out && mt < M) {
+    float* urow = p.U_out + mt * r;
+#pragma unroll
+    for (int q = 0; q < RQ; ++q)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 32 * q + 8 * v + 4 * h;
+        if (j < r)  // r % 8 == 0: all four or none
+          *reinterpret_cast<f32x4*>(urow + j) =
+              f32x4{uacc[q][4 * v], uacc[q][4 * v + 1], uacc[q][4 * v + 2], uacc[q][4 * v + 3]};
+      }
+  }
+  const uint32_t tl = sbase + 65536;
+  {
+    const uint32_t trow = tl + (uint32_t)((64 * wj + 32 * wi + l32) * 128);
+    const float sc = p.s;
+#pragma unroll
+    for (int q = 0; q < RQ; ++q)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 32 * q + 8 * v + 4 * h;
+        const bool in = j < r;
+        typedef __attribute__((address_space(3))) u32x2* lds_ptr;
+        *(lds_ptr)(uintptr_t)(trow + 2 * j) =
+            in ? u32x2{pack_bf16x2(sc * uacc[q][4 * v], sc * uacc[q][4 * v + 1]),
+                       pack_bf16x2(sc * uacc[q][4 * v + 2], sc * uacc[q][4 * v + 3])}
+               : u32x2{0u, 0u};
+      }
+  }
+  __syncthreads();
+
+  // ---- expand: acc += A columns x bf16(s U) over rank chunks of 16
+  for (int c = 0; c < r; c += 16) {
+    const int jr = c + 8 * h;
+    u32x4 ef[2], vf[2];
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns) {
+      const int64_t i = i0 + 64 * wi + 32 * ns + l32;
+      ef[ns] = e_operand_col(p.E, K, i, jr, r);
+    }
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms)
+      vf[ms] = read16(tl + (uint32_t)((64 * wj + 32 * ms + l32) * 128 + 2 * jr));
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(ef[ns], vf[ms], acc[ns][ms]);
+  }
+
+  // ---- store: bf16 tile in LDS (row j of 256 bytes; chunk c at c ^ (j & 15)),
+  // then whole 256-byte output row segments with 16-byte stores
+  __syncthreads();
+#pragma unroll
+  for (int ms = 0; ms < 2; ++ms) {
+    const int j = 64 * wj + 32 * ms + l32;
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 64 * wi + 32 * ns + 8 * q + 4 * h;  // 4 outputs i .. i + 3
+        const uint32_t a = sbase + (uint32_t)(j * 256 + (((i >> 3) ^ (j & 15)) << 4) + (i & 7) * 2);
+        typedef __attribute__((address_space(3))) u32x2* lds_ptr;
+        *(lds_ptr)(uintptr_t)a = u32x2{pack_bf16x2(acc[ns][ms][4 * q], acc[ns][ms][4 * q + 1]),
+                                       pack_bf16x2(acc[ns][ms][4 * q + 2], acc[ns][ms][4 * q + 3])};
+      }
+  }
+  __syncthreads();
+  const int cl = tid & 15;
+#pragma unroll 4
+  for (int it = 0; it < 8; ++it) {
+    const int j = 32 * it + (tid >> 4);
+    const int64_t m = j0 + j;
+    const u32x4 v = read16(sbase + (uint32_t)(j * 256 + ((cl ^ (j & 15)) << 4)));
+    if (m < M) *reinterpret_cast<u32x4*>(p.Y + m * K + i0 + 8 * cl) = v;
   }
 }
 
@@ -1037,12 +1493,23 @@ bool q256_fwd_fits(const lq_weight& W, int64_t M) {
          (W.N / kQI) * cdiv(M, kQJ) >= 192 && (double)M * W.K * 2 < 4294967296.0;
 }
 
-int launch_q256_fwd(const void* X, int64_t M, const lq_weight& W, const float* T, const void* B,
-                    int64_t r, float s, void* Y, hipStream_t st) {
+template <int RQ>
+void launch_q256_fmt(const lq_weight& W, const Q256Params& p, unsigned blocks, hipStream_t st) {
+  if (W.double_quant == LQ_DQ_FP8)
+    hipLaunchKernelGGL((q256_fwd_kernel<kNF4DQ, true, RQ>), dim3(blocks), dim3(kQThreads), 0, st, p);
+  else if (W.double_quant)
+    hipLaunchKernelGGL((q256_fwd_kernel<kNF4DQ, false, RQ>), dim3(blocks), dim3(kQThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((q256_fwd_kernel<kNF4, false, RQ>), dim3(blocks), dim3(kQThreads), 0, st, p);
+}
+
+int launch_q256_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, float* T_out,
+                    const void* B, int64_t r, float s, void* Y, hipStream_t st) {
   Q256Params p{};
   p.P = (const uint16_t*)X;
   p.W = weight_args(W);
-  p.V = T;
+  p.A = (const uint16_t*)A;
+  p.T_out = T_out;
   p.E = (const uint16_t*)B;
   p.Y = (uint16_t*)Y;
   p.M = M;
@@ -1055,14 +1522,59 @@ int launch_q256_fwd(const void* X, int64_t M, const lq_weight& W, const float* T
   p.tab = nf4_table(W.codebook);
   const unsigned blocks = (unsigned)(p.ti * p.tj);
   timing_begin("q256_fwd", st);
-  if (W.double_quant == LQ_DQ_FP8)
-    hipLaunchKernelGGL((q256_fwd_kernel<kNF4DQ, true>), dim3(blocks), dim3(kQThreads), 0, st, p);
-  else if (W.double_quant)
-    hipLaunchKernelGGL((q256_fwd_kernel<kNF4DQ, false>), dim3(blocks), dim3(kQThreads), 0, st, p);
+  if (r <= 32)
+    launch_q256_fmt<1>(W, p, blocks, st);
   else
-    hipLaunchKernelGGL((q256_fwd_kernel<kNF4, false>), dim3(blocks), dim3(kQThreads), 0, st, p);
+    launch_q256_fmt<2>(W, p, blocks, st);
   timing_end(st);
   return hip_fail(hipGetLastError(), "q256 launch");
+}
+
+// dX of an NF4 weight with the dequantisation and U in the K loop: whole
+// 128-column output tiles, weight rows in groups of 128, whole dwords of
+// 8-bit constants per row (K % 256), r % 8 == 0, enough tiles to fill the
+// chip.
+bool q256_dx_fits(const lq_weight& W, int64_t M, int64_t r) {
+  return W.kind == LQ_WEIGHT_NF4 && W.K % 256 == 0 && W.N % 128 == 0 && r % 8 == 0 && r <= 64 &&
+         (W.K / kQI) * cdiv(M, kQJ) >= 192 && (double)M * W.N * 2 < 4294967296.0;
+}
+
+template <int RQ>
+void launch_q256dx_fmt(const lq_weight& W, const Q256DxParams& p, unsigned blocks,
+                       hipStream_t st) {
+  if (W.double_quant == LQ_DQ_FP8)
+    hipLaunchKernelGGL((q256_dx_kernel<kNF4DQ, true, RQ>), dim3(blocks), dim3(kQThreads), 0, st, p);
+  else if (W.double_quant)
+    hipLaunchKernelGGL((q256_dx_kernel<kNF4DQ, false, RQ>), dim3(blocks), dim3(kQThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((q256_dx_kernel<kNF4, false, RQ>), dim3(blocks), dim3(kQThreads), 0, st, p);
+}
+
+int launch_q256_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B,
+                   int64_t r, float s, void* dX, float* U_out, hipStream_t st) {
+  Q256DxParams p{};
+  p.P = (const uint16_t*)dY;
+  p.W = weight_args(W);
+  p.G = (const uint16_t*)B;
+  p.U_out = U_out;
+  p.E = (const uint16_t*)A;
+  p.Y = (uint16_t*)dX;
+  p.M = M;
+  p.N = W.N;
+  p.K = W.K;
+  p.r = (int32_t)r;
+  p.s = s;
+  p.ti = (int32_t)(W.K / kQI);
+  p.tj = (int32_t)cdiv(M, kQJ);
+  p.tab = nf4_table(W.codebook);
+  const unsigned blocks = (unsigned)(p.ti * p.tj);
+  timing_begin("q256_dx", st);
+  if (r <= 32)
+    launch_q256dx_fmt<1>(W, p, blocks, st);
+  else
+    launch_q256dx_fmt<2>(W, p, blocks, st);
+  timing_end(st);
+  return hip_fail(hipGetLastError(), "q256 dx launch");
 }
 
 // the NF4 weight dequantised to bf16 into the workspace at q (when the prep
@@ -1111,12 +1623,16 @@ int big_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const v
 }
 
 bool inloop_fwd_eligible(const lq_weight& W, int64_t M) { return q256_fwd_fits(W, M); }
+bool inloop_dx_eligible(const lq_weight& W, int64_t M, int64_t r) { return q256_dx_fits(W, M, r); }
+
+int inloop_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B,
+              int64_t r, float s, void* dX, float* U_out, hipStream_t st) {
+  return launch_q256_dx(dY, M, W, A, B, r, s, dX, U_out, st);
+}
 
 int inloop_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
-               int64_t r, float s, void* Y, float* T, hipStream_t st) {
-  int e = t_only(X, M, W.K, A, r, T, st, nullptr, 0, 1.0f);
-  if (e) return e;
-  return launch_q256_fwd(X, M, W, T, B, r, s, Y, st);
+               int64_t r, float s, void* Y, float* T_out, hipStream_t st) {
+  return launch_q256_fwd(X, M, W, A, T_out, B, r, s, Y, st);
 }
 
 int big_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,

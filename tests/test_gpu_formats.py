@@ -119,10 +119,12 @@ def one_hot_rows(M, K, ks):
 @pytest.mark.parametrize("v", VARIANTS, ids=VIDS)
 @pytest.mark.parametrize("M,N,K,fused", [(300, 512, 768, True), (300, 256, 4096, True),
                                          (2100, 512, 768, False), (2048, 256, 4096, False),
-                                         (2100, 3072, 768, True),
+                                         (2100, 3072, 768, True), (2100, 256, 3072, True),
+                                         (2100, 256, 4096, False),
                                          (4, 512, 768, True), (16, 256, 4096, True),
                                          (48, 512, 768, False), (64, 256, 4096, False)],
                          ids=["fused", "fused-k4096", "large", "large-k4096", "kloop",
+                              "kloop-dx", "kloop-dx-k4096",
                               "decode", "decode-k4096", "small-dx", "small-dx-k4096"])
 def test_in_register_dequant_is_exact(v, M, N, K, fused):
     """Y = onehot(k) W'^T with B = 0 returns column k of the dequantised W'
