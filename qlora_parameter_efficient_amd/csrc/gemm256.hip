@@ -597,6 +597,9 @@ constexpr int kQThreads = 512;  // 8 waves: two per SIMD
 constexpr int kQCQ8 = 16384, kQCC2 = 16384 + 2048, kQCB = 16384 + 2048 + 2048;
 // slice of A (or of B^T) for one step: up to 64 rank rows x 128 bytes
 constexpr int kQAS = 64 * 128;
+// second-level steps fl32(c2 / 127) of a 128-row weight tile: 128 K / 64 / 256
+// groups (+ 2 for the ends) for K <= 65536
+constexpr int kQMaxG = 520;
 
 struct Q256Params {
   const uint16_t* P;  // X, M x K
@@ -632,6 +635,40 @@ __device__ __forceinline__ PermTable perm_table(const NF4Table& tab, float a) {
     t.hi[k] = __builtin_amdgcn_perm(pr[2 * k + 1], pr[2 * k], 0x07050301u);
   }
   return t;
+}
+
+// The same table built by the four lanes of a quad that share the block: lane
+// q of the quad forms t_4q .. t_4q+3 from its four levels cbq = cb[4q ..
+// 4q + 3] (same products and rounding, so the same bits), and the eight bf16
+// pairs are gathered with quad broadcasts: 4 multiplies, 2 conversions and 8
+// moves per lane instead of 16 multiplies and 8 conversions.
+__device__ __forceinline__ PermTable perm_table_quad(const float (&cbq)[4], float a) {
+  const int p0 = (int)pack_bf16x2(cbq[0] * a, cbq[1] * a);
+  const int p1 = (int)pack_bf16x2(cbq[2] * a, cbq[3] * a);
+  uint32_t pr[8];  // bf16 pairs (t_2k, t_2k+1)
+  pr[0] = (uint32_t)__builtin_amdgcn_mov_dpp(p0, 0x00, 0xF, 0xF, false);
+  pr[1] = (uint32_t)__builtin_amdgcn_mov_dpp(p1, 0x00, 0xF, 0xF, false);
+  pr[2] = (uint32_t)__builtin_amdgcn_mov_dpp(p0, 0x55, 0xF, 0xF, false);
+  pr[3] = (uint32_t)__builtin_amdgcn_mov_dpp(p1, 0x55, 0xF, 0xF, false);
+  pr[4] = (uint32_t)__builtin_amdgcn_mov_dpp(p0, 0xAA, 0xF, 0xF, false);
+  pr[5] = (uint32_t)__builtin_amdgcn_mov_dpp(p1, 0xAA, 0xF, 0xF, false);
+  pr[6] = (uint32_t)__builtin_amdgcn_mov_dpp(p0, 0xFF, 0xF, 0xF, false);
+  pr[7] = (uint32_t)__builtin_amdgcn_mov_dpp(p1, 0xFF, 0xF, 0xF, false);
+  PermTable t;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    t.lo[k] = __builtin_amdgcn_perm(pr[2 * k + 1], pr[2 * k], 0x06040200u);
+    t.hi[k] = __builtin_amdgcn_perm(pr[2 * k + 1], pr[2 * k], 0x07050301u);
+  }
+  return t;
+}
+
+// the four levels cb[4q .. 4q + 3] of quad lane q = lane & 3
+__device__ __forceinline__ void quad_levels(const NF4Table& tab, int lane, float (&cbq)[4]) {
+  const int q = lane & 3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    cbq[i] = q == 0 ? tab.cb[i] : q == 1 ? tab.cb[4 + i] : q == 2 ? tab.cb[8 + i] : tab.cb[12 + i];
 }
 
 // one byte plane for four codes (one per byte of c, values 0..15): the byte
@@ -670,10 +707,13 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * kQStage];
   __shared__ __attribute__((aligned(1024))) char cst[2 * kQCB];
   __shared__ __attribute__((aligned(1024))) char aslc[2 * kQAS];
+  __shared__ float steptab[WK == kNF4DQ ? kQMaxG : 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = wave & 1, wj = wave >> 1;
   const int h = lane >> 5, l32 = lane & 31;
+  float cbq[4];
+  quad_levels(p.tab, lane, cbq);
   // tiles in activation-row order, so that an XCD's contiguous range of
   // tiles shares one activation tile (its rows stay in that XCD's L2)
   const int t = xcd_tile(blockIdx.x, p.ti * p.tj);
@@ -728,12 +768,21 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
   // x at physical chunk c ^ (x & 7)), the dword of 8-bit constants of each row
   // that holds the group's four blocks (waves 0 and 1; the other waves load
   // copies into unused space, so that every wave issues the same loads), and
-  // each row's c2 (or float32 absmax) for the four steps, [step][row].  Group
-  // g + 1 is loaded during step 4 g + 1.  Thread t dequantises row t / 4,
-  // weights 16 (t & 3) .. + 15 of each block, from LDS.
-  constexpr int NGD = (WK == kNF4DQ ? 1 : 0) + 3;  // group loads per wave
+  // without a second level each row's float32 absmax for the four steps,
+  // [step][row].  (The steps fl32(c2 / 127) of the tile's groups are formed
+  // once, into LDS, before the loop.)  Group g + 1 is loaded during step
+  // 4 g + 1.  Thread t dequantises row t / 4, weights 16 (t & 3) .. + 15 of
+  // each block, from LDS; the quad of threads sharing a row builds its level
+  // table together.
+  constexpr int NGD = 3;  // group loads per wave
   const uint32_t cbase = lds_addr(cst);
   const int64_t KB = K / 64;
+  const int64_t g_lo = (i0 * KB) >> 8;
+  if (WK == kNF4DQ) {
+    const int ng = (int)((((i0 + kQI) * KB - 1) >> 8) - g_lo + 1);
+    for (int i = tid; i < ng; i += kQThreads) steptab[i] = dq_step(p.W.c2[g_lo + i]);
+  }
+  const int64_t wrow_blk = (i0 + (tid >> 2)) * KB;  // first block of this thread's row
   const int NG = KT / 4;
   const int wx = tid >> 2, wq = tid & 3;
   uint32_t coff[2];
@@ -754,12 +803,12 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
     for (int u = 0; u < 2; ++u)
       dma16(reinterpret_cast<const char*>(p.W.codes) + (int64_t)g * 128, coff[u],
             cb + (16 * wave + 8 * u) * 128);
-    if (WK == kNF4DQ) dma4(p.W.q8 + 4 * g, qoff, cb + kQCQ8 + 256 * wave);
-    const int64_t blk = sblk + 4 * g;
-    if (WK == kNF4DQ)
-      dma4(p.W.c2, (uint32_t)((blk >> 8) * 4), cb + kQCC2 + 256 * wave);
-    else
+    if (WK == kNF4DQ) {
+      dma4(p.W.q8 + 4 * g, qoff, cb + kQCQ8 + 256 * wave);
+    } else {
+      const int64_t blk = sblk + 4 * g;
       dma4(p.W.absmax, (uint32_t)(blk * 4), cb + kQCC2 + 256 * wave);
+    }
   };
   // this thread's 16 codes of the step at position pos of the group in code
   // buffer buf (two words), and the raw constants of its block: (c2 or float32
@@ -769,18 +818,19 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
     const int ch = (2 * pos + (wq >> 1)) ^ (wx & 7);
     return *(lp)(uintptr_t)(cbase + buf * kQCB + wx * 128 + ch * 16 + 8 * (wq & 1));
   };
+  // (float32 absmax bits, or the row's word of 8-bit constants)
   auto raw_at = [&](int buf, int pos) {
     typedef __attribute__((address_space(3))) const uint32_t* lp;
     const uint32_t cb = cbase + buf * kQCB;
-    u32x2 v;
-    v[0] = *(lp)(uintptr_t)(cb + kQCC2 + 4 * (128 * pos + wx));
-    v[1] = WK == kNF4DQ ? *(lp)(uintptr_t)(cb + kQCQ8 + 4 * wx) : 0u;
-    return v;
+    return WK == kNF4DQ ? *(lp)(uintptr_t)(cb + kQCQ8 + 4 * wx)
+                        : *(lp)(uintptr_t)(cb + kQCC2 + 4 * (128 * pos + wx));
   };
-  auto scale_of = [&](const u32x2& v, int pos) {
+  // block scale of this thread's row at step kt (position pos of its group)
+  auto scale_of = [&](uint32_t v, int pos, int kt) {
     if (WK == kNF4DQ)
-      return dq_value<FP8>((v[1] >> (8 * pos)) & 0xFFu) * dq_step(__uint_as_float(v[0]));
-    return __uint_as_float(v[0]);
+      return dq_value<FP8>((v >> (8 * pos)) & 0xFFu) *
+             steptab[(int)(((wrow_blk + kt) >> 8) - g_lo)];
+    return __uint_as_float(v);
   };
 
   // operand reads (128-byte-row tiles, as g256_kernel)
@@ -788,13 +838,17 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
   uint32_t pcx[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) pcx[s] = (uint32_t)(((2 * s + h) ^ sw) << 4);
-  const uint32_t prow = (uint32_t)((64 * wj + l32) * 128);
+  // activation operand ms covers rows 64 wj + 32 (ms ^ wi) .. + 31 of the
+  // tile, so that operand 0 is always the 32 rows of this wave's shrink
+  uint32_t prowm[2];
+#pragma unroll
+  for (int ms = 0; ms < 2; ++ms) prowm[ms] = (uint32_t)((64 * wj + 32 * (ms ^ wi) + l32) * 128);
   const uint32_t qrow = (uint32_t)((64 * wi + l32) * 128);
   const uint32_t arow = (uint32_t)(l32 * 128);
   auto load_frags = [&](uint32_t st, uint32_t as, int s, u32x4 (&wf)[2], u32x4 (&xf)[2],
                         u32x4 (&af)[RQ]) {
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) xf[ms] = read16(st + kQWT + prow + ms * 32 * 128 + pcx[s]);
+    for (int ms = 0; ms < 2; ++ms) xf[ms] = read16(st + kQWT + prowm[ms] + pcx[s]);
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) wf[ns] = read16(st + qrow + ns * 32 * 128 + pcx[s]);
 #pragma unroll
@@ -821,7 +875,7 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
   __syncthreads();
   {
     const u32x2 cw = codes_at(0, 0);
-    const PermTable pt = perm_table(p.tab, scale_of(raw_at(0, 0), 0));
+    const PermTable pt = perm_table_quad(cbq, scale_of(raw_at(0, 0), 0, 0));
 #pragma unroll
     for (int d = 0; d < 2; ++d) write16(sbase + wdst[d], perm_deq8(cw[d], pt));
   }
@@ -854,21 +908,20 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
     u32x4 wf[2][2], xf[2][2], af[2][RQ];
     load_frags(st, as, 0, wf[0], xf[0], af[0]);
     const u32x2 cw = codes_at(NBUF, NPOS);
-    const u32x2 raw = raw_at(NBUF, NPOS);
+    const uint32_t raw = raw_at(NBUF, NPOS);
     __builtin_amdgcn_sched_barrier(0);
     PermTable pt;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c = s & 1;
       if (s < 3) load_frags(st, as, s + 1, wf[c ^ 1], xf[c ^ 1], af[c ^ 1]);
-      if (s == 0) pt = perm_table(p.tab, scale_of(raw, NPOS));
+      if (s == 0) pt = perm_table_quad(cbq, scale_of(raw, NPOS, kt + 1));
 #pragma unroll
       for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf[c][ms], acc[ns][ms]);
-      const u32x4 xt = wi ? xf[c][1] : xf[c][0];
 #pragma unroll
-      for (int q = 0; q < RQ; ++q) tacc[q] = mfma32(af[c][q], xt, tacc[q]);
+      for (int q = 0; q < RQ; ++q) tacc[q] = mfma32(af[c][q], xf[c][0], tacc[q]);
       if (s == 1 || s == 2) write16(wt + wdst[s - 1], perm_deq8(cw[s - 1], pt));
       // the next substep's reads first, then each MFMA followed by a share of
       // the dequantisation, then the store of the dequantised word
@@ -974,7 +1027,7 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
     }
 #pragma unroll
     for (int ms = 0; ms < 2; ++ms)
-      vf[ms] = read16(tl + (uint32_t)((64 * wj + 32 * ms + l32) * 128 + 2 * jr));
+      vf[ms] = read16(tl + (uint32_t)((64 * wj + 32 * (ms ^ wi) + l32) * 128 + 2 * jr));
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
@@ -986,7 +1039,7 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
   __syncthreads();
 #pragma unroll
   for (int ms = 0; ms < 2; ++ms) {
-    const int j = 64 * wj + 32 * ms + l32;
+    const int j = 64 * wj + 32 * (ms ^ wi) + l32;
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
@@ -1068,6 +1121,8 @@ __global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = wave & 1, wj = wave >> 1;
   const int h = lane >> 5, l32 = lane & 31;
+  float cbq[4];
+  quad_levels(p.tab, lane, cbq);
   const int t = xcd_tile(blockIdx.x, p.ti * p.tj);
   const int tile_j = t / p.ti, tile_i = t - tile_j * p.ti;
   const int64_t i0 = (int64_t)tile_i * kQI, j0 = (int64_t)tile_j * kQJ;
@@ -1160,7 +1215,9 @@ __global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
   uint32_t pcx[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) pcx[s] = (uint32_t)(((2 * s + h) ^ sw) << 4);
-  const uint32_t prow = (uint32_t)((64 * wj + l32) * 128);
+  uint32_t prowm[2];  // dY operand ms: rows 64 wj + 32 (ms ^ wi) .. + 31, as the forward
+#pragma unroll
+  for (int ms = 0; ms < 2; ++ms) prowm[ms] = (uint32_t)((64 * wj + 32 * (ms ^ wi) + l32) * 128);
   const int gc = l32 & 15, half = l32 >> 4, nlo = gc >> 2;
   uint32_t qtr[2];
 #pragma unroll
@@ -1172,7 +1229,7 @@ __global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
   auto load_frags = [&](uint32_t st, uint32_t bs, int s, u32x4 (&wf)[2], u32x4 (&xf)[2],
                         u32x4 (&bf)[RQ]) {
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) xf[ms] = read16(st + kQWT + prow + ms * 32 * 128 + pcx[s]);
+    for (int ms = 0; ms < 2; ++ms) xf[ms] = read16(st + kQWT + prowm[ms] + pcx[s]);
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
       const uint32_t a = st + (uint32_t)(16 * s * 256) + qtr[ns];
@@ -1209,7 +1266,7 @@ __global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
   __syncthreads();
   {
     const u32x2 cw = codes_at(0, 0);
-    const PermTable pt = perm_table(p.tab, scale_of(raw_at(0, 0)));
+    const PermTable pt = perm_table_quad(cbq, scale_of(raw_at(0, 0)));
 #pragma unroll
     for (int d = 0; d < 2; ++d) write16(sbase + wdst[d], perm_deq8(cw[d], pt));
   }
@@ -1246,14 +1303,13 @@ __global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
     for (int s = 0; s < 4; ++s) {
       const int c = s & 1;
       if (s < 3) load_frags(st, bs, s + 1, wf[c ^ 1], xf[c ^ 1], bf[c ^ 1]);
-      if (s == 0) pt = perm_table(p.tab, scale_of(raw));
+      if (s == 0) pt = perm_table_quad(cbq, scale_of(raw));
 #pragma unroll
       for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf[c][ms], acc[ns][ms]);
-      const u32x4 xt = wi ? xf[c][1] : xf[c][0];
 #pragma unroll
-      for (int q = 0; q < RQ; ++q) uacc[q] = mfma32(bf[c][q], xt, uacc[q]);
+      for (int q = 0; q < RQ; ++q) uacc[q] = mfma32(bf[c][q], xf[c][0], uacc[q]);
       if (s == 1 || s == 2) write16(wt + wdst[s - 1], perm_deq8(cw[s - 1], pt));
       if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6 + 2 * RQ, 0);
       if (s == 0) {
@@ -1339,7 +1395,7 @@ __global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
     }
 #pragma unroll
     for (int ms = 0; ms < 2; ++ms)
-      vf[ms] = read16(tl + (uint32_t)((64 * wj + 32 * ms + l32) * 128 + 2 * jr));
+      vf[ms] = read16(tl + (uint32_t)((64 * wj + 32 * (ms ^ wi) + l32) * 128 + 2 * jr));
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
@@ -1351,7 +1407,7 @@ __global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
   __syncthreads();
 #pragma unroll
   for (int ms = 0; ms < 2; ++ms) {
-    const int j = 64 * wj + 32 * ms + l32;
+    const int j = 64 * wj + 32 * (ms ^ wi) + l32;
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
