@@ -886,8 +886,24 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
   // code group, the MFMAs of step kt with the dequantisation of step kt + 1
   // (level table, then one code word in each of the next two substeps) into
   // the other weight tile scheduled between them; at the end, wait for
-  // everything but the code group loads issued in this step.  Unrolled by
-  // eight so that every LDS address is a base plus an immediate.
+  // everything but the code group loads issued in this step.  The MFMAs of a
+  // step's last substep run after the barrier, behind the first LDS reads of
+  // the next step, whose latency they cover (their operands are already in
+  // registers; the first step's are zeros).  Unrolled by eight so that every
+  // LDS address is a base plus an immediate.
+  u32x4 pw[2], px[2], pa[RQ];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) pw[i] = px[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) pa[q] = u32x4{0u, 0u, 0u, 0u};
+  auto pending = [&]() {
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(pw[ns], px[ms], acc[ns][ms]);
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) tacc[q] = mfma32(pa[q], px[0], tacc[q]);
+  };
   auto step = [&](int kt, auto jj) {
     constexpr int J = decltype(jj)::value;
     constexpr int B = J & 1, POS = J & 3, BUF = J >> 2;
@@ -910,18 +926,30 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
     const u32x2 cw = codes_at(NBUF, NPOS);
     const uint32_t raw = raw_at(NBUF, NPOS);
     __builtin_amdgcn_sched_barrier(0);
+    pending();  // the previous step's last substep
+    __builtin_amdgcn_sched_barrier(0);
     PermTable pt;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c = s & 1;
       if (s < 3) load_frags(st, as, s + 1, wf[c ^ 1], xf[c ^ 1], af[c ^ 1]);
       if (s == 0) pt = perm_table_quad(cbq, scale_of(raw, NPOS, kt + 1));
+      if (s < 3) {
 #pragma unroll
-      for (int ns = 0; ns < 2; ++ns)
+        for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf[c][ms], acc[ns][ms]);
+          for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf[c][ms], acc[ns][ms]);
 #pragma unroll
-      for (int q = 0; q < RQ; ++q) tacc[q] = mfma32(af[c][q], xf[c][0], tacc[q]);
+        for (int q = 0; q < RQ; ++q) tacc[q] = mfma32(af[c][q], xf[c][0], tacc[q]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          pw[i] = wf[c][i];
+          px[i] = xf[c][i];
+        }
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) pa[q] = af[c][q];
+      }
       if (s == 1 || s == 2) write16(wt + wdst[s - 1], perm_deq8(cw[s - 1], pt));
       // the next substep's reads first, then each MFMA followed by a share of
       // the dequantisation, then the store of the dequantised word
@@ -973,6 +1001,7 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
     step(kt + 2, I2{});
     step(kt + 3, I3{});
   }
+  pending();  // the last step's last substep
 
   // ---- T: lane (l32, h) of wave (wi, wj) holds T[m][32 q + 8 v + 4 h + e]
   // in tacc[q][4 v + e], m = 64 wj + 32 wi + l32 of the tile.  The column
@@ -1277,6 +1306,20 @@ __global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
   // loads of group kt / 2 + 2 into this step's (now free) code buffer; the
   // MFMAs of step kt with the dequantisation of step kt + 1 between them; at
   // the end, wait for everything but the group loads issued in this step.
+  // As in the forward, a step's last substep of MFMAs runs after the barrier.
+  u32x4 pw[2], px[2], pb[RQ];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) pw[i] = px[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) pb[q] = u32x4{0u, 0u, 0u, 0u};
+  auto pending = [&]() {
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+      for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(pw[ns], px[ms], acc[ns][ms]);
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) uacc[q] = mfma32(pb[q], px[0], uacc[q]);
+  };
   auto step = [&](int kt, auto jj) {
     constexpr int J = decltype(jj)::value;
     constexpr int B = J & 1, POS = J & 1, BUF = J >> 1;
@@ -1298,18 +1341,30 @@ __global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
     const u32x2 cw = codes_at(NBUF, NPOS);
     const u32x2 raw = raw_at(NBUF, NPOS);
     __builtin_amdgcn_sched_barrier(0);
+    pending();  // the previous step's last substep
+    __builtin_amdgcn_sched_barrier(0);
     PermTable pt;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int c = s & 1;
       if (s < 3) load_frags(st, bs, s + 1, wf[c ^ 1], xf[c ^ 1], bf[c ^ 1]);
       if (s == 0) pt = perm_table_quad(cbq, scale_of(raw));
+      if (s < 3) {
 #pragma unroll
-      for (int ns = 0; ns < 2; ++ns)
+        for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf[c][ms], acc[ns][ms]);
+          for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf[c][ms], acc[ns][ms]);
 #pragma unroll
-      for (int q = 0; q < RQ; ++q) uacc[q] = mfma32(bf[c][q], xf[c][0], uacc[q]);
+        for (int q = 0; q < RQ; ++q) uacc[q] = mfma32(bf[c][q], xf[c][0], uacc[q]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          pw[i] = wf[c][i];
+          px[i] = xf[c][i];
+        }
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) pb[q] = bf[c][q];
+      }
       if (s == 1 || s == 2) write16(wt + wdst[s - 1], perm_deq8(cw[s - 1], pt));
       if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6 + 2 * RQ, 0);
       if (s == 0) {
@@ -1349,6 +1404,7 @@ __global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
     step(kt, I0{});
     step(kt + 1, I1{});
   }
+  pending();  // the last step's last substep
 
   // ---- U as T in the forward: column tile 0 stores it, bf16(s U) (zero
   // past r) goes through LDS to the waves of the expand
