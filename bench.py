@@ -30,7 +30,7 @@ Default run (python bench.py [--steps K] [--warmup W]):
 * cpu_baseline: the CPU oracle (float64 NumPy) on the same step.
 * secondary lines in the same JSON object: NF4 decode (M = 1, 4, 16) GB/s on
   the weight stream with cold weights, merge, quantise, multi-adapter, the
-  forwards of 32 and 64 rows (16-row decode chunks), the step with LoRA-input
+  forwards of 32 and 64 rows (the weight streamed once), the step with LoRA-input
   dropout and as DoRA, the AdamW step, the plain bf16
   GEMMs of the product kernel's shape through torch (context), and forward +
   backward of config 2 (q and v, bf16, M = 4096, r = 8) and of config 4 (the
@@ -354,7 +354,7 @@ def secondary(S, torch, dec=None):
     lq = S["lq"]
     res = {}
     res["decode_nf4"] = dec if dec is not None else decode_bench(S, torch)
-    # forwards of 32 and 64 rows (16-row decode chunks), graph-launched, warm weights
+    # forwards of 32 and 64 rows (the weight-streaming kernel), graph-launched, warm weights
     from qlora_parameter_efficient_amd import workloads as wlc
     chunks = {}
     for m in (32, 64):
@@ -366,7 +366,7 @@ def secondary(S, torch, dec=None):
         t = graph_time(lambda: lq.lq_lora_fwd(Xm, S["W"], S["A"], S["B"], S["s"], ws=wsm, Y=Ym),
                        torch)
         chunks[f"M{m}"] = {"us_per_call_graph": round(t * 1e3, 2)}
-    res["forward_nf4_decode_chunks"] = chunks
+    res["forward_nf4_small_rows"] = chunks
     # one-time ops, HBM-bound: GPU time per call from graph-captured sequences
     Wm = torch.empty((N, K), dtype=torch.bfloat16, device=S["dev"])
     t = graph_time(lambda: lq.lq_lora_merge(S["W"], S["A"], S["B"], S["s"],

@@ -368,11 +368,20 @@ size_t lq_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int64_t r,
   if (M < 0 || N < 0 || K < 0 || r < 0) return 0;
   switch (op) {
     case LQ_OP_FWD: {  // the decode path's partial sums of T, or float32 T
+      // 17 to 64 rows of an NF4 weight in whole pieces: the weight-streaming
+      // kernel's partial sums (the largest of the sizes those rows can use)
+      const size_t sf = (M > kDecodeMaxM && M <= 64 && N % 128 == 0 && K % 512 == 0)
+                            ? dispatch::small_fwd_ws_bytes(M, N, K, r)
+                            : 0;
       // up to chunk_max_m rows (either format) never the large-tile path
-      if (M <= kDecodeMaxM || M <= chunk_max_m(N, true)) return decode_bytes(M, N, K, r);
+      if (M <= kDecodeMaxM || M <= chunk_max_m(N, true)) {
+        const size_t d = decode_bytes(M, N, K, r);
+        return sf > d ? sf : d;
+      }
       const size_t base = M <= kDecodeChunkMaxM ? decode_bytes(M, N, K, r) : (size_t)(M * r) * 4;
       const size_t big = fwd_big_bytes(M, N, K, r);
-      return big > base ? big : base;
+      const size_t mx = big > base ? big : base;
+      return sf > mx ? sf : mx;
     }
     case LQ_OP_BWD: {
       const size_t big = bwd_big_bytes(M, N, K);
@@ -472,6 +481,11 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
     return f32_lora_fwd((const float*)X, M, *W0, (const float*)A, (const float*)B, r, scale,
                         (float*)Y, T, stream);
   }
+  // 17 to 64 rows of an NF4 weight, given the LQ_OP_FWD workspace: the
+  // weight-streaming kernel (the weight read once, not once per 16 rows)
+  if (M > kDecodeMaxM && dispatch::small_fwd_eligible(*W0, M, r) && ws &&
+      ws_bytes >= dispatch::small_fwd_ws_bytes(M, W0->N, W0->K, r))
+    return dispatch::small_fwd(X, M, *W0, A, B, r, scale, Y, T_out, ws, stream);
   const size_t big = fwd_big_bytes(M, W0->N, W0->K, r);
   const bool big_ok = big && ws && ws_bytes >= big;
   if (M <= kDecodeMaxM ||

@@ -130,6 +130,15 @@ bool small_dx_eligible(const lq_weight& W, int64_t M, int64_t r);
 size_t small_dx_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 int small_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B,
              int64_t r, float s, float* U, void* dX, void* ws, hipStream_t st);
+// Forward for 16 < M <= 64 rows with an NF4 weight (N % 128 == 0, K % 512
+// == 0, r <= 64): the weight streamed once by (128-row, 512-column) pieces,
+// float32 partial sums of X Wd^T and of T per column range in ws
+// (small_fwd_ws_bytes), added in a second launch that applies the expand and
+// writes T (M x r float32, when T_out is not NULL).
+bool small_fwd_eligible(const lq_weight& W, int64_t M, int64_t r);
+size_t small_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+int small_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
+              int64_t r, float s, void* Y, float* T_out, void* ws, hipStream_t st);
 // U (M x r float32) is written as well, times uscale: the expand needs it.
 int big_dx(const void* dY, int64_t M, const lq_weight& W, const void* A, const void* B, int64_t r,
            float s, void* dX, float* U, void* ws, hipStream_t st, float uscale = 1.0f);

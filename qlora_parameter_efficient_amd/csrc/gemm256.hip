@@ -615,87 +615,6 @@ struct Q256Params {
   NF4Table tab;
 };
 
-// Per-block level table in registers: the 16 bf16 results t_i =
-// RNE(fl32(cb[i] a')) of one NF4 block, as byte planes (lo[k] holds the low
-// bytes of t_4k .. t_4k+3, hi[k] the high bytes), so that one v_perm_b32
-// looks up four codes at once.
-struct PermTable {
-  uint32_t lo[4], hi[4];
-};
-
-__device__ __forceinline__ PermTable perm_table(const NF4Table& tab, float a) {
-  uint32_t pr[8];  // bf16 pairs (t_2k, t_2k+1)
-#pragma unroll
-  for (int k = 0; k < 8; ++k) pr[k] = pack_bf16x2(tab.cb[2 * k] * a, tab.cb[2 * k + 1] * a);
-  PermTable t;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    // bytes 0, 2 of pr[2k] and of pr[2k + 1]; bytes 1, 3 for the high plane
-    t.lo[k] = __builtin_amdgcn_perm(pr[2 * k + 1], pr[2 * k], 0x06040200u);
-    t.hi[k] = __builtin_amdgcn_perm(pr[2 * k + 1], pr[2 * k], 0x07050301u);
-  }
-  return t;
-}
-
-// The same table built by the four lanes of a quad that share the block: lane
-// q of the quad forms t_4q .. t_4q+3 from its four levels cbq = cb[4q ..
-// 4q + 3] (same products and rounding, so the same bits), and the eight bf16
-// pairs are gathered with quad broadcasts: 4 multiplies, 2 conversions and 8
-// moves per lane instead of 16 multiplies and 8 conversions.
-__device__ __forceinline__ PermTable perm_table_quad(const float (&cbq)[4], float a) {
-  const int p0 = (int)pack_bf16x2(cbq[0] * a, cbq[1] * a);
-  const int p1 = (int)pack_bf16x2(cbq[2] * a, cbq[3] * a);
-  uint32_t pr[8];  // bf16 pairs (t_2k, t_2k+1)
-  pr[0] = (uint32_t)__builtin_amdgcn_mov_dpp(p0, 0x00, 0xF, 0xF, false);
-  pr[1] = (uint32_t)__builtin_amdgcn_mov_dpp(p1, 0x00, 0xF, 0xF, false);
-  pr[2] = (uint32_t)__builtin_amdgcn_mov_dpp(p0, 0x55, 0xF, 0xF, false);
-  pr[3] = (uint32_t)__builtin_amdgcn_mov_dpp(p1, 0x55, 0xF, 0xF, false);
-  pr[4] = (uint32_t)__builtin_amdgcn_mov_dpp(p0, 0xAA, 0xF, 0xF, false);
-  pr[5] = (uint32_t)__builtin_amdgcn_mov_dpp(p1, 0xAA, 0xF, 0xF, false);
-  pr[6] = (uint32_t)__builtin_amdgcn_mov_dpp(p0, 0xFF, 0xF, 0xF, false);
-  pr[7] = (uint32_t)__builtin_amdgcn_mov_dpp(p1, 0xFF, 0xF, 0xF, false);
-  PermTable t;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    t.lo[k] = __builtin_amdgcn_perm(pr[2 * k + 1], pr[2 * k], 0x06040200u);
-    t.hi[k] = __builtin_amdgcn_perm(pr[2 * k + 1], pr[2 * k], 0x07050301u);
-  }
-  return t;
-}
-
-// the four levels cb[4q .. 4q + 3] of quad lane q = lane & 3
-__device__ __forceinline__ void quad_levels(const NF4Table& tab, int lane, float (&cbq)[4]) {
-  const int q = lane & 3;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    cbq[i] = q == 0 ? tab.cb[i] : q == 1 ? tab.cb[4 + i] : q == 2 ? tab.cb[8 + i] : tab.cb[12 + i];
-}
-
-// one byte plane for four codes (one per byte of c, values 0..15): the byte
-// of t_code for each
-__device__ __forceinline__ uint32_t perm_plane(const uint32_t (&pl)[4], uint32_t c7, uint32_t s2) {
-  const uint32_t a = __builtin_amdgcn_perm(pl[1], pl[0], c7);  // codes 0..7
-  const uint32_t b = __builtin_amdgcn_perm(pl[3], pl[2], c7);  // codes 8..15
-  return __builtin_amdgcn_perm(b, a, s2);                       // by bit 3 of each code
-}
-
-// Eight codes (element e in bits 4e .. 4e + 3) -> the eight bf16 values t_code
-// in natural element order (bit-identical to deq8 with the same a')
-__device__ __forceinline__ u32x4 perm_deq8(uint32_t w, const PermTable& t) {
-  const uint32_t ce = w & 0x0F0F0F0Fu, co = (w >> 4) & 0x0F0F0F0Fu;  // elements 0,2,4,6 / 1,3,5,7
-  const uint32_t ce7 = ce & 0x07070707u, co7 = co & 0x07070707u;
-  const uint32_t es2 = ((ce >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t os2 = ((co >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t le = perm_plane(t.lo, ce7, es2), he = perm_plane(t.hi, ce7, es2);
-  const uint32_t lo = perm_plane(t.lo, co7, os2), ho = perm_plane(t.hi, co7, os2);
-  const uint32_t x01 = __builtin_amdgcn_perm(he, le, 0x05010400u);  // (e0, e2)
-  const uint32_t x23 = __builtin_amdgcn_perm(he, le, 0x07030602u);  // (e4, e6)
-  const uint32_t y01 = __builtin_amdgcn_perm(ho, lo, 0x05010400u);  // (e1, e3)
-  const uint32_t y23 = __builtin_amdgcn_perm(ho, lo, 0x07030602u);  // (e5, e7)
-  return u32x4{__builtin_amdgcn_perm(y01, x01, 0x05040100u), __builtin_amdgcn_perm(y01, x01, 0x07060302u),
-               __builtin_amdgcn_perm(y23, x23, 0x05040100u), __builtin_amdgcn_perm(y23, x23, 0x07060302u)};
-}
-
 __device__ __forceinline__ void write16(uint32_t addr, const u32x4& v) {
   typedef __attribute__((address_space(3))) u32x4* lds_ptr;
   *(lds_ptr)(uintptr_t)addr = v;

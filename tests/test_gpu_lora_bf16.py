@@ -212,6 +212,27 @@ def test_small_rows_nf4_dx(M):
     check_gpu(c, Wd, oracle_ref(c, Wo), label="small-rows-dx single-level")
 
 
+@pytest.mark.parametrize("M", [17, 32, 33, 64])
+def test_small_rows_nf4_fwd(M):
+    """Forward of 17 to 64 rows with an NF4 weight and the default workspace:
+    the weight-streaming kernel (128-row x 512-column pieces, each code read
+    and dequantised once, partial sums per column range added in order by a
+    second launch that applies the expand and writes T).  The config-3 weight
+    at 4096^2 (8 column ranges); 1024 x 1536 at rank 40 (two 32-rank blocks of
+    T partial sums, three column ranges); 384 x 1024 at rank 5 with
+    single-level constants."""
+    c = wl.config3(M=M)
+    check_layer(c, "nf4", bwd=False, merge=False, label="small-rows-fwd config3")
+    c = wl.small_case(M, 1024, 1536, 40, seed=700 + M)
+    check_layer(c, "nf4", bwd=False, merge=False, label="small-rows-fwd r40")
+    c = wl.small_case(M, 384, 1024, 5, seed=800 + M)
+    Wd = lq.lq_nf4_quantize(to_dev(c["W0"]), double_quant=False)
+    W0v = c["W0"].value
+    Wo = onf4.bf16_bits_to_f64(onf4.nf4_dequantize_bf16(
+        onf4.nf4_quantize(W0v, double_quant=False))).reshape(W0v.shape)
+    check_gpu(c, Wd, oracle_ref(c, Wo, bwd=False), label="small-rows-fwd single-level r5")
+
+
 @pytest.mark.parametrize("kind", ["dense", "nf4"])
 @pytest.mark.parametrize("M", [1, 16, 96])
 def test_decode_rank64(M, kind):
