@@ -1031,10 +1031,13 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
 //     step (one block: the same byte-plane table and v_perm_b32 lookups as
 //     the forward), between the current step's MFMAs, and stores them into
 //     the other stage's weight tile in storage order (row n of 256 bytes,
-//     16-byte chunk c at c ^ 4 (n & 3));
+//     16-byte chunk c at c ^ 4 (n & 3) ^ (n >> 2 & 1));
 //   * the weight operand (one output column, eight consecutive n) is read
 //     with the transposing ds_read_b64_tr_b16; with the swizzle above the 32
-//     lanes of a read touch 16 distinct 16-byte bank groups;
+//     lanes of a read touch 16 distinct 16-byte bank groups, and so do the
+//     16 lanes of each quarter of a dequantising store (8 rows x 8 chunks per
+//     instruction: the low bit of the swizzle puts rows n and n + 4 on
+//     opposite halves of the bank groups);
 //   * U: the waves holding the same 64 dY rows split them as in the forward;
 //     the B operand (one rank, eight consecutive n) is read from the step's
 //     rows of B with the same transposing read (ranks past r read
@@ -1154,7 +1157,8 @@ __global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
   uint32_t wdst[2];
 #pragma unroll
   for (int d = 0; d < 2; ++d)
-    wdst[d] = (uint32_t)(dx_row * 256 + (((2 * dx_j + d) ^ (4 * (dx_row & 3))) << 4));
+    wdst[d] = (uint32_t)(dx_row * 256 +
+                         (((2 * dx_j + d) ^ (4 * (dx_row & 3)) ^ ((dx_row >> 2) & 1)) << 4));
 
   // operand reads: dY as the forward's activations; the weight and B
   // operands transposed (lane group of 16: rows nlo = gc / 4 and nlo + 4,
@@ -1167,11 +1171,14 @@ __global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
 #pragma unroll
   for (int ms = 0; ms < 2; ++ms) prowm[ms] = (uint32_t)((64 * wj + 32 * (ms ^ wi) + l32) * 128);
   const int gc = l32 & 15, half = l32 >> 4, nlo = gc >> 2;
-  uint32_t qtr[2];
+  // rows 16 s + 8 h + nlo (swizzle bit 0 clear) and those + 4 (bit 0 set)
+  uint32_t qtr[2], qtrh[2];
 #pragma unroll
   for (int ns = 0; ns < 2; ++ns) {
     const int col = 64 * wi + 32 * ns + 16 * half + 4 * (gc & 3);
-    qtr[ns] = (uint32_t)((8 * h + nlo) * 256 + (((col >> 3) ^ (4 * nlo)) << 4) + (col & 7) * 2);
+    const int pc = (col >> 3) ^ (4 * nlo);
+    qtr[ns] = (uint32_t)((8 * h + nlo) * 256 + (pc << 4) + (col & 7) * 2);
+    qtrh[ns] = (uint32_t)((8 * h + nlo + 4) * 256 + ((pc ^ 1) << 4) + (col & 7) * 2);
   }
   const uint32_t btr = (uint32_t)((8 * h + nlo) * 2 * r + 2 * (16 * half + 4 * (gc & 3)));
   auto load_frags = [&](uint32_t st, uint32_t bs, int s, u32x4 (&wf)[2], u32x4 (&xf)[2],
@@ -1180,8 +1187,8 @@ __global__ __launch_bounds__(kQThreads) void q256_dx_kernel(Q256DxParams p) {
     for (int ms = 0; ms < 2; ++ms) xf[ms] = read16(st + kQWT + prowm[ms] + pcx[s]);
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
-      const uint32_t a = st + (uint32_t)(16 * s * 256) + qtr[ns];
-      const u32x2 lo = read_tr(a), hi = read_tr(a + 4 * 256);
+      const uint32_t a = st + (uint32_t)(16 * s * 256);
+      const u32x2 lo = read_tr(a + qtr[ns]), hi = read_tr(a + qtrh[ns]);
       wf[ns] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
 #pragma unroll

@@ -162,6 +162,9 @@ KLOOP = [
     (2100, 2816, 2816, 40),
     (2100, 2816, 2816, 8),
     (2100, 2816, 2816, 5),
+    (1024, 128, 6144, 16),   # dX in the K loop with one code group (N = 128, two steps)
+    (1000, 256, 6144, 64),   # dX with two code groups, rank 64, ragged M
+    (1536, 24576, 256, 24),  # forward in the K loop with one code group (K = 256), rank 24
 ]
 
 
