@@ -498,8 +498,10 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
   }
   // an NF4 weight with enough 128 x 256 tiles: the product that dequantises
   // in its K loop and forms T in the same loop (no bf16 copy of W0, no
-  // workspace), whatever workspace was given
-  if (dispatch::inloop_fwd_eligible(*W0, M))
+  // workspace) -- unless the copy's workspace was given and the large-tile
+  // product would run 256 x 256 tiles, where it is the faster of the two
+  if (dispatch::inloop_fwd_eligible(*W0, M) &&
+      !(big_ok && dispatch::big_wide_tiles(M, W0->N)))
     return dispatch::inloop_fwd(X, M, *W0, A, B, r, scale, Y, T_out, stream);
   if (big_ok) return dispatch::big_fwd(X, M, *W0, A, B, r, scale, Y, T_out, ws, stream);
   return dispatch::bf16_fwd(X, M, *W0, A, B, r, scale, Y, T_out, stream);

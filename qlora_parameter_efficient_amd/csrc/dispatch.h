@@ -89,6 +89,11 @@ int launch_shrink(const void* Z, int64_t M, int64_t K, const void* G, bool gt, i
 // 256 x 256-tile product with the rank-r expand fused.  Eligible when the
 // product's output width is a multiple of 256 and there are enough rows.
 bool big_fwd_eligible(int64_t M, int64_t N, int64_t K);
+// The large-tile product would use 256 x 256 tiles (enough of them to fill
+// the chip): there it outruns the K-loop NF4 products even with the copy of
+// W0 (a Llama-2-7B block at M = 8192, r = 64: 862 against 668 TFLOP/s), so
+// an NF4 call given the copy's workspace takes it.
+bool big_wide_tiles(int64_t M, int64_t NI);
 bool big_dx_eligible(int64_t M, int64_t N, int64_t K);
 size_t big_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 size_t big_dx_ws_bytes(int64_t M, int64_t N, int64_t K);

@@ -1625,6 +1625,7 @@ int bf16_weight(const lq_weight& W, void* q, hipStream_t st) {
 }  // namespace
 
 bool big_fwd_eligible(int64_t M, int64_t N, int64_t K) { return g256_fits(M, N, K); }
+bool big_wide_tiles(int64_t M, int64_t NI) { return g256_plan(M, NI).jm == 4; }
 bool big_dx_eligible(int64_t M, int64_t N, int64_t K) { return g256_fits(M, K, N); }
 
 // [g256: header, flags, split-K slots] [T when T_out is NULL] [bf16 W0]

@@ -385,13 +385,15 @@ int bf16_bwd(const void* dY, const void* X, int64_t M, const lq_weight& W, const
     return launch_zero_f32(dB, N * r, st);
   }
   // dX (and U = dY B on the way): for an NF4 weight at large M by the
-  // product that dequantises in its K loop (no workspace); by the large-tile
-  // path when it has its workspace (for an NF4 weight and at most 64 rows, by
-  // the weight-streaming kernel, its partial sums in that workspace), else by
-  // the fused kernel
+  // product that dequantises in its K loop (no workspace), unless the
+  // large-tile path has its workspace and would run 256 x 256 tiles; by the
+  // large-tile path when it has its workspace (for an NF4 weight and at most
+  // 64 rows, by the weight-streaming kernel, its partial sums in that
+  // workspace), else by the fused kernel
   auto run_dx = [&](float* Uo) {
     if (big_ws && small_dx_eligible(W, M, r)) return small_dx(dY, M, W, A, B, r, s, U, dX, big_ws, st);
-    if (inloop_dx_eligible(W, M, r)) return inloop_dx(dY, M, W, A, B, r, s, dX, Uo, st);
+    if (inloop_dx_eligible(W, M, r) && !(big_ws && big_wide_tiles(M, W.K)))
+      return inloop_dx(dY, M, W, A, B, r, s, dX, Uo, st);
     return big_ws ? big_dx(dY, M, W, A, B, r, s, dX, U, big_ws, st)
                   : bf16_dx(dY, M, W, A, B, r, s, dX, Uo, st);
   };
