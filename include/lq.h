@@ -180,29 +180,34 @@ int lq_nf4_dequantize(const uint8_t* codes, const uint8_t* q8, const float* c2,
  *   ws / ws_bytes: device workspace (caller-owned, contents not preserved).
  *   lq_workspace_size(LQ_OP_FWD, M, N, K, r, 0) bytes select the fastest
  *   path; lq_workspace_size(LQ_OP_FWD_FUSED, ...) is the smallest workspace
- *   that works.  The decode path (dt = LQ_BF16, M <= 96) needs no workspace
- *   up to 16 rows (one launch; T is formed inside it); 17 to 96 rows run as
- *   16-row chunks and need 8 M' r floats of partial sums of T (M' = M rounded
- *   up to a multiple of 16).  With the LQ_OP_FWD workspace and N > 4096 the
- *   chunks stop at 32 rows for an NF4 W0 and at 16 for a bf16 one (the
- *   large-tile path is faster past those).  The float32 path needs M r floats of T when
- *   T_out is NULL; otherwise ws may be NULL.
+ *   that works.  The float32 path needs M r floats of T when T_out is NULL;
+ *   otherwise ws may be NULL.
  *   dt = LQ_BF16: bf16 inputs, float32 accumulation, bf16 RNE output; W0 dense
- *   bf16 or NF4.  Past the decode rows, the path follows the workspace:
+ *   bf16 or NF4.  Paths:
+ *     - M <= 16 (decode, memory-bound): one launch, T formed inside it, no
+ *       workspace;
+ *     - 16 < M <= 64, NF4 W0 with N % 128 == 0 and K % 512 == 0, and at least
+ *       the LQ_OP_FWD size: the weight streamed once in (128-row, 512-column)
+ *       pieces, float32 partial sums (K/512 M (N + r) floats) in ws, added
+ *       in order by a second launch;
+ *     - other forwards of up to 96 rows: 16-row chunks, 8 M' r floats of
+ *       partial sums of T (M' = M rounded up to a multiple of 16), each chunk
+ *       streaming W0 once; with the LQ_OP_FWD workspace and N > 4096 the
+ *       chunks stop at 32 rows for an NF4 W0 and at 16 for a bf16 one;
+ *     - NF4 W0 with N % 128 == 0, K % 256 == 0 and at least 192 tiles of
+ *       128 x 256: one launch that dequantises the codes inside the product's
+ *       K loop and forms T there too (no workspace, no dense W0), unless ws
+ *       holds the LQ_OP_FWD size and the large-tile product would run
+ *       256 x 256 tiles (M > 2816 at N = 4096), where the next case is faster;
  *     - at least the LQ_OP_FWD size, N % 256 == 0: the large-tile path; an
  *       NF4 W0 is first dequantised (bit-exactly, as lq_nf4_dequantize) to a
- *       bf16 copy inside ws, then multiplied (fastest);
- *     - at least M r floats (the LQ_OP_FWD_FUSED size), NF4 W0 with
- *       N % 128 == 0, K % 256 == 0 and at least 192 tiles of 128 x 256: T
- *       into T_out (or ws), then a product that dequantises the codes inside
- *       its K loop; no dense W0 is ever written;
+ *       transient bf16 copy inside ws, then multiplied;
  *     - otherwise the fused kernels (T in the same K loop, NF4 dequantised in
  *       registers / LDS, no dense W0 either).
- *   All three give "dequantise, then multiply in bf16" with identical
- *   dequantised values.
+ *   All give "dequantise, then multiply in bf16" with identical dequantised
+ *   values.
  *   Requires K % 64 == 0, N % 64 == 0, N, K <= 65536, M*K and M*N < 2^31,
- *   1 <= r <= 64.  M <= 96 takes the memory-bound decode path, 16 rows at a
- *   time (each chunk streams W0 once).
+ *   1 <= r <= 64.
  *   dt = LQ_F32: float32 throughout (W0 dense f32 or NF4), 1 <= r <= 64.
  * M = 0 is a no-op returning LQ_OK.
  */
@@ -225,9 +230,14 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A,
  *   accumulate = 1 adds into dA and dB (gradient accumulation over
  *   micro-batches); 0 overwrites them.
  *   ws / ws_bytes: device workspace of at least
- *   lq_workspace_size(LQ_OP_BWD_FUSED, M, N, K, r, 0) bytes (caller-owned);
- *   with lq_workspace_size(LQ_OP_BWD, ...) bytes and K % 256 == 0, dX takes
- *   the large-tile path (bf16 copy of W0 in ws).
+ *   lq_workspace_size(LQ_OP_BWD_FUSED, M, N, K, r, 0) bytes (caller-owned).
+ *   dX of an NF4 W0 with K % 256 == 0, N % 128 == 0, r % 8 == 0 and at least
+ *   192 tiles of 128 x 256 runs one launch that dequantises the codes inside
+ *   its K loop and forms U = dY B there too; with lq_workspace_size(LQ_OP_BWD,
+ *   ...) bytes it runs instead, for an NF4 W0 and at most 64 rows, a
+ *   weight-streaming kernel, and where the large-tile product would run
+ *   256 x 256 tiles (or the weight is dense), the large-tile path (a bf16
+ *   copy of an NF4 W0 in ws).
  * Same shape rules as lq_lora_fwd.
  */
 int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0,
@@ -246,8 +256,8 @@ int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0,
  * routine); its first call on a device looks up that device's address of the
  * array once.  A backward whose smallest workspace (the LQ_OP_BWD_FUSED size)
  * exceeds LQ_NOALLOC_SCRATCH_BYTES returns LQ_ERR_WORKSPACE before any
- * launch; where the LQ_OP_BWD size fits as well, dX takes the large-tile
- * path.  All calls on one GPU share the array: calls that overlap in time on
+ * launch; where the LQ_OP_BWD size fits as well, dX takes the path that
+ * size selects.  All calls on one GPU share the array: calls that overlap in time on
  * one GPU (several streams, several host threads) race and must be ordered
  * by the caller.  Timing (lq_timing_enable) must be off.
  */
@@ -467,8 +477,9 @@ int lq_check_segments(const int32_t* h_offsets, const int32_t* h_adapter,
 
 /* Workspace sizes (bytes) for the ops that need one.  LQ_OP_FWD, LQ_OP_BWD
  * and LQ_OP_FWD_MULTI: the size that lets the call take its fastest path
- * (at large M the large-tile path, whose part holds the bf16 copy of W0 and
- * the split-K slots); LQ_OP_FWD_FUSED, LQ_OP_BWD_FUSED and
+ * (it holds the large-tile path's part, the bf16 copy of W0 and the split-K
+ * slots, and the weight-streaming kernels' partial sums, whichever the shape
+ * can use); LQ_OP_FWD_FUSED, LQ_OP_BWD_FUSED and
  * LQ_OP_FWD_MULTI_FUSED: the smallest size each call accepts, with which the
  * fused kernels run.  LQ_OP_{FWD,BWD}_DROPOUT and LQ_OP_DORA_{FWD,BWD} and
  * their _FUSED forms: the same pair for the dropout and DoRA entry points
