@@ -620,8 +620,14 @@ __device__ __forceinline__ void write16(uint32_t addr, const u32x4& v) {
   *(lds_ptr)(uintptr_t)addr = v;
 }
 
-// RQ: 32-rank blocks of the shrink (1 for r <= 32, 2 for r <= 64)
-template <int WK, bool FP8, int RQ>
+// RQ: 32-rank blocks of the shrink (1 for r <= 32, 2 for r <= 64).  T16 (r <=
+// 16): the shrink runs as one 16 x 16 x 32 MFMA per 16 rows and pair of
+// substeps instead of one 32 x 32 x 16 per substep (half the MFMA cycles and
+// half the A reads): its activation operand (16 rows x 32 reduction elements,
+// four 8-element pieces) is the wave's first activation operands of the two
+// substeps with their 16-lane rows regrouped by v_permlane32_swap and
+// v_permlane16_swap, and its A operand one 16-byte read per pair.
+template <int WK, bool FP8, int RQ, bool T16>
 __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * kQStage];
   __shared__ __attribute__((aligned(1024))) char cst[2 * kQCB];
@@ -764,17 +770,25 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
   for (int ms = 0; ms < 2; ++ms) prowm[ms] = (uint32_t)((64 * wj + 32 * (ms ^ wi) + l32) * 128);
   const uint32_t qrow = (uint32_t)((64 * wi + l32) * 128);
   const uint32_t arow = (uint32_t)(l32 * 128);
+  // T16: lane l reads rank l % 16, 8-element piece l / 16 of the substep pair
+  uint32_t a16[2];
+#pragma unroll
+  for (int w = 0; w < 2; ++w)
+    a16[w] = (uint32_t)((lane & 15) * 128 + (((4 * w + (lane >> 4)) ^ rswz(lane & 15)) << 4));
   auto load_frags = [&](uint32_t st, uint32_t as, int s, u32x4 (&wf)[2], u32x4 (&xf)[2],
                         u32x4 (&af)[RQ]) {
 #pragma unroll
     for (int ms = 0; ms < 2; ++ms) xf[ms] = read16(st + kQWT + prowm[ms] + pcx[s]);
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) wf[ns] = read16(st + qrow + ns * 32 * 128 + pcx[s]);
+    if (!T16) {
 #pragma unroll
-    for (int q = 0; q < RQ; ++q) af[q] = read16(as + arow + q * 32 * 128 + pcx[s]);
+      for (int q = 0; q < RQ; ++q) af[q] = read16(as + arow + q * 32 * 128 + pcx[s]);
+    }
   };
 
-  f32x16 acc[2][2], tacc[RQ];
+  f32x16 acc[2][2], tacc[T16 ? 1 : RQ];
+  f32x4 t16[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -782,9 +796,25 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 #pragma unroll
-  for (int q = 0; q < RQ; ++q)
+  for (int q = 0; q < (T16 ? 1 : RQ); ++q)
 #pragma unroll
     for (int v = 0; v < 16; ++v) tacc[q][v] = 0.0f;
+  // T16: the 16 x 16 x 32 shrink over a substep pair from the first activation
+  // operands x0 (first substep) and x1 (second): 16-lane rows (x0: rows 0-15 h0,
+  // rows 16-31 h0, rows 0-15 h1, rows 16-31 h1) regrouped so that operand lo
+  // holds rows 0-15 and hi rows 16-31, pieces in reduction order
+  auto shrink16 = [&](const u32x4& x0, const u32x4& x1, const u32x4& a) {
+    u32x4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const auto s32 = __builtin_amdgcn_permlane32_swap(x0[e], x1[e], false, false);
+      const auto s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);
+      lo[e] = s16[0];
+      hi[e] = s16[1];
+    }
+    t16[0] = mfma16(a, lo, t16[0]);
+    t16[1] = mfma16(a, hi, t16[1]);
+  };
 
   // prologue: step 0's tiles in stage 0, group 0's codes in code buffer 0
   issue_act(0, 0);
@@ -810,18 +840,23 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
   // the next step, whose latency they cover (their operands are already in
   // registers; the first step's are zeros).  Unrolled by eight so that every
   // LDS address is a base plus an immediate.
-  u32x4 pw[2], px[2], pa[RQ];
+  u32x4 pw[2], px[2], pa[RQ], px2, pa16;
 #pragma unroll
   for (int i = 0; i < 2; ++i) pw[i] = px[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int q = 0; q < RQ; ++q) pa[q] = u32x4{0u, 0u, 0u, 0u};
+  px2 = pa16 = u32x4{0u, 0u, 0u, 0u};
   auto pending = [&]() {
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
       for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(pw[ns], px[ms], acc[ns][ms]);
+    if (T16) {
+      shrink16(px2, px[0], pa16);  // the second substep pair
+    } else {
 #pragma unroll
-    for (int q = 0; q < RQ; ++q) tacc[q] = mfma32(pa[q], px[0], tacc[q]);
+      for (int q = 0; q < RQ; ++q) tacc[q] = mfma32(pa[q], px[0], tacc[q]);
+    }
   };
   auto step = [&](int kt, auto jj) {
     constexpr int J = decltype(jj)::value;
@@ -842,6 +877,11 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
     // dequantisation can be scheduled between the MFMAs)
     u32x4 wf[2][2], xf[2][2], af[2][RQ];
     load_frags(st, as, 0, wf[0], xf[0], af[0]);
+    u32x4 ta16[2], x16[2];
+    if (T16) {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) ta16[w] = read16(as + a16[w]);
+    }
     const u32x2 cw = codes_at(NBUF, NPOS);
     const uint32_t raw = raw_at(NBUF, NPOS);
     __builtin_amdgcn_sched_barrier(0);
@@ -858,8 +898,13 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
         for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
           for (int ms = 0; ms < 2; ++ms) acc[ns][ms] = mfma32(wf[c][ns], xf[c][ms], acc[ns][ms]);
+        if (T16) {
+          if (s == 0 || s == 2) x16[s >> 1] = xf[c][0];
+          if (s == 1) shrink16(x16[0], xf[c][0], ta16[0]);
+        } else {
 #pragma unroll
-        for (int q = 0; q < RQ; ++q) tacc[q] = mfma32(af[c][q], xf[c][0], tacc[q]);
+          for (int q = 0; q < RQ; ++q) tacc[q] = mfma32(af[c][q], xf[c][0], tacc[q]);
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -868,22 +913,35 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
         }
 #pragma unroll
         for (int q = 0; q < RQ; ++q) pa[q] = af[c][q];
+        if (T16) {
+          px2 = x16[1];
+          pa16 = ta16[1];
+        }
       }
       if (s == 1 || s == 2) write16(wt + wdst[s - 1], perm_deq8(cw[s - 1], pt));
       // the next substep's reads first, then each MFMA followed by a share of
-      // the dequantisation, then the store of the dequantised word
-      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 4 + RQ, 0);
+      // the dequantisation (and the lane swaps of the 16-row shrink), then the
+      // store of the dequantised word
+      constexpr int NR = T16 ? 4 : 4 + RQ;  // LDS reads of a substep
+      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
       if (s == 0) {
 #pragma unroll
-        for (int i = 0; i < 4 + RQ; ++i) {
+        for (int i = 0; i < (T16 ? 4 : 4 + RQ); ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 52 / (4 + RQ), 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 52 / (T16 ? 4 : 4 + RQ), 0);
         }
+      } else if (s == 1 && T16) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 40 / 6, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
       } else if (s < 3) {
 #pragma unroll
-        for (int i = 0; i < 4 + RQ; ++i) {
+        for (int i = 0; i < (T16 ? 4 : 4 + RQ); ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 32 / (4 + RQ), 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 32 / (T16 ? 4 : 4 + RQ), 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
       }
@@ -927,8 +985,34 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
   // tile 0 stores it; every tile passes bf16(s T) (zero past r) through LDS
   // (row m, 128 bytes, after the stages' 64 KB of output staging) to the
   // waves of the expand.
+  if (T16) {
+    // lane l holds T[m][4 (l / 16) + e] in t16[q][e], m = 64 wj + 32 wi + 16 q
+    // + l % 16 (ranks past r: garbage rows of the A slice, never used)
+    const int j = 4 * (lane >> 4);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int ml = 64 * wj + 32 * wi + 16 * q + (lane & 15);
+      const int64_t m16 = j0 + ml;
+      if (tile_i == 0 && p.T_out && m16 < M) {
+        float* trow = p.T_out + m16 * r;
+        if (j + 4 <= r && (r & 3) == 0) {
+          *reinterpret_cast<f32x4*>(trow + j) = t16[q];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j + e < r) trow[j + e] = t16[q][e];
+        }
+      }
+      float e4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) e4[e] = j + e < r ? p.s * t16[q][e] : 0.0f;
+      typedef __attribute__((address_space(3))) u32x2* lds_ptr;
+      *(lds_ptr)(uintptr_t)(sbase + 65536 + (uint32_t)(ml * 128 + 2 * j)) =
+          u32x2{pack_bf16x2(e4[0], e4[1]), pack_bf16x2(e4[2], e4[3])};
+    }
+  }
   const int64_t mt = j0 + 64 * wj + 32 * wi + l32;
-  if (tile_i == 0 && p.T_out && mt < M) {
+  if (!T16 && tile_i == 0 && p.T_out && mt < M) {
     float* trow = p.T_out + mt * r;
 #pragma unroll
     for (int q = 0; q < RQ; ++q)
@@ -946,7 +1030,7 @@ __global__ __launch_bounds__(kQThreads) void q256_fwd_kernel(Q256Params p) {
       }
   }
   const uint32_t tl = sbase + 65536;
-  {
+  if (!T16) {
     const uint32_t trow = tl + (uint32_t)((64 * wj + 32 * wi + l32) * 128);
     const float sc = p.s;
 #pragma unroll
@@ -1531,14 +1615,14 @@ bool q256_fwd_fits(const lq_weight& W, int64_t M) {
          (W.N / kQI) * cdiv(M, kQJ) >= 192 && (double)M * W.K * 2 < 4294967296.0;
 }
 
-template <int RQ>
+template <int RQ, bool T16>
 void launch_q256_fmt(const lq_weight& W, const Q256Params& p, unsigned blocks, hipStream_t st) {
   if (W.double_quant == LQ_DQ_FP8)
-    hipLaunchKernelGGL((q256_fwd_kernel<kNF4DQ, true, RQ>), dim3(blocks), dim3(kQThreads), 0, st, p);
+    hipLaunchKernelGGL((q256_fwd_kernel<kNF4DQ, true, RQ, T16>), dim3(blocks), dim3(kQThreads), 0, st, p);
   else if (W.double_quant)
-    hipLaunchKernelGGL((q256_fwd_kernel<kNF4DQ, false, RQ>), dim3(blocks), dim3(kQThreads), 0, st, p);
+    hipLaunchKernelGGL((q256_fwd_kernel<kNF4DQ, false, RQ, T16>), dim3(blocks), dim3(kQThreads), 0, st, p);
   else
-    hipLaunchKernelGGL((q256_fwd_kernel<kNF4, false, RQ>), dim3(blocks), dim3(kQThreads), 0, st, p);
+    hipLaunchKernelGGL((q256_fwd_kernel<kNF4, false, RQ, T16>), dim3(blocks), dim3(kQThreads), 0, st, p);
 }
 
 int launch_q256_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, float* T_out,
@@ -1560,10 +1644,12 @@ int launch_q256_fwd(const void* X, int64_t M, const lq_weight& W, const void* A,
   p.tab = nf4_table(W.codebook);
   const unsigned blocks = (unsigned)(p.ti * p.tj);
   timing_begin("q256_fwd", st);
-  if (r <= 32)
-    launch_q256_fmt<1>(W, p, blocks, st);
+  if (r <= 16)
+    launch_q256_fmt<1, true>(W, p, blocks, st);
+  else if (r <= 32)
+    launch_q256_fmt<1, false>(W, p, blocks, st);
   else
-    launch_q256_fmt<2>(W, p, blocks, st);
+    launch_q256_fmt<2, false>(W, p, blocks, st);
   timing_end(st);
   return hip_fail(hipGetLastError(), "q256 launch");
 }
