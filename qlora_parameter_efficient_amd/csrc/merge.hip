@@ -85,8 +85,46 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
       }
     }
   };
-  // NF4: the codes and constants of all slices are loaded up front (4 slices
-  // x 4 chunks); dense: one slice ahead
+  // Loads, in the order they are waited for (they return in order): A's and
+  // B's rows and the c2 of the block's groups first, then the weight (NF4:
+  // the codes and constants of all slices, 4 slices x 4 chunks; dense: one
+  // slice ahead).  Staging A, B and the steps in LDS then waits for the
+  // first only, and the weight is still in flight during the first slice's
+  // low-rank product.
+  // A rows j < RP for columns k0 .. k0+255, B rows nb .. nb+127 (zero past r / K)
+  // (clamped addresses, zeros selected)
+  constexpr int NA = RP * (kTK / 8) / kThreads;  // 16-byte chunks of A per thread
+  u32x4 av[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int idx = tid + kThreads * i, j = idx / (kTK / 8), c = idx % (kTK / 8);
+    int64_t k = k0 + 8 * c;
+    k = k < K ? k : K - 8;
+    av[i] = *reinterpret_cast<const u32x4*>(p.A + (int64_t)(j < r ? j : 0) * K + k);
+  }
+  constexpr int NB = kSlices * kTN * RP / kThreads;  // elements of B per thread
+  uint16_t bv[NB];
+  const int64_t nmax = (int64_t)slices * kTN;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int idx = tid + kThreads * i, n = idx / RP, j = idx % RP;
+    const bool ok = j < r && n < nmax;
+    bv[i] = p.B[(nb + (ok ? n : 0)) * r + (ok ? j : 0)];
+  }
+  // second-level steps of groups g_lo .. g_hi (at most kMergeTab)
+  const int64_t g_lo = (nb * K) >> 14;
+  constexpr int NC = (kMergeTab + kThreads - 1) / kThreads;
+  float c2v[NC];
+  int ng = 0;
+  if (WK == kNF4DQ) {
+    const int64_t g_hi = ((nb + (int64_t)slices * kTN - 1) * K + K - 1) >> 14;
+    ng = (int)(g_hi - g_lo + 1);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int gi = tid + kThreads * i;
+      c2v[i] = p.W.c2[g_lo + (gi < ng ? gi : 0)];
+    }
+  }
   constexpr int NS = WK == kDense ? 2 : kSlices;
   MergeStage<WK> st[NS];
   if (WK == kDense) {
@@ -96,43 +134,21 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
     for (int sl = 0; sl < NS; ++sl) load_slice(sl < slices ? sl : 0, st[sl]);
   }
 
-  const int64_t g_lo = (nb * K) >> 14;
   if (WK != kDense) build_lut(lut, p.tab);
   if (WK == kNF4DQ) {
-    const int64_t g_hi = ((nb + (int64_t)slices * kTN - 1) * K + K - 1) >> 14;
-    build_steps(stab, p.W, g_lo, (int)(g_hi - g_lo + 1));
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      if (tid + kThreads * i < ng) stab[tid + kThreads * i] = dq_step(c2v[i]);
   }
-  // A rows j < RP for columns k0 .. k0+255, B rows nb .. nb+255 (zero past r / K)
-  // (all loads issued before any store; clamped addresses, zeros selected)
-  {
-    constexpr int NA = RP * (kTK / 8) / kThreads;  // 16-byte chunks of A per thread
-    u32x4 av[NA];
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int idx = tid + kThreads * i, j = idx / (kTK / 8), c = idx % (kTK / 8);
-      int64_t k = k0 + 8 * c;
-      k = k < K ? k : K - 8;
-      av[i] = *reinterpret_cast<const u32x4*>(p.A + (int64_t)(j < r ? j : 0) * K + k);
-    }
-    constexpr int NB = kSlices * kTN * RP / kThreads;  // elements of B per thread
-    uint16_t bv[NB];
-    const int64_t nmax = (int64_t)slices * kTN;
+  for (int i = 0; i < NA; ++i) {
+    const int idx = tid + kThreads * i, j = idx / (kTK / 8), c = idx % (kTK / 8);
+    *reinterpret_cast<u32x4*>(At + j * kAPitch + 8 * c) = sel4(j < r && k0 + 8 * c < K, av[i]);
+  }
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int idx = tid + kThreads * i, n = idx / RP, j = idx % RP;
-      const bool ok = j < r && n < nmax;
-      bv[i] = p.B[(nb + (ok ? n : 0)) * r + (ok ? j : 0)];
-    }
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int idx = tid + kThreads * i, j = idx / (kTK / 8), c = idx % (kTK / 8);
-      *reinterpret_cast<u32x4*>(At + j * kAPitch + 8 * c) = sel4(j < r && k0 + 8 * c < K, av[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int idx = tid + kThreads * i, n = idx / RP, j = idx % RP;
-      Bt[idx] = (j < r && n < nmax) ? bv[i] : (uint16_t)0;
-    }
+  for (int i = 0; i < NB; ++i) {
+    const int idx = tid + kThreads * i, n = idx / RP, j = idx % RP;
+    Bt[idx] = (j < r && n < nmax) ? bv[i] : (uint16_t)0;
   }
   __syncthreads();
 
