@@ -37,7 +37,7 @@ Default run (python bench.py [--steps K] [--warmup W]):
   seven projections of a block, NF4, M = 8192, r = 64).
 
 Profiling helpers (for rocprofv3): --mode fwd | fwd_fused | dx | step
-| decode | copy | quant run only that part, a few iterations (after CLOCK_WARMUP_S seconds of
+| decode | decode_layers | copy | quant run only that part, a few iterations (after CLOCK_WARMUP_S seconds of
 the same work for the first five), and print one line.
 """
 from __future__ import annotations
@@ -331,6 +331,50 @@ def decode_bench(S, torch, iters=200, copies=40, replays=20):
     return out
 
 
+def decode_layers_bench(S, torch, n_layers=3, groups=14, replays=20):
+    """One-launch decode of n_layers 4096^2 NF4 layers that read the same X
+    (the query, key and value projections of a block), M = 1, 4, 16, with
+    cold weights: `groups` calls over groups x n_layers distinct weight copies
+    (> the 256 MB Infinity Cache), captured in a HIP graph and replayed.  GB/s
+    counts the 4-bit weight streams of the call's layers."""
+    import numpy as np
+
+    from qlora_parameter_efficient_amd import workloads as wl
+    lq = S["lq"]
+    W = S["W"]
+    Ws = [[lq.NF4Weight(W.codes.clone(), N, K, W.q8.clone(), W.c2.clone())
+           for _ in range(n_layers)] for _ in range(groups)]
+    As, Bs = [S["A"]] * n_layers, [S["B"]] * n_layers
+    sc = [S["s"]] * n_layers
+    out = {"layers": n_layers, "N": N, "K": K, "r": R}
+    for m in (1, 4, 16):
+        Xm = torch.from_numpy(wl.decode_inputs(m).bits.view(np.int16).copy()).view(
+            torch.bfloat16).to(S["dev"])
+        Ys = [torch.empty((m, N), dtype=torch.bfloat16, device=S["dev"]) for _ in range(n_layers)]
+
+        def call(ws):
+            lq.lq_lora_fwd_decode_layers(Xm, ws, As, Bs, sc, Ys=Ys)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call(Ws[0])
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for ws in Ws:
+                call(ws)
+        g.replay()
+        t = cuda_time(g.replay, replays, torch) / groups
+        out[f"M{m}"] = {"us_per_call_graph_cold": round(t * 1e3, 2),
+                        "us_per_layer": round(t * 1e3 / n_layers, 2),
+                        "weight_stream_GBs_graph_cold":
+                            round(n_layers * NF4_STREAM_BYTES / (t * 1e-3) / 1e9, 1)}
+        del g
+    del Ws
+    return out
+
+
 def graph_time(fn, torch, calls=20, replays=10):
     """GPU time (ms) per fn() call: `calls` calls captured in one HIP graph,
     replayed `replays` times (host and launch overhead amortised)."""
@@ -354,6 +398,7 @@ def secondary(S, torch, dec=None):
     lq = S["lq"]
     res = {}
     res["decode_nf4"] = dec if dec is not None else decode_bench(S, torch)
+    res["decode_nf4_three_layers_one_launch"] = decode_layers_bench(S, torch)
     # forwards of 32 and 64 rows (the weight-streaming kernel), graph-launched, warm weights
     from qlora_parameter_efficient_amd import workloads as wlc
     chunks = {}
@@ -528,7 +573,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--mode", default="full",
-                    choices=["full", "step", "fwd", "fwd_fused", "dx", "decode", "copy", "quant"])
+                    choices=["full", "step", "fwd", "fwd_fused", "dx", "decode", "decode_layers", "copy",
+                             "quant"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-secondary", action="store_true")
     a = ap.parse_args(argv)
@@ -602,6 +648,9 @@ def main(argv=None):
     if a.mode == "decode":
         print(json.dumps({"mode": "decode", "decode_nf4": decode_bench(S, torch, iters=a.steps)}))
         return 0
+    if a.mode == "decode_layers":
+        print(json.dumps({"mode": "decode_layers", "decode_layers": decode_layers_bench(S, torch)}))
+        return 0
 
     # The GPU's clocks settle only after some milliseconds of sustained work:
     # with five warm-up steps (about 1 ms) the first timed steps run up to 10%
@@ -619,14 +668,22 @@ def main(argv=None):
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    # nothing else runs in this process during the timed region (the clock
+    # sampler's thread contends for the interpreter lock with the launches, so
+    # the clock is sampled over a second, untimed run of the same steps below)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(a.steps):
+        step(S)
+    ev1.record()
+    spin_sync(ev1, torch)
+    wall = time.perf_counter() - t0
     with SclkSampler() as clk:
-        t0 = time.perf_counter()
-        ev0.record()
-        for _ in range(a.steps):
-            step(S)
-        ev1.record()
-        spin_sync(ev1, torch)
-        wall = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < max(wall, 0.02):
+            for _ in range(a.steps):
+                step(S)
+            torch.cuda.synchronize()
     ms_per_step = wall * 1e3 / a.steps
     ev_ms_per_step = ev0.elapsed_time(ev1) / a.steps
     value = STEP_FLOP / (wall / a.steps) / 1e12
@@ -703,7 +760,7 @@ def main(argv=None):
            "gpu_event_ms_per_step_steady": round(t_step_ev, 4),
            "clock_warmup_steps": n_clock,
            "graph_ms_per_step": round(ms_graph, 4),
-           "sclk_mhz_timed_region": clk.mhz, "sclk_samples": len(clk.samples),
+           "sclk_mhz_same_steps": clk.mhz, "sclk_samples": len(clk.samples),
            "roofline": roof}
     if not a.no_cpu:
         log("timing the CPU oracle ...")

@@ -420,6 +420,39 @@ int lq_lora_fwd_multi_ranks(const void* X, int64_t T_tokens, const lq_weight* W0
                             int32_t n_seg, lq_dtype dt, void* Y, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Decode forward of several adapted layers that read the same activations,
+ * in one launch: for g < n_layers,
+ *   Y[g] = X W[g]^T + s[g] (X A[g]^T) B[g]^T
+ * ([MF] 4 "Targeting Attention and MLP Projection Layers": adapters on every
+ * linear projection of a block; the query, key and value projections read the
+ * same input, and so do the MLP's gate and up projections; [FT] "Which Layers
+ * to Adapt").  Each layer's result is that of lq_lora_fwd on the same inputs
+ * (up to the summation order of T), with the same decode kernel: every
+ * layer's weight is streamed once in one launch, which pays the launch and
+ * the first memory round trip once for all of them.
+ *   X        device M x K bf16, 0 <= M <= 16 (M = 0 is a no-op)
+ *   n_layers 1 .. LQ_DECODE_MAX_LAYERS
+ *   W        host array of n_layers weights (device data as in lq_lora_fwd,
+ *            bf16 path rules: K % 64 == 0, N % 64 == 0, N, K <= 65536); all
+ *            with the same K, kind, constant format and codebook
+ *   A, B     host arrays of device pointers: A[g] r x K bf16, B[g] N_g x r
+ *   r        1 <= r <= 64, the same for every layer
+ *   s        host float[n_layers]: each layer's alpha / r
+ *   Y        host array of device pointers: Y[g] M x N_g bf16 (written)
+ *   T_out    NULL, or a host array whose entries are NULL or device M x r
+ *            float32 (receives T = X A[g]^T)
+ * No workspace.  Calls on one stream are ordered; calls that overlap on
+ * different streams use different slots of the decode's library memory, as
+ * lq_lora_fwd's decode does.  Argument errors return a negative status
+ * before any launch.
+ */
+#define LQ_DECODE_MAX_LAYERS 8
+int lq_lora_fwd_decode_layers(const void* X, int64_t M, int32_t n_layers, const lq_weight* W,
+                              const void* const* A, const void* const* B, int64_t r,
+                              const float* s, void* const* Y, float* const* T_out,
+                              hipStream_t stream);
+
 /* ------------------------------------------------- optimizer step (A, B) */
 
 /*

@@ -507,6 +507,37 @@ int lq_lora_fwd(const void* X, int64_t M, const lq_weight* W0, const void* A, co
   return dispatch::bf16_fwd(X, M, *W0, A, B, r, scale, Y, T_out, stream);
 }
 
+int lq_lora_fwd_decode_layers(const void* X, int64_t M, int32_t n_layers, const lq_weight* W,
+                              const void* const* A, const void* const* B, int64_t r,
+                              const float* s, void* const* Y, float* const* T_out,
+                              hipStream_t stream) {
+  static_assert(LQ_DECODE_MAX_LAYERS == kDecodeMaxGroup, "layer limit");
+  REQUIRE(n_layers >= 1 && n_layers <= LQ_DECODE_MAX_LAYERS, LQ_ERR_INVALID_ARG,
+          "n_layers = %d outside [1, %d]", (int)n_layers, LQ_DECODE_MAX_LAYERS);
+  REQUIRE(W && A && B && s && Y, LQ_ERR_INVALID_ARG, "W, A, B, s or Y array is NULL");
+  REQUIRE(M >= 0 && M <= kDecodeMaxM, LQ_ERR_UNSUPPORTED, "M = %lld outside [0, %lld]",
+          (long long)M, (long long)kDecodeMaxM);
+  REQUIRE(r >= 1 && r <= kMaxRank, LQ_ERR_UNSUPPORTED, "rank %lld outside [1, %lld]",
+          (long long)r, (long long)kMaxRank);
+  for (int g = 0; g < n_layers; ++g) {
+    int rc = check_weight(&W[g], LQ_BF16);
+    if (rc) return rc;
+    if ((rc = check_bf16_shape(&W[g]))) return rc;
+    if ((rc = check_bf16_rows(M, &W[g]))) return rc;
+    REQUIRE(W[g].K == W[0].K, LQ_ERR_INVALID_ARG, "layer %d has K=%lld, layer 0 K=%lld", g,
+            (long long)W[g].K, (long long)W[0].K);
+    REQUIRE(W[g].kind == W[0].kind && (W[g].kind == LQ_WEIGHT_DENSE ||
+                                       (W[g].double_quant == W[0].double_quant &&
+                                        W[g].codebook == W[0].codebook)),
+            LQ_ERR_INVALID_ARG, "layer %d's weight format differs from layer 0's", g);
+    REQUIRE(M == 0 || (A[g] && B[g] && Y[g]), LQ_ERR_INVALID_ARG,
+            "A, B or Y of layer %d is NULL", g);
+  }
+  if (M == 0) return LQ_OK;
+  REQUIRE(X != nullptr, LQ_ERR_INVALID_ARG, "X is NULL");
+  return dispatch::decode_fwd_group(X, M, n_layers, W, A, B, r, s, Y, T_out, stream);
+}
+
 int lq_lora_bwd(const void* dY, const void* X, int64_t M, const lq_weight* W0, const void* A,
                 const void* B, int64_t r, float scale, lq_dtype dt, const float* T_saved,
                 void* dX, float* dA, float* dB, int32_t accumulate, void* ws, size_t ws_bytes,

@@ -16,6 +16,8 @@
 // takes 32 rows of Z straight into MFMA registers; the small G tile of each
 // step is staged in LDS (transposed for B).
 #include <atomic>
+#include <climits>
+#include <cstring>
 #include <map>
 #include <mutex>
 
@@ -405,8 +407,12 @@ __device__ __forceinline__ void dec_t_direct(const DecParams& p, float* T) {
   }
 }
 
+// The body of the one-launch decode.  lb is the workgroup's block within its
+// layer (output rows 16 lb ..), pbase the index of the layer's first producer
+// in the slot's partial-sum words; blockIdx.x and gridDim.x keep their
+// call-wide meaning (counting in, the workgroup that moves the epoch on).
 template <int WK, int XS, int JT, bool SS>
-__global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
+__device__ __forceinline__ void dq_body(const DecParams& p, const int lb, const int pbase) {
   constexpr bool XL = XS > 0;
   constexpr int CH = 2;
   constexpr int NT = 64 * kGemvWaves;
@@ -429,7 +435,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, q = lane >> 4;
   const int64_t N = p.W.N, K = p.W.K, M = p.M;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n0 = (int64_t)lb * 16;
   const int r = p.r, ET = (int)M * r;
   const int64_t G = K / 32;
 
@@ -448,9 +454,9 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
     }
   }
   // producers: granule g0 + wave of the range [g0, g1) (at most one per wave)
-  const bool producer = (int)blockIdx.x < p.P;
-  const int64_t g0 = producer ? (int64_t)blockIdx.x * G / p.P : 0;
-  const int64_t g1 = producer ? (int64_t)(blockIdx.x + 1) * G / p.P : 0;
+  const bool producer = lb < p.P;
+  const int64_t g0 = producer ? (int64_t)lb * G / p.P : 0;
+  const int64_t g1 = producer ? (int64_t)(lb + 1) * G / p.P : 0;
   const bool twave = producer && g0 + wave < g1;  // wave-uniform
   u32x4 af[JT];
   if (twave) {
@@ -590,7 +596,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
         for (int i = 0; i < 4; ++i) {
           const int j = 16 * jt + 4 * q + i;
           if (j < r)
-            __hip_atomic_store(&sl->part[blockIdx.x * kDecMaxT + l16 * r + j], tagged(tag, s4[i]),
+            __hip_atomic_store(&sl->part[(pbase + lb) * kDecMaxT + l16 * r + j],
+                               tagged(tag, s4[i]),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
@@ -613,7 +620,10 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
         for (int d = 0; d < 4; ++d) acc[i] = mfma16(wraw[i][d], sel4(ok[i], xf[i][d]), acc[i]);
       } else {
         // SS: the granule's block within its row, (4 t + q) / 2
-        const float a = SS ? sa[l16 * 65 + (int)((4 * (base + kGemvWaves * i) + q) >> 1)]
+        // (granules past the row's end read the last block's scale: their
+        // activations are masked, and an unwritten scale could be NaN)
+        const int sblk = (int)((4 * (base + kGemvWaves * i) + q) >> 1);
+        const float a = SS ? sa[l16 * 65 + (sblk < KB ? sblk : KB - 1)]
                         : WK == kNF4DQ ? dq_q_rt(p.W.dq, sq[i]) * dq_step(sc2[i])
                                        : __uint_as_float(sq[i]);
 #pragma unroll
@@ -646,7 +656,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
 #pragma unroll
     for (int b = 0; b < kDecMaxP; ++b)
       if (b < p.P)
-        v[b] = __hip_atomic_load(&sl->part[b * kDecMaxT + tid], __ATOMIC_RELAXED,
+        v[b] = __hip_atomic_load(&sl->part[(pbase + b) * kDecMaxT + tid], __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
     float t = 0.0f;
 #pragma unroll
@@ -656,8 +666,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
         while ((uint32_t)(v[b] >> 32) != tag && got) {
           if (++it > p.spin) got = false;
           __builtin_amdgcn_s_sleep(1);
-          v[b] = __hip_atomic_load(&sl->part[b * kDecMaxT + tid], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+          v[b] = __hip_atomic_load(&sl->part[(pbase + b) * kDecMaxT + tid],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         t += __uint_as_float((uint32_t)v[b]);
       }
@@ -671,7 +681,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
       __hip_atomic_fetch_add(&g_dec_giveups, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     dec_t_direct(p, tT);
   }
-  if (blockIdx.x == 0 && p.T_out)
+  if (lb == 0 && p.T_out)
     for (int e = lane; e < ET; e += 64) p.T_out[e] = tT[64 * (e / r) + e % r];
   f32x4 sum = part[0][lane];
 #pragma unroll
@@ -714,6 +724,410 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
         __hip_atomic_store(&sl->started[x][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_add(&sl->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+}
+
+template <int WK, int XS, int JT, bool SS>
+__global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
+  dq_body<WK, XS, JT, SS>(p, (int)blockIdx.x, 0);
+}
+
+// Several adapted layers that read the same activations (the query, key and
+// value projections of an attention block, the gate and up projections of its
+// MLP) in one launch.  The layers' 16-row blocks are numbered one after the
+// other (layer g owns blocks blk0 .. blk0 + N_g / 16 - 1) and the grid has at
+// most one workgroup per compute unit: workgroup w takes blocks w, w + grid,
+// w + 2 grid, ... in turn, and the code loads (and constants and B rows) of
+// its next block are issued before it works on the current one, so that
+// their memory latency overlaps the dequantisation, the handoff of T and the
+// stores of the current block.  Each block's work is the single-layer
+// decode's (16 waves split the reduction, dequantised codes fed to
+// 16 x 16 x 32 MFMAs, wave partials added through LDS, rank-r expand).  The
+// first nprod workgroups also form partial sums of T, producer pbase + i of
+// layer g reducing its share of that layer's A, published as tagged words
+// in the stream's slot before their first block; every block reads its
+// layer's words after its own stream.  All layers share X, K, r, the weight
+// format and the call's tag.
+constexpr int kDecMaxGroup = kDecodeMaxGroup;
+struct DecLayer {
+  WeightArgs W;
+  const uint16_t* A;
+  const uint16_t* B;
+  float* T_out;
+  uint16_t* Y;
+  float s;
+  int32_t blk0, P, pbase;
+};
+struct DecGroupParams {
+  DecParams c;  // X, M, r, tab, slot, spin, and layer 0's weight (K, format)
+  DecLayer l[kDecMaxGroup];
+  int32_t n;        // layers
+  int32_t nblocks;  // 16-row blocks of all layers
+  int32_t nprod;    // producers of all layers
+};
+
+// Index of the layer whose range holds v (blocks, or producers when prod);
+// wave-uniform.  The kernel keeps layer indexes and reads a layer's fields
+// from the argument block where it needs them.
+__device__ __forceinline__ int dec_layer_at(const DecGroupParams& gp, int v, bool prod) {
+  int g = 0;
+#pragma unroll
+  for (int i = 1; i < kDecMaxGroup; ++i)
+    if (i < gp.n && v >= (prod ? gp.l[i].pbase : gp.l[i].blk0)) g = i;
+  return g;
+}
+
+// waves of a grouped-decode workgroup, and granules per lane and round (one
+// round covers K = 4096): 256 registers per lane with one workgroup per
+// compute unit
+constexpr int kDecGWaves = 8, kDecGCH = 4;
+
+template <int WK, bool SS>
+struct DecBlockLoads {
+  u32x4 w[kDecGCH][WK == kDense ? 4 : 1];  // one round of this lane's granules
+  uint32_t sq[kDecGCH];                    // their block constants (not SS)
+  float sc2[kDecGCH];
+  // SS: the constants of blocks tid and tid + 64 kDecGWaves of the 16 rows
+  uint32_t sraw[2];
+  float sc2raw[2];
+  uint16_t braw[2];  // elements tid and tid + 64 kDecGWaves of its 16 rows of B
+};
+
+template <int WK, int XS, int JT, bool SS>
+__global__ __launch_bounds__(64 * kDecGWaves) void dqg_kernel(DecGroupParams gp) {
+  constexpr bool XL = XS > 0;
+  constexpr int CH = kDecGCH;
+  constexpr int NT = 64 * kDecGWaves;
+  constexpr int XC = XL ? XS / 8 / NT : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[XL ? XS : 8];
+  __shared__ float2 lut[256];
+  __shared__ f32x4 part[kDecGWaves][64];
+  __shared__ float tB[16 * 64];
+  __shared__ float tT[16 * 64];
+  __shared__ float sa[SS ? 16 * 65 : 1];
+  const DecParams& c = gp.c;
+  DecSlot* sl = g_dec_slot + c.slot;
+  const uint32_t tag =
+      __hip_atomic_load(&sl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  asm volatile("" ::: "memory");  // keep the epoch load first
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, q = lane >> 4;
+  const int64_t K = c.W.K, M = c.M;
+  const int r = c.r, ET = (int)M * r;
+  const int64_t G = K / 32;
+  const int64_t steps = (G + 3) / 4;
+  const int KB = (int)(K / 64);
+  const int EB = 16 * r;
+  // B elements and (SS) block constants: two per thread (16 r and 16 K / 64
+  // are at most 1024)
+  int tb[2], tq[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + NT * u;
+    tb[u] = e < EB ? e : EB - 1;
+    tq[u] = SS ? (e < 16 * KB ? e : 16 * KB - 1) : 0;
+  }
+  const bool mrow = l16 < M;
+  const int64_t xm = mrow ? l16 : 0;
+
+  // X chunks first (clamped, branchless), staged in LDS below
+  const int64_t nxc = M * K / 8, rowc = K / 8;
+  u32x4 xc[XC];
+  uint32_t xsto[XC];
+  if (XL) {
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      int64_t ci = tid + (int64_t)NT * i;
+      ci = ci < nxc ? ci : nxc - 1;
+      xc[i] = *reinterpret_cast<const u32x4*>(c.X + 8 * ci);
+      const int64_t m = ci / rowc, ch = ci - m * rowc;
+      xsto[i] = (uint32_t)(m * K + 8 * (ch ^ (m & 15)));
+    }
+  }
+  // producer role: granules [g0, g1) of its layer's reduction, one per wave
+  // (the first one's A fragments loaded now)
+  const bool producer = (int)blockIdx.x < gp.nprod;
+  const DecLayer& PL = gp.l[dec_layer_at(gp, producer ? (int)blockIdx.x : 0, true)];
+  const int lp = (int)blockIdx.x - PL.pbase;
+  const int64_t g0 = producer ? (int64_t)lp * G / PL.P : 0;
+  const int64_t g1 = producer ? (int64_t)(lp + 1) * G / PL.P : 0;
+  const bool twave = producer && g0 + wave < g1;  // wave-uniform
+  u32x4 af[JT];
+  if (twave) {
+    const int64_t k = 32 * (g0 + wave) + 8 * q;
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      const int j = 16 * jt + l16;
+      af[jt] = *reinterpret_cast<const u32x4*>(PL.A + (int64_t)(j < r ? j : 0) * K + k);
+    }
+  }
+
+  // loads of one round (granule steps base, base + 16) of block bid
+  auto issue_round = [&](DecBlockLoads<WK, SS>& o, int gi, int bid, int64_t base) {
+    const DecLayer& L = gp.l[gi];
+    const int64_t n = (int64_t)(bid - L.blk0) * 16 + l16;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int64_t t = base + kDecGWaves * i;
+      const int64_t g = 4 * t + q;
+      const bool ok = t < steps && g < G;
+      const int64_t e = n * K + (ok ? 32 * g : 0);
+      if (WK == kDense) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          o.w[i][d] = *reinterpret_cast<const u32x4*>(L.W.dense + e + 8 * d);
+      } else {
+        o.w[i][0] = *reinterpret_cast<const u32x4*>(L.W.codes + (e >> 1));
+        if (SS) {
+        } else if (WK == kNF4DQ) {
+          o.sq[i] = L.W.q8[e >> 6];
+          o.sc2[i] = L.W.c2[e >> 14];
+        } else {
+          o.sq[i] = __float_as_uint(L.W.absmax[e >> 6]);
+        }
+      }
+    }
+  };
+  // the block's B rows and (SS) the constants of its 16 rows
+  auto issue_consts = [&](DecBlockLoads<WK, SS>& o, int gi, int bid) {
+    const DecLayer& L = gp.l[gi];
+    const int64_t n0 = (int64_t)(bid - L.blk0) * 16;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      o.braw[u] = L.B[n0 * r + tb[u]];
+      if (SS) {
+        const int64_t e = n0 * KB + tq[u];
+        if (WK == kNF4DQ) {
+          o.sraw[u] = L.W.q8[e];
+          o.sc2raw[u] = L.W.c2[e >> 8];
+        } else {
+          o.sraw[u] = __float_as_uint(L.W.absmax[e]);
+        }
+      }
+    }
+  };
+
+  int bid = (int)blockIdx.x;
+  int gi = dec_layer_at(gp, bid, false);
+  DecBlockLoads<WK, SS> cur;
+  issue_round(cur, gi, bid, wave);
+  issue_consts(cur, gi, bid);
+  if (WK != kDense) build_lut(lut, c.tab);
+  if (XL) {
+#pragma unroll
+    for (int i = 0; i < XC; ++i) *reinterpret_cast<u32x4*>(xs + xsto[i]) = xc[i];
+  }
+  __syncthreads();  // level table, staged X
+  // count this workgroup in: its epoch load, issued before the loads waited
+  // for above, has returned (loads complete in order)
+  if (tid == 0)
+    __hip_atomic_fetch_add(&sl->started[blockIdx.x & 7][0], 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+
+  // ---- producers: partial sums of their layer's T over [g0, g1), added
+  // over the waves through LDS one rank tile at a time
+  if (producer) {
+    f32x4 ta[JT];
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) ta[jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (twave) {
+      for (int64_t g = g0 + wave; g < g1; g += kDecGWaves) {
+        const int64_t k = 32 * g + 8 * q;
+        u32x4 x;
+        if (XL)
+          x = *reinterpret_cast<const u32x4*>(xs + xm * K + 8 * ((k >> 3) ^ (xm & 15)));
+        else
+          x = *reinterpret_cast<const u32x4*>(c.X + xm * K + k);
+        x = sel4(mrow, x);
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          const int j = 16 * jt + l16;
+          const u32x4 a =
+              g == g0 + wave
+                  ? af[jt]
+                  : *reinterpret_cast<const u32x4*>(PL.A + (int64_t)(j < r ? j : 0) * K + k);
+          ta[jt] = mfma16(sel4(j < r, a), x, ta[jt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) {
+      part[wave][lane] = ta[jt];
+      __syncthreads();
+      if (wave == 0 && mrow) {
+        f32x4 s4 = part[0][lane];
+        for (int w = 1; w < kDecGWaves; ++w) {
+          const f32x4 o = part[w][lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s4[i] += o[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 16 * jt + 4 * q + i;
+          if (j < r)
+            __hip_atomic_store(&sl->part[blockIdx.x * kDecMaxT + l16 * r + j],
+                               tagged(tag, s4[i]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- the blocks
+  for (; bid < gp.nblocks; bid += (int)gridDim.x) {
+    const int nb = bid + (int)gridDim.x;
+    const bool more = nb < gp.nblocks;
+    const int gn = dec_layer_at(gp, more ? nb : bid, false);
+    DecBlockLoads<WK, SS> nxt;
+    if (more) {
+      issue_round(nxt, gn, nb, wave);
+      issue_consts(nxt, gn, nb);
+    }
+    const DecLayer& L = gp.l[gi];
+    const int lb = bid - L.blk0;
+    const int64_t N = L.W.N, n0 = (int64_t)lb * 16;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + NT * u;
+      if (e < EB) {
+        const int nn = e / r, j = e - nn * r;
+        tB[nn * 64 + j] = bf16_to_f32(cur.braw[u]);
+      }
+      if (SS && e < 16 * KB) {
+        const int rr = e / KB;
+        sa[rr * 65 + (e - rr * KB)] =
+            WK == kNF4DQ ? dq_q_rt(L.W.dq, cur.sraw[u]) * dq_step(cur.sc2raw[u])
+                         : __uint_as_float(cur.sraw[u]);
+      }
+    }
+    __syncthreads();  // B rows, block scales
+
+    f32x4 acc[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t base = wave; base < steps; base += kDecGWaves * CH) {
+      if (base != wave) issue_round(cur, gi, bid, base);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int64_t t = base + kDecGWaves * i;
+        const int64_t g = 4 * t + q;
+        const bool ok = t < steps && g < G && mrow;
+        const int64_t kk = ok ? 32 * g : 0;
+        u32x4 xf[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          xf[d] = XL ? *reinterpret_cast<const u32x4*>(
+                           xs + xm * K + 8 * (((kk >> 3) + d) ^ (xm & 15)))
+                     : *reinterpret_cast<const u32x4*>(c.X + xm * K + kk + 8 * d);
+        if (WK == kDense) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) acc[i] = mfma16(cur.w[i][d], sel4(ok, xf[d]), acc[i]);
+        } else {
+          // (granules past the row's end read the last block's scale: their
+          // activations are masked, and an unwritten scale could be NaN)
+          const int sblk = (int)((4 * t + q) >> 1);
+          const float a = SS ? sa[l16 * 65 + (sblk < KB ? sblk : KB - 1)]
+                          : WK == kNF4DQ ? dq_q_rt(L.W.dq, cur.sq[i]) * dq_step(cur.sc2[i])
+                                         : __uint_as_float(cur.sq[i]);
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            acc[i] = mfma16(deq8(cur.w[i][0][d], a, lut), sel4(ok, xf[d]), acc[i]);
+        }
+      }
+    }
+    f32x4 a0 = acc[0];
+#pragma unroll
+    for (int i = 1; i < CH; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) a0[v] += acc[i][v];
+    part[wave][lane] = a0;
+
+    // T of this block's layer: thread t reads the P words of elements t and
+    // t + 64 kDecGWaves (below M r; all of an element's words in flight),
+    // re-reads any that is not yet this call's (bounded), adds them in
+    // producer order
+    bool got = c.spin >= 0;
+    for (int e = tid; e < ET && got; e += NT) {
+      uint64_t v[kDecMaxP];
+#pragma unroll
+      for (int b = 0; b < kDecMaxP; ++b)
+        if (b < L.P)
+          v[b] = __hip_atomic_load(&sl->part[(L.pbase + b) * kDecMaxT + e], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+      float tsum = 0.0f;
+#pragma unroll
+      for (int b = 0; b < kDecMaxP; ++b) {
+        if (b < L.P) {
+          int it = 0;
+          while ((uint32_t)(v[b] >> 32) != tag && got) {
+            if (++it > c.spin) got = false;
+            __builtin_amdgcn_s_sleep(1);
+            v[b] = __hip_atomic_load(&sl->part[(L.pbase + b) * kDecMaxT + e], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          }
+          tsum += __uint_as_float((uint32_t)v[b]);
+        }
+      }
+      tT[64 * (e / r) + e % r] = tsum;
+    }
+    const bool gave_up = __syncthreads_or(!got);
+    if (wave == 0) {
+      if (gave_up) {
+        if (lane == 0)
+          __hip_atomic_fetch_add(&g_dec_giveups, 1ull, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        DecParams fp = c;
+        fp.A = L.A;
+        dec_t_direct(fp, tT);
+      }
+      if (lb == 0 && L.T_out)
+        for (int e = lane; e < ET; e += 64) L.T_out[e] = tT[64 * (e / r) + e % r];
+      f32x4 sum = part[0][lane];
+#pragma unroll
+      for (int w = 1; w < kDecGWaves; ++w) {
+        const f32x4 o = part[w][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[i] += o[i];
+      }
+      if (mrow) {
+        const int m = l16;
+        float d[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < r; ++j) {
+          const float t = tT[m * 64 + j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d[i] = fmaf(t, tB[(4 * q + i) * 64 + j], d[i]);
+        }
+        float y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = sum[i] + L.s * d[i];
+        *reinterpret_cast<u32x2*>(L.Y + m * N + n0 + 4 * q) =
+            u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      }
+    }
+    __syncthreads();  // part, tT, tB and sa are rewritten for the next block
+    if (more) {
+      cur = nxt;
+      gi = gn;
+    }
+  }
+
+  // ---- workgroup 0, last: once every workgroup has read the epoch, move it on
+  if (blockIdx.x == 0 && tid == 0) {
+    uint32_t cnt = 0;
+    int it = 0;
+    for (;;) {
+      cnt = 0;
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+        cnt += __hip_atomic_load(&sl->started[x][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (cnt >= gridDim.x || ++it > dispatch::kDefaultWaitPolls) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      __hip_atomic_store(&sl->started[x][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&sl->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -860,32 +1274,30 @@ int take_decode_giveups(uint64_t* n) {
   return hip_fail(e, "decode give-up count");
 }
 
-int decode_fwd1(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
-                int64_t r, float s, void* Y, float* T_out, float*, hipStream_t st) {
-  DecParams p;
-  p.X = (const uint16_t*)X;
-  p.M = M;
-  p.W = weight_args(W);
-  p.A = (const uint16_t*)A;
-  p.B = (const uint16_t*)B;
-  p.T_out = T_out;
-  p.r = (int32_t)r;
-  p.s = s;
-  p.Y = (uint16_t*)Y;
-  p.tab = nf4_table(W.codebook);
-  p.P = dec_producers(W.N, W.K);
-  p.slot = stream_slot(st);
-  p.spin = wait_limit();
-  const dim3 grid((unsigned)(W.N / 16)), block(64 * kGemvWaves);
+template <int WK, int XS, int JT, bool SS>
+static void dec_launch(const DecParams* p, const DecGroupParams* gp, unsigned blocks,
+                       hipStream_t st) {
+  const dim3 grid(blocks);
+  if (gp)
+    hipLaunchKernelGGL((dqg_kernel<WK, XS, JT, SS>), grid, dim3(64 * kDecGWaves), 0, st, *gp);
+  else
+    hipLaunchKernelGGL((dq_kernel<WK, XS, JT, SS>), grid, dim3(64 * kGemvWaves), 0, st, *p);
+}
+
+// Picks the instance of the one-launch decode for the weight format, the size
+// of the activations and the rank, and launches it over `blocks` workgroups
+// (the single-layer kernel when gp is NULL, else the grouped one).
+static int dec_select_launch(const lq_weight& W, int64_t M, int64_t r, const DecParams* p,
+                             const DecGroupParams* gp, unsigned blocks, hipStream_t st) {
   const int64_t mk = M * W.K;
   const int xs = W.K % 128 ? 0 : mk <= 16384 ? 1 : mk <= 65536 ? 2 : 0;
   const int jt = r <= 16 ? 0 : r <= 32 ? 1 : 2;
   // block scales staged per workgroup for an NF4 weight with K <= 4096
   const bool ss = W.kind == LQ_WEIGHT_NF4 && W.K <= 4096;
   const int sel = ((weight_format(W) * 3 + xs) * 3 + jt) * 2 + (ss ? 1 : 0);
-#define LQ_DEC(WKv, XSv, JTv, SSv, idx)                                            \
-  case idx:                                                                        \
-    hipLaunchKernelGGL((dq_kernel<WKv, XSv, JTv, SSv>), grid, block, 0, st, p);    \
+#define LQ_DEC(WKv, XSv, JTv, SSv, idx)                \
+  case idx:                                            \
+    dec_launch<WKv, XSv, JTv, SSv>(p, gp, blocks, st); \
     break;
 #define LQ_DEC3(WKv, XSv, base)                                                    \
   LQ_DEC(WKv, XSv, 1, false, 2 * (base)) LQ_DEC(WKv, XSv, 2, false, 2 * (base) + 2) \
@@ -910,6 +1322,70 @@ int decode_fwd1(const void* X, int64_t M, const lq_weight& W, const void* A, con
 #undef LQ_DEC3
 #undef LQ_DEC
   return hip_fail(hipGetLastError(), "decode launch");
+}
+
+int decode_fwd1(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
+                int64_t r, float s, void* Y, float* T_out, float*, hipStream_t st) {
+  DecParams p;
+  p.X = (const uint16_t*)X;
+  p.M = M;
+  p.W = weight_args(W);
+  p.A = (const uint16_t*)A;
+  p.B = (const uint16_t*)B;
+  p.T_out = T_out;
+  p.r = (int32_t)r;
+  p.s = s;
+  p.Y = (uint16_t*)Y;
+  p.tab = nf4_table(W.codebook);
+  p.P = dec_producers(W.N, W.K);
+  p.slot = stream_slot(st);
+  p.spin = wait_limit();
+  return dec_select_launch(W, M, r, &p, nullptr, (unsigned)(W.N / 16), st);
+}
+
+int decode_fwd_group(const void* X, int64_t M, int32_t n, const lq_weight* W,
+                     const void* const* A, const void* const* B, int64_t r, const float* s,
+                     void* const* Y, float* const* T_out, hipStream_t st) {
+  DecGroupParams gp;
+  memset(&gp, 0, sizeof(gp));
+  gp.c.X = (const uint16_t*)X;
+  gp.c.M = M;
+  gp.c.r = (int32_t)r;
+  gp.c.tab = nf4_table(W[0].codebook);
+  gp.c.slot = stream_slot(st);
+  gp.c.spin = wait_limit();
+  gp.c.W = weight_args(W[0]);
+  gp.n = n;
+  // producers per layer: at most kDecMaxP in all
+  const int pmax = kDecMaxP / n;
+  int32_t blk = 0, pb = 0;
+  for (int g = 0; g < n; ++g) {
+    DecLayer& L = gp.l[g];
+    L.W = weight_args(W[g]);
+    L.A = (const uint16_t*)A[g];
+    L.B = (const uint16_t*)B[g];
+    L.T_out = T_out ? T_out[g] : nullptr;
+    L.Y = (uint16_t*)Y[g];
+    L.s = s[g];
+    const int pg = dec_producers(W[g].N, W[g].K);
+    L.P = pg < pmax ? pg : pmax;
+    L.blk0 = blk;
+    L.pbase = pb;
+    blk += (int32_t)(W[g].N / 16);
+    pb += L.P;
+  }
+  for (int g = n; g < kDecMaxGroup; ++g) gp.l[g].blk0 = gp.l[g].pbase = INT32_MAX;
+  gp.nblocks = blk;
+  gp.nprod = pb;
+  // one workgroup per compute unit at most (a workgroup of this kernel fills
+  // one), each taking every grid-th block
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  const int grid = blk < cus ? blk : cus;
+  return dec_select_launch(W[0], M, r, nullptr, &gp, (unsigned)(grid > pb ? grid : pb), st);
 }
 
 int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,

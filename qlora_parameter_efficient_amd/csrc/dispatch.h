@@ -24,6 +24,8 @@ int f32_lora_merge(const lq_weight& W, const float* A, const float* B, int64_t r
 
 // Partial sums of T = X A^T kept by the decode path.
 constexpr int kTParts = 8;
+// Layers one grouped decode call may take (layers that read the same X).
+constexpr int kDecodeMaxGroup = 8;
 
 namespace dispatch {
 
@@ -42,6 +44,13 @@ int decode_fwd(const void* X, int64_t M, const lq_weight& W, const void* A, cons
 size_t decode1_floats(int64_t M, int64_t N, int64_t K, int64_t r);
 int decode_fwd1(const void* X, int64_t M, const lq_weight& W, const void* A, const void* B,
                 int64_t r, float s, void* Y, float* T_out, float* part, hipStream_t st);
+// The one-launch decode over n <= kDecodeMaxGroup layers that read the same
+// X (M <= 16): layer g has weight W[g] (all with the same K, kind, constant
+// format and codebook), factors A[g], B[g], scale s[g] and output Y[g];
+// T_out (or T_out[g]) may be NULL.  Arguments are checked by the caller.
+int decode_fwd_group(const void* X, int64_t M, int32_t n, const lq_weight* W,
+                     const void* const* A, const void* const* B, int64_t r, const float* s,
+                     void* const* Y, float* const* T_out, hipStream_t st);
 // Bound (in polls) of a workgroup's wait for data another workgroup publishes
 // (the decode kernel's T words, the split-K partner's partial sums): polls > 0
 // sets it, 0 restores the default, < 0 makes every such wait give up at once

@@ -82,6 +82,8 @@ _SIGS = {
                                          _i32, _vp, _vp, _sz, _vp]),
     "lq_lora_fwd_multi_ranks": (ctypes.c_int, [_vp, _i64, _WP, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
                                                _i32, _i32, _vp, _vp, _sz, _vp]),
+    "lq_lora_fwd_decode_layers": (ctypes.c_int, [_vp, _i64, _i32, _WP, _vp, _vp, _i64, _vp, _vp,
+                                                 _vp, _vp]),
     "lq_adamw_step": (ctypes.c_int, [ctypes.POINTER(LqAdamwTensor), _i32, _i32, _f32, _f32, _f32,
                                      _f32, _f32, _i64, _f32, _vp]),
     "lq_check_segments": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i32]),
@@ -451,6 +453,32 @@ def lq_lora_fwd_multi_ranks(X, W0, A_cat, B_cat, rank_offsets, scales, seg_offse
                                          _ptr(seg_adapter), seg_adapter.numel(), dt, _ptr(Y),
                                          _ptr(ws), ws.numel(), _stream()))
     return Y
+
+
+def lq_lora_fwd_decode_layers(X, Ws, As, Bs, scales, T_outs=None, Ys=None):
+    """Decode forward of len(Ws) layers that read the same X (M <= 16) in one
+    launch; returns the list of Y.  Ws, As, Bs, scales (and T_outs, Ys when
+    given, entries may be None) are sequences with one entry per layer."""
+    _dev(X, *As, *Bs)
+    n = len(Ws)
+    M = X.shape[0]
+    r = As[0].shape[0]
+    dt = _dt(X)
+    ws = [weight_struct(w, dt) for w in Ws]
+    warr = (LqWeightStruct * n)(*ws)
+    if Ys is None:
+        Ys = [torch.empty((M, w.N), dtype=X.dtype, device=X.device) for w in ws]
+    vp = ctypes.c_void_p * n
+    a = vp(*[_ptr(t) for t in As])
+    b = vp(*[_ptr(t) for t in Bs])
+    y = vp(*[_ptr(t) for t in Ys])
+    sc = (ctypes.c_float * n)(*[float(v) for v in scales])
+    tp = None if T_outs is None else vp(*[_ptr(t) for t in T_outs])
+    _check(lib().lq_lora_fwd_decode_layers(
+        _ptr(X), M, n, ctypes.cast(warr, _WP), ctypes.cast(a, _vp), ctypes.cast(b, _vp), r,
+        ctypes.cast(sc, _vp), ctypes.cast(y, _vp), None if tp is None else ctypes.cast(tp, _vp),
+        _stream()))
+    return Ys
 
 
 def lq_adamw_step(params, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,

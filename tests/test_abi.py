@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(lq.LIB_PATH),
 
 def test_exports_every_declared_symbol():
     declared = lq.declared_symbols()
-    assert len(declared) == 23
+    assert len(declared) == 24
     L = lq.lib()
     for name in declared:
         assert hasattr(L, name), name
@@ -255,3 +255,37 @@ def test_noalloc_size_matches_header():
     text = open(lq.HEADER).read()
     assert "#define LQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
     assert lq.LQ_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_decode_layers_argument_errors_launch_nothing():
+    """lq_lora_fwd_decode_layers rejects bad layer counts, M > 16, layers with
+    different K or weight formats and NULL pointers before any launch."""
+    L = lq.lib()
+
+    def call(ws, M=4, n=None, r=16, X=0x1000, ptrs=0x1000):
+        n = len(ws) if n is None else n
+        k = max(len(ws), 1)
+        warr = (lq.LqWeightStruct * k)(*ws) if ws else None
+        vp = ctypes.c_void_p * k
+        arr = vp(*([ptrs] * k))
+        sc = (ctypes.c_float * k)(*([2.0] * k))
+        return L.lq_lora_fwd_decode_layers(
+            X, M, n, None if warr is None else ctypes.cast(warr, ctypes.POINTER(lq.LqWeightStruct)),
+            ctypes.cast(arr, ctypes.c_void_p), ctypes.cast(arr, ctypes.c_void_p), r,
+            ctypes.cast(sc, ctypes.c_void_p), ctypes.cast(arr, ctypes.c_void_p), None, None)
+
+    nf4 = lambda N=256, K=256: _weight(kind=1, N=N, K=K)
+    assert call([nf4()], n=0) == -1
+    assert call([nf4()] * 9) == -1
+    assert call([nf4()], M=17) == -2
+    assert call([nf4()], r=65) == -2
+    assert call([nf4(), nf4(K=512)]) == -1
+    assert call([nf4(), _weight(kind=0)]) == -1
+    single = nf4()
+    single.double_quant = 0
+    single.absmax = 0x1000
+    assert call([nf4(), single]) == -1
+    assert call([nf4(), nf4(N=96)]) == -2       # N % 64 != 0
+    assert call([nf4(), nf4()], ptrs=0) == -1   # NULL A / B / Y entries
+    assert call([nf4()], X=0) == -1
+    assert call([nf4(), nf4()], M=0, ptrs=0) == 0  # M = 0: nothing to do
