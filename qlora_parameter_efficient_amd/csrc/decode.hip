@@ -736,13 +736,16 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
 // value projections of an attention block, the gate and up projections of its
 // MLP) in one launch.  The layers' 16-row blocks are numbered one after the
 // other (layer g owns blocks blk0 .. blk0 + N_g / 16 - 1) and the grid has at
-// most one workgroup per compute unit: workgroup w takes blocks w, w + grid,
-// w + 2 grid, ... in turn, and the code loads (and constants and B rows) of
-// its next block are issued before it works on the current one, so that
-// their memory latency overlaps the dequantisation, the handoff of T and the
-// stores of the current block.  Each block's work is the single-layer
-// decode's (16 waves split the reduction, dequantised codes fed to
-// 16 x 16 x 32 MFMAs, wave partials added through LDS, rank-r expand).  The
+// most one workgroup per compute unit: workgroup w takes a contiguous range of
+// blocks in turn (consecutive weight rows, mostly of one layer), and the code
+// loads (and constants and B rows) of its next block are issued before it
+// works on the current one, so that their memory latency overlaps the
+// dequantisation, the expand and the stores of the current block.  A layer's
+// T is read once per workgroup, at its first block of that layer.  Each
+// block's work is the single-layer decode's with 8 waves (each two granules
+// per lane more, so that the registers of two blocks in flight fit): the
+// waves split the reduction, dequantised codes feed 16 x 16 x 32 MFMAs, wave
+// partials are added through LDS, then the rank-r expand.  The
 // first nprod workgroups also form partial sums of T, producer pbase + i of
 // layer g reducing its share of that layer's A, published as tagged words
 // in the stream's slot before their first block; every block reads its
@@ -908,8 +911,12 @@ __global__ __launch_bounds__(64 * kDecGWaves) void dqg_kernel(DecGroupParams gp)
     }
   };
 
-  int bid = (int)blockIdx.x;
-  int gi = dec_layer_at(gp, bid, false);
+  // this workgroup's blocks: a contiguous range (consecutive rows, mostly of
+  // one layer, so that a layer's T is read once per workgroup)
+  const int bend = (int)(((int64_t)blockIdx.x + 1) * gp.nblocks / gridDim.x);
+  int bid = (int)((int64_t)blockIdx.x * gp.nblocks / gridDim.x);
+  int gi = dec_layer_at(gp, bid < bend ? bid : 0, false);
+  int tlayer = -1;  // the layer whose T is in tT
   DecBlockLoads<WK, SS> cur;
   issue_round(cur, gi, bid, wave);
   issue_consts(cur, gi, bid);
@@ -975,9 +982,9 @@ __global__ __launch_bounds__(64 * kDecGWaves) void dqg_kernel(DecGroupParams gp)
   }
 
   // ---- the blocks
-  for (; bid < gp.nblocks; bid += (int)gridDim.x) {
-    const int nb = bid + (int)gridDim.x;
-    const bool more = nb < gp.nblocks;
+  for (; bid < bend; ++bid) {
+    const int nb = bid + 1;
+    const bool more = nb < bend;
     const int gn = dec_layer_at(gp, more ? nb : bid, false);
     DecBlockLoads<WK, SS> nxt;
     if (more) {
@@ -1043,12 +1050,14 @@ __global__ __launch_bounds__(64 * kDecGWaves) void dqg_kernel(DecGroupParams gp)
       for (int v = 0; v < 4; ++v) a0[v] += acc[i][v];
     part[wave][lane] = a0;
 
-    // T of this block's layer: thread t reads the P words of elements t and
+    // T of this block's layer, unless the previous block's layer was the same
+    // (tT holds it then): thread t reads the P words of elements t and
     // t + 64 kDecGWaves (below M r; all of an element's words in flight),
     // re-reads any that is not yet this call's (bounded), adds them in
     // producer order
+    const bool tnew = gi != tlayer;  // wave-uniform
     bool got = c.spin >= 0;
-    for (int e = tid; e < ET && got; e += NT) {
+    for (int e = tid; e < ET && got && tnew; e += NT) {
       uint64_t v[kDecMaxP];
 #pragma unroll
       for (int b = 0; b < kDecMaxP; ++b)
@@ -1072,8 +1081,9 @@ __global__ __launch_bounds__(64 * kDecGWaves) void dqg_kernel(DecGroupParams gp)
       tT[64 * (e / r) + e % r] = tsum;
     }
     const bool gave_up = __syncthreads_or(!got);
+    tlayer = gi;
     if (wave == 0) {
-      if (gave_up) {
+      if (gave_up && tnew) {
         if (lane == 0)
           __hip_atomic_fetch_add(&g_dec_giveups, 1ull, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
