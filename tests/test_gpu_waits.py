@@ -8,6 +8,8 @@ and every kernel still runs to its end).
 * Split K (the large-tile path with few tiles): the waiting workgroup of each
   tile gives up and leaves its partner's partial sums unread; the count is
   reported and the output differs from the normal one.
+* Grouped decode (several layers in one launch): one give-up per workgroup
+  and layer it touches, outputs still within the bar.
 * With the default bound nothing gives up, and the outputs are those of the
   normal path again (the flags are cleared by each call)."""
 import numpy as np
@@ -103,4 +105,37 @@ def test_no_giveups_in_normal_operation():
         for _ in range(3):
             lq.lq_lora_fwd(X, Wd, A, B, 2.0)
             lq.lq_lora_bwd(dY, X, Wd, A, B, 2.0, need_grads=False)
+    assert lq.lq_debug_wait_giveups() == 0
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_grouped_decode_giveups_fall_back_to_direct_t(M, forced_giveups):
+    """lq_lora_fwd_decode_layers: a workgroup reads a layer's T once, at its
+    first block of that layer, so with every wait giving up it computes T
+    itself once per layer it touches (its blocks are a contiguous range over
+    the layers' blocks, one workgroup per compute unit)."""
+    from .test_gpu_decode_layers import make_layers, run_group, x_rows
+    K, r, Ns = 4096, 16, [4096, 4096, 4096]
+    layers = make_layers(Ns, K, r, seed=503)
+    Xh = x_rows(M, K, seed=61)
+    nb = sum(n // 16 for n in Ns)
+    grid = min(nb, torch.cuda.get_device_properties(0).multi_processor_count)
+    starts = np.cumsum([0] + [n // 16 for n in Ns])
+    layer_of = lambda b: int(np.searchsorted(starts, b, side="right") - 1)
+    per_call = sum(len({layer_of(b) for b in range(w * nb // grid, (w + 1) * nb // grid)})
+                   for w in range(grid))
+    announce(f"waits grouped decode forced give-up M={M}")
+    calls = 2
+    for _ in range(calls):
+        Ys, Ts = run_group(layers, to_dev(Xh), M, r)
+    n = lq.lq_debug_wait_giveups()
+    assert n == calls * per_call, f"{n} give-ups, expected {calls * per_call}"
+    for g, (L, Y, T) in enumerate(zip(layers, Ys, Ts)):
+        c = L["c"]
+        Yo, _, To = olora.lora_forward(Xh.f64(), L["Wo"], c["A"].f64(), c["B"].f64(), L["s"])
+        assert rel_err(f64(Y), Yo) <= BF16_TOL, f"layer {g}"
+        assert rel_err(f64(T), To) <= BF16_TOL, f"layer {g}"
+    lq.lq_debug_set_wait_limit(0)
+    run_group(layers, to_dev(Xh), M, r)
+    torch.cuda.synchronize()
     assert lq.lq_debug_wait_giveups() == 0
