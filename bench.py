@@ -37,7 +37,7 @@ Default run (python bench.py [--steps K] [--warmup W]):
   seven projections of a block, NF4, M = 8192, r = 64).
 
 Profiling helpers (for rocprofv3): --mode fwd | fwd_fused | dx | step
-| decode | decode_layers | copy | quant run only that part, a few iterations (after CLOCK_WARMUP_S seconds of
+| decode | decode1 (M = 1 only) | decode_layers | copy | quant run only that part, a few iterations (after CLOCK_WARMUP_S seconds of
 the same work for the first five), and print one line.
 """
 from __future__ import annotations
@@ -77,6 +77,7 @@ def src_hash(files):
 
 
 PROD_SOURCES = ["gemm256.hip", "device_util.h", "common.h"]
+DEC_SOURCES = ["decode.hip", "device_util.h", "common.h", "dispatch.h"]
 
 
 def traffic_for(kernel, sources):
@@ -279,7 +280,7 @@ def cpu_baseline(S):
                       f"layer on the NF4-dequantised weight, median of 3 ({t:.2f} s each)"}
 
 
-def decode_bench(S, torch, iters=200, copies=40, replays=20):
+def decode_bench(S, torch, iters=200, copies=40, replays=20, ms=(1, 4, 16)):
     """NF4 decode (M = 1, 4, 16) with cold weights: a sequence of calls over
     `copies` distinct NF4 copies (copies x 8.65 MB > the 256 MB Infinity
     Cache).  Graph: the sequence captured once in a HIP graph and replayed
@@ -292,7 +293,7 @@ def decode_bench(S, torch, iters=200, copies=40, replays=20):
     W = S["W"]
     Ws = [lq.NF4Weight(W.codes.clone(), N, K, W.q8.clone(), W.c2.clone()) for _ in range(copies)]
     out = {}
-    for m in (1, 4, 16):
+    for m in ms:
         Xm = torch.from_numpy(wl.decode_inputs(m).bits.view(np.int16).copy()).view(
             torch.bfloat16).to(S["dev"])
         Ym = torch.empty((m, N), dtype=torch.bfloat16, device=S["dev"])
@@ -573,8 +574,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--mode", default="full",
-                    choices=["full", "step", "fwd", "fwd_fused", "dx", "decode", "decode_layers", "copy",
-                             "quant"])
+                    choices=["full", "step", "fwd", "fwd_fused", "dx", "decode", "decode1",
+                             "decode_layers", "copy", "quant"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-secondary", action="store_true")
     a = ap.parse_args(argv)
@@ -647,6 +648,10 @@ def main(argv=None):
         return 0
     if a.mode == "decode":
         print(json.dumps({"mode": "decode", "decode_nf4": decode_bench(S, torch, iters=a.steps)}))
+        return 0
+    if a.mode == "decode1":
+        print(json.dumps({"mode": "decode1", "decode_nf4": decode_bench(S, torch, iters=a.steps,
+                                                                         replays=2, ms=(1,))}))
         return 0
     if a.mode == "decode_layers":
         print(json.dumps({"mode": "decode_layers", "decode_layers": decode_layers_bench(S, torch)}))
@@ -748,7 +753,8 @@ def main(argv=None):
                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
                       "frac": round(d1["weight_stream_GBs_graph_cold"] / PEAK_HBM_GBS, 4),
                       "bytes_per_call": NF4_STREAM_BYTES,
-                      "us_per_call": d1["us_per_call_graph_cold"], "traffic": None}
+                      "us_per_call": d1["us_per_call_graph_cold"],
+                      "traffic": traffic_for("dq_m1", DEC_SOURCES)}
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
