@@ -157,3 +157,31 @@ def test_graph_with_single_layer_calls():
         run()
         torch.cuda.synchronize()
     del g
+
+
+@pytest.mark.parametrize("v", [(True, "int8", "nf4"), (False, "int8", "nf4"), (True, "fp8", "nf4"),
+                               (True, "int8", "nf4_symmetric")],
+                         ids=["default", "single", "fp8", "sym"])
+@pytest.mark.parametrize("M,K", [(4, 4096), (16, 4096), (3, 8192)], ids=["m4", "m16", "k8192"])
+def test_grouped_dequant_is_exact(v, M, K):
+    """With B = 0 and one-hot activation rows, Y[g] = onehot(k) W'_g^T is
+    column k of layer g's dequantised weight (bf16) bit for bit: the grouped
+    kernel's register level tables give the codec's values."""
+    from .test_gpu_formats import one_hot_rows, quant_both
+    from .gpu_helpers import bits
+    r, Ns = 16, (512, 256, 768)
+    rng = np.random.default_rng(M + K + len(v[1]))
+    qs, Wps = [], []
+    for N in Ns:
+        W = wl.Tensor((rng.standard_normal((N, K)) * 0.02).astype(np.float32), "bf16")
+        q, o = quant_both(W.value, to_dev(W), v)
+        qs.append(q)
+        Wps.append(onf4.nf4_dequantize_bf16(o).reshape(N, K))
+    A = torch.zeros((r, K), dtype=torch.bfloat16, device=DEV)
+    Bs = [torch.zeros((N, r), dtype=torch.bfloat16, device=DEV) for N in Ns]
+    ks = rng.integers(0, K, M)
+    announce(f"decode layers exact dequant M={M} K={K} {v}")
+    Ys = lq.lq_lora_fwd_decode_layers(one_hot_rows(M, K, ks), qs, [A] * 3, Bs, [2.0] * 3)
+    torch.cuda.synchronize()
+    for g, (Y, Wp) in enumerate(zip(Ys, Wps)):
+        assert np.array_equal(bits(Y), Wp[:, ks].T), f"layer {g}: dequant differs"
