@@ -748,9 +748,9 @@ __global__ __launch_bounds__(64 * kGemvWaves) void dq_kernel(DecParams p) {
 // partials are added through LDS, then the rank-r expand.  The
 // first nprod workgroups also form partial sums of T, producer pbase + i of
 // layer g reducing its share of that layer's A, published as tagged words
-// in the stream's slot before their first block; every block reads its
-// layer's words after its own stream.  All layers share X, K, r, the weight
-// format and the call's tag.
+// in the stream's slot before their first block; a workgroup reads a
+// layer's words after the stream of its first block of that layer.  All
+// layers share X, K, r, the weight format and the call's tag.
 constexpr int kDecMaxGroup = kDecodeMaxGroup;
 struct DecLayer {
   WeightArgs W;
