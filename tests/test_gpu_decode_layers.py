@@ -92,11 +92,15 @@ def test_qkv_shapes(M):
     check(layers, Xh, Ys, Ts)
 
 
-@pytest.mark.parametrize("Ns,M,r", [((4096, 1024, 1024), 4, 64), ((11008, 11008), 16, 16),
-                                    ((256,) * 8, 3, 8)],
-                         ids=["gqa-r64", "gate-up", "eight-layers"])
-def test_mixed_widths(Ns, M, r):
-    K = 4096
+@pytest.mark.parametrize("Ns,M,r,K", [((4096, 1024, 1024), 4, 64, 4096),
+                                      ((11008, 11008), 16, 16, 4096),
+                                      ((256,) * 8, 3, 8, 4096),
+                                      ((1024, 512), 16, 64, 4096),
+                                      ((1024, 4096), 2, 16, 11008)],
+                         ids=["gqa-r64", "gate-up", "eight-layers", "m16-r64", "down-k11008"])
+def test_mixed_widths(Ns, M, r, K):
+    """m16-r64: M r = 1024 elements of T and 16 r = 1024 of B, two per thread;
+    down-k11008: no activation staging, several rounds of loads per block."""
     layers = make_layers(list(Ns), K, r, seed=211)
     Xh = x_rows(M, K, seed=17)
     announce(f"decode layers {Ns} M={M} r={r}")
