@@ -189,3 +189,19 @@ def test_grouped_dequant_is_exact(v, M, K):
     torch.cuda.synchronize()
     for g, (Y, Wp) in enumerate(zip(Ys, Wps)):
         assert np.array_equal(bits(Y), Wp[:, ks].T), f"layer {g}: dequant differs"
+
+
+@pytest.mark.parametrize("Ns,K", [((65536, 256), 256), ((256, 128), 65536)],
+                         ids=["n64k", "k64k"])
+def test_limits(Ns, K):
+    """The widest output and reduction the boundary accepts: N = 65536 (about
+    16 blocks per workgroup, a layer switch inside one range) and K = 65536
+    (16 rounds of loads per block, activations read from global memory);
+    whole tensors against the oracle."""
+    M, r = 16, 16
+    layers = make_layers(list(Ns), K, r, seed=601)
+    Xh = x_rows(M, K, seed=67)
+    announce(f"decode layers limits {Ns} K={K}")
+    Ys, Ts = run_group(layers, to_dev(Xh), M, r)
+    torch.cuda.synchronize()
+    check(layers, Xh, Ys, Ts)
